@@ -1,0 +1,285 @@
+"""Plain float64 CPU oracle for one tensor-parallel rank's shard of a Megatron Transformer layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the benchmark's CPU-baseline
+leg may import this module.  It shares no code with the HIP path: it imports numpy and scipy's erf
+and nothing from the package.
+
+Sources (the pages this follows; each is cited by title and section):
+  [TP-essay]  "Megatron-LM技术演进与大规模模型训练实践", §2.1 并行范式奠基期: Y = X·W with W split by
+              columns W = [W1 W2]; each device computes X·W1 or X·W2.
+  [Digest]    "Megatron-LM 深度解读报告", §2.1 (column blocks computed independently, then joined)
+              and the table of §2.2 (Q/K/V projections column-split by head; MLP first matmul
+              column-split, second row-split; LayerNorm / Dropout replicated, not split).
+  [Arch]      "Megatron-LM — 架构与原理", §4 巧妙之处: copy (identity forward, all-reduce backward)
+              and reduce (all-reduce forward, identity backward) are duals; the column->row pairing
+              leaves the MLP with one all-reduce at the RowParallelLinear exit.
+  [Intro]     "Megatron-LM（英伟达超大模型训练框架）完整介绍", §二.2 张量并行: QKV split by column,
+              heads computed independently on each card; MLP fc1 by column, fc2 by row.
+
+Readings where the pages are silent (each is listed in the design notes):
+  R1 activation  = exact GeLU, x·Φ(x) = ½x(1 + erf(x/√2)); the pages name no activation.
+  R2 attention   = scaled dot-product, scores·1/√d, causal (key j visible to query i iff j <= i),
+                   softmax over keys; LSE_i = log Σ_j exp(score_ij) over visible keys.
+  R3 QKV columns = head-interleaved: column h·3d + s·d + j holds part s∈{q,k,v}, element j of head h,
+                   so a contiguous column block is a set of whole heads ("split by column, by head").
+  R4 uneven split = balanced, lower ranks take the remainder (25 heads over 2 ranks -> 13 / 12).
+  R5 biases      = bqkv and b1 split with their weight columns; b2 (row-split layer) added once, by
+                   rank 0, so the partials sum to the unsharded output; db2 produced by rank 0 only.
+  R6 upstream gradient dZ of the row-split output is the full [T, H] tensor on every rank
+                   (backward of reduce is the identity, [Arch] §4).
+  R7 layout      = row-major; activations [B, S, ·] flattened to token b·S + s; weights [in, out].
+
+Every function takes and returns float64 numpy arrays; nothing is rounded to the device's types.
+"""
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+# ---- A0: shard geometry ----------------------------------------------------------------------
+
+def shard_range(n: int, tp_size: int, rank: int):
+    """Offset and count of the items (heads, MLP columns) rank `rank` owns out of n.
+
+    Column blocks of one split ([TP-essay] §2.1; [Digest] §2.1).  Uneven split: reading R4.
+    """
+    if tp_size < 1 or not 0 <= rank < tp_size or n < 0:
+        raise ValueError("bad shard request")
+    base, rem = divmod(n, tp_size)
+    count = base + (1 if rank < rem else 0)
+    offset = rank * base + min(rank, rem)
+    return offset, count
+
+
+def qkv_column_range(n_heads: int, head_dim: int, tp_size: int, rank: int):
+    """Columns [c0, c1) of the full QKV weight owned by `rank`: its heads, whole (reading R3)."""
+    h0, nh = shard_range(n_heads, tp_size, rank)
+    return 3 * head_dim * h0, 3 * head_dim * (h0 + nh)
+
+
+# ---- explicit slicing of the unsharded weights ------------------------------------------------
+
+def slice_qkv(Wqkv, bqkv, n_heads: int, tp_size: int, rank: int):
+    """Column block of the QKV ColumnParallelLinear ([Digest] §2.2 table, attention row)."""
+    d = Wqkv.shape[0] // n_heads
+    c0, c1 = qkv_column_range(n_heads, d, tp_size, rank)
+    return Wqkv[:, c0:c1], bqkv[c0:c1]
+
+
+def slice_fc1(W1, b1, tp_size: int, rank: int):
+    """Column block of fc1 ([Digest] §2.2 table, MLP row: first matmul column-split)."""
+    f0, fr = shard_range(W1.shape[1], tp_size, rank)
+    return W1[:, f0:f0 + fr], b1[f0:f0 + fr]
+
+
+def slice_fc2(W2, tp_size: int, rank: int):
+    """Row block of fc2 ([Digest] §2.2 table, MLP row: second matmul row-split)."""
+    f0, fr = shard_range(W2.shape[0], tp_size, rank)
+    return W2[f0:f0 + fr, :]
+
+
+# ---- element-wise activation (reading R1) ------------------------------------------------------
+
+def gelu(x):
+    """GeLU(x) = x·Φ(x), Φ the standard normal CDF = ½(1 + erf(x/√2))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / _SQRT2))
+
+
+def gelu_grad(x):
+    """d/dx [x·Φ(x)] = Φ(x) + x·φ(x), φ the standard normal density."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(x / _SQRT2)) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
+
+
+# ---- attention (readings R2, R3) ---------------------------------------------------------------
+
+def _heads(QKV, B: int, S: int, n_heads: int, d: int):
+    """q, k, v of every head, each [B, n_heads, S, d], from the head-interleaved columns."""
+    t = np.asarray(QKV).reshape(B, S, n_heads, 3, d)
+    return (t[:, :, :, 0, :].transpose(0, 2, 1, 3),
+            t[:, :, :, 1, :].transpose(0, 2, 1, 3),
+            t[:, :, :, 2, :].transpose(0, 2, 1, 3))
+
+
+def _softmax_causal(q, k, d: int):
+    """P = softmax_j(q·kᵀ/√d) over visible keys j <= i, and LSE_i (reading R2)."""
+    S = q.shape[0]
+    sc = (q @ k.T) / math.sqrt(d)
+    visible = np.tril(np.ones((S, S), dtype=bool))
+    sc = np.where(visible, sc, -np.inf)
+    m = sc.max(axis=1, keepdims=True)
+    e = np.exp(sc - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, (m + np.log(l))[:, 0]
+
+
+def attention_fwd(QKV, B: int, S: int, n_heads: int, d: int):
+    """Per-head causal attention; heads are independent ([Intro] §二.2; [Digest] §2.2 table).
+
+    Returns ctx [B·S, n_heads·d] (head h in columns h·d .. h·d+d-1) and LSE [B, n_heads, S].
+    """
+    q, k, v = _heads(QKV, B, S, n_heads, d)
+    ctx = np.zeros((B, S, n_heads, d))
+    lse = np.zeros((B, n_heads, S))
+    for b in range(B):
+        for h in range(n_heads):
+            p, lse[b, h] = _softmax_causal(q[b, h], k[b, h], d)
+            ctx[b, :, h, :] = p @ v[b, h]
+    return ctx.reshape(B * S, n_heads * d), lse
+
+
+def attention_bwd(QKV, dctx, B: int, S: int, n_heads: int, d: int):
+    """Gradient of the causal attention w.r.t. its QKV input, from the definitions.
+
+    P is recomputed from q, k (recomputation instead of storing it: [Intro] 三.2).
+    dV = Pᵀ·dO;  dP = dO·Vᵀ;  softmax Jacobian dS_ij = P_ij·(dP_ij − Σ_k P_ik·dP_ik);
+    dQ = dS·K/√d;  dK = dSᵀ·Q/√d.  Returned in the same interleaved [B·S, 3·n_heads·d] layout.
+    """
+    q, k, v = _heads(QKV, B, S, n_heads, d)
+    do = np.asarray(dctx).reshape(B, S, n_heads, d)
+    dqkv = np.zeros((B, S, n_heads, 3, d))
+    for b in range(B):
+        for h in range(n_heads):
+            p, _ = _softmax_causal(q[b, h], k[b, h], d)
+            dO = do[b, :, h, :]
+            dP = dO @ v[b, h].T
+            dS = p * (dP - (p * dP).sum(axis=1, keepdims=True))
+            dqkv[b, :, h, 0, :] = dS @ k[b, h] / math.sqrt(d)
+            dqkv[b, :, h, 1, :] = dS.T @ q[b, h] / math.sqrt(d)
+            dqkv[b, :, h, 2, :] = p.T @ dO
+    return dqkv.reshape(B * S, n_heads * 3 * d)
+
+
+# ---- linear parts ------------------------------------------------------------------------------
+
+def qkv_fwd(X, Wqkv, bqkv):
+    """QKV = X·Wqkv + bqkv ([TP-essay] §2.1: Y = X·W)."""
+    return X @ Wqkv + bqkv
+
+
+def qkv_bwd(X, Wqkv, dQKV):
+    """dW = Xᵀ·dQKV, db = Σ_t dQKV, dX = dQKV·Wᵀ (input gradient; a partial sum on a shard)."""
+    return {"dX": dQKV @ Wqkv.T, "dW": X.T @ dQKV, "db": dQKV.sum(axis=0)}
+
+
+def mlp_fwd(X, W1, b1, W2, b2):
+    """A1 = X·W1 + b1;  Y = GeLU(A1);  Z = Y·W2 (+ b2 when b2 is not None)."""
+    A1 = X @ W1 + b1
+    Y = gelu(A1)
+    Z = Y @ W2
+    if b2 is not None:
+        Z = Z + b2
+    return {"A1": A1, "Y": Y, "Z": Z}
+
+
+def mlp_bwd(X, W1, W2, A1, Y, dZ, with_db2: bool):
+    """Backward of mlp_fwd, from the chain rule written out:
+
+    dW2 = Yᵀ·dZ;  db2 = Σ_t dZ;  dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1);  db1 = Σ_t dA1;
+    dW1 = Xᵀ·dA1;  dX = dA1·W1ᵀ.
+    """
+    dA1 = (dZ @ W2.T) * gelu_grad(A1)
+    return {"dX": dA1 @ W1.T, "dW1": X.T @ dA1, "db1": dA1.sum(axis=0),
+            "dW2": Y.T @ dZ, "db2": dZ.sum(axis=0) if with_db2 else None, "dA1": dA1}
+
+
+# ---- the unsharded layer ------------------------------------------------------------------------
+
+def layer_fwd(X, Wqkv, bqkv, W1, b1, W2, b2, B: int, S: int, n_heads: int):
+    """QKV projection + per-head causal attention, and the MLP, on one device, unsplit.
+
+    LayerNorm, dropout and residuals are replicated outside the split ([Digest] §2.2 table) and
+    are not part of the shard; X is the already-normalised input of both blocks.
+    """
+    d = X.shape[1] // n_heads
+    QKV = qkv_fwd(X, Wqkv, bqkv)
+    ctx, lse = attention_fwd(QKV, B, S, n_heads, d)
+    out = mlp_fwd(X, W1, b1, W2, b2)
+    out.update(QKV=QKV, ctx=ctx, lse=lse)
+    return out
+
+
+# ---- one rank's shard: the same names and arguments as the C ABI ---------------------------------
+
+def _check_heads(H, n_heads, tp_size, rank):
+    if H % n_heads:
+        raise ValueError("H must be a multiple of n_heads")
+    h0, nh = shard_range(n_heads, tp_size, rank)
+    return h0, nh, H // n_heads
+
+
+def tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, bqkv_r):
+    """QKV ColumnParallelLinear of rank r: X·Wqkv_r + bqkv_r, no gather ([Arch] §4; [Digest] §2.2)."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert X.shape == (B * S, H) and Wqkv_r.shape == (H, 3 * nh * d)
+    return qkv_fwd(X, Wqkv_r, bqkv_r)
+
+
+def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r):
+    """Causal attention over the rank's own heads ([Intro] §二.2: each card computes its heads)."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert QKV_r.shape == (B * S, 3 * nh * d)
+    return attention_fwd(QKV_r, B, S, nh, d)
+
+
+def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2):
+    """fc1 column shard + GeLU, fc2 row shard -> partial Z_r; b2 added iff rank == 0 (R5).
+
+    Σ_r Z_r is the unsharded Z: the all-reduce at the RowParallelLinear exit ([Arch] §4).
+    """
+    _, fr = shard_range(F, tp_size, rank)
+    assert X.shape == (T, H) and W1_r.shape == (H, fr) and W2_r.shape == (fr, H)
+    return mlp_fwd(X, W1_r, b1_r, W2_r, b2 if rank == 0 else None)
+
+
+def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ):
+    """Backward of the rank's MLP shard.  dZ is the full upstream gradient (R6); dX_r is a partial
+    whose sum over ranks is dX (copy's backward all-reduce, [Arch] §4); db2 iff rank == 0 (R5)."""
+    _, fr = shard_range(F, tp_size, rank)
+    assert dZ.shape == (T, H) and A1_r.shape == (T, fr) and Y_r.shape == (T, fr)
+    return mlp_bwd(X, W1_r, W2_r, A1_r, Y_r, dZ, with_db2=(rank == 0))
+
+
+def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r):
+    """Backward of the QKV column shard; dX_r is a partial summed over ranks ([Arch] §4)."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert dQKV_r.shape == (B * S, 3 * nh * d)
+    return qkv_bwd(X, Wqkv_r, dQKV_r)
+
+
+def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, dctx_r):
+    """Backward of the rank's heads.  The definition needs only QKV_r and dctx_r: P is recomputed."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert dctx_r.shape == (B * S, nh * d)
+    return attention_bwd(QKV_r, dctx_r, B, S, nh, d)
+
+
+def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):
+    """Expert MLP shards applied to the rows each expert owns.
+
+    Rows [o_e, o_{e+1}) of the expert-sorted token matrix go through expert e's column shard of fc1,
+    GeLU, and its row shard of fc2 (expert FFNs as grouped GEMMs: "Megatron-LM — 架构与原理", §6,
+    TE GroupedLinear).  No bias on the expert's fc2 partial.
+    """
+    G = W1_r.shape[0]
+    Z = np.zeros((X_perm.shape[0], W2_r.shape[2]))
+    for e in range(G):
+        lo, hi = int(group_offsets[e]), int(group_offsets[e + 1])
+        if hi > lo:
+            Z[lo:hi] = gelu(X_perm[lo:hi] @ W1_r[e] + b1_r[e]) @ W2_r[e]
+    return Z
+
+
+def normwise_error(got, ref):
+    """‖got − ref‖_F / ‖ref‖_F in float64 (absolute ‖got‖_F when ‖ref‖_F = 0)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    return num / den if den > 0 else num

@@ -1,0 +1,367 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each pin raises AssertionError on failure.  Pins look the oracle's functions up on the module at call
+time, so tests/test_oracle_mutations.py can plant a mistake in the oracle and check that some pin
+fails.  What pins what:
+
+  geometry    golden fixture (the workloads' stated splits) + invariants (cover, contiguous, balanced)
+  gelu        textbook normal-CDF values; odd-part identity; derivative by central differences
+  brute       pure-Python scalar loops (tests/bruteforce.py) on the tiny layer, both ranks
+  identities  column split X·[W1 W2] = [X·W1, X·W2]; row split Σ_r Z_r = Z; Σ_r dX_r = dX;
+              weight-gradient blocks; tp=1 equals the unsharded layer
+  closed      attention closed forms: S=1, query 0, Q=0 (prefix mean, LSE = log(i+1)), constant keys
+              (LSE = q·k/√d + log(i+1)), one dominant key, dV for Q=0
+  fd          central finite differences in fp64 for every gradient output
+"""
+
+import math
+import os
+
+import numpy as np
+
+import oracle.tp_shard as T
+import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    den = max(np.linalg.norm(b), 1e-300)
+    err = np.linalg.norm(a - b) / den
+    assert err <= tol, f"{what}: normwise error {err:.3e} > {tol:.1e}"
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append([float(x) for x in line.split()])
+    return rows
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---- geometry ---------------------------------------------------------------------------------
+
+def pin_geometry():
+    for n, t, r, off, cnt in _read_table("shard_geometry.txt"):
+        got = T.shard_range(int(n), int(t), int(r))
+        assert got == (int(off), int(cnt)), f"shard_range({n},{t},{r}) = {got}"
+    for n in range(0, 40):
+        for t in range(1, 10):
+            parts = [T.shard_range(n, t, r) for r in range(t)]
+            assert sum(c for _, c in parts) == n
+            assert parts[0][0] == 0
+            for (o0, c0), (o1, _) in zip(parts, parts[1:]):
+                assert o1 == o0 + c0, "blocks must be contiguous"
+            counts = [c for _, c in parts]
+            assert max(counts) - min(counts) <= 1
+            assert counts == sorted(counts, reverse=True), "lower ranks take the remainder"
+    assert T.qkv_column_range(25, 64, 2, 1) == (13 * 192, 25 * 192)
+
+
+# ---- GeLU ---------------------------------------------------------------------------------------
+
+def pin_gelu():
+    for x, phi_cdf in _read_table("normal_cdf.txt"):
+        assert abs(float(T.gelu(x)) - x * phi_cdf) <= 1e-13, f"GeLU({x})"
+        dens = math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+        assert abs(float(T.gelu_grad(x)) - (phi_cdf + x * dens)) <= 1e-13, f"GeLU'({x})"
+    xs = np.linspace(-6, 6, 241)
+    assert np.allclose(T.gelu(xs) - T.gelu(-xs), xs, rtol=0, atol=1e-13), "odd-part identity"
+    assert float(T.gelu(0.0)) == 0.0 and abs(float(T.gelu_grad(0.0)) - 0.5) < 1e-15
+    eps = 1e-5
+    fd = (T.gelu(xs + eps) - T.gelu(xs - eps)) / (2 * eps)
+    assert np.max(np.abs(fd - T.gelu_grad(xs))) < 1e-9, "GeLU' vs central differences"
+    assert abs(float(T.gelu(12.0)) - 12.0) < 1e-12 and abs(float(T.gelu(-12.0))) < 1e-12
+
+
+# ---- tiny layer --------------------------------------------------------------------------------
+
+TINY = dict(B=2, S=32, H=64, nh=4, F=256, t=2)
+
+
+def _tiny_full(seed=7, wstd=0.02, bstd=0.02, xstd=1.0, H=None, nh=None, F=None, B=None, S=None):
+    cfg = dict(TINY)
+    for k, v in dict(H=H, nh=nh, F=F, B=B, S=S).items():
+        if v is not None:
+            cfg[k] = v
+    g = _rng(seed)
+    Tt, H, F = cfg["B"] * cfg["S"], cfg["H"], cfg["F"]
+    p = dict(
+        X=g.standard_normal((Tt, H)) * xstd,
+        Wqkv=g.standard_normal((H, 3 * H)) * wstd, bqkv=g.standard_normal(3 * H) * bstd,
+        W1=g.standard_normal((H, F)) * wstd, b1=g.standard_normal(F) * bstd,
+        W2=g.standard_normal((F, H)) * wstd, b2=g.standard_normal(H) * bstd)
+    return cfg, p
+
+
+def pin_brute_forward():
+    cfg, p = _tiny_full()
+    B, S, H, nh, F, t = (cfg[k] for k in ("B", "S", "H", "nh", "F", "t"))
+    d = H // nh
+    for r in range(t):
+        Wq, bq = T.slice_qkv(p["Wqkv"], p["bqkv"], nh, t, r)
+        qkv = T.tp_qkv_shard_fwd(t, r, B, S, H, nh, p["X"], Wq, bq)
+        _close(qkv, bf.matmul_bias(p["X"], Wq, bq), 1e-13, f"QKV r{r}")
+        # sharper scores than the layer's own weights give, so the softmax is far from flat
+        sharp = qkv * 12.0
+        ctx, lse = T.tp_attn_heads_fwd(t, r, B, S, H, nh, sharp)
+        _, nh_r = T.shard_range(nh, t, r)
+        bctx, blse = bf.attention(sharp, B, S, nh_r, d)
+        _close(ctx, bctx, 1e-13, f"ctx r{r}")
+        _close(lse, blse, 1e-13, f"lse r{r}")
+        W1, b1 = T.slice_fc1(p["W1"], p["b1"], t, r)
+        W2 = T.slice_fc2(p["W2"], t, r)
+        out = T.tp_mlp_shard_fwd(t, r, B * S, H, F, p["X"] * 20.0, W1, b1, W2, p["b2"])
+        A1, Y, Z = bf.mlp_forward(p["X"] * 20.0, W1, b1, W2, p["b2"] if r == 0 else None)
+        _close(out["A1"], A1, 1e-13, f"A1 r{r}")
+        _close(out["Y"], Y, 1e-13, f"Y r{r}")
+        _close(out["Z"], Z, 1e-13, f"Z r{r}")
+
+
+def pin_brute_backward():
+    g = _rng(11)
+    Tt, H, F, t = 8, 16, 32, 2
+    X = g.standard_normal((Tt, H))
+    W1, b1 = g.standard_normal((H, F)) * 0.3, g.standard_normal(F) * 0.3
+    W2 = g.standard_normal((F, H)) * 0.3
+    dZ = g.standard_normal((Tt, H))
+    for r in range(t):
+        W1r, b1r = T.slice_fc1(W1, b1, t, r)
+        W2r = T.slice_fc2(W2, t, r)
+        fw = T.tp_mlp_shard_fwd(t, r, Tt, H, F, X, W1r, b1r, W2r, None)
+        got = T.tp_mlp_shard_bwd(t, r, Tt, H, F, X, W1r, W2r, fw["A1"], fw["Y"], dZ)
+        ref = bf.mlp_backward(X, W1r, W2r, fw["A1"], fw["Y"], dZ)
+        for k in ("dX", "dW1", "db1", "dW2"):
+            _close(got[k], ref[k], 1e-13, f"MLP {k} r{r}")
+        if r == 0:
+            _close(got["db2"], ref["db2"], 1e-13, "db2 r0")
+        else:
+            assert got["db2"] is None, "db2 belongs to rank 0 only"
+    B, S, nh = 1, 8, 4
+    d = H // nh
+    Wqkv = g.standard_normal((H, 3 * H)) * 0.3
+    for r in range(t):
+        Wq, _ = T.slice_qkv(Wqkv, np.zeros(3 * H), nh, t, r)
+        dQKV = g.standard_normal((B * S, Wq.shape[1]))
+        got = T.tp_qkv_shard_bwd(t, r, B, S, H, nh, X, Wq, dQKV)
+        ref = bf.linear_backward(X, Wq, dQKV)
+        for k in ("dX", "dW", "db"):
+            _close(got[k], ref[k], 1e-13, f"QKV {k} r{r}")
+
+
+# ---- identities -------------------------------------------------------------------------------
+
+def _run_ranks(cfg, p, t):
+    B, S, H, nh, F = (cfg[k] for k in ("B", "S", "H", "nh", "F"))
+    outs = []
+    for r in range(t):
+        Wq, bq = T.slice_qkv(p["Wqkv"], p["bqkv"], nh, t, r)
+        qkv = T.tp_qkv_shard_fwd(t, r, B, S, H, nh, p["X"], Wq, bq)
+        ctx, lse = T.tp_attn_heads_fwd(t, r, B, S, H, nh, qkv)
+        W1, b1 = T.slice_fc1(p["W1"], p["b1"], t, r)
+        W2 = T.slice_fc2(p["W2"], t, r)
+        mlp = T.tp_mlp_shard_fwd(t, r, B * S, H, F, p["X"], W1, b1, W2, p["b2"])
+        outs.append(dict(qkv=qkv, ctx=ctx, lse=lse, **mlp, W1=W1, W2=W2, Wq=Wq))
+    return outs
+
+
+def pin_identities():
+    for (H, nh, F, t) in ((64, 4, 256, 2), (48, 6, 100, 4), (50, 5, 90, 3), (64, 4, 256, 1)):
+        cfg, p = _tiny_full(seed=3, H=H, nh=nh, F=F, B=2, S=12, wstd=0.2, bstd=0.1)
+        B, S = cfg["B"], cfg["S"]
+        d = H // nh
+        full = T.layer_fwd(p["X"], p["Wqkv"], p["bqkv"], p["W1"], p["b1"], p["W2"], p["b2"], B, S, nh)
+        outs = _run_ranks(cfg, p, t)
+        # column identity: QKV, ctx, lse, A1, Y are column blocks of the unsharded results
+        _close(np.concatenate([o["qkv"] for o in outs], 1), full["QKV"], 1e-13, "QKV concat")
+        _close(np.concatenate([o["ctx"] for o in outs], 1), full["ctx"], 1e-13, "ctx concat")
+        _close(np.concatenate([o["lse"] for o in outs], 1), full["lse"], 1e-13, "lse concat")
+        _close(np.concatenate([o["A1"] for o in outs], 1), full["A1"], 1e-13, "A1 concat")
+        _close(np.concatenate([o["Y"] for o in outs], 1), full["Y"], 1e-13, "Y concat")
+        # row identity: the partials sum to the unsharded output
+        _close(sum(o["Z"] for o in outs), full["Z"], 1e-13, f"sum Z_r (t={t})")
+        # backward: weight-gradient blocks and input-gradient partials
+        g = _rng(5)
+        dZ = g.standard_normal((B * S, H))
+        dctx = g.standard_normal((B * S, H))
+        fullm = T.mlp_bwd(p["X"], p["W1"], p["W2"], full["A1"], full["Y"], dZ, True)
+        d_full_attn = T.attention_bwd(full["QKV"], dctx, B, S, nh, d)
+        fullq = T.qkv_bwd(p["X"], p["Wqkv"], d_full_attn)
+        dXm = np.zeros_like(p["X"])
+        dXq = np.zeros_like(p["X"])
+        dW1s, dW2s, db1s, dWqs, dbqs, dqkvs = [], [], [], [], [], []
+        for r, o in enumerate(outs):
+            m = T.tp_mlp_shard_bwd(t, r, B * S, H, F, p["X"], o["W1"], o["W2"], o["A1"], o["Y"], dZ)
+            h0, nhr = T.shard_range(nh, t, r)
+            dq = T.tp_attn_heads_bwd(t, r, B, S, H, nh, o["qkv"], dctx[:, h0 * d:(h0 + nhr) * d])
+            q = T.tp_qkv_shard_bwd(t, r, B, S, H, nh, p["X"], o["Wq"], dq)
+            dXm += m["dX"]
+            dXq += q["dX"]
+            dW1s.append(m["dW1"]); dW2s.append(m["dW2"]); db1s.append(m["db1"])
+            dWqs.append(q["dW"]); dbqs.append(q["db"]); dqkvs.append(dq)
+            if r == 0:
+                _close(m["db2"], fullm["db2"], 1e-13, "db2")
+        _close(dXm, fullm["dX"], 1e-13, "sum dX_r (MLP)")
+        _close(dXq, fullq["dX"], 1e-13, "sum dX_r (QKV)")
+        _close(np.concatenate(dW1s, 1), fullm["dW1"], 1e-13, "dW1 blocks")
+        _close(np.concatenate(db1s), fullm["db1"], 1e-13, "db1 blocks")
+        _close(np.concatenate(dW2s, 0), fullm["dW2"], 1e-13, "dW2 blocks")
+        _close(np.concatenate(dqkvs, 1), d_full_attn, 1e-13, "dQKV blocks")
+        _close(np.concatenate(dWqs, 1), fullq["dW"], 1e-13, "dWqkv blocks")
+        _close(np.concatenate(dbqs), fullq["db"], 1e-13, "dbqkv blocks")
+
+
+# ---- attention closed forms --------------------------------------------------------------------
+
+def _qkv_from(q, k, v):
+    """Assemble the interleaved [B*S, 3*nh*d] matrix from per-head q, k, v [B, nh, S, d]."""
+    B, nh, S, d = q.shape
+    t = np.stack([q, k, v], axis=3)              # [B, nh, S, 3, d]
+    return t.transpose(0, 2, 1, 3, 4).reshape(B * S, nh * 3 * d)
+
+
+def pin_attention_closed_forms():
+    g = _rng(21)
+    B, nh, S, d = 2, 3, 9, 8
+    q, k, v = (g.standard_normal((B, nh, S, d)) for _ in range(3))
+    # S = 1: ctx = v, LSE = q·k/√d
+    ctx, lse = T.attention_fwd(_qkv_from(q[:, :, :1], k[:, :, :1], v[:, :, :1]), B, 1, nh, d)
+    _close(ctx.reshape(B, 1, nh, d).transpose(0, 2, 1, 3), v[:, :, :1], 1e-15, "S=1 ctx")
+    _close(lse[:, :, 0], (q[:, :, 0] * k[:, :, 0]).sum(-1) / math.sqrt(d), 1e-15, "S=1 lse")
+    # query 0 sees only key 0
+    ctx, lse = T.attention_fwd(_qkv_from(q, k, v), B, S, nh, d)
+    c = ctx.reshape(B, S, nh, d).transpose(0, 2, 1, 3)
+    _close(c[:, :, 0], v[:, :, 0], 1e-15, "row 0 ctx")
+    # Q = 0: uniform weights over the visible prefix, LSE = log(i+1)
+    ctx, lse = T.attention_fwd(_qkv_from(np.zeros_like(q), k, v), B, S, nh, d)
+    c = ctx.reshape(B, S, nh, d).transpose(0, 2, 1, 3)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    _close(c, prefix, 1e-14, "Q=0 prefix mean")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, S + 1)), lse.shape), 1e-14, "Q=0 LSE")
+    # all keys equal: uniform weights, LSE_i = q_i·k/√d + log(i+1)  (pins the 1/√d scale)
+    kc = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    ctx, lse = T.attention_fwd(_qkv_from(q, kc, v), B, S, nh, d)
+    c = ctx.reshape(B, S, nh, d).transpose(0, 2, 1, 3)
+    _close(c, prefix, 1e-13, "constant-key prefix mean")
+    want = (q * kc).sum(-1) / math.sqrt(d) + np.log(np.arange(1, S + 1))[None, None, :]
+    _close(lse, want, 1e-13, "constant-key LSE")
+    # one dominant visible key: ctx_i -> v_j* for i >= j*, while queries before j* cannot see it
+    jstar = 4
+    kd = k.copy() * 0.01
+    kd[:, :, jstar] = 0.0
+    kd[:, :, jstar, 0] = 1.0
+    qd = np.zeros_like(q)
+    qd[..., 0] = 400.0
+    ctx, _ = T.attention_fwd(_qkv_from(qd, kd, v), B, S, nh, d)
+    c = ctx.reshape(B, S, nh, d).transpose(0, 2, 1, 3)
+    _close(c[:, :, jstar:], np.broadcast_to(v[:, :, jstar:jstar + 1], c[:, :, jstar:].shape), 1e-12,
+           "dominant key")
+    assert np.max(np.abs(c[:, :, :jstar] - v[:, :, jstar:jstar + 1])) > 0.1, "future key leaked"
+    # backward with Q = 0: dV_j = Σ_{i>=j} dO_i / (i+1)
+    dO = g.standard_normal((B, S, nh, d))
+    dqkv = T.attention_bwd(_qkv_from(np.zeros_like(q), k, v), dO.reshape(B * S, nh * d), B, S, nh, d)
+    dv = dqkv.reshape(B, S, nh, 3, d)[:, :, :, 2, :]
+    w = dO / np.arange(1, S + 1)[None, :, None, None]
+    want_dv = np.flip(np.cumsum(np.flip(w, axis=1), axis=1), axis=1)
+    _close(dv, want_dv, 1e-13, "Q=0 dV")
+
+
+# ---- finite differences -----------------------------------------------------------------------
+
+def _fd_dir(f, x, v, eps=1e-6):
+    return (f(x + eps * v) - f(x - eps * v)) / (2 * eps)
+
+
+def pin_finite_differences():
+    g = _rng(31)
+    Tt, H, F, t = 6, 8, 12, 2
+    X = g.standard_normal((Tt, H))
+    W1, b1 = g.standard_normal((H, F)) * 0.5, g.standard_normal(F) * 0.5
+    W2, b2 = g.standard_normal((F, H)) * 0.5, g.standard_normal(H) * 0.5
+    dZ = g.standard_normal((Tt, H))
+    for r in range(t):
+        W1r, b1r = T.slice_fc1(W1, b1, t, r)
+        W2r = T.slice_fc2(W2, t, r)
+
+        def loss(X_=X, W1_=W1r, b1_=b1r, W2_=W2r, b2_=b2):
+            return float((T.tp_mlp_shard_fwd(t, r, Tt, H, F, X_, W1_, b1_, W2_, b2_)["Z"] * dZ).sum())
+
+        fw = T.tp_mlp_shard_fwd(t, r, Tt, H, F, X, W1r, b1r, W2r, b2)
+        gr = T.tp_mlp_shard_bwd(t, r, Tt, H, F, X, W1r, W2r, fw["A1"], fw["Y"], dZ)
+        for name, x0, grad, call in (
+                ("dX", X, gr["dX"], lambda z: loss(X_=z)),
+                ("dW1", W1r, gr["dW1"], lambda z: loss(W1_=z)),
+                ("db1", b1r, gr["db1"], lambda z: loss(b1_=z)),
+                ("dW2", W2r, gr["dW2"], lambda z: loss(W2_=z))):
+            for _ in range(3):
+                vdir = g.standard_normal(x0.shape)
+                want = _fd_dir(call, x0, vdir)
+                got = float((grad * vdir).sum())
+                assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD {name} r{r}: {got} vs {want}"
+        vdir = g.standard_normal(b2.shape)
+        want = _fd_dir(lambda z: loss(b2_=z), b2, vdir)
+        if r == 0:
+            assert abs(float((gr["db2"] * vdir).sum()) - want) <= 1e-7 * max(1, abs(want)), "FD db2"
+        else:
+            assert abs(want) < 1e-9, "b2 must not enter a rank other than 0"
+    # QKV projection
+    B, S, nh = 1, 6, 2
+    Wq, bq = g.standard_normal((H, 3 * H)) * 0.5, g.standard_normal(3 * H) * 0.5
+    dQ = g.standard_normal((B * S, 3 * H))
+    gq = T.tp_qkv_shard_bwd(1, 0, B, S, H, nh, X, Wq, dQ)
+    for name, x0, grad, call in (
+            ("dX", X, gq["dX"], lambda z: float((T.tp_qkv_shard_fwd(1, 0, B, S, H, nh, z, Wq, bq) * dQ).sum())),
+            ("dW", Wq, gq["dW"], lambda z: float((T.tp_qkv_shard_fwd(1, 0, B, S, H, nh, X, z, bq) * dQ).sum())),
+            ("db", bq, gq["db"], lambda z: float((T.tp_qkv_shard_fwd(1, 0, B, S, H, nh, X, Wq, z) * dQ).sum()))):
+        vdir = g.standard_normal(x0.shape)
+        want = _fd_dir(call, x0, vdir)
+        got = float((grad * vdir).sum())
+        assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD QKV {name}"
+    # attention, a mild and a sharp case, every component checked through random directions
+    for scale in (1.0, 3.0):
+        B, S, nh, d = 2, 7, 2, 4
+        qkv = g.standard_normal((B * S, 3 * nh * d)) * scale
+        dctx = g.standard_normal((B * S, nh * d))
+        H2 = nh * d
+        grad = T.tp_attn_heads_bwd(1, 0, B, S, H2, nh, qkv, dctx)
+
+        def aloss(z):
+            return float((T.tp_attn_heads_fwd(1, 0, B, S, H2, nh, z)[0] * dctx).sum())
+
+        for part in range(3):          # q, k, v columns separately
+            mask = np.zeros((B * S, nh, 3, d))
+            mask[:, :, part, :] = 1.0
+            vdir = g.standard_normal(qkv.shape) * mask.reshape(qkv.shape)
+            want = _fd_dir(aloss, qkv, vdir)
+            got = float((grad * vdir).sum())
+            assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD attention part {part} x{scale}"
+
+
+def pin_grouped():
+    """Grouped expert shards = the dense MLP shard applied per expert to its rows (no bias on fc2)."""
+    g = _rng(41)
+    G, H, Fr = 4, 8, 6
+    offsets = np.array([0, 3, 3, 10, 12])
+    Xp = g.standard_normal((12, H))
+    W1 = g.standard_normal((G, H, Fr)) * 0.4
+    b1 = g.standard_normal((G, Fr)) * 0.4
+    W2 = g.standard_normal((G, Fr, H)) * 0.4
+    Z = T.tp_mlp_grouped_shard_fwd(8, 0, offsets, Xp, W1, b1, W2)
+    for e in range(G):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            _, _, ref = bf.mlp_forward(Xp[lo:hi], W1[e], b1[e], W2[e], None)
+            _close(Z[lo:hi], ref, 1e-13, f"expert {e}")
+
+
+ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
+            pin_attention_closed_forms, pin_finite_differences, pin_grouped]

@@ -1,0 +1,136 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that some pin catches each one."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.tp_shard as T
+import oracle_pins as P
+
+_erf = T._erf
+
+
+def _softmax_variant(mask_k=0, scale=None, lse_without_max=False, no_mask=False):
+    def f(q, k, d):
+        S = q.shape[0]
+        sc = (q @ k.T) / (scale(d) if scale else math.sqrt(d))
+        if not no_mask:
+            sc = np.where(np.tril(np.ones((S, S), dtype=bool), k=mask_k), sc, -np.inf)
+        m = sc.max(axis=1, keepdims=True)
+        e = np.exp(sc - m)
+        l = e.sum(axis=1, keepdims=True)
+        lse = np.log(l)[:, 0] if lse_without_max else (m + np.log(l))[:, 0]
+        return e / l, lse
+    return f
+
+
+def _heads_blocked(QKV, B, S, n_heads, d):
+    t = np.asarray(QKV).reshape(B, S, 3, n_heads, d)      # [Q_all | K_all | V_all]
+    return tuple(t[:, :, s].transpose(0, 2, 1, 3) for s in range(3))
+
+
+def _gelu_tanh(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _gelu_grad_no_density(x):
+    return 0.5 * (1.0 + _erf(np.asarray(x) / math.sqrt(2.0)))
+
+
+def _shard_range_last_takes_rest(n, t, r):
+    base, rem = divmod(n, t)
+    return r * base, base + (rem if r == t - 1 else 0)
+
+
+def _mlp_fwd_b2_everywhere(tp_size, rank, Tt, H, F, X, W1_r, b1_r, W2_r, b2):
+    return T.mlp_fwd(X, W1_r, b1_r, W2_r, b2)
+
+
+def _mlp_fwd_no_b1(X, W1, b1, W2, b2):
+    A1 = X @ W1
+    Y = T.gelu(A1)
+    Z = Y @ W2 + (b2 if b2 is not None else 0)
+    return {"A1": A1, "Y": Y, "Z": Z}
+
+
+def _attn_bwd_variant(drop_D=False, dK_untransposed=False, dQ_unscaled=False, dV_wrong=False):
+    def f(QKV, dctx, B, S, n_heads, d):
+        q, k, v = T._heads(QKV, B, S, n_heads, d)
+        do = np.asarray(dctx).reshape(B, S, n_heads, d)
+        out = np.zeros((B, S, n_heads, 3, d))
+        for b in range(B):
+            for h in range(n_heads):
+                p, _ = T._softmax_causal(q[b, h], k[b, h], d)
+                dO = do[b, :, h, :]
+                dP = dO @ v[b, h].T
+                dS = p * dP if drop_D else p * (dP - (p * dP).sum(axis=1, keepdims=True))
+                out[b, :, h, 0, :] = dS @ k[b, h] / (1.0 if dQ_unscaled else math.sqrt(d))
+                out[b, :, h, 1, :] = (dS if dK_untransposed else dS.T) @ q[b, h] / math.sqrt(d)
+                out[b, :, h, 2, :] = (p @ dO) if dV_wrong else (p.T @ dO)
+        return out.reshape(B * S, n_heads * 3 * d)
+    return f
+
+
+def _mlp_bwd_variant(gelu_not_grad=False, db1_before_gelu=False, dW2_from_A1=False):
+    def f(X, W1, W2, A1, Y, dZ, with_db2):
+        dY = dZ @ W2.T
+        dA1 = dY * (T.gelu(A1) if gelu_not_grad else T.gelu_grad(A1))
+        return {"dX": dA1 @ W1.T, "dW1": X.T @ dA1,
+                "db1": dY.sum(axis=0) if db1_before_gelu else dA1.sum(axis=0),
+                "dW2": (A1 if dW2_from_A1 else Y).T @ dZ,
+                "db2": dZ.sum(axis=0) if with_db2 else None, "dA1": dA1}
+    return f
+
+
+def _qkv_bwd_db_wrong_axis(X, Wqkv, dQKV):
+    return {"dX": dQKV @ Wqkv.T, "dW": X.T @ dQKV, "db": dQKV.mean(axis=0)}
+
+
+def _grouped_off_by_one(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):
+    Z = np.zeros((X_perm.shape[0], W2_r.shape[2]))
+    for e in range(W1_r.shape[0]):
+        lo, hi = int(group_offsets[e]), int(group_offsets[e + 1])
+        if hi > lo + 1:
+            Z[lo:hi - 1] = T.gelu(X_perm[lo:hi - 1] @ W1_r[e] + b1_r[e]) @ W2_r[e]
+    return Z
+
+
+MUTANTS = {
+    "gelu_tanh_approx": {"gelu": _gelu_tanh},
+    "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
+    "scale_1_over_d": {"_softmax_causal": _softmax_variant(scale=lambda d: d)},
+    "mask_sees_next_key": {"_softmax_causal": _softmax_variant(mask_k=1)},
+    "mask_strict": {"_softmax_causal": _softmax_variant(mask_k=-1)},
+    "no_causal_mask": {"_softmax_causal": _softmax_variant(no_mask=True)},
+    "lse_without_max": {"_softmax_causal": _softmax_variant(lse_without_max=True)},
+    "qkv_blocked_layout": {"_heads": _heads_blocked},
+    "remainder_to_last_rank": {"shard_range": _shard_range_last_takes_rest},
+    "b2_on_every_rank": {"tp_mlp_shard_fwd": _mlp_fwd_b2_everywhere},
+    "fc1_bias_dropped": {"mlp_fwd": _mlp_fwd_no_b1},
+    "attn_bwd_drops_D": {"attention_bwd": _attn_bwd_variant(drop_D=True)},
+    "attn_bwd_dK_untransposed": {"attention_bwd": _attn_bwd_variant(dK_untransposed=True)},
+    "attn_bwd_dQ_unscaled": {"attention_bwd": _attn_bwd_variant(dQ_unscaled=True)},
+    "attn_bwd_dV_untransposed": {"attention_bwd": _attn_bwd_variant(dV_wrong=True)},
+    "mlp_bwd_gelu_for_grad": {"mlp_bwd": _mlp_bwd_variant(gelu_not_grad=True)},
+    "mlp_bwd_db1_before_gelu": {"mlp_bwd": _mlp_bwd_variant(db1_before_gelu=True)},
+    "mlp_bwd_dW2_from_A1": {"mlp_bwd": _mlp_bwd_variant(dW2_from_A1=True)},
+    "qkv_bwd_db_mean": {"qkv_bwd": _qkv_bwd_db_wrong_axis},
+    "grouped_drops_last_row": {"tp_mlp_grouped_shard_fwd": _grouped_off_by_one},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    for attr, fn in MUTANTS[name].items():
+        assert hasattr(T, attr), attr
+        monkeypatch.setattr(T, attr, fn)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in P.ALL_PINS:
+            try:
+                pin()
+            except Exception as e:          # an assertion or a crash both reveal the mistake
+                caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"mutant {name} passed every pin"
