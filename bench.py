@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's shard of a Megatron Transformer layer, on one MI355X.
+
+Workload: the GPT-3 175B layer at tp_size=8, rank 0 — B=1, S=2048, H=12288, 96 heads (12 per rank,
+head_dim 128), ffn 49152 (6144 columns per rank) — bf16 inputs with fp32 accumulation.  One step is
+the whole hot path, forward and backward, through the C ABI of libtpshard.so:
+    tp_qkv_shard_fwd -> tp_attn_heads_fwd -> tp_mlp_shard_fwd ->
+    tp_mlp_shard_bwd -> tp_attn_heads_bwd -> tp_qkv_shard_bwd
+Inputs are synthetic and seeded (X, dZ, dctx ~ N(0, 1); weights and biases ~ N(0, 0.006)) and
+resident in HBM before the timed region.  The metric is algorithmic TFLOP/s of the step (GEMM flops
+2·M·N·K; causal attention 4·d per visible (query, key) pair forward and 8·d backward) and its
+fraction of the bf16 dense MFMA peak, 2516.6 TFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-seq S | --no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seq", type=int, default=2048,
+                    help="tokens of the oracle's CPU sample (the first S of the sequence)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time without the per-kernel events (the roofline object is then null)")
+    return ap.parse_args()
+
+
+def step_flops(T, S, B, H, Nq, nh, d, Fr):
+    gemm_fwd = 2.0 * T * H * Nq + 2.0 * T * H * Fr + 2.0 * T * Fr * H
+    pairs = B * nh * S * (S + 1) / 2.0
+    return {"gemm": 3.0 * gemm_fwd, "attn_fwd": 4.0 * d * pairs, "attn_bwd": 8.0 * d * pairs}
+
+
+def cpu_baseline(wl, rank, seq, min_seconds=10.0, max_reps=4):
+    """The fp64 oracle, as it stands, on the first `seq` tokens of the same shard (same weights)."""
+    import numpy as np
+    import oracle
+    from tensor_transformer_layer_mlp_amd import synth
+    from tensor_transformer_layer_mlp_amd.configs import LayerWorkload
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    sw = LayerWorkload(wl.name + f"_first{seq}", 1, seq, wl.H, wl.n_heads, wl.F, wl.tp_size, (rank,), wl.w_std)
+    h0, nh = oracle.shard_range(wl.n_heads, wl.tp_size, rank)
+    f0, Fr = oracle.shard_range(wl.F, wl.tp_size, rank)
+    d = wl.head_dim
+    c0, c1 = 3 * d * h0, 3 * d * (h0 + nh)
+    dt = "bf16"
+    X = synth.X(sw, dt).f64
+    W = synth.qkv_weight(sw, c0, c1, dt).f64
+    bq = synth.qkv_bias(sw, c0, c1, dt).f64
+    W1 = synth.fc1_weight(sw, f0, f0 + Fr, dt).f64
+    b1 = synth.fc1_bias(sw, f0, f0 + Fr, dt).f64
+    W2 = synth.fc2_weight(sw, f0, f0 + Fr, dt).f64
+    b2 = synth.fc2_bias(sw, dt).f64
+    dZ = synth.upstream(sw, wl.H, dt, "dZ").f64
+    dctx = synth.column_blocks("dctx", sw.T, h0 * d, (h0 + nh) * d, 1.0, dt).f64
+    t, T, H, F = wl.tp_size, sw.T, wl.H, wl.F
+    reps, secs = 0, 0.0
+    while reps < max_reps and (reps == 0 or secs < min_seconds):
+        t0 = time.perf_counter()
+        qkv = oracle.tp_qkv_shard_fwd(t, rank, 1, seq, H, wl.n_heads, X, W, bq)
+        oracle.tp_attn_heads_fwd(t, rank, 1, seq, H, wl.n_heads, qkv)
+        fw = oracle.tp_mlp_shard_fwd(t, rank, T, H, F, X, W1, b1, W2, b2)
+        oracle.tp_mlp_shard_bwd(t, rank, T, H, F, X, W1, W2, fw["A1"], fw["Y"], dZ)
+        dq = oracle.tp_attn_heads_bwd(t, rank, 1, seq, H, wl.n_heads, qkv, dctx)
+        oracle.tp_qkv_shard_bwd(t, rank, 1, seq, H, wl.n_heads, X, W, dq)
+        secs += time.perf_counter() - t0
+        reps += 1
+    fl = step_flops(T, seq, 1, H, c1 - c0, nh, d, Fr)
+    total = sum(fl.values()) * reps
+    return {"value": total / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the fp64 numpy oracle, fwd+bwd of the same rank-0 shard (same shapes and "
+                      f"weights) on {seq} of the 2048 tokens, {reps} pass(es): "
+                      f"{total / 1e9:.1f} GFLOP in {secs:.1f} s",
+            "seconds": round(secs, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the shard of one rank runs on one MI355X, and no "
+              f"collective is part of this build (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_transformer_layer_mlp_amd import binding as bd
+    from tensor_transformer_layer_mlp_amd.configs import GPT3_175B
+
+    wl, rank = GPT3_175B, 0
+    t, B, S, H, nh_all, F = wl.tp_size, wl.B, wl.S, wl.H, wl.n_heads, wl.F
+    T, d = wl.T, wl.head_dim
+    h0, nh = bd.tp_shard_range(nh_all, t, rank)
+    f0, Fr = bd.tp_shard_range(F, t, rank)
+    Nq = 3 * nh * d
+    dev = "cuda"
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+
+    def randn(shape, std):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+
+    X, dZ, dctx = randn((T, H), 1.0), randn((T, H), 1.0), randn((T, nh * d), 1.0)
+    Wq, bq = randn((H, Nq), wl.w_std), randn((Nq,), wl.w_std)
+    W1, b1 = randn((H, Fr), wl.w_std), randn((Fr,), wl.w_std)
+    W2, b2 = randn((Fr, H), wl.w_std), randn((H,), wl.w_std)
+    e = lambda *s, dt=bf: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+    QKV, ctx, lse = e(T, Nq), e(T, nh * d), e(B, nh, S, dt=torch.float32)
+    Z, A1, Y = e(T, H), e(T, Fr), e(T, Fr)
+    dXm, dW1, db1, dW2, db2 = e(T, H), e(H, Fr), e(Fr), e(Fr, H), e(H)
+    dQKV, dXq, dWq, dbq = e(T, Nq), e(T, H), e(H, Nq), e(Nq)
+    ws_m = bd.workspace("tp_mlp_shard_bwd", t, rank, B, S, H, nh_all, F, bf)
+    ws_q = bd.workspace("tp_qkv_shard_bwd", t, rank, B, S, H, nh_all, F, bf)
+    ws_a = bd.workspace("tp_attn_heads_bwd", t, rank, B, S, H, nh_all, F, bf)
+
+    def step():
+        bd.tp_qkv_shard_fwd(t, rank, B, S, H, nh_all, X, Wq, bq, QKV)
+        bd.tp_attn_heads_fwd(t, rank, B, S, H, nh_all, QKV, ctx, lse)
+        bd.tp_mlp_shard_fwd(t, rank, T, H, F, X, W1, b1, W2, b2, Z, A1, Y)
+        bd.tp_mlp_shard_bwd(t, rank, T, H, F, X, W1, W2, A1, Y, dZ, dXm, dW1, db1, dW2, db2, ws_m)
+        bd.tp_attn_heads_bwd(t, rank, B, S, H, nh_all, QKV, ctx, lse, dctx, dQKV, ws_a)
+        bd.tp_qkv_shard_bwd(t, rank, B, S, H, nh_all, X, Wq, dQKV, dXq, dWq, dbq, ws_q)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = not args.no_kernel_events
+    if events:
+        bd.tp_prof_collect()          # drop anything recorded before
+        bd.tp_prof_enable(True)
+    stream = torch.cuda.current_stream()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if events:
+        bd.tp_prof_enable(False)
+        kernels = bd.tp_prof_collect()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    fl = step_flops(T, S, B, H, Nq, nh, d, Fr)
+    flop_step = sum(fl.values())
+    tflops = flop_step / (ms_step * 1e-3) / 1e12
+
+    roofline, breakdown = None, None
+    if events:
+        breakdown = {}
+        for tag, (n, ms, flop, byts) in kernels.items():
+            breakdown[tag] = {"launches_per_step": n / args.steps, "ms_per_step": round(ms / args.steps, 4),
+                              "avg_launch_us": round(1e3 * ms / n, 2),
+                              "tflops": round(flop / (ms * 1e-3) / 1e12, 2) if ms > 0 else None}
+        dom = max(kernels, key=lambda k: kernels[k][1])
+        n, ms, flop, byts = kernels[dom]
+        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)      # flop per byte
+        gemmish = flop / max(byts, 1.0) > ridge
+        avg_s = ms * 1e-3 / n
+        if gemmish:
+            ach = flop / n / avg_s / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "launches_per_step": n / args.steps,
+                        "avg_launch_us": round(avg_s * 1e6, 2), "flop_per_launch": flop / n}
+        else:
+            ach = byts / n / avg_s / 1e9
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                        "launches_per_step": n / args.steps, "avg_launch_us": round(avg_s * 1e6, 2),
+                        "bytes_per_launch": byts / n}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, rank, args.cpu_seq)
+
+    out = {
+        "metric": "TFLOPs/s and % of bf16 MFMA peak per TP-rank layer shard (fwd+bwd)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gpt3_175b_tp8_rank0_layer_shard_fwd_bwd", "B": B, "S": S, "H": H,
+                   "n_heads": nh_all, "head_dim": d, "F": F, "tp_size": t, "rank": rank,
+                   "heads_per_rank": nh, "ffn_cols_per_rank": Fr, "global_batch": B, "seq_len": S,
+                   "parallelism": "tp8, rank 0's shard on one GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "gflop_per_step": round(flop_step / 1e9, 1),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

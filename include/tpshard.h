@@ -1,0 +1,148 @@
+/*
+ * tpshard.h — C ABI of libtpshard.so: one tensor-parallel rank's shard of a Megatron Transformer
+ * layer on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *  - The QKV ColumnParallelLinear split by head, then each rank's heads computed independently
+ *    ("Megatron-LM 深度解读报告", table of §2.2, attention row; "Megatron-LM（英伟达超大模型训练框架）
+ *    完整介绍", §二.2 张量并行).
+ *  - The MLP: fc1 split by columns, fc2 split by rows, no synchronisation between them; the row-split
+ *    output is a partial sum that an all-reduce would complete ("Megatron-LM — 架构与原理", §4 巧妙之处,
+ *    the Column->Row pairing; same table of "Megatron-LM 深度解读报告" §2.2, MLP row).
+ *  - The column split itself, Y = X·W with W = [W1 W2] computed as X·W1 and X·W2 on different devices
+ *    ("Megatron-LM技术演进与大规模模型训练实践", §2.1).
+ *  - Backward: copy is the identity forward and an all-reduce backward, reduce the reverse
+ *    ("Megatron-LM — 架构与原理", §4): every rank receives the full dZ and returns a partial dX.
+ * The pages leave the activation, the attention formula and the bias placement open; this library
+ * takes: exact GeLU x·Φ(x); scores q·k/√d with a causal mask (key j visible to query i iff j <= i)
+ * and a max-subtracted softmax; bqkv and b1 split with their columns; b2 added by rank 0 only.
+ *
+ * Conventions for every entry point:
+ *  - Shard geometry: a rank owns cnt(n,t,r) = floor(n/t) + (r < n mod t) of n heads (or MLP
+ *    columns), starting at off(n,t,r) = r*floor(n/t) + min(r, n mod t).  d = H / n_heads.
+ *  - Layout: row-major, contiguous.  Activations [B, S, ·] flattened to token b*S + s (T = B*S rows).
+ *    Weights [in, out], so Y = X·W.  QKV columns are head-interleaved: column h*3d + s*d + j holds
+ *    part s (0 = q, 1 = k, 2 = v), element j, of local head h.  ctx column h*d + j is head h.
+ *  - Pointers are device pointers (hipMalloc'd or torch CUDA storage), 16-byte aligned.  The caller
+ *    owns every buffer; the library never allocates, frees or keeps a pointer after returning.
+ *  - `dtype`: TP_BF16 (bf16 in/out, fp32 accumulation and fp32 softmax/GeLU) or TP_F32 (fp32
+ *    throughout: the check mode).  Every output has that type except LSE and workspace, fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it; calls return
+ *    without synchronising.  Outputs are overwritten (never accumulated into).
+ *  - Errors: arguments are validated on the host before any launch; a negative tp_status is
+ *    returned and nothing is enqueued.  A failed launch returns TP_EHIP; tp_last_error() then holds
+ *    the HIP message for the calling thread.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Calls are thread-safe; calls that share output buffers on one stream order
+ *    themselves by the stream.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
+
+typedef enum {
+  TP_OK = 0,
+  TP_EINVAL = -1,        /* a size, rank or dtype out of range, or a shape the split does not allow */
+  TP_ENULL = -2,         /* a required pointer is NULL                                             */
+  TP_EALIGN = -3,        /* a pointer is not 16-byte aligned                                       */
+  TP_EUNSUPPORTED = -4,  /* valid request this build does not implement (e.g. head_dim > 128)      */
+  TP_EWORKSPACE = -5,    /* workspace missing or smaller than tp_workspace_bytes() asks            */
+  TP_EHIP = -6           /* a HIP call failed; see tp_last_error()                                 */
+} tp_status;
+
+/* A0 — shard geometry (host only, no device work).  The rank's [offset, offset+count) of n items:
+ * balanced, lower ranks take the remainder (25 heads over 2 ranks: 13 then 12).  Returns TP_EINVAL
+ * for n < 0, tp_size < 1 or rank outside [0, tp_size); TP_ENULL for NULL outputs. */
+int tp_shard_range(int n, int tp_size, int rank, int* offset, int* count);
+
+/* A1 — QKV ColumnParallelLinear of one rank, split by head, output not gathered.
+ *   QKV_r[T, 3*nh_r*d] = X[T, H] · Wqkv_r[H, 3*nh_r*d] + bqkv_r[3*nh_r*d]
+ * Wqkv_r / bqkv_r are the columns [3d*h0, 3d*(h0+nh_r)) of the full head-interleaved weight / bias.
+ * Requires H % n_heads == 0, n_heads >= tp_size; bqkv_r may not be NULL. */
+int tp_qkv_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                     const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r,
+                     void* stream);
+
+/* A2 — causal softmax attention over the rank's nh_r heads, each independent.
+ *   per (b, h): P = softmax_j(Q·Kᵀ/√d, key j visible to query i iff j <= i); ctx = P·V
+ *   ctx_r[T, nh_r*d];  lse_r[B, nh_r, S] (fp32, nullable) = m_i + log Σ_j exp(score_ij - m_i).
+ * Supports d in {16, 32, 64, 96, 128}. */
+int tp_attn_heads_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                      const void* QKV_r, void* ctx_r, float* lse_r, void* stream);
+
+/* A3 + A4 — MLP shard: fc1 column block with the bias and GeLU fused into its epilogue, then the
+ * fc2 row block producing the partial sum Z_r that an all-reduce over ranks would complete.
+ *   A1_r[T, F_r] = X·W1_r + b1_r ;  Y_r = GeLU(A1_r) = A1_r·Φ(A1_r)
+ *   Z_r[T, H]    = Y_r·W2_r  (+ b2 iff rank == 0 and b2 != NULL)
+ * W1_r[H, F_r], b1_r[F_r] are columns [f0, f0+F_r) of W1, b1; W2_r[F_r, H] rows [f0, f0+F_r) of W2.
+ * Y_r is required (fc2 reads it); A1_r is nullable (not stored; the backward needs it). */
+int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype,
+                     const void* X, const void* W1_r, const void* b1_r, const void* W2_r,
+                     const void* b2, void* Z_r, void* A1_r, void* Y_r, void* stream);
+
+/* A5 — MLP shard backward.  dZ[T, H] is the full upstream gradient (reduce's backward is the
+ * identity), the same on every rank.
+ *   dW2_r = Y_rᵀ·dZ ;  db2 = Σ_t dZ (iff rank == 0 and db2 != NULL)
+ *   dA1   = (dZ·W2_rᵀ) ∘ GeLU'(A1_r),  GeLU'(x) = Φ(x) + x·φ(x)
+ *   db1_r = Σ_t dA1 ;  dW1_r = Xᵀ·dA1 ;  dX_r = dA1·W1_rᵀ (a partial: Σ_r dX_r = dX)
+ * workspace: device memory of at least tp_workspace_bytes("tp_mlp_shard_bwd", ...) bytes. */
+int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype,
+                     const void* X, const void* W1_r, const void* W2_r, const void* A1_r,
+                     const void* Y_r, const void* dZ, void* dX_r, void* dW1_r, void* db1_r,
+                     void* dW2_r, void* db2, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* A6 — QKV shard backward: dWqkv_r = Xᵀ·dQKV_r ; dbqkv_r = Σ_t dQKV_r ; dX_r = dQKV_r·Wqkv_rᵀ
+ * (a partial).  workspace: tp_workspace_bytes("tp_qkv_shard_bwd", ...). */
+int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                     const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
+                     void* dWqkv_r, void* dbqkv_r, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* A7 — attention backward over the rank's heads, P recomputed from Q, K and the saved LSE:
+ *   D_i = Σ_c dO_ic·O_ic ; dV = Pᵀ·dO ; dP = dO·Vᵀ ; dS = P∘(dP − D) ; dQ = dS·K/√d ; dK = dSᵀ·Q/√d
+ * ctx_r and lse_r must be this call's forward outputs for QKV_r.  dQKV_r has QKV_r's layout.
+ * workspace: tp_workspace_bytes("tp_attn_heads_bwd", ...). Deterministic (no atomics). */
+int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                      const void* QKV_r, const void* ctx_r, const float* lse_r,
+                      const void* dctx_r, void* dQKV_r, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
+ * "tp_attn_heads_bwd"; 0 for the others).  T = B*S; F is used by the MLP only, n_heads by the
+ * others.  Returns 0 for an unknown name or invalid sizes. */
+size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,
+                          int n_heads, int F, int dtype);
+
+/* Kernel timing for benchmarks.  While enabled, every kernel this library launches is bracketed by
+ * two hipEvents recorded on that launch's own stream and tagged with the kernel's name and the
+ * launch's algorithmic FLOPs and bytes.  Off by default; the cost is two event records per launch. */
+int tp_prof_enable(int enable);
+
+/* Waits for the recorded events, aggregates them per kernel tag (first-seen order) and clears the
+ * record.  Writes up to max_entries rows: tag (NUL-terminated, in names + i*name_len, at most
+ * name_len bytes), launches, total milliseconds, total FLOPs, total bytes.  Returns the number of
+ * distinct tags (possibly more than max_entries), or a negative tp_status. */
+int tp_prof_collect(int max_entries, char* names, int name_len, int* launches, double* total_ms,
+                    double* total_flop, double* total_bytes);
+
+/* Static description of a status code. */
+const char* tp_status_str(int status);
+
+/* Message of the last TP_EHIP (or TP_EUNSUPPORTED detail) on the calling thread; "" if none. */
+const char* tp_last_error(void);
+
+/* Library version string, e.g. "tpshard 0.1 gfx950". */
+const char* tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

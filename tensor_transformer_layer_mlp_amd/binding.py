@@ -1,0 +1,192 @@
+"""ctypes binding of libtpshard.so: the C ABI's entry points under the same names.
+
+Marshalling only.  Each function takes torch CUDA tensors (contiguous, all of one dtype: bfloat16 or
+float32), passes their device pointers and the current torch stream to the library, and raises
+TpError on a negative status.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind.  Outputs and workspaces are caller-allocated tensors.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+
+TP_BF16, TP_F32 = 0, 1
+STATUS = {0: "TP_OK", -1: "TP_EINVAL", -2: "TP_ENULL", -3: "TP_EALIGN", -4: "TP_EUNSUPPORTED",
+          -5: "TP_EWORKSPACE", -6: "TP_EHIP"}
+
+_I, _P, _Z = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_SIGNATURES = {
+    "tp_shard_range": (_I, [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "tp_qkv_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
+    "tp_attn_heads_fwd": (_I, [_I] * 7 + [_P] * 3 + [_P]),
+    "tp_mlp_shard_fwd": (_I, [_I] * 6 + [_P] * 8 + [_P]),
+    "tp_mlp_shard_bwd": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _P]),
+    "tp_qkv_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
+    "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
+    "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
+    "tp_status_str": (ctypes.c_char_p, [_I]),
+    "tp_last_error": (ctypes.c_char_p, []),
+    "tp_version": (ctypes.c_char_p, []),
+    "tp_prof_enable": (_I, [_I]),
+    "tp_prof_collect": (_I, [_I, ctypes.c_char_p, _I, ctypes.POINTER(_I)] + [ctypes.POINTER(ctypes.c_double)] * 3),
+}
+ENTRY_POINTS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class TpError(RuntimeError):
+    def __init__(self, status, fn, detail):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} {detail}")
+
+
+def raw():
+    """The loaded ctypes library (loaded on first use; raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tensor_transformer_layer_mlp_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(rc, fn):
+    if rc != 0:
+        raise TpError(rc, fn, raw().tp_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def tp_shard_range(n, tp_size, rank):
+    off, cnt = _I(), _I()
+    _check(raw().tp_shard_range(n, tp_size, rank, ctypes.byref(off), ctypes.byref(cnt)), "tp_shard_range")
+    return off.value, cnt.value
+
+
+def tp_workspace_bytes(fn, tp_size, rank, B, S, H, n_heads, F, dtype):
+    code = dtype if isinstance(dtype, int) else (TP_BF16 if dtype == torch.bfloat16 else TP_F32)
+    return raw().tp_workspace_bytes(fn.encode(), tp_size, rank, B, S, H, n_heads, F, code)
+
+
+def tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, bqkv_r, QKV_r, stream=None):
+    dt = X.dtype
+    rc = raw().tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, _dtype_code(X), _ptr(X, "X", dt),
+                                _ptr(Wqkv_r, "Wqkv_r", dt), _ptr(bqkv_r, "bqkv_r", dt),
+                                _ptr(QKV_r, "QKV_r", dt), _stream(stream))
+    _check(rc, "tp_qkv_shard_fwd")
+
+
+def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r=None, stream=None):
+    dt = QKV_r.dtype
+    rc = raw().tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, _dtype_code(QKV_r),
+                                 _ptr(QKV_r, "QKV_r", dt), _ptr(ctx_r, "ctx_r", dt),
+                                 _ptr(lse_r, "lse_r", torch.float32, True), _stream(stream))
+    _check(rc, "tp_attn_heads_fwd")
+
+
+def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r, Y_r, stream=None):
+    dt = X.dtype
+    rc = raw().tp_mlp_shard_fwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
+                                _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),
+                                _ptr(W2_r, "W2_r", dt), _ptr(b2, "b2", dt, True),
+                                _ptr(Z_r, "Z_r", dt), _ptr(A1_r, "A1_r", dt, True),
+                                _ptr(Y_r, "Y_r", dt), _stream(stream))
+    _check(rc, "tp_mlp_shard_fwd")
+
+
+def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r, dW1_r, db1_r,
+                     dW2_r, db2, workspace, stream=None):
+    dt = X.dtype
+    rc = raw().tp_mlp_shard_bwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
+                                _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
+                                _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(dZ, "dZ", dt),
+                                _ptr(dX_r, "dX_r", dt), _ptr(dW1_r, "dW1_r", dt),
+                                _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt),
+                                _ptr(db2, "db2", dt, True), _ptr(workspace, "workspace", None, True),
+                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                _stream(stream))
+    _check(rc, "tp_mlp_shard_bwd")
+
+
+def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r,
+                     workspace, stream=None):
+    dt = X.dtype
+    rc = raw().tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, _dtype_code(X), _ptr(X, "X", dt),
+                                _ptr(Wqkv_r, "Wqkv_r", dt), _ptr(dQKV_r, "dQKV_r", dt),
+                                _ptr(dX_r, "dX_r", dt), _ptr(dWqkv_r, "dWqkv_r", dt),
+                                _ptr(dbqkv_r, "dbqkv_r", dt), _ptr(workspace, "workspace", None, True),
+                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                _stream(stream))
+    _check(rc, "tp_qkv_shard_bwd")
+
+
+def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,
+                      workspace, stream=None):
+    dt = QKV_r.dtype
+    rc = raw().tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, _dtype_code(QKV_r),
+                                 _ptr(QKV_r, "QKV_r", dt), _ptr(ctx_r, "ctx_r", dt),
+                                 _ptr(lse_r, "lse_r", torch.float32), _ptr(dctx_r, "dctx_r", dt),
+                                 _ptr(dQKV_r, "dQKV_r", dt), _ptr(workspace, "workspace", None, True),
+                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                 _stream(stream))
+    _check(rc, "tp_attn_heads_bwd")
+
+
+def workspace(fn, tp_size, rank, B, S, H, n_heads, F, dtype, device="cuda"):
+    """A caller-owned workspace tensor of the size the library asks for (None if it needs none)."""
+    n = tp_workspace_bytes(fn, tp_size, rank, B, S, H, n_heads, F, dtype)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def tp_prof_enable(on: bool):
+    _check(raw().tp_prof_enable(1 if on else 0), "tp_prof_enable")
+
+
+def tp_prof_collect(max_entries=64, name_len=128):
+    """Per-kernel-tag totals since the last collection: {tag: (launches, ms, flop, bytes)}."""
+    names = ctypes.create_string_buffer(max_entries * name_len)
+    n_l = (_I * max_entries)()
+    ms, fl, by = ((ctypes.c_double * max_entries)() for _ in range(3))
+    n = raw().tp_prof_collect(max_entries, names, name_len, n_l, ms, fl, by)
+    if n < 0:
+        raise TpError(n, "tp_prof_collect", raw().tp_last_error().decode())
+    out = {}
+    for i in range(min(n, max_entries)):
+        tag = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[tag] = (n_l[i], ms[i], fl[i], by[i])
+    return out

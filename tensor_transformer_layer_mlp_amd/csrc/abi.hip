@@ -1,0 +1,305 @@
+// C ABI of libtpshard: argument validation, shard geometry, and the launch sequence of each entry
+// point.  Every check happens on the host before anything is enqueued.  See include/tpshard.h.
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "tpshard.h"
+#include "kernels.h"
+
+using namespace tp;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return TP_OK;
+  set_err("%s: %s", where, hipGetErrorString(e));
+  return TP_EHIP;
+}
+
+#define TP_TRY(call, where)                          \
+  do {                                               \
+    int st_ = hip_status((call), (where));           \
+    if (st_ != TP_OK) return st_;                    \
+  } while (0)
+
+#define TP_CHECK(cond, code, ...)                    \
+  do {                                               \
+    if (!(cond)) {                                   \
+      set_err(__VA_ARGS__);                          \
+      return (code);                                 \
+    }                                                \
+  } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t esize(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Balanced split, lower ranks take the remainder.
+inline void shard(int n, int t, int r, int* off, int* cnt) {
+  const int base = n / t, rem = n % t;
+  *cnt = base + (r < rem ? 1 : 0);
+  *off = r * base + (r < rem ? r : rem);
+}
+
+int check_rank_dtype(int tp_size, int rank, int dtype) {
+  TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
+  TP_CHECK(tp_size >= 1, TP_EINVAL, "tp_size %d < 1", tp_size);
+  TP_CHECK(rank >= 0 && rank < tp_size, TP_EINVAL, "rank %d outside [0, %d)", rank, tp_size);
+  return TP_OK;
+}
+
+struct HeadGeom {
+  int h0, nh, d, T, Nq;
+};
+
+int head_geom(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype, HeadGeom* g) {
+  int st = check_rank_dtype(tp_size, rank, dtype);
+  if (st) return st;
+  TP_CHECK(B >= 0 && S >= 0, TP_EINVAL, "negative batch %d or sequence %d", B, S);
+  TP_CHECK(H >= 1 && n_heads >= 1, TP_EINVAL, "H %d and n_heads %d must be >= 1", H, n_heads);
+  TP_CHECK(H % n_heads == 0, TP_EINVAL, "H %d is not a multiple of n_heads %d", H, n_heads);
+  TP_CHECK(n_heads >= tp_size, TP_EINVAL, "n_heads %d < tp_size %d leaves a rank without heads", n_heads, tp_size);
+  TP_CHECK((long)B * S <= INT_MAX / 4, TP_EINVAL, "B*S too large");
+  shard(n_heads, tp_size, rank, &g->h0, &g->nh);
+  g->d = H / n_heads;
+  g->T = B * S;
+  g->Nq = 3 * g->nh * g->d;
+  return TP_OK;
+}
+
+struct MlpGeom {
+  int f0, Fr;
+};
+
+int mlp_geom(int tp_size, int rank, int T, int H, int F, int dtype, MlpGeom* g) {
+  int st = check_rank_dtype(tp_size, rank, dtype);
+  if (st) return st;
+  TP_CHECK(T >= 0 && T <= INT_MAX / 4, TP_EINVAL, "T %d out of range", T);
+  TP_CHECK(H >= 1, TP_EINVAL, "H %d < 1", H);
+  TP_CHECK(F >= tp_size, TP_EINVAL, "F %d < tp_size %d leaves a rank without columns", F, tp_size);
+  shard(F, tp_size, rank, &g->f0, &g->Fr);
+  return TP_OK;
+}
+
+// A buffer of n elements: NULL is accepted only when n == 0 (torch gives empty tensors no storage).
+#define NEED(p, name, n)                                                              \
+  do {                                                                                \
+    TP_CHECK((p) != nullptr || (n) == 0, TP_ENULL, "%s is NULL", (name));             \
+    TP_CHECK(aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name));           \
+  } while (0)
+#define MAYBE(p, name)                                                                   \
+  do {                                                                                   \
+    TP_CHECK((p) == nullptr || aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name)); \
+  } while (0)
+
+size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
+  const size_t cs = colsum_ws_bytes(T, Fr) > colsum_ws_bytes(T, H) ? colsum_ws_bytes(T, Fr)
+                                                                   : colsum_ws_bytes(T, H);
+  return align256((size_t)T * Fr * esize(dtype)) + align256(cs);
+}
+
+size_t qkv_bwd_ws(int T, int Nq) { return align256(colsum_ws_bytes(T, Nq)); }
+
+GemmDesc gemm_desc(int dtype, int M, int N, int K, const void* A, long lda, bool a_kmajor,
+                   const void* B, long ldb, bool b_kmajor, void* C, long ldc, int epi) {
+  GemmDesc d;
+  memset(&d, 0, sizeof(d));
+  d.M = M; d.N = N; d.K = K;
+  d.A = A; d.lda = lda; d.a_kmajor = a_kmajor;
+  d.B = B; d.ldb = ldb; d.b_kmajor = b_kmajor;
+  d.C = C; d.ldc = ldc; d.epi = epi; d.dtype = dtype;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_shard_range(int n, int tp_size, int rank, int* offset, int* count) {
+  TP_CHECK(offset != nullptr && count != nullptr, TP_ENULL, "offset/count is NULL");
+  TP_CHECK(n >= 0 && tp_size >= 1 && rank >= 0 && rank < tp_size, TP_EINVAL,
+           "bad shard request n=%d tp_size=%d rank=%d", n, tp_size, rank);
+  shard(n, tp_size, rank, offset, count);
+  return TP_OK;
+}
+
+int tp_qkv_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                     const void* X, const void* Wqkv_r, const void* bqkv_r, void* QKV_r,
+                     void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  const long T = g.T;
+  NEED(X, "X", T * H); NEED(Wqkv_r, "Wqkv_r", 1); NEED(bqkv_r, "bqkv_r", 1);
+  NEED(QKV_r, "QKV_r", T * g.Nq);
+  hipStream_t s = (hipStream_t)stream;
+  GemmDesc d = gemm_desc(dtype, g.T, g.Nq, H, X, H, true, Wqkv_r, g.Nq, false, QKV_r, g.Nq, EPI_BIAS);
+  d.bias = bqkv_r;
+  TP_TRY(launch_gemm(d, s), "qkv gemm");
+  return TP_OK;
+}
+
+int tp_attn_heads_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                      const void* QKV_r, void* ctx_r, float* lse_r, void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  TP_CHECK(attn_supported_dim(g.d), TP_EUNSUPPORTED, "head_dim %d not in {16, 32, 64, 96, 128}", g.d);
+  NEED(QKV_r, "QKV_r", (long)g.T); NEED(ctx_r, "ctx_r", (long)g.T); MAYBE(lse_r, "lse_r");
+  TP_TRY(launch_attn_fwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, (hipStream_t)stream), "attention fwd");
+  return TP_OK;
+}
+
+int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                     const void* W1_r, const void* b1_r, const void* W2_r, const void* b2, void* Z_r,
+                     void* A1_r, void* Y_r, void* stream) {
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, T, H, F, dtype, &g);
+  if (st) return st;
+  NEED(X, "X", (long)T); NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1);
+  NEED(Z_r, "Z_r", (long)T); NEED(Y_r, "Y_r", (long)T); MAYBE(A1_r, "A1_r"); MAYBE(b2, "b2");
+  hipStream_t s = (hipStream_t)stream;
+  GemmDesc fc1 = gemm_desc(dtype, T, g.Fr, H, X, H, true, W1_r, g.Fr, false, Y_r, g.Fr, EPI_BIAS_GELU);
+  fc1.bias = b1_r;
+  fc1.C2 = A1_r;
+  TP_TRY(launch_gemm(fc1, s), "fc1 gemm");
+  const bool add_b2 = (rank == 0 && b2 != nullptr);
+  GemmDesc fc2 = gemm_desc(dtype, T, H, g.Fr, Y_r, g.Fr, true, W2_r, H, false, Z_r, H,
+                           add_b2 ? EPI_BIAS : EPI_STORE);
+  fc2.bias = add_b2 ? b2 : nullptr;
+  TP_TRY(launch_gemm(fc2, s), "fc2 gemm");
+  return TP_OK;
+}
+
+int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
+                     const void* dZ, void* dX_r, void* dW1_r, void* db1_r, void* dW2_r, void* db2,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, T, H, F, dtype, &g);
+  if (st) return st;
+  NEED(X, "X", (long)T); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1); NEED(A1_r, "A1_r", (long)T);
+  NEED(Y_r, "Y_r", (long)T); NEED(dZ, "dZ", (long)T); NEED(dX_r, "dX_r", (long)T);
+  NEED(dW1_r, "dW1_r", 1); NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1); MAYBE(db2, "db2");
+  const size_t need = mlp_bwd_ws(T, H, g.Fr, dtype);
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int Fr = g.Fr;
+  void* dA1 = workspace;
+  float* cs = (float*)((char*)workspace + align256((size_t)T * Fr * esize(dtype)));
+
+  // dW2_r = Y_rᵀ·dZ   (M = F_r, N = H, K = T)
+  GemmDesc g1 = gemm_desc(dtype, Fr, H, T, Y_r, Fr, false, dZ, H, false, dW2_r, H, EPI_STORE);
+  TP_TRY(launch_gemm(g1, s), "dW2 gemm");
+  // dA1 = (dZ·W2_rᵀ) ∘ GeLU'(A1_r)   (M = T, N = F_r, K = H)
+  GemmDesc g2 = gemm_desc(dtype, T, Fr, H, dZ, H, true, W2_r, H, true, dA1, Fr, EPI_DGELU);
+  g2.aux = A1_r;
+  g2.ld_aux = Fr;
+  TP_TRY(launch_gemm(g2, s), "dA1 gemm");
+  TP_TRY(launch_colsum(dtype, dA1, Fr, T, Fr, cs, db1_r, s), "db1 colsum");
+  // dW1_r = Xᵀ·dA1   (M = H, N = F_r, K = T)
+  GemmDesc g3 = gemm_desc(dtype, H, Fr, T, X, H, false, dA1, Fr, false, dW1_r, Fr, EPI_STORE);
+  TP_TRY(launch_gemm(g3, s), "dW1 gemm");
+  // dX_r = dA1·W1_rᵀ   (M = T, N = H, K = F_r)
+  GemmDesc g4 = gemm_desc(dtype, T, H, Fr, dA1, Fr, true, W1_r, Fr, true, dX_r, H, EPI_STORE);
+  TP_TRY(launch_gemm(g4, s), "dX gemm");
+  if (rank == 0 && db2 != nullptr) TP_TRY(launch_colsum(dtype, dZ, H, T, H, cs, db2, s), "db2 colsum");
+  return TP_OK;
+}
+
+int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                     const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
+                     void* dWqkv_r, void* dbqkv_r, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  NEED(X, "X", (long)g.T); NEED(Wqkv_r, "Wqkv_r", 1); NEED(dQKV_r, "dQKV_r", (long)g.T);
+  NEED(dX_r, "dX_r", (long)g.T); NEED(dWqkv_r, "dWqkv_r", 1); NEED(dbqkv_r, "dbqkv_r", 1);
+  const size_t need = qkv_bwd_ws(g.T, g.Nq);
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  // dWqkv_r = Xᵀ·dQKV_r   (M = H, N = Nq, K = T)
+  GemmDesc g1 = gemm_desc(dtype, H, g.Nq, g.T, X, H, false, dQKV_r, g.Nq, false, dWqkv_r, g.Nq, EPI_STORE);
+  TP_TRY(launch_gemm(g1, s), "dWqkv gemm");
+  TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, (float*)workspace, dbqkv_r, s), "dbqkv colsum");
+  // dX_r = dQKV_r·Wqkv_rᵀ   (M = T, N = H, K = Nq)
+  GemmDesc g2 = gemm_desc(dtype, g.T, H, g.Nq, dQKV_r, g.Nq, true, Wqkv_r, g.Nq, true, dX_r, H, EPI_STORE);
+  TP_TRY(launch_gemm(g2, s), "dX gemm");
+  return TP_OK;
+}
+
+int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                      const void* QKV_r, const void* ctx_r, const float* lse_r, const void* dctx_r,
+                      void* dQKV_r, void* workspace, size_t workspace_bytes, void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  TP_CHECK(attn_supported_dim(g.d), TP_EUNSUPPORTED, "head_dim %d not in {16, 32, 64, 96, 128}", g.d);
+  const long T = g.T;
+  NEED(QKV_r, "QKV_r", T); NEED(ctx_r, "ctx_r", T); NEED(lse_r, "lse_r", T);
+  NEED(dctx_r, "dctx_r", T); NEED(dQKV_r, "dQKV_r", T);
+  const size_t need = align256(attn_bwd_ws_bytes(B, S, g.nh, g.d));
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_attn_bwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,
+                         (float*)workspace, (hipStream_t)stream), "attention bwd");
+  return TP_OK;
+}
+
+size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H, int n_heads,
+                          int F, int dtype) {
+  if (fn == nullptr) return 0;
+  if (strcmp(fn, "tp_mlp_shard_bwd") == 0) {
+    MlpGeom g;
+    if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4) return 0;
+    if (mlp_geom(tp_size, rank, B * S, H, F, dtype, &g)) return 0;
+    return mlp_bwd_ws(B * S, H, g.Fr, dtype);
+  }
+  HeadGeom g;
+  if (strcmp(fn, "tp_qkv_shard_bwd") == 0) {
+    if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
+    return qkv_bwd_ws(g.T, g.Nq);
+  }
+  if (strcmp(fn, "tp_attn_heads_bwd") == 0) {
+    if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
+    return align256(attn_bwd_ws_bytes(B, S, g.nh, g.d));
+  }
+  return 0;
+}
+
+const char* tp_status_str(int status) {
+  switch (status) {
+    case TP_OK: return "TP_OK: success";
+    case TP_EINVAL: return "TP_EINVAL: invalid size, rank, dtype or split";
+    case TP_ENULL: return "TP_ENULL: a required pointer is NULL";
+    case TP_EALIGN: return "TP_EALIGN: a pointer is not aligned as required";
+    case TP_EUNSUPPORTED: return "TP_EUNSUPPORTED: valid request not implemented";
+    case TP_EWORKSPACE: return "TP_EWORKSPACE: workspace missing or too small";
+    case TP_EHIP: return "TP_EHIP: a HIP call failed";
+    default: return "unknown tp_status";
+  }
+}
+
+const char* tp_last_error(void) { return g_err; }
+
+const char* tp_version(void) { return "tpshard 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Shared device helpers for the gfx950 kernels of libtpshard.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define TP_LDS __attribute__((address_space(3)))
+
+// ---- element conversion -------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// ---- exact GeLU and its derivative (fp32; erff / expf from the device math library) -------------
+// GeLU(x) = x·Φ(x), Φ(x) = ½(1 + erf(x/√2)); GeLU'(x) = Φ(x) + x·φ(x), φ(x) = exp(−x²/2)/√(2π).
+__device__ __forceinline__ float gelu_f(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) +
+         x * 0.39894228040143268f * expf(-0.5f * x * x);
+}
+
+// ---- matrix-core instructions (CDNA4) ------------------------------------------------------------
+// 16x16x32 bf16: lane l supplies row (l % 16), k = 8*(l / 16) .. +7 of its operand; the result lane l
+// holds D[4*(l / 16) + e][l % 16], e = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x4 fp32: lane l supplies row (l % 16), k = l / 16; same result layout.
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace tp

@@ -1,0 +1,63 @@
+// Kernel selection: the tuned bf16 kernels where the shape allows, the generic ones elsewhere.
+// Each launch is wrapped in a ProfScope carrying its kernel tag and algorithmic work.
+#include <string>
+
+#include "kernels.h"
+#include "prof.h"
+
+namespace tp {
+
+hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t s);
+hipError_t launch_attn_fwd_generic(int dtype, int B, int S, int nh, int d, const void* qkv,
+                                   void* ctx, float* lse, hipStream_t s);
+hipError_t launch_attn_bwd_generic(int dtype, int B, int S, int nh, int d, const void* qkv,
+                                   const void* ctx, const float* lse, const void* dctx, void* dqkv,
+                                   hipStream_t s);
+
+namespace {
+
+const char* tname(int dtype) { return dtype == DT_BF16 ? "__bf16" : "float"; }
+
+double gemm_bytes(const GemmDesc& d) {
+  const double es = d.dtype == DT_BF16 ? 2.0 : 4.0;
+  double outs = 1.0 + (d.epi == EPI_BIAS_GELU && d.C2 ? 1.0 : 0.0) + (d.epi == EPI_DGELU ? 1.0 : 0.0);
+  return es * ((double)d.M * d.K + (double)d.K * d.N + outs * (double)d.M * d.N);
+}
+
+// Visible (query, key) pairs of a causal S x S attention: S(S+1)/2.
+double causal_pairs(int S) { return 0.5 * (double)S * ((double)S + 1.0); }
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
+  std::string tag = std::string("gemm_generic_kernel<") + tname(d.dtype) + ", " + std::to_string(d.epi) + ">";
+  ProfScope p(tag.c_str(), s, 2.0 * d.M * d.N * (double)d.K, gemm_bytes(d));
+  return launch_gemm_generic(d, s);
+}
+
+hipError_t launch_attn_fwd(int dtype, int B, int S, int nh, int d, const void* qkv, void* ctx,
+                           float* lse, hipStream_t s) {
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  std::string tag = std::string("attn_fwd_generic<") + tname(dtype) + ", " + std::to_string(d) + ">";
+  ProfScope p(tag.c_str(), s, 4.0 * B * nh * d * causal_pairs(S),
+              es * (double)B * S * nh * d * 4.0 + 4.0 * B * nh * S);
+  return launch_attn_fwd_generic(dtype, B, S, nh, d, qkv, ctx, lse, s);
+}
+
+size_t attn_bwd_ws_bytes(int B, int S, int nh, int d) {
+  (void)d;
+  return (size_t)B * (size_t)S * (size_t)nh * sizeof(float);   // D_i per (b, h, i)
+}
+
+hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* qkv,
+                           const void* ctx, const float* lse, const void* dctx, void* dqkv,
+                           float* ws, hipStream_t s) {
+  (void)ws;
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  std::string tag = std::string("attn_bwd_generic<") + tname(dtype) + ", " + std::to_string(d) + ">";
+  ProfScope p(tag.c_str(), s, 8.0 * B * nh * d * causal_pairs(S),
+              es * (double)B * S * nh * d * 8.0 + 4.0 * B * nh * S);
+  return launch_attn_bwd_generic(dtype, B, S, nh, d, qkv, ctx, lse, dctx, dqkv, s);
+}
+
+}  // namespace tp

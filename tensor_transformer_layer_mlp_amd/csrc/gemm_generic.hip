@@ -1,0 +1,119 @@
+// Generic MFMA GEMM: any M, N, K, any operand layout, bf16 or fp32, all epilogues.
+//
+// It serves the fp32 check mode, shapes the tiled bf16 kernel does not take (ragged leading
+// dimensions, tiny problems), and is the second opinion the bf16 kernel is tested against.
+// 64x64 output tile, 4 waves in a 2x2 grid, each wave 32x32 = 2x2 MFMA blocks of 16x16.
+// Operands are staged through LDS in a k-contiguous layout with bounds-checked loads (zero fill).
+#include "common.h"
+#include "kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr int GBM = 64, GBN = 64;
+
+template <typename T> struct GenericK;
+template <> struct GenericK<bf16> { static constexpr int BK = 32, PAD = 8; };
+template <> struct GenericK<float> { static constexpr int BK = 16, PAD = 4; };
+
+template <typename T, int EPI>
+__device__ __forceinline__ void store_epi(const GemmDesc& d, int m, int n, float v) {
+  T* C = (T*)d.C;
+  long o = (long)m * d.ldc + n;
+  if constexpr (EPI == EPI_STORE) {
+    C[o] = from_f32<T>(v);
+  } else if constexpr (EPI == EPI_BIAS) {
+    C[o] = from_f32<T>(v + to_f32(((const T*)d.bias)[n]));
+  } else if constexpr (EPI == EPI_BIAS_GELU) {
+    float a = v + to_f32(((const T*)d.bias)[n]);
+    if (d.C2) ((T*)d.C2)[o] = from_f32<T>(a);
+    C[o] = from_f32<T>(gelu_f(a));
+  } else {
+    float a = to_f32(((const T*)d.aux)[(long)m * d.ld_aux + n]);
+    C[o] = from_f32<T>(v * gelu_grad_f(a));
+  }
+}
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d) {
+  constexpr int BK = GenericK<T>::BK, PAD = GenericK<T>::PAD;
+  __shared__ __attribute__((aligned(16))) T As[GBM][BK + PAD];
+  __shared__ __attribute__((aligned(16))) T Bs[GBN][BK + PAD];
+  const T* A = (const T*)d.A;
+  const T* B = (const T*)d.B;
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int r16 = lane & 15, g = lane >> 4;
+  f32x4 acc[2][2];
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < d.K; k0 += BK) {
+    for (int i = tid; i < GBM * BK; i += 256) {
+      int m, k;
+      if (d.a_kmajor) { m = i / BK; k = i % BK; } else { k = i / GBM; m = i % GBM; }
+      const int gm = m0 + m, gk = k0 + k;
+      T v = from_f32<T>(0.f);
+      if (gm < d.M && gk < d.K) v = d.a_kmajor ? A[(long)gm * d.lda + gk] : A[(long)gk * d.lda + gm];
+      As[m][k] = v;
+    }
+    for (int i = tid; i < GBN * BK; i += 256) {
+      int n, k;
+      if (d.b_kmajor) { n = i / BK; k = i % BK; } else { k = i / GBN; n = i % GBN; }
+      const int gn = n0 + n, gk = k0 + k;
+      T v = from_f32<T>(0.f);
+      if (gn < d.N && gk < d.K) v = d.b_kmajor ? B[(long)gn * d.ldb + gk] : B[(long)gk * d.ldb + gn];
+      Bs[n][k] = v;
+    }
+    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 af[2], bfr[2];
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)&As[wm + i * 16 + r16][8 * g];
+      for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)&Bs[wn + j * 16 + r16][8 * g];
+      // operands swapped so that lane l holds C[m = l%16][n = 4*(l/16) + e]
+      for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[j], af[i], acc[i][j]);
+    } else {
+      for (int kk = 0; kk < BK; kk += 4) {
+        float af[2], bfr[2];
+        for (int i = 0; i < 2; ++i) af[i] = As[wm + i * 16 + r16][kk + g];
+        for (int j = 0; j < 2; ++j) bfr[j] = Bs[wn + j * 16 + r16][kk + g];
+        for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x4_f32(bfr[j], af[i], acc[i][j]);
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm + i * 16 + r16;
+        const int n = n0 + wn + j * 16 + 4 * g + e;
+        if (m < d.M && n < d.N) store_epi<T, EPI>(d, m, n, acc[i][j][e]);
+      }
+}
+
+template <typename T>
+hipError_t launch_generic_t(const GemmDesc& d, hipStream_t s) {
+  dim3 grid((d.N + GBN - 1) / GBN, (d.M + GBM - 1) / GBM);
+  switch (d.epi) {
+    case EPI_STORE: gemm_generic_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d); break;
+    case EPI_BIAS: gemm_generic_kernel<T, EPI_BIAS><<<grid, 256, 0, s>>>(d); break;
+    case EPI_BIAS_GELU: gemm_generic_kernel<T, EPI_BIAS_GELU><<<grid, 256, 0, s>>>(d); break;
+    case EPI_DGELU: gemm_generic_kernel<T, EPI_DGELU><<<grid, 256, 0, s>>>(d); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t s) {
+  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  if ((d.N + GBN - 1) / GBN > 0x7fffffff || (d.M + GBM - 1) / GBM > 65535) return hipErrorInvalidValue;
+  return d.dtype == DT_BF16 ? launch_generic_t<bf16>(d, s) : launch_generic_t<float>(d, s);
+}
+
+}  // namespace tp

@@ -1,0 +1,50 @@
+// Internal host-side launch interface of libtpshard (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace tp {
+
+enum Dtype { DT_BF16 = 0, DT_F32 = 1 };
+
+// Epilogues fused into the GEMM's store.
+enum Epi {
+  EPI_STORE = 0,      // C = acc
+  EPI_BIAS = 1,       // C = acc + bias[n]
+  EPI_BIAS_GELU = 2,  // C2 = acc + bias[n] (if C2), C = GeLU(acc + bias[n])
+  EPI_DGELU = 3       // C = acc * GeLU'(aux[m, n])
+};
+
+// C[M, N] = op(A)·op(B) with the epilogue applied.  Element (m, k) of A sits at A[m*lda + k] when
+// a_kmajor, else at A[k*lda + m]; element (k, n) of B at B[n*ldb + k] when b_kmajor, else at
+// B[k*ldb + n].  C, C2 and aux are row-major with leading dimensions ldc / ldc / ld_aux.
+struct GemmDesc {
+  int M, N, K;
+  const void* A; long lda; bool a_kmajor;
+  const void* B; long ldb; bool b_kmajor;
+  void* C; long ldc;
+  int epi;
+  const void* bias;
+  const void* aux; long ld_aux;
+  void* C2;
+  int dtype;
+};
+
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+
+// out[c] = Σ_{r < rows} in[r*ld + c] for c < cols, deterministic (fixed chunked order, fp32).
+size_t colsum_ws_bytes(int rows, int cols);
+hipError_t launch_colsum(int dtype, const void* in, long ld, int rows, int cols, float* ws,
+                         void* out, hipStream_t s);
+
+// Causal attention over nh interleaved heads of width d (see the ABI header for the layout).
+bool attn_supported_dim(int d);
+hipError_t launch_attn_fwd(int dtype, int B, int S, int nh, int d, const void* qkv, void* ctx,
+                           float* lse, hipStream_t s);
+size_t attn_bwd_ws_bytes(int B, int S, int nh, int d);
+hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* qkv,
+                           const void* ctx, const float* lse, const void* dctx, void* dqkv,
+                           float* ws, hipStream_t s);
+
+}  // namespace tp

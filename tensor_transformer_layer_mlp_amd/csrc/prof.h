@@ -1,0 +1,24 @@
+// Optional per-launch timing with HIP events (used by benchmarks; off by default).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace tp {
+
+bool prof_enabled();
+
+// Brackets one kernel launch: records an event on `s` now and another when the scope ends.
+// `tag` names the kernel instantiation; flop/bytes are the launch's algorithmic work.
+class ProfScope {
+ public:
+  ProfScope(const char* tag, hipStream_t s, double flop, double bytes);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  int slot_;
+  hipStream_t s_;
+};
+
+}  // namespace tp

@@ -8,8 +8,9 @@ Every full weight is drawn in fixed blocks, each from its own counter-seeded PCG
 (seed = (1234, crc32(tensor name), block index)).  Any rank's shard is therefore the exact slice of
 one fixed full tensor, whatever tp_size is, and costs only the blocks it covers.
 
-Values are drawn in float64, rounded to float32 (round-to-nearest-even), and for bf16 once more to
-bf16 (round-to-nearest-even on the top 16 bits).  `Operand.f64` is the exact value the device sees.
+Values are standard normals drawn in float32 (numpy's ziggurat), scaled by the tensor's standard
+deviation in float32, and for bf16 rounded once more to bf16 (round-to-nearest-even on the top 16
+bits).  `Operand.f64` is the exact value the device sees.
 """
 
 from dataclasses import dataclass
@@ -28,14 +29,18 @@ def _rng(tag: str, block: int) -> np.random.Generator:
 
 def to_bf16_bits(x) -> np.ndarray:
     """float64/float32 values -> bf16 bit patterns (uint16), round to nearest even (finite inputs)."""
-    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32)
-    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> 16).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    u += r
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
-    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).astype(np.uint32) << 16
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).astype(np.uint32)
+    b <<= np.uint32(16)
     return b.view(np.float32).astype(np.float64)
 
 
@@ -52,57 +57,58 @@ class Operand:
 
 
 def make_operand(values, dtype: str) -> Operand:
-    v = np.asarray(values, dtype=np.float64)
+    """Operand from float32 (or float64) values: fp32 kept as is, bf16 rounded once (RNE)."""
     if dtype == "bf16":
-        bits = to_bf16_bits(v)
+        bits = to_bf16_bits(values)
         return Operand(bits, bf16_bits_to_f64(bits), dtype)
     if dtype == "f32":
-        f = v.astype(np.float32)
+        f = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
         return Operand(f, f.astype(np.float64), dtype)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def _normal32(tag, block, shape, std):
+    v = _rng(tag, block).standard_normal(shape, dtype=np.float32)
+    v *= np.float32(std)
+    return v
+
+
 def normal(tag: str, shape, std: float, dtype: str) -> Operand:
     """A whole tensor from one stream (activations, upstream gradients, small biases)."""
-    v = _rng(tag, 0).standard_normal(shape) * std
-    return make_operand(v, dtype)
+    return make_operand(_normal32(tag, 0, shape, std), dtype)
 
 
 def column_blocks(tag: str, rows: int, col_lo: int, col_hi: int, std: float, dtype: str,
                   block: int = BLOCK) -> Operand:
     """Columns [col_lo, col_hi) of a [rows, *] tensor drawn in `block`-wide column blocks."""
-    parts = []
+    out = np.empty((rows, max(col_hi - col_lo, 0)), dtype=np.float32)
     for b in range(col_lo // block, (col_hi + block - 1) // block):
-        blk = _rng(tag, b).standard_normal((rows, block)) * std
-        lo = max(col_lo, b * block) - b * block
-        hi = min(col_hi, (b + 1) * block) - b * block
-        parts.append(blk[:, lo:hi])
-    v = np.concatenate(parts, axis=1) if parts else np.zeros((rows, 0))
-    return make_operand(v, dtype)
+        blk = _normal32(tag, b, (rows, block), std)
+        lo, hi = max(col_lo, b * block), min(col_hi, (b + 1) * block)
+        out[:, lo - col_lo:hi - col_lo] = blk[:, lo - b * block:hi - b * block]
+    return make_operand(out, dtype)
 
 
 def row_blocks(tag: str, cols: int, row_lo: int, row_hi: int, std: float, dtype: str,
                block: int = BLOCK) -> Operand:
     """Rows [row_lo, row_hi) of a [*, cols] tensor drawn in `block`-high row blocks."""
-    parts = []
+    out = np.empty((max(row_hi - row_lo, 0), cols), dtype=np.float32)
     for b in range(row_lo // block, (row_hi + block - 1) // block):
-        blk = _rng(tag, b).standard_normal((block, cols)) * std
-        lo = max(row_lo, b * block) - b * block
-        hi = min(row_hi, (b + 1) * block) - b * block
-        parts.append(blk[lo:hi, :])
-    v = np.concatenate(parts, axis=0) if parts else np.zeros((0, cols))
-    return make_operand(v, dtype)
+        blk = _normal32(tag, b, (block, cols), std)
+        lo, hi = max(row_lo, b * block), min(row_hi, (b + 1) * block)
+        out[lo - row_lo:hi - row_lo] = blk[lo - b * block:hi - b * block]
+    return make_operand(out, dtype)
 
 
 def vector_blocks(tag: str, lo: int, hi: int, std: float, dtype: str,
                   block: int = BLOCK) -> Operand:
     """Entries [lo, hi) of a bias vector drawn in `block`-long pieces."""
-    parts = []
+    out = np.empty(max(hi - lo, 0), dtype=np.float32)
     for b in range(lo // block, (hi + block - 1) // block):
-        blk = _rng(tag, b).standard_normal(block) * std
-        parts.append(blk[max(lo, b * block) - b * block: min(hi, (b + 1) * block) - b * block])
-    v = np.concatenate(parts) if parts else np.zeros(0)
-    return make_operand(v, dtype)
+        blk = _normal32(tag, b, block, std)
+        a, z = max(lo, b * block), min(hi, (b + 1) * block)
+        out[a - lo:z - lo] = blk[a - b * block:z - b * block]
+    return make_operand(out, dtype)
 
 
 # ---- the layer's tensors, by name --------------------------------------------------------------

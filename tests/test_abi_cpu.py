@@ -1,0 +1,131 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header declares, validates
+arguments before any device work, and its shard geometry equals the oracle's (no GPU needed:
+every call here is rejected by validation before a launch, or is host-only)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from tensor_transformer_layer_mlp_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tpshard.h")
+P = 0x100000          # a 16-byte aligned fake device address: never dereferenced, validation fails first
+MIS = 0x100008        # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bd.raw()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)", out))
+    for s in syms:
+        assert s in exported, f"{s} declared in tpshard.h but not exported"
+        assert hasattr(lib, s)
+    assert set(bd.ENTRY_POINTS) <= set(syms)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tp_version().decode().startswith("tpshard")
+    for code, name in bd.STATUS.items():
+        assert lib.tp_status_str(code).decode().startswith(name)
+    assert "unknown" in lib.tp_status_str(-99).decode()
+
+
+def test_shard_range_matches_oracle_exactly():
+    for n in range(0, 70):
+        for t in range(1, 12):
+            for r in range(t):
+                assert bd.tp_shard_range(n, t, r) == oracle.shard_range(n, t, r)
+    for n, t in ((25, 2), (96, 8), (49152, 8), (12288, 8), (2048, 8), (6400, 2)):
+        for r in range(t):
+            assert bd.tp_shard_range(n, t, r) == oracle.shard_range(n, t, r)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((5, 0, 0), -1), ((5, 2, 2), -1), ((5, 2, -1), -1), ((-1, 2, 0), -1)])
+def test_shard_range_rejects(lib, args, code):
+    off, cnt = ctypes.c_int(), ctypes.c_int()
+    assert lib.tp_shard_range(*args, ctypes.byref(off), ctypes.byref(cnt)) == code
+    assert lib.tp_shard_range(4, 2, 0, None, ctypes.byref(cnt)) == -2
+
+
+def qkv(lib, tp=2, r=0, B=2, S=32, H=64, nh=4, dt=0, X=P, W=P, b=P, Y=P):
+    return lib.tp_qkv_shard_fwd(tp, r, B, S, H, nh, dt, X, W, b, Y, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tp=0), -1), (dict(r=2), -1), (dict(r=-1), -1), (dict(dt=2), -1), (dict(H=65), -1),
+    (dict(nh=1), -1), (dict(B=-1), -1), (dict(H=0), -1), (dict(X=None), -2), (dict(W=None), -2),
+    (dict(b=None), -2), (dict(Y=None), -2), (dict(X=MIS), -3), (dict(Y=MIS), -3)])
+def test_qkv_fwd_validation(lib, kw, code):
+    assert qkv(lib, **kw) == code
+    assert lib.tp_last_error().decode() != ""
+
+
+def test_attention_validation(lib):
+    f = lib.tp_attn_heads_fwd
+    assert f(2, 0, 2, 32, 80, 4, 0, P, P, None, None) == -4           # d = 20 unsupported
+    assert f(2, 0, 2, 32, 64, 4, 0, None, P, None, None) == -2
+    assert f(2, 0, 2, 32, 64, 4, 0, P, P, MIS, None) == -3
+    b = lib.tp_attn_heads_bwd
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, None, P, P, P, 1 << 20, None) == -2   # lse required
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, None, 0, None) == -5        # workspace
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, 8, None) == -5
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P + 16, 1 << 20, None) == -3  # ws alignment
+
+
+def test_mlp_validation(lib):
+    f = lib.tp_mlp_shard_fwd
+    assert f(2, 0, 64, 64, 1, 0, P, P, P, P, P, P, P, P, None) == -1          # F < tp_size
+    assert f(2, 0, 64, 64, 256, 0, P, P, P, P, P, P, P, None, None) == -2     # Y_r required
+    assert f(2, 0, 64, 64, 256, 0, P, P, P, P, MIS, P, P, P, None) == -3      # b2 misaligned
+    assert f(2, 0, -1, 64, 256, 0, P, P, P, P, P, P, P, P, None) == -1
+    b = lib.tp_mlp_shard_bwd
+    args = [2, 0, 64, 64, 256, 0] + [P] * 11
+    assert b(*args, None, 0, None) == -5
+    args2 = [2, 0, 64, 64, 256, 0] + [P] * 4 + [None] + [P] * 6
+    assert b(*args2, P, 1 << 30, None) == -2                                 # dZ NULL
+
+
+def test_qkv_bwd_validation(lib):
+    b = lib.tp_qkv_shard_bwd
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, None, 0, None) == -5
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, None, P, P, 1 << 20, None) == -2
+    assert b(3, 0, 2, 32, 64, 2, 0, P, P, P, P, P, P, P, 1 << 20, None) == -1   # nh < tp
+
+
+def test_workspace_bytes(lib):
+    T, H, F, t = 64, 64, 256, 2
+    got = bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 0)
+    # dA1 [T, F_r] bf16 plus fp32 column-sum partials (chunks of 64 rows) of the wider of F_r, H
+    dA1 = T * 128 * 2
+    assert got >= dA1 + 1 * max(128, H) * 4
+    assert bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 1) >= T * 128 * 4
+    assert bd.tp_workspace_bytes("tp_qkv_shard_bwd", t, 0, 2, 32, H, 4, F, 0) >= 96 * 4
+    assert bd.tp_workspace_bytes("tp_attn_heads_bwd", t, 0, 2, 32, H, 4, F, 0) >= 2 * 32 * 2 * 4
+    assert bd.tp_workspace_bytes("tp_qkv_shard_fwd", t, 0, 2, 32, H, 4, F, 0) == 0
+    assert bd.tp_workspace_bytes("nope", t, 0, 2, 32, H, 4, F, 0) == 0
+    assert bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 5, 2, 32, H, 4, F, 0) == 0   # bad rank
+    assert lib.tp_workspace_bytes(None, t, 0, 2, 32, H, 4, F, 0) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bd.tp_qkv_shard_fwd(1, 0, 1, 4, 4, 1, x, x, x[0], x)

@@ -1,0 +1,123 @@
+"""GPU parity at the full GPT-shaped shard sizes, in the launch configuration the benchmark times.
+
+The GPU runs each entry point on the whole shard.  The oracle checks sampled outputs: rows of
+row-separable results (QKV, Z, dX), columns of column-separable ones (dW1, db1, dW2, dWqkv), and
+whole heads of the attention.  Each sample is the oracle's own function applied to a row or column
+block of the inputs, which the column and row split identities make exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import Shard, assert_close, host
+from test_gpu_parity import (run_attn_bwd, run_attn_fwd, run_mlp_bwd, run_mlp_fwd, run_qkv_bwd,
+                             run_qkv_fwd)
+from tensor_transformer_layer_mlp_amd import synth
+from tensor_transformer_layer_mlp_amd.configs import GPT2_1P5B, GPT3_175B, GPT_8P3B
+
+pytestmark = pytest.mark.gpu
+
+
+def sample(n, k, seed):
+    g = np.random.default_rng(seed)
+    idx = set([0, n - 1]) | set(g.choice(n, size=min(k, n), replace=False).tolist())
+    return np.array(sorted(idx))
+
+
+def check_shard(wl, rank):
+    dt = "bf16"
+    sh = Shard(wl, rank, dt, qkv_std=1.0)
+    t, B, S, H, nh, F = wl.tp_size, wl.B, wl.S, wl.H, wl.n_heads, wl.F
+    rows = sample(wl.T, 40, 1 + rank)
+    cols_f = sample(sh.Fr, 48, 2 + rank)
+    cols_q = sample(sh.Nq, 48, 3 + rank)
+    X, W, bq = sh.f64("X"), sh.f64("Wqkv"), sh.f64("bqkv")
+
+    qkv = run_qkv_fwd(sh)
+    ref = oracle.tp_qkv_shard_fwd(t, rank, 1, len(rows), H, nh, X[rows], W, bq)
+    assert_close(host(qkv)[rows], ref, dt, "QKV_r rows")
+
+    Z, A1, Y = run_mlp_fwd(sh)
+    r = oracle.tp_mlp_shard_fwd(t, rank, len(rows), H, F, X[rows], sh.f64("W1"), sh.f64("b1"),
+                                sh.f64("W2"), sh.f64("b2"))
+    for got, key in ((Z, "Z"), (A1, "A1"), (Y, "Y")):
+        assert_close(host(got)[rows], r[key], dt, f"{key} rows")
+
+    m = run_mlp_bwd(sh, sh.d_("A1"), sh.d_("Y"))
+    A1h, Yh, dZ = sh.f64("A1"), sh.f64("Y"), sh.f64("dZ")
+    rr = oracle.mlp_bwd(X[rows], sh.f64("W1"), sh.f64("W2"), A1h[rows], Yh[rows], dZ[rows], False)
+    assert_close(host(m["dX"])[rows], rr["dX"], dt, "dX_r rows")
+    rc = oracle.mlp_bwd(X, sh.f64("W1")[:, cols_f], sh.f64("W2")[cols_f], A1h[:, cols_f],
+                        Yh[:, cols_f], dZ, rank == 0)
+    assert_close(host(m["dW1"])[:, cols_f], rc["dW1"], dt, "dW1_r cols")
+    assert_close(host(m["db1"])[cols_f], rc["db1"], dt, "db1_r cols")
+    assert_close(host(m["dW2"])[cols_f], rc["dW2"], dt, "dW2_r rows")
+    if rank == 0:
+        assert_close(m["db2"], rc["db2"], dt, "db2")
+
+    q = run_qkv_bwd(sh, sh.d_("dQKV"))
+    dQ = sh.f64("dQKV")
+    assert_close(host(q["dX"])[rows], dQ[rows] @ W.T, dt, "qkv dX_r rows")
+    rq = oracle.qkv_bwd(X, W[:, cols_q], dQ[:, cols_q])
+    assert_close(host(q["dW"])[:, cols_q], rq["dW"], dt, "dWqkv_r cols")
+    assert_close(q["db"], dQ.sum(axis=0), dt, "dbqkv_r")
+
+    QKV = sh.d_("QKV")
+    ctx, lse = run_attn_fwd(sh, QKV)
+    dqkv = run_attn_bwd(sh, QKV, ctx, lse, sh.d_("dctx"))
+    d = sh.d
+    Qh, dctx = sh.f64("QKV"), sh.f64("dctx")
+    ctx_h, lse_h, dqkv_h = host(ctx), host(lse), host(dqkv)
+    for h in sorted({0, sh.nh - 1}):
+        for b in sorted({0, B - 1}):
+            tok = slice(b * S, (b + 1) * S)
+            qh = Qh[tok, 3 * d * h: 3 * d * (h + 1)]
+            rctx, rlse = oracle.attention_fwd(qh, 1, S, 1, d)
+            assert_close(ctx_h[tok, d * h: d * (h + 1)], rctx, dt, f"ctx head {h} batch {b}")
+            assert_close(lse_h[b, h], rlse[0, 0], dt, f"lse head {h} batch {b}", tol=2e-3)
+            rd = oracle.attention_bwd(qh, dctx[tok, d * h: d * (h + 1)], 1, S, 1, d)
+            assert_close(dqkv_h[tok, 3 * d * h: 3 * d * (h + 1)], rd, dt, f"dQKV head {h} batch {b}")
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_gpt2_1p5b_tp2(rank):
+    check_shard(GPT2_1P5B, rank)
+
+
+def test_gpt3_175b_tp8_rank0():
+    check_shard(GPT3_175B, 0)
+
+
+def test_gpt_8p3b_tp8_all_ranks_sum():
+    """All 8 ranks of the 8.3B layer in sequence on the one GPU: Σ_r Z_r and Σ_r dX_r (fp32 sums)
+    equal the unsharded layer's rows, and each rank passes its own sampled checks."""
+    wl = GPT_8P3B
+    dt = "bf16"
+    rows = sample(wl.T, 32, 9)
+    Zsum = torch.zeros(wl.T, wl.H, dtype=torch.float32, device="cuda")
+    dXsum = torch.zeros_like(Zsum)
+    for r in range(wl.tp_size):
+        sh = Shard(wl, r, dt)
+        Z, A1, Y = run_mlp_fwd(sh)
+        Zsum += Z.float()
+        dXsum += run_mlp_bwd(sh, sh.d_("A1"), sh.d_("Y"))["dX"].float()
+        del sh
+    X = synth.X(wl, dt).f64[rows]
+    W1 = synth.fc1_weight(wl, 0, wl.F, dt).f64
+    b1 = synth.fc1_bias(wl, 0, wl.F, dt).f64
+    W2 = synth.fc2_weight(wl, 0, wl.F, dt).f64
+    b2 = synth.fc2_bias(wl, dt).f64
+    full = oracle.mlp_fwd(X, W1, b1, W2, b2)
+    assert_close(host(Zsum)[rows], full["Z"], dt, "sum_r Z_r rows vs unsharded")
+    A1 = synth.column_blocks("A1", wl.T, 0, wl.F, 1.0, dt).f64[rows]
+    Y = synth.column_blocks("Y", wl.T, 0, wl.F, 1.0, dt).f64[rows]
+    dZ = synth.upstream(wl, wl.H, dt, "dZ").f64[rows]
+    fb = oracle.mlp_bwd(X, W1, W2, A1, Y, dZ, True)
+    assert_close(host(dXsum)[rows], fb["dX"], dt, "sum_r dX_r rows vs unsharded")
+
+
+@pytest.mark.parametrize("rank", [3, 7])
+def test_gpt_8p3b_tp8_rank(rank):
+    check_shard(GPT_8P3B, rank)
