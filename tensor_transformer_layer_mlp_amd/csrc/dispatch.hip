@@ -8,6 +8,9 @@
 namespace tp {
 
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t s);
+bool gemm_bf16_eligible(const GemmDesc& d);
+const char* gemm_bf16_pick(const GemmDesc& d, int* cfg);
+hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s);
 hipError_t launch_attn_fwd_generic(int dtype, int B, int S, int nh, int d, const void* qkv,
                                    void* ctx, float* lse, hipStream_t s);
 hipError_t launch_attn_bwd_generic(int dtype, int B, int S, int nh, int d, const void* qkv,
@@ -29,9 +32,23 @@ double causal_pairs(int S) { return 0.5 * (double)S * ((double)S + 1.0); }
 
 }  // namespace
 
+const char* layout_name(const GemmDesc& d) {
+  return d.a_kmajor ? (d.b_kmajor ? "nt" : "nn") : (d.b_kmajor ? "tt" : "tn");
+}
+
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
+  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  const double flop = 2.0 * d.M * d.N * (double)d.K;
+  if (gemm_bf16_eligible(d)) {
+    int cfg = 0;
+    const char* tile = gemm_bf16_pick(d, &cfg);
+    std::string tag = std::string("gemm_bf16_kernel<") + tile + ", " + layout_name(d) + ", epi" +
+                      std::to_string(d.epi) + ">";
+    ProfScope p(tag.c_str(), s, flop, gemm_bytes(d));
+    return launch_gemm_bf16(d, cfg, s);
+  }
   std::string tag = std::string("gemm_generic_kernel<") + tname(d.dtype) + ", " + std::to_string(d.epi) + ">";
-  ProfScope p(tag.c_str(), s, 2.0 * d.M * d.N * (double)d.K, gemm_bytes(d));
+  ProfScope p(tag.c_str(), s, flop, gemm_bytes(d));
   return launch_gemm_generic(d, s);
 }
 

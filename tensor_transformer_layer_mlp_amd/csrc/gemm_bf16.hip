@@ -1,0 +1,287 @@
+// Tiled bf16 GEMM for gfx950: C = op(A)·op(B) with fp32 accumulation and a fused epilogue.
+//
+// Tile BM x BN x 64 per workgroup, WM x WN waves, each wave (BM/WM) x (BN/WN) built from
+// v_mfma_f32_16x16x32_bf16 blocks.  Operands go global -> LDS directly (buffer_load_dwordx4 ... lds,
+// no register staging) into two LDS stages: the loads of k-tile t+1 are in flight while the MFMAs
+// consume k-tile t.
+//
+// LDS layouts (per operand, per stage):
+//  * K-major operand (row m holds k contiguous: X·W's X, dY·Wᵀ's both operands): BMN rows of 128
+//    bytes; the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so the 16 rows one
+//    ds_read_b128 touches land on distinct banks.
+//  * MN-major operand (row k holds m or n contiguous: the [in, out] weights of the forward, both
+//    operands of the weight gradients): 64 rows of 2*BMN bytes; the 32-byte chunk q of row k sits at
+//    q ^ f(k), f(k) = (k & 3) | ((k >> 3) & 1) << 2.  Fragments are read with ds_read_b64_tr_b16,
+//    which hands lane i of each 16-lane group column i of a 4 x 16 block: two of them give a lane the
+//    8 consecutive k values of one m (or n) that the MFMA operand needs.
+// Out-of-range rows, columns and k (ragged tails) are loaded as zeros: such lanes get a byte offset
+// past the buffer descriptor's range.  Requires M, N, K, the leading dimensions and the base
+// addresses to be multiples of 8 elements / 16 bytes (the host checks).
+//
+// The MFMA is issued with the B fragment as its first operand, so lane l holds
+// C[m = l % 16][n = 4*(l / 16) + e], e = 0..3: four consecutive columns, stored as one 8-byte write.
+#include "common.h"
+#include "kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr int BKT = 64;                 // k per tile
+constexpr unsigned OOB = 0x80000000u;   // byte offset beyond any descriptor range -> loads zero
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int A_BYTES = BM * BKT * 2, B_BYTES = BN * BKT * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int IPW_A = A_BYTES / 1024 / NW, IPW_B = B_BYTES / 1024 / NW;  // loads per wave
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "loads must split evenly");
+  static_assert(BM >= 128 && BN >= 128, "MN-major swizzle needs at least 8 chunks of 32 bytes");
+};
+
+__device__ __forceinline__ int swz_f(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// Byte offset inside an operand's tile of the 16-byte piece lane `lane` of load `j` carries, and the
+// (row, col) of the global matrix it comes from, relative to the tile origin.  For a K-major tile the
+// global piece is (mn = r, k = 8c .. 8c+7); for an MN-major one (k = r, mn = c .. c+7).
+template <bool KMAJ, int BMN>
+__device__ __forceinline__ void piece(int o, int& r, int& c) {
+  if constexpr (KMAJ) {
+    r = o >> 7;
+    const int p = (o >> 4) & 7;
+    c = 8 * (p ^ ((r >> 1) & 7));
+  } else {
+    r = o / (2 * BMN);
+    const int s = (o % (2 * BMN)) >> 4;
+    c = 16 * ((s >> 1) ^ swz_f(r)) + 8 * (s & 1);
+  }
+}
+
+// Fragment of 16 (m or n) x 32 (k): lane l gets mn = mn0 + l % 16, k = kb + 8*(l / 16) .. +7.
+template <bool KMAJ, int BMN>
+__device__ __forceinline__ bf16x8 frag(const TP_LDS char* tile, int mn0, int kb, int lane) {
+  if constexpr (KMAJ) {
+    const int r = mn0 + (lane & 15);
+    const int c = (kb >> 3) + (lane >> 4);
+    return *(const TP_LDS bf16x8*)(tile + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+  } else {
+    const int i = lane & 15;
+    const int mn = mn0 + 4 * (i & 3);
+    const int k1 = kb + 8 * (lane >> 4) + (i >> 2);
+    const int k2 = k1 + 4;
+    const int p1 = ((((mn >> 4) ^ swz_f(k1)) << 4) | (mn & 15)) * 2;
+    const int p2 = ((((mn >> 4) ^ swz_f(k2)) << 4) | (mn & 15)) * 2;
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TP_LDS bf16x4*)(tile + k1 * 2 * BMN + p1));
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TP_LDS bf16x4*)(tile + k2 * 2 * BMN + p2));
+    return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+struct Operand {
+  const bf16* p;
+  long ld;
+  int mn_total;   // extent along m (A) or n (B)
+};
+
+// One operand's loads for one k-tile.
+template <bool KMAJ, int BMN, int IPW>
+__device__ __forceinline__ void load_tile(const Operand& op, int mn0, int k0, int K, TP_LDS char* dst,
+                                          const int (&r)[IPW], const int (&c)[IPW], int wave) {
+  const bf16* base;
+  unsigned span;
+  if constexpr (KMAJ) {
+    base = op.p + (long)mn0 * op.ld + k0;
+    span = (unsigned)(((long)(BMN - 1) * op.ld + BKT) * 2);
+  } else {
+    base = op.p + (long)k0 * op.ld + mn0;
+    span = (unsigned)(((long)(BKT - 1) * op.ld + BMN) * 2);
+  }
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)span, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    bool ok;
+    unsigned off;
+    if constexpr (KMAJ) {
+      ok = (mn0 + r[j] < op.mn_total) && (k0 + c[j] < K);
+      off = (unsigned)(((long)r[j] * op.ld + c[j]) * 2);
+    } else {
+      ok = (k0 + r[j] < K) && (mn0 + c[j] < op.mn_total);
+      off = (unsigned)(((long)r[j] * op.ld + c[j]) * 2);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TP_LDS void*)(dst + (wave * IPW + j) * 1024), 16,
+                                             ok ? off : OOB, 0, 0, 0);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4 v) {
+  // four consecutive columns n .. n+3 of row m (N is a multiple of 8, so all four are in range)
+  const long o = (long)m * d.ldc + n;
+  float a[4] = {v[0], v[1], v[2], v[3]};
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+    const bf16x4 b = *(const bf16x4*)((const bf16*)d.bias + n);
+    for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
+  }
+  if constexpr (EPI == EPI_BIAS_GELU) {
+    if (d.C2) *(bf16x4*)((bf16*)d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    for (int e = 0; e < 4; ++e) a[e] = gelu_f(a[e]);
+  }
+  if constexpr (EPI == EPI_DGELU) {
+    const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
+    for (int e = 0; e < 4; ++e) a[e] *= gelu_grad_f((float)x[e]);
+  }
+  *(bf16x4*)((bf16*)d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+}
+
+template <class Cfg, bool AK, bool BK, int EPI>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD owns a
+  // contiguous run of tiles (shared A rows / B columns stay in that XCD's L2), then walk the tiles
+  // m-fastest inside groups of 8 along m.
+  const int nwg = tiles_m * tiles_n;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int tm = wg % tiles_m, tn = wg / tiles_m;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+
+  const Operand A{(const bf16*)d.A, d.lda, d.M};
+  const Operand B{(const bf16*)d.B, d.ldb, d.N};
+  int ar[Cfg::IPW_A], ac[Cfg::IPW_A], br[Cfg::IPW_B], bc[Cfg::IPW_B];
+#pragma unroll
+  for (int j = 0; j < Cfg::IPW_A; ++j) piece<AK, Cfg::BM>((wave * Cfg::IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
+#pragma unroll
+  for (int j = 0; j < Cfg::IPW_B; ++j) piece<BK, Cfg::BN>((wave * Cfg::IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+
+  const int wm = (wave / Cfg::WN) * Cfg::TM, wn = (wave % Cfg::WN) * Cfg::TN;
+  f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (d.K + BKT - 1) / BKT;
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  if (nk > 0) {
+    load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, 0, d.K, lds, ar, ac, wave);
+    load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, 0, d.K, lds + Cfg::A_BYTES, br, bc, wave);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed in LDS
+    __syncthreads();                   // ... and every wave's; the other stage is free again
+    TP_LDS char* cur = lds + (kt & 1) * Cfg::STAGE;
+    if (kt + 1 < nk) {
+      TP_LDS char* nxt = lds + ((kt + 1) & 1) * Cfg::STAGE;
+      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, (kt + 1) * BKT, d.K, nxt, ar, ac, wave);
+      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, (kt + 1) * BKT, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
+    }
+    const TP_LDS char* at = cur;
+    const TP_LDS char* bt = cur + Cfg::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BKT; kk += 32) {
+      bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i) af[i] = frag<AK, Cfg::BM>(at, wm + 16 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) bfr[j] = frag<BK, Cfg::BN>(bt, wn + 16 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[j], af[i], acc[i][j]);
+    }
+  }
+
+  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i) {
+    const int m = m0 + wm + 16 * i + r16;
+    if (m >= d.M) continue;
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int n = n0 + wn + 16 * j + g4;
+      if (n < d.N) epilogue4<EPI>(d, m, n, acc[i][j]);
+    }
+  }
+}
+
+template <class Cfg, bool AK, bool BK, int EPI>
+hipError_t run(const GemmDesc& d, hipStream_t s) {
+  const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
+  gemm_bf16_kernel<Cfg, AK, BK, EPI><<<tiles_m * tiles_n, Cfg::NT, 0, s>>>(d, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <class Cfg>
+hipError_t run_cfg(const GemmDesc& d, hipStream_t s) {
+  // the layouts and epilogues the shard uses: X·W (A K-major, B MN-major) with bias / bias+GeLU /
+  // none; dY·Wᵀ (both K-major) with GeLU' / none; Xᵀ·dY (both MN-major) with none.
+  if (d.a_kmajor && !d.b_kmajor) {
+    if (d.epi == EPI_BIAS) return run<Cfg, true, false, EPI_BIAS>(d, s);
+    if (d.epi == EPI_BIAS_GELU) return run<Cfg, true, false, EPI_BIAS_GELU>(d, s);
+    if (d.epi == EPI_STORE) return run<Cfg, true, false, EPI_STORE>(d, s);
+  } else if (d.a_kmajor && d.b_kmajor) {
+    if (d.epi == EPI_DGELU) return run<Cfg, true, true, EPI_DGELU>(d, s);
+    if (d.epi == EPI_STORE) return run<Cfg, true, true, EPI_STORE>(d, s);
+  } else if (!d.a_kmajor && !d.b_kmajor) {
+    if (d.epi == EPI_STORE) return run<Cfg, false, false, EPI_STORE>(d, s);
+  }
+  return hipErrorNotSupported;
+}
+
+using T256x256 = Tile<256, 256, 2, 2>;
+using T256x128 = Tile<256, 128, 2, 2>;
+using T128x256 = Tile<128, 256, 2, 2>;
+using T128x128 = Tile<128, 128, 2, 2>;
+
+}  // namespace
+
+// Whether the tiled kernel takes this GEMM (else the generic one runs).
+bool gemm_bf16_eligible(const GemmDesc& d) {
+  if (d.dtype != DT_BF16 || d.M <= 0 || d.N <= 0 || d.K <= 0) return false;
+  if ((d.M | d.N | d.K) & 7) return false;
+  if ((d.lda | d.ldb | d.ldc) & 7) return false;
+  if (d.lda > (1L << 22) || d.ldb > (1L << 22)) return false;
+  if ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) return false;
+  if (d.epi == EPI_BIAS_GELU && d.C2 && (((uintptr_t)d.C2) & 15)) return false;
+  if (d.epi == EPI_DGELU && ((d.ld_aux & 7) || (((uintptr_t)d.aux) & 15))) return false;
+  const bool supported = (d.a_kmajor && !d.b_kmajor && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_GELU || d.epi == EPI_STORE)) ||
+                         (d.a_kmajor && d.b_kmajor && (d.epi == EPI_DGELU || d.epi == EPI_STORE)) ||
+                         (!d.a_kmajor && !d.b_kmajor && d.epi == EPI_STORE);
+  return supported;
+}
+
+// Tile choice: the largest tile whose wave count fills the 256 CUs well.
+const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
+  auto fill = [&](int bm, int bn) {
+    const long t = (long)((d.M + bm - 1) / bm) * ((d.N + bn - 1) / bn);
+    const long waves = (t + 255) / 256;
+    return (double)t / (double)(waves * 256);
+  };
+  const double f0 = fill(256, 256), f1 = fill(256, 128), f2 = fill(128, 256), f3 = fill(128, 128);
+  if (f0 >= 0.85) { *cfg = 0; return "256x256"; }
+  if (f1 >= 0.85 && f1 >= f2) { *cfg = 1; return "256x128"; }
+  if (f2 >= 0.85) { *cfg = 2; return "128x256"; }
+  if (f0 >= f1 && f0 >= f2 && f0 >= f3) { *cfg = 0; return "256x256"; }
+  if (f1 >= f2 && f1 >= f3) { *cfg = 1; return "256x128"; }
+  if (f2 >= f3) { *cfg = 2; return "128x256"; }
+  *cfg = 3;
+  return "128x128";
+}
+
+hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case 0: return run_cfg<T256x256>(d, s);
+    case 1: return run_cfg<T256x128>(d, s);
+    case 2: return run_cfg<T128x256>(d, s);
+    default: return run_cfg<T128x128>(d, s);
+  }
+}
+
+}  // namespace tp

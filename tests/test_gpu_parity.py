@@ -22,7 +22,9 @@ D96 = LayerWorkload("d96_b2_s100_h384_nh4_f776_tp2", 2, 100, 384, 4, 776, 2, (0,
 D128 = LayerWorkload("d128_b1_s130_h256_nh2_f520_tp1", 1, 130, 256, 2, 520, 1, (0,), 0.05)
 D32 = LayerWorkload("d32_b2_s80_h128_nh4_f256_tp4", 2, 80, 128, 4, 256, 4, (0, 3), 0.05)
 TILES = LayerWorkload("tiles_b2_s320_h512_nh8_f2560_tp2", 2, 320, 512, 8, 2560, 2, (1,), 0.03)
-SMALL = [TINY, RAGGED, UNEVEN, D96, D128, D32, TILES]
+# dimensions multiples of 8 but ragged against every tile: M = 264, N = 336, K = 328 / 264
+RAGGED8 = LayerWorkload("ragged8_b3_s88_h320_nh20_f984_tp3", 3, 88, 320, 20, 984, 3, (0, 2), 0.05)
+SMALL = [TINY, RAGGED, UNEVEN, D96, D128, D32, TILES, RAGGED8]
 DTYPES = ["bf16", "f32"]
 
 
@@ -201,7 +203,7 @@ def test_chain(wl, dtype, rank):
 # ---- sharding identity on the GPU ---------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("wl", [TINY, RAGGED, UNEVEN, D32], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [TINY, RAGGED, UNEVEN, D32, RAGGED8], ids=lambda w: w.name)
 def test_sharding_identity(wl, dtype):
     """Run every rank's shard in sequence on the one GPU; the fp32 sum of the partials Z_r and dX_r
     and the concatenation of the column outputs equal the unsharded layer (oracle) and the GPU's
