@@ -1,0 +1,553 @@
+// Causal attention on the matrix cores (bf16 inputs, fp32 scores / softmax / accumulation).
+//
+// Heads are read from the head-interleaved QKV rows (q at h*3d, k at h*3d + d, v at h*3d + 2d), row
+// stride 3*nh*d.  Every MFMA is v_mfma_f32_16x16x32_bf16; its result lane l holds D[4*(l/16) + e]
+// [l % 16].  The kernels choose operand order so that a lane always owns one query (forward, dQ) or
+// one key (dK/dV) of the result, which keeps the softmax row statistics in registers:
+//
+// Forward (one workgroup = 64 queries, two waves of 32): for each 64-key block,
+//   S = K·Qᵀ     lane: query q, keys 4g+e of each 16-key slice      (K from LDS, Q in registers)
+//   online softmax in the exp2 domain: t = s·log2(e)/√d; running max m (two xor-shuffles give the
+//   row max across the 4 lanes of a query) and per-lane partial sums l, merged at the end
+//   Oᵀ += Vᵀ·Pᵀ  P stays in registers as the second operand; the key order of its 8 k-slots
+//                (4g+e and 16+4g+e) is matched by reading V with ds_read_b64_tr_b16.
+//   LSE = (m + log2 l)·ln 2.
+// Backward, deterministic (no atomics):
+//   rowdot  D_i = Σ_c dO_ic·O_ic                                   (fp32 workspace)
+//   dK/dV   one workgroup = 64 keys, waves of 32 keys, loop over the query blocks at or after them:
+//           Sᵀ, P = exp2(t − LSE·log2 e), dPᵀ = (dO·Vᵀ)ᵀ, dS = P∘(dP − D),
+//           dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS  (dO and Q read transposed from LDS)
+//   dQ      one workgroup = 64 queries, waves of 32 queries, loop over the key blocks up to them:
+//           S, dP, dS as above in the query-owned layout, dQᵀ += Kᵀ·dSᵀ (K read transposed).
+// LDS tiles are 64 rows x (d padded to 32, 64 or 128) with the 32-byte chunk q of row r stored at
+// q ^ sw(r), which keeps both the 16-byte row reads and the transposed 4x16 reads spread over the
+// banks.  Tiles arrive by buffer_load_dwordx4 ... lds (two stages, next block in flight); rows past S
+// and columns past d arrive as zeros.
+#include "common.h"
+#include "kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr unsigned OOB = 0x80000000u;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <int D>
+struct AC {
+  static constexpr int DP = D <= 32 ? 32 : (D <= 64 ? 64 : 128);  // d padded to the MFMA k-step
+  static constexpr int PB = 2 * DP;           // LDS row pitch, bytes
+  static constexpr int RS = 256 / PB;         // rows per 256-byte bank window
+  static constexpr int NC32 = PB / 32;        // 32-byte chunks per row
+  static constexpr int TILE = 64 * PB;        // 64-row tile
+  static constexpr int NKK = DP / 32;         // 32-wide k-steps over d
+  static constexpr int NDB = DP / 16;         // 16-wide d blocks of the outputs
+  static constexpr int LOADS = TILE / 1024;   // 1 KiB wave-loads per tile
+};
+
+template <int D>
+__device__ __forceinline__ int sw(int r) { return (r / AC<D>::RS) & (AC<D>::NC32 - 1); }
+
+// Byte address of (row r, element d) in a tile.
+template <int D>
+__device__ __forceinline__ int taddr(int r, int d) {
+  return r * AC<D>::PB + ((((d >> 4) ^ sw<D>(r)) << 5) | ((d & 15) << 1));
+}
+
+// 64 rows starting at `rows` (row stride rs elements), columns [0, D) -> tile; rows >= nvalid and
+// columns >= D are zero.  Two waves share the loads.
+template <int D>
+__device__ __forceinline__ void load_tile(const bf16* rows, long rs, int nvalid, TP_LDS char* dst,
+                                          int wave, int lane) {
+  using C = AC<D>;
+  constexpr int PER = C::LOADS / 2;
+  const unsigned span = (unsigned)((63L * rs + D) * 2);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, (int)span, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int slot = wave * PER + j;
+    const int o = slot * 1024 + 16 * lane;
+    const int row = o / C::PB;
+    const int s16 = (o % C::PB) >> 4;
+    const int d = 16 * ((s16 >> 1) ^ sw<D>(row)) + 8 * (s16 & 1);
+    const bool ok = row < nvalid && d < D;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)(dst + slot * 1024), 16,
+                                             ok ? (unsigned)((row * rs + d) * 2) : OOB, 0, 0, 0);
+  }
+}
+
+// Row fragment: lane l gets row r0 + l%16, elements d0 + 8*(l/16) .. +7 (one 16-byte read).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_row(const TP_LDS char* t, int r0, int d0, int lane) {
+  return *(const TP_LDS bf16x8*)(t + taddr<D>(r0 + (lane & 15), d0 + 8 * (lane >> 4)));
+}
+
+// Transposed fragment: lane l gets column d0 + l%16 at rows r0 + 4g + {0..3} and r0 + 16 + 4g +
+// {0..3} (g = l/16) — the k-slot order of a P (or dS) fragment held in registers.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(const TP_LDS char* t, int r0, int d0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int r1 = r0 + 4 * g + (i >> 2), r2 = r1 + 16;
+  const int d = d0 + 4 * (i & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TP_LDS bf16x4*)(t + taddr<D>(r1, d)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TP_LDS bf16x4*)(t + taddr<D>(r2, d)));
+  return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 16 rows x 32 columns straight from global memory into a fragment (lane: row r0 + l%16, columns
+// d0 + 8*(l/16) .. +7), zero outside [0, nvalid) x [0, D).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_global(const bf16* rows, long rs, int r0, int nvalid, int d0,
+                                              int lane) {
+  const int r = r0 + (lane & 15), d = d0 + 8 * (lane >> 4);
+  if (r < nvalid && d < D) return *(const bf16x8*)(rows + (long)r * rs + d);
+  return (bf16x8){};
+}
+
+__device__ __forceinline__ float xmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float xsum4(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
+  return (bf16x8){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                  (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+
+__device__ __forceinline__ void store4(bf16* p, f32x4 v, float s) {
+  *(bf16x4*)p = (bf16x4){(bf16)(v[0] * s), (bf16)(v[1] * s), (bf16)(v[2] * s), (bf16)(v[3] * s)};
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void attn_fwd_mfma(int B, int S, int nh, int nqb,
+                                                     const bf16* __restrict__ qkv,
+                                                     bf16* __restrict__ ctx, float* __restrict__ lse) {
+  using C = AC<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int nbh = nh * B, idx = blockIdx.x;
+  const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;  // long blocks first
+  const long rs = 3L * nh * D;
+  const bf16* qrows = qkv + (long)b * S * rs + (long)h * 3 * D;
+  const int qw = qb * 64 + 32 * wave;
+  const float c = LOG2E / sqrtf((float)D);
+
+  bf16x8 qf[2][C::NKK];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) qf[qs][kk] = frag_global<D>(qrows, rs, qw + 16 * qs, S, 32 * kk, lane);
+  f32x4 o[2][C::NDB];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[qs][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+  const int nkb = min((S + 63) / 64, qb + 1);
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  load_tile<D>(qrows + D, rs, S, lds, wave, lane);
+  load_tile<D>(qrows + 2 * D, rs, S, lds + C::TILE, wave, lane);
+  for (int j = 0; j < nkb; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < nkb) {
+      TP_LDS char* nx = lds + ((j + 1) & 1) * 2 * C::TILE;
+      load_tile<D>(qrows + (long)(j + 1) * 64 * rs + D, rs, S - (j + 1) * 64, nx, wave, lane);
+      load_tile<D>(qrows + (long)(j + 1) * 64 * rs + 2 * D, rs, S - (j + 1) * 64, nx + C::TILE, wave, lane);
+    }
+    const int k0 = 64 * j;
+    if (k0 > qw + 31) continue;   // every key of this block is in the future of every query here
+    const TP_LDS char* kt = lds + (j & 1) * 2 * C::TILE;
+    const TP_LDS char* vt = kt + C::TILE;
+    f32x4 s[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kf[C::NKK];
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) kf[kk] = frag_row<D>(kt, 16 * kb, 32 * kk, lane);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) a = mfma_16x16x32_bf16(kf[kk], qf[qs][kk], a);
+        s[qs][kb] = a;
+      }
+    }
+    const bool edge = (k0 + 63 > qw) || (k0 + 64 > S);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int q = qw + 16 * qs + i16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float t = s[qs][kb][e] * c;
+          const int key = k0 + 16 * kb + 4 * g + e;
+          if (edge && (key > q || key >= S)) t = -INFINITY;
+          s[qs][kb][e] = t;
+          mx = fmaxf(mx, t);
+        }
+      const float mn = fmaxf(m[qs], xmax4(mx));
+      const float corr = __builtin_amdgcn_exp2f(m[qs] - mn);
+      m[qs] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[qs][kb][e] - mn);
+          s[qs][kb][e] = p;
+          ls += p;
+        }
+      l[qs] = l[qs] * corr + ls;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[qs][db] *= corr;
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) pf[qs] = pack8(s[qs][2 * kc], s[qs][2 * kc + 1]);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 vf = frag_tr<D>(vt, 32 * kc, 16 * db, lane);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) o[qs][db] = mfma_16x16x32_bf16(vf, pf[qs], o[qs][db]);
+      }
+    }
+  }
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const float lt = xsum4(l[qs]);
+    const int q = qw + 16 * qs + i16;
+    if (q < S) {
+      const float inv = 1.0f / lt;
+      bf16* out = ctx + ((long)b * S + q) * nh * D + (long)h * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 16 * db + 4 * g;
+        if (d < D) store4(out + d, o[qs][db], inv);
+      }
+      if (lse && g == 0) lse[((long)b * nh + h) * S + q] = (m[qs] + __log2f(lt)) * LN2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_rowdot(int B, int S, int nh, const bf16* __restrict__ ctx,
+                                                   const bf16* __restrict__ dctx, float* __restrict__ Dws) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)B * S * nh) return;
+  const int h = (int)(id % nh);
+  const long t = id / nh;
+  const bf16* o = ctx + t * nh * D + (long)h * D;
+  const bf16* dO = dctx + t * nh * D + (long)h * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const bf16x8 a = *(const bf16x8*)(o + c), z = *(const bf16x8*)(dO + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)z[e];
+  }
+  const long b = t / S, s = t % S;
+  Dws[(b * nh + h) * S + s] = acc;
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, int nqb,
+                                                         const bf16* __restrict__ qkv,
+                                                         const bf16* __restrict__ dctx,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ Dws,
+                                                         bf16* __restrict__ dqkv) {
+  using C = AC<D>;
+  constexpr int STG = 2 * C::TILE + 512;     // Q tile, dO tile, LSE[64], D[64]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int nbh = nh * B, idx = blockIdx.x;
+  const int kb = idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;   // early keys see most queries
+  const long rs = 3L * nh * D, cs = (long)nh * D;
+  const bf16* rows = qkv + (long)b * S * rs + (long)h * 3 * D;
+  const bf16* dorows = dctx + (long)b * S * cs + (long)h * D;
+  const float* lse_bh = lse + ((long)b * nh + h) * S;
+  const float* D_bh = Dws + ((long)b * nh + h) * S;
+  const int kw = kb * 64 + 32 * wave;
+  const float c = LOG2E / sqrtf((float)D);
+
+  bf16x8 kf[2][C::NKK], vf[2][C::NKK];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      kf[ks][kk] = frag_global<D>(rows + D, rs, kw + 16 * ks, S, 32 * kk, lane);
+      vf[ks][kk] = frag_global<D>(rows + 2 * D, rs, kw + 16 * ks, S, 32 * kk, lane);
+    }
+  f32x4 dk[2][C::NDB], dv[2][C::NDB];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      dk[ks][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dv[ks][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  auto stage = [&](int qb, TP_LDS char* dst) {
+    const int q0 = qb * 64;
+    load_tile<D>(rows + (long)q0 * rs, rs, S - q0, dst, wave, lane);
+    load_tile<D>(dorows + (long)q0 * cs, cs, S - q0, dst + C::TILE, wave, lane);
+    if (threadIdx.x < 64) {
+      const int q = q0 + threadIdx.x;
+      ((TP_LDS float*)(dst + 2 * C::TILE))[threadIdx.x] = q < S ? lse_bh[q] : INFINITY;
+      ((TP_LDS float*)(dst + 2 * C::TILE + 256))[threadIdx.x] = q < S ? D_bh[q] : 0.f;
+    }
+  };
+  const int nq = nqb - kb;
+  stage(kb, lds);
+  for (int j = 0; j < nq; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < nq) stage(kb + j + 1, lds + ((j + 1) & 1) * STG);
+    const int q0 = (kb + j) * 64;
+    if (q0 + 63 < kw) continue;      // every query of this block precedes every key of this wave
+    const TP_LDS char* qt = lds + (j & 1) * STG;
+    const TP_LDS char* dt = qt + C::TILE;
+    const TP_LDS float* Ls = (const TP_LDS float*)(qt + 2 * C::TILE);
+    const TP_LDS float* Ds = Ls + 64;
+    // P and dS for the 64 queries x this wave's 32 keys; lane: key kw + 16ks + i16,
+    // queries q0 + 16qsub + 4g + e
+    f32x4 p[4][2], ds[4][2];
+#pragma unroll
+    for (int qsub = 0; qsub < 4; ++qsub) {
+      bf16x8 qa[C::NKK], da[C::NKK];
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        qa[kk] = frag_row<D>(qt, 16 * qsub, 32 * kk, lane);
+        da[kk] = frag_row<D>(dt, 16 * qsub, 32 * kk, lane);
+      }
+      const f32x4 lq = *(const TP_LDS f32x4*)(Ls + 16 * qsub + 4 * g);
+      const f32x4 dq = *(const TP_LDS f32x4*)(Ds + 16 * qsub + 4 * g);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          sa = mfma_16x16x32_bf16(qa[kk], kf[ks][kk], sa);
+          pa = mfma_16x16x32_bf16(da[kk], vf[ks][kk], pa);
+        }
+        const int key = kw + 16 * ks + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = q0 + 16 * qsub + 4 * g + e;
+          float pv = __builtin_amdgcn_exp2f(sa[e] * c - lq[e] * LOG2E);
+          if (key > q) pv = 0.f;
+          p[qsub][ks][e] = pv;
+          ds[qsub][ks][e] = pv * (pa[e] - dq[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      bf16x8 pf[2], sf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[ks] = pack8(p[2 * qc][ks], p[2 * qc + 1][ks]);
+        sf[ks] = pack8(ds[2 * qc][ks], ds[2 * qc + 1][ks]);
+      }
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 doT = frag_tr<D>(dt, 32 * qc, 16 * db, lane);
+        const bf16x8 qT = frag_tr<D>(qt, 32 * qc, 16 * db, lane);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dv[ks][db] = mfma_16x16x32_bf16(doT, pf[ks], dv[ks][db]);
+          dk[ks][db] = mfma_16x16x32_bf16(qT, sf[ks], dk[ks][db]);
+        }
+      }
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int key = kw + 16 * ks + i16;
+    if (key >= S) continue;
+    bf16* out = dqkv + ((long)b * S + key) * rs + (long)h * 3 * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = 16 * db + 4 * g;
+      if (d < D) {
+        store4(out + D + d, dk[ks][db], scale);
+        store4(out + 2 * D + d, dv[ks][db], 1.0f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void attn_bwd_dq_mfma(int B, int S, int nh, int nqb,
+                                                        const bf16* __restrict__ qkv,
+                                                        const bf16* __restrict__ dctx,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ Dws,
+                                                        bf16* __restrict__ dqkv) {
+  using C = AC<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];   // K and V tiles
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int nbh = nh * B, idx = blockIdx.x;
+  const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;
+  const long rs = 3L * nh * D, cs = (long)nh * D;
+  const bf16* rows = qkv + (long)b * S * rs + (long)h * 3 * D;
+  const bf16* dorows = dctx + (long)b * S * cs + (long)h * D;
+  const int qw = qb * 64 + 32 * wave;
+  const float c = LOG2E / sqrtf((float)D);
+
+  bf16x8 qf[2][C::NKK], df[2][C::NKK];
+  float lq[2], dq_[2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      qf[qs][kk] = frag_global<D>(rows, rs, qw + 16 * qs, S, 32 * kk, lane);
+      df[qs][kk] = frag_global<D>(dorows, cs, qw + 16 * qs, S, 32 * kk, lane);
+    }
+    const int q = qw + 16 * qs + i16;
+    lq[qs] = q < S ? lse[((long)b * nh + h) * S + q] * LOG2E : INFINITY;
+    dq_[qs] = q < S ? Dws[((long)b * nh + h) * S + q] : 0.f;
+  }
+  f32x4 acc[2][C::NDB];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[qs][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nkb = min((S + 63) / 64, qb + 1);
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  load_tile<D>(rows + D, rs, S, lds, wave, lane);
+  load_tile<D>(rows + 2 * D, rs, S, lds + C::TILE, wave, lane);
+  for (int j = 0; j < nkb; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < nkb) {
+      TP_LDS char* nx = lds + ((j + 1) & 1) * 2 * C::TILE;
+      load_tile<D>(rows + (long)(j + 1) * 64 * rs + D, rs, S - (j + 1) * 64, nx, wave, lane);
+      load_tile<D>(rows + (long)(j + 1) * 64 * rs + 2 * D, rs, S - (j + 1) * 64, nx + C::TILE, wave, lane);
+    }
+    const int k0 = 64 * j;
+    if (k0 > qw + 31) continue;
+    const TP_LDS char* kt = lds + (j & 1) * 2 * C::TILE;
+    const TP_LDS char* vt = kt + C::TILE;
+    f32x4 dsv[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kfr[C::NKK], vfr[C::NKK];
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        kfr[kk] = frag_row<D>(kt, 16 * kb, 32 * kk, lane);
+        vfr[kk] = frag_row<D>(vt, 16 * kb, 32 * kk, lane);
+      }
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          sa = mfma_16x16x32_bf16(kfr[kk], qf[qs][kk], sa);
+          pa = mfma_16x16x32_bf16(vfr[kk], df[qs][kk], pa);
+        }
+        const int q = qw + 16 * qs + i16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 16 * kb + 4 * g + e;
+          float pv = __builtin_amdgcn_exp2f(sa[e] * c - lq[qs]);
+          if (key > q || key >= S) pv = 0.f;
+          dsv[qs][kb][e] = pv * (pa[e] - dq_[qs]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 sf[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) sf[qs] = pack8(dsv[qs][2 * kc], dsv[qs][2 * kc + 1]);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 kT = frag_tr<D>(kt, 32 * kc, 16 * db, lane);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) acc[qs][db] = mfma_16x16x32_bf16(kT, sf[qs], acc[qs][db]);
+      }
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int q = qw + 16 * qs + i16;
+    if (q >= S) continue;
+    bf16* out = dqkv + ((long)b * S + q) * rs + (long)h * 3 * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = 16 * db + 4 * g;
+      if (d < D) store4(out + d, acc[qs][db], scale);
+    }
+  }
+}
+
+template <int D>
+hipError_t fwd_t(int B, int S, int nh, const void* qkv, void* ctx, float* lse, hipStream_t s) {
+  const int nqb = (S + 63) / 64;
+  attn_fwd_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_t(int B, int S, int nh, const void* qkv, const void* ctx, const float* lse,
+                 const void* dctx, void* dqkv, float* ws, hipStream_t s) {
+  const int nqb = (S + 63) / 64;
+  const long rows = (long)B * S * nh;
+  attn_rowdot<D><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
+  attn_bwd_dkv_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (const bf16*)dctx,
+                                                    lse, ws, (bf16*)dqkv);
+  attn_bwd_dq_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (const bf16*)dctx,
+                                                   lse, ws, (bf16*)dqkv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_mfma(int B, int S, int nh, int d, const void* qkv, void* ctx, float* lse,
+                                hipStream_t s) {
+  if (B <= 0 || S <= 0 || nh <= 0) return hipSuccess;
+  switch (d) {
+    case 16: return fwd_t<16>(B, S, nh, qkv, ctx, lse, s);
+    case 32: return fwd_t<32>(B, S, nh, qkv, ctx, lse, s);
+    case 64: return fwd_t<64>(B, S, nh, qkv, ctx, lse, s);
+    case 96: return fwd_t<96>(B, S, nh, qkv, ctx, lse, s);
+    case 128: return fwd_t<128>(B, S, nh, qkv, ctx, lse, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_bwd_mfma(int B, int S, int nh, int d, const void* qkv, const void* ctx,
+                                const float* lse, const void* dctx, void* dqkv, float* ws,
+                                hipStream_t s) {
+  if (B <= 0 || S <= 0 || nh <= 0) return hipSuccess;
+  switch (d) {
+    case 16: return bwd_t<16>(B, S, nh, qkv, ctx, lse, dctx, dqkv, ws, s);
+    case 32: return bwd_t<32>(B, S, nh, qkv, ctx, lse, dctx, dqkv, ws, s);
+    case 64: return bwd_t<64>(B, S, nh, qkv, ctx, lse, dctx, dqkv, ws, s);
+    case 96: return bwd_t<96>(B, S, nh, qkv, ctx, lse, dctx, dqkv, ws, s);
+    case 128: return bwd_t<128>(B, S, nh, qkv, ctx, lse, dctx, dqkv, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tp

@@ -16,6 +16,11 @@ hipError_t launch_attn_fwd_generic(int dtype, int B, int S, int nh, int d, const
 hipError_t launch_attn_bwd_generic(int dtype, int B, int S, int nh, int d, const void* qkv,
                                    const void* ctx, const float* lse, const void* dctx, void* dqkv,
                                    hipStream_t s);
+hipError_t launch_attn_fwd_mfma(int B, int S, int nh, int d, const void* qkv, void* ctx, float* lse,
+                                hipStream_t s);
+hipError_t launch_attn_bwd_mfma(int B, int S, int nh, int d, const void* qkv, const void* ctx,
+                                const float* lse, const void* dctx, void* dqkv, float* ws,
+                                hipStream_t s);
 
 namespace {
 
@@ -55,9 +60,15 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
 hipError_t launch_attn_fwd(int dtype, int B, int S, int nh, int d, const void* qkv, void* ctx,
                            float* lse, hipStream_t s) {
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  const double flop = 4.0 * B * nh * d * causal_pairs(S);
+  const double bytes = es * (double)B * S * nh * d * 4.0 + 4.0 * B * nh * S;
+  if (dtype == DT_BF16) {
+    std::string tag = "attn_fwd_mfma<" + std::to_string(d) + ">";
+    ProfScope p(tag.c_str(), s, flop, bytes);
+    return launch_attn_fwd_mfma(B, S, nh, d, qkv, ctx, lse, s);
+  }
   std::string tag = std::string("attn_fwd_generic<") + tname(dtype) + ", " + std::to_string(d) + ">";
-  ProfScope p(tag.c_str(), s, 4.0 * B * nh * d * causal_pairs(S),
-              es * (double)B * S * nh * d * 4.0 + 4.0 * B * nh * S);
+  ProfScope p(tag.c_str(), s, flop, bytes);
   return launch_attn_fwd_generic(dtype, B, S, nh, d, qkv, ctx, lse, s);
 }
 
@@ -69,11 +80,16 @@ size_t attn_bwd_ws_bytes(int B, int S, int nh, int d) {
 hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* qkv,
                            const void* ctx, const float* lse, const void* dctx, void* dqkv,
                            float* ws, hipStream_t s) {
-  (void)ws;
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  const double flop = 8.0 * B * nh * d * causal_pairs(S);
+  const double bytes = es * (double)B * S * nh * d * 8.0 + 4.0 * B * nh * S;
+  if (dtype == DT_BF16) {
+    std::string tag = "attn_bwd_mfma<" + std::to_string(d) + ">";
+    ProfScope p(tag.c_str(), s, flop, bytes);
+    return launch_attn_bwd_mfma(B, S, nh, d, qkv, ctx, lse, dctx, dqkv, ws, s);
+  }
   std::string tag = std::string("attn_bwd_generic<") + tname(dtype) + ", " + std::to_string(d) + ">";
-  ProfScope p(tag.c_str(), s, 8.0 * B * nh * d * causal_pairs(S),
-              es * (double)B * S * nh * d * 8.0 + 4.0 * B * nh * S);
+  ProfScope p(tag.c_str(), s, flop, bytes);
   return launch_attn_bwd_generic(dtype, B, S, nh, d, qkv, ctx, lse, dctx, dqkv, s);
 }
 
