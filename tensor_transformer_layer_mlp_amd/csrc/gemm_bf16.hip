@@ -30,9 +30,9 @@ namespace {
 constexpr int BKT = 64;                 // k per tile
 constexpr unsigned OOB = 0x80000000u;   // byte offset beyond any descriptor range -> loads zero
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int ST_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_;
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
@@ -42,7 +42,15 @@ struct Tile {
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "loads must split evenly");
   static_assert(BM >= 128 && BN >= 128, "MN-major swizzle needs at least 8 chunks of 32 bytes");
+  static_assert(STAGES * STAGE <= 160 * 1024, "LDS holds 160 KiB");
 };
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ int swz_f(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
@@ -139,13 +147,14 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
-__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
+void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD owns a
   // contiguous run of tiles (shared A rows / B columns stay in that XCD's L2), then walk the tiles
-  // m-fastest inside groups of 8 along m.
+  // m-fastest.
   const int nwg = tiles_m * tiles_n;
   int wg = blockIdx.x;
   if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
@@ -169,21 +178,29 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
   const int nk = (d.K + BKT - 1) / BKT;
   TP_LDS char* lds = (TP_LDS char*)smem;
-  if (nk > 0) {
-    load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, 0, d.K, lds, ar, ac, wave);
-    load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, 0, d.K, lds + Cfg::A_BYTES, br, bc, wave);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed in LDS
-    __syncthreads();                   // ... and every wave's; the other stage is free again
-    TP_LDS char* cur = lds + (kt & 1) * Cfg::STAGE;
-    if (kt + 1 < nk) {
-      TP_LDS char* nxt = lds + ((kt + 1) & 1) * Cfg::STAGE;
-      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, (kt + 1) * BKT, d.K, nxt, ar, ac, wave);
-      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, (kt + 1) * BKT, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
+  // prologue: tiles 0 .. STAGES-2 in flight
+#pragma unroll
+  for (int t = 0; t < Cfg::STAGES - 1; ++t)
+    if (t < nk) {
+      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, t * BKT, d.K, lds + t * Cfg::STAGE, ar, ac, wave);
+      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, t * BKT, d.K, lds + t * Cfg::STAGE + Cfg::A_BYTES, br, bc, wave);
     }
-    const TP_LDS char* at = cur;
-    const TP_LDS char* bt = cur + Cfg::A_BYTES;
+  int cur_stage = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most the loads of the STAGES-2 younger tiles are outstanding
+    if (kt + Cfg::STAGES - 2 < nk) wait_vmcnt<(Cfg::STAGES - 2) * (Cfg::IPW_A + Cfg::IPW_B)>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // every wave's part of tile kt is in LDS; the stage loaded next is free
+    if (kt + Cfg::STAGES - 1 < nk) {
+      int ns = cur_stage + Cfg::STAGES - 1;
+      if (ns >= Cfg::STAGES) ns -= Cfg::STAGES;
+      TP_LDS char* nxt = lds + ns * Cfg::STAGE;
+      const int k1 = (kt + Cfg::STAGES - 1) * BKT;
+      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, k1, d.K, nxt, ar, ac, wave);
+      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, k1, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
+    }
+    const TP_LDS char* at = lds + cur_stage * Cfg::STAGE;
+    const TP_LDS char* bt = at + Cfg::A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BKT; kk += 32) {
       bf16x8 af[Cfg::FM], bfr[Cfg::FN];
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[j], af[i], acc[i][j]);
     }
+    if (++cur_stage == Cfg::STAGES) cur_stage = 0;
   }
 
   const int r16 = lane & 15, g4 = 4 * (lane >> 4);
@@ -235,10 +253,17 @@ hipError_t run_cfg(const GemmDesc& d, hipStream_t s) {
   return hipErrorNotSupported;
 }
 
-using T256x256 = Tile<256, 256, 2, 2>;
-using T256x128 = Tile<256, 128, 2, 2>;
-using T128x256 = Tile<128, 256, 2, 2>;
-using T128x128 = Tile<128, 128, 2, 2>;
+// Tile configurations (BM, BN, waves along m, waves along n, LDS stages).  Eight waves = two per
+// SIMD, so one wave's LDS reads overlap the other's MFMAs.
+using C0 = Tile<256, 256, 4, 2, 2>;   // 64x128 per wave
+using C1 = Tile<256, 128, 2, 4, 3>;   // 128x32 per wave
+using C2 = Tile<128, 256, 4, 2, 3>;   // 32x128 per wave
+using C3 = Tile<128, 128, 2, 4, 3>;   // 64x32 per wave
+constexpr int kTileM[] = {256, 256, 128, 128};
+constexpr int kTileN[] = {256, 128, 256, 128};
+// relative throughput per CU of each configuration on large shapes (measured on MI355X)
+constexpr double kTileRate[] = {1.0, 0.82, 0.80, 0.63};
+constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128"};
 
 }  // namespace
 
@@ -257,30 +282,32 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
   return supported;
 }
 
-// Tile choice: the largest tile whose wave count fills the 256 CUs well.
+// Tile choice by a small cost model.  A build may pin one
+// configuration with -DTP_GEMM_FORCE_CFG=<index> (tuning).
 const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
-  auto fill = [&](int bm, int bn) {
-    const long t = (long)((d.M + bm - 1) / bm) * ((d.N + bn - 1) / bn);
-    const long waves = (t + 255) / 256;
-    return (double)t / (double)(waves * 256);
-  };
-  const double f0 = fill(256, 256), f1 = fill(256, 128), f2 = fill(128, 256), f3 = fill(128, 128);
-  if (f0 >= 0.85) { *cfg = 0; return "256x256"; }
-  if (f1 >= 0.85 && f1 >= f2) { *cfg = 1; return "256x128"; }
-  if (f2 >= 0.85) { *cfg = 2; return "128x256"; }
-  if (f0 >= f1 && f0 >= f2 && f0 >= f3) { *cfg = 0; return "256x256"; }
-  if (f1 >= f2 && f1 >= f3) { *cfg = 1; return "256x128"; }
-  if (f2 >= f3) { *cfg = 2; return "128x256"; }
-  *cfg = 3;
-  return "128x128";
+#ifdef TP_GEMM_FORCE_CFG
+  *cfg = TP_GEMM_FORCE_CFG;
+  return kTileName[TP_GEMM_FORCE_CFG];
+#else
+  // modelled time: (number of 256-CU waves of tiles) x (tile area) / (relative rate)
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < 4; ++c) {
+    const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
+    const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
+    if (est < best_t * 0.999) { best_t = est; best = c; }
+  }
+  *cfg = best;
+  return kTileName[best];
+#endif
 }
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
   switch (cfg) {
-    case 0: return run_cfg<T256x256>(d, s);
-    case 1: return run_cfg<T256x128>(d, s);
-    case 2: return run_cfg<T128x256>(d, s);
-    default: return run_cfg<T128x128>(d, s);
+    case 0: return run_cfg<C0>(d, s);
+    case 1: return run_cfg<C1>(d, s);
+    case 2: return run_cfg<C2>(d, s);
+    default: return run_cfg<C3>(d, s);
   }
 }
 
