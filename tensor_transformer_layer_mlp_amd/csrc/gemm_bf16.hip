@@ -27,16 +27,16 @@ namespace tp {
 
 namespace {
 
-constexpr int BKT = 64;                 // k per tile
 constexpr unsigned OOB = 0x80000000u;   // byte offset beyond any descriptor range -> loads zero
 
-template <int BM_, int BN_, int WM_, int WN_, int ST_ = 2>
+template <int BM_, int BN_, int WM_, int WN_, int ST_ = 2, int BK_ = 64>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, BKT = BK_;
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
   static constexpr int A_BYTES = BM * BKT * 2, B_BYTES = BN * BKT * 2;
+  static_assert(BKT == 32 || BKT == 64, "k per tile is 32 or 64");
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int IPW_A = A_BYTES / 1024 / NW, IPW_B = B_BYTES / 1024 / NW;  // loads per wave
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -54,15 +54,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ int swz_f(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
+// K-major tile rows are 2*BKT bytes; chunk c of row r sits at c ^ ks(r), which spreads the 16 rows a
+// ds_read_b128 touches over all 16 bank groups of a 256-byte window.
+template <int BKT>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (BKT == 64) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
 // Byte offset inside an operand's tile of the 16-byte piece lane `lane` of load `j` carries, and the
 // (row, col) of the global matrix it comes from, relative to the tile origin.  For a K-major tile the
 // global piece is (mn = r, k = 8c .. 8c+7); for an MN-major one (k = r, mn = c .. c+7).
-template <bool KMAJ, int BMN>
+template <bool KMAJ, int BMN, int BKT>
 __device__ __forceinline__ void piece(int o, int& r, int& c) {
   if constexpr (KMAJ) {
-    r = o >> 7;
-    const int p = (o >> 4) & 7;
-    c = 8 * (p ^ ((r >> 1) & 7));
+    r = o / (2 * BKT);
+    const int p = (o >> 4) & (BKT / 8 - 1);
+    c = 8 * (p ^ swz_k<BKT>(r));
   } else {
     r = o / (2 * BMN);
     const int s = (o % (2 * BMN)) >> 4;
@@ -71,12 +79,12 @@ __device__ __forceinline__ void piece(int o, int& r, int& c) {
 }
 
 // Fragment of 16 (m or n) x 32 (k): lane l gets mn = mn0 + l % 16, k = kb + 8*(l / 16) .. +7.
-template <bool KMAJ, int BMN>
+template <bool KMAJ, int BMN, int BKT>
 __device__ __forceinline__ bf16x8 frag(const TP_LDS char* tile, int mn0, int kb, int lane) {
   if constexpr (KMAJ) {
     const int r = mn0 + (lane & 15);
     const int c = (kb >> 3) + (lane >> 4);
-    return *(const TP_LDS bf16x8*)(tile + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+    return *(const TP_LDS bf16x8*)(tile + r * (2 * BKT) + ((c ^ swz_k<BKT>(r)) << 4));
   } else {
     const int i = lane & 15;
     const int mn = mn0 + 4 * (i & 3);
@@ -97,7 +105,7 @@ struct Operand {
 };
 
 // One operand's loads for one k-tile.
-template <bool KMAJ, int BMN, int IPW>
+template <bool KMAJ, int BMN, int IPW, int BKT>
 __device__ __forceinline__ void load_tile(const Operand& op, int mn0, int k0, int K, TP_LDS char* dst,
                                           const int (&r)[IPW], const int (&c)[IPW], int wave) {
   const bf16* base;
@@ -150,24 +158,30 @@ template <class Cfg, bool AK, bool BK, int EPI>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
 void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
 
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD owns a
-  // contiguous run of tiles (shared A rows / B columns stay in that XCD's L2), then walk the tiles
-  // m-fastest.
+  // contiguous run of tiles, then walk that run in groups of GROUP_M tile rows x all tile columns
+  // (column-major inside a group): the tiles an XCD runs at once form a compact block, so both their
+  // A row panels and B column panels are shared in that XCD's L2.
+  constexpr int GROUP_M = 4;
   const int nwg = tiles_m * tiles_n;
   int wg = blockIdx.x;
   if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
-  const int tm = wg % tiles_m, tn = wg / tiles_m;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (wg / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
   const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
 
   const Operand A{(const bf16*)d.A, d.lda, d.M};
   const Operand B{(const bf16*)d.B, d.ldb, d.N};
   int ar[Cfg::IPW_A], ac[Cfg::IPW_A], br[Cfg::IPW_B], bc[Cfg::IPW_B];
 #pragma unroll
-  for (int j = 0; j < Cfg::IPW_A; ++j) piece<AK, Cfg::BM>((wave * Cfg::IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
+  for (int j = 0; j < Cfg::IPW_A; ++j) piece<AK, Cfg::BM, Cfg::BKT>((wave * Cfg::IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
 #pragma unroll
-  for (int j = 0; j < Cfg::IPW_B; ++j) piece<BK, Cfg::BN>((wave * Cfg::IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+  for (int j = 0; j < Cfg::IPW_B; ++j) piece<BK, Cfg::BN, Cfg::BKT>((wave * Cfg::IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
 
   const int wm = (wave / Cfg::WN) * Cfg::TM, wn = (wave % Cfg::WN) * Cfg::TN;
   f32x4 acc[Cfg::FM][Cfg::FN];
@@ -176,14 +190,16 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  constexpr int BKT = Cfg::BKT, NKK = BKT / 32;
+  constexpr bool EARLY = !(AK && BK);
   const int nk = (d.K + BKT - 1) / BKT;
   TP_LDS char* lds = (TP_LDS char*)smem;
   // prologue: tiles 0 .. STAGES-2 in flight
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
     if (t < nk) {
-      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, t * BKT, d.K, lds + t * Cfg::STAGE, ar, ac, wave);
-      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, t * BKT, d.K, lds + t * Cfg::STAGE + Cfg::A_BYTES, br, bc, wave);
+      load_tile<AK, Cfg::BM, Cfg::IPW_A, Cfg::BKT>(A, m0, t * BKT, d.K, lds + t * Cfg::STAGE, ar, ac, wave);
+      load_tile<BK, Cfg::BN, Cfg::IPW_B, Cfg::BKT>(B, n0, t * BKT, d.K, lds + t * Cfg::STAGE + Cfg::A_BYTES, br, bc, wave);
     }
   int cur_stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
@@ -191,27 +207,41 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
     if (kt + Cfg::STAGES - 2 < nk) wait_vmcnt<(Cfg::STAGES - 2) * (Cfg::IPW_A + Cfg::IPW_B)>();
     else wait_vmcnt<0>();
     __syncthreads();   // every wave's part of tile kt is in LDS; the stage loaded next is free
+    const TP_LDS char* at = lds + cur_stage * Cfg::STAGE;
+    const TP_LDS char* bt = at + Cfg::A_BYTES;
+    bf16x8 af[NKK][Cfg::FM], bfr[NKK][Cfg::FN];
+    // With an MN-major operand (transposed LDS reads), reading every fragment of the tile before
+    // issuing the next tile's loads keeps the LDS reads off the critical path after the barrier;
+    // with two K-major operands the plain order is faster (measured).
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int q = 0; q < NKK; ++q) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, Cfg::BM, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, Cfg::BN, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
+      }
+    }
     if (kt + Cfg::STAGES - 1 < nk) {
       int ns = cur_stage + Cfg::STAGES - 1;
       if (ns >= Cfg::STAGES) ns -= Cfg::STAGES;
       TP_LDS char* nxt = lds + ns * Cfg::STAGE;
       const int k1 = (kt + Cfg::STAGES - 1) * BKT;
-      load_tile<AK, Cfg::BM, Cfg::IPW_A>(A, m0, k1, d.K, nxt, ar, ac, wave);
-      load_tile<BK, Cfg::BN, Cfg::IPW_B>(B, n0, k1, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
+      load_tile<AK, Cfg::BM, Cfg::IPW_A, Cfg::BKT>(A, m0, k1, d.K, nxt, ar, ac, wave);
+      load_tile<BK, Cfg::BN, Cfg::IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
     }
-    const TP_LDS char* at = lds + cur_stage * Cfg::STAGE;
-    const TP_LDS char* bt = at + Cfg::A_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BKT; kk += 32) {
-      bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+    for (int q = 0; q < NKK; ++q) {
+      if constexpr (!EARLY) {
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i) af[i] = frag<AK, Cfg::BM>(at, wm + 16 * i, kk, lane);
+        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, Cfg::BM, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) bfr[j] = frag<BK, Cfg::BN>(bt, wn + 16 * j, kk, lane);
+        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, Cfg::BN, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
+      }
 #pragma unroll
       for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[j], af[i], acc[i][j]);
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[q][j], af[q][i], acc[i][j]);
     }
     if (++cur_stage == Cfg::STAGES) cur_stage = 0;
   }
@@ -259,11 +289,15 @@ using C0 = Tile<256, 256, 4, 2, 2>;   // 64x128 per wave
 using C1 = Tile<256, 128, 2, 4, 3>;   // 128x32 per wave
 using C2 = Tile<128, 256, 4, 2, 3>;   // 32x128 per wave
 using C3 = Tile<128, 128, 2, 4, 3>;   // 64x32 per wave
-constexpr int kTileM[] = {256, 256, 128, 128};
-constexpr int kTileN[] = {256, 128, 256, 128};
+using C4 = Tile<256, 256, 4, 2, 3, 32>;
+using C5 = Tile<256, 256, 4, 2, 4, 32>;
+using C6 = Tile<256, 256, 4, 2, 5, 32>;
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.82, 0.80, 0.63};
-constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128"};
+constexpr double kTileRate[] = {1.0, 0.82, 0.80, 0.63, 1.0, 1.0, 1.0};
+constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
+                                     "256x256k32s4", "256x256k32s5"};
 
 }  // namespace
 
@@ -307,7 +341,10 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 0: return run_cfg<C0>(d, s);
     case 1: return run_cfg<C1>(d, s);
     case 2: return run_cfg<C2>(d, s);
-    default: return run_cfg<C3>(d, s);
+    case 3: return run_cfg<C3>(d, s);
+    case 4: return run_cfg<C4>(d, s);
+    case 5: return run_cfg<C5>(d, s);
+    default: return run_cfg<C6>(d, s);
   }
 }
 
