@@ -114,9 +114,26 @@ int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
                       const void* dctx_r, void* dQKV_r, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* A9 — grouped expert MLP shard (MoE experts as grouped GEMMs: "Megatron-LM — 架构与原理", §6, TE
+ * GroupedLinear).  Rows [off[e], off[e+1]) of the expert-sorted token matrix X_perm[rows, H] belong to
+ * expert e (e < n_groups); each goes through expert e's column shard of fc1 with bias and GeLU and
+ * its row shard of fc2:
+ *   A1_r[row] = X_perm[row]·W1_r[e] + b1_r[e] ;  Y_r[row] = GeLU(A1_r[row]) ;  Z_r[row] = Y_r[row]·W2_r[e]
+ * W1_r [n_groups, H, F_r], b1_r [n_groups, F_r], W2_r [n_groups, F_r, H]; F_r = cnt(F_group, t, r).
+ * group_offsets: n_groups+1 ints in device memory (the routing produced them there), expected
+ * non-decreasing from 0; the library clamps each to [previous, rows] before use, so malformed offsets
+ * cannot cause out-of-range accesses.  Rows outside [off[0], off[n_groups]) of Z_r, Y_r, A1_r are
+ * left untouched.  No bias on the experts' fc2 partial.  Y_r required (fc2 reads it), A1_r nullable.
+ * workspace: tp_workspace_bytes("tp_mlp_grouped_shard_fwd", ...) with n_heads = n_groups. */
+int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows,
+                             int H, int F_group, int dtype, const void* X_perm, const void* W1_r,
+                             const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
- * "tp_attn_heads_bwd"; 0 for the others).  T = B*S; F is used by the MLP only, n_heads by the
- * others.  Returns 0 for an unknown name or invalid sizes. */
+ * "tp_attn_heads_bwd", "tp_mlp_grouped_shard_fwd"; 0 for the others).  T = B*S; F is used by the
+ * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
+ * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,
                           int n_heads, int F, int dtype);
 

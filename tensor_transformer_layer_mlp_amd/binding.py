@@ -27,6 +27,7 @@ _SIGNATURES = {
     "tp_mlp_shard_bwd": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _P]),
     "tp_qkv_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
     "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
+    "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -165,6 +166,18 @@ def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx
                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                  _stream(stream))
     _check(rc, "tp_attn_heads_bwd")
+
+
+def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_group, X_perm, W1_r,
+                             b1_r, W2_r, Z_r, A1_r, Y_r, workspace, stream=None):
+    dt = X_perm.dtype
+    rc = raw().tp_mlp_grouped_shard_fwd(
+        tp_size, rank, n_groups, _ptr(group_offsets, "group_offsets", torch.int32), rows, H, F_group,
+        _dtype_code(X_perm), _ptr(X_perm, "X_perm", dt), _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),
+        _ptr(W2_r, "W2_r", dt), _ptr(Z_r, "Z_r", dt), _ptr(A1_r, "A1_r", dt, True), _ptr(Y_r, "Y_r", dt),
+        _ptr(workspace, "workspace", None, True),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
+    _check(rc, "tp_mlp_grouped_shard_fwd")
 
 
 def workspace(fn, tp_size, rank, B, S, H, n_heads, F, dtype, device="cuda"):

@@ -264,6 +264,27 @@ int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
   return TP_OK;
 }
 
+int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows,
+                             int H, int F_group, int dtype, const void* X_perm, const void* W1_r,
+                             const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, rows, H, F_group, dtype, &g);
+  if (st) return st;
+  TP_CHECK(n_groups >= 1 && n_groups <= (1 << 20), TP_EINVAL, "n_groups %d out of range", n_groups);
+  TP_CHECK(group_offsets != nullptr, TP_ENULL, "group_offsets is NULL");
+  TP_CHECK(((uintptr_t)group_offsets & 3u) == 0, TP_EALIGN, "group_offsets is not 4-byte aligned");
+  NEED(X_perm, "X_perm", (long)rows); NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1);
+  NEED(Z_r, "Z_r", (long)rows); NEED(Y_r, "Y_r", (long)rows); MAYBE(A1_r, "A1_r");
+  const size_t need = align256(grouped_ws_bytes(n_groups));
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_mlp_grouped(dtype, n_groups, group_offsets, rows, H, g.Fr, X_perm, W1_r, b1_r, W2_r, Z_r,
+                            A1_r, Y_r, workspace, (hipStream_t)stream), "grouped mlp");
+  return TP_OK;
+}
+
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H, int n_heads,
                           int F, int dtype) {
   if (fn == nullptr) return 0;
@@ -277,6 +298,10 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   if (strcmp(fn, "tp_qkv_shard_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
     return qkv_bwd_ws(g.T, g.Nq);
+  }
+  if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0) {
+    if (n_heads < 1 || n_heads > (1 << 20)) return 0;
+    return align256(grouped_ws_bytes(n_heads));
   }
   if (strcmp(fn, "tp_attn_heads_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;

@@ -154,27 +154,10 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
   *(bf16x4*)((bf16*)d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
 }
 
+// One BM x BN output tile at (m0, n0): the k loop over LDS stages and the fused epilogue.
 template <class Cfg, bool AK, bool BK, int EPI>
-__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
-void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
-
-  // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD owns a
-  // contiguous run of tiles, then walk that run in groups of GROUP_M tile rows x all tile columns
-  // (column-major inside a group): the tiles an XCD runs at once form a compact block, so both their
-  // A row panels and B column panels are shared in that XCD's L2.
-  constexpr int GROUP_M = 4;
-  const int nwg = tiles_m * tiles_n;
-  int wg = blockIdx.x;
-  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
-  const int per_group = GROUP_M * tiles_n;
-  const int first_m = (wg / per_group) * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-
+__device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
+                                          int lane) {
   const Operand A{(const bf16*)d.A, d.lda, d.M};
   const Operand B{(const bf16*)d.B, d.ldb, d.N};
   int ar[Cfg::IPW_A], ac[Cfg::IPW_A], br[Cfg::IPW_B], bc[Cfg::IPW_B];
@@ -193,7 +176,6 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   constexpr int BKT = Cfg::BKT, NKK = BKT / 32;
   constexpr bool EARLY = !(AK && BK);
   const int nk = (d.K + BKT - 1) / BKT;
-  TP_LDS char* lds = (TP_LDS char*)smem;
   // prologue: tiles 0 .. STAGES-2 in flight
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
@@ -260,6 +242,66 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
+void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD owns a
+  // contiguous run of tiles, then walk that run in groups of GROUP_M tile rows x all tile columns
+  // (column-major inside a group): the tiles an XCD runs at once form a compact block, so both their
+  // A row panels and B column panels are shared in that XCD's L2.
+  constexpr int GROUP_M = 4;
+  const int nwg = tiles_m * tiles_n;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (wg / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  gemm_tile<Cfg, AK, BK, EPI>(d, m0, n0, (TP_LDS char*)smem, wave, lane);
+}
+
+// Grouped GEMM: expert e owns rows [off[e], off[e+1]) of A and C and its own B (and bias), at
+// b_stride (bias_stride) elements from expert e-1's.  prefix[e] = Σ_{j<e} ceil(rows_j / BM) (from
+// grouped_plan_kernel) numbers the m-tiles of all experts; blockIdx.x is that m-tile number,
+// blockIdx.y the n-tile.  Workgroups past the last m-tile return at once.
+struct GroupedArgs {
+  GemmDesc d;          // A, B, C, C2, bias, lda, ldb, ldc, N, K, epi; M unused
+  const int* off;      // [groups + 1] row offsets (device)
+  const int* prefix;   // [groups + 1] m-tile prefix (device workspace)
+  int groups;
+  long b_stride, bias_stride;
+};
+
+template <class Cfg, int EPI>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
+void gemm_bf16_grouped_kernel(GroupedArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mt = blockIdx.x;
+  if (mt >= g.prefix[g.groups]) return;
+  int lo = 0, hi = g.groups;           // largest e with prefix[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.prefix[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int row0 = g.off[e] + (mt - g.prefix[e]) * Cfg::BM;
+  GemmDesc d = g.d;
+  d.M = g.off[e + 1] - row0;           // rows of this expert from row0 on (>= 1)
+  d.A = (const bf16*)g.d.A + (long)row0 * g.d.lda;
+  d.B = (const bf16*)g.d.B + (long)e * g.b_stride;
+  d.C = (bf16*)g.d.C + (long)row0 * g.d.ldc;
+  if (g.d.C2) d.C2 = (bf16*)g.d.C2 + (long)row0 * g.d.ldc;
+  if (g.d.bias) d.bias = (const bf16*)g.d.bias + (long)e * g.bias_stride;
+  gemm_tile<Cfg, true, false, EPI>(d, 0, blockIdx.y * Cfg::BN, (TP_LDS char*)smem, wave, lane);
+}
+
+template <class Cfg, bool AK, bool BK, int EPI>
 hipError_t run(const GemmDesc& d, hipStream_t s) {
   const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
   gemm_bf16_kernel<Cfg, AK, BK, EPI><<<tiles_m * tiles_n, Cfg::NT, 0, s>>>(d, tiles_m, tiles_n);
@@ -292,12 +334,13 @@ using C3 = Tile<128, 128, 2, 4, 3>;   // 64x32 per wave
 using C4 = Tile<256, 256, 4, 2, 3, 32>;
 using C5 = Tile<256, 256, 4, 2, 4, 32>;
 using C6 = Tile<256, 256, 4, 2, 5, 32>;
-constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256};
-constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256};
+using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.82, 0.80, 0.63, 1.0, 1.0, 1.0};
+constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0};
 constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
-                                     "256x256k32s4", "256x256k32s5"};
+                                     "256x256k32s4", "256x256k32s5", "256x256w4"};
 
 }  // namespace
 
@@ -344,8 +387,22 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 3: return run_cfg<C3>(d, s);
     case 4: return run_cfg<C4>(d, s);
     case 5: return run_cfg<C5>(d, s);
-    default: return run_cfg<C6>(d, s);
+    case 6: return run_cfg<C6>(d, s);
+    default: return run_cfg<C7>(d, s);
   }
+}
+
+int gemm_bf16_grouped_bm() { return C0::BM; }
+
+hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
+                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+  GroupedArgs g{d, off, prefix, groups, b_stride, bias_stride};
+  dim3 grid(max_mtiles, (d.N + C0::BN - 1) / C0::BN);
+  if (max_mtiles <= 0) return hipSuccess;
+  if (d.epi == EPI_BIAS_GELU) gemm_bf16_grouped_kernel<C0, EPI_BIAS_GELU><<<grid, C0::NT, 0, s>>>(g);
+  else if (d.epi == EPI_STORE) gemm_bf16_grouped_kernel<C0, EPI_STORE><<<grid, C0::NT, 0, s>>>(g);
+  else return hipErrorNotSupported;
+  return hipGetLastError();
 }
 
 }  // namespace tp

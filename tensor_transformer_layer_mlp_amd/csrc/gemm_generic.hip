@@ -36,13 +36,12 @@ __device__ __forceinline__ void store_epi(const GemmDesc& d, int m, int n, float
 }
 
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d) {
+__device__ __forceinline__ void generic_tile(const GemmDesc& d, int m0, int n0) {
   constexpr int BK = GenericK<T>::BK, PAD = GenericK<T>::PAD;
   __shared__ __attribute__((aligned(16))) T As[GBM][BK + PAD];
   __shared__ __attribute__((aligned(16))) T Bs[GBN][BK + PAD];
   const T* A = (const T*)d.A;
   const T* B = (const T*)d.B;
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   const int r16 = lane & 15, g = lane >> 4;
@@ -95,6 +94,36 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d) {
       }
 }
 
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d) {
+  generic_tile<T, EPI>(d, blockIdx.y * GBM, blockIdx.x * GBN);
+}
+
+// Grouped form (see the tiled bf16 kernel): expert e owns rows [off[e], off[e+1]); prefix[] numbers
+// the GBM-row tiles of all experts; blockIdx.y is that tile number, blockIdx.x the n-tile.
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_generic_grouped_kernel(GemmDesc g, const int* off,
+                                                                   const int* prefix, int groups,
+                                                                   long b_stride, long bias_stride) {
+  const int mt = blockIdx.y;
+  if (mt >= prefix[groups]) return;
+  int lo = 0, hi = groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int row0 = off[e] + (mt - prefix[e]) * GBM;
+  GemmDesc d = g;
+  d.M = off[e + 1] - row0;
+  d.A = (const T*)g.A + (long)row0 * g.lda;
+  d.B = (const T*)g.B + (long)e * b_stride;
+  d.C = (T*)g.C + (long)row0 * g.ldc;
+  if (g.C2) d.C2 = (T*)g.C2 + (long)row0 * g.ldc;
+  if (g.bias) d.bias = (const T*)g.bias + (long)e * bias_stride;
+  generic_tile<T, EPI>(d, 0, blockIdx.x * GBN);
+}
+
 template <typename T>
 hipError_t launch_generic_t(const GemmDesc& d, hipStream_t s) {
   dim3 grid((d.N + GBN - 1) / GBN, (d.M + GBM - 1) / GBM);
@@ -108,7 +137,31 @@ hipError_t launch_generic_t(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int* prefix, int groups,
+                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+  dim3 grid((d.N + GBN - 1) / GBN, max_mtiles);
+  if (d.epi == EPI_BIAS_GELU)
+    gemm_generic_grouped_kernel<T, EPI_BIAS_GELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+  else if (d.epi == EPI_STORE)
+    gemm_generic_grouped_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+  else
+    return hipErrorNotSupported;
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_generic_grouped_bm() { return GBM; }
+
+hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
+                                       long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+  if (max_mtiles <= 0 || d.N <= 0) return hipSuccess;
+  if (max_mtiles > 65535) return hipErrorInvalidValue;
+  return d.dtype == DT_BF16
+             ? launch_generic_grouped_t<bf16>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s)
+             : launch_generic_grouped_t<float>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s);
+}
 
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;

@@ -1,0 +1,113 @@
+// Grouped expert MLP shard: each expert's rows of the expert-sorted token matrix go through that
+// expert's fc1 column shard (bias + GeLU fused) and its fc2 row shard.
+//
+// The row offsets live on the device (routing happened there), so the host never sees the group
+// sizes.  A one-workgroup plan kernel sanitises the offsets (clamped to [0, rows], made
+// non-decreasing, so no later access can leave the buffers) and numbers the BM-row tiles of all
+// experts (prefix[e] = Σ_{j<e} ceil(rows_j / BM)); the grouped GEMM kernels launch an upper bound of
+// ceil(rows / BM) + groups m-tiles and find their expert by binary search in prefix[].
+#include <cstring>
+
+#include "common.h"
+#include "kernels.h"
+#include "prof.h"
+
+namespace tp {
+
+hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
+                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
+                                       long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
+int gemm_bf16_grouped_bm();
+int gemm_generic_grouped_bm();
+bool gemm_bf16_eligible(const GemmDesc& d);
+
+namespace {
+
+constexpr int PLAN_CHUNK = 1024;
+
+__global__ __launch_bounds__(256) void grouped_plan_kernel(const int* __restrict__ off_in, int groups,
+                                                           int rows, int bm, int* __restrict__ off_out,
+                                                           int* __restrict__ prefix) {
+  __shared__ int so[PLAN_CHUNK];
+  int prev = 0, p = 0;
+  if (threadIdx.x == 0) {
+    prev = min(max(off_in[0], 0), rows);
+    off_out[0] = prev;
+    prefix[0] = 0;
+  }
+  for (int c0 = 0; c0 < groups; c0 += PLAN_CHUNK) {
+    const int n = min(PLAN_CHUNK, groups - c0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) so[i] = off_in[c0 + 1 + i];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < n; ++i) {
+        const int o = min(max(so[i], prev), rows);
+        off_out[c0 + 1 + i] = o;
+        p += (o - prev + bm - 1) / bm;
+        prefix[c0 + 1 + i] = p;
+        prev = o;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t grouped_ws_bytes(int groups) { return (size_t)2 * (groups + 1) * sizeof(int); }
+
+hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
+                              const void* X, const void* W1, const void* b1, const void* W2, void* Z,
+                              void* A1, void* Y, void* ws, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  int* off_s = (int*)ws;
+  int* prefix = off_s + (groups + 1);
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+
+  GemmDesc fc1;
+  memset(&fc1, 0, sizeof(fc1));
+  fc1.M = rows; fc1.N = Fr; fc1.K = H;
+  fc1.A = X; fc1.lda = H; fc1.a_kmajor = true;
+  fc1.B = W1; fc1.ldb = Fr; fc1.b_kmajor = false;
+  fc1.C = Y; fc1.ldc = Fr; fc1.C2 = A1; fc1.bias = b1; fc1.epi = EPI_BIAS_GELU; fc1.dtype = dtype;
+  GemmDesc fc2 = fc1;
+  fc2.N = H; fc2.K = Fr;
+  fc2.A = Y; fc2.lda = Fr;
+  fc2.B = W2; fc2.ldb = H;
+  fc2.C = Z; fc2.ldc = H; fc2.C2 = nullptr; fc2.bias = nullptr; fc2.epi = EPI_STORE;
+
+  // Each expert's slice is a plain row-major problem with the same leading dimensions, so the tiled
+  // kernel's alignment rules are those of the whole matrices.
+  const bool tiled = gemm_bf16_eligible(fc1) && gemm_bf16_eligible(fc2);
+  const int bm = tiled ? gemm_bf16_grouped_bm() : gemm_generic_grouped_bm();
+  const long maxmt = (long)(rows + bm - 1) / bm + groups;
+  if (maxmt > 0x7fffffffL) return hipErrorInvalidValue;
+  {
+    ProfScope p("grouped_plan", s, 0.0, 8.0 * (groups + 1));
+    grouped_plan_kernel<<<1, 256, 0, s>>>(off, groups, rows, bm, off_s, prefix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const double f1 = 2.0 * rows * (double)Fr * H;
+  const double by1 = es * ((double)rows * H + (double)groups * H * Fr + (A1 ? 2.0 : 1.0) * rows * Fr);
+  const double by2 = es * ((double)rows * Fr + (double)groups * Fr * H + (double)rows * H);
+  if (tiled) {
+    {
+      ProfScope p("gemm_bf16_grouped<fc1, bias+gelu>", s, f1, by1);
+      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix, groups, (long)H * Fr, Fr, (int)maxmt, s);
+      if (e != hipSuccess) return e;
+    }
+    ProfScope p("gemm_bf16_grouped<fc2>", s, f1, by2);
+    return launch_gemm_bf16_grouped(fc2, off_s, prefix, groups, (long)Fr * H, 0, (int)maxmt, s);
+  }
+  {
+    ProfScope p("gemm_generic_grouped<fc1, bias+gelu>", s, f1, by1);
+    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix, groups, (long)H * Fr, Fr, (int)maxmt, s);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
+  return launch_gemm_generic_grouped(fc2, off_s, prefix, groups, (long)Fr * H, 0, (int)maxmt, s);
+}
+
+}  // namespace tp

@@ -47,4 +47,10 @@ hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* q
                            const void* ctx, const float* lse, const void* dctx, void* dqkv,
                            float* ws, hipStream_t s);
 
+// Grouped expert MLP shard (rows [off[e], off[e+1]) use expert e's weights); off is device memory.
+size_t grouped_ws_bytes(int groups);
+hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
+                              const void* X, const void* W1, const void* b1, const void* W2, void* Z,
+                              void* A1, void* Y, void* ws, hipStream_t s);
+
 }  // namespace tp

@@ -1,7 +1,10 @@
 // Column sums over the token dimension (bias gradients): out[c] = Σ_r in[r, c].
-// Deterministic: fixed 64-row chunks summed in order into an fp32 workspace, then the chunks in
-// order.  Bandwidth-bound; each thread owns 8 adjacent columns so rows are read in 16-byte pieces
-// when the layout allows.
+//
+// Deterministic two-pass reduction in fp32.  Pass 1: a workgroup owns a 256-column x 256-row block;
+// its 256 threads are 32 column groups (8 adjacent columns each, 16-byte loads, so a half-wave reads
+// 512 contiguous bytes of a row) x 8 row groups (rows r0 + g, r0 + g + 8, ...); the 8 row-group
+// sums meet in LDS in a fixed order and one fp32 partial per column and block row is written.
+// Pass 2 adds the block-row partials of each column in order.  HBM-bound: the input is read once.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -10,43 +13,51 @@ namespace tp {
 
 namespace {
 
-constexpr int CS_ROWS = 64;   // rows per chunk
-constexpr int CS_COLS = 8;    // columns per thread
-constexpr int CS_THREADS = 256;
+constexpr int CS_ROWS = 256;   // rows per partial
+constexpr int CS_COLS = 256;   // columns per workgroup
+constexpr int CS_RG = 8;       // row groups per workgroup
 
 template <typename T>
-__global__ __launch_bounds__(CS_THREADS) void colsum_partial_kernel(const T* in, long ld, int rows,
-                                                                    int cols, float* ws) {
-  const int c0 = (blockIdx.x * CS_THREADS + threadIdx.x) * CS_COLS;
-  const int chunk = blockIdx.y;
-  if (c0 >= cols) return;
-  const int r0 = chunk * CS_ROWS, r1 = min(rows, r0 + CS_ROWS);
-  float s[CS_COLS];
-  for (int j = 0; j < CS_COLS; ++j) s[j] = 0.f;
-  const bool full = (c0 + CS_COLS <= cols) && ((ld * sizeof(T)) % 16 == 0) &&
-                    (((uintptr_t)in) % 16 == 0);
-  for (int r = r0; r < r1; ++r) {
-    const T* p = in + (long)r * ld + c0;
-    if (full) {
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 v = *(const bf16x8*)p;
-        for (int j = 0; j < 8; ++j) s[j] += (float)v[j];
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ in, long ld, int rows,
+                                                             int cols, float* __restrict__ ws) {
+  __shared__ float red[CS_RG][CS_COLS + 1];
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c0 = blockIdx.x * CS_COLS + 8 * cg;
+  const int r0 = blockIdx.y * CS_ROWS;
+  const int r1 = min(rows, r0 + CS_ROWS);
+  float s[8];
+  for (int j = 0; j < 8; ++j) s[j] = 0.f;
+  const bool vec = (c0 + 8 <= cols) && ((ld * sizeof(T)) % 16 == 0) && (((uintptr_t)in) % 16 == 0);
+  if (c0 < cols) {
+    for (int r = r0 + rg; r < r1; r += CS_RG) {
+      const T* p = in + (long)r * ld + c0;
+      if (vec) {
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 v = *(const bf16x8*)p;
+          for (int j = 0; j < 8; ++j) s[j] += (float)v[j];
+        } else {
+          const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+          for (int j = 0; j < 4; ++j) { s[j] += a[j]; s[4 + j] += b[j]; }
+        }
       } else {
-        f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-        for (int j = 0; j < 4; ++j) { s[j] += a[j]; s[4 + j] += b[j]; }
+        for (int j = 0; j < 8; ++j)
+          if (c0 + j < cols) s[j] += to_f32(p[j]);
       }
-    } else {
-      for (int j = 0; j < CS_COLS; ++j)
-        if (c0 + j < cols) s[j] += to_f32(p[j]);
     }
   }
-  for (int j = 0; j < CS_COLS; ++j)
-    if (c0 + j < cols) ws[(long)chunk * cols + c0 + j] = s[j];
+  for (int j = 0; j < 8; ++j) red[rg][8 * cg + j] = s[j];
+  __syncthreads();
+  const int c = blockIdx.x * CS_COLS + threadIdx.x;
+  if (c < cols) {
+    float t = 0.f;
+    for (int g = 0; g < CS_RG; ++g) t += red[g][threadIdx.x];
+    ws[(long)blockIdx.y * cols + c] = t;
+  }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* ws, int chunks, int cols,
-                                                           T* out) {
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ ws, int chunks,
+                                                           int cols, T* __restrict__ out) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= cols) return;
   float s = 0.f;
@@ -55,12 +66,11 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* ws, int 
 }
 
 template <typename T>
-hipError_t colsum_t(const void* in, long ld, int rows, int cols, float* ws, void* out,
-                    hipStream_t s) {
+hipError_t colsum_t(const void* in, long ld, int rows, int cols, float* ws, void* out, hipStream_t s) {
   const int chunks = (rows + CS_ROWS - 1) / CS_ROWS;
   if (chunks > 0) {
-    dim3 grid((cols + CS_THREADS * CS_COLS - 1) / (CS_THREADS * CS_COLS), chunks);
-    colsum_partial_kernel<T><<<grid, CS_THREADS, 0, s>>>((const T*)in, ld, rows, cols, ws);
+    dim3 grid((cols + CS_COLS - 1) / CS_COLS, chunks);
+    colsum_partial_kernel<T><<<grid, 256, 0, s>>>((const T*)in, ld, rows, cols, ws);
   }
   colsum_final_kernel<T><<<(cols + 255) / 256, 256, 0, s>>>(ws, chunks, cols, (T*)out);
   return hipGetLastError();

@@ -129,3 +129,24 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 4, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bd.tp_qkv_shard_fwd(1, 0, 1, 4, 4, 1, x, x, x[0], x)
+
+
+def test_grouped_validation(lib):
+    f = lib.tp_mlp_grouped_shard_fwd
+    base = [8, 0, 128, P, 1024, 8192, 2048, 0, P, P, P, P, P, P, P, P, 1 << 20, None]
+    ok = list(base)
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=0) == -1                 # no groups
+    assert call(a3=None) == -2              # offsets
+    assert call(a3=P + 2) == -3             # offsets alignment
+    assert call(a6=4) == -1                 # F_group < tp_size
+    assert call(a8=None) == -2              # X_perm
+    assert call(a14=None) == -2             # Y_r required
+    assert call(a15=None, a16=0) == -5      # workspace
+    assert call(a15=P + 16) == -3           # workspace alignment
+    assert bd.tp_workspace_bytes("tp_mlp_grouped_shard_fwd", 8, 0, 1, 1, 8192, 128, 2048, 0) >= 2 * 129 * 4
+    assert ok is not base

@@ -11,11 +11,11 @@ import pytest
 import torch
 
 import oracle
-from gpu_harness import Shard, assert_close, host
+from gpu_harness import Shard, assert_close, dev, host
 from test_gpu_parity import (run_attn_bwd, run_attn_fwd, run_mlp_bwd, run_mlp_fwd, run_qkv_bwd,
                              run_qkv_fwd)
-from tensor_transformer_layer_mlp_amd import synth
-from tensor_transformer_layer_mlp_amd.configs import GPT2_1P5B, GPT3_175B, GPT_8P3B
+from tensor_transformer_layer_mlp_amd import binding as bd, synth
+from tensor_transformer_layer_mlp_amd.configs import GPT2_1P5B, GPT3_175B, GPT_8P3B  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,45 @@ def test_gpt_8p3b_tp8_all_ranks_sum():
 @pytest.mark.parametrize("rank", [3, 7])
 def test_gpt_8p3b_tp8_rank(rank):
     check_shard(GPT_8P3B, rank)
+
+
+def test_moe_expert_shard_tp8_rank0():
+    """The 128-expert MoE FFN shard (hidden 8192, expert ffn 2048 -> 256 columns on rank 0 of 8,
+    16384 tokens routed top-8 -> 131072 rows) at full size; sampled experts and rows checked."""
+    from tensor_transformer_layer_mlp_amd.configs import MOE_E128 as mw
+    dt, tp, rank = "bf16", mw.tp_size, 0
+    f0, Fr = oracle.shard_range(mw.F_expert, tp, rank)
+    off, tok = synth.moe_assignments(mw.tokens, mw.n_experts, mw.top_k)
+    rows, H, G = int(off[-1]), mw.H, mw.n_experts
+    print(f"moe: rows {rows} experts {G} H {H} Fr {Fr}", flush=True)
+    Xop = synth.normal("moeX", (mw.tokens, H), 1.0, dt)
+    X = dev(Xop)
+    Xperm = X.index_select(0, torch.from_numpy(tok).to("cuda")).contiguous()
+    keep = {0, G // 2, G - 1}
+    W1 = torch.empty(G, H, Fr, dtype=torch.bfloat16, device="cuda")
+    b1 = torch.empty(G, Fr, dtype=torch.bfloat16, device="cuda")
+    W2 = torch.empty(G, Fr, H, dtype=torch.bfloat16, device="cuda")
+    host_w = {}
+    for e in range(G):
+        w1 = synth.column_blocks(f"W1_e{e}", H, f0, f0 + Fr, mw.w_std, dt)
+        bb = synth.vector_blocks(f"b1_e{e}", f0, f0 + Fr, mw.w_std, dt)
+        w2 = synth.row_blocks(f"W2_e{e}", H, f0, f0 + Fr, mw.w_std, dt)
+        W1[e], b1[e], W2[e] = dev(w1), dev(bb), dev(w2)
+        if e in keep:
+            host_w[e] = (w1.f64, bb.f64, w2.f64)
+    print("moe: inputs ready", flush=True)
+    Z = torch.empty(rows, H, dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty(rows, Fr, dtype=torch.bfloat16, device="cuda")
+    ws = bd.workspace("tp_mlp_grouped_shard_fwd", tp, rank, 1, rows, H, G, mw.F_expert, torch.bfloat16)
+    bd.tp_mlp_grouped_shard_fwd(tp, rank, G, torch.from_numpy(off).to("cuda"), rows, H, mw.F_expert,
+                                Xperm, W1, b1, W2, Z, None, Y, ws)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    for e in sorted(keep):
+        lo, hi = int(off[e]), int(off[e + 1])
+        pick = np.unique(np.concatenate([[lo, hi - 1], g.integers(lo, hi, 8)]))
+        xs = Xop.f64[tok[pick]]
+        w1, bb, w2 = host_w[e]
+        r = oracle.mlp_fwd(xs, w1, bb, w2, None)
+        assert_close(host(Z[torch.from_numpy(pick).to("cuda")]), r["Z"], dt, f"Z rows of expert {e}")
+        assert_close(host(Y[torch.from_numpy(pick).to("cuda")]), r["Y"], dt, f"Y rows of expert {e}")

@@ -317,3 +317,75 @@ def test_empty_batch(dtype):
     for t_ in (dW1, db1, dW2, db2, dWq, dbq):
         assert (t_ == 0).all()
     assert wl.T == 0
+
+
+# ---- grouped expert MLP shard -----------------------------------------------------------------
+
+GROUP_CASES = {
+    "tiled_ragged": ([0, 5, 300, 1, 257, 77], 0),        # 640 rows: tiled path, ragged and empty groups
+    "tiled_aligned": ([256, 512, 0, 256], 0),
+    "generic_ragged": ([3, 0, 200, 131, 300], 7),         # 634 + 7 rows: generic path, untouched tail
+}
+
+
+def _grouped_inputs(sizes, extra, dtype, H=192, F_group=128, tp=2, rank=1, std=0.05):
+    G = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(off[-1]) + extra
+    _, Fr = oracle.shard_range(F_group, tp, rank)
+    ops = dict(X=synth.normal("Xperm", (rows, H), 1.0, dtype),
+               W1=synth.normal("W1g", (G, H, Fr), std, dtype),
+               b1=synth.normal("b1g", (G, Fr), std, dtype),
+               W2=synth.normal("W2g", (G, Fr, H), std, dtype))
+    return off, rows, Fr, ops
+
+
+def _run_grouped(off, rows, H, F_group, tp, rank, ops, dtype, Fr):
+    G = len(off) - 1
+    Z, A1, Y = empty((rows, H), dtype), empty((rows, Fr), dtype), empty((rows, Fr), dtype)
+    ws = bd.workspace("tp_mlp_grouped_shard_fwd", tp, rank, 1, rows, H, G, F_group, TORCH_DT[dtype])
+    bd.tp_mlp_grouped_shard_fwd(tp, rank, G, torch.from_numpy(off).to("cuda"), rows, H, F_group,
+                                dev(ops["X"]), dev(ops["W1"]), dev(ops["b1"]), dev(ops["W2"]), Z, A1, Y, ws)
+    torch.cuda.synchronize()
+    return Z, A1, Y
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("case", sorted(GROUP_CASES))
+def test_grouped_mlp(case, dtype):
+    sizes, extra = GROUP_CASES[case]
+    H, F_group, tp, rank = 192, 128, 2, 1
+    off, rows, Fr, ops = _grouped_inputs(sizes, extra, dtype, H, F_group, tp, rank)
+    Z, A1, Y = _run_grouped(off, rows, H, F_group, tp, rank, ops, dtype, Fr)
+    f = {k: v.f64 for k, v in ops.items()}
+    ref = oracle.tp_mlp_grouped_shard_fwd(tp, rank, off, f["X"], f["W1"], f["b1"], f["W2"])
+    n = int(off[-1])
+    assert_close(host(Z)[:n], ref[:n], dtype, "Z_r grouped")
+    for e in range(len(sizes)):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            r = oracle.mlp_fwd(f["X"][lo:hi], f["W1"][e], f["b1"][e], f["W2"][e], None)
+            assert_close(host(Y)[lo:hi], r["Y"], dtype, f"Y expert {e}")
+            assert_close(host(A1)[lo:hi], r["A1"], dtype, f"A1 expert {e}")
+    if extra:
+        assert torch.isnan(Z[n:]).all() and torch.isnan(Y[n:]).all(), "rows past the last group untouched"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_mlp_malformed_offsets(dtype):
+    """Decreasing offsets and offsets past the end are clamped (prev <= off[e] <= rows) before use."""
+    H, F_group, tp, rank = 192, 128, 2, 0
+    raw_off = np.array([0, 300, 100, 500, 900], dtype=np.int32)      # 900 > rows = 640
+    _, rows, Fr, ops = _grouped_inputs([300, 0, 200, 140], 0, dtype, H, F_group, tp, rank)
+    Z, A1, Y = _run_grouped(raw_off, rows, H, F_group, tp, rank, ops, dtype, Fr)
+    clamped = np.array([0, 300, 300, 500, 640])
+    f = {k: v.f64 for k, v in ops.items()}
+    ref = oracle.tp_mlp_grouped_shard_fwd(tp, rank, clamped, f["X"], f["W1"], f["b1"], f["W2"])
+    assert_close(Z, ref, dtype, "Z_r with clamped offsets")
+
+
+def test_grouped_mlp_deterministic():
+    off, rows, Fr, ops = _grouped_inputs([0, 5, 300, 1, 257, 77], 0, "bf16")
+    a = _run_grouped(off, rows, 192, 128, 2, 1, ops, "bf16", Fr)[0]
+    b = _run_grouped(off, rows, 192, 128, 2, 1, ops, "bf16", Fr)[0]
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
