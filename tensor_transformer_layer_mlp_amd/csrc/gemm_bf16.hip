@@ -35,12 +35,14 @@ struct Tile {
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int A_BYTES = BM * BKT * 2, B_BYTES = BN * BKT * 2;
   static_assert(BKT == 32 || BKT == 64, "k per tile is 32 or 64");
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int IPW_A = A_BYTES / 1024 / NW, IPW_B = B_BYTES / 1024 / NW;  // loads per wave
+  // An MN-major tile is stored as k-rows whose pitch is the tile width rounded up to a power of two
+  // (the XOR swizzle needs it); columns past the width are loaded as zeros and never read.
+  static constexpr int pitch(int w) { return w <= 128 ? 128 : (w <= 256 ? 256 : 512); }
+  static constexpr int PM = pitch(BM), PN = pitch(BN);
+  template <bool KMAJ, int W> static constexpr int bytes() { return (KMAJ ? W : pitch(W)) * BKT * 2; }
+  static constexpr int STAGE = bytes<false, BM>() + bytes<false, BN>();   // room for either layout
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "loads must split evenly");
   static_assert(BM >= 128 && BN >= 128, "MN-major swizzle needs at least 8 chunks of 32 bytes");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS holds 160 KiB");
 };
@@ -65,7 +67,7 @@ __device__ __forceinline__ int swz_k(int r) {
 // Byte offset inside an operand's tile of the 16-byte piece lane `lane` of load `j` carries, and the
 // (row, col) of the global matrix it comes from, relative to the tile origin.  For a K-major tile the
 // global piece is (mn = r, k = 8c .. 8c+7); for an MN-major one (k = r, mn = c .. c+7).
-template <bool KMAJ, int BMN, int BKT>
+template <bool KMAJ, int BMN, int BKT>   // BMN: the LDS row pitch (elements) of an MN-major tile
 __device__ __forceinline__ void piece(int o, int& r, int& c) {
   if constexpr (KMAJ) {
     r = o / (2 * BKT);
@@ -105,17 +107,18 @@ struct Operand {
 };
 
 // One operand's loads for one k-tile.
-template <bool KMAJ, int BMN, int IPW, int BKT>
+// BMN: rows (K-major) or the LDS pitch (MN-major); W: the tile's width along m / n.
+template <bool KMAJ, int BMN, int W, int IPW, int BKT>
 __device__ __forceinline__ void load_tile(const Operand& op, int mn0, int k0, int K, TP_LDS char* dst,
                                           const int (&r)[IPW], const int (&c)[IPW], int wave) {
   const bf16* base;
   unsigned span;
   if constexpr (KMAJ) {
     base = op.p + (long)mn0 * op.ld + k0;
-    span = (unsigned)(((long)(BMN - 1) * op.ld + BKT) * 2);
+    span = (unsigned)(((long)(W - 1) * op.ld + BKT) * 2);
   } else {
     base = op.p + (long)k0 * op.ld + mn0;
-    span = (unsigned)(((long)(BKT - 1) * op.ld + BMN) * 2);
+    span = (unsigned)(((long)(BKT - 1) * op.ld + W) * 2);
   }
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)span, 0x00020000);
 #pragma unroll
@@ -126,7 +129,7 @@ __device__ __forceinline__ void load_tile(const Operand& op, int mn0, int k0, in
       ok = (mn0 + r[j] < op.mn_total) && (k0 + c[j] < K);
       off = (unsigned)(((long)r[j] * op.ld + c[j]) * 2);
     } else {
-      ok = (k0 + r[j] < K) && (mn0 + c[j] < op.mn_total);
+      ok = (k0 + r[j] < K) && (c[j] < W) && (mn0 + c[j] < op.mn_total);
       off = (unsigned)(((long)r[j] * op.ld + c[j]) * 2);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TP_LDS void*)(dst + (wave * IPW + j) * 1024), 16,
@@ -158,13 +161,17 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
 template <class Cfg, bool AK, bool BK, int EPI>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
                                           int lane) {
+  constexpr int LA = AK ? Cfg::BM : Cfg::PM, LB = BK ? Cfg::BN : Cfg::PN;   // rows or pitch
+  constexpr int A_BYTES = Cfg::template bytes<AK, Cfg::BM>(), B_BYTES = Cfg::template bytes<BK, Cfg::BN>();
+  constexpr int IPW_A = A_BYTES / 1024 / Cfg::NW, IPW_B = B_BYTES / 1024 / Cfg::NW;   // loads per wave
+  static_assert(A_BYTES % (1024 * Cfg::NW) == 0 && B_BYTES % (1024 * Cfg::NW) == 0, "loads must split evenly");
   const Operand A{(const bf16*)d.A, d.lda, d.M};
   const Operand B{(const bf16*)d.B, d.ldb, d.N};
-  int ar[Cfg::IPW_A], ac[Cfg::IPW_A], br[Cfg::IPW_B], bc[Cfg::IPW_B];
+  int ar[IPW_A], ac[IPW_A], br[IPW_B], bc[IPW_B];
 #pragma unroll
-  for (int j = 0; j < Cfg::IPW_A; ++j) piece<AK, Cfg::BM, Cfg::BKT>((wave * Cfg::IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
+  for (int j = 0; j < IPW_A; ++j) piece<AK, LA, Cfg::BKT>((wave * IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
 #pragma unroll
-  for (int j = 0; j < Cfg::IPW_B; ++j) piece<BK, Cfg::BN, Cfg::BKT>((wave * Cfg::IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+  for (int j = 0; j < IPW_B; ++j) piece<BK, LB, Cfg::BKT>((wave * IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
 
   const int wm = (wave / Cfg::WN) * Cfg::TM, wn = (wave % Cfg::WN) * Cfg::TN;
   f32x4 acc[Cfg::FM][Cfg::FN];
@@ -180,17 +187,17 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
     if (t < nk) {
-      load_tile<AK, Cfg::BM, Cfg::IPW_A, Cfg::BKT>(A, m0, t * BKT, d.K, lds + t * Cfg::STAGE, ar, ac, wave);
-      load_tile<BK, Cfg::BN, Cfg::IPW_B, Cfg::BKT>(B, n0, t * BKT, d.K, lds + t * Cfg::STAGE + Cfg::A_BYTES, br, bc, wave);
+      load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, t * BKT, d.K, lds + t * Cfg::STAGE, ar, ac, wave);
+      load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, t * BKT, d.K, lds + t * Cfg::STAGE + A_BYTES, br, bc, wave);
     }
   int cur_stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt has landed once at most the loads of the STAGES-2 younger tiles are outstanding
-    if (kt + Cfg::STAGES - 2 < nk) wait_vmcnt<(Cfg::STAGES - 2) * (Cfg::IPW_A + Cfg::IPW_B)>();
+    if (kt + Cfg::STAGES - 2 < nk) wait_vmcnt<(Cfg::STAGES - 2) * (IPW_A + IPW_B)>();
     else wait_vmcnt<0>();
     __syncthreads();   // every wave's part of tile kt is in LDS; the stage loaded next is free
     const TP_LDS char* at = lds + cur_stage * Cfg::STAGE;
-    const TP_LDS char* bt = at + Cfg::A_BYTES;
+    const TP_LDS char* bt = at + A_BYTES;
     bf16x8 af[NKK][Cfg::FM], bfr[NKK][Cfg::FN];
     // With an MN-major operand (transposed LDS reads), reading every fragment of the tile before
     // issuing the next tile's loads keeps the LDS reads off the critical path after the barrier;
@@ -199,9 +206,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
 #pragma unroll
       for (int q = 0; q < NKK; ++q) {
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, Cfg::BM, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
+        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, LA, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, Cfg::BN, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
+        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, LB, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
       }
     }
     if (kt + Cfg::STAGES - 1 < nk) {
@@ -209,16 +216,16 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
       if (ns >= Cfg::STAGES) ns -= Cfg::STAGES;
       TP_LDS char* nxt = lds + ns * Cfg::STAGE;
       const int k1 = (kt + Cfg::STAGES - 1) * BKT;
-      load_tile<AK, Cfg::BM, Cfg::IPW_A, Cfg::BKT>(A, m0, k1, d.K, nxt, ar, ac, wave);
-      load_tile<BK, Cfg::BN, Cfg::IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + Cfg::A_BYTES, br, bc, wave);
+      load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, k1, d.K, nxt, ar, ac, wave);
+      load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + A_BYTES, br, bc, wave);
     }
 #pragma unroll
     for (int q = 0; q < NKK; ++q) {
       if constexpr (!EARLY) {
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, Cfg::BM, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
+        for (int i = 0; i < Cfg::FM; ++i) af[q][i] = frag<AK, LA, Cfg::BKT>(at, wm + 16 * i, 32 * q, lane);
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, Cfg::BN, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
+        for (int j = 0; j < Cfg::FN; ++j) bfr[q][j] = frag<BK, LB, Cfg::BKT>(bt, wn + 16 * j, 32 * q, lane);
       }
 #pragma unroll
       for (int i = 0; i < Cfg::FM; ++i)
@@ -335,12 +342,13 @@ using C4 = Tile<256, 256, 4, 2, 3, 32>;
 using C5 = Tile<256, 256, 4, 2, 4, 32>;
 using C6 = Tile<256, 256, 4, 2, 5, 32>;
 using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
-constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256};
-constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256};
+using C8 = Tile<256, 192, 4, 2, 2, 64>;   // 2 waves / SIMD, 64x96 per wave
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0};
+constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95};
 constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
-                                     "256x256k32s4", "256x256k32s5", "256x256w4"};
+                                     "256x256k32s4", "256x256k32s5", "256x256w4", "256x192"};
 
 }  // namespace
 
@@ -369,7 +377,7 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   // modelled time: (number of 256-CU waves of tiles) x (tile area) / (relative rate)
   int best = 0;
   double best_t = 1e300;
-  for (int c = 0; c < 4; ++c) {
+  for (int c : {0, 8, 1, 2, 3}) {
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
     const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
     if (est < best_t * 0.999) { best_t = est; best = c; }
@@ -388,7 +396,8 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 4: return run_cfg<C4>(d, s);
     case 5: return run_cfg<C5>(d, s);
     case 6: return run_cfg<C6>(d, s);
-    default: return run_cfg<C7>(d, s);
+    case 7: return run_cfg<C7>(d, s);
+    default: return run_cfg<C8>(d, s);
   }
 }
 
