@@ -32,6 +32,7 @@ def parse():
     ap.add_argument("--cpu-seq", type=int, default=2048,
                     help="tokens of the oracle's CPU sample (the first S of the sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped-shard measurement")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time without the per-kernel events (the roofline object is then null)")
     return ap.parse_args()
@@ -90,6 +91,47 @@ def cpu_baseline(wl, rank, seq, min_seconds=10.0, max_reps=4):
             "seconds": round(secs, 2)}
 
 
+def moe_grouped(bd, torch, steps, warmup):
+    """The 128-expert MoE FFN shard (row A9) on its own workload: rank 0 of tp=8, 16384 tokens routed
+    top-8 -> 131072 expert-sorted rows, hidden 8192, 256 expert-ffn columns per rank.  HBM-bound:
+    bytes = X_perm read + expert weights + Y written and read back + Z written."""
+    from tensor_transformer_layer_mlp_amd import synth
+    from tensor_transformer_layer_mlp_amd.configs import MOE_E128 as mw
+    tp, rank = mw.tp_size, 0
+    _, Fr = bd.tp_shard_range(mw.F_expert, tp, rank)
+    off, _ = synth.moe_assignments(mw.tokens, mw.n_experts, mw.top_k)
+    rows, H, G = int(off[-1]), mw.H, mw.n_experts
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    bf = torch.bfloat16
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    Xp = r(rows, H)
+    W1, b1, W2 = r(G, H, Fr, std=mw.w_std), r(G, Fr, std=mw.w_std), r(G, Fr, H, std=mw.w_std)
+    Z, Y = torch.empty(rows, H, dtype=bf, device="cuda"), torch.empty(rows, Fr, dtype=bf, device="cuda")
+    offs = torch.from_numpy(off).to("cuda")
+    ws = bd.workspace("tp_mlp_grouped_shard_fwd", tp, rank, 1, rows, H, G, mw.F_expert, bf)
+    call = lambda: bd.tp_mlp_grouped_shard_fwd(tp, rank, G, offs, rows, H, mw.F_expert, Xp, W1, b1,  # noqa: E731
+                                               W2, Z, None, Y, ws)
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flop = 4.0 * rows * H * Fr
+    byts = 2.0 * (2 * rows * H + 2 * G * H * Fr + G * Fr + 2 * rows * Fr)
+    out = {"workload": mw.name + "_rank0", "rows": rows, "ms": round(ms, 4),
+           "tflops": round(flop / ms / 1e9, 2), "gb_per_s": round(byts / ms / 1e6, 1),
+           "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3)}
+    del Xp, W1, W2, Z, Y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -140,25 +182,34 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(with_events):
+        if with_events:
+            bd.tp_prof_collect()          # drop anything recorded before
+            bd.tp_prof_enable(True)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        w = time.perf_counter() - w0
+        k = None
+        if with_events:
+            bd.tp_prof_enable(False)
+            k = bd.tp_prof_collect()
+        return t0.elapsed_time(t1) / args.steps, w, k
+
+    # timed region 1: the headline number, nothing but the step on the stream
+    ms_step, wall, _ = timed(False)
+    # timed region 2: the same steps with two HIP events around every kernel launch (on the launch
+    # stream), for the per-kernel durations behind the roofline figures
     events = not args.no_kernel_events
     if events:
-        bd.tp_prof_collect()          # drop anything recorded before
-        bd.tp_prof_enable(True)
-    stream = torch.cuda.current_stream()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    if events:
-        bd.tp_prof_enable(False)
-        kernels = bd.tp_prof_collect()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+        ms_step_ev, _, kernels = timed(True)
     fl = step_flops(T, S, B, H, Nq, nh, d, Fr)
     flop_step = sum(fl.values())
     tflops = flop_step / (ms_step * 1e-3) / 1e12
@@ -188,6 +239,8 @@ def main():
                         "launches_per_step": n / args.steps, "avg_launch_us": round(avg_s * 1e6, 2),
                         "bytes_per_launch": byts / n}
 
+    moe = None if args.no_moe else moe_grouped(bd, torch, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, rank, args.cpu_seq)
@@ -204,9 +257,11 @@ def main():
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "gflop_per_step": round(flop_step / 1e9, 1),
         "wall_s_timed_region": round(wall, 3),
+        "ms_per_step_with_kernel_events": round(ms_step_ev, 4) if events else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": breakdown,
+        "moe_grouped_shard": moe,
     }
     print(json.dumps(out), flush=True)
 
