@@ -22,6 +22,12 @@ import time
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of `--pmc-pass`
+# scaled by the same counters on a copy of known size; valid only while the kernel's sources hash the
+# same as when the counters were taken.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_tn_gpt3_175b_tp8_rank0_traffic.txt")
+GEMM_SOURCES = ["gemm_bf16.hip", "common.h", "kernels.h"]
 
 
 def parse():
@@ -33,9 +39,36 @@ def parse():
                     help="tokens of the oracle's CPU sample (the first S of the sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped-shard measurement")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
+                         "calibrated on), then --warmup + --steps steps, and nothing else")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time without the per-kernel events (the roofline object is then null)")
     return ap.parse_args()
+
+
+def gemm_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "tensor_transformer_layer_mlp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """Bytes per launch recorded for `kernel`, or None when absent or taken on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel") != kernel or kv.get("sources_sha256") != gemm_sources_sha256():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def step_flops(T, S, B, H, Nq, nh, d, Fr):
@@ -180,6 +213,20 @@ def main():
         bd.tp_attn_heads_bwd(t, rank, B, S, H, nh_all, QKV, ctx, lse, dctx, dQKV, ws_a)
         bd.tp_qkv_shard_bwd(t, rank, B, S, H, nh_all, X, Wq, dQKV, dXq, dWq, dbq, ws_q)
 
+    if args.pmc_pass:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        c = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=c)                     # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del a, c
+        for _ in range(args.warmup + args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "calibration_bytes": 1 << 30, "steps": args.warmup + args.steps,
+                          "gemm_sources_sha256": gemm_sources_sha256()}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream()
@@ -230,12 +277,13 @@ def main():
             ach = flop / n / avg_s / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                        "traffic": None, "launches_per_step": n / args.steps,
-                        "avg_launch_us": round(avg_s * 1e6, 2), "flop_per_launch": flop / n}
+                        "traffic": recorded_traffic(dom), "launches_per_step": n / args.steps,
+                        "avg_launch_us": round(avg_s * 1e6, 2), "flop_per_launch": flop / n,
+                        "algorithmic_bytes_per_launch": byts / n}
         else:
             ach = byts / n / avg_s / 1e9
             roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(dom),
                         "launches_per_step": n / args.steps, "avg_launch_us": round(avg_s * 1e6, 2),
                         "bytes_per_launch": byts / n}
 
