@@ -5,10 +5,16 @@
 // [l % 16].  The kernels choose operand order so that a lane always owns one query (forward, dQ) or
 // one key (dK/dV) of the result, which keeps the softmax row statistics in registers:
 //
-// Forward (one workgroup = 64 queries, two waves of 32): for each 64-key block,
+// Work split: a workgroup owns 64 queries (forward, dQ) or 64 keys (dK/dV) as two waves of 32, and
+// G such wave pairs ("groups") share the other dimension's 64-wide blocks round-robin (group g takes
+// blocks g, g+G, ...), each group with its own double-buffered LDS tiles.  This shortens the causal
+// chain of the longest workgroups G-fold and puts 2G waves on a CU.  At the end the groups' partial
+// results meet in LDS and group 0 combines them in a fixed order (deterministic).
+// Forward (per wave of 32 queries): for each 64-key block of its group,
 //   S = K·Qᵀ     lane: query q, keys 4g+e of each 16-key slice      (K from LDS, Q in registers)
-//   online softmax in the exp2 domain: t = s·log2(e)/√d; running max m (two xor-shuffles give the
-//   row max across the 4 lanes of a query) and per-lane partial sums l, merged at the end
+//   online softmax in the exp2 domain: t = s·log2(e)/√d; running max m (two lane swaps give the
+//   row max across the 4 lanes of a query) and per-lane partial sums l; groups merge as
+//   m = max m_g, o = Σ o_g·2^(m_g − m), l = Σ l_g·2^(m_g − m)
 //   Oᵀ += Vᵀ·Pᵀ  P stays in registers as the second operand; the key order of its 8 k-slots
 //                (4g+e and 16+4g+e) is matched by reading V with ds_read_b64_tr_b16.
 //   LSE = (m + log2 l)·ln 2.
@@ -105,14 +111,27 @@ __device__ __forceinline__ bf16x8 frag_global(const bf16* rows, long rs, int r0,
   return (bf16x8){};
 }
 
-__device__ __forceinline__ float xmax4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// v_permlane16_swap / v_permlane32_swap applied to two copies of v leave {v[l], v[l^16]} (resp.
+// {v[l], v[l^32]}) in the two results of lane l: a cross-row exchange in one VALU op, no LDS.
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xsum4(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// over the 4 lanes l%16 + 16g (g = 0..3) that share one query or key row
+__device__ __forceinline__ float xmax4(float v) { return pair32_max(pair16_max(v)); }
+__device__ __forceinline__ float xsum4(float v) { return pair32_sum(pair16_sum(v)); }
 
 __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
   return (bf16x8){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
@@ -124,18 +143,22 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v, float s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_mfma(int B, int S, int nh, int nqb,
-                                                     const bf16* __restrict__ qkv,
-                                                     bf16* __restrict__ ctx, float* __restrict__ lse) {
+template <int D, int G>
+__global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, int nqb,
+                                                         const bf16* __restrict__ qkv,
+                                                         bf16* __restrict__ ctx, float* __restrict__ lse) {
   using C = AC<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  constexpr int GST = 2 * 2 * C::TILE;          // per group: two stages of (K tile, V tile)
+  constexpr int SLOT = 64 * (2 * C::NDB * 16 + 16);   // one wave's partial (o, m, l) for the merge
+  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
+  __shared__ __attribute__((aligned(1024))) char smem[G * GST];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;  // long blocks first
   const long rs = 3L * nh * D;
   const bf16* qrows = qkv + (long)b * S * rs + (long)h * 3 * D;
-  const int qw = qb * 64 + 32 * wave;
+  const int qw = qb * 64 + 32 * half;
   const float c = LOG2E / sqrtf((float)D);
 
   bf16x8 qf[2][C::NKK];
@@ -151,20 +174,24 @@ __global__ __launch_bounds__(128) void attn_fwd_mfma(int B, int S, int nh, int n
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
   const int nkb = min((S + 63) / 64, qb + 1);
-  TP_LDS char* lds = (TP_LDS char*)smem;
-  load_tile<D>(qrows + D, rs, S, lds, wave, lane);
-  load_tile<D>(qrows + 2 * D, rs, S, lds + C::TILE, wave, lane);
-  for (int j = 0; j < nkb; ++j) {
+  const int nit = (nkb + G - 1) / G;
+  TP_LDS char* lds = (TP_LDS char*)smem + grp * GST;
+  if (grp < nkb) {
+    load_tile<D>(qrows + (long)grp * 64 * rs + D, rs, S - grp * 64, lds, half, lane);
+    load_tile<D>(qrows + (long)grp * 64 * rs + 2 * D, rs, S - grp * 64, lds + C::TILE, half, lane);
+  }
+  for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nkb) {
-      TP_LDS char* nx = lds + ((j + 1) & 1) * 2 * C::TILE;
-      load_tile<D>(qrows + (long)(j + 1) * 64 * rs + D, rs, S - (j + 1) * 64, nx, wave, lane);
-      load_tile<D>(qrows + (long)(j + 1) * 64 * rs + 2 * D, rs, S - (j + 1) * 64, nx + C::TILE, wave, lane);
+    const int j = it * G + grp, jn = j + G;
+    if (jn < nkb) {
+      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * C::TILE;
+      load_tile<D>(qrows + (long)jn * 64 * rs + D, rs, S - jn * 64, nx, half, lane);
+      load_tile<D>(qrows + (long)jn * 64 * rs + 2 * D, rs, S - jn * 64, nx + C::TILE, half, lane);
     }
     const int k0 = 64 * j;
-    if (k0 > qw + 31) continue;   // every key of this block is in the future of every query here
-    const TP_LDS char* kt = lds + (j & 1) * 2 * C::TILE;
+    if (j >= nkb || k0 > qw + 31) continue;   // no block, or every key in the future of every query
+    const TP_LDS char* kt = lds + (it & 1) * 2 * C::TILE;
     const TP_LDS char* vt = kt + C::TILE;
     f32x4 s[2][4];
 #pragma unroll
@@ -195,6 +222,7 @@ __global__ __launch_bounds__(128) void attn_fwd_mfma(int B, int S, int nh, int n
           s[qs][kb][e] = t;
           mx = fmaxf(mx, t);
         }
+      // every processed block holds at least one visible key of every query, so mn is finite
       const float mn = fmaxf(m[qs], xmax4(mx));
       const float corr = __builtin_amdgcn_exp2f(m[qs] - mn);
       m[qs] = mn;
@@ -221,6 +249,38 @@ __global__ __launch_bounds__(128) void attn_fwd_mfma(int B, int S, int nh, int n
         const bf16x8 vf = frag_tr<D>(vt, 32 * kc, 16 * db, lane);
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) o[qs][db] = mfma_16x16x32_bf16(vf, pf[qs], o[qs][db]);
+      }
+    }
+  }
+
+  if constexpr (G > 1) {
+    // groups 1..G-1 leave (o, m, l) in LDS in lane order; group 0 folds them in, group by group
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (grp > 0) {
+      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = o[qs][db];
+      *(TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16) = (f32x4){m[0], m[1], l[0], l[1]};
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) {
+      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
+      const f32x4 ml = *(const TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float mo = ml[qs], mn = fmaxf(m[qs], mo);
+        if (mn == -INFINITY) continue;      // neither side has seen a key (rows past S only)
+        const float ca = __builtin_amdgcn_exp2f(m[qs] - mn), cb = __builtin_amdgcn_exp2f(mo - mn);
+        m[qs] = mn;
+        l[qs] = l[qs] * ca + ml[2 + qs] * cb;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          o[qs][db] = o[qs][db] * ca + *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) * cb;
       }
     }
   }
@@ -263,17 +323,20 @@ __global__ __launch_bounds__(256) void attn_rowdot(int B, int S, int nh, const b
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, int nqb,
-                                                         const bf16* __restrict__ qkv,
-                                                         const bf16* __restrict__ dctx,
-                                                         const float* __restrict__ lse,
-                                                         const float* __restrict__ Dws,
-                                                         bf16* __restrict__ dqkv) {
+template <int D, int G>
+__global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int nh, int nqb,
+                                                             const bf16* __restrict__ qkv,
+                                                             const bf16* __restrict__ dctx,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ Dws,
+                                                             bf16* __restrict__ dqkv) {
   using C = AC<D>;
   constexpr int STG = 2 * C::TILE + 512;     // Q tile, dO tile, LSE[64], D[64]
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  constexpr int SLOT = 64 * 4 * C::NDB * 16;  // one wave's partial (dK, dV) for the merge
+  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * 2 * STG, "merge slots exceed the tile memory");
+  __shared__ __attribute__((aligned(1024))) char smem[G * 2 * STG];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int kb = idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;   // early keys see most queries
   const long rs = 3L * nh * D, cs = (long)nh * D;
@@ -281,7 +344,7 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, i
   const bf16* dorows = dctx + (long)b * S * cs + (long)h * D;
   const float* lse_bh = lse + ((long)b * nh + h) * S;
   const float* D_bh = Dws + ((long)b * nh + h) * S;
-  const int kw = kb * 64 + 32 * wave;
+  const int kw = kb * 64 + 32 * half;
   const float c = LOG2E / sqrtf((float)D);
 
   bf16x8 kf[2][C::NKK], vf[2][C::NKK];
@@ -301,26 +364,29 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, i
       dv[ks][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-  TP_LDS char* lds = (TP_LDS char*)smem;
+  TP_LDS char* lds = (TP_LDS char*)smem + grp * 2 * STG;
+  // the 64 threads of the group's first wave fill the LSE / D rows
   auto stage = [&](int qb, TP_LDS char* dst) {
     const int q0 = qb * 64;
-    load_tile<D>(rows + (long)q0 * rs, rs, S - q0, dst, wave, lane);
-    load_tile<D>(dorows + (long)q0 * cs, cs, S - q0, dst + C::TILE, wave, lane);
-    if (threadIdx.x < 64) {
-      const int q = q0 + threadIdx.x;
-      ((TP_LDS float*)(dst + 2 * C::TILE))[threadIdx.x] = q < S ? lse_bh[q] : INFINITY;
-      ((TP_LDS float*)(dst + 2 * C::TILE + 256))[threadIdx.x] = q < S ? D_bh[q] : 0.f;
+    load_tile<D>(rows + (long)q0 * rs, rs, S - q0, dst, half, lane);
+    load_tile<D>(dorows + (long)q0 * cs, cs, S - q0, dst + C::TILE, half, lane);
+    if (half == 0) {
+      const int q = q0 + lane;
+      ((TP_LDS float*)(dst + 2 * C::TILE))[lane] = q < S ? lse_bh[q] : INFINITY;
+      ((TP_LDS float*)(dst + 2 * C::TILE + 256))[lane] = q < S ? D_bh[q] : 0.f;
     }
   };
-  const int nq = nqb - kb;
-  stage(kb, lds);
-  for (int j = 0; j < nq; ++j) {
+  const int nq = nqb - kb;                 // query blocks at or after this key block
+  const int nit = (nq + G - 1) / G;
+  if (grp < nq) stage(kb + grp, lds);
+  for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nq) stage(kb + j + 1, lds + ((j + 1) & 1) * STG);
+    const int j = it * G + grp, jn = j + G;
+    if (jn < nq) stage(kb + jn, lds + ((it + 1) & 1) * STG);
     const int q0 = (kb + j) * 64;
-    if (q0 + 63 < kw) continue;      // every query of this block precedes every key of this wave
-    const TP_LDS char* qt = lds + (j & 1) * STG;
+    if (j >= nq || q0 + 63 < kw) continue;   // no block, or every query precedes every key here
+    const TP_LDS char* qt = lds + (it & 1) * STG;
     const TP_LDS char* dt = qt + C::TILE;
     const TP_LDS float* Ls = (const TP_LDS float*)(qt + 2 * C::TILE);
     const TP_LDS float* Ds = Ls + 64;
@@ -376,6 +442,35 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, i
       }
     }
   }
+
+  if constexpr (G > 1) {
+    // partial sums over each group's query blocks, added in group order by group 0
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (grp > 0) {
+      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          *(TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dk[ks][db];
+          *(TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dv[ks][db];
+        }
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) {
+      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dk[ks][db] += *(const TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
+          dv[ks][db] += *(const TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
+        }
+    }
+  }
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -394,22 +489,26 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_mfma(int B, int S, int nh, i
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(128) void attn_bwd_dq_mfma(int B, int S, int nh, int nqb,
-                                                        const bf16* __restrict__ qkv,
-                                                        const bf16* __restrict__ dctx,
-                                                        const float* __restrict__ lse,
-                                                        const float* __restrict__ Dws,
-                                                        bf16* __restrict__ dqkv) {
+template <int D, int G>
+__global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh, int nqb,
+                                                            const bf16* __restrict__ qkv,
+                                                            const bf16* __restrict__ dctx,
+                                                            const float* __restrict__ lse,
+                                                            const float* __restrict__ Dws,
+                                                            bf16* __restrict__ dqkv) {
   using C = AC<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];   // K and V tiles
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  constexpr int GST = 2 * 2 * C::TILE;       // per group: two stages of (K tile, V tile)
+  constexpr int SLOT = 64 * 2 * C::NDB * 16;  // one wave's partial dQ for the merge
+  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
+  __shared__ __attribute__((aligned(1024))) char smem[G * GST];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;
   const long rs = 3L * nh * D, cs = (long)nh * D;
   const bf16* rows = qkv + (long)b * S * rs + (long)h * 3 * D;
   const bf16* dorows = dctx + (long)b * S * cs + (long)h * D;
-  const int qw = qb * 64 + 32 * wave;
+  const int qw = qb * 64 + 32 * half;
   const float c = LOG2E / sqrtf((float)D);
 
   bf16x8 qf[2][C::NKK], df[2][C::NKK];
@@ -432,20 +531,24 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_mfma(int B, int S, int nh, in
     for (int db = 0; db < C::NDB; ++db) acc[qs][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int nkb = min((S + 63) / 64, qb + 1);
-  TP_LDS char* lds = (TP_LDS char*)smem;
-  load_tile<D>(rows + D, rs, S, lds, wave, lane);
-  load_tile<D>(rows + 2 * D, rs, S, lds + C::TILE, wave, lane);
-  for (int j = 0; j < nkb; ++j) {
+  const int nit = (nkb + G - 1) / G;
+  TP_LDS char* lds = (TP_LDS char*)smem + grp * GST;
+  if (grp < nkb) {
+    load_tile<D>(rows + (long)grp * 64 * rs + D, rs, S - grp * 64, lds, half, lane);
+    load_tile<D>(rows + (long)grp * 64 * rs + 2 * D, rs, S - grp * 64, lds + C::TILE, half, lane);
+  }
+  for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nkb) {
-      TP_LDS char* nx = lds + ((j + 1) & 1) * 2 * C::TILE;
-      load_tile<D>(rows + (long)(j + 1) * 64 * rs + D, rs, S - (j + 1) * 64, nx, wave, lane);
-      load_tile<D>(rows + (long)(j + 1) * 64 * rs + 2 * D, rs, S - (j + 1) * 64, nx + C::TILE, wave, lane);
+    const int j = it * G + grp, jn = j + G;
+    if (jn < nkb) {
+      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * C::TILE;
+      load_tile<D>(rows + (long)jn * 64 * rs + D, rs, S - jn * 64, nx, half, lane);
+      load_tile<D>(rows + (long)jn * 64 * rs + 2 * D, rs, S - jn * 64, nx + C::TILE, half, lane);
     }
     const int k0 = 64 * j;
-    if (k0 > qw + 31) continue;
-    const TP_LDS char* kt = lds + (j & 1) * 2 * C::TILE;
+    if (j >= nkb || k0 > qw + 31) continue;
+    const TP_LDS char* kt = lds + (it & 1) * 2 * C::TILE;
     const TP_LDS char* vt = kt + C::TILE;
     f32x4 dsv[2][4];
 #pragma unroll
@@ -487,6 +590,30 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_mfma(int B, int S, int nh, in
       }
     }
   }
+
+  if constexpr (G > 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (grp > 0) {
+      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = acc[qs][db];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) {
+      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          acc[qs][db] += *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16);
+    }
+  }
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -501,10 +628,15 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_mfma(int B, int S, int nh, in
   }
 }
 
+// Groups per workgroup: as many as keep the tiles within 128 KiB of LDS, at most 4.
+template <int D>
+constexpr int attn_groups() { return AC<D>::TILE >= 16384 ? 2 : 4; }
+
 template <int D>
 hipError_t fwd_t(int B, int S, int nh, const void* qkv, void* ctx, float* lse, hipStream_t s) {
+  constexpr int G = attn_groups<D>();
   const int nqb = (S + 63) / 64;
-  attn_fwd_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
+  attn_fwd_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
   return hipGetLastError();
 }
 
@@ -514,10 +646,11 @@ hipError_t bwd_t(int B, int S, int nh, const void* qkv, const void* ctx, const f
   const int nqb = (S + 63) / 64;
   const long rows = (long)B * S * nh;
   attn_rowdot<D><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
-  attn_bwd_dkv_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (const bf16*)dctx,
-                                                    lse, ws, (bf16*)dqkv);
-  attn_bwd_dq_mfma<D><<<nqb * nh * B, 128, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (const bf16*)dctx,
-                                                   lse, ws, (bf16*)dqkv);
+  constexpr int G = attn_groups<D>();
+  attn_bwd_dkv_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
+                                                           (const bf16*)dctx, lse, ws, (bf16*)dqkv);
+  attn_bwd_dq_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
+                                                          (const bf16*)dctx, lse, ws, (bf16*)dqkv);
   return hipGetLastError();
 }
 
