@@ -25,6 +25,9 @@ SOURCES = ["abi.hip", "prof.hip", "dispatch.hip", "gemm_generic.hip", "gemm_bf16
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+# The attention kernels rescale and read their MFMA results with vector ops every block: MFMA results
+# in ordinary VGPRs (not accumulation registers) save the copies between the two register files.
+EXTRA = {"attention_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):
@@ -42,7 +45,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in srcs]
-    cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[HIPCC, *CFLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()

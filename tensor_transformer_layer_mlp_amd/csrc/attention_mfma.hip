@@ -25,10 +25,12 @@
 //           dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS  (dO and Q read transposed from LDS)
 //   dQ      one workgroup = 64 queries, waves of 32 queries, loop over the key blocks up to them:
 //           S, dP, dS as above in the query-owned layout, dQᵀ += Kᵀ·dSᵀ (K read transposed).
-// LDS tiles are 64 rows x (d padded to 32, 64 or 128) with the 32-byte chunk q of row r stored at
+// LDS tiles are KB rows (32 or 64) x (d padded to 32, 64 or 128) with the 32-byte chunk q of row r stored at
 // q ^ sw(r), which keeps both the 16-byte row reads and the transposed 4x16 reads spread over the
 // banks.  Tiles arrive by buffer_load_dwordx4 ... lds (two stages, next block in flight); rows past S
 // and columns past d arrive as zeros.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -46,10 +48,9 @@ struct AC {
   static constexpr int PB = 2 * DP;           // LDS row pitch, bytes
   static constexpr int RS = 256 / PB;         // rows per 256-byte bank window
   static constexpr int NC32 = PB / 32;        // 32-byte chunks per row
-  static constexpr int TILE = 64 * PB;        // 64-row tile
   static constexpr int NKK = DP / 32;         // 32-wide k-steps over d
   static constexpr int NDB = DP / 16;         // 16-wide d blocks of the outputs
-  static constexpr int LOADS = TILE / 1024;   // 1 KiB wave-loads per tile
+  template <int R> static constexpr int tile() { return R * PB; }   // R-row tile, bytes
 };
 
 template <int D>
@@ -61,14 +62,15 @@ __device__ __forceinline__ int taddr(int r, int d) {
   return r * AC<D>::PB + ((((d >> 4) ^ sw<D>(r)) << 5) | ((d & 15) << 1));
 }
 
-// 64 rows starting at `rows` (row stride rs elements), columns [0, D) -> tile; rows >= nvalid and
-// columns >= D are zero.  Two waves share the loads.
-template <int D>
+// R rows starting at `rows` (row stride rs elements), columns [0, D) -> tile; rows >= nvalid and
+// columns >= D are zero.  Two waves share the loads (1 KiB per wave-load).
+template <int D, int R>
 __device__ __forceinline__ void load_tile(const bf16* rows, long rs, int nvalid, TP_LDS char* dst,
                                           int wave, int lane) {
   using C = AC<D>;
-  constexpr int PER = C::LOADS / 2;
-  const unsigned span = (unsigned)((63L * rs + D) * 2);
+  constexpr int PER = C::template tile<R>() / 1024 / 2;
+  static_assert(PER >= 1, "tile smaller than two wave-loads");
+  const unsigned span = (unsigned)(((R - 1L) * rs + D) * 2);
   __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, (int)span, 0x00020000);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -143,16 +145,18 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v, float s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, int KB>
 __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, int nqb,
                                                          const bf16* __restrict__ qkv,
                                                          bf16* __restrict__ ctx, float* __restrict__ lse) {
   using C = AC<D>;
-  constexpr int GST = 2 * 2 * C::TILE;          // per group: two stages of (K tile, V tile)
+  constexpr int TILE = C::template tile<KB>();
+  constexpr int GST = 2 * 2 * TILE;             // per group: two stages of (K tile, V tile)
   constexpr int SLOT = 64 * (2 * C::NDB * 16 + 16);   // one wave's partial (o, m, l) for the merge
-  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
+  static_assert(G == 1 || 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
   __shared__ __attribute__((aligned(1024))) char smem[G * GST];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar registers
   const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;  // long blocks first
@@ -173,29 +177,29 @@ __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, i
     for (int db = 0; db < C::NDB; ++db) o[qs][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  const int nkb = min((S + 63) / 64, qb + 1);
+  const int nkb = min((S + KB - 1) / KB, (64 * qb + 63) / KB + 1);   // key blocks up to the diagonal
   const int nit = (nkb + G - 1) / G;
   TP_LDS char* lds = (TP_LDS char*)smem + grp * GST;
   if (grp < nkb) {
-    load_tile<D>(qrows + (long)grp * 64 * rs + D, rs, S - grp * 64, lds, half, lane);
-    load_tile<D>(qrows + (long)grp * 64 * rs + 2 * D, rs, S - grp * 64, lds + C::TILE, half, lane);
+    load_tile<D, KB>(qrows + (long)grp * KB * rs + D, rs, S - grp * KB, lds, half, lane);
+    load_tile<D, KB>(qrows + (long)grp * KB * rs + 2 * D, rs, S - grp * KB, lds + TILE, half, lane);
   }
   for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int j = it * G + grp, jn = j + G;
     if (jn < nkb) {
-      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * C::TILE;
-      load_tile<D>(qrows + (long)jn * 64 * rs + D, rs, S - jn * 64, nx, half, lane);
-      load_tile<D>(qrows + (long)jn * 64 * rs + 2 * D, rs, S - jn * 64, nx + C::TILE, half, lane);
+      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * TILE;
+      load_tile<D, KB>(qrows + (long)jn * KB * rs + D, rs, S - jn * KB, nx, half, lane);
+      load_tile<D, KB>(qrows + (long)jn * KB * rs + 2 * D, rs, S - jn * KB, nx + TILE, half, lane);
     }
-    const int k0 = 64 * j;
+    const int k0 = KB * j;
     if (j >= nkb || k0 > qw + 31) continue;   // no block, or every key in the future of every query
-    const TP_LDS char* kt = lds + (it & 1) * 2 * C::TILE;
-    const TP_LDS char* vt = kt + C::TILE;
-    f32x4 s[2][4];
+    const TP_LDS char* kt = lds + (it & 1) * 2 * TILE;
+    const TP_LDS char* vt = kt + TILE;
+    f32x4 s[2][KB / 16];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB / 16; ++kb) {
       bf16x8 kf[C::NKK];
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) kf[kk] = frag_row<D>(kt, 16 * kb, 32 * kk, lane);
@@ -207,40 +211,58 @@ __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, i
         s[qs][kb] = a;
       }
     }
-    const bool edge = (k0 + 63 > qw) || (k0 + 64 > S);
+    if ((k0 + KB - 1 > qw) || (k0 + KB > S)) {
+      // diagonal or ragged block (wave-uniform test): hide future keys and keys past S
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int kb = 0; kb < KB / 16; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = qw + 16 * qs + i16, key = k0 + 16 * kb + 4 * g + e;
+            if (key > q || key >= S) s[qs][kb][e] = -INFINITY;
+          }
+    }
+    // Block max per query in the scaled log2 domain (c > 0, so max(s)·c = max(s·c)).  The reference
+    // max m moves only when a block max passes it by more than 8: p = 2^(s·c − m) then stays ≤ 256
+    // and most blocks skip the rescale of o and l, which always share one m, so the result is the
+    // same softmax.  Every processed block holds a visible key of every query: the maxima are finite.
+    float mxs[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const int q = qw + 16 * qs + i16;
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB / 16; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float t = s[qs][kb][e] * c;
-          const int key = k0 + 16 * kb + 4 * g + e;
-          if (edge && (key > q || key >= S)) t = -INFINITY;
-          s[qs][kb][e] = t;
-          mx = fmaxf(mx, t);
-        }
-      // every processed block holds at least one visible key of every query, so mn is finite
-      const float mn = fmaxf(m[qs], xmax4(mx));
-      const float corr = __builtin_amdgcn_exp2f(m[qs] - mn);
-      m[qs] = mn;
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[qs][kb][e]);
+      mxs[qs] = xmax4(mx) * c;
+    }
+    if (__builtin_amdgcn_ballot_w64(mxs[0] > m[0] + 8.f || mxs[1] > m[1] + 8.f)) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float mn = fmaxf(m[qs], mxs[qs]);
+        const float corr = __builtin_amdgcn_exp2f(m[qs] - mn);
+        m[qs] = mn;
+        l[qs] *= corr;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[qs][db] *= corr;
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB / 16; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[qs][kb][e] - mn);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qs][kb][e], c, -m[qs]));
           s[qs][kb][e] = p;
           ls += p;
         }
-      l[qs] = l[qs] * corr + ls;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[qs][db] *= corr;
+      l[qs] += ls;
     }
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KB / 32; ++kc) {
       bf16x8 pf[2];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) pf[qs] = pack8(s[qs][2 * kc], s[qs][2 * kc + 1]);
@@ -254,35 +276,37 @@ __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, i
   }
 
   if constexpr (G > 1) {
-    // groups 1..G-1 leave (o, m, l) in LDS in lane order; group 0 folds them in, group by group
+    // group gg (1..G-1) leaves (o, m, l) in LDS in lane order and group 0 folds it in, one group
+    // per round, so that the merge needs two wave slots of LDS whatever G is
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (grp > 0) {
-      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = o[qs][db];
-      *(TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16) = (f32x4){m[0], m[1], l[0], l[1]};
-    }
-    __syncthreads();
-    if (grp > 0) return;
-#pragma unroll
+    TP_LDS char* slot = (TP_LDS char*)smem + half * SLOT;
     for (int gg = 1; gg < G; ++gg) {
-      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
-      const f32x4 ml = *(const TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16);
+      __syncthreads();
+      if (grp == gg) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const float mo = ml[qs], mn = fmaxf(m[qs], mo);
-        if (mn == -INFINITY) continue;      // neither side has seen a key (rows past S only)
-        const float ca = __builtin_amdgcn_exp2f(m[qs] - mn), cb = __builtin_amdgcn_exp2f(mo - mn);
-        m[qs] = mn;
-        l[qs] = l[qs] * ca + ml[2 + qs] * cb;
+        for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          o[qs][db] = o[qs][db] * ca + *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) * cb;
+          for (int db = 0; db < C::NDB; ++db)
+            *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = o[qs][db];
+        *(TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16) = (f32x4){m[0], m[1], l[0], l[1]};
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const f32x4 ml = *(const TP_LDS f32x4*)(slot + 2 * C::NDB * 64 * 16 + lane * 16);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          const float mo = ml[qs], mn = fmaxf(m[qs], mo);
+          if (mn == -INFINITY) continue;      // neither side has seen a key (rows past S only)
+          const float ca = __builtin_amdgcn_exp2f(m[qs] - mn), cb = __builtin_amdgcn_exp2f(mo - mn);
+          m[qs] = mn;
+          l[qs] = l[qs] * ca + ml[2 + qs] * cb;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            o[qs][db] = o[qs][db] * ca + *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) * cb;
+        }
       }
     }
+    if (grp > 0) return;
   }
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -323,7 +347,7 @@ __global__ __launch_bounds__(256) void attn_rowdot(int B, int S, int nh, const b
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, int KB>
 __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int nh, int nqb,
                                                              const bf16* __restrict__ qkv,
                                                              const bf16* __restrict__ dctx,
@@ -331,11 +355,13 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
                                                              const float* __restrict__ Dws,
                                                              bf16* __restrict__ dqkv) {
   using C = AC<D>;
-  constexpr int STG = 2 * C::TILE + 512;     // Q tile, dO tile, LSE[64], D[64]
+  constexpr int TILE = C::template tile<KB>();
+  constexpr int STG = 2 * TILE + 8 * KB;     // Q tile, dO tile, LSE[KB], D[KB]
   constexpr int SLOT = 64 * 4 * C::NDB * 16;  // one wave's partial (dK, dV) for the merge
-  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * 2 * STG, "merge slots exceed the tile memory");
+  static_assert(G == 1 || 2 * SLOT <= G * 2 * STG, "merge slots exceed the tile memory");
   __shared__ __attribute__((aligned(1024))) char smem[G * 2 * STG];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar registers
   const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int kb = idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;   // early keys see most queries
@@ -367,63 +393,68 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
   TP_LDS char* lds = (TP_LDS char*)smem + grp * 2 * STG;
   // the 64 threads of the group's first wave fill the LSE / D rows
   auto stage = [&](int qb, TP_LDS char* dst) {
-    const int q0 = qb * 64;
-    load_tile<D>(rows + (long)q0 * rs, rs, S - q0, dst, half, lane);
-    load_tile<D>(dorows + (long)q0 * cs, cs, S - q0, dst + C::TILE, half, lane);
-    if (half == 0) {
+    const int q0 = qb * KB;
+    load_tile<D, KB>(rows + (long)q0 * rs, rs, S - q0, dst, half, lane);
+    load_tile<D, KB>(dorows + (long)q0 * cs, cs, S - q0, dst + TILE, half, lane);
+    if (half == 0 && lane < KB) {
       const int q = q0 + lane;
-      ((TP_LDS float*)(dst + 2 * C::TILE))[lane] = q < S ? lse_bh[q] : INFINITY;
-      ((TP_LDS float*)(dst + 2 * C::TILE + 256))[lane] = q < S ? D_bh[q] : 0.f;
+      ((TP_LDS float*)(dst + 2 * TILE))[lane] = q < S ? lse_bh[q] : INFINITY;
+      ((TP_LDS float*)(dst + 2 * TILE + 4 * KB))[lane] = q < S ? D_bh[q] : 0.f;
     }
   };
-  const int nq = nqb - kb;                 // query blocks at or after this key block
+  const int jq0 = 64 * kb / KB;            // first query block that reaches this key block
+  const int nq = (S + KB - 1) / KB - jq0;
   const int nit = (nq + G - 1) / G;
-  if (grp < nq) stage(kb + grp, lds);
+  if (grp < nq) stage(jq0 + grp, lds);
   for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int j = it * G + grp, jn = j + G;
-    if (jn < nq) stage(kb + jn, lds + ((it + 1) & 1) * STG);
-    const int q0 = (kb + j) * 64;
-    if (j >= nq || q0 + 63 < kw) continue;   // no block, or every query precedes every key here
+    if (jn < nq) stage(jq0 + jn, lds + ((it + 1) & 1) * STG);
+    const int q0 = (jq0 + j) * KB;
+    if (j >= nq || q0 + KB - 1 < kw) continue;   // no block, or every query precedes every key here
     const TP_LDS char* qt = lds + (it & 1) * STG;
-    const TP_LDS char* dt = qt + C::TILE;
-    const TP_LDS float* Ls = (const TP_LDS float*)(qt + 2 * C::TILE);
-    const TP_LDS float* Ds = Ls + 64;
-    // P and dS for the 64 queries x this wave's 32 keys; lane: key kw + 16ks + i16,
-    // queries q0 + 16qsub + 4g + e
-    f32x4 p[4][2], ds[4][2];
+    const TP_LDS char* dt = qt + TILE;
+    const TP_LDS float* Ls = (const TP_LDS float*)(qt + 2 * TILE);
+    const TP_LDS float* Ds = Ls + KB;
+    // P and dS for the KB queries x this wave's 32 keys; lane: key kw + 16ks + i16,
+    // queries q0 + 16qsub + 4g + e.  Only blocks that reach below the diagonal need the causal mask
+    // (wave-uniform choice); keys past S need none, their rows of dK and dV are never stored.
+    f32x4 p[KB / 16][2], ds[KB / 16][2];
+    auto pds = [&](auto masked) {
 #pragma unroll
-    for (int qsub = 0; qsub < 4; ++qsub) {
-      bf16x8 qa[C::NKK], da[C::NKK];
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        qa[kk] = frag_row<D>(qt, 16 * qsub, 32 * kk, lane);
-        da[kk] = frag_row<D>(dt, 16 * qsub, 32 * kk, lane);
-      }
-      const f32x4 lq = *(const TP_LDS f32x4*)(Ls + 16 * qsub + 4 * g);
-      const f32x4 dq = *(const TP_LDS f32x4*)(Ds + 16 * qsub + 4 * g);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int qsub = 0; qsub < KB / 16; ++qsub) {
+        bf16x8 qa[C::NKK], da[C::NKK];
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) {
-          sa = mfma_16x16x32_bf16(qa[kk], kf[ks][kk], sa);
-          pa = mfma_16x16x32_bf16(da[kk], vf[ks][kk], pa);
+          qa[kk] = frag_row<D>(qt, 16 * qsub, 32 * kk, lane);
+          da[kk] = frag_row<D>(dt, 16 * qsub, 32 * kk, lane);
         }
-        const int key = kw + 16 * ks + i16;
+        const f32x4 lq = *(const TP_LDS f32x4*)(Ls + 16 * qsub + 4 * g);
+        const f32x4 dq = *(const TP_LDS f32x4*)(Ds + 16 * qsub + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = q0 + 16 * qsub + 4 * g + e;
-          float pv = __builtin_amdgcn_exp2f(sa[e] * c - lq[e] * LOG2E);
-          if (key > q) pv = 0.f;
-          p[qsub][ks][e] = pv;
-          ds[qsub][ks][e] = pv * (pa[e] - dq[e]);
+        for (int ks = 0; ks < 2; ++ks) {
+          f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < C::NKK; ++kk) {
+            sa = mfma_16x16x32_bf16(qa[kk], kf[ks][kk], sa);
+            pa = mfma_16x16x32_bf16(da[kk], vf[ks][kk], pa);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = __builtin_amdgcn_exp2f(fmaf(sa[e], c, -lq[e] * LOG2E));
+            if constexpr (decltype(masked)::value) {
+              if (kw + 16 * ks + i16 > q0 + 16 * qsub + 4 * g + e) pv = 0.f;
+            }
+            p[qsub][ks][e] = pv;
+            ds[qsub][ks][e] = pv * (pa[e] - dq[e]);
+          }
         }
       }
-    }
+    };
+    if (kw + 31 > q0) pds(std::true_type{}); else pds(std::false_type{});
 #pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
+    for (int qc = 0; qc < KB / 32; ++qc) {
       bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -444,32 +475,33 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
   }
 
   if constexpr (G > 1) {
-    // partial sums over each group's query blocks, added in group order by group 0
+    // partial sums over each group's query blocks, added in group order by group 0, one group per
+    // round through two wave slots of LDS
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (grp > 0) {
-      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          *(TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dk[ks][db];
-          *(TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dv[ks][db];
-        }
-    }
-    __syncthreads();
-    if (grp > 0) return;
-#pragma unroll
+    TP_LDS char* slot = (TP_LDS char*)smem + half * SLOT;
     for (int gg = 1; gg < G; ++gg) {
-      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
+      __syncthreads();
+      if (grp == gg) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          dk[ks][db] += *(const TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
-          dv[ks][db] += *(const TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
-        }
+          for (int db = 0; db < C::NDB; ++db) {
+            *(TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dk[ks][db];
+            *(TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16) = dv[ks][db];
+          }
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            dk[ks][db] += *(const TP_LDS f32x4*)(slot + (((0 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
+            dv[ks][db] += *(const TP_LDS f32x4*)(slot + (((1 * 2 + ks) * C::NDB + db) * 64 + lane) * 16);
+          }
+      }
     }
+    if (grp > 0) return;
   }
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
@@ -489,7 +521,7 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, int KB>
 __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh, int nqb,
                                                             const bf16* __restrict__ qkv,
                                                             const bf16* __restrict__ dctx,
@@ -497,11 +529,13 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
                                                             const float* __restrict__ Dws,
                                                             bf16* __restrict__ dqkv) {
   using C = AC<D>;
-  constexpr int GST = 2 * 2 * C::TILE;       // per group: two stages of (K tile, V tile)
+  constexpr int TILE = C::template tile<KB>();
+  constexpr int GST = 2 * 2 * TILE;          // per group: two stages of (K tile, V tile)
   constexpr int SLOT = 64 * 2 * C::NDB * 16;  // one wave's partial dQ for the merge
-  static_assert(G == 1 || (G - 1) * 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
+  static_assert(G == 1 || 2 * SLOT <= G * GST, "merge slots exceed the tile memory");
   __shared__ __attribute__((aligned(1024))) char smem[G * GST];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, i16 = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar registers
   const int half = w & 1, grp = w >> 1;
   const int nbh = nh * B, idx = blockIdx.x;
   const int qb = nqb - 1 - idx / nbh, h = (idx % nbh) % nh, b = (idx % nbh) / nh;
@@ -530,55 +564,60 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) acc[qs][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int nkb = min((S + 63) / 64, qb + 1);
+  const int nkb = min((S + KB - 1) / KB, (64 * qb + 63) / KB + 1);   // key blocks up to the diagonal
   const int nit = (nkb + G - 1) / G;
   TP_LDS char* lds = (TP_LDS char*)smem + grp * GST;
   if (grp < nkb) {
-    load_tile<D>(rows + (long)grp * 64 * rs + D, rs, S - grp * 64, lds, half, lane);
-    load_tile<D>(rows + (long)grp * 64 * rs + 2 * D, rs, S - grp * 64, lds + C::TILE, half, lane);
+    load_tile<D, KB>(rows + (long)grp * KB * rs + D, rs, S - grp * KB, lds, half, lane);
+    load_tile<D, KB>(rows + (long)grp * KB * rs + 2 * D, rs, S - grp * KB, lds + TILE, half, lane);
   }
   for (int it = 0; it < nit; ++it) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int j = it * G + grp, jn = j + G;
     if (jn < nkb) {
-      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * C::TILE;
-      load_tile<D>(rows + (long)jn * 64 * rs + D, rs, S - jn * 64, nx, half, lane);
-      load_tile<D>(rows + (long)jn * 64 * rs + 2 * D, rs, S - jn * 64, nx + C::TILE, half, lane);
+      TP_LDS char* nx = lds + ((it + 1) & 1) * 2 * TILE;
+      load_tile<D, KB>(rows + (long)jn * KB * rs + D, rs, S - jn * KB, nx, half, lane);
+      load_tile<D, KB>(rows + (long)jn * KB * rs + 2 * D, rs, S - jn * KB, nx + TILE, half, lane);
     }
-    const int k0 = 64 * j;
+    const int k0 = KB * j;
     if (j >= nkb || k0 > qw + 31) continue;
-    const TP_LDS char* kt = lds + (it & 1) * 2 * C::TILE;
-    const TP_LDS char* vt = kt + C::TILE;
-    f32x4 dsv[2][4];
+    const TP_LDS char* kt = lds + (it & 1) * 2 * TILE;
+    const TP_LDS char* vt = kt + TILE;
+    f32x4 dsv[2][KB / 16];
+    // dS = P∘(dP − D) in the query-owned layout; the causal / ragged mask only on blocks that need it
+    auto dsblock = [&](auto masked) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 kfr[C::NKK], vfr[C::NKK];
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        kfr[kk] = frag_row<D>(kt, 16 * kb, 32 * kk, lane);
-        vfr[kk] = frag_row<D>(vt, 16 * kb, 32 * kk, lane);
-      }
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KB / 16; ++kb) {
+        bf16x8 kfr[C::NKK], vfr[C::NKK];
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) {
-          sa = mfma_16x16x32_bf16(kfr[kk], qf[qs][kk], sa);
-          pa = mfma_16x16x32_bf16(vfr[kk], df[qs][kk], pa);
+          kfr[kk] = frag_row<D>(kt, 16 * kb, 32 * kk, lane);
+          vfr[kk] = frag_row<D>(vt, 16 * kb, 32 * kk, lane);
         }
-        const int q = qw + 16 * qs + i16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + 16 * kb + 4 * g + e;
-          float pv = __builtin_amdgcn_exp2f(sa[e] * c - lq[qs]);
-          if (key > q || key >= S) pv = 0.f;
-          dsv[qs][kb][e] = pv * (pa[e] - dq_[qs]);
+        for (int qs = 0; qs < 2; ++qs) {
+          f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < C::NKK; ++kk) {
+            sa = mfma_16x16x32_bf16(kfr[kk], qf[qs][kk], sa);
+            pa = mfma_16x16x32_bf16(vfr[kk], df[qs][kk], pa);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = __builtin_amdgcn_exp2f(fmaf(sa[e], c, -lq[qs]));
+            if constexpr (decltype(masked)::value) {
+              const int q = qw + 16 * qs + i16, key = k0 + 16 * kb + 4 * g + e;
+              if (key > q || key >= S) pv = 0.f;
+            }
+            dsv[qs][kb][e] = pv * (pa[e] - dq_[qs]);
+          }
         }
       }
-    }
+    };
+    if ((k0 + KB - 1 > qw) || (k0 + KB > S)) dsblock(std::true_type{}); else dsblock(std::false_type{});
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KB / 32; ++kc) {
       bf16x8 sf[2];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) sf[qs] = pack8(dsv[qs][2 * kc], dsv[qs][2 * kc + 1]);
@@ -593,26 +632,26 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
 
   if constexpr (G > 1) {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (grp > 0) {
-      TP_LDS char* slot = (TP_LDS char*)smem + ((grp - 1) * 2 + half) * SLOT;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = acc[qs][db];
-    }
-    __syncthreads();
-    if (grp > 0) return;
-#pragma unroll
+    TP_LDS char* slot = (TP_LDS char*)smem + half * SLOT;
     for (int gg = 1; gg < G; ++gg) {
-      const TP_LDS char* slot = (const TP_LDS char*)smem + ((gg - 1) * 2 + half) * SLOT;
+      __syncthreads();
+      if (grp == gg) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
+        for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          acc[qs][db] += *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16);
+          for (int db = 0; db < C::NDB; ++db)
+            *(TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16) = acc[qs][db];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            acc[qs][db] += *(const TP_LDS f32x4*)(slot + ((qs * C::NDB + db) * 64 + lane) * 16);
+      }
     }
+    if (grp > 0) return;
   }
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
@@ -628,29 +667,40 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
   }
 }
 
-// Groups per workgroup: as many as keep the tiles within 128 KiB of LDS, at most 4.
+// Launch shape: G wave-pair groups per workgroup and KB-row blocks of the looped-over dimension,
+// chosen so that the double-buffered tiles of all groups take at most 128 KiB of LDS.
+#ifndef TP_ATTN_G
+#define TP_ATTN_G 0
+#endif
+#ifndef TP_ATTN_KB
+#define TP_ATTN_KB 0
+#endif
 template <int D>
-constexpr int attn_groups() { return AC<D>::TILE >= 16384 ? 2 : 4; }
+struct AttnShape {
+  static constexpr int KB = TP_ATTN_KB ? TP_ATTN_KB : 64;
+  static constexpr int G = TP_ATTN_G ? TP_ATTN_G
+                                     : (4 * AC<D>::template tile<KB>() >= 65536 ? 2 : 4);
+};
 
 template <int D>
 hipError_t fwd_t(int B, int S, int nh, const void* qkv, void* ctx, float* lse, hipStream_t s) {
-  constexpr int G = attn_groups<D>();
+  constexpr int G = AttnShape<D>::G, KB = AttnShape<D>::KB;
   const int nqb = (S + 63) / 64;
-  attn_fwd_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
+  attn_fwd_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_t(int B, int S, int nh, const void* qkv, const void* ctx, const float* lse,
                  const void* dctx, void* dqkv, float* ws, hipStream_t s) {
+  constexpr int G = AttnShape<D>::G, KB = AttnShape<D>::KB;
   const int nqb = (S + 63) / 64;
   const long rows = (long)B * S * nh;
   attn_rowdot<D><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
-  constexpr int G = attn_groups<D>();
-  attn_bwd_dkv_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
-                                                           (const bf16*)dctx, lse, ws, (bf16*)dqkv);
-  attn_bwd_dq_mfma<D, G><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
-                                                          (const bf16*)dctx, lse, ws, (bf16*)dqkv);
+  attn_bwd_dkv_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
+                                                               (const bf16*)dctx, lse, ws, (bf16*)dqkv);
+  attn_bwd_dq_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
+                                                              (const bf16*)dctx, lse, ws, (bf16*)dqkv);
   return hipGetLastError();
 }
 
