@@ -3,9 +3,10 @@
 //
 // The row offsets live on the device (routing happened there), so the host never sees the group
 // sizes.  A one-workgroup plan kernel sanitises the offsets (clamped to [0, rows], made
-// non-decreasing, so no later access can leave the buffers) and numbers the BM-row tiles of all
-// experts (prefix[e] = Σ_{j<e} ceil(rows_j / BM)); the grouped GEMM kernels launch an upper bound of
-// ceil(rows / BM) + groups m-tiles and find their expert by binary search in prefix[].
+// non-decreasing, so no later access can leave the buffers) and numbers the row tiles of all
+// experts for each of the two GEMMs' tile heights (prefix[e] = Σ_{j<e} ceil(rows_j / BM)); the
+// grouped GEMM kernels launch an upper bound of ceil(rows / BM) + groups m-tiles and find their
+// expert by binary search in prefix[].
 #include <cstring>
 
 #include "common.h"
@@ -18,7 +19,7 @@ hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int
                                     long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
 hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
                                        long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
-int gemm_bf16_grouped_bm();
+int gemm_bf16_grouped_bm(int K);
 int gemm_generic_grouped_bm();
 bool gemm_bf16_eligible(const GemmDesc& d);
 
@@ -27,14 +28,17 @@ namespace {
 constexpr int PLAN_CHUNK = 1024;
 
 __global__ __launch_bounds__(256) void grouped_plan_kernel(const int* __restrict__ off_in, int groups,
-                                                           int rows, int bm, int* __restrict__ off_out,
-                                                           int* __restrict__ prefix) {
+                                                           int rows, int bm1, int bm2,
+                                                           int* __restrict__ off_out,
+                                                           int* __restrict__ prefix1,
+                                                           int* __restrict__ prefix2) {
   __shared__ int so[PLAN_CHUNK];
-  int prev = 0, p = 0;
+  int prev = 0, p1 = 0, p2 = 0;
   if (threadIdx.x == 0) {
     prev = min(max(off_in[0], 0), rows);
     off_out[0] = prev;
-    prefix[0] = 0;
+    prefix1[0] = 0;
+    prefix2[0] = 0;
   }
   for (int c0 = 0; c0 < groups; c0 += PLAN_CHUNK) {
     const int n = min(PLAN_CHUNK, groups - c0);
@@ -45,8 +49,10 @@ __global__ __launch_bounds__(256) void grouped_plan_kernel(const int* __restrict
       for (int i = 0; i < n; ++i) {
         const int o = min(max(so[i], prev), rows);
         off_out[c0 + 1 + i] = o;
-        p += (o - prev + bm - 1) / bm;
-        prefix[c0 + 1 + i] = p;
+        p1 += (o - prev + bm1 - 1) / bm1;
+        p2 += (o - prev + bm2 - 1) / bm2;
+        prefix1[c0 + 1 + i] = p1;
+        prefix2[c0 + 1 + i] = p2;
         prev = o;
       }
     }
@@ -55,14 +61,15 @@ __global__ __launch_bounds__(256) void grouped_plan_kernel(const int* __restrict
 
 }  // namespace
 
-size_t grouped_ws_bytes(int groups) { return (size_t)2 * (groups + 1) * sizeof(int); }
+size_t grouped_ws_bytes(int groups) { return (size_t)3 * (groups + 1) * sizeof(int); }
 
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
                               void* A1, void* Y, void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   int* off_s = (int*)ws;
-  int* prefix = off_s + (groups + 1);
+  int* prefix1 = off_s + (groups + 1);       // m-tiles of fc1's tile height
+  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of fc2's
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
 
   GemmDesc fc1;
@@ -80,12 +87,13 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   // Each expert's slice is a plain row-major problem with the same leading dimensions, so the tiled
   // kernel's alignment rules are those of the whole matrices.
   const bool tiled = gemm_bf16_eligible(fc1) && gemm_bf16_eligible(fc2);
-  const int bm = tiled ? gemm_bf16_grouped_bm() : gemm_generic_grouped_bm();
-  const long maxmt = (long)(rows + bm - 1) / bm + groups;
-  if (maxmt > 0x7fffffffL) return hipErrorInvalidValue;
+  const int bm1 = tiled ? gemm_bf16_grouped_bm(fc1.K) : gemm_generic_grouped_bm();
+  const int bm2 = tiled ? gemm_bf16_grouped_bm(fc2.K) : gemm_generic_grouped_bm();
+  const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
+  if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
   {
-    ProfScope p("grouped_plan", s, 0.0, 8.0 * (groups + 1));
-    grouped_plan_kernel<<<1, 256, 0, s>>>(off, groups, rows, bm, off_s, prefix);
+    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
+    grouped_plan_kernel<<<1, 256, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -95,19 +103,19 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   if (tiled) {
     {
       ProfScope p("gemm_bf16_grouped<fc1, bias+gelu>", s, f1, by1);
-      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix, groups, (long)H * Fr, Fr, (int)maxmt, s);
+      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
       if (e != hipSuccess) return e;
     }
     ProfScope p("gemm_bf16_grouped<fc2>", s, f1, by2);
-    return launch_gemm_bf16_grouped(fc2, off_s, prefix, groups, (long)Fr * H, 0, (int)maxmt, s);
+    return launch_gemm_bf16_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
   }
   {
     ProfScope p("gemm_generic_grouped<fc1, bias+gelu>", s, f1, by1);
-    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix, groups, (long)H * Fr, Fr, (int)maxmt, s);
+    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }
   ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
-  return launch_gemm_generic_grouped(fc2, off_s, prefix, groups, (long)Fr * H, 0, (int)maxmt, s);
+  return launch_gemm_generic_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
 }
 
 }  // namespace tp

@@ -1,6 +1,6 @@
 // Column sums over the token dimension (bias gradients): out[c] = Σ_r in[r, c].
 //
-// Deterministic two-pass reduction in fp32.  Pass 1: a workgroup owns a 256-column x 256-row block;
+// Deterministic two-pass reduction in fp32.  Pass 1: a workgroup owns a 256-column x 64-row block;
 // its 256 threads are 32 column groups (8 adjacent columns each, 16-byte loads, so a half-wave reads
 // 512 contiguous bytes of a row) x 8 row groups (rows r0 + g, r0 + g + 8, ...); the 8 row-group
 // sums meet in LDS in a fixed order and one fp32 partial per column and block row is written.
@@ -13,7 +13,7 @@ namespace tp {
 
 namespace {
 
-constexpr int CS_ROWS = 256;   // rows per partial
+constexpr int CS_ROWS = 64;    // rows per partial (enough workgroups to fill the chip at T = 2048)
 constexpr int CS_COLS = 256;   // columns per workgroup
 constexpr int CS_RG = 8;       // row groups per workgroup
 
