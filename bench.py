@@ -39,6 +39,7 @@ def parse():
                     help="tokens of the oracle's CPU sample (the first S of the sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped-shard measurement")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
                          "calibrated on), then --warmup + --steps steps, and nothing else")
@@ -257,6 +258,30 @@ def main():
     events = not args.no_kernel_events
     if events:
         ms_step_ev, _, kernels = timed(True)
+    # timed region 3: the same step captured once in a HIP graph and replayed (the entry points
+    # allocate and synchronise nothing, so capture is legal); reported beside the eager figure
+    ms_graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / args.steps
+        del graph
     fl = step_flops(T, S, B, H, Nq, nh, d, Fr)
     flop_step = sum(fl.values())
     tflops = flop_step / (ms_step * 1e-3) / 1e12
@@ -306,6 +331,8 @@ def main():
         "gflop_per_step": round(flop_step / 1e9, 1),
         "wall_s_timed_region": round(wall, 3),
         "ms_per_step_with_kernel_events": round(ms_step_ev, 4) if events else None,
+        "ms_per_step_graph_replay": round(ms_graph, 4) if ms_graph else None,
+        "tflops_graph_replay": round(flop_step / (ms_graph * 1e-3) / 1e12, 2) if ms_graph else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": breakdown,

@@ -4,7 +4,7 @@
 // its 256 threads are 32 column groups (8 adjacent columns each, 16-byte loads, so a half-wave reads
 // 512 contiguous bytes of a row) x 8 row groups (rows r0 + g, r0 + g + 8, ...); the 8 row-group
 // sums meet in LDS in a fixed order and one fp32 partial per column and block row is written.
-// Pass 2 adds the block-row partials of each column in order.  HBM-bound: the input is read once.
+// Pass 2 adds the block-row partials of each column in a fixed order.  HBM-bound: the input is read once.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -55,14 +55,19 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
   }
 }
 
+// Pass 2: 64 columns per workgroup; its four waves add every fourth partial of a column (chunks
+// g, g+4, ...), and the four sums meet in LDS in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ ws, int chunks,
                                                            int cols, T* __restrict__ out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float red[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63), g = threadIdx.x >> 6;
   float s = 0.f;
-  for (int k = 0; k < chunks; ++k) s += ws[(long)k * cols + c];
-  out[c] = from_f32<T>(s);
+  if (c < cols)
+    for (int k = g; k < chunks; k += 4) s += ws[(long)k * cols + c];
+  red[g][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (g == 0 && c < cols) out[c] = from_f32<T>(((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x]);
 }
 
 template <typename T>
@@ -72,7 +77,7 @@ hipError_t colsum_t(const void* in, long ld, int rows, int cols, float* ws, void
     dim3 grid((cols + CS_COLS - 1) / CS_COLS, chunks);
     colsum_partial_kernel<T><<<grid, 256, 0, s>>>((const T*)in, ld, rows, cols, ws);
   }
-  colsum_final_kernel<T><<<(cols + 255) / 256, 256, 0, s>>>(ws, chunks, cols, (T*)out);
+  colsum_final_kernel<T><<<(cols + 63) / 64, 256, 0, s>>>(ws, chunks, cols, (T*)out);
   return hipGetLastError();
 }
 
