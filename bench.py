@@ -72,6 +72,25 @@ def recorded_traffic(kernel):
         return None
 
 
+def kernel_roofline(n, ms, flop, byts, steps):
+    """Per-kernel figures from the library's per-launch events: the bound is MFMA when the kernel's
+    algorithmic flop per byte is above the ridge (2516.6 TFLOP/s / 8 TB/s), else HBM."""
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    out = {"launches_per_step": n / steps, "ms_per_step": round(ms / steps, 4),
+           "avg_launch_us": round(1e3 * ms / n, 2) if n else None}
+    if s <= 0:
+        return out
+    if flop / max(byts, 1.0) > ridge:
+        a = flop / s / 1e12
+        out.update(bound="mfma", achieved=round(a, 2), unit="TFLOP/s", frac=round(a / PEAK_BF16_TFLOPS, 4))
+    else:
+        a = byts / s / 1e9
+        out.update(bound="hbm", achieved=round(a, 1), unit="GB/s", frac=round(a / PEAK_HBM_GBS, 4))
+    out["tflops"] = round(flop / s / 1e12, 2)
+    return out
+
+
 def step_flops(T, S, B, H, Nq, nh, d, Fr):
     gemm_fwd = 2.0 * T * H * Nq + 2.0 * T * H * Fr + 2.0 * T * Fr * H
     pairs = B * nh * S * (S + 1) / 2.0
@@ -156,11 +175,19 @@ def moe_grouped(bd, torch, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    bd.tp_prof_enable(False)
+    kernels = {tag: kernel_roofline(n, kms, fl, by, steps) for tag, (n, kms, fl, by) in bd.tp_prof_collect().items()}
     flop = 4.0 * rows * H * Fr
     byts = 2.0 * (2 * rows * H + 2 * G * H * Fr + G * Fr + 2 * rows * Fr)
     out = {"workload": mw.name + "_rank0", "rows": rows, "ms": round(ms, 4),
            "tflops": round(flop / ms / 1e9, 2), "gb_per_s": round(byts / ms / 1e6, 1),
-           "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3)}
+           "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3),
+           "kernels": kernels}
     del Xp, W1, W2, Z, Y
     torch.cuda.empty_cache()
     return out
@@ -288,11 +315,7 @@ def main():
 
     roofline, breakdown = None, None
     if events:
-        breakdown = {}
-        for tag, (n, ms, flop, byts) in kernels.items():
-            breakdown[tag] = {"launches_per_step": n / args.steps, "ms_per_step": round(ms / args.steps, 4),
-                              "avg_launch_us": round(1e3 * ms / n, 2),
-                              "tflops": round(flop / (ms * 1e-3) / 1e12, 2) if ms > 0 else None}
+        breakdown = {tag: kernel_roofline(n, ms, flop, byts, args.steps) for tag, (n, ms, flop, byts) in kernels.items()}
         dom = max(kernels, key=lambda k: kernels[k][1])
         n, ms, flop, byts = kernels[dom]
         ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)      # flop per byte

@@ -27,8 +27,13 @@
  *    owns every buffer; the library never allocates, frees or keeps a pointer after returning.
  *  - `dtype`: TP_BF16 (bf16 in/out, fp32 accumulation and fp32 softmax/GeLU) or TP_F32 (fp32
  *    throughout: the check mode).  Every output has that type except LSE and workspace, fp32.
- *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it; calls return
- *    without synchronising.  Outputs are overwritten (never accumulated into).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is ordered on it; calls return
+ *    without synchronising.  Outputs are overwritten (never accumulated into).  The two backward
+ *    calls with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd) may run some of them on a
+ *    library-owned side stream of the current device (created once, outside graph capture, default
+ *    priority), forked from and joined back into `stream` with events before they return: to the
+ *    caller the effect is the same as if everything ran on `stream`, and a captured graph simply
+ *    gets two branches.  While per-launch timing is on, everything runs on `stream`.
  *  - Errors: arguments are validated on the host before any launch; a negative tp_status is
  *    returned and nothing is enqueued.  A failed launch returns TP_EHIP; tp_last_error() then holds
  *    the HIP message for the calling thread.  Faults inside kernels surface at the caller's next

@@ -5,9 +5,11 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "tpshard.h"
 #include "kernels.h"
+#include "prof.h"
 
 using namespace tp;
 
@@ -41,6 +43,41 @@ int hip_status(hipError_t e, const char* where) {
       return (code);                                 \
     }                                                \
   } while (0)
+
+// A per-device side stream for launches that do not depend on each other inside one call: the
+// caller's stream forks onto it through an event and joins back before the call returns, so the
+// caller still sees one ordered stream (and a captured graph gets two branches).  The side stream and
+// its events are created on first use outside graph capture and live until the process ends; the
+// mutex serialises the enqueue phase of calls that use them.  Without them, everything runs on the
+// caller's stream.
+struct Side {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+Side g_side[64];
+
+Side* side_stream(hipStream_t s) {
+  if (prof_enabled()) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  Side& sd = g_side[dev];
+  if (sd.s2) return &sd;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+  Side n;
+  if (hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&n.mid, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+    for (hipEvent_t e : {n.fork, n.mid, n.join})
+      if (e) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(n.s2);
+    return nullptr;
+  }
+  sd = n;
+  return &sd;
+}
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t esize(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
@@ -104,10 +141,10 @@ int mlp_geom(int tp_size, int rank, int T, int H, int F, int dtype, MlpGeom* g) 
     TP_CHECK((p) == nullptr || aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name)); \
   } while (0)
 
+// dA1, then the db1 and db2 column-sum partials (separate: the two sums may run concurrently)
 size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
-  const size_t cs = colsum_ws_bytes(T, Fr) > colsum_ws_bytes(T, H) ? colsum_ws_bytes(T, Fr)
-                                                                   : colsum_ws_bytes(T, H);
-  return align256((size_t)T * Fr * esize(dtype)) + align256(cs);
+  return align256((size_t)T * Fr * esize(dtype)) + align256(colsum_ws_bytes(T, Fr)) +
+         align256(colsum_ws_bytes(T, H));
 }
 
 size_t qkv_bwd_ws(int T, int Nq) { return align256(colsum_ws_bytes(T, Nq)); }
@@ -200,25 +237,45 @@ int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
   hipStream_t s = (hipStream_t)stream;
   const int Fr = g.Fr;
   void* dA1 = workspace;
-  float* cs = (float*)((char*)workspace + align256((size_t)T * Fr * esize(dtype)));
+  float* cs1 = (float*)((char*)workspace + align256((size_t)T * Fr * esize(dtype)));
+  float* cs2 = (float*)((char*)cs1 + align256(colsum_ws_bytes(T, Fr)));
 
   // dW2_r = Y_rᵀ·dZ   (M = F_r, N = H, K = T)
   GemmDesc g1 = gemm_desc(dtype, Fr, H, T, Y_r, Fr, false, dZ, H, false, dW2_r, H, EPI_STORE);
-  TP_TRY(launch_gemm(g1, s), "dW2 gemm");
   // dA1 = (dZ·W2_rᵀ) ∘ GeLU'(A1_r)   (M = T, N = F_r, K = H)
   GemmDesc g2 = gemm_desc(dtype, T, Fr, H, dZ, H, true, W2_r, H, true, dA1, Fr, EPI_DGELU);
   g2.aux = A1_r;
   g2.ld_aux = Fr;
-  TP_TRY(launch_gemm(g2, s), "dA1 gemm");
-  TP_TRY(launch_colsum(dtype, dA1, Fr, T, Fr, cs, db1_r, s), "db1 colsum");
   // dW1_r = Xᵀ·dA1   (M = H, N = F_r, K = T)
   GemmDesc g3 = gemm_desc(dtype, H, Fr, T, X, H, false, dA1, Fr, false, dW1_r, Fr, EPI_STORE);
-  TP_TRY(launch_gemm(g3, s), "dW1 gemm");
   // dX_r = dA1·W1_rᵀ   (M = T, N = H, K = F_r)
   GemmDesc g4 = gemm_desc(dtype, T, H, Fr, dA1, Fr, true, W1_r, Fr, true, dX_r, H, EPI_STORE);
-  TP_TRY(launch_gemm(g4, s), "dX gemm");
-  if (rank == 0 && db2 != nullptr) TP_TRY(launch_colsum(dtype, dZ, H, T, H, cs, db2, s), "db2 colsum");
-  return TP_OK;
+
+  // caller's stream: dA1 -> db1, dW1;  side stream: dW2, db2, then (after dA1) dX
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = side_stream(s);
+  hipStream_t s2 = sd ? sd->s2 : s;
+  if (sd) {
+    TP_TRY(hipEventRecord(sd->fork, s), "fork");
+    TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
+  }
+  auto body = [&]() -> int {
+    TP_TRY(launch_gemm(g2, s), "dA1 gemm");
+    if (sd) TP_TRY(hipEventRecord(sd->mid, s), "dA1 event");
+    TP_TRY(launch_gemm(g1, s2), "dW2 gemm");
+    if (rank == 0 && db2 != nullptr) TP_TRY(launch_colsum(dtype, dZ, H, T, H, cs2, db2, s2), "db2 colsum");
+    if (sd) TP_TRY(hipStreamWaitEvent(s2, sd->mid, 0), "dA1 wait");
+    TP_TRY(launch_gemm(g4, s2), "dX gemm");
+    TP_TRY(launch_colsum(dtype, dA1, Fr, T, Fr, cs1, db1_r, s), "db1 colsum");
+    TP_TRY(launch_gemm(g3, s), "dW1 gemm");
+    return TP_OK;
+  };
+  const int rc = body();
+  if (sd) {   // join even after a failed launch, so the side stream never runs ahead of the caller's
+    TP_TRY(hipEventRecord(sd->join, s2), "join");
+    TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
+  }
+  return rc;
 }
 
 int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
@@ -237,12 +294,29 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
   hipStream_t s = (hipStream_t)stream;
   // dWqkv_r = Xᵀ·dQKV_r   (M = H, N = Nq, K = T)
   GemmDesc g1 = gemm_desc(dtype, H, g.Nq, g.T, X, H, false, dQKV_r, g.Nq, false, dWqkv_r, g.Nq, EPI_STORE);
-  TP_TRY(launch_gemm(g1, s), "dWqkv gemm");
-  TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, (float*)workspace, dbqkv_r, s), "dbqkv colsum");
   // dX_r = dQKV_r·Wqkv_rᵀ   (M = T, N = H, K = Nq)
   GemmDesc g2 = gemm_desc(dtype, g.T, H, g.Nq, dQKV_r, g.Nq, true, Wqkv_r, g.Nq, true, dX_r, H, EPI_STORE);
-  TP_TRY(launch_gemm(g2, s), "dX gemm");
-  return TP_OK;
+
+  // caller's stream: dWqkv;  side stream: dbqkv, dX (all three independent)
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = side_stream(s);
+  hipStream_t s2 = sd ? sd->s2 : s;
+  if (sd) {
+    TP_TRY(hipEventRecord(sd->fork, s), "fork");
+    TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
+  }
+  auto body = [&]() -> int {
+    TP_TRY(launch_gemm(g1, s), "dWqkv gemm");
+    TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, (float*)workspace, dbqkv_r, s2), "dbqkv colsum");
+    TP_TRY(launch_gemm(g2, s2), "dX gemm");
+    return TP_OK;
+  };
+  const int rc = body();
+  if (sd) {
+    TP_TRY(hipEventRecord(sd->join, s2), "join");
+    TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
+  }
+  return rc;
 }
 
 int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
