@@ -420,47 +420,51 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
     // P and dS for the KB queries x this wave's 32 keys; lane: key kw + 16ks + i16,
     // queries q0 + 16qsub + 4g + e.  Only blocks that reach below the diagonal need the causal mask
     // (wave-uniform choice); keys past S need none, their rows of dK and dV are never stored.
-    f32x4 p[KB / 16][2], ds[KB / 16][2];
-    auto pds = [&](auto masked) {
-#pragma unroll
-      for (int qsub = 0; qsub < KB / 16; ++qsub) {
-        bf16x8 qa[C::NKK], da[C::NKK];
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
-          qa[kk] = frag_row<D>(qt, 16 * qsub, 32 * kk, lane);
-          da[kk] = frag_row<D>(dt, 16 * qsub, 32 * kk, lane);
-        }
-        const f32x4 lq = *(const TP_LDS f32x4*)(Ls + 16 * qsub + 4 * g);
-        const f32x4 dq = *(const TP_LDS f32x4*)(Ds + 16 * qsub + 4 * g);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < C::NKK; ++kk) {
-            sa = mfma_16x16x32_bf16(qa[kk], kf[ks][kk], sa);
-            pa = mfma_16x16x32_bf16(da[kk], vf[ks][kk], pa);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pv = __builtin_amdgcn_exp2f(fmaf(sa[e], c, -lq[e] * LOG2E));
-            if constexpr (decltype(masked)::value) {
-              if (kw + 16 * ks + i16 > q0 + 16 * qsub + 4 * g + e) pv = 0.f;
-            }
-            p[qsub][ks][e] = pv;
-            ds[qsub][ks][e] = pv * (pa[e] - dq[e]);
-          }
-        }
-      }
-    };
-    if (kw + 31 > q0) pds(std::true_type{}); else pds(std::false_type{});
+    // One 32-query chunk at a time: P and dS of its two 16-query slices are packed to bf16 right
+    // away and consumed by the dV / dK MFMAs, so only one chunk's P and dS are ever live.
 #pragma unroll
     for (int qc = 0; qc < KB / 32; ++qc) {
       bf16x8 pf[2], sf[2];
+      auto pds = [&](auto masked) {
+        f32x4 p[2][2], ds[2][2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pf[ks] = pack8(p[2 * qc][ks], p[2 * qc + 1][ks]);
-        sf[ks] = pack8(ds[2 * qc][ks], ds[2 * qc + 1][ks]);
-      }
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int qsub = 2 * qc + h2;
+          bf16x8 qa[C::NKK], da[C::NKK];
+#pragma unroll
+          for (int kk = 0; kk < C::NKK; ++kk) {
+            qa[kk] = frag_row<D>(qt, 16 * qsub, 32 * kk, lane);
+            da[kk] = frag_row<D>(dt, 16 * qsub, 32 * kk, lane);
+          }
+          const f32x4 lq = *(const TP_LDS f32x4*)(Ls + 16 * qsub + 4 * g);
+          const f32x4 dq = *(const TP_LDS f32x4*)(Ds + 16 * qsub + 4 * g);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            f32x4 sa = (f32x4){0.f, 0.f, 0.f, 0.f}, pa = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; ++kk) {
+              sa = mfma_16x16x32_bf16(qa[kk], kf[ks][kk], sa);
+              pa = mfma_16x16x32_bf16(da[kk], vf[ks][kk], pa);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pv = __builtin_amdgcn_exp2f(fmaf(sa[e], c, -lq[e] * LOG2E));
+              if constexpr (decltype(masked)::value) {
+                if (kw + 16 * ks + i16 > q0 + 16 * qsub + 4 * g + e) pv = 0.f;
+              }
+              p[h2][ks][e] = pv;
+              ds[h2][ks][e] = pv * (pa[e] - dq[e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          pf[ks] = pack8(p[0][ks], p[1][ks]);
+          sf[ks] = pack8(ds[0][ks], ds[1][ks]);
+        }
+      };
+      // the causal mask only where a key of this wave can follow a query of this chunk
+      if (kw + 31 > q0 + 32 * qc) pds(std::true_type{}); else pds(std::false_type{});
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
         const bf16x8 doT = frag_tr<D>(dt, 32 * qc, 16 * db, lane);
