@@ -33,7 +33,8 @@
  *    library-owned side stream of the current device (created once, outside graph capture, default
  *    priority), forked from and joined back into `stream` with events before they return: to the
  *    caller the effect is the same as if everything ran on `stream`, and a captured graph simply
- *    gets two branches.  While per-launch timing is on, everything runs on `stream`.
+ *    gets two branches.  While per-launch timing is on, or when the environment variable TP_SERIAL is
+ *    set to a non-zero value, everything runs on `stream`.
  *  - Errors: arguments are validated on the host before any launch; a negative tp_status is
  *    returned and nothing is enqueued.  A failed launch returns TP_EHIP; tp_last_error() then holds
  *    the HIP message for the calling thread.  Faults inside kernels surface at the caller's next

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -58,7 +59,11 @@ std::mutex g_side_mu;
 Side g_side[64];
 
 Side* side_stream(hipStream_t s) {
-  if (prof_enabled()) return nullptr;
+  static const bool serial = [] {
+    const char* v = getenv("TP_SERIAL");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  if (serial || prof_enabled()) return nullptr;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   Side& sd = g_side[dev];
