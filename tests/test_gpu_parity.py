@@ -171,9 +171,10 @@ def test_attn_bwd(wl, dtype, rank, qkv_std):
 # ---- the whole shard, chained --------------------------------------------------------------------
 
 @pytest.mark.parametrize("wl,dtype,rank", list(cases()))
-def test_chain(wl, dtype, rank):
+def test_chain(wl, dtype, rank, lse_tol=None):
     """QKV -> attention -> MLP forward, then MLP, attention and QKV backward, all on the GPU, each
-    stage fed the previous stage's device output; the oracle runs the same chain in fp64."""
+    stage fed the previous stage's device output; the oracle runs the same chain in fp64.
+    lse_tol overrides the LSE bound (see the single-token case)."""
     sh = Shard(wl, rank, dtype)
     t, B, S, H, nh, F = wl.tp_size, wl.B, wl.S, wl.H, wl.n_heads, wl.F
     qkv = run_qkv_fwd(sh)
@@ -197,7 +198,9 @@ def test_chain(wl, dtype, rank):
              (q["dX"], Rq["dX"], "qkv dX"), (q["dW"], Rq["dW"], "dWqkv"), (q["db"], Rq["db"], "dbqkv")]
     for got, ref, what in pairs:
         assert_close(got, ref, dtype, what)
-    assert_close(lse, R_lse, dtype, "lse", tol=1e-5 if dtype == "f32" else 2e-3)
+    if lse_tol is None:
+        lse_tol = 1e-5 if dtype == "f32" else 2e-3
+    assert_close(lse, R_lse, dtype, "lse", tol=lse_tol)
 
 
 # ---- sharding identity on the GPU ---------------------------------------------------------------
