@@ -88,6 +88,27 @@ def _ptr(t, name, dtype=None, allow_none=False):
     return t.data_ptr()
 
 
+def _need(t, n, name):
+    """The library takes raw pointers and cannot see buffer sizes: refuse a tensor with fewer
+    elements than the call will touch, before anything is launched."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, the call needs {n}")
+
+
+def _heads(tp_size, rank, H, n_heads):
+    """(heads on this rank, head width) when the geometry is well formed, else None (the library
+    then rejects the call with its own message)."""
+    if not (1 <= tp_size and 0 <= rank < tp_size and n_heads >= tp_size and H >= 1 and H % n_heads == 0):
+        return None
+    return tp_shard_range(n_heads, tp_size, rank)[1], H // n_heads
+
+
+def _cols(tp_size, rank, F):
+    if not (1 <= tp_size and 0 <= rank < tp_size and F >= tp_size):
+        return None
+    return tp_shard_range(F, tp_size, rank)[1]
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -106,6 +127,11 @@ def tp_workspace_bytes(fn, tp_size, rank, B, S, H, n_heads, F, dtype):
 
 def tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, bqkv_r, QKV_r, stream=None):
     dt = X.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, Nq = B * S, 3 * g[0] * g[1]
+        for t, n, name in ((X, T * H, "X"), (Wqkv_r, H * Nq, "Wqkv_r"), (bqkv_r, Nq, "bqkv_r"), (QKV_r, T * Nq, "QKV_r")):
+            _need(t, n, name)
     rc = raw().tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, _dtype_code(X), _ptr(X, "X", dt),
                                 _ptr(Wqkv_r, "Wqkv_r", dt), _ptr(bqkv_r, "bqkv_r", dt),
                                 _ptr(QKV_r, "QKV_r", dt), _stream(stream))
@@ -114,6 +140,11 @@ def tp_qkv_shard_fwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, bqkv_r, QKV_r, 
 
 def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r=None, stream=None):
     dt = QKV_r.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, nh, d = B * S, g[0], g[1]
+        for t, n, name in ((QKV_r, T * 3 * nh * d, "QKV_r"), (ctx_r, T * nh * d, "ctx_r"), (lse_r, B * nh * S, "lse_r")):
+            _need(t, n, name)
     rc = raw().tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, _dtype_code(QKV_r),
                                  _ptr(QKV_r, "QKV_r", dt), _ptr(ctx_r, "ctx_r", dt),
                                  _ptr(lse_r, "lse_r", torch.float32, True), _stream(stream))
@@ -122,6 +153,11 @@ def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r=None,
 
 def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r, Y_r, stream=None):
     dt = X.dtype
+    Fr = _cols(tp_size, rank, F)
+    if Fr and T >= 0 and H >= 1:
+        for t, n, name in ((X, T * H, "X"), (W1_r, H * Fr, "W1_r"), (b1_r, Fr, "b1_r"), (W2_r, Fr * H, "W2_r"),
+                           (b2, H, "b2"), (Z_r, T * H, "Z_r"), (A1_r, T * Fr, "A1_r"), (Y_r, T * Fr, "Y_r")):
+            _need(t, n, name)
     rc = raw().tp_mlp_shard_fwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
                                 _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),
                                 _ptr(W2_r, "W2_r", dt), _ptr(b2, "b2", dt, True),
@@ -133,6 +169,12 @@ def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r,
 def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r, dW1_r, db1_r,
                      dW2_r, db2, workspace, stream=None):
     dt = X.dtype
+    Fr = _cols(tp_size, rank, F)
+    if Fr and T >= 0 and H >= 1:
+        for t, n, name in ((X, T * H, "X"), (W1_r, H * Fr, "W1_r"), (W2_r, Fr * H, "W2_r"), (A1_r, T * Fr, "A1_r"),
+                           (Y_r, T * Fr, "Y_r"), (dZ, T * H, "dZ"), (dX_r, T * H, "dX_r"), (dW1_r, H * Fr, "dW1_r"),
+                           (db1_r, Fr, "db1_r"), (dW2_r, Fr * H, "dW2_r"), (db2, H, "db2")):
+            _need(t, n, name)
     rc = raw().tp_mlp_shard_bwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
                                 _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
                                 _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(dZ, "dZ", dt),
@@ -147,6 +189,12 @@ def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r,
 def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r,
                      workspace, stream=None):
     dt = X.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, Nq = B * S, 3 * g[0] * g[1]
+        for t, n, name in ((X, T * H, "X"), (Wqkv_r, H * Nq, "Wqkv_r"), (dQKV_r, T * Nq, "dQKV_r"),
+                           (dX_r, T * H, "dX_r"), (dWqkv_r, H * Nq, "dWqkv_r"), (dbqkv_r, Nq, "dbqkv_r")):
+            _need(t, n, name)
     rc = raw().tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, _dtype_code(X), _ptr(X, "X", dt),
                                 _ptr(Wqkv_r, "Wqkv_r", dt), _ptr(dQKV_r, "dQKV_r", dt),
                                 _ptr(dX_r, "dX_r", dt), _ptr(dWqkv_r, "dWqkv_r", dt),
@@ -159,6 +207,12 @@ def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, d
 def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,
                       workspace, stream=None):
     dt = QKV_r.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, nh, d = B * S, g[0], g[1]
+        for t, n, name in ((QKV_r, T * 3 * nh * d, "QKV_r"), (ctx_r, T * nh * d, "ctx_r"), (lse_r, B * nh * S, "lse_r"),
+                           (dctx_r, T * nh * d, "dctx_r"), (dQKV_r, T * 3 * nh * d, "dQKV_r")):
+            _need(t, n, name)
     rc = raw().tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, _dtype_code(QKV_r),
                                  _ptr(QKV_r, "QKV_r", dt), _ptr(ctx_r, "ctx_r", dt),
                                  _ptr(lse_r, "lse_r", torch.float32), _ptr(dctx_r, "dctx_r", dt),
@@ -171,6 +225,13 @@ def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx
 def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_group, X_perm, W1_r,
                              b1_r, W2_r, Z_r, A1_r, Y_r, workspace, stream=None):
     dt = X_perm.dtype
+    Fr = _cols(tp_size, rank, F_group)
+    if Fr and rows >= 0 and H >= 1 and n_groups >= 1:
+        G = n_groups
+        for t, n, name in ((group_offsets, G + 1, "group_offsets"), (X_perm, rows * H, "X_perm"),
+                           (W1_r, G * H * Fr, "W1_r"), (b1_r, G * Fr, "b1_r"), (W2_r, G * Fr * H, "W2_r"),
+                           (Z_r, rows * H, "Z_r"), (A1_r, rows * Fr, "A1_r"), (Y_r, rows * Fr, "Y_r")):
+            _need(t, n, name)
     rc = raw().tp_mlp_grouped_shard_fwd(
         tp_size, rank, n_groups, _ptr(group_offsets, "group_offsets", torch.int32), rows, H, F_group,
         _dtype_code(X_perm), _ptr(X_perm, "X_perm", dt), _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),

@@ -61,3 +61,26 @@ def test_single_token_attention_is_v(dtype):
                            rtol=tol, atol=tol), f"dV != dctx, head {h}"
     R_ctx, R_lse = oracle.tp_attn_heads_fwd(wl.tp_size, rank, wl.B, wl.S, wl.H, wl.n_heads, q)
     assert_close(ctx, R_ctx, dtype, "ctx vs oracle")
+
+
+def test_binding_rejects_short_buffers():
+    """The library sees raw pointers only; the binding refuses a tensor smaller than the call reads or
+    writes, before anything is enqueued."""
+    from tensor_transformer_layer_mlp_amd import binding as bd
+    bf = torch.bfloat16
+    e = lambda *s: torch.empty(*s, dtype=bf, device="cuda")  # noqa: E731
+    T, H, F, tp, r = 16, 64, 128, 2, 0
+    Fr = F // tp
+    good = {"X": e(T, H), "W1_r": e(H, Fr), "b1_r": e(Fr), "W2_r": e(Fr, H), "b2": e(H), "Z_r": e(T, H),
+            "A1_r": e(T, Fr), "Y_r": e(T, Fr)}
+    bd.tp_mlp_shard_fwd(tp, r, T, H, F, *good.values())
+    for k in good:
+        bad = dict(good)
+        bad[k] = good[k].reshape(-1)[:-1]
+        with pytest.raises(ValueError, match=f"^{k} has"):
+            bd.tp_mlp_shard_fwd(tp, r, T, H, F, *bad.values())
+    B, S, nh_all = 2, 8, 4
+    QKV, ctx = e(B * S, 3 * 2 * 16), e(B * S, 2 * 16)
+    with pytest.raises(ValueError, match="^ctx_r has"):
+        bd.tp_attn_heads_fwd(tp, r, B, S, H, nh_all, QKV, ctx[:-1])
+    torch.cuda.synchronize()
