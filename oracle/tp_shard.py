@@ -28,6 +28,12 @@ Readings where the pages are silent (each is listed in the design notes):
   R6 upstream gradient dZ of the row-split output is the full [T, H] tensor on every rank
                    (backward of reduce is the identity, [Arch] §4).
   R7 layout      = row-major; activations [B, S, ·] flattened to token b·S + s; weights [in, out].
+  R8 the heads' outputs are combined by the attention output projection O = ctx·Wo + bo, taken as a
+                   RowParallelLinear: rank r holds the rows of Wo that multiply its own heads' ctx
+                   columns and yields a partial that the all-reduce completes, the same column->row
+                   pairing as the MLP ([Intro] §二.2 says the heads' outputs are aggregated after
+                   the per-card attention; [Arch] §2.3 lists RowParallelLinear, §4 the pairing).
+                   bo is added once, by rank 0, as b2 (R5); dO is the full tensor on every rank (R6).
 
 Every function takes and returns float64 numpy arrays; nothing is rounded to the device's types.
 """
@@ -81,6 +87,14 @@ def slice_fc2(W2, tp_size: int, rank: int):
     """Row block of fc2 ([Digest] §2.2 table, MLP row: second matmul row-split)."""
     f0, fr = shard_range(W2.shape[0], tp_size, rank)
     return W2[f0:f0 + fr, :]
+
+
+def slice_attn_out(Wo, n_heads: int, tp_size: int, rank: int):
+    """Row block of the attention output projection: the d·nh_r rows that multiply the rank's own
+    heads' context columns (reading R8)."""
+    d = Wo.shape[0] // n_heads
+    h0, nh = shard_range(n_heads, tp_size, rank)
+    return Wo[d * h0:d * (h0 + nh), :]
 
 
 # ---- element-wise activation (reading R1) ------------------------------------------------------
@@ -189,10 +203,24 @@ def mlp_bwd(X, W1, W2, A1, Y, dZ, with_db2: bool):
             "dW2": Y.T @ dZ, "db2": dZ.sum(axis=0) if with_db2 else None, "dA1": dA1}
 
 
+def attn_out_fwd(ctx, Wo, bo):
+    """O = ctx·Wo (+ bo when bo is not None): the heads' outputs combined (reading R8)."""
+    O = ctx @ Wo
+    if bo is not None:
+        O = O + bo
+    return O
+
+
+def attn_out_bwd(ctx, Wo, dO, with_db: bool):
+    """Backward of attn_out_fwd from the chain rule: dWo = ctxᵀ·dO; dbo = Σ_t dO; dctx = dO·Woᵀ."""
+    return {"dctx": dO @ Wo.T, "dW": ctx.T @ dO, "db": dO.sum(axis=0) if with_db else None}
+
+
 # ---- the unsharded layer ------------------------------------------------------------------------
 
-def layer_fwd(X, Wqkv, bqkv, W1, b1, W2, b2, B: int, S: int, n_heads: int):
-    """QKV projection + per-head causal attention, and the MLP, on one device, unsplit.
+def layer_fwd(X, Wqkv, bqkv, W1, b1, W2, b2, B: int, S: int, n_heads: int, Wo=None, bo=None):
+    """QKV projection + per-head causal attention (+ the output projection O when Wo is given), and
+    the MLP, on one device, unsplit.
 
     LayerNorm, dropout and residuals are replicated outside the split ([Digest] §2.2 table) and
     are not part of the shard; X is the already-normalised input of both blocks.
@@ -202,6 +230,8 @@ def layer_fwd(X, Wqkv, bqkv, W1, b1, W2, b2, B: int, S: int, n_heads: int):
     ctx, lse = attention_fwd(QKV, B, S, n_heads, d)
     out = mlp_fwd(X, W1, b1, W2, b2)
     out.update(QKV=QKV, ctx=ctx, lse=lse)
+    if Wo is not None:
+        out["O"] = attn_out_fwd(ctx, Wo, bo)
     return out
 
 
@@ -258,6 +288,22 @@ def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, dctx_r):
     _, nh, d = _check_heads(H, n_heads, tp_size, rank)
     assert dctx_r.shape == (B * S, nh * d)
     return attention_bwd(QKV_r, dctx_r, B, S, nh, d)
+
+
+def tp_attn_out_shard_fwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, bo):
+    """Output projection of the rank's heads, a RowParallelLinear: O_r = ctx_r·Wo_r (+ bo iff
+    rank == 0).  Σ_r O_r is the unsharded ctx·Wo + bo (reading R8)."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert ctx_r.shape == (B * S, nh * d) and Wo_r.shape == (nh * d, H)
+    return attn_out_fwd(ctx_r, Wo_r, bo if rank == 0 else None)
+
+
+def tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO):
+    """Backward of the rank's output projection.  dO is the full upstream gradient (R6); dctx_r is
+    the rank's own column block of dctx (no sum needed); dbo iff rank == 0 (R8)."""
+    _, nh, d = _check_heads(H, n_heads, tp_size, rank)
+    assert dO.shape == (B * S, H) and ctx_r.shape == (B * S, nh * d)
+    return attn_out_bwd(ctx_r, Wo_r, dO, with_db=(rank == 0))
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):

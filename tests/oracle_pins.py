@@ -7,8 +7,9 @@ fails.  What pins what:
   geometry    golden fixture (the workloads' stated splits) + invariants (cover, contiguous, balanced)
   gelu        textbook normal-CDF values; odd-part identity; derivative by central differences
   brute       pure-Python scalar loops (tests/bruteforce.py) on the tiny layer, both ranks
-  identities  column split X·[W1 W2] = [X·W1, X·W2]; row split Σ_r Z_r = Z; Σ_r dX_r = dX;
-              weight-gradient blocks; tp=1 equals the unsharded layer
+  identities  column split X·[W1 W2] = [X·W1, X·W2]; row split Σ_r Z_r = Z and Σ_r O_r = O (the
+              attention output projection); Σ_r dX_r = dX; dctx and weight-gradient blocks; tp=1
+              equals the unsharded layer
   closed      attention closed forms: S=1, query 0, Q=0 (prefix mean, LSE = log(i+1)), constant keys
               (LSE = q·k/√d + log(i+1)), one dominant key, dV for Q=0
   fd          central finite differences in fp64 for every gradient output
@@ -100,6 +101,7 @@ def _tiny_full(seed=7, wstd=0.02, bstd=0.02, xstd=1.0, H=None, nh=None, F=None, 
         Wqkv=g.standard_normal((H, 3 * H)) * wstd, bqkv=g.standard_normal(3 * H) * bstd,
         W1=g.standard_normal((H, F)) * wstd, b1=g.standard_normal(F) * bstd,
         W2=g.standard_normal((F, H)) * wstd, b2=g.standard_normal(H) * bstd)
+    p.update(Wo=g.standard_normal((H, H)) * wstd, bo=g.standard_normal(H) * bstd)
     return cfg, p
 
 
@@ -118,6 +120,9 @@ def pin_brute_forward():
         bctx, blse = bf.attention(sharp, B, S, nh_r, d)
         _close(ctx, bctx, 1e-13, f"ctx r{r}")
         _close(lse, blse, 1e-13, f"lse r{r}")
+        Wo = T.slice_attn_out(p["Wo"], nh, t, r)
+        O = T.tp_attn_out_shard_fwd(t, r, B, S, H, nh, ctx, Wo, p["bo"])
+        _close(O, bf.matmul_bias(ctx, Wo, p["bo"] if r == 0 else None), 1e-13, f"O r{r}")
         W1, b1 = T.slice_fc1(p["W1"], p["b1"], t, r)
         W2 = T.slice_fc2(p["W2"], t, r)
         out = T.tp_mlp_shard_fwd(t, r, B * S, H, F, p["X"] * 20.0, W1, b1, W2, p["b2"])
@@ -156,6 +161,19 @@ def pin_brute_backward():
         ref = bf.linear_backward(X, Wq, dQKV)
         for k in ("dX", "dW", "db"):
             _close(got[k], ref[k], 1e-13, f"QKV {k} r{r}")
+    Wo = g.standard_normal((H, H)) * 0.3
+    dO = g.standard_normal((B * S, H))
+    for r in range(t):
+        Wor = T.slice_attn_out(Wo, nh, t, r)
+        ctx = g.standard_normal((B * S, Wor.shape[0]))
+        got = T.tp_attn_out_shard_bwd(t, r, B, S, H, nh, ctx, Wor, dO)
+        ref = bf.linear_backward(ctx, Wor, dO)
+        _close(got["dctx"], ref["dX"], 1e-13, f"out-proj dctx r{r}")
+        _close(got["dW"], ref["dW"], 1e-13, f"out-proj dWo r{r}")
+        if r == 0:
+            _close(got["db"], ref["db"], 1e-13, "out-proj dbo r0")
+        else:
+            assert got["db"] is None, "dbo belongs to rank 0 only"
 
 
 # ---- identities -------------------------------------------------------------------------------
@@ -170,7 +188,9 @@ def _run_ranks(cfg, p, t):
         W1, b1 = T.slice_fc1(p["W1"], p["b1"], t, r)
         W2 = T.slice_fc2(p["W2"], t, r)
         mlp = T.tp_mlp_shard_fwd(t, r, B * S, H, F, p["X"], W1, b1, W2, p["b2"])
-        outs.append(dict(qkv=qkv, ctx=ctx, lse=lse, **mlp, W1=W1, W2=W2, Wq=Wq))
+        Wo = T.slice_attn_out(p["Wo"], nh, t, r)
+        O = T.tp_attn_out_shard_fwd(t, r, B, S, H, nh, ctx, Wo, p["bo"])
+        outs.append(dict(qkv=qkv, ctx=ctx, lse=lse, **mlp, W1=W1, W2=W2, Wq=Wq, Wo=Wo, O=O))
     return outs
 
 
@@ -179,7 +199,8 @@ def pin_identities():
         cfg, p = _tiny_full(seed=3, H=H, nh=nh, F=F, B=2, S=12, wstd=0.2, bstd=0.1)
         B, S = cfg["B"], cfg["S"]
         d = H // nh
-        full = T.layer_fwd(p["X"], p["Wqkv"], p["bqkv"], p["W1"], p["b1"], p["W2"], p["b2"], B, S, nh)
+        full = T.layer_fwd(p["X"], p["Wqkv"], p["bqkv"], p["W1"], p["b1"], p["W2"], p["b2"], B, S, nh,
+                           p["Wo"], p["bo"])
         outs = _run_ranks(cfg, p, t)
         # column identity: QKV, ctx, lse, A1, Y are column blocks of the unsharded results
         _close(np.concatenate([o["qkv"] for o in outs], 1), full["QKV"], 1e-13, "QKV concat")
@@ -189,6 +210,11 @@ def pin_identities():
         _close(np.concatenate([o["Y"] for o in outs], 1), full["Y"], 1e-13, "Y concat")
         # row identity: the partials sum to the unsharded output
         _close(sum(o["Z"] for o in outs), full["Z"], 1e-13, f"sum Z_r (t={t})")
+        _close(sum(o["O"] for o in outs), full["O"], 1e-13, f"sum O_r (t={t})")
+        # the unsharded output projection, from its definition written out per head: the heads'
+        # contexts each times their own d rows of Wo, summed, plus the bias once
+        per_head = sum(full["ctx"][:, h * d:(h + 1) * d] @ p["Wo"][h * d:(h + 1) * d] for h in range(nh))
+        _close(full["O"], per_head + p["bo"], 1e-13, "O as a sum over heads")
         # backward: weight-gradient blocks and input-gradient partials
         g = _rng(5)
         dZ = g.standard_normal((B * S, H))
@@ -218,6 +244,15 @@ def pin_identities():
         _close(np.concatenate(dqkvs, 1), d_full_attn, 1e-13, "dQKV blocks")
         _close(np.concatenate(dWqs, 1), fullq["dW"], 1e-13, "dWqkv blocks")
         _close(np.concatenate(dbqs), fullq["db"], 1e-13, "dbqkv blocks")
+        # output projection backward: dctx_r is the rank's column block of dctx (no sum), dWo_r its
+        # row block of dWo, dbo from rank 0 only
+        dO = g.standard_normal((B * S, H))
+        fullo = T.attn_out_bwd(full["ctx"], p["Wo"], dO, True)
+        ob = [T.tp_attn_out_shard_bwd(t, r, B, S, H, nh, o["ctx"], o["Wo"], dO) for r, o in enumerate(outs)]
+        _close(np.concatenate([b["dctx"] for b in ob], 1), fullo["dctx"], 1e-13, "dctx blocks")
+        _close(np.concatenate([b["dW"] for b in ob], 0), fullo["dW"], 1e-13, "dWo blocks")
+        _close(ob[0]["db"], fullo["db"], 1e-13, "dbo")
+        assert all(b["db"] is None for b in ob[1:]), "dbo belongs to rank 0 only"
 
 
 # ---- attention closed forms --------------------------------------------------------------------
@@ -326,6 +361,30 @@ def pin_finite_differences():
         want = _fd_dir(call, x0, vdir)
         got = float((grad * vdir).sum())
         assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD QKV {name}"
+    # attention output projection, each rank of a 2-way split
+    B, S, nh, Ho = 1, 5, 4, 8
+    Wo, bo = g.standard_normal((Ho, Ho)) * 0.5, g.standard_normal(Ho) * 0.5
+    dO = g.standard_normal((B * S, Ho))
+    for r in range(2):
+        Wor = T.slice_attn_out(Wo, nh, 2, r)
+        ctx = g.standard_normal((B * S, Wor.shape[0]))
+        go = T.tp_attn_out_shard_bwd(2, r, B, S, Ho, nh, ctx, Wor, dO)
+
+        def oloss(c=ctx, w=Wor, b=bo):
+            return float((T.tp_attn_out_shard_fwd(2, r, B, S, Ho, nh, c, w, b) * dO).sum())
+
+        for name, x0, grad, call in (("dctx", ctx, go["dctx"], lambda z: oloss(c=z)),
+                                     ("dWo", Wor, go["dW"], lambda z: oloss(w=z))):
+            vdir = g.standard_normal(x0.shape)
+            want = _fd_dir(call, x0, vdir)
+            got = float((grad * vdir).sum())
+            assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD out-proj {name} r{r}"
+        vdir = g.standard_normal(bo.shape)
+        want = _fd_dir(lambda z: oloss(b=z), bo, vdir)
+        if r == 0:
+            assert abs(float((go["db"] * vdir).sum()) - want) <= 1e-7 * max(1, abs(want)), "FD dbo"
+        else:
+            assert abs(want) < 1e-9, "bo must not enter a rank other than 0"
     # attention, a mild and a sharp case, every component checked through random directions
     for scale in (1.0, 3.0):
         B, S, nh, d = 2, 7, 2, 4

@@ -97,6 +97,24 @@ def _grouped_off_by_one(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):
     return Z
 
 
+def _attn_out_rows_at_qkv_offset(Wo, n_heads, tp_size, rank):
+    d = Wo.shape[0] // n_heads
+    h0, nh = T.shard_range(n_heads, tp_size, rank)
+    return Wo[3 * d * h0:3 * d * h0 + d * nh, :]
+
+
+def _attn_out_fwd_bo_everywhere(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, bo):
+    return T.attn_out_fwd(ctx_r, Wo_r, bo)
+
+
+def _attn_out_bwd_dbo_everywhere(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO):
+    return T.attn_out_bwd(ctx_r, Wo_r, dO, with_db=True)
+
+
+def _attn_out_bwd_untransposed(ctx, Wo, dO, with_db):
+    return {"dctx": dO @ Wo[:, :Wo.shape[0]], "dW": ctx.T @ dO, "db": dO.sum(axis=0) if with_db else None}
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -118,6 +136,10 @@ MUTANTS = {
     "mlp_bwd_dW2_from_A1": {"mlp_bwd": _mlp_bwd_variant(dW2_from_A1=True)},
     "qkv_bwd_db_mean": {"qkv_bwd": _qkv_bwd_db_wrong_axis},
     "grouped_drops_last_row": {"tp_mlp_grouped_shard_fwd": _grouped_off_by_one},
+    "attn_out_rows_at_qkv_offset": {"slice_attn_out": _attn_out_rows_at_qkv_offset},
+    "attn_out_bo_on_every_rank": {"tp_attn_out_shard_fwd": _attn_out_fwd_bo_everywhere},
+    "attn_out_dbo_on_every_rank": {"tp_attn_out_shard_bwd": _attn_out_bwd_dbo_everywhere},
+    "attn_out_bwd_untransposed": {"attn_out_bwd": _attn_out_bwd_untransposed},
 }
 
 
