@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped-shard measurement")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-attn-out", action="store_true",
+                    help="skip the attention output-projection measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
                          "calibrated on), then --warmup + --steps steps, and nothing else")
@@ -193,6 +195,53 @@ def moe_grouped(bd, torch, steps, warmup):
     return out
 
 
+def attn_out_proj(bd, torch, wl, rank, steps, warmup):
+    """The attention output projection of the same shard (a RowParallelLinear over the rank's 12
+    heads: O_r = ctx_r·Wo_r + bo, then dWo_r, dbo, dctx_r), forward + backward, timed on its own
+    beside the step: 3 GEMMs of 2·T·(nh_r·d)·H flop each."""
+    t, B, S, H, nh_all = wl.tp_size, wl.B, wl.S, wl.H, wl.n_heads
+    T, d = wl.T, wl.head_dim
+    _, nh = bd.tp_shard_range(nh_all, t, rank)
+    Kr = nh * d
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5678)
+    bf = torch.bfloat16
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    ctx, dO = r(T, Kr), r(T, H)
+    Wo, bo = r(Kr, H, std=wl.w_std), r(H, std=wl.w_std)
+    e = lambda *sh: torch.empty(*sh, dtype=bf, device="cuda")  # noqa: E731
+    O, dctx, dWo, dbo = e(T, H), e(T, Kr), e(Kr, H), e(H)
+    ws = bd.workspace("tp_attn_out_shard_bwd", t, rank, B, S, H, nh_all, wl.F, bf)
+
+    def call():
+        bd.tp_attn_out_shard_fwd(t, rank, B, S, H, nh_all, ctx, Wo, bo, O)
+        bd.tp_attn_out_shard_bwd(t, rank, B, S, H, nh_all, ctx, Wo, dO, dctx, dWo, dbo, ws)
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    bd.tp_prof_enable(False)
+    kernels = {tag: kernel_roofline(n, kms, fl, by, steps) for tag, (n, kms, fl, by) in bd.tp_prof_collect().items()}
+    flop = 3 * 2.0 * T * Kr * H
+    out = {"workload": "gpt3_175b_tp8_rank0_attn_out_proj_fwd_bwd", "ms": round(ms, 4),
+           "gflop": round(flop / 1e9, 1), "tflops": round(flop / ms / 1e9, 2),
+           "pct_of_peak": round(100.0 * flop / ms / 1e9 / PEAK_BF16_TFLOPS, 2), "kernels": kernels}
+    del ctx, dO, Wo, O, dctx, dWo
+    torch.cuda.empty_cache()
+    return out, flop
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -336,6 +385,8 @@ def main():
                         "bytes_per_launch": byts / n}
 
     moe = None if args.no_moe else moe_grouped(bd, torch, args.steps, args.warmup)
+    oproj, oproj_flop = (None, 0.0) if args.no_attn_out else attn_out_proj(bd, torch, wl, rank, args.steps,
+                                                                           args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -360,6 +411,10 @@ def main():
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "moe_grouped_shard": moe,
+        "attn_out_proj_shard": oproj,
+        # the step plus the attention output projection: the whole Megatron layer shard's GEMMs
+        "tflops_layer_with_out_proj": round((flop_step + oproj_flop) / ((ms_step + oproj["ms"]) * 1e-3) / 1e12, 2)
+        if oproj else None,
     }
     print(json.dumps(out), flush=True)
 

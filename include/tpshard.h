@@ -28,12 +28,12 @@
  *  - `dtype`: TP_BF16 (bf16 in/out, fp32 accumulation and fp32 softmax/GeLU) or TP_F32 (fp32
  *    throughout: the check mode).  Every output has that type except LSE and workspace, fp32.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is ordered on it; calls return
- *    without synchronising.  Outputs are overwritten (never accumulated into).  The two backward
- *    calls with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd) may run some of them on a
- *    library-owned side stream of the current device (created once, outside graph capture, default
- *    priority), forked from and joined back into `stream` with events before they return: to the
- *    caller the effect is the same as if everything ran on `stream`, and a captured graph simply
- *    gets two branches.  While per-launch timing is on, or when the environment variable TP_SERIAL is
+ *    without synchronising.  Outputs are overwritten (never accumulated into).  The backward
+ *    calls with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_out_shard_bwd) may
+ *    run some of them on a library-owned side stream of the current device (created once, outside
+ *    graph capture, default priority), forked from and joined back into `stream` with events before
+ *    they return: to the caller the effect is the same as if everything ran on `stream`, and a
+ *    captured graph simply gets two branches.  While per-launch timing is on, or when the environment variable TP_SERIAL is
  *    set to a non-zero value, everything runs on `stream`.
  *  - Errors: arguments are validated on the host before any launch; a negative tp_status is
  *    returned and nothing is enqueued.  A failed launch returns TP_EHIP; tp_last_error() then holds
@@ -120,6 +120,28 @@ int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
                       const void* dctx_r, void* dQKV_r, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Attention output projection, a RowParallelLinear over the rank's heads.  The pages have the
+ * heads' outputs aggregated after each card's attention ("Megatron-LM（英伟达超大模型训练框架）完整介绍",
+ * §二.2); the row-split linear layer and the column->row pairing that needs one all-reduce at its exit
+ * are in "Megatron-LM — 架构与原理", §2.3 and §4.  The rank holds the d*nh_r rows of the full
+ * Wo[H, H] that multiply its own heads' context columns, and produces a partial sum:
+ *   O_r[T, H] = ctx_r[T, nh_r*d] · Wo_r[nh_r*d, H]  (+ bo[H] iff rank == 0 and bo != NULL)
+ * so Σ_r O_r = ctx·Wo + bo.  Wo_r is rows [d*h0, d*(h0+nh_r)) of Wo; ctx_r is the output of
+ * tp_attn_heads_fwd.  Same geometry checks as tp_qkv_shard_fwd. */
+int tp_attn_out_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                          const void* ctx_r, const void* Wo_r, const void* bo, void* O_r,
+                          void* stream);
+
+/* Backward of tp_attn_out_shard_fwd.  dO[T, H] is the full upstream gradient, the same on every
+ * rank (the all-reduce's backward is the identity):
+ *   dWo_r = ctx_rᵀ·dO ;  dbo = Σ_t dO (iff rank == 0 and dbo != NULL) ;  dctx_r = dO·Wo_rᵀ
+ * dctx_r is the rank's own column block of dctx (no sum over ranks), ready for tp_attn_heads_bwd.
+ * workspace: tp_workspace_bytes("tp_attn_out_shard_bwd", ...). */
+int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                          const void* ctx_r, const void* Wo_r, const void* dO, void* dctx_r,
+                          void* dWo_r, void* dbo, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* A9 — grouped expert MLP shard (MoE experts as grouped GEMMs: "Megatron-LM — 架构与原理", §6, TE
  * GroupedLinear).  Rows [off[e], off[e+1]) of the expert-sorted token matrix X_perm[rows, H] belong to
  * expert e (e < n_groups); each goes through expert e's column shard of fc1 with bias and GeLU and
@@ -137,7 +159,7 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
- * "tp_attn_heads_bwd", "tp_mlp_grouped_shard_fwd"; 0 for the others).  T = B*S; F is used by the
+ * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_mlp_grouped_shard_fwd"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

@@ -27,6 +27,8 @@ _SIGNATURES = {
     "tp_mlp_shard_bwd": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _P]),
     "tp_qkv_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
     "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
+    "tp_attn_out_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
+    "tp_attn_out_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -220,6 +222,37 @@ def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx
                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                  _stream(stream))
     _check(rc, "tp_attn_heads_bwd")
+
+
+def tp_attn_out_shard_fwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, bo, O_r, stream=None):
+    dt = ctx_r.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, Kr = B * S, g[0] * g[1]
+        for t, n, name in ((ctx_r, T * Kr, "ctx_r"), (Wo_r, Kr * H, "Wo_r"), (bo, H, "bo"), (O_r, T * H, "O_r")):
+            _need(t, n, name)
+    rc = raw().tp_attn_out_shard_fwd(tp_size, rank, B, S, H, n_heads, _dtype_code(ctx_r),
+                                     _ptr(ctx_r, "ctx_r", dt), _ptr(Wo_r, "Wo_r", dt),
+                                     _ptr(bo, "bo", dt, True), _ptr(O_r, "O_r", dt), _stream(stream))
+    _check(rc, "tp_attn_out_shard_fwd")
+
+
+def tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO, dctx_r, dWo_r, dbo,
+                          workspace, stream=None):
+    dt = ctx_r.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, Kr = B * S, g[0] * g[1]
+        for t, n, name in ((ctx_r, T * Kr, "ctx_r"), (Wo_r, Kr * H, "Wo_r"), (dO, T * H, "dO"),
+                           (dctx_r, T * Kr, "dctx_r"), (dWo_r, Kr * H, "dWo_r"), (dbo, H, "dbo")):
+            _need(t, n, name)
+    rc = raw().tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, _dtype_code(ctx_r),
+                                     _ptr(ctx_r, "ctx_r", dt), _ptr(Wo_r, "Wo_r", dt), _ptr(dO, "dO", dt),
+                                     _ptr(dctx_r, "dctx_r", dt), _ptr(dWo_r, "dWo_r", dt),
+                                     _ptr(dbo, "dbo", dt, True), _ptr(workspace, "workspace", None, True),
+                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                     _stream(stream))
+    _check(rc, "tp_attn_out_shard_bwd")
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_group, X_perm, W1_r,

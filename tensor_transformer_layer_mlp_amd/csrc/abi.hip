@@ -154,6 +154,8 @@ size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
 
 size_t qkv_bwd_ws(int T, int Nq) { return align256(colsum_ws_bytes(T, Nq)); }
 
+size_t out_bwd_ws(int T, int H) { return align256(colsum_ws_bytes(T, H)); }
+
 GemmDesc gemm_desc(int dtype, int M, int N, int K, const void* A, long lda, bool a_kmajor,
                    const void* B, long ldb, bool b_kmajor, void* C, long ldc, int epi) {
   GemmDesc d;
@@ -343,6 +345,66 @@ int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
   return TP_OK;
 }
 
+int tp_attn_out_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                          const void* ctx_r, const void* Wo_r, const void* bo, void* O_r,
+                          void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  const int Kr = g.nh * g.d;
+  NEED(ctx_r, "ctx_r", (long)g.T); NEED(Wo_r, "Wo_r", 1); NEED(O_r, "O_r", (long)g.T); MAYBE(bo, "bo");
+  const bool add_bo = (rank == 0 && bo != nullptr);
+  // O_r = ctx_r·Wo_r (+ bo)   (M = T, N = H, K = nh_r*d)
+  GemmDesc d = gemm_desc(dtype, g.T, H, Kr, ctx_r, Kr, true, Wo_r, H, false, O_r, H,
+                         add_bo ? EPI_BIAS : EPI_STORE);
+  d.bias = add_bo ? bo : nullptr;
+  TP_TRY(launch_gemm(d, (hipStream_t)stream), "out-proj gemm");
+  return TP_OK;
+}
+
+int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                          const void* ctx_r, const void* Wo_r, const void* dO, void* dctx_r,
+                          void* dWo_r, void* dbo, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  HeadGeom g;
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
+  if (st) return st;
+  const int Kr = g.nh * g.d;
+  NEED(ctx_r, "ctx_r", (long)g.T); NEED(Wo_r, "Wo_r", 1); NEED(dO, "dO", (long)g.T);
+  NEED(dctx_r, "dctx_r", (long)g.T); NEED(dWo_r, "dWo_r", 1); MAYBE(dbo, "dbo");
+  const size_t need = out_bwd_ws(g.T, H);
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  // dWo_r = ctx_rᵀ·dO   (M = nh_r*d, N = H, K = T)
+  GemmDesc g1 = gemm_desc(dtype, Kr, H, g.T, ctx_r, Kr, false, dO, H, false, dWo_r, H, EPI_STORE);
+  // dctx_r = dO·Wo_rᵀ   (M = T, N = nh_r*d, K = H)
+  GemmDesc g2 = gemm_desc(dtype, g.T, Kr, H, dO, H, true, Wo_r, H, true, dctx_r, Kr, EPI_STORE);
+
+  // caller's stream: dWo;  side stream: dbo (rank 0), dctx (all independent)
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = side_stream(s);
+  hipStream_t s2 = sd ? sd->s2 : s;
+  if (sd) {
+    TP_TRY(hipEventRecord(sd->fork, s), "fork");
+    TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
+  }
+  auto body = [&]() -> int {
+    TP_TRY(launch_gemm(g1, s), "dWo gemm");
+    if (rank == 0 && dbo != nullptr)
+      TP_TRY(launch_colsum(dtype, dO, H, g.T, H, (float*)workspace, dbo, s2), "dbo colsum");
+    TP_TRY(launch_gemm(g2, s2), "dctx gemm");
+    return TP_OK;
+  };
+  const int rc = body();
+  if (sd) {
+    TP_TRY(hipEventRecord(sd->join, s2), "join");
+    TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
+  }
+  return rc;
+}
+
 int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows,
                              int H, int F_group, int dtype, const void* X_perm, const void* W1_r,
                              const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
@@ -381,6 +443,10 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0) {
     if (n_heads < 1 || n_heads > (1 << 20)) return 0;
     return align256(grouped_ws_bytes(n_heads));
+  }
+  if (strcmp(fn, "tp_attn_out_shard_bwd") == 0) {
+    if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
+    return out_bwd_ws(g.T, H);
   }
   if (strcmp(fn, "tp_attn_heads_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;

@@ -147,6 +147,15 @@ def fc2_bias(wl, dtype) -> Operand:
     return vector_blocks("b2", 0, wl.H, wl.w_std, dtype)
 
 
+def attn_out_weight(wl, row_lo: int, row_hi: int, dtype) -> Operand:
+    """Rows [row_lo, row_hi) of the full [H, H] attention output-projection weight."""
+    return row_blocks("Wo", wl.H, row_lo, row_hi, wl.w_std, dtype)
+
+
+def attn_out_bias(wl, dtype) -> Operand:
+    return vector_blocks("bo", 0, wl.H, wl.w_std, dtype)
+
+
 # ---- MoE routing (input construction only) -----------------------------------------------------
 
 def moe_assignments(tokens: int, n_experts: int, top_k: int, seed_tag="router_logits"):

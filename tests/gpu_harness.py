@@ -73,6 +73,10 @@ class Shard:
             "dQKV": synth.column_blocks("dQKV", wl.T, c0, c1, 1.0, dtype),
             "A1": synth.column_blocks("A1", wl.T, self.f0, self.f0 + self.Fr, 1.0, dtype),
             "Y": synth.column_blocks("Y", wl.T, self.f0, self.f0 + self.Fr, 1.0, dtype),
+            "Wo": synth.attn_out_weight(wl, self.h0 * d, (self.h0 + self.nh) * d, dtype),
+            "bo": synth.attn_out_bias(wl, dtype),
+            "dO": synth.upstream(wl, wl.H, dtype, "dO"),
+            "ctx": synth.column_blocks("ctxin", wl.T, self.h0 * d, (self.h0 + self.nh) * d, 1.0, dtype),
         }
         if qkv_std is not None:   # a free-standing QKV input for the attention stage tests
             self.ops["QKV"] = synth.column_blocks("QKVin", wl.T, c0, c1, qkv_std, dtype)

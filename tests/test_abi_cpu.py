@@ -109,6 +109,22 @@ def test_qkv_bwd_validation(lib):
     assert b(3, 0, 2, 32, 64, 2, 0, P, P, P, P, P, P, P, 1 << 20, None) == -1   # nh < tp
 
 
+def test_attn_out_validation(lib):
+    f = lib.tp_attn_out_shard_fwd
+    assert f(2, 0, 2, 32, 64, 4, 0, None, P, P, P, None) == -2          # ctx_r
+    assert f(2, 0, 2, 32, 64, 4, 0, P, P, P, None, None) == -2          # O_r
+    assert f(2, 0, 2, 32, 64, 4, 0, P, P, MIS, P, None) == -3           # bo misaligned
+    assert f(2, 0, 2, 32, 65, 4, 0, P, P, P, P, None) == -1             # H % n_heads
+    assert f(3, 0, 2, 32, 64, 2, 0, P, P, P, P, None) == -1             # n_heads < tp_size
+    b = lib.tp_attn_out_shard_bwd
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, None, 0, None) == -5          # workspace
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, P, 8, None) == -5
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, P + 16, 1 << 20, None) == -3  # ws alignment
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, None, P, P, P, P, 1 << 20, None) == -2    # dO
+    assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, None, P, P, 1 << 20, None) == -2    # dWo_r
+    assert b(2, 1, 2, 32, 64, 4, 2, P, P, P, P, P, None, P, 1 << 20, None) == -1    # dtype
+
+
 def test_workspace_bytes(lib):
     T, H, F, t = 64, 64, 256, 2
     got = bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 0)
@@ -118,6 +134,9 @@ def test_workspace_bytes(lib):
     assert bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 1) >= T * 128 * 4
     assert bd.tp_workspace_bytes("tp_qkv_shard_bwd", t, 0, 2, 32, H, 4, F, 0) >= 96 * 4
     assert bd.tp_workspace_bytes("tp_attn_heads_bwd", t, 0, 2, 32, H, 4, F, 0) >= 2 * 32 * 2 * 4
+    assert bd.tp_workspace_bytes("tp_attn_out_shard_bwd", t, 0, 2, 32, H, 4, F, 0) >= H * 4
+    assert bd.tp_workspace_bytes("tp_attn_out_shard_bwd", t, 0, 2, 32, H, 1, F, 0) == 0   # nh < tp
+    assert bd.tp_workspace_bytes("tp_attn_out_shard_fwd", t, 0, 2, 32, H, 4, F, 0) == 0
     assert bd.tp_workspace_bytes("tp_qkv_shard_fwd", t, 0, 2, 32, H, 4, F, 0) == 0
     assert bd.tp_workspace_bytes("nope", t, 0, 2, 32, H, 4, F, 0) == 0
     assert bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 5, 2, 32, H, 4, F, 0) == 0   # bad rank

@@ -1,9 +1,10 @@
 """GPU parity at the full GPT-shaped shard sizes, in the launch configuration the benchmark times.
 
 The GPU runs each entry point on the whole shard.  The oracle checks sampled outputs: rows of
-row-separable results (QKV, Z, dX), columns of column-separable ones (dW1, db1, dW2, dWqkv), and
-whole heads of the attention.  Each sample is the oracle's own function applied to a row or column
-block of the inputs, which the column and row split identities make exact.
+row-separable results (QKV, Z, O, dX, dctx), columns of column-separable ones (dW1, db1, dW2,
+dWqkv, dWo, dbo), and whole heads of the attention.  Each sample is the oracle's own function
+applied to a row or column block of the inputs, which the column and row split identities make
+exact.
 """
 
 import numpy as np
@@ -12,6 +13,7 @@ import torch
 
 import oracle
 from gpu_harness import Shard, assert_close, dev, host
+from test_gpu_attn_out import run_out_bwd, run_out_fwd
 from test_gpu_parity import (run_attn_bwd, run_attn_fwd, run_mlp_bwd, run_mlp_fwd, run_qkv_bwd,
                              run_qkv_fwd)
 from tensor_transformer_layer_mlp_amd import binding as bd, synth
@@ -63,6 +65,20 @@ def check_shard(wl, rank):
     rq = oracle.qkv_bwd(X, W[:, cols_q], dQ[:, cols_q])
     assert_close(host(q["dW"])[:, cols_q], rq["dW"], dt, "dWqkv_r cols")
     assert_close(q["db"], dQ.sum(axis=0), dt, "dbqkv_r")
+
+    # attention output projection: rows of O_r and dctx_r, columns of dWo_r, all of dbo
+    cols_h = sample(H, 48, 4 + rank)
+    C, Wo, dO = sh.f64("ctx"), sh.f64("Wo"), sh.f64("dO")
+    O = run_out_fwd(sh, sh.d_("ctx"))
+    ro = oracle.tp_attn_out_shard_fwd(t, rank, 1, len(rows), H, nh, C[rows], Wo, sh.f64("bo"))
+    assert_close(host(O)[rows], ro, dt, "O_r rows")
+    ob = run_out_bwd(sh, sh.d_("ctx"), sh.d_("dO"))
+    rd = oracle.attn_out_bwd(C[rows], Wo, dO[rows], False)
+    assert_close(host(ob["dctx"])[rows], rd["dctx"], dt, "dctx_r rows")
+    rb = oracle.attn_out_bwd(C, Wo[:, cols_h], dO[:, cols_h], rank == 0)
+    assert_close(host(ob["dW"])[:, cols_h], rb["dW"], dt, "dWo_r cols")
+    if rank == 0:
+        assert_close(host(ob["db"])[cols_h], rb["db"], dt, "dbo cols")
 
     QKV = sh.d_("QKV")
     ctx, lse = run_attn_fwd(sh, QKV)
