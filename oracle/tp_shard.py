@@ -16,7 +16,7 @@ Sources (the pages this follows; each is cited by title and section):
   [Intro]     "Megatron-LM（英伟达超大模型训练框架）完整介绍", §二.2 张量并行: QKV split by column,
               heads computed independently on each card; MLP fc1 by column, fc2 by row.
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent (numbered as in the design notes):
   R1 activation  = exact GeLU, x·Φ(x) = ½x(1 + erf(x/√2)); the pages name no activation.
   R2 attention   = scaled dot-product, scores·1/√d, causal (key j visible to query i iff j <= i),
                    softmax over keys; LSE_i = log Σ_j exp(score_ij) over visible keys.
@@ -25,15 +25,15 @@ Readings where the pages are silent (each is listed in the design notes):
   R4 uneven split = balanced, lower ranks take the remainder (25 heads over 2 ranks -> 13 / 12).
   R5 biases      = bqkv and b1 split with their weight columns; b2 (row-split layer) added once, by
                    rank 0, so the partials sum to the unsharded output; db2 produced by rank 0 only.
-  R6 upstream gradient dZ of the row-split output is the full [T, H] tensor on every rank
-                   (backward of reduce is the identity, [Arch] §4).
-  R7 layout      = row-major; activations [B, S, ·] flattened to token b·S + s; weights [in, out].
-  R8 the heads' outputs are combined by the attention output projection O = ctx·Wo + bo, taken as a
+  R6 the heads' outputs are combined by the attention output projection O = ctx·Wo + bo, taken as a
                    RowParallelLinear: rank r holds the rows of Wo that multiply its own heads' ctx
                    columns and yields a partial that the all-reduce completes, the same column->row
                    pairing as the MLP ([Intro] §二.2 says the heads' outputs are aggregated after
                    the per-card attention; [Arch] §2.3 lists RowParallelLinear, §4 the pairing).
-                   bo is added once, by rank 0, as b2 (R5); dO is the full tensor on every rank (R6).
+                   bo is added once, by rank 0, as b2 (R5); dO is the full tensor on every rank (R9).
+  R9 upstream gradient dZ of the row-split output is the full [T, H] tensor on every rank
+                   (backward of reduce is the identity, [Arch] §4).
+  R10 layout     = row-major; activations [B, S, ·] flattened to token b·S + s; weights [in, out].
 
 Every function takes and returns float64 numpy arrays; nothing is rounded to the device's types.
 """
@@ -91,7 +91,7 @@ def slice_fc2(W2, tp_size: int, rank: int):
 
 def slice_attn_out(Wo, n_heads: int, tp_size: int, rank: int):
     """Row block of the attention output projection: the d·nh_r rows that multiply the rank's own
-    heads' context columns (reading R8)."""
+    heads' context columns (reading R6)."""
     d = Wo.shape[0] // n_heads
     h0, nh = shard_range(n_heads, tp_size, rank)
     return Wo[d * h0:d * (h0 + nh), :]
@@ -204,7 +204,7 @@ def mlp_bwd(X, W1, W2, A1, Y, dZ, with_db2: bool):
 
 
 def attn_out_fwd(ctx, Wo, bo):
-    """O = ctx·Wo (+ bo when bo is not None): the heads' outputs combined (reading R8)."""
+    """O = ctx·Wo (+ bo when bo is not None): the heads' outputs combined (reading R6)."""
     O = ctx @ Wo
     if bo is not None:
         O = O + bo
@@ -269,7 +269,7 @@ def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2):
 
 
 def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ):
-    """Backward of the rank's MLP shard.  dZ is the full upstream gradient (R6); dX_r is a partial
+    """Backward of the rank's MLP shard.  dZ is the full upstream gradient (R9); dX_r is a partial
     whose sum over ranks is dX (copy's backward all-reduce, [Arch] §4); db2 iff rank == 0 (R5)."""
     _, fr = shard_range(F, tp_size, rank)
     assert dZ.shape == (T, H) and A1_r.shape == (T, fr) and Y_r.shape == (T, fr)
@@ -292,15 +292,15 @@ def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, dctx_r):
 
 def tp_attn_out_shard_fwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, bo):
     """Output projection of the rank's heads, a RowParallelLinear: O_r = ctx_r·Wo_r (+ bo iff
-    rank == 0).  Σ_r O_r is the unsharded ctx·Wo + bo (reading R8)."""
+    rank == 0).  Σ_r O_r is the unsharded ctx·Wo + bo (reading R6)."""
     _, nh, d = _check_heads(H, n_heads, tp_size, rank)
     assert ctx_r.shape == (B * S, nh * d) and Wo_r.shape == (nh * d, H)
     return attn_out_fwd(ctx_r, Wo_r, bo if rank == 0 else None)
 
 
 def tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO):
-    """Backward of the rank's output projection.  dO is the full upstream gradient (R6); dctx_r is
-    the rank's own column block of dctx (no sum needed); dbo iff rank == 0 (R8)."""
+    """Backward of the rank's output projection.  dO is the full upstream gradient (R9); dctx_r is
+    the rank's own column block of dctx (no sum needed); dbo iff rank == 0 (R6)."""
     _, nh, d = _check_heads(H, n_heads, tp_size, rank)
     assert dO.shape == (B * S, H) and ctx_r.shape == (B * S, nh * d)
     return attn_out_bwd(ctx_r, Wo_r, dO, with_db=(rank == 0))
