@@ -10,5 +10,6 @@ from .tp_shard import (shard_range, qkv_column_range, slice_qkv, slice_fc1, slic
                        gelu_grad, attention_fwd, attention_bwd, qkv_fwd, qkv_bwd, mlp_fwd, mlp_bwd,
                        layer_fwd, tp_qkv_shard_fwd, tp_attn_heads_fwd, tp_mlp_shard_fwd,
                        tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_heads_bwd,
-                       tp_attn_out_shard_fwd, tp_attn_out_shard_bwd,
+                       tp_attn_out_shard_fwd, tp_attn_out_shard_bwd, dropout_add, layernorm,
+                       layernorm_bwd, sp_rows, tp_residual_ln_fwd, tp_residual_ln_bwd,
                        tp_mlp_grouped_shard_fwd, normwise_error)

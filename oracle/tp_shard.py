@@ -15,6 +15,9 @@ Sources (the pages this follows; each is cited by title and section):
               leaves the MLP with one all-reduce at the RowParallelLinear exit.
   [Intro]     "Megatron-LM（英伟达超大模型训练框架）完整介绍", §二.2 张量并行: QKV split by column,
               heads computed independently on each card; MLP fc1 by column, fc2 by row.
+  [Overview]  "NVIDIA Megatron-LM：大规模Transformer模型分布式训练框架", §核心架构：五大并行策略的协同艺术,
+              sequence parallelism: LayerNorm and dropout activations, replicated under plain TP,
+              are split along the sequence.
 
 Readings where the pages are silent (numbered as in the design notes):
   R1 activation  = exact GeLU, x·Φ(x) = ½x(1 + erf(x/√2)); the pages name no activation.
@@ -34,6 +37,17 @@ Readings where the pages are silent (numbered as in the design notes):
   R9 upstream gradient dZ of the row-split output is the full [T, H] tensor on every rank
                    (backward of reduce is the identity, [Arch] §4).
   R10 layout     = row-major; activations [B, S, ·] flattened to token b·S + s; weights [in, out].
+  R11 LayerNorm, residual, dropout = replicated outside the split ([Digest] §2.2 table): the shard's
+                   GEMMs take the already-normalised input.  As an op of its own: h = x + dropout(o)
+                   (o the sublayer's summed output, bias included), y = LayerNorm(h)·γ + β per token
+                   over the H features, biased variance, eps inside the square root; inverted dropout
+                   (kept values scaled by 1/(1-p)) with the keep mask an input (the method's random
+                   draws are passed in).  Pre-norm blocks carry h on as the residual stream, post-norm
+                   blocks carry y; the op is the same.
+  R13 sequence parallelism = LayerNorm and dropout split along the sequence ([Overview]; [Arch], the
+                   table under 它能做什么): rank r owns rows [off(T,t,r), off+cnt) of the flattened
+                   tokens (the sequence itself when B = 1) and its dγ, dβ are partial sums over its
+                   rows; without it every rank holds all T rows and the full dγ, dβ.
 
 Every function takes and returns float64 numpy arrays; nothing is rounded to the device's types.
 """
@@ -216,6 +230,51 @@ def attn_out_bwd(ctx, Wo, dO, with_db: bool):
     return {"dctx": dO @ Wo.T, "dW": ctx.T @ dO, "db": dO.sum(axis=0) if with_db else None}
 
 
+# ---- replicated-side ops: residual add with dropout, LayerNorm (readings R11, R13) ------------
+
+def dropout_add(x, o, keep, p_drop):
+    """h = x + o ∘ keep / (1 − p): inverted dropout of the sublayer output o, then the residual add.
+    o None: h = x.  keep None: no dropout."""
+    x = np.asarray(x, dtype=np.float64)
+    if o is None:
+        return x.copy()
+    if keep is None:
+        return x + o
+    return x + o * np.asarray(keep, dtype=np.float64) / (1.0 - p_drop)
+
+
+def layernorm(h, gamma, beta, eps):
+    """Per row over the features: mean, biased variance, y = (h − mean)/√(var + eps)·γ + β.
+    Returns y, mean, rstd = 1/√(var + eps)."""
+    mean = h.mean(axis=1)
+    c = h - mean[:, None]
+    var = (c * c).mean(axis=1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    return c * rstd[:, None] * gamma + beta, mean, rstd
+
+
+def layernorm_bwd(h, gamma, dy, eps):
+    """Gradients of layernorm by the chain rule through the row mean and variance.  With
+    x̂ = (h − mean)·rstd and g = dy·γ:  dβ = Σ_t dy;  dγ = Σ_t dy·x̂;
+    dh = rstd·(g − mean_H(g) − x̂·mean_H(g·x̂))."""
+    mean = h.mean(axis=1)
+    c = h - mean[:, None]
+    rstd = 1.0 / np.sqrt((c * c).mean(axis=1) + eps)
+    xhat = c * rstd[:, None]
+    g = dy * gamma
+    dh = rstd[:, None] * (g - g.mean(axis=1, keepdims=True) - xhat * (g * xhat).mean(axis=1, keepdims=True))
+    return dh, (dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def sp_rows(T: int, tp_size: int, rank: int, sequence_parallel: bool):
+    """Rows [r0, r0 + n) of the T tokens a rank normalises (reading R13)."""
+    if sequence_parallel:
+        return shard_range(T, tp_size, rank)
+    if tp_size < 1 or not 0 <= rank < tp_size:
+        raise ValueError("bad rank")
+    return 0, T
+
+
 # ---- the unsharded layer ------------------------------------------------------------------------
 
 def layer_fwd(X, Wqkv, bqkv, W1, b1, W2, b2, B: int, S: int, n_heads: int, Wo=None, bo=None):
@@ -304,6 +363,30 @@ def tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO):
     _, nh, d = _check_heads(H, n_heads, tp_size, rank)
     assert dO.shape == (B * S, H) and ctx_r.shape == (B * S, nh * d)
     return attn_out_bwd(ctx_r, Wo_r, dO, with_db=(rank == 0))
+
+
+def tp_residual_ln_fwd(tp_size, rank, sequence_parallel, T, H, x, o, keep, p_drop, gamma, beta, eps):
+    """Residual add with dropout, then LayerNorm, on the rank's rows (all T, or its block of the
+    sequence under sequence parallelism): h = x + dropout(o); y = LayerNorm(h)·γ + β (R11, R13)."""
+    _, n = sp_rows(T, tp_size, rank, sequence_parallel)
+    assert np.shape(x) == (n, H)
+    h = dropout_add(x, o, keep, p_drop)
+    y, mean, rstd = layernorm(h, gamma, beta, eps)
+    return {"h": h, "y": y, "mean": mean, "rstd": rstd}
+
+
+def tp_residual_ln_bwd(tp_size, rank, sequence_parallel, T, H, dy, dh_in, h, gamma, keep, p_drop, eps):
+    """Backward of tp_residual_ln_fwd on the rank's rows.  dh_in is the gradient reaching h along
+    the residual stream (None: none); dh is the gradient of h, which is also that of x (the
+    residual passes it through); do = dh ∘ keep/(1 − p).  dγ, dβ sum over the rank's rows: partials
+    under sequence parallelism, whose sum over ranks is the full gradient (R13)."""
+    _, n = sp_rows(T, tp_size, rank, sequence_parallel)
+    assert np.shape(dy) == (n, H)
+    dh, dgamma, dbeta = layernorm_bwd(h, gamma, dy, eps)
+    if dh_in is not None:
+        dh = dh + dh_in
+    do = dh * np.asarray(keep, dtype=np.float64) / (1.0 - p_drop) if keep is not None else dh.copy()
+    return {"dh": dh, "do": do, "dgamma": dgamma, "dbeta": dbeta}
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):

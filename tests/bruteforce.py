@@ -90,3 +90,24 @@ def linear_backward(X, W, dY):
     db = [sum(dY[t][j] for t in range(T)) for j in range(N)]
     dX = [[sum(dY[t][j] * W[i][j] for j in range(N)) for i in range(H)] for t in range(T)]
     return {"dX": dX, "dW": dW, "db": db}
+
+
+def layernorm(h, gamma, beta, eps):
+    """y, mean, rstd of each row by scalar loops: two passes (mean, then the biased variance)."""
+    h, gamma, beta = map(tolist, (h, gamma, beta))
+    ys, means, rstds = [], [], []
+    for row in h:
+        n = len(row)
+        m = 0.0
+        for v in row:
+            m += v
+        m /= n
+        var = 0.0
+        for v in row:
+            var += (v - m) * (v - m)
+        var /= n
+        r = 1.0 / math.sqrt(var + eps)
+        ys.append([(row[j] - m) * r * gamma[j] + beta[j] for j in range(n)])
+        means.append(m)
+        rstds.append(r)
+    return ys, means, rstds

@@ -13,6 +13,10 @@ fails.  What pins what:
   closed      attention closed forms: S=1, query 0, Q=0 (prefix mean, LSE = log(i+1)), constant keys
               (LSE = q·k/√d + log(i+1)), one dominant key, dV for Q=0
   fd          central finite differences in fp64 for every gradient output
+  layernorm   scalar loops; a textbook row; zero mean / unit mean square (eps = 0); shift and scale
+              invariance; constant rows; dropout-add cases by hand; finite differences through the
+              fused residual + dropout + LayerNorm op; the sequence-parallel split (row blocks
+              concatenate, dγ / dβ partials sum)
 """
 
 import math
@@ -422,5 +426,83 @@ def pin_grouped():
             _close(Z[lo:hi], ref, 1e-13, f"expert {e}")
 
 
+def pin_layernorm():
+    g = _rng(51)
+    # scalar loops
+    h = g.standard_normal((5, 7)) * 3.0 + 1.5
+    gam, bet = g.standard_normal(7), g.standard_normal(7)
+    y, mean, rstd = T.layernorm(h, gam, bet, 1e-5)
+    by, bm, br = bf.layernorm(h, gam, bet, 1e-5)
+    _close(y, by, 1e-13, "LN y brute")
+    _close(mean, bm, 1e-13, "LN mean brute")
+    _close(rstd, br, 1e-13, "LN rstd brute")
+    # a textbook row: [1, 2, 3, 4] has mean 2.5 and variance 1.25
+    y, mean, rstd = T.layernorm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.ones(4), np.zeros(4), 0.0)
+    _close(y, np.array([[-1.5, -0.5, 0.5, 1.5]]) / math.sqrt(1.25), 1e-15, "LN textbook row")
+    assert abs(mean[0] - 2.5) < 1e-15 and abs(rstd[0] - 1 / math.sqrt(1.25)) < 1e-15
+    # eps = 0, γ = 1, β = 0: every row has mean 0 and mean square 1; shift and scale invariance
+    h = g.standard_normal((6, 33)) * 2.0 - 3.0
+    y, _, _ = T.layernorm(h, np.ones(33), np.zeros(33), 0.0)
+    assert np.abs(y.mean(axis=1)).max() < 1e-14 and np.abs((y * y).mean(axis=1) - 1).max() < 1e-13
+    a, c = np.abs(g.standard_normal((6, 1))) + 0.5, g.standard_normal((6, 1)) * 10
+    _close(T.layernorm(a * h + c, np.ones(33), np.zeros(33), 0.0)[0], y, 1e-12, "LN shift/scale invariance")
+    # a constant row normalises to β; x̂ = 0 there, so its input gradient is (g − mean(g))/√eps
+    hc = np.vstack([np.full(9, 2.75), g.standard_normal(9)])
+    bet, gam, dyc = g.standard_normal(9), g.standard_normal(9), g.standard_normal((2, 9))
+    assert np.abs(T.layernorm(hc, gam, bet, 1e-5)[0][0] - bet).max() < 1e-15
+    dh, _, _ = T.layernorm_bwd(hc, gam, dyc, 1e-5)
+    gc = dyc[0] * gam
+    _close(dh[0], (gc - gc.mean()) / math.sqrt(1e-5), 1e-12, "constant row input gradient")
+    # dropout + residual add, by hand
+    x, o = np.array([[1.0, 2.0]]), np.array([[4.0, 8.0]])
+    _close(T.dropout_add(x, o, np.array([[1, 0]], np.uint8), 0.5), np.array([[9.0, 2.0]]), 1e-15, "dropout-add")
+    _close(T.dropout_add(x, o, None, 0.5), x + o, 1e-15, "add without dropout")
+    _close(T.dropout_add(x, None, None, 0.0), x, 1e-15, "no sublayer output")
+    _close(T.dropout_add(x, o, np.ones((1, 2), np.uint8), 0.2), x + o / 0.8, 1e-15, "all kept")
+    # finite differences through h = x + dropout(o), y = LN(h)·γ + β, loss = Σ y·dy + Σ h·dh_in
+    n, H, p, eps = 4, 10, 0.3, 1e-5
+    x, o = g.standard_normal((n, H)), g.standard_normal((n, H)) * 2
+    keep = (g.random((n, H)) > p).astype(np.uint8)
+    gam, bet = g.standard_normal(H), g.standard_normal(H)
+    dy, dh_in = g.standard_normal((n, H)), g.standard_normal((n, H))
+    for sp, t, r in ((False, 2, 1), (True, 1, 0)):
+        def loss(x_=x, o_=o, gm=gam, bt=bet):
+            f = T.tp_residual_ln_fwd(t, r, sp, n, H, x_, o_, keep, p, gm, bt, eps)
+            return float((f["y"] * dy).sum() + (f["h"] * dh_in).sum())
+        fw = T.tp_residual_ln_fwd(t, r, sp, n, H, x, o, keep, p, gam, bet, eps)
+        gr = T.tp_residual_ln_bwd(t, r, sp, n, H, dy, dh_in, fw["h"], gam, keep, p, eps)
+        for name, x0, grad, call in (("dx", x, gr["dh"], lambda z: loss(x_=z)),
+                                     ("do", o, gr["do"], lambda z: loss(o_=z)),
+                                     ("dgamma", gam, gr["dgamma"], lambda z: loss(gm=z)),
+                                     ("dbeta", bet, gr["dbeta"], lambda z: loss(bt=z))):
+            for _ in range(3):
+                vdir = g.standard_normal(x0.shape)
+                want = _fd_dir(call, x0, vdir)
+                got = float((grad * vdir).sum())
+                assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), f"FD LN {name}: {got} vs {want}"
+    # sequence parallelism: rank row blocks concatenate to the replicated result; dγ, dβ partials sum
+    Tt, H, t = 11, 6, 3
+    x, o = g.standard_normal((Tt, H)), g.standard_normal((Tt, H))
+    keep = (g.random((Tt, H)) > 0.1).astype(np.uint8)
+    gam, bet, dy = g.standard_normal(H), g.standard_normal(H), g.standard_normal((Tt, H))
+    full = T.tp_residual_ln_fwd(t, 1, False, Tt, H, x, o, keep, 0.1, gam, bet, 1e-5)
+    fullb = T.tp_residual_ln_bwd(t, 1, False, Tt, H, dy, None, full["h"], gam, keep, 0.1, 1e-5)
+    parts, bparts = [], []
+    for r in range(t):
+        r0, nr = T.sp_rows(Tt, t, r, True)
+        sl = slice(r0, r0 + nr)
+        f = T.tp_residual_ln_fwd(t, r, True, Tt, H, x[sl], o[sl], keep[sl], 0.1, gam, bet, 1e-5)
+        parts.append(f)
+        bparts.append(T.tp_residual_ln_bwd(t, r, True, Tt, H, dy[sl], None, f["h"], gam, keep[sl], 0.1, 1e-5))
+    for k in ("h", "y", "mean", "rstd"):
+        _close(np.concatenate([f[k] for f in parts]), full[k], 1e-15, f"SP concat {k}")
+    for k in ("dh", "do"):
+        _close(np.concatenate([b[k] for b in bparts]), fullb[k], 1e-15, f"SP concat {k}")
+    for k in ("dgamma", "dbeta"):
+        _close(sum(b[k] for b in bparts), fullb[k], 1e-13, f"SP sum of {k} partials")
+    assert [T.sp_rows(Tt, t, r, True) for r in range(t)] == [(0, 4), (4, 4), (8, 3)]
+    assert T.sp_rows(Tt, t, 2, False) == (0, Tt)
+
+
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
-            pin_attention_closed_forms, pin_finite_differences, pin_grouped]
+            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm]

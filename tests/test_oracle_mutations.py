@@ -115,6 +115,50 @@ def _attn_out_bwd_untransposed(ctx, Wo, dO, with_db):
     return {"dctx": dO @ Wo[:, :Wo.shape[0]], "dW": ctx.T @ dO, "db": dO.sum(axis=0) if with_db else None}
 
 
+def _ln_variant(ddof=0, eps_outside=False, over_tokens=False):
+    def f(h, gamma, beta, eps):
+        ax = 0 if over_tokens else 1
+        mean = h.mean(axis=ax, keepdims=True)
+        c = h - mean
+        var = (c * c).sum(axis=ax, keepdims=True) / (h.shape[ax] - ddof)
+        rstd = 1.0 / (np.sqrt(var) + eps) if eps_outside else 1.0 / np.sqrt(var + eps)
+        y = c * rstd * gamma + beta
+        if over_tokens:
+            return y, np.broadcast_to(mean, h.shape)[:, 0], np.broadcast_to(rstd, h.shape)[:, 0]
+        return y, mean[:, 0], rstd[:, 0]
+    return f
+
+
+def _ln_bwd_variant(drop_mean=False, drop_proj=False, dgamma_plain=False):
+    def f(h, gamma, dy, eps):
+        mean = h.mean(axis=1)
+        c = h - mean[:, None]
+        rstd = 1.0 / np.sqrt((c * c).mean(axis=1) + eps)
+        xhat = c * rstd[:, None]
+        g = dy * gamma
+        t = g.copy()
+        if not drop_mean:
+            t = t - g.mean(axis=1, keepdims=True)
+        if not drop_proj:
+            t = t - xhat * (g * xhat).mean(axis=1, keepdims=True)
+        return rstd[:, None] * t, (dy if dgamma_plain else dy * xhat).sum(axis=0), dy.sum(axis=0)
+    return f
+
+
+def _dropout_add_unscaled(x, o, keep, p_drop):
+    x = np.asarray(x, dtype=np.float64)
+    if o is None:
+        return x.copy()
+    return x + (o if keep is None else o * keep)
+
+
+def _ln_bwd_ignores_dh_in(tp_size, rank, sp, Tt, H, dy, dh_in, h, gamma, keep, p_drop, eps):
+    return _ORIG_LN_BWD(tp_size, rank, sp, Tt, H, dy, None, h, gamma, keep, p_drop, eps)
+
+
+_ORIG_LN_BWD = T.tp_residual_ln_bwd
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -140,6 +184,14 @@ MUTANTS = {
     "attn_out_bo_on_every_rank": {"tp_attn_out_shard_fwd": _attn_out_fwd_bo_everywhere},
     "attn_out_dbo_on_every_rank": {"tp_attn_out_shard_bwd": _attn_out_bwd_dbo_everywhere},
     "attn_out_bwd_untransposed": {"attn_out_bwd": _attn_out_bwd_untransposed},
+    "ln_unbiased_variance": {"layernorm": _ln_variant(ddof=1)},
+    "ln_eps_outside_sqrt": {"layernorm": _ln_variant(eps_outside=True)},
+    "ln_stats_over_tokens": {"layernorm": _ln_variant(over_tokens=True)},
+    "ln_bwd_drops_mean_term": {"layernorm_bwd": _ln_bwd_variant(drop_mean=True)},
+    "ln_bwd_drops_projection": {"layernorm_bwd": _ln_bwd_variant(drop_proj=True)},
+    "ln_bwd_dgamma_without_xhat": {"layernorm_bwd": _ln_bwd_variant(dgamma_plain=True)},
+    "dropout_without_rescale": {"dropout_add": _dropout_add_unscaled},
+    "ln_bwd_ignores_residual_grad": {"tp_residual_ln_bwd": _ln_bwd_ignores_dh_in},
 }
 
 
