@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--no-attn-out", action="store_true",
                     help="skip the attention output-projection measurement")
+    ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
                          "calibrated on), then --warmup + --steps steps, and nothing else")
@@ -242,6 +243,59 @@ def attn_out_proj(bd, torch, wl, rank, steps, warmup):
     return out, flop
 
 
+def residual_ln(bd, torch, wl, steps, warmup):
+    """The residual add with dropout + LayerNorm of the same layer, forward + backward, on its own:
+    replicated (all 2048 tokens of H = 12288, as plain tensor parallelism holds it) and sequence-
+    parallel (rank 0's 256-token block of 8).  HBM-bound: algorithmic bytes = x, o read, keep read,
+    h, y written (9 B per element in bf16) forward; dy, h, dh_in, keep read, dh, d_o written (11 B)
+    backward, then dy and h read again for dγ, dβ (4 B)."""
+    T, H, p = wl.T, wl.H, 0.1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2468)
+    bf = torch.bfloat16
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    out = {}
+    for name, sp, rows in (("replicated", False, T), ("sequence_parallel_rank0", True, bd.tp_shard_range(T, 8, 0)[1])):
+        x, o, dy, dh_in = r(rows, H), r(rows, H), r(rows, H), r(rows, H)
+        gamma, beta = 1.0 + r(H, std=0.1).float(), r(H, std=0.1)
+        gamma = gamma.to(bf)
+        keep = (torch.rand(rows, H, generator=g, device="cuda") >= p).to(torch.uint8)
+        e = lambda *sh, dt=bf: torch.empty(*sh, dtype=dt, device="cuda")  # noqa: E731
+        h, y, dh, d_o, dg, db = e(rows, H), e(rows, H), e(rows, H), e(rows, H), e(H), e(H)
+        mean, rstd = e(rows, dt=torch.float32), e(rows, dt=torch.float32)
+        ws = bd.workspace("tp_residual_ln_bwd", 8, 0, 1, T, H, 1, 1, bf)
+
+        def call():
+            bd.tp_residual_ln_fwd(8, 0, sp, T, H, x, o, keep, p, gamma, beta, 1e-5, h, y, mean, rstd)
+            bd.tp_residual_ln_bwd(8, 0, sp, T, H, dy, dh_in, h, mean, rstd, gamma, keep, p, dh, d_o, dg, db, ws)
+        for _ in range(warmup):
+            call()
+        bd.tp_prof_collect()
+        bd.tp_prof_enable(True)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        bd.tp_prof_enable(False)
+        k = bd.tp_prof_collect()
+        n = rows * H
+        res = {"rows": rows, "H": H}
+        for tag, alg in (("ln_fwd", 9.0 * n), ("ln_bwd", 11.0 * n)):
+            if tag in k:
+                cnt, ms, _, _ = k[tag]
+                us = 1e3 * ms / cnt
+                res[tag] = {"avg_launch_us": round(us, 2), "algorithmic_bytes": alg,
+                            "gb_per_s": round(alg / us / 1e3, 1), "hbm_frac": round(alg / us / 1e3 / PEAK_HBM_GBS, 4)}
+        if "ln_bwd_params" in k:           # dγ, dβ: dy and h read again (4 B per element), two sums
+            cnt, ms, _, _ = k["ln_bwd_params"]
+            us = 1e3 * ms / cnt
+            res["ln_bwd_params"] = {"avg_launch_us": round(us, 2), "algorithmic_bytes": 4.0 * n,
+                                    "gb_per_s": round(4.0 * n / us / 1e3, 1)}
+        out[name] = res
+        del x, o, dy, dh_in, keep, h, y, dh, d_o
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -388,6 +442,8 @@ def main():
     oproj, oproj_flop = (None, 0.0) if args.no_attn_out else attn_out_proj(bd, torch, wl, rank, args.steps,
                                                                            args.warmup)
 
+    ln = None if args.no_ln else residual_ln(bd, torch, wl, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, rank, args.cpu_seq)
@@ -412,6 +468,7 @@ def main():
         "kernels": breakdown,
         "moe_grouped_shard": moe,
         "attn_out_proj_shard": oproj,
+        "residual_layernorm": ln,
         # the step plus the attention output projection: the whole Megatron layer shard's GEMMs
         "tflops_layer_with_out_proj": round((flop_step + oproj_flop) / ((ms_step + oproj["ms"]) * 1e-3) / 1e12, 2)
         if oproj else None,

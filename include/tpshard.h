@@ -142,6 +142,40 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
                           void* dWo_r, void* dbo, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Residual add with dropout, then LayerNorm: the ops outside the tensor split, which every rank
+ * holds whole ("Megatron-LM 深度解读报告", §2.2 table, LayerNorm / Dropout row) or, under sequence
+ * parallelism, splits along the sequence ("NVIDIA Megatron-LM：大规模Transformer模型分布式训练框架",
+ * the five-strategies section; "Megatron-LM — 架构与原理", capability table).  Per row:
+ *   h = x + o∘keep/(1 − p_drop)           (o nullable: h = x;  keep nullable: no dropout)
+ *   y = (h − mean)·rstd·γ + β,  mean and the biased variance over the H features,
+ *   rstd = 1/√(var + eps)
+ * o is the sublayer's output after its all-reduce (bias included).  A pre-norm block carries h on
+ * as its residual stream, a post-norm block y; the op is the same.  Rows: all T = B·S tokens when
+ * sequence_parallel == 0; else the rank's block [off(T,t,r), off+cnt) of them (the sequence itself
+ * when B = 1), and every pointer then addresses that block, [cnt, H].  keep: uint8 [rows, H],
+ * non-zero = kept (the caller draws the mask).  h: required when o != NULL (nullable otherwise);
+ * y, mean [rows], rstd [rows] (fp32) required.  In bf16 mode the statistics are those of h as
+ * stored (rounded to bf16).  Requires 0 <= p_drop < 1, eps >= 0 (finite), H <= 24576
+ * (TP_EUNSUPPORTED above). */
+int tp_residual_ln_fwd(int tp_size, int rank, int sequence_parallel, int T, int H, int dtype,
+                       const void* x, const void* o, const unsigned char* keep, float p_drop,
+                       const void* gamma, const void* beta, float eps, void* h, void* y, float* mean,
+                       float* rstd, void* stream);
+
+/* Backward of tp_residual_ln_fwd on the same rows, with g = dy∘γ and x̂ = (h − mean)·rstd:
+ *   dh = dh_in + rstd·(g − mean_H(g) − x̂·mean_H(g·x̂))   (dh_in nullable: the gradient reaching h
+ *        along the residual stream; dh is also the gradient of x)
+ *   d_o = dh∘keep/(1 − p_drop)                             (nullable)
+ *   dγ = Σ_rows dy∘x̂ ;  dβ = Σ_rows dy                    (partials under sequence parallelism:
+ *        Σ_r over ranks is the full gradient; deterministic)
+ * mean and rstd are the forward's.  workspace: tp_workspace_bytes("tp_residual_ln_bwd", ...) (sized
+ * for all T rows, so it also serves the sequence-parallel call). */
+int tp_residual_ln_bwd(int tp_size, int rank, int sequence_parallel, int T, int H, int dtype,
+                       const void* dy, const void* dh_in, const void* h, const float* mean,
+                       const float* rstd, const void* gamma, const unsigned char* keep, float p_drop,
+                       void* dh, void* d_o, void* dgamma, void* dbeta, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* A9 — grouped expert MLP shard (MoE experts as grouped GEMMs: "Megatron-LM — 架构与原理", §6, TE
  * GroupedLinear).  Rows [off[e], off[e+1]) of the expert-sorted token matrix X_perm[rows, H] belong to
  * expert e (e < n_groups); each goes through expert e's column shard of fc1 with bias and GeLU and
@@ -159,7 +193,8 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
- * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_mlp_grouped_shard_fwd"; 0 for the others).  T = B*S; F is used by the
+ * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd";
+ * 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

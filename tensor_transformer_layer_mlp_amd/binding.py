@@ -18,7 +18,7 @@ TP_BF16, TP_F32 = 0, 1
 STATUS = {0: "TP_OK", -1: "TP_EINVAL", -2: "TP_ENULL", -3: "TP_EALIGN", -4: "TP_EUNSUPPORTED",
           -5: "TP_EWORKSPACE", -6: "TP_EHIP"}
 
-_I, _P, _Z = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_I, _P, _Z, _F = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 _SIGNATURES = {
     "tp_shard_range": (_I, [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "tp_qkv_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
@@ -29,6 +29,8 @@ _SIGNATURES = {
     "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
     "tp_attn_out_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
     "tp_attn_out_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
+    "tp_residual_ln_fwd": (_I, [_I] * 6 + [_P, _P, _P, _F, _P, _P, _F, _P, _P, _P, _P, _P]),
+    "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -253,6 +255,52 @@ def tp_attn_out_shard_bwd(tp_size, rank, B, S, H, n_heads, ctx_r, Wo_r, dO, dctx
                                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                      _stream(stream))
     _check(rc, "tp_attn_out_shard_bwd")
+
+
+def _ln_rows(tp_size, rank, sequence_parallel, T):
+    if not (1 <= tp_size and 0 <= rank < tp_size and T >= 0):
+        return None
+    return tp_shard_range(T, tp_size, rank)[1] if sequence_parallel else T
+
+
+def tp_residual_ln_fwd(tp_size, rank, sequence_parallel, T, H, x, o, keep, p_drop, gamma, beta, eps, h, y, mean,
+                       rstd, stream=None):
+    """Residual add with dropout, then LayerNorm, on the rank's rows (all T, or its sequence block
+    when sequence_parallel); keep is a uint8 tensor (non-zero = kept) or None."""
+    dt = x.dtype
+    rows = _ln_rows(tp_size, rank, sequence_parallel, T)
+    if rows is not None and H >= 1:
+        n = rows * H
+        for t, k, name in ((x, n, "x"), (o, n, "o"), (keep, n, "keep"), (gamma, H, "gamma"), (beta, H, "beta"),
+                           (h, n, "h"), (y, n, "y"), (mean, rows, "mean"), (rstd, rows, "rstd")):
+            _need(t, k, name)
+    rc = raw().tp_residual_ln_fwd(tp_size, rank, 1 if sequence_parallel else 0, T, H, _dtype_code(x),
+                                  _ptr(x, "x", dt), _ptr(o, "o", dt, True), _ptr(keep, "keep", torch.uint8, True),
+                                  float(p_drop), _ptr(gamma, "gamma", dt), _ptr(beta, "beta", dt), float(eps),
+                                  _ptr(h, "h", dt, True), _ptr(y, "y", dt), _ptr(mean, "mean", torch.float32),
+                                  _ptr(rstd, "rstd", torch.float32), _stream(stream))
+    _check(rc, "tp_residual_ln_fwd")
+
+
+def tp_residual_ln_bwd(tp_size, rank, sequence_parallel, T, H, dy, dh_in, h, mean, rstd, gamma, keep, p_drop,
+                       dh, d_o, dgamma, dbeta, workspace, stream=None):
+    dt = dy.dtype
+    rows = _ln_rows(tp_size, rank, sequence_parallel, T)
+    if rows is not None and H >= 1:
+        n = rows * H
+        for t, k, name in ((dy, n, "dy"), (dh_in, n, "dh_in"), (h, n, "h"), (mean, rows, "mean"), (rstd, rows, "rstd"),
+                           (gamma, H, "gamma"), (keep, n, "keep"), (dh, n, "dh"), (d_o, n, "d_o"),
+                           (dgamma, H, "dgamma"), (dbeta, H, "dbeta")):
+            _need(t, k, name)
+    rc = raw().tp_residual_ln_bwd(tp_size, rank, 1 if sequence_parallel else 0, T, H, _dtype_code(dy),
+                                  _ptr(dy, "dy", dt), _ptr(dh_in, "dh_in", dt, True), _ptr(h, "h", dt),
+                                  _ptr(mean, "mean", torch.float32), _ptr(rstd, "rstd", torch.float32),
+                                  _ptr(gamma, "gamma", dt), _ptr(keep, "keep", torch.uint8, True), float(p_drop),
+                                  _ptr(dh, "dh", dt), _ptr(d_o, "d_o", dt, True), _ptr(dgamma, "dgamma", dt),
+                                  _ptr(dbeta, "dbeta", dt), _ptr(workspace, "workspace", None, True),
+                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                  _stream(stream))
+    _check(rc, "tp_residual_ln_bwd")
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_group, X_perm, W1_r,

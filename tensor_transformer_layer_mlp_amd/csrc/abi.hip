@@ -1,6 +1,7 @@
 // C ABI of libtpshard: argument validation, shard geometry, and the launch sequence of each entry
 // point.  Every check happens on the host before anything is enqueued.  See include/tpshard.h.
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -132,6 +133,19 @@ int mlp_geom(int tp_size, int rank, int T, int H, int F, int dtype, MlpGeom* g) 
   TP_CHECK(H >= 1, TP_EINVAL, "H %d < 1", H);
   TP_CHECK(F >= tp_size, TP_EINVAL, "F %d < tp_size %d leaves a rank without columns", F, tp_size);
   shard(F, tp_size, rank, &g->f0, &g->Fr);
+  return TP_OK;
+}
+
+// Rows a residual-LayerNorm call covers: all T, or the rank's block of them under sequence parallelism.
+int ln_geom(int tp_size, int rank, int sequence_parallel, int T, int H, int dtype, int* rows) {
+  int st = check_rank_dtype(tp_size, rank, dtype);
+  if (st) return st;
+  TP_CHECK(T >= 0 && T <= INT_MAX / 4, TP_EINVAL, "T %d out of range", T);
+  TP_CHECK(H >= 1, TP_EINVAL, "H %d < 1", H);
+  TP_CHECK(H <= ln_max_h(), TP_EUNSUPPORTED, "H %d above the %d features a LayerNorm row holds", H, ln_max_h());
+  int off = 0;
+  *rows = T;
+  if (sequence_parallel) shard(T, tp_size, rank, &off, rows);
   return TP_OK;
 }
 
@@ -405,6 +419,46 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
   return rc;
 }
 
+int tp_residual_ln_fwd(int tp_size, int rank, int sequence_parallel, int T, int H, int dtype,
+                       const void* x, const void* o, const unsigned char* keep, float p_drop,
+                       const void* gamma, const void* beta, float eps, void* h, void* y, float* mean,
+                       float* rstd, void* stream) {
+  int rows = 0;
+  int st = ln_geom(tp_size, rank, sequence_parallel, T, H, dtype, &rows);
+  if (st) return st;
+  TP_CHECK(std::isfinite(p_drop) && p_drop >= 0.f && p_drop < 1.f, TP_EINVAL, "p_drop %g outside [0, 1)", p_drop);
+  TP_CHECK(std::isfinite(eps) && eps >= 0.f, TP_EINVAL, "eps %g is negative or not finite", eps);
+  const long n = (long)rows * H;
+  NEED(x, "x", n); MAYBE(o, "o"); MAYBE(keep, "keep"); NEED(gamma, "gamma", H); NEED(beta, "beta", H);
+  NEED(y, "y", n); NEED(mean, "mean", rows); NEED(rstd, "rstd", rows);
+  if (o) NEED(h, "h", n); else MAYBE(h, "h");
+  TP_TRY(launch_ln_fwd(dtype, rows, H, x, o, keep, (float)(1.0 / (1.0 - (double)p_drop)), gamma, beta, eps, h, y,
+                       mean, rstd, (hipStream_t)stream), "residual layernorm fwd");
+  return TP_OK;
+}
+
+int tp_residual_ln_bwd(int tp_size, int rank, int sequence_parallel, int T, int H, int dtype,
+                       const void* dy, const void* dh_in, const void* h, const float* mean,
+                       const float* rstd, const void* gamma, const unsigned char* keep, float p_drop,
+                       void* dh, void* d_o, void* dgamma, void* dbeta, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rows = 0;
+  int st = ln_geom(tp_size, rank, sequence_parallel, T, H, dtype, &rows);
+  if (st) return st;
+  TP_CHECK(std::isfinite(p_drop) && p_drop >= 0.f && p_drop < 1.f, TP_EINVAL, "p_drop %g outside [0, 1)", p_drop);
+  const long n = (long)rows * H;
+  NEED(dy, "dy", n); MAYBE(dh_in, "dh_in"); NEED(h, "h", n); NEED(mean, "mean", rows); NEED(rstd, "rstd", rows);
+  NEED(gamma, "gamma", H); MAYBE(keep, "keep"); NEED(dh, "dh", n); MAYBE(d_o, "d_o");
+  NEED(dgamma, "dgamma", H); NEED(dbeta, "dbeta", H);
+  const size_t need = align256(ln_bwd_ws_bytes(rows, H));
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_ln_bwd(dtype, rows, H, dy, dh_in, h, mean, rstd, gamma, keep, (float)(1.0 / (1.0 - (double)p_drop)),
+                       dh, d_o, dgamma, dbeta, (float*)workspace, (hipStream_t)stream), "residual layernorm bwd");
+  return TP_OK;
+}
+
 int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows,
                              int H, int F_group, int dtype, const void* X_perm, const void* W1_r,
                              const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
@@ -443,6 +497,12 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0) {
     if (n_heads < 1 || n_heads > (1 << 20)) return 0;
     return align256(grouped_ws_bytes(n_heads));
+  }
+  if (strcmp(fn, "tp_residual_ln_bwd") == 0) {
+    int rows = 0;
+    if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4) return 0;
+    if (ln_geom(tp_size, rank, 0, B * S, H, dtype, &rows)) return 0;
+    return align256(ln_bwd_ws_bytes(rows, H));
   }
   if (strcmp(fn, "tp_attn_out_shard_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;

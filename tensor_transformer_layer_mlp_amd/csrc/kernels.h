@@ -37,6 +37,23 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 size_t colsum_ws_bytes(int rows, int cols);
 hipError_t launch_colsum(int dtype, const void* in, long ld, int rows, int cols, float* ws,
                          void* out, hipStream_t s);
+// out[c] = Σ_{k < chunks} ws[k*cols + c] in that order (the second pass of launch_colsum).
+hipError_t launch_colsum_final(int dtype, const float* ws, int chunks, int cols, void* out, hipStream_t s);
+
+// Residual add with dropout, then LayerNorm over the H features of each of `rows` rows:
+// h = x + o∘keep·keep_scale (o, keep nullable), y = (h − mean)·rstd·γ + β, rstd = 1/√(var + eps).
+// In bf16 mode the statistics are taken over h as stored (rounded).  H <= ln_max_h().
+int ln_max_h();
+hipError_t launch_ln_fwd(int dtype, int rows, int H, const void* x, const void* o, const unsigned char* keep,
+                         float keep_scale, const void* gamma, const void* beta, float eps, void* h, void* y,
+                         float* mean, float* rstd, hipStream_t s);
+// dh = dh_in + rstd·(g − mean(g) − x̂·mean(g·x̂)), g = dy∘γ, x̂ = (h − mean)·rstd; do = dh∘keep·scale;
+// dγ = Σ dy∘x̂, dβ = Σ dy over the rows (fp32 partials per row block in ws, then a fixed-order sum).
+size_t ln_bwd_ws_bytes(int rows, int H);
+hipError_t launch_ln_bwd(int dtype, int rows, int H, const void* dy, const void* dh_in, const void* h,
+                         const float* mean, const float* rstd, const void* gamma, const unsigned char* keep,
+                         float keep_scale, void* dh, void* d_o, void* dgamma, void* dbeta, float* ws,
+                         hipStream_t s);
 
 // Causal attention over nh interleaved heads of width d (see the ABI header for the layout).
 bool attn_supported_dim(int d);

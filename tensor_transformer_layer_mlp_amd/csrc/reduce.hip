@@ -88,6 +88,15 @@ size_t colsum_ws_bytes(int rows, int cols) {
   return chunks * (size_t)cols * sizeof(float);
 }
 
+hipError_t launch_colsum_final(int dtype, const float* ws, int chunks, int cols, void* out, hipStream_t s) {
+  if (cols <= 0) return hipSuccess;
+  if (dtype == DT_BF16)
+    colsum_final_kernel<bf16><<<(cols + 63) / 64, 256, 0, s>>>(ws, chunks, cols, (bf16*)out);
+  else
+    colsum_final_kernel<float><<<(cols + 63) / 64, 256, 0, s>>>(ws, chunks, cols, (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_colsum(int dtype, const void* in, long ld, int rows, int cols, float* ws,
                          void* out, hipStream_t s) {
   if (cols <= 0) return hipSuccess;

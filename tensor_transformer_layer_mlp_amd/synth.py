@@ -156,6 +156,13 @@ def attn_out_bias(wl, dtype) -> Operand:
     return vector_blocks("bo", 0, wl.H, wl.w_std, dtype)
 
 
+def keep_mask(tag: str, shape, p_drop: float) -> np.ndarray:
+    """A dropout keep mask (uint8, 1 = kept): uniform draws in [0, 1) above p_drop.  The draws are
+    an input of the residual-dropout op, made here like every other random input."""
+    u = _rng(tag, 0).random(shape, dtype=np.float32)
+    return (u >= np.float32(p_drop)).astype(np.uint8)
+
+
 # ---- MoE routing (input construction only) -----------------------------------------------------
 
 def moe_assignments(tokens: int, n_experts: int, top_k: int, seed_tag="router_logits"):

@@ -125,6 +125,36 @@ def test_attn_out_validation(lib):
     assert b(2, 1, 2, 32, 64, 4, 2, P, P, P, P, P, None, P, 1 << 20, None) == -1    # dtype
 
 
+def _with(base, **kw):
+    a = list(base)
+    for i, v in kw.items():
+        a[int(i[1:])] = v
+    return a
+
+
+def test_residual_ln_validation(lib):
+    f = lib.tp_residual_ln_fwd
+    # tp, rank, sp, T, H, dtype, x, o, keep, p_drop, gamma, beta, eps, h, y, mean, rstd, stream
+    base = [2, 0, 0, 64, 128, 0, P, P, P, 0.1, P, P, 1e-5, P, P, P, P, None]
+    for kw, code in ((dict(a9=1.0), -1), (dict(a9=-0.1), -1), (dict(a9=float("nan")), -1),
+                     (dict(a12=-1.0), -1), (dict(a12=float("inf")), -1), (dict(a4=24577), -4), (dict(a4=0), -1),
+                     (dict(a3=-1), -1), (dict(a1=2), -1), (dict(a5=3), -1), (dict(a13=None), -2),
+                     (dict(a7=None, a13=None, a14=None), -2), (dict(a6=None), -2), (dict(a10=None), -2),
+                     (dict(a16=None), -2), (dict(a8=MIS), -3), (dict(a13=MIS), -3)):
+        assert f(*_with(base, **kw)) == code, kw
+    b = lib.tp_residual_ln_bwd
+    # tp, rank, sp, T, H, dtype, dy, dh_in, h, mean, rstd, gamma, keep, p_drop, dh, d_o, dgamma, dbeta, ws, wsb, stream
+    bb = [2, 1, 1, 64, 128, 0, P, P, P, P, P, P, P, 0.1, P, P, P, P, P, 1 << 20, None]
+    for kw, code in ((dict(a18=None, a19=0), -5), (dict(a19=16), -5), (dict(a18=P + 16), -3), (dict(a14=None), -2),
+                     (dict(a16=None), -2), (dict(a17=None), -2), (dict(a8=None), -2), (dict(a13=1.5), -1),
+                     (dict(a4=30000), -4), (dict(a12=MIS), -3)):
+        assert b(*_with(bb, **kw)) == code, kw
+    full = bd.tp_workspace_bytes("tp_residual_ln_bwd", 2, 1, 1, 64, 128, 1, 1, 0)
+    assert full >= 2 * 128 * 4 and full % 256 == 0     # dγ and dβ partials of one 64-row block
+    assert bd.tp_workspace_bytes("tp_residual_ln_bwd", 2, 1, 1, 64, 30000, 1, 1, 0) == 0
+    assert bd.tp_workspace_bytes("tp_residual_ln_fwd", 2, 1, 1, 64, 128, 1, 1, 0) == 0
+
+
 def test_workspace_bytes(lib):
     T, H, F, t = 64, 64, 256, 2
     got = bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 0)
