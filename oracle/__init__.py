@@ -12,4 +12,5 @@ from .tp_shard import (shard_range, qkv_column_range, slice_qkv, slice_fc1, slic
                        tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_heads_bwd,
                        tp_attn_out_shard_fwd, tp_attn_out_shard_bwd, dropout_add, layernorm,
                        layernorm_bwd, sp_rows, tp_residual_ln_fwd, tp_residual_ln_bwd,
-                       tp_mlp_grouped_shard_fwd, normwise_error)
+                       tp_mlp_grouped_shard_fwd, moe_route, moe_combine, tp_moe_shard_fwd,
+                       normwise_error)

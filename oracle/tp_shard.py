@@ -44,6 +44,14 @@ Readings where the pages are silent (numbered as in the design notes):
                    (kept values scaled by 1/(1-p)) with the keep mask an input (the method's random
                    draws are passed in).  Pre-norm blocks carry h on as the residual stream, post-norm
                    blocks carry y; the op is the same.
+  R14 MoE routing = each token's top-k experts by router logit (softmax is monotone, so the same
+                   choice as the top-k of the softmax probabilities); equal logits go to the lower
+                   expert id; the choice is made on the fp32 logits, as the device makes it.  Gate =
+                   that expert's softmax probability over all experts (no renormalisation over the
+                   k).  Dispatch order: rows sorted by (expert, token), stable.  No capacity limit.
+                   Combine = Σ_j gate_j · expert output, j in the token's top-k order; it is linear,
+                   so a rank may combine its fc2 partials before the all-reduce ([Arch] §4: route ->
+                   dispatch (permute) -> experts -> combine (unpermute)).
   R13 sequence parallelism = LayerNorm and dropout split along the sequence ([Overview]; [Arch], the
                    table under 它能做什么): rank r owns rows [off(T,t,r), off+cnt) of the flattened
                    tokens (the sequence itself when B = 1) and its dγ, dβ are partial sums over its
@@ -387,6 +395,54 @@ def tp_residual_ln_bwd(tp_size, rank, sequence_parallel, T, H, dy, dh_in, h, gam
         dh = dh + dh_in
     do = dh * np.asarray(keep, dtype=np.float64) / (1.0 - p_drop) if keep is not None else dh.copy()
     return {"dh": dh, "do": do, "dgamma": dgamma, "dbeta": dbeta}
+
+
+def moe_route(logits32, top_k: int):
+    """Top-k routing (reading R14).  logits32: float32 [tokens, E].  Returns gates [tokens, k]
+    (float64 softmax probabilities of the chosen experts), experts [tokens, k] (descending logit,
+    ties to the lower id), group_offsets [E+1], row_token [tokens·k] (the token of each
+    expert-sorted row) and token_row [tokens, k] (the row of each (token, j))."""
+    lg = np.asarray(logits32, dtype=np.float32)
+    n, E = lg.shape
+    experts = np.zeros((n, top_k), dtype=np.int64)
+    for t in range(n):
+        # sort by (−logit, id): compare the float32 values exactly, lower id first on ties
+        order = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))
+        experts[t] = order[:top_k]
+    l64 = lg.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    gates = np.take_along_axis(p, experts, axis=1)
+    counts = np.bincount(experts.reshape(-1), minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    row_token = np.zeros(n * top_k, dtype=np.int64)
+    token_row = np.zeros((n, top_k), dtype=np.int64)
+    fill = offsets[:-1].copy()
+    for t in range(n):                      # token order within each expert: stable
+        for j in range(top_k):
+            e = experts[t, j]
+            row_token[fill[e]] = t
+            token_row[t, j] = fill[e]
+            fill[e] += 1
+    return {"gates": gates, "experts": experts, "group_offsets": offsets, "row_token": row_token,
+            "token_row": token_row}
+
+
+def moe_combine(Z_rows, gates, token_row):
+    """out[t] = Σ_j gates[t, j] · Z_rows[token_row[t, j]] (reading R14)."""
+    out = np.zeros((gates.shape[0], Z_rows.shape[1]))
+    for j in range(gates.shape[1]):
+        out += gates[:, j:j + 1] * Z_rows[token_row[:, j]]
+    return out
+
+
+def tp_moe_shard_fwd(tp_size, rank, X, route, W1_r, b1_r, W2_r):
+    """The MoE expert block on rank r: dispatch (the rows of X in expert-sorted order), each
+    expert's fc1 column shard with bias and GeLU and its fc2 row shard, then the gate-weighted
+    combine of the rank's partials.  Σ_r over ranks is the full MoE output ([Arch] §4, §6)."""
+    Xp = np.asarray(X)[route["row_token"]]
+    Z = tp_mlp_grouped_shard_fwd(tp_size, rank, route["group_offsets"], Xp, W1_r, b1_r, W2_r)
+    return {"out": moe_combine(Z, route["gates"], route["token_row"]), "Z": Z}
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):

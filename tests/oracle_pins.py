@@ -13,6 +13,9 @@ fails.  What pins what:
   closed      attention closed forms: S=1, query 0, Q=0 (prefix mean, LSE = log(i+1)), constant keys
               (LSE = q·k/√d + log(i+1)), one dominant key, dV for Q=0
   fd          central finite differences in fp64 for every gradient output
+  moe         routing against numpy's stable argsort, exact ties to the lower id, permutation and
+              inverse invariants, gates summing to 1 when k = E; the whole MoE block against scalar
+              per-token loops; E = k = 1 equals the dense MLP shard; Σ over TP ranks = unsharded
   layernorm   scalar loops; a textbook row; zero mean / unit mean square (eps = 0); shift and scale
               invariance; constant rows; dropout-add cases by hand; finite differences through the
               fused residual + dropout + LayerNorm op; the sequence-parallel split (row blocks
@@ -504,5 +507,64 @@ def pin_layernorm():
     assert T.sp_rows(Tt, t, 2, False) == (0, Tt)
 
 
+def pin_moe():
+    g = _rng(61)
+    n, E, k = 23, 7, 3
+    lg = g.standard_normal((n, E)).astype(np.float32)
+    lg[4, :] = 0.5                         # all equal: experts 0, 1, 2 in that order
+    lg[9, 5] = lg[9, 2] = lg[9].max() + 1  # a tie at the top between experts 2 and 5
+    r = T.moe_route(lg, k)
+    want = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    assert (r["experts"] == want).all(), "top-k differs from a stable argsort of -logits"
+    assert list(r["experts"][4]) == [0, 1, 2] and list(r["experts"][9][:2]) == [2, 5], "ties to the lower id"
+    p = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    _close(r["gates"], np.take_along_axis(p, want, axis=1), 1e-15, "gates = softmax probabilities")
+    assert (r["gates"].sum(axis=1) <= 1 + 1e-12).all()
+    off, rt, tr = r["group_offsets"], r["row_token"], r["token_row"]
+    assert off[0] == 0 and off[-1] == n * k and (np.diff(off) == np.bincount(want.reshape(-1), minlength=E)).all()
+    for e in range(E):
+        blk = rt[off[e]:off[e + 1]]
+        assert (np.diff(blk) > 0).all(), "rows of an expert in token order"
+        assert all(e in want[t] for t in blk)
+    assert sorted(tr.reshape(-1).tolist()) == list(range(n * k)), "token_row is a permutation"
+    for t in range(n):
+        for j in range(k):
+            row = tr[t, j]
+            assert rt[row] == t and off[want[t, j]] <= row < off[want[t, j] + 1]
+    # k = E: the gates are the whole softmax; combining equal rows returns the row itself
+    rr = T.moe_route(lg, E)
+    _close(rr["gates"].sum(axis=1), np.ones(n), 1e-14, "k = E gates sum to 1")
+    c = g.standard_normal(5)
+    _close(T.moe_combine(np.tile(c, (n * E, 1)), rr["gates"], rr["token_row"]), np.tile(c, (n, 1)), 1e-14,
+           "combine of equal rows")
+    # the whole block against per-token scalar loops, on a 2-way split of each expert's ffn columns
+    n, E, k, H, Fe, t = 6, 4, 2, 5, 6, 2
+    X = g.standard_normal((n, H))
+    lg = g.standard_normal((n, E)).astype(np.float32)
+    W1, b1 = g.standard_normal((E, H, Fe)) * 0.5, g.standard_normal((E, Fe)) * 0.5
+    W2 = g.standard_normal((E, Fe, H)) * 0.5
+    r = T.moe_route(lg, k)
+    total = np.zeros((n, H))
+    for rank in range(t):
+        f0, fr = T.shard_range(Fe, t, rank)
+        out = T.tp_moe_shard_fwd(t, rank, X, r, W1[:, :, f0:f0 + fr], b1[:, f0:f0 + fr], W2[:, f0:f0 + fr])["out"]
+        ref = np.zeros((n, H))
+        for tok in range(n):
+            for j in range(k):
+                e = r["experts"][tok, j]
+                _, _, z = bf.mlp_forward(X[tok:tok + 1], W1[e][:, f0:f0 + fr], b1[e][f0:f0 + fr],
+                                         W2[e][f0:f0 + fr], None)
+                ref[tok] += r["gates"][tok, j] * np.array(z[0])
+        _close(out, ref, 1e-13, f"MoE block r{rank} vs scalar loops")
+        total += out
+    full = T.tp_moe_shard_fwd(1, 0, X, r, W1, b1, W2)["out"]
+    _close(total, full, 1e-13, "MoE: sum over TP ranks = unsharded")
+    # one expert, top-1: the gate is 1 and the block is the dense MLP shard (no fc2 bias)
+    r1 = T.moe_route(g.standard_normal((n, 1)).astype(np.float32), 1)
+    d = T.tp_moe_shard_fwd(1, 0, X, r1, W1[:1], b1[:1], W2[:1])["out"]
+    _close(d, T.tp_mlp_shard_fwd(1, 0, n, H, Fe, X, W1[0], b1[0], W2[0], None)["Z"], 1e-14, "E = k = 1")
+
+
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
-            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm]
+            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe]

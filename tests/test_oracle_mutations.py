@@ -159,6 +159,55 @@ def _ln_bwd_ignores_dh_in(tp_size, rank, sp, Tt, H, dy, dh_in, h, gamma, keep, p
 _ORIG_LN_BWD = T.tp_residual_ln_bwd
 
 
+def _route_variant(ties_high=False, renorm=False, by_token=False):
+    orig = _ORIG_ROUTE
+
+    def f(logits32, top_k):
+        lg = np.asarray(logits32, dtype=np.float32)
+        if ties_high:
+            lg2 = lg[:, ::-1]
+            r = orig(lg2, top_k)
+            E = lg.shape[1]
+            ex = E - 1 - r["experts"]
+            # rebuild the rest from the flipped choice with the same bookkeeping
+            return _rebuild(lg, ex)
+        r = orig(lg, top_k)
+        if renorm:
+            r["gates"] = r["gates"] / r["gates"].sum(axis=1, keepdims=True)
+        if by_token:
+            n, k = r["experts"].shape
+            r["row_token"] = np.repeat(np.arange(n), k)
+            r["token_row"] = np.arange(n * k).reshape(n, k)
+        return r
+    return f
+
+
+def _rebuild(lg, experts):
+    n, k = experts.shape
+    E = lg.shape[1]
+    l64 = lg.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    counts = np.bincount(experts.reshape(-1), minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    fill, rt, tr = off[:-1].copy(), np.zeros(n * k, dtype=np.int64), np.zeros((n, k), dtype=np.int64)
+    for t in range(n):
+        for j in range(k):
+            e = experts[t, j]
+            rt[fill[e]] = t
+            tr[t, j] = fill[e]
+            fill[e] += 1
+    return {"gates": np.take_along_axis(p, experts, axis=1), "experts": experts, "group_offsets": off,
+            "row_token": rt, "token_row": tr}
+
+
+def _combine_first_choice_only(Z_rows, gates, token_row):
+    return gates[:, :1] * Z_rows[token_row[:, 0]]
+
+
+_ORIG_ROUTE = T.moe_route
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -192,6 +241,10 @@ MUTANTS = {
     "ln_bwd_dgamma_without_xhat": {"layernorm_bwd": _ln_bwd_variant(dgamma_plain=True)},
     "dropout_without_rescale": {"dropout_add": _dropout_add_unscaled},
     "ln_bwd_ignores_residual_grad": {"tp_residual_ln_bwd": _ln_bwd_ignores_dh_in},
+    "moe_ties_to_higher_id": {"moe_route": _route_variant(ties_high=True)},
+    "moe_gates_renormalised": {"moe_route": _route_variant(renorm=True)},
+    "moe_rows_in_token_order": {"moe_route": _route_variant(by_token=True)},
+    "moe_combine_first_choice_only": {"moe_combine": _combine_first_choice_only},
 }
 
 
