@@ -192,9 +192,40 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
                              const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* MoE routing, the first of the four beats route -> dispatch (permute) -> experts -> combine
+ * (unpermute) of "Megatron-LM — 架构与原理", §4, for one device's tokens.  logits: fp32 [tokens, E].
+ * Each token takes its top_k experts by logit — the same choice as the top_k of the softmax, made
+ * on the fp32 logits themselves; equal logits go to the lower expert id — in descending order:
+ *   expert_idx[t, j], gates[t, j] = softmax(logits[t])[expert_idx[t, j]]  (fp32, not renormalised)
+ * and the dispatch order, rows sorted by (expert, token):
+ *   group_offsets[E+1] (expert e owns rows [off[e], off[e+1])), row_token[tokens·k] (the token of
+ *   each row), token_row[tokens, k] (the row of (t, j)).
+ * Integer outputs are deterministic and exact.  Logits must be finite.  E <= 1024, top_k <= 32.
+ * All arrays int32 / fp32 in device memory, 4-byte aligned.  No workspace. */
+int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, float* gates, int* expert_idx,
+                 int* group_offsets, int* row_token, int* token_row, void* stream);
+
+/* The MoE expert block of one tensor-parallel rank, on tp_moe_route's outputs: the dispatch is fused
+ * into fc1's operand loads (row r of the expert-sorted matrix is read straight from X[row_token[r]],
+ * no permuted copy of X is made), each expert's fc1 column shard with bias and GeLU, its fc2 row
+ * shard, and the gate-weighted combine of the rank's partials:
+ *   Y_r[r] = GeLU(X[row_token[r]]·W1_r[e] + b1_r[e]),  Z_r[r] = Y_r[r]·W2_r[e]   (r in expert e's rows)
+ *   out_r[t] = Σ_j gates[t, j]·Z_r[token_row[t, j]]   (fp32 sum, j in order)
+ * The combine is linear, so combining before the all-reduce gives the same sum over ranks with a
+ * message k times smaller ([tokens, H] instead of [tokens·k, H]).  X [tokens, H]; W1_r [E, H, F_r],
+ * b1_r [E, F_r], W2_r [E, F_r, H] with F_r = cnt(F_expert, t, r); Z_r [tokens·k, H] and Y_r
+ * [tokens·k, F_r] required (written), A1_r nullable; out_r [tokens, H].  Offsets are clamped on the
+ * device as in tp_mlp_grouped_shard_fwd; gathered and combined row indices outside their ranges read
+ * as zero.  The fused gather needs X under 2 GiB for the bf16 tiled kernels (larger X runs the
+ * generic kernels).  workspace: tp_workspace_bytes("tp_moe_shard_fwd", ...) with n_heads = E. */
+int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
+                     const void* X, const float* gates, const int* group_offsets, const int* row_token,
+                     const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
+                     void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
- * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd";
- * 0 for the others).  T = B*S; F is used by the
+ * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd",
+ * "tp_moe_shard_fwd"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

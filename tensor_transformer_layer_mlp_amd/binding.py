@@ -32,6 +32,8 @@ _SIGNATURES = {
     "tp_residual_ln_fwd": (_I, [_I] * 6 + [_P, _P, _P, _F, _P, _P, _F, _P, _P, _P, _P, _P]),
     "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
+    "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P]),
+    "tp_moe_shard_fwd": (_I, [_I] * 8 + [_P] * 12 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -320,6 +322,43 @@ def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_
         _ptr(workspace, "workspace", None, True),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
     _check(rc, "tp_mlp_grouped_shard_fwd")
+
+
+def tp_moe_route(tokens, n_experts, top_k, logits, gates, expert_idx, group_offsets, row_token, token_row,
+                 stream=None):
+    """Top-k routing and the expert-sorted dispatch order (int32 outputs, fp32 gates)."""
+    n = tokens * top_k if tokens >= 0 and top_k >= 1 else 0
+    for t, k, name in ((logits, tokens * n_experts, "logits"), (gates, n, "gates"), (expert_idx, n, "expert_idx"),
+                       (group_offsets, n_experts + 1, "group_offsets"), (row_token, n, "row_token"),
+                       (token_row, n, "token_row")):
+        _need(t, k, name)
+    rc = raw().tp_moe_route(tokens, n_experts, top_k, _ptr(logits, "logits", torch.float32),
+                            _ptr(gates, "gates", torch.float32), _ptr(expert_idx, "expert_idx", torch.int32),
+                            _ptr(group_offsets, "group_offsets", torch.int32), _ptr(row_token, "row_token", torch.int32),
+                            _ptr(token_row, "token_row", torch.int32), _stream(stream))
+    _check(rc, "tp_moe_route")
+
+
+def tp_moe_shard_fwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, gates, group_offsets, row_token,
+                     token_row, W1_r, b1_r, W2_r, out_r, Z_r, A1_r, Y_r, workspace, stream=None):
+    dt = X.dtype
+    Fr = _cols(tp_size, rank, F_expert)
+    if Fr and tokens >= 0 and top_k >= 1 and H >= 1 and n_experts >= 1:
+        n, E = tokens * top_k, n_experts
+        for t, k, name in ((X, tokens * H, "X"), (gates, n, "gates"), (group_offsets, E + 1, "group_offsets"),
+                           (row_token, n, "row_token"), (token_row, n, "token_row"), (W1_r, E * H * Fr, "W1_r"),
+                           (b1_r, E * Fr, "b1_r"), (W2_r, E * Fr * H, "W2_r"), (out_r, tokens * H, "out_r"),
+                           (Z_r, n * H, "Z_r"), (A1_r, n * Fr, "A1_r"), (Y_r, n * Fr, "Y_r")):
+            _need(t, k, name)
+    rc = raw().tp_moe_shard_fwd(
+        tp_size, rank, tokens, H, n_experts, top_k, F_expert, _dtype_code(X), _ptr(X, "X", dt),
+        _ptr(gates, "gates", torch.float32), _ptr(group_offsets, "group_offsets", torch.int32),
+        _ptr(row_token, "row_token", torch.int32), _ptr(token_row, "token_row", torch.int32),
+        _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt), _ptr(W2_r, "W2_r", dt), _ptr(out_r, "out_r", dt),
+        _ptr(Z_r, "Z_r", dt), _ptr(A1_r, "A1_r", dt, True), _ptr(Y_r, "Y_r", dt),
+        _ptr(workspace, "workspace", None, True),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
+    _check(rc, "tp_moe_shard_fwd")
 
 
 def workspace(fn, tp_size, rank, B, S, H, n_heads, F, dtype, device="cuda"):

@@ -155,6 +155,12 @@ int ln_geom(int tp_size, int rank, int sequence_parallel, int T, int H, int dtyp
     TP_CHECK((p) != nullptr || (n) == 0, TP_ENULL, "%s is NULL", (name));             \
     TP_CHECK(aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name));           \
   } while (0)
+// The same for 4-byte element arrays (indices, gates, logits): 4-byte alignment.
+#define NEED4(p, name, n)                                                             \
+  do {                                                                                \
+    TP_CHECK((p) != nullptr || (n) == 0, TP_ENULL, "%s is NULL", (name));             \
+    TP_CHECK(((uintptr_t)(p) & 3u) == 0, TP_EALIGN, "%s is not 4-byte aligned", (name)); \
+  } while (0)
 #define MAYBE(p, name)                                                                   \
   do {                                                                                   \
     TP_CHECK((p) == nullptr || aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name)); \
@@ -480,6 +486,51 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
   return TP_OK;
 }
 
+int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, float* gates, int* expert_idx,
+                 int* group_offsets, int* row_token, int* token_row, void* stream) {
+  TP_CHECK(tokens >= 0, TP_EINVAL, "tokens %d < 0", tokens);
+  TP_CHECK(n_experts >= 1 && n_experts <= moe_max_experts(), TP_EUNSUPPORTED, "n_experts %d outside [1, %d]",
+           n_experts, moe_max_experts());
+  TP_CHECK(top_k >= 1 && top_k <= n_experts && top_k <= moe_max_top_k(), TP_EINVAL,
+           "top_k %d outside [1, min(n_experts, %d)]", top_k, moe_max_top_k());
+  TP_CHECK((long)tokens * top_k <= INT_MAX / 4 && (long)tokens * n_experts <= INT_MAX, TP_EINVAL, "too many tokens");
+  const long n = (long)tokens * top_k;
+  NEED4(logits, "logits", (long)tokens * n_experts); NEED4(gates, "gates", n); NEED4(expert_idx, "expert_idx", n);
+  NEED4(group_offsets, "group_offsets", n_experts + 1); NEED4(row_token, "row_token", n);
+  NEED4(token_row, "token_row", n);
+  TP_TRY(launch_moe_route(tokens, n_experts, top_k, logits, gates, expert_idx, group_offsets, row_token, token_row,
+                          (hipStream_t)stream), "moe route");
+  return TP_OK;
+}
+
+int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
+                     const void* X, const float* gates, const int* group_offsets, const int* row_token,
+                     const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
+                     void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream) {
+  TP_CHECK(tokens >= 0 && top_k >= 1 && (long)tokens * top_k <= INT_MAX / 4, TP_EINVAL,
+           "tokens %d, top_k %d out of range", tokens, top_k);
+  TP_CHECK(n_experts >= 1 && n_experts <= (1 << 20), TP_EINVAL, "n_experts %d out of range", n_experts);
+  TP_CHECK(top_k <= n_experts, TP_EINVAL, "top_k %d > n_experts %d", top_k, n_experts);
+  const int rows = tokens * top_k;
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, rows, H, F_expert, dtype, &g);
+  if (st) return st;
+  const long n = (long)rows;
+  NEED(X, "X", (long)tokens * H); NEED4(gates, "gates", n); NEED4(group_offsets, "group_offsets", 1);
+  NEED4(row_token, "row_token", n); NEED4(token_row, "token_row", n);
+  NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1); NEED(out_r, "out_r", (long)tokens * H);
+  NEED(Z_r, "Z_r", n * H); NEED(Y_r, "Y_r", n); MAYBE(A1_r, "A1_r");
+  const size_t need = align256(grouped_ws_bytes(n_experts));
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  TP_TRY(launch_mlp_grouped(dtype, n_experts, group_offsets, rows, H, g.Fr, X, W1_r, b1_r, W2_r, Z_r, A1_r, Y_r,
+                            workspace, s, row_token, tokens), "moe experts");
+  TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, Z_r, gates, token_row, rows, out_r, s), "moe combine");
+  return TP_OK;
+}
+
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H, int n_heads,
                           int F, int dtype) {
   if (fn == nullptr) return 0;
@@ -494,7 +545,7 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
     return qkv_bwd_ws(g.T, g.Nq);
   }
-  if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0) {
+  if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0 || strcmp(fn, "tp_moe_shard_fwd") == 0) {
     if (n_heads < 1 || n_heads > (1 << 20)) return 0;
     return align256(grouped_ws_bytes(n_heads));
   }

@@ -138,6 +138,21 @@ __device__ __forceinline__ void load_tile(const Operand& op, int mn0, int k0, in
   }
 }
 
+// The K-major A operand with its rows gathered: piece j of this lane reads row ga[j] (an element
+// offset into the `bytes`-byte matrix at X, or -1 for a row outside it or past the tile) at k0 + c[j].
+template <int IPW>
+__device__ __forceinline__ void load_tile_gather(const bf16* X, unsigned bytes, int k0, int K, TP_LDS char* dst,
+                                                 const int (&ga)[IPW], const int (&c)[IPW], int wave) {
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const bool ok = ga[j] >= 0 && k0 + c[j] < K;
+    const unsigned off = ((unsigned)ga[j] + (unsigned)(k0 + c[j])) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TP_LDS void*)(dst + (wave * IPW + j) * 1024), 16,
+                                             ok ? off : OOB, 0, 0, 0);
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4 v) {
   // four consecutive columns n .. n+3 of row m (N is a multiple of 8, so all four are in range)
@@ -159,9 +174,10 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
 }
 
 // One BM x BN output tile at (m0, n0): the k loop over LDS stages and the fused epilogue.
-template <class Cfg, bool AK, bool BK, int EPI>
+template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
                                           int lane, int rot = 0) {
+  static_assert(!GATHER || AK, "rows are gathered for a K-major A only");
   constexpr int LA = AK ? Cfg::BM : Cfg::PM, LB = BK ? Cfg::BN : Cfg::PN;   // rows or pitch
   constexpr int A_BYTES = Cfg::template bytes<AK, Cfg::BM>(), B_BYTES = Cfg::template bytes<BK, Cfg::BN>();
   constexpr int IPW_A = A_BYTES / 1024 / Cfg::NW, IPW_B = B_BYTES / 1024 / Cfg::NW;   // loads per wave
@@ -173,6 +189,22 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
   for (int j = 0; j < IPW_A; ++j) piece<AK, LA, Cfg::BKT>((wave * IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
 #pragma unroll
   for (int j = 0; j < IPW_B; ++j) piece<BK, LB, Cfg::BKT>((wave * IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+
+  int ga[IPW_A];   // gathered A: element offset of each piece's source row, -1 outside
+  unsigned gbytes = 0;
+  if constexpr (GATHER) {
+    gbytes = (unsigned)((long)d.a_rows_n * d.lda * 2);
+#pragma unroll
+    for (int j = 0; j < IPW_A; ++j) {
+      const int m = m0 + ar[j];
+      const int src = m < d.M ? d.a_rows[m] : -1;
+      ga[j] = (src >= 0 && src < d.a_rows_n) ? src * (int)d.lda : -1;
+    }
+  }
+  auto load_a = [&](int k, TP_LDS char* dst) {
+    if constexpr (GATHER) load_tile_gather<IPW_A>((const bf16*)d.A, gbytes, k, d.K, dst, ga, ac, wave);
+    else load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, k, d.K, dst, ar, ac, wave);
+  };
 
   const int wm = (wave / Cfg::WN) * Cfg::TM, wn = (wave % Cfg::WN) * Cfg::TN;
   f32x4 acc[Cfg::FM][Cfg::FN];
@@ -192,7 +224,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
     if (t < nk) {
-      load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, kpos(t), d.K, lds + t * Cfg::STAGE, ar, ac, wave);
+      load_a(kpos(t), lds + t * Cfg::STAGE);
       load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, kpos(t), d.K, lds + t * Cfg::STAGE + A_BYTES, br, bc, wave);
     }
   int cur_stage = 0;
@@ -221,7 +253,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
       if (ns >= Cfg::STAGES) ns -= Cfg::STAGES;
       TP_LDS char* nxt = lds + ns * Cfg::STAGE;
       const int k1 = kpos(kt + Cfg::STAGES - 1);
-      load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, k1, d.K, nxt, ar, ac, wave);
+      load_a(k1, nxt);
       load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + A_BYTES, br, bc, wave);
     }
 #pragma unroll
@@ -351,7 +383,7 @@ struct GroupedArgs {
 };
 
 
-template <class Cfg, int EPI>
+template <class Cfg, int EPI, bool GATHER>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void gemm_bf16_grouped_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -376,14 +408,15 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   const int row0 = g.off[e] + (mt - g.prefix[e]) * Cfg::BM;
   GemmDesc d = g.d;
   d.M = g.off[e + 1] - row0;           // rows of this expert from row0 on (>= 1)
-  d.A = (const bf16*)g.d.A + (long)row0 * g.d.lda;
+  if constexpr (GATHER) d.a_rows = g.d.a_rows + row0;   // A stays the whole gathered-from matrix
+  else d.A = (const bf16*)g.d.A + (long)row0 * g.d.lda;
   d.B = (const bf16*)g.d.B + (long)e * g.b_stride;
   d.C = (bf16*)g.d.C + (long)row0 * g.d.ldc;
   if (g.d.C2) d.C2 = (bf16*)g.d.C2 + (long)row0 * g.d.ldc;
   if (g.d.bias) d.bias = (const bf16*)g.d.bias + (long)e * g.bias_stride;
   // k loops start at k-tile mt (mod the count): the row tiles of the same expert stream their rows
   // of A through different memory channels at the same moment (measured: fc1 2x faster)
-  gemm_tile<Cfg, true, false, EPI>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
+  gemm_tile<Cfg, true, false, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
@@ -488,9 +521,16 @@ static hipError_t grouped_t(const GroupedArgs& g, int max_mtiles, hipStream_t s)
   const long tiles = (long)max_mtiles * ((g.d.N + Cfg::BN - 1) / Cfg::BN);
   if (tiles > 0x7ffffff0L) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
-  if (g.d.epi == EPI_BIAS_GELU) gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU><<<grid, Cfg::NT, 0, s>>>(g);
-  else if (g.d.epi == EPI_STORE) gemm_bf16_grouped_kernel<Cfg, EPI_STORE><<<grid, Cfg::NT, 0, s>>>(g);
-  else return hipErrorNotSupported;
+  if (g.d.a_rows) {
+    if (g.d.epi != EPI_BIAS_GELU || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, true><<<grid, Cfg::NT, 0, s>>>(g);
+  } else if (g.d.epi == EPI_BIAS_GELU) {
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, false><<<grid, Cfg::NT, 0, s>>>(g);
+  } else if (g.d.epi == EPI_STORE) {
+    gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false><<<grid, Cfg::NT, 0, s>>>(g);
+  } else {
+    return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

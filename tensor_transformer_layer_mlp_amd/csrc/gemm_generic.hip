@@ -55,7 +55,14 @@ __device__ __forceinline__ void generic_tile(const GemmDesc& d, int m0, int n0) 
       if (d.a_kmajor) { m = i / BK; k = i % BK; } else { k = i / GBM; m = i % GBM; }
       const int gm = m0 + m, gk = k0 + k;
       T v = from_f32<T>(0.f);
-      if (gm < d.M && gk < d.K) v = d.a_kmajor ? A[(long)gm * d.lda + gk] : A[(long)gk * d.lda + gm];
+      if (gm < d.M && gk < d.K) {
+        if (d.a_rows) {          // gathered rows (K-major A only); outside [0, a_rows_n) reads zero
+          const int src = d.a_rows[gm];
+          if (src >= 0 && src < d.a_rows_n) v = A[(long)src * d.lda + gk];
+        } else {
+          v = d.a_kmajor ? A[(long)gm * d.lda + gk] : A[(long)gk * d.lda + gm];
+        }
+      }
       As[m][k] = v;
     }
     for (int i = tid; i < GBN * BK; i += 256) {
@@ -116,7 +123,8 @@ __global__ __launch_bounds__(256) void gemm_generic_grouped_kernel(GemmDesc g, c
   const int row0 = off[e] + (mt - prefix[e]) * GBM;
   GemmDesc d = g;
   d.M = off[e + 1] - row0;
-  d.A = (const T*)g.A + (long)row0 * g.lda;
+  if (g.a_rows) d.a_rows = g.a_rows + row0;   // A stays the whole gathered-from matrix
+  else d.A = (const T*)g.A + (long)row0 * g.lda;
   d.B = (const T*)g.B + (long)e * b_stride;
   d.C = (T*)g.C + (long)row0 * g.ldc;
   if (g.C2) d.C2 = (T*)g.C2 + (long)row0 * g.ldc;

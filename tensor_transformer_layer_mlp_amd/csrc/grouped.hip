@@ -65,7 +65,7 @@ size_t grouped_ws_bytes(int groups) { return (size_t)3 * (groups + 1) * sizeof(i
 
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
-                              void* A1, void* Y, void* ws, hipStream_t s) {
+                              void* A1, void* Y, void* ws, hipStream_t s, const int* row_token, int tokens) {
   if (rows <= 0) return hipSuccess;
   int* off_s = (int*)ws;
   int* prefix1 = off_s + (groups + 1);       // m-tiles of fc1's tile height
@@ -79,6 +79,8 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   fc1.B = W1; fc1.ldb = Fr; fc1.b_kmajor = false;
   fc1.C = Y; fc1.ldc = Fr; fc1.C2 = A1; fc1.bias = b1; fc1.epi = EPI_BIAS_GELU; fc1.dtype = dtype;
   GemmDesc fc2 = fc1;
+  fc1.a_rows = row_token;          // nullptr: X is already in expert-sorted order
+  fc1.a_rows_n = tokens;
   fc2.N = H; fc2.K = Fr;
   fc2.A = Y; fc2.lda = Fr;
   fc2.B = W2; fc2.ldb = H;
@@ -86,7 +88,9 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
 
   // Each expert's slice is a plain row-major problem with the same leading dimensions, so the tiled
   // kernel's alignment rules are those of the whole matrices.
-  const bool tiled = gemm_bf16_eligible(fc1) && gemm_bf16_eligible(fc2);
+  // (the tiled gather addresses X through one 32-bit buffer range: X must stay under 2 GiB)
+  const bool tiled = gemm_bf16_eligible(fc1) && gemm_bf16_eligible(fc2) &&
+                     (!row_token || (long)tokens * H * 2 <= 0x7fffffffL);
   const int bm1 = tiled ? gemm_bf16_grouped_bm(fc1.K) : gemm_generic_grouped_bm();
   const int bm2 = tiled ? gemm_bf16_grouped_bm(fc2.K) : gemm_generic_grouped_bm();
   const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
@@ -98,11 +102,13 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
     if (e != hipSuccess) return e;
   }
   const double f1 = 2.0 * rows * (double)Fr * H;
-  const double by1 = es * ((double)rows * H + (double)groups * H * Fr + (A1 ? 2.0 : 1.0) * rows * Fr);
+  const double by1 = es * ((double)rows * H + (double)groups * H * Fr + (A1 ? 2.0 : 1.0) * rows * Fr) +
+                     (row_token ? 4.0 * rows : 0.0);
   const double by2 = es * ((double)rows * Fr + (double)groups * Fr * H + (double)rows * H);
   if (tiled) {
     {
-      ProfScope p("gemm_bf16_grouped<fc1, bias+gelu>", s, f1, by1);
+      ProfScope p(row_token ? "gemm_bf16_grouped<fc1, gather, bias+gelu>" : "gemm_bf16_grouped<fc1, bias+gelu>",
+                  s, f1, by1);
       hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
       if (e != hipSuccess) return e;
     }
@@ -110,7 +116,8 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
     return launch_gemm_bf16_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
   }
   {
-    ProfScope p("gemm_generic_grouped<fc1, bias+gelu>", s, f1, by1);
+    ProfScope p(row_token ? "gemm_generic_grouped<fc1, gather, bias+gelu>" : "gemm_generic_grouped<fc1, bias+gelu>",
+                s, f1, by1);
     hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }

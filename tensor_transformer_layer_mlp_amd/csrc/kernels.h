@@ -29,6 +29,10 @@ struct GemmDesc {
   const void* aux; long ld_aux;
   void* C2;
   int dtype;
+  // Row gather of a K-major A (grouped GEMMs only): when a_rows is set, row m of A is row a_rows[m]
+  // of the a_rows_n-row matrix at A; indices outside [0, a_rows_n) read as zero rows.
+  const int* a_rows;
+  int a_rows_n;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
@@ -66,8 +70,19 @@ hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* q
 
 // Grouped expert MLP shard (rows [off[e], off[e+1]) use expert e's weights); off is device memory.
 size_t grouped_ws_bytes(int groups);
+// With row_token set, row r of the expert-sorted matrix is row row_token[r] of X (tokens rows),
+// gathered inside fc1's operand loads.
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
-                              void* A1, void* Y, void* ws, hipStream_t s);
+                              void* A1, void* Y, void* ws, hipStream_t s, const int* row_token = nullptr,
+                              int tokens = 0);
+
+// MoE routing and combine (see moe.hip).
+int moe_max_experts();
+int moe_max_top_k();
+hipError_t launch_moe_route(int tokens, int experts, int top_k, const float* logits, float* gates, int* expert_idx,
+                            int* group_offsets, int* row_token, int* token_row, hipStream_t s);
+hipError_t launch_moe_combine(int dtype, int tokens, int top_k, int H, const void* Z, const float* gates,
+                              const int* token_row, int rows, void* out, hipStream_t s);
 
 }  // namespace tp

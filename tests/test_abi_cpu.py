@@ -155,6 +155,23 @@ def test_residual_ln_validation(lib):
     assert bd.tp_workspace_bytes("tp_residual_ln_fwd", 2, 1, 1, 64, 128, 1, 1, 0) == 0
 
 
+def test_moe_validation(lib):
+    r = lib.tp_moe_route
+    # tokens, E, k, logits, gates, experts, offsets, row_token, token_row, stream
+    base = [16, 8, 2, P, P, P, P, P, P, None]
+    for kw, code in ((dict(a1=1025), -4), (dict(a1=0), -4), (dict(a2=9), -1), (dict(a2=0), -1), (dict(a1=64, a2=33), -1),
+                     (dict(a0=-1), -1), (dict(a3=None), -2), (dict(a6=None), -2), (dict(a5=P + 2), -3)):
+        assert r(*_with(base, **kw)) == code, kw
+    f = lib.tp_moe_shard_fwd
+    # tp, rank, tokens, H, E, k, F, dtype, X, gates, off, row_token, token_row, W1, b1, W2, out, Z, A1, Y, ws, wsb, stream
+    base = [2, 0, 16, 64, 8, 2, 128, 0] + [P] * 12 + [P, 1 << 20, None]
+    for kw, code in ((dict(a5=9), -1), (dict(a1=2), -1), (dict(a6=1), -1), (dict(a8=None), -2), (dict(a17=None), -2),
+                     (dict(a19=None), -2), (dict(a20=None), -5), (dict(a21=8), -5), (dict(a20=P + 16), -3),
+                     (dict(a10=P + 2), -3), (dict(a7=3), -1)):
+        assert f(*_with(base, **kw)) == code, kw
+    assert bd.tp_workspace_bytes("tp_moe_shard_fwd", 8, 0, 1, 1, 8192, 128, 2048, 0) >= 3 * 129 * 4
+
+
 def test_workspace_bytes(lib):
     T, H, F, t = 64, 64, 256, 2
     got = bd.tp_workspace_bytes("tp_mlp_shard_bwd", t, 0, 2, 32, H, 4, F, 0)
