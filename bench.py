@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--cpu-seq", type=int, default=2048,
                     help="tokens of the oracle's CPU sample (the first S of the sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped-shard measurement")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE measurements")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--no-attn-out", action="store_true",
                     help="skip the attention output-projection measurement")
@@ -194,6 +194,64 @@ def moe_grouped(bd, torch, steps, warmup):
     del Xp, W1, W2, Z, Y
     torch.cuda.empty_cache()
     return out
+
+
+def moe_layer(bd, torch, steps, warmup):
+    """The whole MoE expert block of rank 0 on the 128-expert workload, from router logits to the
+    combined partial: tp_moe_route (top-8 of 128, dispatch order) then tp_moe_shard_fwd (fc1 with
+    the dispatch gathered from X inside its operand loads, GeLU, fc2, gate-weighted combine).
+    Algorithmic bytes: logits, X, the expert weights, Y written and read, Z written and read back by
+    the combine, out written."""
+    from tensor_transformer_layer_mlp_amd.configs import MOE_E128 as mw
+    tp, rank, E, k, H, tokens = mw.tp_size, 0, mw.n_experts, mw.top_k, mw.H, mw.tokens
+    _, Fr = bd.tp_shard_range(mw.F_expert, tp, rank)
+    n = tokens * k
+    g = torch.Generator(device="cuda")
+    g.manual_seed(97531)
+    bf = torch.bfloat16
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    logits = torch.randn(tokens, E, generator=g, device="cuda")
+    X = r(tokens, H)
+    W1, b1, W2 = r(E, H, Fr, std=mw.w_std), r(E, Fr, std=mw.w_std), r(E, Fr, H, std=mw.w_std)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    gates, ex, off = torch.empty(tokens, k, device="cuda"), torch.empty(tokens, k, **i32), torch.empty(E + 1, **i32)
+    rt, tr = torch.empty(n, **i32), torch.empty(tokens, k, **i32)
+    out, Z, Y = torch.empty(tokens, H, dtype=bf, device="cuda"), torch.empty(n, H, dtype=bf, device="cuda"), \
+        torch.empty(n, Fr, dtype=bf, device="cuda")
+    ws = bd.workspace("tp_moe_shard_fwd", tp, rank, 1, n, H, E, mw.F_expert, bf)
+    wsr = bd.workspace("tp_moe_route", tp, rank, 1, tokens, H, E, mw.F_expert, bf)
+
+    def call():
+        bd.tp_moe_route(tokens, E, k, logits, gates, ex, off, rt, tr, wsr)
+        bd.tp_moe_shard_fwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, b1, W2, out, Z, None,
+                            Y, ws)
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    bd.tp_prof_enable(False)
+    kernels = {tag: kernel_roofline(c, kms, fl, by, steps) for tag, (c, kms, fl, by) in bd.tp_prof_collect().items()}
+    byts = 4.0 * tokens * E + 2.0 * tokens * H + 2.0 * (2 * E * H * Fr + E * Fr) + 2.0 * 2 * n * Fr + \
+        2.0 * 2 * n * H + 2.0 * tokens * H
+    flop = 4.0 * n * H * Fr + 2.0 * n * H
+    res = {"workload": mw.name + "_rank0_route_experts_combine", "tokens": tokens, "rows": n, "ms": round(ms, 4),
+           "tflops": round(flop / ms / 1e9, 2), "gb_per_s": round(byts / ms / 1e6, 1),
+           "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3),
+           "kernels": kernels}
+    del X, W1, W2, Z, Y, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def attn_out_proj(bd, torch, wl, rank, steps, warmup):
@@ -439,6 +497,7 @@ def main():
                         "bytes_per_launch": byts / n}
 
     moe = None if args.no_moe else moe_grouped(bd, torch, args.steps, args.warmup)
+    moe_l = None if args.no_moe else moe_layer(bd, torch, args.steps, args.warmup)
     oproj, oproj_flop = (None, 0.0) if args.no_attn_out else attn_out_proj(bd, torch, wl, rank, args.steps,
                                                                            args.warmup)
 
@@ -467,6 +526,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "moe_grouped_shard": moe,
+        "moe_layer_shard": moe_l,
         "attn_out_proj_shard": oproj,
         "residual_layernorm": ln,
         # the step plus the attention output projection: the whole Megatron layer shard's GEMMs

@@ -201,9 +201,11 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
  *   group_offsets[E+1] (expert e owns rows [off[e], off[e+1])), row_token[tokens·k] (the token of
  *   each row), token_row[tokens, k] (the row of (t, j)).
  * Integer outputs are deterministic and exact.  Logits must be finite.  E <= 1024, top_k <= 32.
- * All arrays int32 / fp32 in device memory, 4-byte aligned.  No workspace. */
+ * All arrays int32 / fp32 in device memory, 4-byte aligned.  workspace:
+ * tp_workspace_bytes("tp_moe_route", ...) with B·S = tokens and n_heads = E. */
 int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, float* gates, int* expert_idx,
-                 int* group_offsets, int* row_token, int* token_row, void* stream);
+                 int* group_offsets, int* row_token, int* token_row, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /* The MoE expert block of one tensor-parallel rank, on tp_moe_route's outputs: the dispatch is fused
  * into fc1's operand loads (row r of the expert-sorted matrix is read straight from X[row_token[r]],
@@ -225,7 +227,7 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
 
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
  * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd",
- * "tp_moe_shard_fwd"; 0 for the others).  T = B*S; F is used by the
+ * "tp_moe_route", "tp_moe_shard_fwd"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

@@ -32,7 +32,7 @@ _SIGNATURES = {
     "tp_residual_ln_fwd": (_I, [_I] * 6 + [_P, _P, _P, _F, _P, _P, _F, _P, _P, _P, _P, _P]),
     "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
-    "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P]),
+    "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P, _Z, _P]),
     "tp_moe_shard_fwd": (_I, [_I] * 8 + [_P] * 12 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -325,7 +325,7 @@ def tp_mlp_grouped_shard_fwd(tp_size, rank, n_groups, group_offsets, rows, H, F_
 
 
 def tp_moe_route(tokens, n_experts, top_k, logits, gates, expert_idx, group_offsets, row_token, token_row,
-                 stream=None):
+                 workspace, stream=None):
     """Top-k routing and the expert-sorted dispatch order (int32 outputs, fp32 gates)."""
     n = tokens * top_k if tokens >= 0 and top_k >= 1 else 0
     for t, k, name in ((logits, tokens * n_experts, "logits"), (gates, n, "gates"), (expert_idx, n, "expert_idx"),
@@ -335,7 +335,9 @@ def tp_moe_route(tokens, n_experts, top_k, logits, gates, expert_idx, group_offs
     rc = raw().tp_moe_route(tokens, n_experts, top_k, _ptr(logits, "logits", torch.float32),
                             _ptr(gates, "gates", torch.float32), _ptr(expert_idx, "expert_idx", torch.int32),
                             _ptr(group_offsets, "group_offsets", torch.int32), _ptr(row_token, "row_token", torch.int32),
-                            _ptr(token_row, "token_row", torch.int32), _stream(stream))
+                            _ptr(token_row, "token_row", torch.int32), _ptr(workspace, "workspace", None, True),
+                            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                            _stream(stream))
     _check(rc, "tp_moe_route")
 
 

@@ -487,7 +487,8 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
 }
 
 int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, float* gates, int* expert_idx,
-                 int* group_offsets, int* row_token, int* token_row, void* stream) {
+                 int* group_offsets, int* row_token, int* token_row, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   TP_CHECK(tokens >= 0, TP_EINVAL, "tokens %d < 0", tokens);
   TP_CHECK(n_experts >= 1 && n_experts <= moe_max_experts(), TP_EUNSUPPORTED, "n_experts %d outside [1, %d]",
            n_experts, moe_max_experts());
@@ -498,8 +499,12 @@ int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, floa
   NEED4(logits, "logits", (long)tokens * n_experts); NEED4(gates, "gates", n); NEED4(expert_idx, "expert_idx", n);
   NEED4(group_offsets, "group_offsets", n_experts + 1); NEED4(row_token, "row_token", n);
   NEED4(token_row, "token_row", n);
+  const size_t need = align256(moe_route_ws_bytes(tokens, n_experts));
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
   TP_TRY(launch_moe_route(tokens, n_experts, top_k, logits, gates, expert_idx, group_offsets, row_token, token_row,
-                          (hipStream_t)stream), "moe route");
+                          (int*)workspace, (hipStream_t)stream), "moe route");
   return TP_OK;
 }
 
@@ -544,6 +549,10 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   if (strcmp(fn, "tp_qkv_shard_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
     return qkv_bwd_ws(g.T, g.Nq);
+  }
+  if (strcmp(fn, "tp_moe_route") == 0) {
+    if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > moe_max_experts()) return 0;
+    return align256(moe_route_ws_bytes(B * S, n_heads));
   }
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0 || strcmp(fn, "tp_moe_shard_fwd") == 0) {
     if (n_heads < 1 || n_heads > (1 << 20)) return 0;

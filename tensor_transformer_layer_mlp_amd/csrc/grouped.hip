@@ -3,8 +3,9 @@
 //
 // The row offsets live on the device (routing happened there), so the host never sees the group
 // sizes.  A one-workgroup plan kernel sanitises the offsets (clamped to [0, rows], made
-// non-decreasing, so no later access can leave the buffers) and numbers the row tiles of all
-// experts for each of the two GEMMs' tile heights (prefix[e] = Σ_{j<e} ceil(rows_j / BM)); the
+// non-decreasing by a running maximum, so no later access can leave the buffers) and numbers the
+// row tiles of all experts for each of the two GEMMs' tile heights (prefix[e] = Σ_{j<e}
+// ceil(rows_j / BM)), all with parallel scans; the
 // grouped GEMM kernels launch an upper bound of ceil(rows / BM) + groups m-tiles and find their
 // expert by binary search in prefix[].
 #include <cstring>
@@ -25,37 +26,65 @@ bool gemm_bf16_eligible(const GemmDesc& d);
 
 namespace {
 
-constexpr int PLAN_CHUNK = 1024;
+constexpr int PLAN_T = 1024;   // threads of the plan kernel: groups handled per pass
 
-__global__ __launch_bounds__(256) void grouped_plan_kernel(const int* __restrict__ off_in, int groups,
-                                                           int rows, int bm1, int bm2,
-                                                           int* __restrict__ off_out,
-                                                           int* __restrict__ prefix1,
-                                                           int* __restrict__ prefix2) {
-  __shared__ int so[PLAN_CHUNK];
-  int prev = 0, p1 = 0, p2 = 0;
+// Inclusive scan over the workgroup's threads, fixed order (Hillis-Steele in LDS).
+template <typename Op>
+__device__ __forceinline__ int block_scan(int v, int* sh, Op op) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = 1; s < PLAN_T; s <<= 1) {
+    const bool has = threadIdx.x >= s;          // threads below the stride keep their value
+    const int o = has ? sh[threadIdx.x - s] : 0;
+    __syncthreads();
+    if (has) v = op(v, o);
+    sh[threadIdx.x] = v;
+    __syncthreads();
+  }
+  return v;
+}
+
+// off_out[i] = max(off_out[i-1], min(off_in[i], rows)) with off_out[0] = clamp(off_in[0], 0, rows):
+// a running maximum, so the clamped offsets come from one max-scan; the m-tile counts of the
+// groups then from two sum-scans.  Groups go PLAN_T at a time, carrying the last values.
+__global__ __launch_bounds__(PLAN_T) void grouped_plan_kernel(const int* __restrict__ off_in, int groups,
+                                                              int rows, int bm1, int bm2,
+                                                              int* __restrict__ off_out,
+                                                              int* __restrict__ prefix1,
+                                                              int* __restrict__ prefix2) {
+  __shared__ int sh[PLAN_T];
+  int carry_o = min(max(off_in[0], 0), rows), carry_1 = 0, carry_2 = 0;
   if (threadIdx.x == 0) {
-    prev = min(max(off_in[0], 0), rows);
-    off_out[0] = prev;
+    off_out[0] = carry_o;
     prefix1[0] = 0;
     prefix2[0] = 0;
   }
-  for (int c0 = 0; c0 < groups; c0 += PLAN_CHUNK) {
-    const int n = min(PLAN_CHUNK, groups - c0);
+  for (int c0 = 0; c0 < groups; c0 += PLAN_T) {
+    const int i = c0 + threadIdx.x;
+    const bool in = i < groups;
+    const int b = in ? max(min(off_in[i + 1], rows), carry_o) : carry_o;
+    const int o = block_scan(b, sh, [](int x, int y) { return max(x, y); });
+    const int prev = threadIdx.x > 0 ? sh[threadIdx.x - 1] : carry_o;   // sh holds the max-scan
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) so[i] = off_in[c0 + 1 + i];
+    const int n = in ? o - prev : 0;
+    const int p1 = block_scan((n + bm1 - 1) / bm1, sh, [](int x, int y) { return x + y; });
+    const int t1 = sh[PLAN_T - 1];
     __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int i = 0; i < n; ++i) {
-        const int o = min(max(so[i], prev), rows);
-        off_out[c0 + 1 + i] = o;
-        p1 += (o - prev + bm1 - 1) / bm1;
-        p2 += (o - prev + bm2 - 1) / bm2;
-        prefix1[c0 + 1 + i] = p1;
-        prefix2[c0 + 1 + i] = p2;
-        prev = o;
-      }
+    const int p2 = block_scan((n + bm2 - 1) / bm2, sh, [](int x, int y) { return x + y; });
+    const int t2 = sh[PLAN_T - 1];
+    __syncthreads();
+    if (in) {
+      off_out[i + 1] = o;
+      prefix1[i + 1] = carry_1 + p1;
+      prefix2[i + 1] = carry_2 + p2;
     }
+    carry_1 += t1;
+    carry_2 += t2;
+    // the last group's offset of this pass (threads past `groups` repeat it)
+    sh[threadIdx.x] = o;
+    __syncthreads();
+    carry_o = sh[PLAN_T - 1];
+    __syncthreads();
   }
 }
 
@@ -97,7 +126,7 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
   {
     ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
-    grouped_plan_kernel<<<1, 256, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
+    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -80,8 +80,9 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
 // MoE routing and combine (see moe.hip).
 int moe_max_experts();
 int moe_max_top_k();
+size_t moe_route_ws_bytes(int tokens, int experts);
 hipError_t launch_moe_route(int tokens, int experts, int top_k, const float* logits, float* gates, int* expert_idx,
-                            int* group_offsets, int* row_token, int* token_row, hipStream_t s);
+                            int* group_offsets, int* row_token, int* token_row, int* ws, hipStream_t s);
 hipError_t launch_moe_combine(int dtype, int tokens, int top_k, int H, const void* Z, const float* gates,
                               const int* token_row, int rows, void* out, hipStream_t s);
 

@@ -1,18 +1,21 @@
 // MoE routing (top-k of the router's softmax, expert-sorted dispatch order) and the gate-weighted
 // combine of the experts' rows back to tokens.
 //
-//   moe_topk_kernel     one wave per token: the row's logits sit in registers (E/64 per lane); wave
-//                       max and Σ exp give the softmax; k rounds of a wave arg-max over (logit, id)
-//                       pick the experts, the larger logit first and the lower id on equal logits.
-//                       The choice compares the fp32 logits themselves (softmax is monotone), so no
-//                       rounding of the probabilities can reorder it.
-//   moe_count_kernel    one workgroup: per-expert counts (LDS integer atomics, order-free) and their
-//                       exclusive prefix, the group offsets.
-//   moe_dispatch_kernel one workgroup per expert: its threads cut the tokens into contiguous blocks,
-//                       count the block's rows for the expert, take an exclusive prefix over the
-//                       blocks, and write the rows in token order: row_token (row -> token) and
-//                       token_row ((token, j) -> row).  Integer work only: bit-exact and
-//                       deterministic.
+//   moe_topk_kernel     a workgroup of 16 waves owns a chunk of 64 consecutive tokens, one wave per
+//                       token at a time: the token's logits sit in registers (E/64 per lane); wave max and Σ exp
+//                       give the softmax; k rounds of a wave arg-max over (logit, id) pick the
+//                       experts, the larger logit first and the lower id on equal logits.  The choice
+//                       compares the fp32 logits themselves (softmax is monotone), so no rounding of
+//                       the probabilities can reorder it.  The chunk's per-expert counts (LDS integer
+//                       atomics: order-free) go to counts[chunk][e].
+//   moe_scan_kernel     a workgroup per expert: the exclusive prefix of its counts over the chunks
+//                       (each thread a contiguous run of chunks, then an LDS scan over the threads)
+//                       and the expert's total.
+//   moe_scatter_kernel  a workgroup per chunk: the exclusive prefix of the experts' totals (the group
+//                       offsets, written by chunk 0); then thread i takes the chunk's i-th (token, j)
+//                       entry in token order and ranks it among the earlier entries with the same
+//                       expert, so rows land in (expert, token) order: row_token (row -> token) and
+//                       token_row ((token, j) -> row).  Integer work only: exact and deterministic.
 //   moe_combine_kernel  one workgroup per token: out[t] = Σ_j gate[t, j]·Z[token_row[t, j]] in fp32,
 //                       j in order; 16-byte loads of the k rows (HBM-bound).  Rows outside
 //                       [0, rows) contribute nothing.
@@ -27,105 +30,144 @@ namespace {
 constexpr int MOE_MAX_E = 1024;
 constexpr int MOE_MAX_K = 32;
 
+constexpr int MOE_CHUNK = 64;                   // tokens per routing chunk
+
+constexpr int TOPK_THREADS = 1024;
+
 template <int EPL>
-__global__ __launch_bounds__(256) void moe_topk_kernel(int tokens, int E, int k, const float* __restrict__ logits,
-                                                       float* __restrict__ gates, int* __restrict__ experts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= tokens) return;                      // whole waves leave together: no block barrier below
-  const float* row = logits + (long)t * E;
-  float v[EPL];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-    m = fmaxf(m, v[i]);
-  }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  float z = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + 64 * i < E) z += expf(v[i] - m);
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) z += __shfl_xor(z, s, 64);
-  unsigned taken = 0;                            // bit i: entry lane + 64 i already chosen
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+__global__ __launch_bounds__(TOPK_THREADS) void moe_topk_kernel(int tokens, int E, int k, const float* __restrict__ logits,
+                                                       float* __restrict__ gates, int* __restrict__ experts,
+                                                       int* __restrict__ counts) {
+  __shared__ int cnt[MOE_MAX_E];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) cnt[e] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * MOE_CHUNK, c1 = min(tokens, c0 + MOE_CHUNK);
+  for (int t = c0 + w; t < c1; t += TOPK_THREADS / 64) {
+    const float* row = logits + (long)t * E;
+    float v[EPL];
+    float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {   // ascending ids: > keeps the lower
-        bv = v[i];
-        bi = e;
-      }
+      v[i] = e < E ? row[e] : -INFINITY;
+      m = fmaxf(m, v[i]);
     }
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float ov = __shfl_xor(bv, s, 64);
-      const int oi = __shfl_xor(bi, s, 64);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i < E) z += expf(v[i] - m);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) z += __shfl_xor(z, s, 64);
+    unsigned taken = 0;                          // bit i: entry lane + 64 i already chosen
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {   // ascending ids: > keeps the lower
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) {
+        const float ov = __shfl_xor(bv, s, 64);
+        const int oi = __shfl_xor(bi, s, 64);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) {
+        experts[(long)t * k + j] = bi;
+        gates[(long)t * k + j] = expf(bv - m) / z;
+        atomicAdd(&cnt[bi], 1);
       }
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == 0) {
-      experts[(long)t * k + j] = bi;
-      gates[(long)t * k + j] = expf(bv - m) / z;
-    }
-  }
-}
-
-__global__ __launch_bounds__(1024) void moe_count_kernel(int n, int E, const int* __restrict__ experts,
-                                                         int* __restrict__ offsets) {
-  __shared__ int cnt[MOE_MAX_E];
-  for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    const int e = experts[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    offsets[0] = 0;
-    for (int e = 0; e < E; ++e) {
-      acc += cnt[e];
-      offsets[e + 1] = acc;
-    }
-  }
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) counts[(long)blockIdx.x * E + e] = cnt[e];
 }
 
-__global__ __launch_bounds__(256) void moe_dispatch_kernel(int tokens, int k, const int* __restrict__ experts,
-                                                           const int* __restrict__ offsets,
-                                                           int* __restrict__ row_token, int* __restrict__ token_row) {
+// Expert blockIdx.x: base[c][e] = Σ_{c' < c} counts[c'][e] (exclusive over the chunks), total[e].
+__global__ __launch_bounds__(256) void moe_scan_kernel(int chunks, int E, const int* __restrict__ counts,
+                                                       int* __restrict__ base, int* __restrict__ total) {
   __shared__ int pre[256];
   const int e = blockIdx.x;
-  const int per = (tokens + 255) / 256;
-  const int t0 = min(tokens, threadIdx.x * per), t1 = min(tokens, t0 + per);
-  int c = 0;
-  for (int t = t0; t < t1; ++t)
-    for (int j = 0; j < k; ++j) c += experts[(long)t * k + j] == e;
-  pre[threadIdx.x] = c;
+  const int per = (chunks + 255) / 256;
+  const int c0 = min(chunks, threadIdx.x * per), c1 = min(chunks, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += counts[(long)c * E + e];
+  pre[threadIdx.x] = sum;
   __syncthreads();
-  // exclusive prefix over the 256 blocks (Hillis-Steele on a copy, fixed order)
   for (int s = 1; s < 256; s <<= 1) {
     const int add = threadIdx.x >= s ? pre[threadIdx.x - s] : 0;
     __syncthreads();
     pre[threadIdx.x] += add;
     __syncthreads();
   }
-  int row = offsets[e] + pre[threadIdx.x] - c;
-  for (int t = t0; t < t1; ++t)
-    for (int j = 0; j < k; ++j)
-      if (experts[(long)t * k + j] == e) {
-        row_token[row] = t;
-        token_row[(long)t * k + j] = row;
-        ++row;
-      }
+  int acc = pre[threadIdx.x] - sum;
+  for (int c = c0; c < c1; ++c) {
+    base[(long)c * E + e] = acc;
+    acc += counts[(long)c * E + e];
+  }
+  if (threadIdx.x == 255) total[e] = pre[255];
+}
+
+__global__ __launch_bounds__(512) void moe_scatter_kernel(int tokens, int k, const int* __restrict__ experts,
+                                                          const int* __restrict__ base,
+                                                          const int* __restrict__ total, int E,
+                                                          int* __restrict__ offsets, int* __restrict__ row_token,
+                                                          int* __restrict__ token_row) {
+  __shared__ int ex[MOE_CHUNK * MOE_MAX_K];
+  __shared__ int off[MOE_MAX_E];
+  // the experts' offsets: exclusive prefix of the totals, two experts per thread then a thread scan
+  {
+    const int a = 2 * threadIdx.x, b = a + 1;
+    const int va = a < E ? total[a] : 0, vb = b < E ? total[b] : 0;
+    off[a] = va + vb;                              // scratch: pair sums, scanned in place below
+    __syncthreads();
+    int v = off[a];
+    for (int s = 1; s < 512; s <<= 1) {
+      const int add = threadIdx.x >= s ? off[2 * (threadIdx.x - s)] : 0;
+      __syncthreads();
+      v += add;
+      off[a] = v;
+      __syncthreads();
+    }
+    const int excl = v - va - vb;                  // rows before expert a
+    __syncthreads();
+    off[a] = excl;
+    off[b] = excl + va;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      if (a < E) offsets[a] = off[a];
+      if (b < E) offsets[b] = off[b];
+      if (threadIdx.x == 0) offsets[E] = off[E - 1] + total[E - 1];
+    }
+  }
+  const int c0 = blockIdx.x * MOE_CHUNK, c1 = min(tokens, c0 + MOE_CHUNK);
+  const int n = (c1 - c0) * k;                   // the chunk's entries, token-major
+  const long first = (long)c0 * k;
+  for (int i = threadIdx.x; i < n; i += 512) ex[i] = experts[first + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 512) {
+    const int e = ex[i];
+    int rank = 0;
+    for (int q = 0; q < i; ++q) rank += ex[q] == e;
+    const int row = off[e] + base[(long)blockIdx.x * E + e] + rank;
+    row_token[row] = c0 + i / k;
+    token_row[first + i] = row;
+  }
+}
+
+__global__ __launch_bounds__(1024) void moe_zero_offsets_kernel(int E, int* __restrict__ offsets) {
+  for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = 0;
 }
 
 template <typename T, int V>
@@ -170,8 +212,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(int k, int H, const T*
 }
 
 template <int EPL>
-hipError_t topk_t(int tokens, int E, int k, const float* logits, float* gates, int* experts, hipStream_t s) {
-  moe_topk_kernel<EPL><<<(tokens + 3) / 4, 256, 0, s>>>(tokens, E, k, logits, gates, experts);
+hipError_t topk_t(int tokens, int E, int k, const float* logits, float* gates, int* experts, int* counts,
+                  hipStream_t s) {
+  moe_topk_kernel<EPL><<<(tokens + MOE_CHUNK - 1) / MOE_CHUNK, TOPK_THREADS, 0, s>>>(tokens, E, k, logits, gates,
+                                                                                     experts, counts);
   return hipGetLastError();
 }
 
@@ -180,29 +224,43 @@ hipError_t topk_t(int tokens, int E, int k, const float* logits, float* gates, i
 int moe_max_experts() { return MOE_MAX_E; }
 int moe_max_top_k() { return MOE_MAX_K; }
 
+size_t moe_route_ws_bytes(int tokens, int E) {
+  const size_t chunks = (size_t)((tokens + MOE_CHUNK - 1) / MOE_CHUNK);
+  return (2 * chunks + 1) * (size_t)E * sizeof(int);
+}
+
 hipError_t launch_moe_route(int tokens, int E, int k, const float* logits, float* gates, int* expert_idx,
-                            int* group_offsets, int* row_token, int* token_row, hipStream_t s) {
+                            int* group_offsets, int* row_token, int* token_row, int* ws, hipStream_t s) {
   if (E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || tokens < 0) return hipErrorInvalidValue;
+  const int chunks = (tokens + MOE_CHUNK - 1) / MOE_CHUNK;
+  int* counts = ws;
+  int* base = ws + (size_t)chunks * E;
+  int* total = base + (size_t)chunks * E;
   const double n = (double)tokens * k;
   if (tokens > 0) {
-    ProfScope p("moe_topk", s, 4.0 * tokens * E, 4.0 * tokens * E + 8.0 * n);
+    ProfScope p("moe_topk", s, 4.0 * tokens * E, 4.0 * tokens * E + 8.0 * n + 4.0 * chunks * E);
     hipError_t e;
-    if (E <= 64) e = topk_t<1>(tokens, E, k, logits, gates, expert_idx, s);
-    else if (E <= 128) e = topk_t<2>(tokens, E, k, logits, gates, expert_idx, s);
-    else if (E <= 256) e = topk_t<4>(tokens, E, k, logits, gates, expert_idx, s);
-    else if (E <= 512) e = topk_t<8>(tokens, E, k, logits, gates, expert_idx, s);
-    else e = topk_t<16>(tokens, E, k, logits, gates, expert_idx, s);
+    if (E <= 64) e = topk_t<1>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 128) e = topk_t<2>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 256) e = topk_t<4>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 512) e = topk_t<8>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else e = topk_t<16>(tokens, E, k, logits, gates, expert_idx, counts, s);
     if (e != hipSuccess) return e;
   }
+  if (tokens == 0) {                             // no chunks: every group is empty
+    ProfScope p("moe_scan", s, 0.0, 4.0 * (E + 1));
+    moe_zero_offsets_kernel<<<1, 1024, 0, s>>>(E, group_offsets);
+    return hipGetLastError();
+  }
   {
-    ProfScope p("moe_count", s, 0.0, 4.0 * n + 4.0 * (E + 1));
-    moe_count_kernel<<<1, 1024, 0, s>>>((int)n, E, expert_idx, group_offsets);
+    ProfScope p("moe_scan", s, 0.0, 12.0 * chunks * E);
+    moe_scan_kernel<<<E, 256, 0, s>>>(chunks, E, counts, base, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (tokens == 0) return hipSuccess;
-  ProfScope p("moe_dispatch", s, 0.0, 4.0 * n * E + 8.0 * n);
-  moe_dispatch_kernel<<<E, 256, 0, s>>>(tokens, k, expert_idx, group_offsets, row_token, token_row);
+  ProfScope p("moe_scatter", s, 0.0, 4.0 * n + 4.0 * chunks * E + 8.0 * n);
+  moe_scatter_kernel<<<chunks, 512, 0, s>>>(tokens, k, expert_idx, base, total, E, group_offsets, row_token,
+                                            token_row);
   return hipGetLastError();
 }
 

@@ -157,10 +157,11 @@ def test_residual_ln_validation(lib):
 
 def test_moe_validation(lib):
     r = lib.tp_moe_route
-    # tokens, E, k, logits, gates, experts, offsets, row_token, token_row, stream
-    base = [16, 8, 2, P, P, P, P, P, P, None]
+    # tokens, E, k, logits, gates, experts, offsets, row_token, token_row, ws, wsb, stream
+    base = [16, 8, 2, P, P, P, P, P, P, P, 1 << 20, None]
     for kw, code in ((dict(a1=1025), -4), (dict(a1=0), -4), (dict(a2=9), -1), (dict(a2=0), -1), (dict(a1=64, a2=33), -1),
-                     (dict(a0=-1), -1), (dict(a3=None), -2), (dict(a6=None), -2), (dict(a5=P + 2), -3)):
+                     (dict(a0=-1), -1), (dict(a3=None), -2), (dict(a6=None), -2), (dict(a5=P + 2), -3),
+                     (dict(a9=None, a10=0), -5), (dict(a10=4), -5), (dict(a9=P + 16), -3)):
         assert r(*_with(base, **kw)) == code, kw
     f = lib.tp_moe_shard_fwd
     # tp, rank, tokens, H, E, k, F, dtype, X, gates, off, row_token, token_row, W1, b1, W2, out, Z, A1, Y, ws, wsb, stream
@@ -170,6 +171,7 @@ def test_moe_validation(lib):
                      (dict(a10=P + 2), -3), (dict(a7=3), -1)):
         assert f(*_with(base, **kw)) == code, kw
     assert bd.tp_workspace_bytes("tp_moe_shard_fwd", 8, 0, 1, 1, 8192, 128, 2048, 0) >= 3 * 129 * 4
+    assert bd.tp_workspace_bytes("tp_moe_route", 8, 0, 1, 16384, 8192, 128, 2048, 0) >= 2 * 256 * 128 * 4
 
 
 def test_workspace_bytes(lib):

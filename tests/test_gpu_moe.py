@@ -31,7 +31,8 @@ def _route_gpu(lg, k):
     o = dict(gates=torch.full((tokens, k), float("nan"), device="cuda"), experts=torch.full((tokens, k), -7, **i32),
              offsets=torch.full((E + 1,), -7, **i32), row_token=torch.full((tokens * k,), -7, **i32),
              token_row=torch.full((tokens, k), -7, **i32))
-    bd.tp_moe_route(tokens, E, k, L, o["gates"], o["experts"], o["offsets"], o["row_token"], o["token_row"])
+    ws = bd.workspace("tp_moe_route", 1, 0, 1, tokens, 1, E, 1, torch.float32)
+    bd.tp_moe_route(tokens, E, k, L, o["gates"], o["experts"], o["offsets"], o["row_token"], o["token_row"], ws)
     torch.cuda.synchronize()
     return o
 
@@ -156,9 +157,10 @@ def test_moe_graph_replay_and_determinism():
     n = tokens * k
     out, Z, Y = (torch.empty(*s, dtype=torch.bfloat16, device="cuda") for s in ((tokens, H), (n, H), (n, Fr)))
     ws = bd.workspace("tp_moe_shard_fwd", 2, 0, 1, n, H, E, F_expert, torch.bfloat16)
+    wsr = bd.workspace("tp_moe_route", 1, 0, 1, tokens, 1, E, 1, torch.float32)
 
     def call():
-        bd.tp_moe_route(tokens, E, k, lg, gates, ex, off, rt, tr)
+        bd.tp_moe_route(tokens, E, k, lg, gates, ex, off, rt, tr, wsr)
         bd.tp_moe_shard_fwd(2, 0, tokens, H, E, k, F_expert, X, gates, off, rt, tr, W1, b1, W2, out, Z, None, Y, ws)
     call()
     torch.cuda.synchronize()

@@ -387,6 +387,21 @@ def test_grouped_mlp_malformed_offsets(dtype):
     assert_close(Z, ref, dtype, "Z_r with clamped offsets")
 
 
+def test_grouped_mlp_many_groups():
+    """More groups than the plan kernel's threads (its passes carry the running offset and tile
+    counts), with empty groups and a decreasing offset that the running maximum clamps."""
+    sizes = [int(v) for v in np.random.default_rng(17).integers(0, 4, 1500)]
+    H, F_group, tp, rank, dtype = 64, 32, 2, 0, "bf16"
+    off, rows, Fr, ops = _grouped_inputs(sizes, 0, dtype, H, F_group, tp, rank)
+    raw = off.copy()
+    raw[700] = raw[650]                      # decreasing: clamped up to off[699]
+    Z, A1, Y = _run_grouped(raw, rows, H, F_group, tp, rank, ops, dtype, Fr)
+    clamped = np.maximum.accumulate(np.minimum(raw, rows))
+    f = {k: v.f64 for k, v in ops.items()}
+    ref = oracle.tp_mlp_grouped_shard_fwd(tp, rank, clamped, f["X"], f["W1"], f["b1"], f["W2"])
+    assert_close(Z, ref, dtype, "Z_r over 1500 groups")
+
+
 def test_grouped_mlp_deterministic():
     off, rows, Fr, ops = _grouped_inputs([0, 5, 300, 1, 257, 77], 0, "bf16")
     a = _run_grouped(off, rows, 192, 128, 2, 1, ops, "bf16", Fr)[0]
