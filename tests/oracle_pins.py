@@ -16,6 +16,9 @@ fails.  What pins what:
   moe         routing against numpy's stable argsort, exact ties to the lower id, permutation and
               inverse invariants, gates summing to 1 when k = E; the whole MoE block against scalar
               per-token loops; E = k = 1 equals the dense MLP shard; Σ over TP ranks = unsharded
+  fp8         E4M3 anchors from the format's definition; every finite code against torch's
+              float8_e4m3fn; encode(decode(c)) = c; midpoints to the even code; saturation; the
+              amax element quantises to ±448; the GEMM on codes against scalar loops
   layernorm   scalar loops; a textbook row; zero mean / unit mean square (eps = 0); shift and scale
               invariance; constant rows; dropout-add cases by hand; finite differences through the
               fused residual + dropout + LayerNorm op; the sequence-parallel split (row blocks
@@ -566,5 +569,57 @@ def pin_moe():
     _close(d, T.tp_mlp_shard_fwd(1, 0, n, H, Fe, X, W1[0], b1[0], W2[0], None)["Z"], 1e-14, "E = k = 1")
 
 
+def pin_fp8():
+    import torch
+    d = T.e4m3_decode(np.arange(256))
+    for code, val in ((0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0),
+                      (0x3C, 1.5), (0x7E, 448.0), (0xB8, -1.0), (0xFE, -448.0)):
+        assert d[code] == val, f"decode 0x{code:02x} = {d[code]} != {val}"
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.signbit(d[0x80]) and d[0x80] == 0
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    fin = ~np.isnan(t)
+    assert np.array_equal(d[fin], t[fin]) and np.array_equal(np.isnan(d), np.isnan(t)), "decode vs torch"
+    codes = np.arange(256)[fin]
+    assert np.array_equal(T.e4m3_encode(d[codes]), codes.astype(np.uint8)), "encode(decode(c)) = c"
+    pos = np.sort(d[(np.arange(256) < 0x7F)])
+    mid = (pos[1:] + pos[:-1]) / 2                 # exact midpoints: ties
+    want = torch.from_numpy(mid.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = T.e4m3_encode(mid)
+    assert np.array_equal(got, want) and (got % 2 == 0).all(), "midpoints round to the even code"
+    g = _rng(71)
+    x = (g.standard_normal(20000) * 60).astype(np.float32).clip(-448, 448)
+    assert np.array_equal(T.e4m3_encode(x), torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert list(T.e4m3_encode([449.0, 1e6, -1e6, 464.0])) == [0x7E, 0x7E, 0xFE, 0x7E], "saturation"
+    # per-tensor quantisation: the largest magnitude maps to 448, the descale undoes the scale
+    X = g.standard_normal((7, 5)).astype(np.float32)
+    X[3, 2] = -4.0 * np.abs(X).max()
+    q, ds = T.fp8_quantize(X)
+    assert q[3, 2] == 0xFE, "the largest magnitude quantises to -448"
+    assert abs(float(ds) - float(np.abs(X).max()) / 448) <= 1e-7 * float(np.abs(X).max())
+    qt, dst = T.fp8_quantize(X, transpose=True)
+    assert np.array_equal(qt, q.T) and dst == ds
+    qz, dz = T.fp8_quantize(np.zeros((3, 4), np.float32))
+    assert dz == 1 and not qz.any()
+    err = np.abs(T.e4m3_decode(q) * float(ds) - X) / np.abs(X).max()
+    assert err.max() <= 2.0 ** -4 * 1.001, "relative rounding error within half an E4M3 step"
+    # the GEMM on codes against scalar loops
+    A = g.integers(0, 256, (5, 9)).astype(np.uint8)
+    B = g.integers(0, 256, (4, 9)).astype(np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x38                   # no NaN codes
+    B[(B & 0x7F) == 0x7F] = 0xB8
+    bias = g.standard_normal(4)
+    da, db = np.float32(0.25), np.float32(3.0)
+    r = T.fp8_gemm_nt(A, da, B, db, bias, gelu_out=True)
+    dA, dB = T.e4m3_decode(A).tolist(), T.e4m3_decode(B).tolist()
+    for i in range(5):
+        for j in range(4):
+            acc = 0.0
+            for k in range(9):
+                acc += dA[i][k] * dB[j][k]
+            pre = acc * 0.25 * 3.0 + bias[j]
+            assert abs(r["pre"][i, j] - pre) <= 1e-12 * max(1.0, abs(pre))
+            assert abs(r["C"][i, j] - bf.gelu(pre)) <= 1e-12 * max(1.0, abs(pre))
+
+
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
-            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe]
+            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe, pin_fp8]

@@ -208,6 +208,29 @@ def _combine_first_choice_only(Z_rows, gates, token_row):
 _ORIG_ROUTE = T.moe_route
 
 
+def _e4m3_decode_bias8(codes):
+    return _ORIG_DECODE(codes) / 2.0
+
+
+def _e4m3_encode_ties_up(y):
+    y = np.asarray(y, dtype=np.float64)
+    pos = T._E4M3_POS
+    a = np.minimum(np.abs(y), 448.0)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    pick = np.where(pos[hi] - a <= a - pos[lo], hi, lo)
+    return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def _fp8_quantize_descale_inverted(x, transpose=False):
+    q, d = _ORIG_QUANT(x, transpose)
+    return q, np.float32(1) / d
+
+
+_ORIG_DECODE = T.e4m3_decode
+_ORIG_QUANT = T.fp8_quantize
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -245,6 +268,9 @@ MUTANTS = {
     "moe_gates_renormalised": {"moe_route": _route_variant(renorm=True)},
     "moe_rows_in_token_order": {"moe_route": _route_variant(by_token=True)},
     "moe_combine_first_choice_only": {"moe_combine": _combine_first_choice_only},
+    "e4m3_exponent_bias_8": {"e4m3_decode": _e4m3_decode_bias8},
+    "e4m3_ties_away": {"e4m3_encode": _e4m3_encode_ties_up},
+    "fp8_descale_inverted": {"fp8_quantize": _fp8_quantize_descale_inverted},
 }
 
 
