@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-attn-out", action="store_true",
                     help="skip the attention output-projection measurement")
     ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 MLP-forward measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
                          "calibrated on), then --warmup + --steps steps, and nothing else")
@@ -250,6 +251,70 @@ def moe_layer(bd, torch, steps, warmup):
            "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3),
            "kernels": kernels}
     del X, W1, W2, Z, Y, out
+    torch.cuda.empty_cache()
+    return res
+
+
+PEAK_FP8_TFLOPS = 5033.2   # dense E4M3 MFMA: twice the bf16 rate
+
+
+def fp8_mlp(bd, torch, wl, steps, warmup):
+    """The MLP shard's two forward GEMMs in FP8 (E4M3 codes, one scale per tensor) on the GPT-3
+    rank-0 shapes: X·W1 (2048 x 6144 x 12288) with bias + GeLU and Y·W2 (2048 x 12288 x 6144), both
+    with K-major code operands; the quantisation of X and Y (per call) and of the weights (once,
+    transposed) is timed apart.  A precision variant beside the bf16 step, against the FP8 peak."""
+    T, H = wl.T, wl.H
+    _, Fr = bd.tp_shard_range(wl.F, wl.tp_size, 0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8642)
+    bf = torch.bfloat16
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    X, W1, b1, W2 = r(T, H), r(H, Fr, std=wl.w_std), r(Fr, std=wl.w_std), r(Fr, H, std=wl.w_std)
+    u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device="cuda")  # noqa: E731
+    qX, qW1t, qW2t, qY = u8(T, H), u8(Fr, H), u8(H, Fr), u8(T, Fr)
+    dX, dW1, dW2, dY = (torch.empty(1, device="cuda") for _ in range(4))
+    Y, Z = torch.empty(T, Fr, dtype=bf, device="cuda"), torch.empty(T, H, dtype=bf, device="cuda")
+    ws = bd.workspace("tp_fp8_quantize", 1, 0, 1, 1, 1, 1, 1, bf)
+    bd.tp_fp8_quantize(W1, qW1t, dW1, ws, transpose=True)
+    bd.tp_fp8_quantize(W2, qW2t, dW2, ws, transpose=True)
+
+    def call():
+        bd.tp_fp8_quantize(X, qX, dX, ws)
+        bd.tp_fp8_gemm_nt(qX, dX, qW1t, dW1, Y, bias=b1, gelu=True)
+        bd.tp_fp8_quantize(Y, qY, dY, ws)
+        bd.tp_fp8_gemm_nt(qY, dY, qW2t, dW2, Z)
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    bd.tp_prof_enable(False)
+    k = bd.tp_prof_collect()
+    flop = 2 * 2.0 * T * H * Fr
+    kernels = {}
+    for tag, (n, kms, fl, by) in k.items():
+        us = 1e3 * kms / n
+        e = {"launches_per_step": n / steps, "avg_launch_us": round(us, 2)}
+        if tag.startswith("gemm_fp8"):
+            tf = fl / n / us / 1e6
+            e.update(tflops=round(tf, 1), frac_of_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        else:
+            e.update(gb_per_s=round(by / n / us / 1e3, 1))
+        kernels[tag] = e
+    res = {"workload": "gpt3_175b_tp8_rank0_mlp_fwd_fp8_e4m3", "ms": round(ms, 4),
+           "tflops": round(flop / ms / 1e9, 1), "pct_of_fp8_peak": round(100 * flop / ms / 1e9 / PEAK_FP8_TFLOPS, 2),
+           "kernels": kernels}
+    del X, W1, W2, qX, qW1t, qW2t, qY, Y, Z
     torch.cuda.empty_cache()
     return res
 
@@ -502,6 +567,7 @@ def main():
                                                                            args.warmup)
 
     ln = None if args.no_ln else residual_ln(bd, torch, wl, args.steps, args.warmup)
+    f8 = None if args.no_fp8 else fp8_mlp(bd, torch, wl, args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -529,6 +595,7 @@ def main():
         "moe_layer_shard": moe_l,
         "attn_out_proj_shard": oproj,
         "residual_layernorm": ln,
+        "fp8_mlp_fwd": f8,
         # the step plus the attention output projection: the whole Megatron layer shard's GEMMs
         "tflops_layer_with_out_proj": round((flop_step + oproj_flop) / ((ms_step + oproj["ms"]) * 1e-3) / 1e12, 2)
         if oproj else None,

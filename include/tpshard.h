@@ -225,9 +225,30 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
                      const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
                      void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream);
 
+/* FP8 (OCP E4M3: 1 sign, 4 exponent bits, bias 7, 3 mantissa bits, max 448): forward and backward
+ * GEMMs in FP8 beside FP32 master weights ("Megatron-LM技术演进与大规模模型训练实践", §2.3); FP8 among
+ * the mixed precisions of the stack ("NVIDIA Megatron-LM：大规模Transformer模型分布式训练框架", the
+ * §技术栈; "Megatron-LM — 架构与原理", capability table).  Per-tensor
+ * quantisation of x [rows, cols] (bf16 or fp32):
+ *   amax = max |x|;  s = 448 / amax and descale = amax / 448 in fp32 (1 and 1 when amax = 0)
+ *   q = E4M3(fp32(x·s)), nearest with ties to the even mantissa, saturating at ±448
+ * transpose != 0 writes the codes transposed, [cols, rows] (the K-major copy of a weight [in, out]
+ * that tp_fp8_gemm_nt takes as B).  descale: one fp32 in device memory (written).  x must be finite.
+ * workspace: tp_workspace_bytes("tp_fp8_quantize", ...) bytes. */
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose, unsigned char* q, float* descale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* GEMM on E4M3 codes, both operands K-major:
+ *   pre = (A·Bᵀ)·a_descale·b_descale (+ bias[n]),  A [M, K] codes, B [N, K] codes, fp32 accumulation
+ *   C = pre (gelu == 0) or GeLU(pre) with C_pre = pre when C_pre != NULL (gelu != 0)
+ * C, C_pre, bias bf16; descales fp32 scalars in device memory (as tp_fp8_quantize writes them).
+ * Requires K % 16 == 0, N % 8 == 0, operands below 2 GiB (TP_EUNSUPPORTED otherwise). */
+int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_descale, const unsigned char* B,
+                   const float* b_descale, const void* bias, int gelu, void* C, void* C_pre, void* stream);
+
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
  * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd",
- * "tp_moe_route", "tp_moe_shard_fwd"; 0 for the others).  T = B*S; F is used by the
+ * "tp_moe_route", "tp_moe_shard_fwd", "tp_fp8_quantize"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P, _Z, _P]),
+    "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _P, _P, _P, _Z, _P]),
+    "tp_fp8_gemm_nt": (_I, [_I, _I, _I] + [_P] * 5 + [_I, _P, _P, _P]),
     "tp_moe_shard_fwd": (_I, [_I] * 8 + [_P] * 12 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -361,6 +363,36 @@ def tp_moe_shard_fwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, ga
         _ptr(workspace, "workspace", None, True),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
     _check(rc, "tp_moe_shard_fwd")
+
+
+def tp_fp8_quantize(x, q, descale, workspace, transpose=False, stream=None):
+    """E4M3 codes of a 2-D tensor x with one scale (q: uint8 [rows, cols], or [cols, rows] when
+    transpose), and its fp32 descale (a one-element device tensor)."""
+    rows, cols = x.shape
+    _need(q, rows * cols, "q")
+    _need(descale, 1, "descale")
+    rc = raw().tp_fp8_quantize(rows, cols, _dtype_code(x), _ptr(x, "x"), 1 if transpose else 0,
+                               _ptr(q, "q", torch.uint8), _ptr(descale, "descale", torch.float32),
+                               _ptr(workspace, "workspace", None, True),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream))
+    _check(rc, "tp_fp8_quantize")
+
+
+def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, gelu=False, C_pre=None, stream=None):
+    """C [M, N] bf16 = (A·Bᵀ)·descales (+ bias) (-> GeLU) for E4M3 codes A [M, K], B [N, K]."""
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"B has {B.shape[1]} columns, A has {K}")
+    for t, k, name in ((C, M * N, "C"), (bias, N, "bias"), (C_pre, M * N, "C_pre"), (a_descale, 1, "a_descale"),
+                       (b_descale, 1, "b_descale")):
+        _need(t, k, name)
+    rc = raw().tp_fp8_gemm_nt(M, N, K, _ptr(A, "A", torch.uint8), _ptr(a_descale, "a_descale", torch.float32),
+                              _ptr(B, "B", torch.uint8), _ptr(b_descale, "b_descale", torch.float32),
+                              _ptr(bias, "bias", torch.bfloat16, True), 1 if gelu else 0,
+                              _ptr(C, "C", torch.bfloat16), _ptr(C_pre, "C_pre", torch.bfloat16, True), _stream(stream))
+    _check(rc, "tp_fp8_gemm_nt")
 
 
 def workspace(fn, tp_size, rank, B, S, H, n_heads, F, dtype, device="cuda"):

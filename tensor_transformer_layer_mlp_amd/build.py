@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "prof.hip", "dispatch.hip", "gemm_generic.hip", "gemm_bf16.hip", "reduce.hip",
-           "attention_generic.hip", "attention_mfma.hip", "grouped.hip", "layernorm.hip", "moe.hip"]
+           "attention_generic.hip", "attention_mfma.hip", "grouped.hip", "layernorm.hip", "moe.hip", "fp8.hip"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]

@@ -536,6 +536,34 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   return TP_OK;
 }
 
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose, unsigned char* q, float* descale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
+  TP_CHECK(rows >= 0 && cols >= 0, TP_EINVAL, "negative size %d x %d", rows, cols);
+  const long n = (long)rows * cols;
+  NEED(x, "x", n); NEED(q, "q", n); NEED4(descale, "descale", 1);
+  const size_t need = align256(fp8_quantize_ws_bytes());
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_fp8_quantize(dtype, rows, cols, x, transpose != 0, q, descale, (float*)workspace, (hipStream_t)stream),
+         "fp8 quantize");
+  return TP_OK;
+}
+
+int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_descale, const unsigned char* B,
+                   const float* b_descale, const void* bias, int gelu, void* C, void* C_pre, void* stream) {
+  TP_CHECK(M >= 0 && N >= 0 && K >= 0, TP_EINVAL, "negative size %d x %d x %d", M, N, K);
+  TP_CHECK(K % 16 == 0, TP_EUNSUPPORTED, "K %d is not a multiple of 16 (rows of 16-byte pieces)", K);
+  TP_CHECK(N % 8 == 0, TP_EUNSUPPORTED, "N %d is not a multiple of 8", N);
+  TP_CHECK((long)M * K < 0x7fffffffL && (long)N * K < 0x7fffffffL, TP_EUNSUPPORTED, "an operand above 2 GiB");
+  NEED(A, "A", (long)M * K); NEED(B, "B", (long)N * K); NEED4(a_descale, "a_descale", 1);
+  NEED4(b_descale, "b_descale", 1); NEED(C, "C", (long)M * N); MAYBE(bias, "bias"); MAYBE(C_pre, "C_pre");
+  TP_TRY(launch_fp8_gemm_nt(M, N, K, A, a_descale, B, b_descale, bias, gelu != 0, C, gelu ? C_pre : nullptr,
+                            (hipStream_t)stream), "fp8 gemm");
+  return TP_OK;
+}
+
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H, int n_heads,
                           int F, int dtype) {
   if (fn == nullptr) return 0;
@@ -550,6 +578,7 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
     return qkv_bwd_ws(g.T, g.Nq);
   }
+  if (strcmp(fn, "tp_fp8_quantize") == 0) return align256(fp8_quantize_ws_bytes());
   if (strcmp(fn, "tp_moe_route") == 0) {
     if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > moe_max_experts()) return 0;
     return align256(moe_route_ws_bytes(B * S, n_heads));

@@ -1,0 +1,374 @@
+// FP8 (OCP E4M3) path: per-tensor quantisation and a GEMM on E4M3 codes for gfx950.
+//
+// Quantisation: amax = max |x| (per-workgroup maxima, then one workgroup: max is order-free, so the
+// result is exact and deterministic), s = 448 / amax and descale = amax / 448 in fp32 (1 and 1 for
+// an all-zero tensor), codes = E4M3(fp32(x·s)) rounded to nearest, ties to the even mantissa,
+// saturating at ±448, by exact bit arithmetic on the fp32 value (no conversion instruction, so the
+// rounding is the one stated).  The transposed form writes the [cols, rows] copy a GEMM operand
+// needs K-major, through 64 x 64 LDS tiles so both the reads and the writes are whole rows.
+//
+// GEMM: C[M, N] = (A·Bᵀ)·descale_a·descale_b (+ bias) (-> GeLU), A [M, K] and B [N, K] codes, both
+// K-major; bf16 out, fp32 accumulation.  v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales:
+// lane l holds row (l % 16) of its 16-row operand block and the 32 bytes k = 32·(l / 16) .. +31 (the
+// instruction pairs byte b of A's lane-group g with byte b of B's lane-group g).  Tiles of BM x BN
+// x 128 bytes go global -> LDS directly (16-byte pieces), in rows of 128 bytes whose 16-byte chunk c
+// sits at c ^ ((r >> 1) & 7); a fragment is two ds_read_b128.  The B fragment is the MFMA's first
+// operand, so lane l holds C[m = l % 16][n = 4·(l / 16) + e], four consecutive columns.  Tiles are
+// ordered XCD by XCD and their k loops start at rotated k-tiles, as in the bf16 kernel.
+#include <algorithm>
+#include <cstdint>
+
+#include "common.h"
+#include "kernels.h"
+#include "prof.h"
+
+namespace tp {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr unsigned F8_OOB = 0x80000000u;
+
+// ---- E4M3 encoding (round to nearest even, saturating) ------------------------------------------
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return 0x7Fu;                       // NaN
+  if (!(a <= 448.f)) return sign | 0x7Eu;         // saturate
+  if (a < 0.015625f) {                            // below 2^-6: multiples of 2^-9 (8 -> 2^-6, normal)
+    const float m = a * 512.f;                    // exact: a power-of-two scaling
+    return sign | (unsigned)rintf(m);             // round to nearest even
+  }
+  int e = (int)((u >> 23) & 0xFFu) - 127;         // -6 .. 8
+  const unsigned mant = u & 0x7FFFFFu;
+  unsigned keep = mant >> 20, rest = mant & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) {
+    keep = 0u;
+    ++e;
+  }
+  if (e > 8 || (e == 8 && keep == 7u)) return sign | 0x7Eu;
+  return sign | ((unsigned)(e + 7) << 3) | keep;
+}
+
+// ---- amax and the scales --------------------------------------------------------------------------
+constexpr int AMAX_WGS = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_amax_kernel(long n, const T* __restrict__ x, float* __restrict__ part) {
+  __shared__ float red[4];
+  float m = 0.f;
+  const long stride = (long)gridDim.x * 256 * 8;
+  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += stride) {
+    if (i + 8 <= n) {
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 v = *(const bf16x8*)(x + i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)v[j]));
+      } else {
+        const f32x4 a = *(const f32x4*)(x + i), b = *(const f32x4*)(x + i + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(a[j]), fabsf(b[j])));
+      }
+    } else {
+      for (long j = i; j < n; ++j) m = fmaxf(m, fabsf(to_f32(x[j])));
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// scale = 448 / amax (the quantiser's), descale = amax / 448 (the GEMM's); 1 and 1 for amax = 0.
+__global__ __launch_bounds__(256) void fp8_scale_kernel(int parts, const float* __restrict__ part,
+                                                        float* __restrict__ scale, float* __restrict__ descale) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < parts; i += 256) m = fmaxf(m, part[i]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    *scale = amax > 0.f ? 448.f / amax : 1.f;
+    *descale = amax > 0.f ? amax / 448.f : 1.f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(long n, const T* __restrict__ x,
+                                                           const float* __restrict__ scale,
+                                                           unsigned char* __restrict__ q) {
+  const float s = *scale;
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (i + 8 <= n) {
+    float v[8];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 a = *(const bf16x8*)(x + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (float)a[j];
+    } else {
+      const f32x4 a = *(const f32x4*)(x + i), b = *(const f32x4*)(x + i + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+    }
+    unsigned long long w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= (unsigned long long)e4m3_code(v[j] * s) << (8 * j);
+    *(unsigned long long*)(q + i) = w;
+  } else {
+    for (long j = i; j < n; ++j) q[j] = (unsigned char)e4m3_code(to_f32(x[j]) * s);
+  }
+}
+
+// x [rows, cols] -> q [cols, rows], one 64 x 64 tile per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_quantize_t_kernel(int rows, int cols, const T* __restrict__ x,
+                                                             const float* __restrict__ scale,
+                                                             unsigned char* __restrict__ q) {
+  __shared__ unsigned char t[64][64 + 4];
+  const float s = *scale;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    const int gr = r0 + r, gc = c0 + c;
+    t[c][r] = (gr < rows && gc < cols) ? (unsigned char)e4m3_code(to_f32(x[(long)gr * cols + gc]) * s) : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i / 64, r = i % 64;
+    const int gr = r0 + r, gc = c0 + c;
+    if (gr < rows && gc < cols) q[(long)gc * rows + gr] = t[c][r];
+  }
+}
+
+// ---- the GEMM -----------------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_, int ST_ = 2>
+struct F8Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
+  static constexpr int IPW_A = A_BYTES / 1024 / NW, IPW_B = B_BYTES / 1024 / NW;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "loads must split evenly");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(STAGES * STAGE <= 160 * 1024, "LDS holds 160 KiB");
+};
+
+template <int N>
+__device__ __forceinline__ void f8_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ int f8_swz(int r) { return (r >> 1) & 7; }
+
+// The 16-byte pieces of one operand's k-tile this lane loads: row r (of the tile) and byte column c.
+template <int IPW>
+__device__ __forceinline__ void f8_pieces(int wave, int lane, int (&r)[IPW], int (&c)[IPW]) {
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int o = (wave * IPW + j) * 1024 + 16 * lane;
+    r[j] = o >> 7;
+    c[j] = 16 * (((o >> 4) & 7) ^ f8_swz(r[j]));
+  }
+}
+
+template <int W, int IPW>
+__device__ __forceinline__ void f8_load(const unsigned char* p, long ld, int rows_total, int mn0, int k0, int K,
+                                        TP_LDS char* dst, const int (&r)[IPW], const int (&c)[IPW], int wave) {
+  const unsigned char* base = p + (long)mn0 * ld + k0;
+  const unsigned span = (unsigned)((long)(W - 1) * ld + 128);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)span, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const bool ok = (mn0 + r[j] < rows_total) && (k0 + c[j] < K);
+    const unsigned off = (unsigned)((long)r[j] * ld + c[j]);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TP_LDS void*)(dst + (wave * IPW + j) * 1024), 16,
+                                             ok ? off : F8_OOB, 0, 0, 0);
+  }
+}
+
+// Fragment of 16 rows x 128 k: lane l gets row mn0 + l % 16, bytes 32·(l / 16) .. +31.
+__device__ __forceinline__ i32x8 f8_frag(const TP_LDS char* tile, int mn0, int lane) {
+  const int r = mn0 + (lane & 15);
+  const int c = 2 * (lane >> 4);
+  const TP_LDS char* row = tile + r * 128;
+  const u32x4 lo = *(const TP_LDS u32x4*)(row + ((c ^ f8_swz(r)) << 4));
+  const u32x4 hi = *(const TP_LDS u32x4*)(row + (((c + 1) ^ f8_swz(r)) << 4));
+  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+struct F8Desc {
+  int M, N, K;
+  const unsigned char* A;   // [M, K]
+  const unsigned char* B;   // [N, K]
+  const float* da;
+  const float* db;
+  const bf16* bias;         // [N] or nullptr
+  bf16* C;                  // [M, N]
+  bf16* C2;                 // pre-activation [M, N] (GeLU epilogue) or nullptr
+  int gelu;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
+void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int GROUP_M = 4;
+  const int nwg = tiles_m * tiles_n;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (wg / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+
+  int ar[Cfg::IPW_A], ac[Cfg::IPW_A], br[Cfg::IPW_B], bc[Cfg::IPW_B];
+  f8_pieces<Cfg::IPW_A>(wave, lane, ar, ac);
+  f8_pieces<Cfg::IPW_B>(wave, lane, br, bc);
+  const int wm = (wave / Cfg::WN) * Cfg::TM, wn = (wave % Cfg::WN) * Cfg::TN;
+  f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (d.K + 127) / 128;
+  const int rot = nk > 0 ? (tm + tn) % nk : 0;
+  auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * 128; };
+  auto load = [&](int t, int stage) {
+    TP_LDS char* dst = lds + stage * Cfg::STAGE;
+    const int k = kpos(t);
+    f8_load<Cfg::BM, Cfg::IPW_A>(d.A, d.K, d.M, m0, k, d.K, dst, ar, ac, wave);
+    f8_load<Cfg::BN, Cfg::IPW_B>(d.B, d.K, d.N, n0, k, d.K, dst + Cfg::A_BYTES, br, bc, wave);
+  };
+#pragma unroll
+  for (int t = 0; t < Cfg::STAGES - 1; ++t)
+    if (t < nk) load(t, t);
+  int cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + Cfg::STAGES - 2 < nk) f8_wait_vmcnt<(Cfg::STAGES - 2) * (Cfg::IPW_A + Cfg::IPW_B)>();
+    else f8_wait_vmcnt<0>();
+    __syncthreads();
+    const TP_LDS char* at = lds + cur * Cfg::STAGE;
+    const TP_LDS char* bt = at + Cfg::A_BYTES;
+    if (kt + Cfg::STAGES - 1 < nk) {
+      int ns = cur + Cfg::STAGES - 1;
+      if (ns >= Cfg::STAGES) ns -= Cfg::STAGES;
+      load(kt + Cfg::STAGES - 1, ns);
+    }
+    i32x8 af[Cfg::FM], bfr[Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) af[i] = f8_frag(at, wm + 16 * i, lane);
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) bfr[j] = f8_frag(bt, wn + 16 * j, lane);
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+    if (++cur == Cfg::STAGES) cur = 0;
+  }
+
+  const float sc = *d.da * *d.db;
+  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i) {
+    const int m = m0 + wm + 16 * i + r16;
+    if (m >= d.M) continue;
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int n = n0 + wn + 16 * j + g4;
+      if (n >= d.N) continue;
+      float a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = acc[i][j][e] * sc;
+      if (d.bias) {
+        const bf16x4 b = *(const bf16x4*)(d.bias + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
+      }
+      const long o = (long)m * d.N + n;
+      if (d.gelu) {
+        if (d.C2) *(bf16x4*)(d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = gelu_f(a[e]);
+      }
+      *(bf16x4*)(d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    }
+  }
+}
+
+using F8C0 = F8Tile<256, 256, 4, 2, 2>;   // 64 x 128 per wave
+using F8C1 = F8Tile<256, 128, 4, 2, 2>;   // 64 x 64 per wave
+
+template <class Cfg>
+hipError_t f8_run(const F8Desc& d, hipStream_t s) {
+  const int tm = (d.M + Cfg::BM - 1) / Cfg::BM, tn = (d.N + Cfg::BN - 1) / Cfg::BN;
+  gemm_fp8_nt_kernel<Cfg><<<tm * tn, Cfg::NT, 0, s>>>(d, tm, tn);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t fp8_quantize_ws_bytes() { return (AMAX_WGS + 64) * sizeof(float); }
+
+hipError_t launch_fp8_quantize(int dtype, int rows, int cols, const void* x, bool transpose, unsigned char* q,
+                               float* descale, float* ws, hipStream_t s) {
+  const long n = (long)rows * cols;
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  float* part = ws;
+  float* scale = ws + AMAX_WGS;
+  const int wgs = n > 0 ? (int)std::min<long>(AMAX_WGS, (n + 2047) / 2048) : 0;
+  {
+    ProfScope p("fp8_amax", s, (double)n, es * n);
+    if (wgs > 0) {
+      if (dtype == DT_BF16) fp8_amax_kernel<bf16><<<wgs, 256, 0, s>>>(n, (const bf16*)x, part);
+      else fp8_amax_kernel<float><<<wgs, 256, 0, s>>>(n, (const float*)x, part);
+    }
+    fp8_scale_kernel<<<1, 256, 0, s>>>(wgs, part, scale, descale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n == 0) return hipSuccess;
+  ProfScope p(transpose ? "fp8_quantize_t" : "fp8_quantize", s, (double)n, es * n + n);
+  if (transpose) {
+    dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+    if (dtype == DT_BF16) fp8_quantize_t_kernel<bf16><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, q);
+    else fp8_quantize_t_kernel<float><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, q);
+  } else {
+    const long blocks = (n + 2047) / 2048;
+    if (dtype == DT_BF16) fp8_quantize_kernel<bf16><<<(unsigned)blocks, 256, 0, s>>>(n, (const bf16*)x, scale, q);
+    else fp8_quantize_kernel<float><<<(unsigned)blocks, 256, 0, s>>>(n, (const float*)x, scale, q);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* da, const unsigned char* B,
+                              const float* db, const void* bias, int gelu, void* C, void* C2, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  F8Desc d{M, N, K, A, B, da, db, (const bf16*)bias, (bf16*)C, (bf16*)C2, gelu};
+  const double flop = 2.0 * M * (double)N * K;
+  const double bytes = (double)M * K + (double)N * K + 2.0 * M * (double)N * (gelu && C2 ? 2.0 : 1.0);
+  // the 256 x 256 tile unless it leaves most of the chip idle (fewer than 192 tiles)
+  const long t0 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (t0 >= 192) {
+    ProfScope p("gemm_fp8_nt<256x256>", s, flop, bytes);
+    return f8_run<F8C0>(d, s);
+  }
+  ProfScope p("gemm_fp8_nt<256x128>", s, flop, bytes);
+  return f8_run<F8C1>(d, s);
+}
+
+}  // namespace tp

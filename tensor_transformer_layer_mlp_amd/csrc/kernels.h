@@ -77,6 +77,13 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
                               void* A1, void* Y, void* ws, hipStream_t s, const int* row_token = nullptr,
                               int tokens = 0);
 
+// FP8 (OCP E4M3) quantisation with one scale per tensor and the GEMM on codes (see fp8.hip).
+size_t fp8_quantize_ws_bytes();
+hipError_t launch_fp8_quantize(int dtype, int rows, int cols, const void* x, bool transpose, unsigned char* q,
+                               float* descale, float* ws, hipStream_t s);
+hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* da, const unsigned char* B,
+                              const float* db, const void* bias, int gelu, void* C, void* C2, hipStream_t s);
+
 // MoE routing and combine (see moe.hip).
 int moe_max_experts();
 int moe_max_top_k();
