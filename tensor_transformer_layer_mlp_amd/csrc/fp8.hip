@@ -312,6 +312,7 @@ void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
 
 using F8C0 = F8Tile<256, 256, 4, 2, 2>;   // 64 x 128 per wave
 using F8C1 = F8Tile<256, 128, 4, 2, 2>;   // 64 x 64 per wave
+using F8C2 = F8Tile<256, 192, 4, 2, 2>;   // 64 x 96 per wave
 
 template <class Cfg>
 hipError_t f8_run(const F8Desc& d, hipStream_t s) {
@@ -361,11 +362,26 @@ hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const
   F8Desc d{M, N, K, A, B, da, db, (const bf16*)bias, (bf16*)C, (bf16*)C2, gelu};
   const double flop = 2.0 * M * (double)N * K;
   const double bytes = (double)M * K + (double)N * K + 2.0 * M * (double)N * (gelu && C2 ? 2.0 : 1.0);
-  // the 256 x 256 tile unless it leaves most of the chip idle (fewer than 192 tiles)
-  const long t0 = (long)((M + 255) / 256) * ((N + 255) / 256);
-  if (t0 >= 192) {
+  // tile choice: (waves of 256 tiles) x tile area / relative per-tile rate, the smallest wins
+  const int bn[3] = {256, 192, 128};
+  const double rate[3] = {1.0, 0.95, 0.8};
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < 3; ++c) {
+    const long t = (long)((M + 255) / 256) * ((N + bn[c] - 1) / bn[c]);
+    const double est = (double)((t + 255) / 256) * 256.0 * bn[c] / rate[c];
+    if (est < best_t * 0.999) {
+      best_t = est;
+      best = c;
+    }
+  }
+  if (best == 0) {
     ProfScope p("gemm_fp8_nt<256x256>", s, flop, bytes);
     return f8_run<F8C0>(d, s);
+  }
+  if (best == 1) {
+    ProfScope p("gemm_fp8_nt<256x192>", s, flop, bytes);
+    return f8_run<F8C2>(d, s);
   }
   ProfScope p("gemm_fp8_nt<256x128>", s, flop, bytes);
   return f8_run<F8C1>(d, s);

@@ -61,8 +61,10 @@ def _codes(shape, tag, std=1.0):
     return q, d
 
 
+# small shapes take the 256 x 128 tile; (2048, 6144) and the ragged (2000, 9000) the 256 x 192 one;
+# (2048, 16384) the 256 x 256 one
 GCASES = [(256, 256, 128, False), (300, 200, 176, True), (17, 8, 16, False), (2048, 6144, 1024, True),
-          (513, 1032, 2064, False)]
+          (513, 1032, 2064, False), (2000, 9000, 64, True), (2048, 16384, 256, False)]
 
 
 @pytest.mark.parametrize("M,N,K,epi", GCASES, ids=[f"m{m}_n{n}_k{k}{'_gelu' if e else ''}" for m, n, k, e in GCASES])
