@@ -5,7 +5,7 @@ CPU-baseline leg, never by the product path.  Shares no code with the HIP librar
 """
 
 from .tp_shard import *  # noqa: F401,F403
-from .tp_shard import (shard_range, qkv_column_range, slice_qkv, slice_fc1, slice_fc2,
+from .tp_shard import (shard_range, qkv_column_range, slice_qkv, slice_fc1, slice_fc2, gelu_tanh, gelu_tanh_grad,
                        slice_attn_out, attn_out_fwd, attn_out_bwd, gelu,
                        gelu_grad, attention_fwd, attention_bwd, qkv_fwd, qkv_bwd, mlp_fwd, mlp_bwd,
                        layer_fwd, tp_qkv_shard_fwd, tp_attn_heads_fwd, tp_mlp_shard_fwd,

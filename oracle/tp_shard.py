@@ -20,7 +20,8 @@ Sources (the pages this follows; each is cited by title and section):
               are split along the sequence.
 
 Readings where the pages are silent (numbered as in the design notes):
-  R1 activation  = exact GeLU, x·Φ(x) = ½x(1 + erf(x/√2)); the pages name no activation.
+  R1 activation  = exact GeLU, x·Φ(x) = ½x(1 + erf(x/√2)); the pages name no activation.  Option:
+                   the tanh form ½x(1 + tanh(√(2/π)(x + 0.044715x³))), GeLU's standard approximation.
   R2 attention   = scaled dot-product, scores·1/√d, causal (key j visible to query i iff j <= i),
                    softmax over keys; LSE_i = log Σ_j exp(score_ij) over visible keys.
   R3 QKV columns = head-interleaved: column h·3d + s·d + j holds part s∈{q,k,v}, element j of head h,
@@ -140,6 +141,31 @@ def gelu_grad(x):
     return 0.5 * (1.0 + _erf(x / _SQRT2)) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
 
 
+_C_TANH = math.sqrt(2.0 / math.pi)
+
+
+def gelu_tanh(x):
+    """The tanh approximation of GeLU: ½x(1 + tanh(√(2/π)(x + 0.044715x³)))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(_C_TANH * (x + 0.044715 * x ** 3)))
+
+
+def gelu_tanh_grad(x):
+    """Its derivative: ½(1 + t) + ½x(1 − t²)·√(2/π)(1 + 3·0.044715x²), t = tanh(√(2/π)(x + 0.044715x³))."""
+    x = np.asarray(x, dtype=np.float64)
+    t = np.tanh(_C_TANH * (x + 0.044715 * x ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * _C_TANH * (1.0 + 3 * 0.044715 * x * x)
+
+
+def _activation(a):
+    """(function, derivative) of activation a: 0 the exact GeLU, 1 its tanh form."""
+    if a == 0:
+        return gelu, gelu_grad
+    if a == 1:
+        return gelu_tanh, gelu_tanh_grad
+    raise ValueError(f"unknown activation {a}")
+
+
 # ---- attention (readings R2, R3) ---------------------------------------------------------------
 
 def _heads(QKV, B: int, S: int, n_heads: int, d: int):
@@ -211,23 +237,23 @@ def qkv_bwd(X, Wqkv, dQKV):
     return {"dX": dQKV @ Wqkv.T, "dW": X.T @ dQKV, "db": dQKV.sum(axis=0)}
 
 
-def mlp_fwd(X, W1, b1, W2, b2):
-    """A1 = X·W1 + b1;  Y = GeLU(A1);  Z = Y·W2 (+ b2 when b2 is not None)."""
+def mlp_fwd(X, W1, b1, W2, b2, activation=0):
+    """A1 = X·W1 + b1;  Y = GeLU(A1) (activation 1: the tanh form);  Z = Y·W2 (+ b2 when b2 is not None)."""
     A1 = X @ W1 + b1
-    Y = gelu(A1)
+    Y = _activation(activation)[0](A1)
     Z = Y @ W2
     if b2 is not None:
         Z = Z + b2
     return {"A1": A1, "Y": Y, "Z": Z}
 
 
-def mlp_bwd(X, W1, W2, A1, Y, dZ, with_db2: bool):
+def mlp_bwd(X, W1, W2, A1, Y, dZ, with_db2: bool, activation=0):
     """Backward of mlp_fwd, from the chain rule written out:
 
     dW2 = Yᵀ·dZ;  db2 = Σ_t dZ;  dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1);  db1 = Σ_t dA1;
     dW1 = Xᵀ·dA1;  dX = dA1·W1ᵀ.
     """
-    dA1 = (dZ @ W2.T) * gelu_grad(A1)
+    dA1 = (dZ @ W2.T) * _activation(activation)[1](A1)
     return {"dX": dA1 @ W1.T, "dW1": X.T @ dA1, "db1": dA1.sum(axis=0),
             "dW2": Y.T @ dZ, "db2": dZ.sum(axis=0) if with_db2 else None, "dA1": dA1}
 
@@ -332,22 +358,22 @@ def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r):
     return attention_fwd(QKV_r, B, S, nh, d)
 
 
-def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2):
+def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, activation=0):
     """fc1 column shard + GeLU, fc2 row shard -> partial Z_r; b2 added iff rank == 0 (R5).
 
     Σ_r Z_r is the unsharded Z: the all-reduce at the RowParallelLinear exit ([Arch] §4).
     """
     _, fr = shard_range(F, tp_size, rank)
     assert X.shape == (T, H) and W1_r.shape == (H, fr) and W2_r.shape == (fr, H)
-    return mlp_fwd(X, W1_r, b1_r, W2_r, b2 if rank == 0 else None)
+    return mlp_fwd(X, W1_r, b1_r, W2_r, b2 if rank == 0 else None, activation)
 
 
-def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ):
+def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, activation=0):
     """Backward of the rank's MLP shard.  dZ is the full upstream gradient (R9); dX_r is a partial
     whose sum over ranks is dX (copy's backward all-reduce, [Arch] §4); db2 iff rank == 0 (R5)."""
     _, fr = shard_range(F, tp_size, rank)
     assert dZ.shape == (T, H) and A1_r.shape == (T, fr) and Y_r.shape == (T, fr)
-    return mlp_bwd(X, W1_r, W2_r, A1_r, Y_r, dZ, with_db2=(rank == 0))
+    return mlp_bwd(X, W1_r, W2_r, A1_r, Y_r, dZ, with_db2=(rank == 0), activation=activation)
 
 
 def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r):

@@ -92,6 +92,25 @@ def pin_gelu():
     fd = (T.gelu(xs + eps) - T.gelu(xs - eps)) / (2 * eps)
     assert np.max(np.abs(fd - T.gelu_grad(xs))) < 1e-9, "GeLU' vs central differences"
     assert abs(float(T.gelu(12.0)) - 12.0) < 1e-12 and abs(float(T.gelu(-12.0))) < 1e-12
+    # the tanh form: its defining value at 1 (tanh(√(2/π)·1.044715) from the standard library),
+    # the odd-part identity (tanh is odd), closeness to the exact GeLU, its derivative by differences
+    t1 = 0.5 * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * 1.044715))
+    assert abs(float(T.gelu_tanh(1.0)) - t1) < 1e-15 and abs(t1 - 0.8411919906082768) < 1e-13
+    assert np.allclose(T.gelu_tanh(xs) - T.gelu_tanh(-xs), xs, rtol=0, atol=1e-13), "tanh form: odd part"
+    assert np.max(np.abs(T.gelu_tanh(xs) - T.gelu(xs))) < 1e-3, "tanh form within 1e-3 of the exact GeLU"
+    assert np.max(np.abs(T.gelu_tanh(xs) - T.gelu(xs))) > 1e-5, "and not equal to it"
+    fdt = (T.gelu_tanh(xs + eps) - T.gelu_tanh(xs - eps)) / (2 * eps)
+    assert np.max(np.abs(fdt - T.gelu_tanh_grad(xs))) < 1e-9, "tanh form derivative vs central differences"
+    # the MLP with the tanh form uses it in both directions
+    g = _rng(81)
+    X, W1, b1, W2 = g.standard_normal((3, 4)), g.standard_normal((4, 5)), g.standard_normal(5), g.standard_normal((5, 2))
+    fw = T.mlp_fwd(X, W1, b1, W2, None, activation=1)
+    _close(fw["Y"], T.gelu_tanh(X @ W1 + b1), 1e-15, "tanh-form MLP forward")
+    dZ = g.standard_normal((3, 2))
+    bw = T.mlp_bwd(X, W1, W2, fw["A1"], fw["Y"], dZ, False, activation=1)
+    want = _fd_dir(lambda z: float((T.mlp_fwd(X, z, b1, W2, None, activation=1)["Z"] * dZ).sum()), W1,
+                   np.ones_like(W1))
+    assert abs(float(bw["dW1"].sum()) - want) < 1e-7 * max(1, abs(want)), "tanh-form backward by differences"
 
 
 # ---- tiny layer --------------------------------------------------------------------------------

@@ -231,6 +231,11 @@ _ORIG_DECODE = T.e4m3_decode
 _ORIG_QUANT = T.fp8_quantize
 
 
+def _gelu_tanh_cubic_dropped(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * x))
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -271,6 +276,7 @@ MUTANTS = {
     "e4m3_exponent_bias_8": {"e4m3_decode": _e4m3_decode_bias8},
     "e4m3_ties_away": {"e4m3_encode": _e4m3_encode_ties_up},
     "fp8_descale_inverted": {"fp8_quantize": _fp8_quantize_descale_inverted},
+    "gelu_tanh_cubic_dropped": {"gelu_tanh": _gelu_tanh_cubic_dropped},
 }
 
 
