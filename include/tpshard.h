@@ -52,6 +52,9 @@ extern "C" {
 
 typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
 
+/* The MLP's activation: the exact GeLU x·Φ(x), or its tanh form ½x(1 + tanh(√(2/π)(x + 0.044715x³))). */
+typedef enum { TP_GELU = 0, TP_GELU_TANH = 1 } tp_activation;
+
 typedef enum {
   TP_OK = 0,
   TP_EINVAL = -1,        /* a size, rank or dtype out of range, or a shape the split does not allow */
@@ -103,6 +106,19 @@ int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype,
                      const void* Y_r, const void* dZ, void* dX_r, void* dW1_r, void* db1_r,
                      void* dW2_r, void* db2, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* tp_mlp_shard_fwd and tp_mlp_shard_bwd with the activation chosen (TP_GELU, as the plain calls
+ * use, or TP_GELU_TANH; its derivative in the backward).  TP_EINVAL for another value.  The tanh
+ * form is GeLU's usual approximation; the pages name no activation, so it is an option beside the
+ * exact form the library takes by default. */
+int tp_mlp_shard_fwd_act(int tp_size, int rank, int T, int H, int F, int dtype,
+                         const void* X, const void* W1_r, const void* b1_r, const void* W2_r,
+                         const void* b2, void* Z_r, void* A1_r, void* Y_r, int activation, void* stream);
+int tp_mlp_shard_bwd_act(int tp_size, int rank, int T, int H, int F, int dtype,
+                         const void* X, const void* W1_r, const void* W2_r, const void* A1_r,
+                         const void* Y_r, const void* dZ, void* dX_r, void* dW1_r, void* db1_r,
+                         void* dW2_r, void* db2, void* workspace, size_t workspace_bytes, int activation,
+                         void* stream);
 
 /* A6 — QKV shard backward: dWqkv_r = Xᵀ·dQKV_r ; dbqkv_r = Σ_t dQKV_r ; dX_r = dQKV_r·Wqkv_rᵀ
  * (a partial).  workspace: tp_workspace_bytes("tp_qkv_shard_bwd", ...). */
@@ -240,7 +256,8 @@ int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose,
 
 /* GEMM on E4M3 codes, both operands K-major:
  *   pre = (A·Bᵀ)·a_descale·b_descale (+ bias[n]),  A [M, K] codes, B [N, K] codes, fp32 accumulation
- *   C = pre (gelu == 0) or GeLU(pre) with C_pre = pre when C_pre != NULL (gelu != 0)
+ *   C = pre (gelu == 0) or GeLU(pre) with C_pre = pre when C_pre != NULL (gelu 1: the exact GeLU,
+ *   gelu 2: its tanh form; TP_EINVAL for another value)
  * C, C_pre, bias bf16; descales fp32 scalars in device memory (as tp_fp8_quantize writes them).
  * Requires K % 16 == 0, N % 8 == 0, operands below 2 GiB (TP_EUNSUPPORTED otherwise). */
 int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_descale, const unsigned char* B,

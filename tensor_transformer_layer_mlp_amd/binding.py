@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 
 TP_BF16, TP_F32 = 0, 1
+TP_GELU, TP_GELU_TANH = 0, 1
 STATUS = {0: "TP_OK", -1: "TP_EINVAL", -2: "TP_ENULL", -3: "TP_EALIGN", -4: "TP_EUNSUPPORTED",
           -5: "TP_EWORKSPACE", -6: "TP_EHIP"}
 
@@ -25,6 +26,8 @@ _SIGNATURES = {
     "tp_attn_heads_fwd": (_I, [_I] * 7 + [_P] * 3 + [_P]),
     "tp_mlp_shard_fwd": (_I, [_I] * 6 + [_P] * 8 + [_P]),
     "tp_mlp_shard_bwd": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _P]),
+    "tp_mlp_shard_fwd_act": (_I, [_I] * 6 + [_P] * 8 + [_I, _P]),
+    "tp_mlp_shard_bwd_act": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _I, _P]),
     "tp_qkv_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
     "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
     "tp_attn_out_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
@@ -159,23 +162,24 @@ def tp_attn_heads_fwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r=None,
     _check(rc, "tp_attn_heads_fwd")
 
 
-def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r, Y_r, stream=None):
+def tp_mlp_shard_fwd(tp_size, rank, T, H, F, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r, Y_r, stream=None, activation=None):
     dt = X.dtype
     Fr = _cols(tp_size, rank, F)
     if Fr and T >= 0 and H >= 1:
         for t, n, name in ((X, T * H, "X"), (W1_r, H * Fr, "W1_r"), (b1_r, Fr, "b1_r"), (W2_r, Fr * H, "W2_r"),
                            (b2, H, "b2"), (Z_r, T * H, "Z_r"), (A1_r, T * Fr, "A1_r"), (Y_r, T * Fr, "Y_r")):
             _need(t, n, name)
-    rc = raw().tp_mlp_shard_fwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
-                                _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),
-                                _ptr(W2_r, "W2_r", dt), _ptr(b2, "b2", dt, True),
-                                _ptr(Z_r, "Z_r", dt), _ptr(A1_r, "A1_r", dt, True),
-                                _ptr(Y_r, "Y_r", dt), _stream(stream))
-    _check(rc, "tp_mlp_shard_fwd")
+    args = (tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt), _ptr(W1_r, "W1_r", dt), _ptr(b1_r, "b1_r", dt),
+            _ptr(W2_r, "W2_r", dt), _ptr(b2, "b2", dt, True), _ptr(Z_r, "Z_r", dt), _ptr(A1_r, "A1_r", dt, True),
+            _ptr(Y_r, "Y_r", dt))
+    if activation is None:      # the plain entry point: the exact GeLU
+        _check(raw().tp_mlp_shard_fwd(*args, _stream(stream)), "tp_mlp_shard_fwd")
+    else:
+        _check(raw().tp_mlp_shard_fwd_act(*args, activation, _stream(stream)), "tp_mlp_shard_fwd_act")
 
 
 def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r, dW1_r, db1_r,
-                     dW2_r, db2, workspace, stream=None):
+                     dW2_r, db2, workspace, stream=None, activation=None):
     dt = X.dtype
     Fr = _cols(tp_size, rank, F)
     if Fr and T >= 0 and H >= 1:
@@ -183,15 +187,15 @@ def tp_mlp_shard_bwd(tp_size, rank, T, H, F, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r,
                            (Y_r, T * Fr, "Y_r"), (dZ, T * H, "dZ"), (dX_r, T * H, "dX_r"), (dW1_r, H * Fr, "dW1_r"),
                            (db1_r, Fr, "db1_r"), (dW2_r, Fr * H, "dW2_r"), (db2, H, "db2")):
             _need(t, n, name)
-    rc = raw().tp_mlp_shard_bwd(tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt),
-                                _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
-                                _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(dZ, "dZ", dt),
-                                _ptr(dX_r, "dX_r", dt), _ptr(dW1_r, "dW1_r", dt),
-                                _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt),
-                                _ptr(db2, "db2", dt, True), _ptr(workspace, "workspace", None, True),
-                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                _stream(stream))
-    _check(rc, "tp_mlp_shard_bwd")
+    args = (tp_size, rank, T, H, F, _dtype_code(X), _ptr(X, "X", dt), _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
+            _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(dZ, "dZ", dt), _ptr(dX_r, "dX_r", dt),
+            _ptr(dW1_r, "dW1_r", dt), _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt), _ptr(db2, "db2", dt, True),
+            _ptr(workspace, "workspace", None, True),
+            workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    if activation is None:      # the plain entry point: the exact GeLU
+        _check(raw().tp_mlp_shard_bwd(*args, _stream(stream)), "tp_mlp_shard_bwd")
+    else:
+        _check(raw().tp_mlp_shard_bwd_act(*args, activation, _stream(stream)), "tp_mlp_shard_bwd_act")
 
 
 def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r,
@@ -380,7 +384,8 @@ def tp_fp8_quantize(x, q, descale, workspace, transpose=False, stream=None):
 
 
 def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, gelu=False, C_pre=None, stream=None):
-    """C [M, N] bf16 = (A·Bᵀ)·descales (+ bias) (-> GeLU) for E4M3 codes A [M, K], B [N, K]."""
+    """C [M, N] bf16 = (A·Bᵀ)·descales (+ bias) (-> GeLU) for E4M3 codes A [M, K], B [N, K].
+    gelu: False / 0 none, True / 1 the exact GeLU, 2 its tanh form."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K:
@@ -390,7 +395,7 @@ def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, gelu=False, C_pre=N
         _need(t, k, name)
     rc = raw().tp_fp8_gemm_nt(M, N, K, _ptr(A, "A", torch.uint8), _ptr(a_descale, "a_descale", torch.float32),
                               _ptr(B, "B", torch.uint8), _ptr(b_descale, "b_descale", torch.float32),
-                              _ptr(bias, "bias", torch.bfloat16, True), 1 if gelu else 0,
+                              _ptr(bias, "bias", torch.bfloat16, True), int(gelu),
                               _ptr(C, "C", torch.bfloat16), _ptr(C_pre, "C_pre", torch.bfloat16, True), _stream(stream))
     _check(rc, "tp_fp8_gemm_nt")
 

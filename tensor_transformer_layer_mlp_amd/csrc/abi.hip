@@ -226,9 +226,10 @@ int tp_attn_heads_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
   return TP_OK;
 }
 
-int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
-                     const void* W1_r, const void* b1_r, const void* W2_r, const void* b2, void* Z_r,
-                     void* A1_r, void* Y_r, void* stream) {
+int tp_mlp_shard_fwd_act(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                         const void* W1_r, const void* b1_r, const void* W2_r, const void* b2, void* Z_r,
+                         void* A1_r, void* Y_r, int activation, void* stream) {
+  TP_CHECK(activation == TP_GELU || activation == TP_GELU_TANH, TP_EINVAL, "activation %d unknown", activation);
   MlpGeom g;
   int st = mlp_geom(tp_size, rank, T, H, F, dtype, &g);
   if (st) return st;
@@ -238,6 +239,7 @@ int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
   GemmDesc fc1 = gemm_desc(dtype, T, g.Fr, H, X, H, true, W1_r, g.Fr, false, Y_r, g.Fr, EPI_BIAS_GELU);
   fc1.bias = b1_r;
   fc1.C2 = A1_r;
+  fc1.act = activation;
   TP_TRY(launch_gemm(fc1, s), "fc1 gemm");
   const bool add_b2 = (rank == 0 && b2 != nullptr);
   GemmDesc fc2 = gemm_desc(dtype, T, H, g.Fr, Y_r, g.Fr, true, W2_r, H, false, Z_r, H,
@@ -247,10 +249,18 @@ int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
   return TP_OK;
 }
 
-int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
-                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
-                     const void* dZ, void* dX_r, void* dW1_r, void* db1_r, void* dW2_r, void* db2,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+int tp_mlp_shard_fwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                     const void* W1_r, const void* b1_r, const void* W2_r, const void* b2, void* Z_r,
+                     void* A1_r, void* Y_r, void* stream) {
+  return tp_mlp_shard_fwd_act(tp_size, rank, T, H, F, dtype, X, W1_r, b1_r, W2_r, b2, Z_r, A1_r, Y_r, TP_GELU,
+                              stream);
+}
+
+int tp_mlp_shard_bwd_act(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                         const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
+                         const void* dZ, void* dX_r, void* dW1_r, void* db1_r, void* dW2_r, void* db2,
+                         void* workspace, size_t workspace_bytes, int activation, void* stream) {
+  TP_CHECK(activation == TP_GELU || activation == TP_GELU_TANH, TP_EINVAL, "activation %d unknown", activation);
   MlpGeom g;
   int st = mlp_geom(tp_size, rank, T, H, F, dtype, &g);
   if (st) return st;
@@ -273,6 +283,7 @@ int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
   GemmDesc g2 = gemm_desc(dtype, T, Fr, H, dZ, H, true, W2_r, H, true, dA1, Fr, EPI_DGELU);
   g2.aux = A1_r;
   g2.ld_aux = Fr;
+  g2.act = activation;
   // dW1_r = Xᵀ·dA1   (M = H, N = F_r, K = T)
   GemmDesc g3 = gemm_desc(dtype, H, Fr, T, X, H, false, dA1, Fr, false, dW1_r, Fr, EPI_STORE);
   // dX_r = dA1·W1_rᵀ   (M = T, N = H, K = F_r)
@@ -303,6 +314,14 @@ int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
     TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
   }
   return rc;
+}
+
+int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, const void* X,
+                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
+                     const void* dZ, void* dX_r, void* dW1_r, void* db1_r, void* dW2_r, void* db2,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return tp_mlp_shard_bwd_act(tp_size, rank, T, H, F, dtype, X, W1_r, W2_r, A1_r, Y_r, dZ, dX_r, dW1_r, db1_r, dW2_r,
+                              db2, workspace, workspace_bytes, TP_GELU, stream);
 }
 
 int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
@@ -559,7 +578,8 @@ int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_d
   TP_CHECK((long)M * K < 0x7fffffffL && (long)N * K < 0x7fffffffL, TP_EUNSUPPORTED, "an operand above 2 GiB");
   NEED(A, "A", (long)M * K); NEED(B, "B", (long)N * K); NEED4(a_descale, "a_descale", 1);
   NEED4(b_descale, "b_descale", 1); NEED(C, "C", (long)M * N); MAYBE(bias, "bias"); MAYBE(C_pre, "C_pre");
-  TP_TRY(launch_fp8_gemm_nt(M, N, K, A, a_descale, B, b_descale, bias, gelu != 0, C, gelu ? C_pre : nullptr,
+  TP_CHECK(gelu >= 0 && gelu <= 2, TP_EINVAL, "gelu %d is not 0 (none), 1 (exact) or 2 (tanh form)", gelu);
+  TP_TRY(launch_fp8_gemm_nt(M, N, K, A, a_descale, B, b_descale, bias, gelu, C, gelu ? C_pre : nullptr,
                             (hipStream_t)stream), "fp8 gemm");
   return TP_OK;
 }

@@ -32,6 +32,19 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) +
          x * 0.39894228040143268f * expf(-0.5f * x * x);
 }
+// The tanh form ½x(1 + tanh(u)), u = √(2/π)(x + 0.044715x³); its derivative
+// ½(1 + t) + ½x(1 − t²)·√(2/π)(1 + 3·0.044715x²), t = tanh(u) (tanhf from the device math library).
+__device__ __forceinline__ float gelu_tanh_f(float x) {
+  const float t = tanhf(0.79788456080286536f * (x + 0.044715f * x * x * x));
+  return 0.5f * x * (1.0f + t);
+}
+__device__ __forceinline__ float gelu_tanh_grad_f(float x) {
+  const float t = tanhf(0.79788456080286536f * (x + 0.044715f * x * x * x));
+  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * 0.79788456080286536f * (1.0f + 0.134145f * x * x);
+}
+// activation `act`: 0 the exact GeLU, 1 its tanh form (a uniform branch in the epilogues)
+__device__ __forceinline__ float act_f(float x, int act) { return act ? gelu_tanh_f(x) : gelu_f(x); }
+__device__ __forceinline__ float act_grad_f(float x, int act) { return act ? gelu_tanh_grad_f(x) : gelu_grad_f(x); }
 
 // ---- matrix-core instructions (CDNA4) ------------------------------------------------------------
 // 16x16x32 bf16: lane l supplies row (l % 16), k = 8*(l / 16) .. +7 of its operand; the result lane l

@@ -214,7 +214,7 @@ struct F8Desc {
   const bf16* bias;         // [N] or nullptr
   bf16* C;                  // [M, N]
   bf16* C2;                 // pre-activation [M, N] (GeLU epilogue) or nullptr
-  int gelu;
+  int gelu;                 // 0 none, 1 exact GeLU, 2 tanh form
 };
 
 template <class Cfg>
@@ -303,7 +303,7 @@ void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
       if (d.gelu) {
         if (d.C2) *(bf16x4*)(d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = gelu_f(a[e]);
+        for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.gelu - 1);
       }
       *(bf16x4*)(d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
     }

@@ -164,11 +164,11 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
   }
   if constexpr (EPI == EPI_BIAS_GELU) {
     if (d.C2) *(bf16x4*)((bf16*)d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    for (int e = 0; e < 4; ++e) a[e] = gelu_f(a[e]);
+    for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.act);
   }
   if constexpr (EPI == EPI_DGELU) {
     const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
-    for (int e = 0; e < 4; ++e) a[e] *= gelu_grad_f((float)x[e]);
+    for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.act);
   }
   *(bf16x4*)((bf16*)d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
 }
@@ -293,7 +293,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
         if constexpr (EPI == EPI_DGELU) {
           if (m < d.M && n < d.N) {
             const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
-            for (int e = 0; e < 4; ++e) a[e] *= gelu_grad_f((float)x[e]);
+            for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.act);
           }
         }
         acc[i][j] = a;
@@ -309,7 +309,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
           const int ob = ((((c >> 3) ^ (r & 7)) << 4) | ((c & 7) << 1));
           f32x4 a = acc[i][j];
           if (gelu)
-            for (int e = 0; e < 4; ++e) a[e] = gelu_f(a[e]);
+            for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.act);
           *(TP_LDS bf16x4*)(lds + r * RB + ob) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
         }
       __syncthreads();

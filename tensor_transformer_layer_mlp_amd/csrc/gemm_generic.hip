@@ -28,10 +28,10 @@ __device__ __forceinline__ void store_epi(const GemmDesc& d, int m, int n, float
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     float a = v + to_f32(((const T*)d.bias)[n]);
     if (d.C2) ((T*)d.C2)[o] = from_f32<T>(a);
-    C[o] = from_f32<T>(gelu_f(a));
+    C[o] = from_f32<T>(act_f(a, d.act));
   } else {
     float a = to_f32(((const T*)d.aux)[(long)m * d.ld_aux + n]);
-    C[o] = from_f32<T>(v * gelu_grad_f(a));
+    C[o] = from_f32<T>(v * act_grad_f(a, d.act));
   }
 }
 

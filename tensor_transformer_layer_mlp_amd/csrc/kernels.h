@@ -12,7 +12,7 @@ enum Dtype { DT_BF16 = 0, DT_F32 = 1 };
 enum Epi {
   EPI_STORE = 0,      // C = acc
   EPI_BIAS = 1,       // C = acc + bias[n]
-  EPI_BIAS_GELU = 2,  // C2 = acc + bias[n] (if C2), C = GeLU(acc + bias[n])
+  EPI_BIAS_GELU = 2,  // C2 = acc + bias[n] (if C2), C = GeLU(acc + bias[n])   (GeLU per `act`)
   EPI_DGELU = 3       // C = acc * GeLU'(aux[m, n])
 };
 
@@ -33,6 +33,7 @@ struct GemmDesc {
   // of the a_rows_n-row matrix at A; indices outside [0, a_rows_n) read as zero rows.
   const int* a_rows;
   int a_rows_n;
+  int act;             // the GeLU epilogues' activation: 0 exact, 1 tanh form
 };
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
@@ -81,6 +82,7 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
 size_t fp8_quantize_ws_bytes();
 hipError_t launch_fp8_quantize(int dtype, int rows, int cols, const void* x, bool transpose, unsigned char* q,
                                float* descale, float* ws, hipStream_t s);
+// gelu: 0 none, 1 the exact GeLU, 2 its tanh form.
 hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* da, const unsigned char* B,
                               const float* db, const void* bias, int gelu, void* C, void* C2, hipStream_t s);
 

@@ -102,6 +102,23 @@ def test_mlp_validation(lib):
     assert b(*args2, P, 1 << 30, None) == -2                                 # dZ NULL
 
 
+def test_activation_validation(lib):
+    f = lib.tp_mlp_shard_fwd_act
+    assert f(2, 0, 64, 64, 256, 0, P, P, P, P, P, P, P, P, 2, None) == -1          # unknown activation
+    assert f(2, 0, 64, 64, 256, 0, P, P, P, P, P, P, P, P, -1, None) == -1
+    assert f(2, 0, 64, 64, 1, 0, P, P, P, P, P, P, P, P, 1, None) == -1           # F < tp_size
+    b = lib.tp_mlp_shard_bwd_act
+    assert b(2, 0, 64, 64, 256, 0, *([P] * 11), P, 1 << 30, 5, None) == -1
+    assert b(2, 0, 64, 64, 256, 0, *([P] * 11), None, 0, 1, None) == -5
+    g = lib.tp_fp8_gemm_nt
+    assert g(16, 16, 16, P, P, P, P, None, 3, P, None, None) == -1                 # gelu 3
+    assert g(16, 16, 24, P, P, P, P, None, 0, P, None, None) == -4                 # K % 16
+    assert g(16, 12, 16, P, P, P, P, None, 0, P, None, None) == -4                 # N % 8
+    q = lib.tp_fp8_quantize
+    assert q(4, 4, 0, P, 0, P, P, None, 0, None) == -5
+    assert q(4, 4, 2, P, 0, P, P, P, 1 << 20, None) == -1
+
+
 def test_qkv_bwd_validation(lib):
     b = lib.tp_qkv_shard_bwd
     assert b(2, 0, 2, 32, 64, 4, 0, P, P, P, P, P, P, None, 0, None) == -5
