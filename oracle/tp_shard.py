@@ -53,13 +53,13 @@ Readings where the pages are silent (numbered as in the design notes):
                    Combine = Σ_j gate_j · expert output, j in the token's top-k order; it is linear,
                    so a rank may combine its fc2 partials before the all-reduce ([Arch] §4: route ->
                    dispatch (permute) -> experts -> combine (unpermute)).
-  R15 FP8 = the OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
-                   infinities; S.1111.111 is NaN; largest finite 448, smallest subnormal 2^-9).
-                   Quantisation with one scale per tensor: s = 448 / amax (fp32), the code of x is
-                   the E4M3 value nearest to fp32(x·s), ties to the even mantissa, saturating at
-                   ±448; the tensor's descale is amax / 448 (1 when amax = 0).  The scale and the
-                   product are taken in fp32 because that is where the device makes the decision.
-                   A GEMM on codes: C = (Σ_k dec(a)·dec(b))·descale_a·descale_b.
+  R15 FP8 = the OCP 8-bit floats: E4M3 (bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN,
+                   largest 448) for weights and activations, E5M2 (bias 15, 2 mantissa bits, IEEE-like
+                   infinities and NaNs, largest 57344) for gradients.  One scale per tensor:
+                   s = vmax / amax (fp32), the code of x is the value nearest to fp32(x·s), ties to
+                   the even mantissa, saturating at ±vmax; descale = amax / vmax (1 when amax = 0).
+                   The scale and the product are taken in fp32 because that is where the device
+                   makes the decision.  A GEMM on codes: C = (Σ_k dec(a)·dec(b))·descale_a·descale_b.
   R13 sequence parallelism = LayerNorm and dropout split along the sequence ([Overview]; [Arch], the
                    table under 它能做什么): rank r owns rows [off(T,t,r), off+cnt) of the flattened
                    tokens (the sequence itself when B = 1) and its dγ, dβ are partial sums over its
@@ -480,52 +480,95 @@ def tp_moe_shard_fwd(tp_size, rank, X, route, W1_r, b1_r, W2_r):
 
 # ---- FP8 (reading R15) -------------------------------------------------------------------------
 
-def e4m3_decode(codes):
-    """Values of E4M3 codes (uint8) from the format's definition; NaN for S.1111.111."""
+def _fp8_format(fmt):
+    """(exponent bits, mantissa bits, bias, largest finite value) of an OCP 8-bit float."""
+    if fmt == "e4m3":
+        return 4, 3, 7, 448.0
+    if fmt == "e5m2":
+        return 5, 2, 15, 57344.0
+    raise ValueError(f"unknown fp8 format {fmt!r}")
+
+
+def fp8_decode(codes, fmt="e4m3"):
+    """Values of 8-bit float codes from the format's definition.  E4M3: no infinities, S.1111.111
+    is NaN.  E5M2: exponent 31 holds ±inf (mantissa 0) and NaN."""
+    eb, mb, bias, _ = _fp8_format(fmt)
     c = np.asarray(codes, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
-    e = (c >> 3) & 0xF
-    m = c & 0x7
-    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
-    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    e = (c >> mb) & ((1 << eb) - 1)
+    m = c & ((1 << mb) - 1)
+    frac = m / float(1 << mb)
+    mag = np.where(e == 0, frac * 2.0 ** (1 - bias), (1.0 + frac) * 2.0 ** (e.astype(np.float64) - bias))
+    if fmt == "e4m3":
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    else:
+        mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
     return sign * mag
 
 
-_E4M3_POS = e4m3_decode(np.arange(0x7F))          # the 127 non-negative finite values, increasing
+def e4m3_decode(codes):
+    return fp8_decode(codes, "e4m3")
 
 
-def e4m3_encode(y):
-    """Nearest E4M3 code to each value (ties to the even mantissa), saturating at ±448."""
+_FP8_POS = {f: fp8_decode(np.arange(0x80), f) for f in ("e4m3", "e5m2")}
+
+
+def fp8_encode(y, fmt="e4m3"):
+    """Nearest finite code to each value (ties to the even mantissa), saturating at ± the largest
+    finite value of the format."""
+    _, _, _, vmax = _fp8_format(fmt)
+    pos = _FP8_POS[fmt]
+    n = int(np.searchsorted(pos, vmax, side="right"))      # the finite non-negative codes: 0 .. n-1
+    fin = pos[:n]
     y = np.asarray(y, dtype=np.float64)
-    a = np.minimum(np.abs(y), 448.0)
-    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)    # first value >= a
+    a = np.minimum(np.abs(y), vmax)
+    hi = np.clip(np.searchsorted(fin, a, side="left"), 0, n - 1)    # first value >= a
     lo = np.maximum(hi - 1, 0)
-    d_hi, d_lo = _E4M3_POS[hi] - a, a - _E4M3_POS[lo]
+    d_hi, d_lo = fin[hi] - a, a - fin[lo]
     pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
-    pick = np.where(a == _E4M3_POS[hi], hi, pick)
+    pick = np.where(a == fin[hi], hi, pick)
     return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 
-def fp8_quantize(x, transpose=False):
-    """Per-tensor E4M3 quantisation (reading R15).  Returns the codes (transposed when asked: the
-    [cols, rows] copy a K-major GEMM operand needs) and the fp32 descale amax / 448."""
+def e4m3_encode(y):
+    return fp8_encode(y, "e4m3")
+
+
+def fp8_quantize(x, transpose=False, fmt="e4m3"):
+    """Per-tensor quantisation (reading R15): s = vmax / amax in fp32, codes = nearest of fp32(x·s),
+    descale = amax / vmax (1 and 1 when amax = 0); vmax = 448 (E4M3) or 57344 (E5M2).  Returns the
+    codes (transposed when asked: the [cols, rows] copy a K-major GEMM operand needs) and the fp32
+    descale."""
+    vmax = np.float32(_fp8_format(fmt)[3])
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
     if amax == 0:
         s, descale = np.float32(1), np.float32(1)
     else:
-        s = np.float32(448) / amax
-        descale = amax / np.float32(448)
-    q = e4m3_encode((x32 * s).astype(np.float32))
+        s = vmax / amax
+        descale = amax / vmax
+    q = fp8_encode((x32 * s).astype(np.float32), fmt)
     return (np.ascontiguousarray(q.T) if transpose else q), descale
 
 
-def fp8_gemm_nt(A_codes, a_descale, B_codes, b_descale, bias=None, gelu_out=False):
-    """C = (dec(A)·dec(B)ᵀ)·descale_a·descale_b (+ bias) (-> GeLU): A [M, K], B [N, K] codes."""
-    C = (e4m3_decode(A_codes) @ e4m3_decode(B_codes).T) * float(a_descale) * float(b_descale)
+FP8_EPI_NONE, FP8_EPI_GELU, FP8_EPI_GELU_TANH, FP8_EPI_DGELU, FP8_EPI_DGELU_TANH = 0, 1, 2, 3, 4
+
+
+def fp8_gemm_nt(A_codes, a_descale, B_codes, b_descale, bias=None, epi=FP8_EPI_NONE, aux=None,
+                fmt_a="e4m3", fmt_b="e4m3"):
+    """pre = (dec(A)·dec(B)ᵀ)·descale_a·descale_b (+ bias);  C = pre, GeLU(pre) (exact or tanh form),
+    or pre ∘ GeLU'(aux) (the fc1 backward's product with the activation's derivative at A1 = aux).
+    A [M, K] and B [N, K] codes in their formats."""
+    pre = (fp8_decode(A_codes, fmt_a) @ fp8_decode(B_codes, fmt_b).T) * float(a_descale) * float(b_descale)
     if bias is not None:
-        C = C + bias
-    return {"pre": C, "C": gelu(C) if gelu_out else C}
+        pre = pre + bias
+    if epi == FP8_EPI_NONE:
+        C = pre
+    elif epi in (FP8_EPI_GELU, FP8_EPI_GELU_TANH):
+        C = _activation(epi - 1)[0](pre)
+    else:
+        C = pre * _activation(epi - 3)[1](np.asarray(aux, dtype=np.float64))
+    return {"pre": pre, "C": C}
 
 
 def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W2_r):

@@ -628,7 +628,7 @@ def pin_fp8():
     B[(B & 0x7F) == 0x7F] = 0xB8
     bias = g.standard_normal(4)
     da, db = np.float32(0.25), np.float32(3.0)
-    r = T.fp8_gemm_nt(A, da, B, db, bias, gelu_out=True)
+    r = T.fp8_gemm_nt(A, da, B, db, bias, epi=T.FP8_EPI_GELU)
     dA, dB = T.e4m3_decode(A).tolist(), T.e4m3_decode(B).tolist()
     for i in range(5):
         for j in range(4):
@@ -638,6 +638,40 @@ def pin_fp8():
             pre = acc * 0.25 * 3.0 + bias[j]
             assert abs(r["pre"][i, j] - pre) <= 1e-12 * max(1.0, abs(pre))
             assert abs(r["C"][i, j] - bf.gelu(pre)) <= 1e-12 * max(1.0, abs(pre))
+    # E5M2 (gradients): anchors, every finite code against torch's float8_e5m2, round trip, ties,
+    # saturation; a mixed-format GEMM with the GeLU' epilogue against scalar loops
+    d5 = T.fp8_decode(np.arange(256), "e5m2")
+    for code, val in ((0x3C, 1.0), (0x7B, 57344.0), (0x01, 2.0 ** -16), (0x04, 2.0 ** -14), (0xBC, -1.0)):
+        assert d5[code] == val, f"e5m2 decode 0x{code:02x} = {d5[code]}"
+    assert d5[0x7C] == np.inf and d5[0xFC] == -np.inf and np.isnan(d5[0x7D]) and np.isnan(d5[0xFF])
+    t5 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).float().numpy().astype(np.float64)
+    fin5 = np.isfinite(t5)
+    assert np.array_equal(d5[fin5], t5[fin5]) and np.array_equal(np.isfinite(d5), fin5), "e5m2 decode vs torch"
+    c5 = np.arange(256)[fin5]
+    assert np.array_equal(T.fp8_encode(d5[c5], "e5m2"), c5.astype(np.uint8)), "e5m2 encode(decode(c)) = c"
+    pos5 = np.sort(d5[np.arange(256) < 0x7C])
+    mid5 = (pos5[1:] + pos5[:-1]) / 2
+    got5 = T.fp8_encode(mid5, "e5m2")
+    assert np.array_equal(got5, torch.from_numpy(mid5.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy())
+    assert (got5 % 2 == 0).all(), "e5m2 midpoints to the even code"
+    x5 = (g.standard_normal(20000) * 3000).astype(np.float32).clip(-57344, 57344)
+    assert np.array_equal(T.fp8_encode(x5, "e5m2"),
+                          torch.from_numpy(x5).to(torch.float8_e5m2).view(torch.uint8).numpy())
+    assert list(T.fp8_encode([60000.0, -1e9], "e5m2")) == [0x7B, 0xFB], "e5m2 saturation"
+    q5, ds5 = T.fp8_quantize(X, fmt="e5m2")
+    assert q5[3, 2] == 0xFB and abs(float(ds5) - float(np.abs(X).max()) / 57344) <= 1e-7 * float(np.abs(X).max())
+    A5 = g.integers(0, 256, (4, 6)).astype(np.uint8)
+    A5[(A5 & 0x7F) >= 0x7C] = 0x3C                    # finite E5M2 codes only
+    B4 = g.integers(0, 256, (3, 6)).astype(np.uint8)
+    B4[(B4 & 0x7F) == 0x7F] = 0x38
+    aux = g.standard_normal((4, 3))
+    r = T.fp8_gemm_nt(A5, np.float32(0.5), B4, np.float32(2.0), epi=T.FP8_EPI_DGELU, aux=aux,
+                      fmt_a="e5m2", fmt_b="e4m3")
+    dA, dB = T.fp8_decode(A5, "e5m2").tolist(), T.fp8_decode(B4, "e4m3").tolist()
+    for i in range(4):
+        for j in range(3):
+            pre = sum(dA[i][k] * dB[j][k] for k in range(6)) * 0.5 * 2.0
+            assert abs(r["C"][i, j] - pre * bf.gelu_prime(aux[i, j])) <= 1e-12 * max(1.0, abs(pre))
 
 
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,

@@ -79,7 +79,7 @@ def test_fp8_gemm(M, N, K, epi):
     tda, tdb = torch.tensor([da], device="cuda"), torch.tensor([db], device="cuda")
     bd.tp_fp8_gemm_nt(tA, tda, tB, tdb, C, bias=dev(bias), gelu=epi, C_pre=Cp)
     torch.cuda.synchronize()
-    ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64, gelu_out=epi)
+    ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64, epi=oracle.FP8_EPI_GELU if epi else oracle.FP8_EPI_NONE)
     assert_close(C, ref["C"], "bf16", "C")
     if epi:
         assert_close(Cp, ref["pre"], "bf16", "C_pre")

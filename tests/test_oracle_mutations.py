@@ -208,27 +208,39 @@ def _combine_first_choice_only(Z_rows, gates, token_row):
 _ORIG_ROUTE = T.moe_route
 
 
-def _e4m3_decode_bias8(codes):
-    return _ORIG_DECODE(codes) / 2.0
+def _fp8_decode_bias8(codes, fmt="e4m3"):
+    v = _ORIG_DECODE(codes, fmt)
+    return v / 2.0 if fmt == "e4m3" else v
 
 
-def _e4m3_encode_ties_up(y):
+def _fp8_encode_ties_up(y, fmt="e4m3"):
+    vmax = T._fp8_format(fmt)[3]
+    pos = T._FP8_POS[fmt]
+    fin = pos[:int(np.searchsorted(pos, vmax, side="right"))]
     y = np.asarray(y, dtype=np.float64)
-    pos = T._E4M3_POS
-    a = np.minimum(np.abs(y), 448.0)
-    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 126)
+    a = np.minimum(np.abs(y), vmax)
+    hi = np.clip(np.searchsorted(fin, a, side="left"), 0, len(fin) - 1)
     lo = np.maximum(hi - 1, 0)
-    pick = np.where(pos[hi] - a <= a - pos[lo], hi, lo)
+    pick = np.where(fin[hi] - a <= a - fin[lo], hi, lo)
     return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 
-def _fp8_quantize_descale_inverted(x, transpose=False):
-    q, d = _ORIG_QUANT(x, transpose)
+def _fp8_quantize_descale_inverted(x, transpose=False, fmt="e4m3"):
+    q, d = _ORIG_QUANT(x, transpose, fmt)
     return q, np.float32(1) / d
 
 
-_ORIG_DECODE = T.e4m3_decode
+def _fp8_gemm_dgelu_uses_gelu(A_codes, a_descale, B_codes, b_descale, bias=None, epi=0, aux=None, fmt_a="e4m3",
+                              fmt_b="e4m3"):
+    r = _ORIG_GEMM(A_codes, a_descale, B_codes, b_descale, bias, epi, aux, fmt_a, fmt_b)
+    if epi == T.FP8_EPI_DGELU:
+        r["C"] = r["pre"] * T.gelu(np.asarray(aux))
+    return r
+
+
+_ORIG_DECODE = T.fp8_decode
 _ORIG_QUANT = T.fp8_quantize
+_ORIG_GEMM = T.fp8_gemm_nt
 
 
 def _gelu_tanh_cubic_dropped(x):
@@ -273,9 +285,10 @@ MUTANTS = {
     "moe_gates_renormalised": {"moe_route": _route_variant(renorm=True)},
     "moe_rows_in_token_order": {"moe_route": _route_variant(by_token=True)},
     "moe_combine_first_choice_only": {"moe_combine": _combine_first_choice_only},
-    "e4m3_exponent_bias_8": {"e4m3_decode": _e4m3_decode_bias8},
-    "e4m3_ties_away": {"e4m3_encode": _e4m3_encode_ties_up},
+    "e4m3_exponent_bias_8": {"fp8_decode": _fp8_decode_bias8},
+    "fp8_ties_away": {"fp8_encode": _fp8_encode_ties_up},
     "fp8_descale_inverted": {"fp8_quantize": _fp8_quantize_descale_inverted},
+    "fp8_dgelu_uses_gelu": {"fp8_gemm_nt": _fp8_gemm_dgelu_uses_gelu},
     "gelu_tanh_cubic_dropped": {"gelu_tanh": _gelu_tanh_cubic_dropped},
 }
 
