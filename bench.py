@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--no-attn-out", action="store_true",
                     help="skip the attention output-projection measurement")
     ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 MLP-forward measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 MLP measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB fp32 negation (the copy the counters are "
                          "calibrated on), then --warmup + --steps steps, and nothing else")
@@ -259,10 +259,14 @@ PEAK_FP8_TFLOPS = 5033.2   # dense E4M3 MFMA: twice the bf16 rate
 
 
 def fp8_mlp(bd, torch, wl, steps, warmup):
-    """The MLP shard's two forward GEMMs in FP8 (E4M3 codes, one scale per tensor) on the GPT-3
-    rank-0 shapes: X·W1 (2048 x 6144 x 12288) with bias + GeLU and Y·W2 (2048 x 12288 x 6144), both
-    with K-major code operands; the quantisation of X and Y (per call) and of the weights (once,
-    transposed) is timed apart.  A precision variant beside the bf16 step, against the FP8 peak."""
+    """The MLP shard in FP8 on the GPT-3 rank-0 shapes (T 2048, H 12288, F_r 6144), forward and
+    backward timed apart.  Forward: quantise X (E4M3), X·W1 (2048 x 6144 x 12288) with bias + GeLU
+    (A1 kept), quantise Y, Y·W2 (2048 x 12288 x 6144).  Backward: dZ in E5M2 (plain and the
+    transposed copy), dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1), dW2 = Yᵀ·dZ, dA1 in E5M2 (both copies),
+    dX = dA1·W1ᵀ, dW1 = Xᵀ·dA1, db1 = Σ_t dA1; the K-major copies of X and Y the weight gradients
+    take are quantised inside the backward.  Weights are quantised once, outside the timed region
+    (both copies; they change once per optimizer step).  A precision variant beside the bf16 step,
+    against the FP8 peak."""
     T, H = wl.T, wl.H
     _, Fr = bd.tp_shard_range(wl.F, wl.tp_size, 0)
     g = torch.Generator(device="cuda")
@@ -270,51 +274,76 @@ def fp8_mlp(bd, torch, wl, steps, warmup):
     bf = torch.bfloat16
     r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device="cuda") * std).to(bf)  # noqa: E731
     X, W1, b1, W2 = r(T, H), r(H, Fr, std=wl.w_std), r(Fr, std=wl.w_std), r(Fr, H, std=wl.w_std)
+    dZ = r(T, H, std=1e-3)
     u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device="cuda")  # noqa: E731
-    qX, qW1t, qW2t, qY = u8(T, H), u8(Fr, H), u8(H, Fr), u8(T, Fr)
-    dX, dW1, dW2, dY = (torch.empty(1, device="cuda") for _ in range(4))
-    Y, Z = torch.empty(T, Fr, dtype=bf, device="cuda"), torch.empty(T, H, dtype=bf, device="cuda")
+    qX, qXt, qW1t, qW1, qW2t, qW2, qY, qYt = u8(T, H), u8(H, T), u8(Fr, H), u8(H, Fr), u8(H, Fr), u8(Fr, H), \
+        u8(T, Fr), u8(Fr, T)
+    qdZ, qdZt, qdA1, qdA1t = u8(T, H), u8(H, T), u8(T, Fr), u8(Fr, T)
+    sX, sW1, sW2, sY, sdZ, sdA1 = (torch.empty(1, device="cuda") for _ in range(6))
+    e = lambda *sh: torch.empty(*sh, dtype=bf, device="cuda")  # noqa: E731
+    A1, Y, Z = e(T, Fr), e(T, Fr), e(T, H)
+    dA1, dW2, dX, dW1, db1 = e(T, Fr), e(Fr, H), e(T, H), e(H, Fr), e(Fr)
     ws = bd.workspace("tp_fp8_quantize", 1, 0, 1, 1, 1, 1, 1, bf)
-    bd.tp_fp8_quantize(W1, qW1t, dW1, ws, transpose=True)
-    bd.tp_fp8_quantize(W2, qW2t, dW2, ws, transpose=True)
+    wsb = bd.workspace("tp_bias_grad", 1, 0, T, 1, Fr, 1, 1, bf)
+    e4, e5 = bd.TP_FP8_E4M3, bd.TP_FP8_E5M2
+    bd.tp_fp8_quantize(W1, qW1t, sW1, ws, transpose=True)
+    bd.tp_fp8_quantize(W1, qW1, sW1, ws)
+    bd.tp_fp8_quantize(W2, qW2t, sW2, ws, transpose=True)
+    bd.tp_fp8_quantize(W2, qW2, sW2, ws)
 
-    def call():
-        bd.tp_fp8_quantize(X, qX, dX, ws)
-        bd.tp_fp8_gemm_nt(qX, dX, qW1t, dW1, Y, bias=b1, gelu=True)
-        bd.tp_fp8_quantize(Y, qY, dY, ws)
-        bd.tp_fp8_gemm_nt(qY, dY, qW2t, dW2, Z)
-    for _ in range(warmup):
-        call()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps):
-        call()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    bd.tp_prof_collect()
-    bd.tp_prof_enable(True)
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    bd.tp_prof_enable(False)
-    k = bd.tp_prof_collect()
-    flop = 2 * 2.0 * T * H * Fr
-    kernels = {}
-    for tag, (n, kms, fl, by) in k.items():
-        us = 1e3 * kms / n
-        e = {"launches_per_step": n / steps, "avg_launch_us": round(us, 2)}
-        if tag.startswith("gemm_fp8"):
-            tf = fl / n / us / 1e6
-            e.update(tflops=round(tf, 1), frac_of_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
-        else:
-            e.update(gb_per_s=round(by / n / us / 1e3, 1))
-        kernels[tag] = e
-    res = {"workload": "gpt3_175b_tp8_rank0_mlp_fwd_fp8_e4m3", "ms": round(ms, 4),
-           "tflops": round(flop / ms / 1e9, 1), "pct_of_fp8_peak": round(100 * flop / ms / 1e9 / PEAK_FP8_TFLOPS, 2),
-           "kernels": kernels}
-    del X, W1, W2, qX, qW1t, qW2t, qY, Y, Z
+    def fwd():
+        bd.tp_fp8_quantize(X, qX, sX, ws)
+        bd.tp_fp8_gemm_nt(qX, sX, qW1t, sW1, Y, bias=b1, epilogue=bd.TP_FP8_EPI_GELU, C_pre=A1)
+        bd.tp_fp8_quantize(Y, qY, sY, ws)
+        bd.tp_fp8_gemm_nt(qY, sY, qW2t, sW2, Z)
+
+    def bwd():
+        bd.tp_fp8_quantize(dZ, qdZ, sdZ, ws, fmt=e5)
+        bd.tp_fp8_quantize(dZ, qdZt, sdZ, ws, transpose=True, fmt=e5)
+        bd.tp_fp8_gemm_nt(qdZ, sdZ, qW2, sW2, dA1, epilogue=bd.TP_FP8_EPI_DGELU, aux=A1, a_fmt=e5, b_fmt=e4)
+        bd.tp_fp8_quantize(Y, qYt, sY, ws, transpose=True)
+        bd.tp_fp8_gemm_nt(qYt, sY, qdZt, sdZ, dW2, a_fmt=e4, b_fmt=e5)
+        bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, fmt=e5)
+        bd.tp_fp8_quantize(dA1, qdA1t, sdA1, ws, transpose=True, fmt=e5)
+        bd.tp_fp8_gemm_nt(qdA1, sdA1, qW1, sW1, dX, a_fmt=e5, b_fmt=e4)
+        bd.tp_fp8_quantize(X, qXt, sX, ws, transpose=True)
+        bd.tp_fp8_gemm_nt(qXt, sX, qdA1t, sdA1, dW1, a_fmt=e4, b_fmt=e5)
+        bd.tp_bias_grad(dA1, db1, wsb)
+
+    def timed(call, flop):
+        for _ in range(warmup):
+            call()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        bd.tp_prof_collect()
+        bd.tp_prof_enable(True)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        bd.tp_prof_enable(False)
+        kernels = {}
+        for tag, (n, kms, fl, by) in bd.tp_prof_collect().items():
+            us = 1e3 * kms / n
+            k = {"launches_per_step": n / steps, "avg_launch_us": round(us, 2)}
+            if tag.startswith("gemm_fp8"):
+                tf = fl / n / us / 1e6
+                k.update(tflops=round(tf, 1), frac_of_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+            else:
+                k.update(gb_per_s=round(by / n / us / 1e3, 1))
+            kernels[tag] = k
+        return {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                "pct_of_fp8_peak": round(100 * flop / ms / 1e9 / PEAK_FP8_TFLOPS, 2), "kernels": kernels}
+
+    fwd()
+    res = {"workload": "gpt3_175b_tp8_rank0_mlp_fp8_e4m3_fwd_e5m2_grads",
+           "fwd": timed(fwd, 2 * 2.0 * T * H * Fr), "bwd": timed(bwd, 4 * 2.0 * T * H * Fr)}
+    del X, W1, W2, dZ, qX, qXt, qW1t, qW1, qW2t, qW2, qY, qYt, qdZ, qdZt, qdA1, qdA1t, A1, Y, Z, dA1, dW2, dX, dW1
     torch.cuda.empty_cache()
     return res
 
@@ -595,7 +624,7 @@ def main():
         "moe_layer_shard": moe_l,
         "attn_out_proj_shard": oproj,
         "residual_layernorm": ln,
-        "fp8_mlp_fwd": f8,
+        "fp8_mlp": f8,
         # the step plus the attention output projection: the whole Megatron layer shard's GEMMs
         "tflops_layer_with_out_proj": round((flop_step + oproj_flop) / ((ms_step + oproj["ms"]) * 1e-3) / 1e12, 2)
         if oproj else None,

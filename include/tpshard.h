@@ -241,31 +241,51 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
                      const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
                      void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream);
 
-/* FP8 (OCP E4M3: 1 sign, 4 exponent bits, bias 7, 3 mantissa bits, max 448): forward and backward
- * GEMMs in FP8 beside FP32 master weights ("Megatron-LM技术演进与大规模模型训练实践", §2.3); FP8 among
- * the mixed precisions of the stack ("NVIDIA Megatron-LM：大规模Transformer模型分布式训练框架", the
- * §技术栈; "Megatron-LM — 架构与原理", capability table).  Per-tensor
- * quantisation of x [rows, cols] (bf16 or fp32):
- *   amax = max |x|;  s = 448 / amax and descale = amax / 448 in fp32 (1 and 1 when amax = 0)
- *   q = E4M3(fp32(x·s)), nearest with ties to the even mantissa, saturating at ±448
- * transpose != 0 writes the codes transposed, [cols, rows] (the K-major copy of a weight [in, out]
- * that tp_fp8_gemm_nt takes as B).  descale: one fp32 in device memory (written).  x must be finite.
- * workspace: tp_workspace_bytes("tp_fp8_quantize", ...) bytes. */
-int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose, unsigned char* q, float* descale,
-                    void* workspace, size_t workspace_bytes, void* stream);
+/* FP8: the OCP 8-bit floats E4M3 (1 sign, 4 exponent bits, bias 7, 3 mantissa bits, max 448) for
+ * weights and activations and E5M2 (5 exponent bits, bias 15, 2 mantissa bits, max 57344) for
+ * gradients.  Forward and backward GEMMs in FP8 beside FP32 master weights
+ * ("Megatron-LM技术演进与大规模模型训练实践", §2.3); FP8 among the stack's mixed precisions ("NVIDIA
+ * Megatron-LM：大规模Transformer模型分布式训练框架", §技术栈; "Megatron-LM — 架构与原理", capability
+ * table). */
+typedef enum { TP_FP8_E4M3 = 0, TP_FP8_E5M2 = 1 } tp_fp8_format;
+typedef enum {
+  TP_FP8_EPI_NONE = 0,        /* C = pre                                     */
+  TP_FP8_EPI_GELU = 1,        /* C = GeLU(pre), C_pre = pre (nullable)       */
+  TP_FP8_EPI_GELU_TANH = 2,   /* C = tanh-form GeLU(pre), C_pre = pre        */
+  TP_FP8_EPI_DGELU = 3,       /* C = pre ∘ GeLU'(aux)   (fc1's backward)     */
+  TP_FP8_EPI_DGELU_TANH = 4   /* C = pre ∘ tanh-form GeLU'(aux)              */
+} tp_fp8_epilogue;
 
-/* GEMM on E4M3 codes, both operands K-major:
- *   pre = (A·Bᵀ)·a_descale·b_descale (+ bias[n]),  A [M, K] codes, B [N, K] codes, fp32 accumulation
- *   C = pre (gelu == 0) or GeLU(pre) with C_pre = pre when C_pre != NULL (gelu 1: the exact GeLU,
- *   gelu 2: its tanh form; TP_EINVAL for another value)
- * C, C_pre, bias bf16; descales fp32 scalars in device memory (as tp_fp8_quantize writes them).
- * Requires K % 16 == 0, N % 8 == 0, operands below 2 GiB (TP_EUNSUPPORTED otherwise). */
-int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_descale, const unsigned char* B,
-                   const float* b_descale, const void* bias, int gelu, void* C, void* C_pre, void* stream);
+/* Per-tensor quantisation of x [rows, cols] (bf16 or fp32) to `format`:
+ *   amax = max |x|;  s = vmax / amax and descale = amax / vmax in fp32 (1 and 1 when amax = 0)
+ *   q = nearest code of fp32(x·s), ties to the even mantissa, saturating at ±vmax
+ * vmax = 448 (E4M3) or 57344 (E5M2).  transpose != 0 writes the codes transposed, [cols, rows] (the
+ * K-major copy tp_fp8_gemm_nt takes).  descale: one fp32 in device memory (written).  x must be
+ * finite.  workspace: tp_workspace_bytes("tp_fp8_quantize", ...) bytes. */
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, int transpose, unsigned char* q,
+                    float* descale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* GEMM on 8-bit codes, both operands K-major:
+ *   pre = (A·Bᵀ)·a_descale·b_descale (+ bias[n]),  A [M, K], B [N, K] codes in their formats
+ *   C per `epilogue` (tp_fp8_epilogue); aux [M, N] bf16 for the GeLU' epilogues
+ * C, C_pre, aux, bias bf16; descales fp32 scalars in device memory (as tp_fp8_quantize writes them);
+ * fp32 accumulation.  Requires K % 16 == 0, N % 8 == 0, operands below 2 GiB, not both operands
+ * E5M2 (TP_EUNSUPPORTED otherwise). */
+int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int a_format, const float* a_descale,
+                   const unsigned char* B, int b_format, const float* b_descale, const void* bias, int epilogue,
+                   const void* aux, void* C, void* C_pre, void* stream);
+
+/* Bias gradient of a linear layer: db[c] = Σ_{r < rows} dy[r, c], dy [rows, cols] row-major and db
+ * [cols] in dtype, fp32 accumulation in a fixed order (repeatable bit for bit).  The backward
+ * composed from the FP8 entry points takes db1 = Σ_t dA1 from it (the chain rule of the linear layer
+ * Y = X·W + b of "Megatron-LM技术演进与大规模模型训练实践", §2.1).  workspace: tp_workspace_bytes("tp_bias_grad", ...) with B·S = rows
+ * and H = cols. */
+int tp_bias_grad(int rows, int cols, int dtype, const void* dy, void* db, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
  * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd",
- * "tp_moe_route", "tp_moe_shard_fwd", "tp_fp8_quantize"; 0 for the others).  T = B*S; F is used by the
+ * "tp_moe_route", "tp_moe_shard_fwd", "tp_fp8_quantize", "tp_bias_grad"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

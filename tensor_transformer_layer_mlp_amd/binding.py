@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 
 TP_BF16, TP_F32 = 0, 1
 TP_GELU, TP_GELU_TANH = 0, 1
+TP_FP8_E4M3, TP_FP8_E5M2 = 0, 1
+TP_FP8_EPI_NONE, TP_FP8_EPI_GELU, TP_FP8_EPI_GELU_TANH, TP_FP8_EPI_DGELU, TP_FP8_EPI_DGELU_TANH = 0, 1, 2, 3, 4
 STATUS = {0: "TP_OK", -1: "TP_EINVAL", -2: "TP_ENULL", -3: "TP_EALIGN", -4: "TP_EUNSUPPORTED",
           -5: "TP_EWORKSPACE", -6: "TP_EHIP"}
 
@@ -36,8 +38,9 @@ _SIGNATURES = {
     "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P, _Z, _P]),
-    "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _P, _P, _P, _Z, _P]),
-    "tp_fp8_gemm_nt": (_I, [_I, _I, _I] + [_P] * 5 + [_I, _P, _P, _P]),
+    "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _I, _P, _P, _P, _Z, _P]),
+    "tp_fp8_gemm_nt": (_I, [_I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
+    "tp_bias_grad": (_I, [_I, _I, _I, _P, _P, _P, _Z, _P]),
     "tp_moe_shard_fwd": (_I, [_I] * 8 + [_P] * 12 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -369,13 +372,13 @@ def tp_moe_shard_fwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, ga
     _check(rc, "tp_moe_shard_fwd")
 
 
-def tp_fp8_quantize(x, q, descale, workspace, transpose=False, stream=None):
-    """E4M3 codes of a 2-D tensor x with one scale (q: uint8 [rows, cols], or [cols, rows] when
-    transpose), and its fp32 descale (a one-element device tensor)."""
+def tp_fp8_quantize(x, q, descale, workspace, transpose=False, fmt=TP_FP8_E4M3, stream=None):
+    """8-bit codes of a 2-D tensor x with one scale (q: uint8 [rows, cols], or [cols, rows] when
+    transpose), and its fp32 descale (a one-element device tensor).  fmt: TP_FP8_E4M3 / TP_FP8_E5M2."""
     rows, cols = x.shape
     _need(q, rows * cols, "q")
     _need(descale, 1, "descale")
-    rc = raw().tp_fp8_quantize(rows, cols, _dtype_code(x), _ptr(x, "x"), 1 if transpose else 0,
+    rc = raw().tp_fp8_quantize(rows, cols, _dtype_code(x), _ptr(x, "x"), fmt, 1 if transpose else 0,
                                _ptr(q, "q", torch.uint8), _ptr(descale, "descale", torch.float32),
                                _ptr(workspace, "workspace", None, True),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
@@ -383,21 +386,33 @@ def tp_fp8_quantize(x, q, descale, workspace, transpose=False, stream=None):
     _check(rc, "tp_fp8_quantize")
 
 
-def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, gelu=False, C_pre=None, stream=None):
-    """C [M, N] bf16 = (A·Bᵀ)·descales (+ bias) (-> GeLU) for E4M3 codes A [M, K], B [N, K].
-    gelu: False / 0 none, True / 1 the exact GeLU, 2 its tanh form."""
+def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, epilogue=TP_FP8_EPI_NONE, aux=None, C_pre=None,
+                   a_fmt=TP_FP8_E4M3, b_fmt=TP_FP8_E4M3, stream=None):
+    """C [M, N] bf16 = (A·Bᵀ)·descales (+ bias), then the epilogue, for 8-bit codes A [M, K], B [N, K]."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K:
         raise ValueError(f"B has {B.shape[1]} columns, A has {K}")
-    for t, k, name in ((C, M * N, "C"), (bias, N, "bias"), (C_pre, M * N, "C_pre"), (a_descale, 1, "a_descale"),
-                       (b_descale, 1, "b_descale")):
+    for t, k, name in ((C, M * N, "C"), (bias, N, "bias"), (C_pre, M * N, "C_pre"), (aux, M * N, "aux"),
+                       (a_descale, 1, "a_descale"), (b_descale, 1, "b_descale")):
         _need(t, k, name)
-    rc = raw().tp_fp8_gemm_nt(M, N, K, _ptr(A, "A", torch.uint8), _ptr(a_descale, "a_descale", torch.float32),
-                              _ptr(B, "B", torch.uint8), _ptr(b_descale, "b_descale", torch.float32),
-                              _ptr(bias, "bias", torch.bfloat16, True), int(gelu),
-                              _ptr(C, "C", torch.bfloat16), _ptr(C_pre, "C_pre", torch.bfloat16, True), _stream(stream))
+    rc = raw().tp_fp8_gemm_nt(M, N, K, _ptr(A, "A", torch.uint8), a_fmt, _ptr(a_descale, "a_descale", torch.float32),
+                              _ptr(B, "B", torch.uint8), b_fmt, _ptr(b_descale, "b_descale", torch.float32),
+                              _ptr(bias, "bias", torch.bfloat16, True), int(epilogue),
+                              _ptr(aux, "aux", torch.bfloat16, True), _ptr(C, "C", torch.bfloat16),
+                              _ptr(C_pre, "C_pre", torch.bfloat16, True), _stream(stream))
     _check(rc, "tp_fp8_gemm_nt")
+
+
+def tp_bias_grad(dy, db, workspace, stream=None):
+    """db [cols] = Σ over the rows of dy [rows, cols] (fixed-order fp32 sum, in dy's dtype)."""
+    rows, cols = dy.shape
+    _need(db, cols, "db")
+    rc = raw().tp_bias_grad(rows, cols, _dtype_code(dy), _ptr(dy, "dy"), _ptr(db, "db", dy.dtype),
+                            _ptr(workspace, "workspace", None, True),
+                            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                            _stream(stream))
+    _check(rc, "tp_bias_grad")
 
 
 def workspace(fn, tp_size, rank, B, S, H, n_heads, F, dtype, device="cuda"):

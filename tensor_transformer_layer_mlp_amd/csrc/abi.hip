@@ -555,9 +555,10 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   return TP_OK;
 }
 
-int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose, unsigned char* q, float* descale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, int transpose, unsigned char* q,
+                    float* descale, void* workspace, size_t workspace_bytes, void* stream) {
   TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
+  TP_CHECK(format == TP_FP8_E4M3 || format == TP_FP8_E5M2, TP_EINVAL, "format %d is neither E4M3 nor E5M2", format);
   TP_CHECK(rows >= 0 && cols >= 0, TP_EINVAL, "negative size %d x %d", rows, cols);
   const long n = (long)rows * cols;
   NEED(x, "x", n); NEED(q, "q", n); NEED4(descale, "descale", 1);
@@ -565,22 +566,42 @@ int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int transpose,
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  TP_TRY(launch_fp8_quantize(dtype, rows, cols, x, transpose != 0, q, descale, (float*)workspace, (hipStream_t)stream),
-         "fp8 quantize");
+  TP_TRY(launch_fp8_quantize(dtype, format, rows, cols, x, transpose != 0, q, descale, (float*)workspace,
+                             (hipStream_t)stream), "fp8 quantize");
   return TP_OK;
 }
 
-int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* a_descale, const unsigned char* B,
-                   const float* b_descale, const void* bias, int gelu, void* C, void* C_pre, void* stream) {
+int tp_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int a_format, const float* a_descale,
+                   const unsigned char* B, int b_format, const float* b_descale, const void* bias, int epilogue,
+                   const void* aux, void* C, void* C_pre, void* stream) {
   TP_CHECK(M >= 0 && N >= 0 && K >= 0, TP_EINVAL, "negative size %d x %d x %d", M, N, K);
+  TP_CHECK((a_format == TP_FP8_E4M3 || a_format == TP_FP8_E5M2) && (b_format == TP_FP8_E4M3 || b_format == TP_FP8_E5M2),
+           TP_EINVAL, "formats %d, %d are not E4M3 / E5M2", a_format, b_format);
+  TP_CHECK(!(a_format == TP_FP8_E5M2 && b_format == TP_FP8_E5M2), TP_EUNSUPPORTED, "two E5M2 operands");
+  TP_CHECK(epilogue >= TP_FP8_EPI_NONE && epilogue <= TP_FP8_EPI_DGELU_TANH, TP_EINVAL, "epilogue %d unknown", epilogue);
   TP_CHECK(K % 16 == 0, TP_EUNSUPPORTED, "K %d is not a multiple of 16 (rows of 16-byte pieces)", K);
   TP_CHECK(N % 8 == 0, TP_EUNSUPPORTED, "N %d is not a multiple of 8", N);
   TP_CHECK((long)M * K < 0x7fffffffL && (long)N * K < 0x7fffffffL, TP_EUNSUPPORTED, "an operand above 2 GiB");
   NEED(A, "A", (long)M * K); NEED(B, "B", (long)N * K); NEED4(a_descale, "a_descale", 1);
   NEED4(b_descale, "b_descale", 1); NEED(C, "C", (long)M * N); MAYBE(bias, "bias"); MAYBE(C_pre, "C_pre");
-  TP_CHECK(gelu >= 0 && gelu <= 2, TP_EINVAL, "gelu %d is not 0 (none), 1 (exact) or 2 (tanh form)", gelu);
-  TP_TRY(launch_fp8_gemm_nt(M, N, K, A, a_descale, B, b_descale, bias, gelu, C, gelu ? C_pre : nullptr,
-                            (hipStream_t)stream), "fp8 gemm");
+  const bool dg = epilogue == TP_FP8_EPI_DGELU || epilogue == TP_FP8_EPI_DGELU_TANH;
+  if (dg) NEED(aux, "aux", (long)M * N); else MAYBE(aux, "aux");
+  const bool g = epilogue == TP_FP8_EPI_GELU || epilogue == TP_FP8_EPI_GELU_TANH;
+  TP_TRY(launch_fp8_gemm_nt(M, N, K, A, a_format, a_descale, B, b_format, b_descale, bias, epilogue,
+                            dg ? aux : nullptr, C, g ? C_pre : nullptr, (hipStream_t)stream), "fp8 gemm");
+  return TP_OK;
+}
+
+int tp_bias_grad(int rows, int cols, int dtype, const void* dy, void* db, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
+  TP_CHECK(rows >= 0 && cols >= 0, TP_EINVAL, "negative size %d x %d", rows, cols);
+  NEED(dy, "dy", (long)rows * cols); NEED(db, "db", cols);
+  const size_t need = align256(colsum_ws_bytes(rows, cols));
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_colsum(dtype, dy, cols, rows, cols, (float*)workspace, db, (hipStream_t)stream), "bias grad");
   return TP_OK;
 }
 
@@ -599,6 +620,10 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
     return qkv_bwd_ws(g.T, g.Nq);
   }
   if (strcmp(fn, "tp_fp8_quantize") == 0) return align256(fp8_quantize_ws_bytes());
+  if (strcmp(fn, "tp_bias_grad") == 0) {
+    if (B < 0 || S < 0 || H < 0 || (long)B * S > INT_MAX / 4) return 0;
+    return align256(colsum_ws_bytes(B * S, H));
+  }
   if (strcmp(fn, "tp_moe_route") == 0) {
     if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > moe_max_experts()) return 0;
     return align256(moe_route_ws_bytes(B * S, n_heads));

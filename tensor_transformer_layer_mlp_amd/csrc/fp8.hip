@@ -1,14 +1,16 @@
-// FP8 (OCP E4M3) path: per-tensor quantisation and a GEMM on E4M3 codes for gfx950.
+// FP8 path (OCP E4M3 for weights and activations, E5M2 for gradients): per-tensor quantisation and a
+// GEMM on 8-bit codes for gfx950.
 //
 // Quantisation: amax = max |x| (per-workgroup maxima, then one workgroup: max is order-free, so the
-// result is exact and deterministic), s = 448 / amax and descale = amax / 448 in fp32 (1 and 1 for
-// an all-zero tensor), codes = E4M3(fp32(x·s)) rounded to nearest, ties to the even mantissa,
-// saturating at ±448, by exact bit arithmetic on the fp32 value (no conversion instruction, so the
-// rounding is the one stated).  The transposed form writes the [cols, rows] copy a GEMM operand
+// result is exact and deterministic), s = vmax / amax and descale = amax / vmax in fp32 (vmax = 448
+// or 57344; 1 and 1 for an all-zero tensor), codes = nearest code of fp32(x·s), ties to the even
+// mantissa, saturating at ±vmax, by exact bit arithmetic on the fp32 value (no conversion
+// instruction, so the rounding is the one stated).  The transposed form writes the [cols, rows] copy a GEMM operand
 // needs K-major, through 64 x 64 LDS tiles so both the reads and the writes are whole rows.
 //
-// GEMM: C[M, N] = (A·Bᵀ)·descale_a·descale_b (+ bias) (-> GeLU), A [M, K] and B [N, K] codes, both
-// K-major; bf16 out, fp32 accumulation.  v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales:
+// GEMM: C[M, N] = (A·Bᵀ)·descale_a·descale_b (+ bias) (-> GeLU, or ∘ GeLU'(aux)), A [M, K] and
+// B [N, K] codes, each E4M3 or E5M2, both K-major; bf16 out, fp32 accumulation.  The operand formats
+// are the instruction's format selectors.  v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales:
 // lane l holds row (l % 16) of its 16-row operand block and the 32 bytes k = 32·(l / 16) .. +31 (the
 // instruction pairs byte b of A's lane-group g with byte b of B's lane-group g).  Tiles of BM x BN
 // x 128 bytes go global -> LDS directly (16-byte pieces), in rows of 128 bytes whose 16-byte chunk c
@@ -17,6 +19,7 @@
 // ordered XCD by XCD and their k loops start at rotated k-tiles, as in the bf16 kernel.
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -53,6 +56,35 @@ __device__ __forceinline__ unsigned e4m3_code(float y) {
   return sign | ((unsigned)(e + 7) << 3) | keep;
 }
 
+// ---- E5M2 encoding (round to nearest even, saturating at ±57344) ---------------------------------
+__device__ __forceinline__ unsigned e5m2_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return 0x7Fu;                       // NaN
+  if (!(a <= 57344.f)) return sign | 0x7Bu;       // saturate
+  if (a < 6.103515625e-05f) {                     // below 2^-14: multiples of 2^-16 (4 -> 2^-14, normal)
+    const float m = a * 65536.f;                  // exact: a power-of-two scaling
+    return sign | (unsigned)rintf(m);
+  }
+  int e = (int)((u >> 23) & 0xFFu) - 127;         // -14 .. 15
+  const unsigned mant = u & 0x7FFFFFu;
+  unsigned keep = mant >> 21, rest = mant & 0x1FFFFFu;
+  if (rest > 0x100000u || (rest == 0x100000u && (keep & 1u))) ++keep;
+  if (keep == 4u) {
+    keep = 0u;
+    ++e;
+  }
+  if (e > 15) return sign | 0x7Bu;
+  return sign | ((unsigned)(e + 15) << 2) | keep;
+}
+
+template <int FMT>
+__device__ __forceinline__ unsigned fp8_code(float y) {
+  if constexpr (FMT == 0) return e4m3_code(y);
+  else return e5m2_code(y);
+}
+
 // ---- amax and the scales --------------------------------------------------------------------------
 constexpr int AMAX_WGS = 1024;
 
@@ -84,7 +116,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(long n, const T* __restri
 }
 
 // scale = 448 / amax (the quantiser's), descale = amax / 448 (the GEMM's); 1 and 1 for amax = 0.
-__global__ __launch_bounds__(256) void fp8_scale_kernel(int parts, const float* __restrict__ part,
+__global__ __launch_bounds__(256) void fp8_scale_kernel(int parts, const float* __restrict__ part, float vmax,
                                                         float* __restrict__ scale, float* __restrict__ descale) {
   __shared__ float red[4];
   float m = 0.f;
@@ -95,12 +127,12 @@ __global__ __launch_bounds__(256) void fp8_scale_kernel(int parts, const float* 
   __syncthreads();
   if (threadIdx.x == 0) {
     const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    *scale = amax > 0.f ? 448.f / amax : 1.f;
-    *descale = amax > 0.f ? amax / 448.f : 1.f;
+    *scale = amax > 0.f ? vmax / amax : 1.f;
+    *descale = amax > 0.f ? amax / vmax : 1.f;
   }
 }
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(long n, const T* __restrict__ x,
                                                            const float* __restrict__ scale,
                                                            unsigned char* __restrict__ q) {
@@ -120,15 +152,15 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(long n, const T* __re
     }
     unsigned long long w = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w |= (unsigned long long)e4m3_code(v[j] * s) << (8 * j);
+    for (int j = 0; j < 8; ++j) w |= (unsigned long long)fp8_code<FMT>(v[j] * s) << (8 * j);
     *(unsigned long long*)(q + i) = w;
   } else {
-    for (long j = i; j < n; ++j) q[j] = (unsigned char)e4m3_code(to_f32(x[j]) * s);
+    for (long j = i; j < n; ++j) q[j] = (unsigned char)fp8_code<FMT>(to_f32(x[j]) * s);
   }
 }
 
 // x [rows, cols] -> q [cols, rows], one 64 x 64 tile per workgroup.
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_t_kernel(int rows, int cols, const T* __restrict__ x,
                                                              const float* __restrict__ scale,
                                                              unsigned char* __restrict__ q) {
@@ -138,7 +170,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_t_kernel(int rows, int cols,
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int r = i / 64, c = i % 64;
     const int gr = r0 + r, gc = c0 + c;
-    t[c][r] = (gr < rows && gc < cols) ? (unsigned char)e4m3_code(to_f32(x[(long)gr * cols + gc]) * s) : 0;
+    t[c][r] = (gr < rows && gc < cols) ? (unsigned char)fp8_code<FMT>(to_f32(x[(long)gr * cols + gc]) * s) : 0;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -213,11 +245,14 @@ struct F8Desc {
   const float* db;
   const bf16* bias;         // [N] or nullptr
   bf16* C;                  // [M, N]
-  bf16* C2;                 // pre-activation [M, N] (GeLU epilogue) or nullptr
-  int gelu;                 // 0 none, 1 exact GeLU, 2 tanh form
+  bf16* C2;                 // pre-activation [M, N] (GeLU epilogues) or nullptr
+  const bf16* aux;          // [M, N]: the GeLU' epilogues' A1
+  int epi;                  // 0 none, 1 GeLU, 2 tanh GeLU, 3 ∘ GeLU'(aux), 4 ∘ tanh GeLU'(aux)
 };
 
-template <class Cfg>
+// FA, FB: the formats of A and B (0 E4M3, 1 E5M2).  The B fragment is the instruction's first
+// operand, so its format goes in the first selector.
+template <class Cfg, int FA, int FB>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::NW / 4, Cfg::NW / 4)))
 void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -277,7 +312,7 @@ void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i], acc[i][j], FB, FA, 0, 127, 0, 127);
     if (++cur == Cfg::STAGES) cur = 0;
   }
 
@@ -300,10 +335,14 @@ void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
         for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
       }
       const long o = (long)m * d.N + n;
-      if (d.gelu) {
+      if (d.epi == 1 || d.epi == 2) {
         if (d.C2) *(bf16x4*)(d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.gelu - 1);
+        for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.epi - 1);
+      } else if (d.epi >= 3) {
+        const bf16x4 x = *(const bf16x4*)(d.aux + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.epi - 3);
       }
       *(bf16x4*)(d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
     }
@@ -315,9 +354,12 @@ using F8C1 = F8Tile<256, 128, 4, 2, 2>;   // 64 x 64 per wave
 using F8C2 = F8Tile<256, 192, 4, 2, 2>;   // 64 x 96 per wave
 
 template <class Cfg>
-hipError_t f8_run(const F8Desc& d, hipStream_t s) {
+hipError_t f8_run(const F8Desc& d, int fa, int fb, hipStream_t s) {
   const int tm = (d.M + Cfg::BM - 1) / Cfg::BM, tn = (d.N + Cfg::BN - 1) / Cfg::BN;
-  gemm_fp8_nt_kernel<Cfg><<<tm * tn, Cfg::NT, 0, s>>>(d, tm, tn);
+  if (fa == 0 && fb == 0) gemm_fp8_nt_kernel<Cfg, 0, 0><<<tm * tn, Cfg::NT, 0, s>>>(d, tm, tn);
+  else if (fa == 1 && fb == 0) gemm_fp8_nt_kernel<Cfg, 1, 0><<<tm * tn, Cfg::NT, 0, s>>>(d, tm, tn);
+  else if (fa == 0 && fb == 1) gemm_fp8_nt_kernel<Cfg, 0, 1><<<tm * tn, Cfg::NT, 0, s>>>(d, tm, tn);
+  else return hipErrorNotSupported;   // two E5M2 operands: not a pairing the MLP uses
   return hipGetLastError();
 }
 
@@ -325,8 +367,8 @@ hipError_t f8_run(const F8Desc& d, hipStream_t s) {
 
 size_t fp8_quantize_ws_bytes() { return (AMAX_WGS + 64) * sizeof(float); }
 
-hipError_t launch_fp8_quantize(int dtype, int rows, int cols, const void* x, bool transpose, unsigned char* q,
-                               float* descale, float* ws, hipStream_t s) {
+hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const void* x, bool transpose,
+                               unsigned char* q, float* descale, float* ws, hipStream_t s) {
   const long n = (long)rows * cols;
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
   float* part = ws;
@@ -338,30 +380,39 @@ hipError_t launch_fp8_quantize(int dtype, int rows, int cols, const void* x, boo
       if (dtype == DT_BF16) fp8_amax_kernel<bf16><<<wgs, 256, 0, s>>>(n, (const bf16*)x, part);
       else fp8_amax_kernel<float><<<wgs, 256, 0, s>>>(n, (const float*)x, part);
     }
-    fp8_scale_kernel<<<1, 256, 0, s>>>(wgs, part, scale, descale);
+    fp8_scale_kernel<<<1, 256, 0, s>>>(wgs, part, fmt ? 57344.f : 448.f, scale, descale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n == 0) return hipSuccess;
   ProfScope p(transpose ? "fp8_quantize_t" : "fp8_quantize", s, (double)n, es * n + n);
-  if (transpose) {
-    dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-    if (dtype == DT_BF16) fp8_quantize_t_kernel<bf16><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, q);
-    else fp8_quantize_t_kernel<float><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, q);
-  } else {
-    const long blocks = (n + 2047) / 2048;
-    if (dtype == DT_BF16) fp8_quantize_kernel<bf16><<<(unsigned)blocks, 256, 0, s>>>(n, (const bf16*)x, scale, q);
-    else fp8_quantize_kernel<float><<<(unsigned)blocks, 256, 0, s>>>(n, (const float*)x, scale, q);
-  }
+  auto go = [&](auto fmt_tag) {
+    constexpr int F = decltype(fmt_tag)::value;
+    if (transpose) {
+      dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+      if (dtype == DT_BF16) fp8_quantize_t_kernel<bf16, F><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, q);
+      else fp8_quantize_t_kernel<float, F><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, q);
+    } else {
+      const long blocks = (n + 2047) / 2048;
+      if (dtype == DT_BF16)
+        fp8_quantize_kernel<bf16, F><<<(unsigned)blocks, 256, 0, s>>>(n, (const bf16*)x, scale, q);
+      else
+        fp8_quantize_kernel<float, F><<<(unsigned)blocks, 256, 0, s>>>(n, (const float*)x, scale, q);
+    }
+  };
+  if (fmt) go(std::integral_constant<int, 1>());
+  else go(std::integral_constant<int, 0>());
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const float* da, const unsigned char* B,
-                              const float* db, const void* bias, int gelu, void* C, void* C2, hipStream_t s) {
+hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int fa, const float* da,
+                              const unsigned char* B, int fb, const float* db, const void* bias, int epi,
+                              const void* aux, void* C, void* C2, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  F8Desc d{M, N, K, A, B, da, db, (const bf16*)bias, (bf16*)C, (bf16*)C2, gelu};
+  F8Desc d{M, N, K, A, B, da, db, (const bf16*)bias, (bf16*)C, (bf16*)C2, (const bf16*)aux, epi};
   const double flop = 2.0 * M * (double)N * K;
-  const double bytes = (double)M * K + (double)N * K + 2.0 * M * (double)N * (gelu && C2 ? 2.0 : 1.0);
+  const double outs = 1.0 + ((epi == 1 || epi == 2) && C2 ? 1.0 : 0.0) + (epi >= 3 ? 1.0 : 0.0);
+  const double bytes = (double)M * K + (double)N * K + 2.0 * M * (double)N * outs;
   // tile choice: (waves of 256 tiles) x tile area / relative per-tile rate, the smallest wins
   const int bn[3] = {256, 192, 128};
   const double rate[3] = {1.0, 0.95, 0.8};
@@ -375,16 +426,15 @@ hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, const
       best = c;
     }
   }
-  if (best == 0) {
-    ProfScope p("gemm_fp8_nt<256x256>", s, flop, bytes);
-    return f8_run<F8C0>(d, s);
-  }
-  if (best == 1) {
-    ProfScope p("gemm_fp8_nt<256x192>", s, flop, bytes);
-    return f8_run<F8C2>(d, s);
-  }
-  ProfScope p("gemm_fp8_nt<256x128>", s, flop, bytes);
-  return f8_run<F8C1>(d, s);
+  static const char* const tags[3][3] = {
+      {"gemm_fp8_nt<256x256, e4m3 x e4m3>", "gemm_fp8_nt<256x256, e5m2 x e4m3>", "gemm_fp8_nt<256x256, e4m3 x e5m2>"},
+      {"gemm_fp8_nt<256x192, e4m3 x e4m3>", "gemm_fp8_nt<256x192, e5m2 x e4m3>", "gemm_fp8_nt<256x192, e4m3 x e5m2>"},
+      {"gemm_fp8_nt<256x128, e4m3 x e4m3>", "gemm_fp8_nt<256x128, e5m2 x e4m3>", "gemm_fp8_nt<256x128, e4m3 x e5m2>"}};
+  const int pair = fa ? 1 : (fb ? 2 : 0);
+  ProfScope p(tags[best][pair], s, flop, bytes);
+  if (best == 0) return f8_run<F8C0>(d, fa, fb, s);
+  if (best == 1) return f8_run<F8C2>(d, fa, fb, s);
+  return f8_run<F8C1>(d, fa, fb, s);
 }
 
 }  // namespace tp

@@ -110,13 +110,31 @@ def test_activation_validation(lib):
     b = lib.tp_mlp_shard_bwd_act
     assert b(2, 0, 64, 64, 256, 0, *([P] * 11), P, 1 << 30, 5, None) == -1
     assert b(2, 0, 64, 64, 256, 0, *([P] * 11), None, 0, 1, None) == -5
+
+
+def test_fp8_validation(lib):
     g = lib.tp_fp8_gemm_nt
-    assert g(16, 16, 16, P, P, P, P, None, 3, P, None, None) == -1                 # gelu 3
-    assert g(16, 16, 24, P, P, P, P, None, 0, P, None, None) == -4                 # K % 16
-    assert g(16, 12, 16, P, P, P, P, None, 0, P, None, None) == -4                 # N % 8
+    ok = lambda M=16, N=16, K=16, fa=0, fb=0, epi=0, aux=None: g(M, N, K, P, fa, P, P, fb, P, None, epi, aux,  # noqa: E731
+                                                                P, None, None)
+    assert ok(epi=5) == -1 and ok(epi=-1) == -1                                    # unknown epilogue
+    assert ok(K=24) == -4                                                          # K % 16
+    assert ok(N=12) == -4                                                          # N % 8
+    assert ok(fa=2) == -1 and ok(fb=-1) == -1                                      # unknown format
+    assert ok(fa=1, fb=1) == -4                                                    # two E5M2 operands
+    assert ok(fa=1, epi=3) == -2 and ok(fa=1, epi=4) == -2                         # GeLU' without aux
+    assert ok(M=-1) == -1
     q = lib.tp_fp8_quantize
-    assert q(4, 4, 0, P, 0, P, P, None, 0, None) == -5
-    assert q(4, 4, 2, P, 0, P, P, P, 1 << 20, None) == -1
+    assert q(4, 4, 0, P, 0, 0, P, P, None, 0, None) == -5                          # no workspace
+    assert q(4, 4, 2, P, 0, 0, P, P, P, 1 << 20, None) == -1                       # dtype
+    assert q(4, 4, 0, P, 2, 0, P, P, P, 1 << 20, None) == -1                       # format
+    assert q(4, 4, 0, P, 1, 0, None, P, P, 1 << 20, None) == -2                    # q NULL
+    assert q(4, 4, 0, P, 1, 0, P, P, MIS, 1 << 20, None) == -3                     # workspace alignment
+    b = lib.tp_bias_grad
+    assert b(4, 4, 0, P, P, None, 0, None) == -5
+    assert b(4, 4, 0, None, P, P, 1 << 20, None) == -2
+    assert b(-1, 4, 0, P, P, P, 1 << 20, None) == -1
+    assert b(4, 4, 3, P, P, P, 1 << 20, None) == -1
+    assert b(4, 4, 0, P, P, P, 16, None) == -5                                     # workspace too small
 
 
 def test_qkv_bwd_validation(lib):

@@ -71,7 +71,8 @@ def test_fp8_gemm_tanh_gelu():
     C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     Cp = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     bd.tp_fp8_gemm_nt(torch.from_numpy(A).cuda(), torch.tensor([da], device="cuda"), torch.from_numpy(B).cuda(),
-                      torch.tensor([db], device="cuda"), C, bias=dev(bias), gelu=2, C_pre=Cp)
+                      torch.tensor([db], device="cuda"), C, bias=dev(bias), epilogue=bd.TP_FP8_EPI_GELU_TANH,
+                      C_pre=Cp)
     torch.cuda.synchronize()
     ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64)
     assert_close(Cp, ref["pre"], "bf16", "pre-activation")

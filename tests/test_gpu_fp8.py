@@ -1,7 +1,8 @@
-"""GPU parity of the FP8 (OCP E4M3) path against the oracle: the per-tensor quantiser's codes bit
-for bit (the code is a decision made in fp32 on both sides) and its descale exactly, plain and
-transposed; and the GEMM on codes against the oracle's product of the decoded codes, with bias and
-GeLU epilogues, over ragged and full-size shapes.  Expected values come from the oracle only.
+"""GPU parity of the FP8 (OCP E4M3 and E5M2) path against the oracle: the per-tensor quantiser's
+codes bit for bit (the code is a decision made in fp32 on both sides) and its descale exactly, plain
+and transposed, in both formats; the GEMM on codes against the oracle's product of the decoded codes,
+with bias, GeLU and GeLU' epilogues and mixed operand formats, over ragged and full-size shapes; and
+the FP8 MLP forward and backward composed from those calls.  Expected values come from the oracle only.
 """
 
 import numpy as np
@@ -19,11 +20,14 @@ def _ws():
     return bd.workspace("tp_fp8_quantize", 1, 0, 1, 1, 1, 1, 1, torch.bfloat16)
 
 
-def _quantize(x, transpose=False):
+FMT = {"e4m3": bd.TP_FP8_E4M3, "e5m2": bd.TP_FP8_E5M2}
+
+
+def _quantize(x, transpose=False, fmt="e4m3"):
     rows, cols = x.shape
     q = torch.full((cols, rows) if transpose else (rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
     d = torch.full((1,), float("nan"), device="cuda")
-    bd.tp_fp8_quantize(x, q, d, _ws(), transpose=transpose)
+    bd.tp_fp8_quantize(x, q, d, _ws(), transpose=transpose, fmt=FMT[fmt])
     torch.cuda.synchronize()
     return q, d
 
@@ -31,57 +35,71 @@ def _quantize(x, transpose=False):
 QCASES = [(1, 1, 1.0), (7, 13, 1.0), (64, 64, 30.0), (130, 70, 1e-3), (257, 1000, 5.0), (3, 8, 0.0)]
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("transpose", [False, True], ids=["plain", "transposed"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rows,cols,std", QCASES, ids=[f"{r}x{c}_s{s}" for r, c, s in QCASES])
-def test_fp8_quantize(rows, cols, std, dtype, transpose):
+def test_fp8_quantize(rows, cols, std, dtype, transpose, fmt):
     op = synth.normal(f"f8q_{rows}_{cols}", (rows, cols), std, dtype)
-    q, d = _quantize(dev(op), transpose)
-    rq, rd = oracle.fp8_quantize(op.f64.astype(np.float32), transpose)
+    q, d = _quantize(dev(op), transpose, fmt)
+    rq, rd = oracle.fp8_quantize(op.f64.astype(np.float32), transpose, fmt)
     assert np.array_equal(host(q).astype(np.uint8), rq), "codes differ from the oracle's"
     assert np.float32(host(d)[0]) == rd, f"descale {host(d)[0]} != {rd}"
 
 
-def test_fp8_quantize_edge_values():
-    """Values at code midpoints (ties), at the subnormal boundary, and the amax element at ±448."""
-    pos = oracle.e4m3_decode(np.arange(0x7F))
+@pytest.mark.parametrize("fmt,vmax", [("e4m3", 448.0), ("e5m2", 57344.0)])
+def test_fp8_quantize_edge_values(fmt, vmax):
+    """Values at code midpoints (ties), at the subnormal boundary, and the amax element at ±vmax."""
+    pos = oracle.fp8_decode(np.arange(0x80), fmt)
+    pos = pos[np.isfinite(pos)]
     mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
-    x = np.concatenate([mids, -mids, pos.astype(np.float32), [448.0, -448.0, 0.0]]).astype(np.float32)
-    x = np.pad(x, (0, (-len(x)) % 8)).reshape(-1, 8)          # amax = 448 -> s = 1: x itself is encoded
+    x = np.concatenate([mids, -mids, pos.astype(np.float32), [vmax, -vmax, 0.0]]).astype(np.float32)
+    x = np.pad(x, (0, (-len(x)) % 8)).reshape(-1, 8)          # amax = vmax -> s = 1: x itself is encoded
     xd = torch.from_numpy(x).cuda()
-    q, d = _quantize(xd)
-    rq, rd = oracle.fp8_quantize(x)
+    q, d = _quantize(xd, fmt=fmt)
+    rq, rd = oracle.fp8_quantize(x, fmt=fmt)
     assert rd == 1.0 and host(d)[0] == 1.0
     assert np.array_equal(host(q).astype(np.uint8), rq)
 
 
-def _codes(shape, tag, std=1.0):
+def _codes(shape, tag, std=1.0, fmt="e4m3"):
     x = synth.normal(tag, shape, std, "f32").f64.astype(np.float32)
-    q, d = oracle.fp8_quantize(x)
+    q, d = oracle.fp8_quantize(x, fmt=fmt)
     return q, d
 
 
+E = oracle
 # small shapes take the 256 x 128 tile; (2048, 6144) and the ragged (2000, 9000) the 256 x 192 one;
-# (2048, 16384) the 256 x 256 one
-GCASES = [(256, 256, 128, False), (300, 200, 176, True), (17, 8, 16, False), (2048, 6144, 1024, True),
-          (513, 1032, 2064, False), (2000, 9000, 64, True), (2048, 16384, 256, False)]
+# (2048, 16384) the 256 x 256 one.  E5M2 operands are the backward's gradients.
+GCASES = [(256, 256, 128, E.FP8_EPI_NONE, "e4m3", "e4m3"), (300, 200, 176, E.FP8_EPI_GELU, "e4m3", "e4m3"),
+          (17, 8, 16, E.FP8_EPI_NONE, "e4m3", "e4m3"), (2048, 6144, 1024, E.FP8_EPI_GELU, "e4m3", "e4m3"),
+          (513, 1032, 2064, E.FP8_EPI_NONE, "e4m3", "e4m3"), (2000, 9000, 64, E.FP8_EPI_GELU, "e4m3", "e4m3"),
+          (2048, 16384, 256, E.FP8_EPI_NONE, "e4m3", "e4m3"),
+          (300, 200, 176, E.FP8_EPI_NONE, "e5m2", "e4m3"), (513, 1032, 2064, E.FP8_EPI_NONE, "e4m3", "e5m2"),
+          (130, 264, 2048, E.FP8_EPI_NONE, "e4m3", "e5m2"), (2000, 9000, 64, E.FP8_EPI_DGELU, "e5m2", "e4m3"),
+          (256, 256, 128, E.FP8_EPI_DGELU_TANH, "e5m2", "e4m3"), (2048, 6144, 1024, E.FP8_EPI_DGELU, "e5m2", "e4m3"),
+          (77, 40, 32, E.FP8_EPI_GELU_TANH, "e4m3", "e5m2")]
 
 
-@pytest.mark.parametrize("M,N,K,epi", GCASES, ids=[f"m{m}_n{n}_k{k}{'_gelu' if e else ''}" for m, n, k, e in GCASES])
-def test_fp8_gemm(M, N, K, epi):
-    print(f"fp8 gemm M={M} N={N} K={K} gelu={epi}", flush=True)
-    A, da = _codes((M, K), f"f8A_{M}_{K}")
-    B, db = _codes((N, K), f"f8B_{N}_{K}", 0.05)
-    bias = synth.normal(f"f8bias_{N}", (N,), 0.1, "bf16")
+@pytest.mark.parametrize("M,N,K,epi,fa,fb", GCASES, ids=[f"m{m}_n{n}_k{k}_epi{e}_{a}x{b}" for m, n, k, e, a, b in GCASES])
+def test_fp8_gemm(M, N, K, epi, fa, fb):
+    print(f"fp8 gemm M={M} N={N} K={K} epilogue={epi} {fa} x {fb}", flush=True)
+    A, da = _codes((M, K), f"f8A_{M}_{K}", 1.0 if fa == "e4m3" else 1e-3, fa)
+    B, db = _codes((N, K), f"f8B_{N}_{K}", 0.05 if fb == "e4m3" else 1e-3, fb)
+    bias = synth.normal(f"f8bias_{N}", (N,), 0.1, "bf16") if epi < E.FP8_EPI_DGELU else None
+    aux = synth.normal(f"f8aux_{M}_{N}", (M, N), 1.0, "bf16") if epi >= E.FP8_EPI_DGELU else None
+    gelu = epi in (E.FP8_EPI_GELU, E.FP8_EPI_GELU_TANH)
     C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
-    Cp = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda") if epi else None
+    Cp = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda") if gelu else None
     tA, tB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
     tda, tdb = torch.tensor([da], device="cuda"), torch.tensor([db], device="cuda")
-    bd.tp_fp8_gemm_nt(tA, tda, tB, tdb, C, bias=dev(bias), gelu=epi, C_pre=Cp)
+    bd.tp_fp8_gemm_nt(tA, tda, tB, tdb, C, bias=dev(bias) if bias is not None else None, epilogue=epi,
+                      aux=dev(aux) if aux is not None else None, C_pre=Cp, a_fmt=FMT[fa], b_fmt=FMT[fb])
     torch.cuda.synchronize()
-    ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64, epi=oracle.FP8_EPI_GELU if epi else oracle.FP8_EPI_NONE)
+    ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64 if bias is not None else None, epi=epi,
+                             aux=aux.f64 if aux is not None else None, fmt_a=fa, fmt_b=fb)
     assert_close(C, ref["C"], "bf16", "C")
-    if epi:
+    if gelu:
         assert_close(Cp, ref["pre"], "bf16", "C_pre")
 
 
@@ -103,7 +121,7 @@ def test_fp8_mlp_forward_against_bf16_definition():
     bd.tp_fp8_quantize(dev(W1), qW1t, dW1, ws, transpose=True)
     bd.tp_fp8_quantize(dev(W2), qW2t, dW2, ws, transpose=True)
     Y = torch.empty(T, Fr, dtype=torch.bfloat16, device="cuda")
-    bd.tp_fp8_gemm_nt(qX, dX, qW1t, dW1, Y, bias=dev(b1), gelu=True)
+    bd.tp_fp8_gemm_nt(qX, dX, qW1t, dW1, Y, bias=dev(b1), epilogue=bd.TP_FP8_EPI_GELU)
     bd.tp_fp8_quantize(Y, qY, dY, ws)
     Z = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     bd.tp_fp8_gemm_nt(qY, dY, qW2t, dW2, Z)
@@ -111,3 +129,79 @@ def test_fp8_mlp_forward_against_bf16_definition():
     ref = oracle.mlp_fwd(X.f64, W1.f64, b1.f64, W2.f64, None)
     assert_close(Y, ref["Y"], "bf16", "Y (fp8 fc1)", tol=8e-2)
     assert_close(Z, ref["Z"], "bf16", "Z (fp8 fc2)", tol=8e-2)
+
+
+def test_fp8_mlp_backward():
+    """The FP8 MLP-shard backward composed from the entry points, the usual FP8 training recipe:
+    gradients in E5M2, weights and activations in E4M3, each GEMM with K-major code operands —
+    dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1) (the GeLU' epilogue), dW2 = Yᵀ·dZ, dX = dA1·W1ᵀ, dW1 = Xᵀ·dA1 — and
+    db1 = Σ_t dA1.  Checked two ways: against the same recipe run by the oracle from the GPU's own
+    bf16 intermediates (A1, Y, dA1: the values the GPU quantised, so every code is the same on both
+    sides and each GEMM is held to the bf16 bar), and against the oracle's
+    exact-precision backward (E5M2 keeps 2 mantissa bits: 1.5e-1 normwise, where the errors the
+    recipe itself makes sit near 9e-2 for these shapes)."""
+    T, H, Fr = 512, 1024, 768
+    X = synth.normal("f8mlpX", (T, H), 1.0, "bf16")
+    W1 = synth.normal("f8mlpW1", (H, Fr), 0.02, "bf16")
+    b1 = synth.normal("f8mlpb1", (Fr,), 0.02, "bf16")
+    W2 = synth.normal("f8mlpW2", (Fr, H), 0.02, "bf16")
+    dZ = synth.normal("f8mlpdZ", (T, H), 1.0, "bf16")
+    u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")  # noqa: E731
+    f1 = lambda: torch.empty(1, device="cuda")  # noqa: E731
+    bf = lambda *s: torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda")  # noqa: E731
+    ws = _ws()
+    e4, e5 = bd.TP_FP8_E4M3, bd.TP_FP8_E5M2
+    # forward (keeps A1 for the backward)
+    qX, qXt, qW1t, qW1, qW2t, qW2 = u8(T, H), u8(H, T), u8(Fr, H), u8(H, Fr), u8(H, Fr), u8(Fr, H)
+    sX, sW1, sW2, sY, sdZ, sdA1 = f1(), f1(), f1(), f1(), f1(), f1()
+    bd.tp_fp8_quantize(dev(X), qX, sX, ws)
+    bd.tp_fp8_quantize(dev(X), qXt, sX, ws, transpose=True)
+    bd.tp_fp8_quantize(dev(W1), qW1t, sW1, ws, transpose=True)
+    bd.tp_fp8_quantize(dev(W1), qW1, sW1, ws)
+    bd.tp_fp8_quantize(dev(W2), qW2t, sW2, ws, transpose=True)
+    bd.tp_fp8_quantize(dev(W2), qW2, sW2, ws)
+    A1, Y = bf(T, Fr), bf(T, Fr)
+    bd.tp_fp8_gemm_nt(qX, sX, qW1t, sW1, Y, bias=dev(b1), epilogue=bd.TP_FP8_EPI_GELU, C_pre=A1)
+    qYt = u8(Fr, T)
+    bd.tp_fp8_quantize(Y, qYt, sY, ws, transpose=True)
+    # backward
+    qdZ, qdZt, qdA1, qdA1t = u8(T, H), u8(H, T), u8(T, Fr), u8(Fr, T)
+    bd.tp_fp8_quantize(dev(dZ), qdZ, sdZ, ws, fmt=e5)
+    bd.tp_fp8_quantize(dev(dZ), qdZt, sdZ, ws, transpose=True, fmt=e5)
+    dA1, dW2, dX, dW1 = bf(T, Fr), bf(Fr, H), bf(T, H), bf(H, Fr)
+    db1 = bf(Fr)
+    bd.tp_fp8_gemm_nt(qdZ, sdZ, qW2, sW2, dA1, epilogue=bd.TP_FP8_EPI_DGELU, aux=A1, a_fmt=e5, b_fmt=e4)
+    bd.tp_fp8_gemm_nt(qYt, sY, qdZt, sdZ, dW2, a_fmt=e4, b_fmt=e5)
+    bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, fmt=e5)
+    bd.tp_fp8_quantize(dA1, qdA1t, sdA1, ws, transpose=True, fmt=e5)
+    bd.tp_fp8_gemm_nt(qdA1, sdA1, qW1, sW1, dX, a_fmt=e5, b_fmt=e4)
+    bd.tp_fp8_gemm_nt(qXt, sX, qdA1t, sdA1, dW1, a_fmt=e4, b_fmt=e5)
+    wsb = bd.workspace("tp_bias_grad", 1, 0, T, 1, Fr, 1, 1, torch.bfloat16)
+    bd.tp_bias_grad(dA1, db1, wsb)
+    torch.cuda.synchronize()
+
+    # the recipe on the oracle, from the GPU's bf16 A1 / Y / dA1 (the values the GPU quantised)
+    A1h, Yh, dA1h = host(A1).astype(np.float32), host(Y).astype(np.float32), host(dA1).astype(np.float32)
+    f32 = lambda a: a.f64.astype(np.float32)  # noqa: E731
+    oq = oracle.fp8_quantize
+    cdZ, odZ = oq(f32(dZ), fmt="e5m2")
+    cdZt, _ = oq(f32(dZ), True, "e5m2")
+    cW2, oW2 = oq(f32(W2))
+    cW1, oW1 = oq(f32(W1))
+    cXt, oX = oq(f32(X), True)
+    cYt, oY = oq(Yh, True)
+    cA, oA = oq(dA1h, fmt="e5m2")
+    cAt, _ = oq(dA1h, True, "e5m2")
+    g = oracle.fp8_gemm_nt
+    emu = {"dA1": g(cdZ, odZ, cW2, oW2, epi=oracle.FP8_EPI_DGELU, aux=A1h, fmt_a="e5m2")["C"],
+           "dW2": g(cYt, oY, cdZt, odZ, fmt_b="e5m2")["C"],
+           "dX": g(cA, oA, cW1, oW1, fmt_a="e5m2")["C"],
+           "dW1": g(cXt, oX, cAt, oA, fmt_b="e5m2")["C"],
+           "db1": dA1h.astype(np.float64).sum(axis=0)}
+    got = {"dA1": dA1, "dW2": dW2, "dX": dX, "dW1": dW1, "db1": db1}
+    for k in emu:
+        assert_close(got[k], emu[k], "bf16", f"{k} (the FP8 recipe on the oracle)")
+    ref = oracle.mlp_bwd(X.f64, W1.f64, W2.f64, *[oracle.mlp_fwd(X.f64, W1.f64, b1.f64, W2.f64, None)[k]
+                                                 for k in ("A1", "Y")], dZ.f64, False)
+    for k in ("dX", "dW1", "db1", "dW2"):
+        assert_close(got[k], ref[k], "bf16", f"{k} (exact precision)", tol=1.5e-1)
