@@ -472,10 +472,84 @@ def moe_combine(Z_rows, gates, token_row):
 def tp_moe_shard_fwd(tp_size, rank, X, route, W1_r, b1_r, W2_r):
     """The MoE expert block on rank r: dispatch (the rows of X in expert-sorted order), each
     expert's fc1 column shard with bias and GeLU and its fc2 row shard, then the gate-weighted
-    combine of the rank's partials.  Σ_r over ranks is the full MoE output ([Arch] §4, §6)."""
+    combine of the rank's partials.  Σ_r over ranks is the full MoE output ([Arch] §4, §6).
+    Also returns the expert-sorted A1, Y and Z rows the backward takes."""
     Xp = np.asarray(X)[route["row_token"]]
-    Z = tp_mlp_grouped_shard_fwd(tp_size, rank, route["group_offsets"], Xp, W1_r, b1_r, W2_r)
-    return {"out": moe_combine(Z, route["gates"], route["token_row"]), "Z": Z}
+    off = route["group_offsets"]
+    A1 = np.zeros((Xp.shape[0], W1_r.shape[2]))
+    for e in range(W1_r.shape[0]):
+        lo, hi = int(off[e]), int(off[e + 1])
+        A1[lo:hi] = Xp[lo:hi] @ W1_r[e] + b1_r[e]
+    Y = gelu(A1)
+    Z = tp_mlp_grouped_shard_fwd(tp_size, rank, off, Xp, W1_r, b1_r, W2_r)
+    return {"out": moe_combine(Z, route["gates"], route["token_row"]), "Z": Z, "A1": A1, "Y": Y}
+
+
+def moe_combine_bwd(d_out, Z_rows, gates, token_row):
+    """Backward of moe_combine (out[t] = Σ_j g[t, j]·Z[token_row[t, j]]), from the chain rule:
+    dZ[token_row[t, j]] = g[t, j]·d_out[t]  (each row is one (t, j): the dispatch is a permutation)
+    dg[t, j] = ⟨d_out[t], Z[token_row[t, j]]⟩."""
+    n, k = gates.shape
+    dZ = np.zeros(Z_rows.shape)
+    dg = np.zeros((n, k))
+    for j in range(k):
+        rows = token_row[:, j]
+        dZ[rows] = gates[:, j:j + 1] * d_out
+        dg[:, j] = np.sum(d_out * Z_rows[rows], axis=1)
+    return {"dZ": dZ, "dgates": dg}
+
+
+def tp_mlp_grouped_shard_bwd(group_offsets, X_perm, W1_r, W2_r, A1, Y, dZ):
+    """Backward of tp_mlp_grouped_shard_fwd: for each expert e, mlp_bwd on its rows with its own
+    weights (dW1[e], db1[e], dW2[e] from its rows only; zero for an expert without rows); the rows'
+    input gradients dX_perm in the same expert-sorted order."""
+    G, H, Fr = W1_r.shape
+    dXp = np.zeros(X_perm.shape)
+    dA1 = np.zeros(A1.shape)
+    dW1, db1, dW2 = np.zeros((G, H, Fr)), np.zeros((G, Fr)), np.zeros((G, Fr, H))
+    for e in range(G):
+        lo, hi = int(group_offsets[e]), int(group_offsets[e + 1])
+        if hi > lo:
+            g = mlp_bwd(X_perm[lo:hi], W1_r[e], W2_r[e], A1[lo:hi], Y[lo:hi], dZ[lo:hi], False)
+            dXp[lo:hi], dA1[lo:hi] = g["dX"], g["dA1"]
+            dW1[e], db1[e], dW2[e] = g["dW1"], g["db1"], g["dW2"]
+    return {"dX_perm": dXp, "dA1": dA1, "dW1": dW1, "db1": db1, "dW2": dW2}
+
+
+def tp_moe_shard_bwd(tp_size, rank, X, route, W1_r, W2_r, fwd, d_out):
+    """Backward of tp_moe_shard_fwd on rank r, given the gradient d_out of the full MoE output (every
+    rank receives it, as the copy / all-reduce pair makes it for the dense MLP): the combine's
+    backward (dZ rows, the rank's partial gate gradient — Σ over ranks is the full one, since the
+    combine is linear in the partials), the experts' grouped backward, and the dispatch's backward
+    dX[t] = Σ_j dX_perm[token_row[t, j]] (the rank's partial input gradient)."""
+    cb = moe_combine_bwd(d_out, fwd["Z"], route["gates"], route["token_row"])
+    Xp = np.asarray(X)[route["row_token"]]
+    g = tp_mlp_grouped_shard_bwd(route["group_offsets"], Xp, W1_r, W2_r, fwd["A1"], fwd["Y"], cb["dZ"])
+    tr = route["token_row"]
+    dX = np.zeros(np.shape(X))
+    for j in range(tr.shape[1]):
+        dX += g["dX_perm"][tr[:, j]]
+    return {"dX": dX, "dgates": cb["dgates"], "dW1": g["dW1"], "db1": g["db1"], "dW2": g["dW2"],
+            "dA1": g["dA1"], "dZ": cb["dZ"]}
+
+
+def moe_route_bwd(logits32, experts, dgates):
+    """Gradient of the router logits from the gates' gradient (reading R14: gate = p_e, the softmax
+    probability over all experts, for the chosen e).  With the choice held fixed, ∂p_i/∂l_e =
+    p_i(δ_ie − p_e), so d_logits[t, e] = Σ_j dg[t, j]·p_{i_j}·(δ_{i_j e} − p_e)."""
+    l64 = np.asarray(logits32, dtype=np.float32).astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    n, E = p.shape
+    dl = np.zeros((n, E))
+    for t in range(n):
+        s = 0.0
+        for j in range(experts.shape[1]):
+            i = int(experts[t, j])
+            dl[t, i] += dgates[t, j] * p[t, i]
+            s += dgates[t, j] * p[t, i]
+        dl[t] -= s * p[t]
+    return dl
 
 
 # ---- FP8 (reading R15) -------------------------------------------------------------------------

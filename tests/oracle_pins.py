@@ -674,5 +674,74 @@ def pin_fp8():
             assert abs(r["C"][i, j] - pre * bf.gelu_prime(aux[i, j])) <= 1e-12 * max(1.0, abs(pre))
 
 
+def pin_moe_backward():
+    """The MoE block's backward against fp64 central differences of Σ out_r ∘ d_out in X, each
+    expert's weight shards and the gates (held as inputs), on both ranks of a split; the router's
+    logit gradient against differences of the routed gates (logits far enough apart that the
+    choice stays fixed); rank sums and shard blocks against the unsharded block; E = k = 1 against
+    the dense MLP backward; k = E with equal gate gradients gives zero logit gradient (Σ_e p_e = 1)."""
+    g = _rng(67)
+    n, E, k, H, Fe, t = 7, 5, 2, 4, 6, 2
+    X = g.standard_normal((n, H))
+    lg = (g.permutation(n * E).reshape(n, E) * 0.375).astype(np.float32)    # distinct, gaps >= 3/8
+    W1, b1 = g.standard_normal((E, H, Fe)) * 0.5, g.standard_normal((E, Fe)) * 0.5
+    W2 = g.standard_normal((E, Fe, H)) * 0.5
+    d_out = g.standard_normal((n, H))
+    r = T.moe_route(lg, k)
+    full_fwd = T.tp_moe_shard_fwd(1, 0, X, r, W1, b1, W2)
+    full = T.tp_moe_shard_bwd(1, 0, X, r, W1, W2, full_fwd, d_out)
+    sum_dX, sum_dg = np.zeros((n, H)), np.zeros((n, k))
+    for rank in range(t):
+        f0, fr = T.shard_range(Fe, t, rank)
+        W1r, b1r, W2r = W1[:, :, f0:f0 + fr], b1[:, f0:f0 + fr], W2[:, f0:f0 + fr]
+        fwd = T.tp_moe_shard_fwd(t, rank, X, r, W1r, b1r, W2r)
+        b = T.tp_moe_shard_bwd(t, rank, X, r, W1r, W2r, fwd, d_out)
+
+        def loss(X_=X, W1_=W1r, b1_=b1r, W2_=W2r, gates_=r["gates"]):
+            rt = dict(r, gates=gates_)
+            return float((T.tp_moe_shard_fwd(t, rank, X_, rt, W1_, b1_, W2_)["out"] * d_out).sum())
+        for name, x, grad, kw in (("X", X, b["dX"], "X_"), ("W1", W1r, b["dW1"], "W1_"), ("b1", b1r, b["db1"], "b1_"),
+                                  ("W2", W2r, b["dW2"], "W2_"), ("gates", r["gates"], b["dgates"], "gates_")):
+            for _ in range(2):
+                v = g.standard_normal(x.shape)
+                fd = _fd_dir(lambda y: loss(**{kw: y}), x, v)
+                _close(np.array([(grad * v).sum()]), np.array([fd]), 1e-7, f"MoE bwd r{rank} d{name} vs differences")
+        sum_dX += b["dX"]
+        sum_dg += b["dgates"]
+        _close(b["dW1"], full["dW1"][:, :, f0:f0 + fr], 1e-12, "dW1 rank block = columns of the unsharded")
+        _close(b["db1"], full["db1"][:, f0:f0 + fr], 1e-12, "db1 rank block")
+        _close(b["dW2"], full["dW2"][:, f0:f0 + fr], 1e-12, "dW2 rank block = rows of the unsharded")
+    _close(sum_dX, full["dX"], 1e-12, "MoE bwd: sum of dX over ranks = unsharded")
+    _close(sum_dg, full["dgates"], 1e-12, "MoE bwd: sum of gate gradients over ranks = unsharded")
+    # router: differences of Σ gates(l)·dg with the choice fixed
+    dg = full["dgates"]
+    dl = T.moe_route_bwd(lg, r["experts"], dg)
+    # directions of small integers and a step of 2⁻¹⁰ keep l ± h·v exact in float32 (the logits are
+    # multiples of 3/8 below 16), so the difference quotient carries no rounding of its inputs
+    for _ in range(3):
+        v = g.integers(-3, 4, lg.shape).astype(np.float64)
+
+        def gsum(l):
+            rr = T.moe_route(l.astype(np.float32), k)
+            assert (rr["experts"] == r["experts"]).all()
+            return float((rr["gates"] * dg).sum())
+        h = 2.0 ** -10
+        fd = (gsum(lg.astype(np.float64) + h * v) - gsum(lg.astype(np.float64) - h * v)) / (2 * h)
+        _close(np.array([(dl * v).sum()]), np.array([fd]), 1e-5, "router logit gradient vs differences")
+    rE = T.moe_route(lg, E)
+    assert np.abs(T.moe_route_bwd(lg, rE["experts"], np.full((n, E), 0.7))).max() < 1e-15, "k = E, equal dg"
+    # one expert, top-1: gate 1, the dense MLP backward; dgate = <d_out, Z>
+    r1 = T.moe_route(np.zeros((n, 1), np.float32), 1)
+    f1 = T.tp_moe_shard_fwd(1, 0, X, r1, W1[:1], b1[:1], W2[:1])
+    b1_ = T.tp_moe_shard_bwd(1, 0, X, r1, W1[:1], W2[:1], f1, d_out)
+    dense = T.mlp_fwd(X, W1[0], b1[0], W2[0], None)
+    db = T.mlp_bwd(X, W1[0], W2[0], dense["A1"], dense["Y"], d_out, False)
+    for a, bb in (("dX", "dX"), ("dW1", "dW1"), ("db1", "db1"), ("dW2", "dW2")):
+        got = b1_[a][0] if a != "dX" else b1_[a]
+        _close(got, db[bb], 1e-13, f"E = k = 1 {a} = dense")
+    _close(b1_["dgates"][:, 0], (d_out * dense["Z"]).sum(axis=1), 1e-13, "E = k = 1 dgate = <d_out, Z>")
+
+
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
-            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe, pin_fp8]
+            pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe, pin_moe_backward,
+            pin_fp8]

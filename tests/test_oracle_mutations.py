@@ -248,6 +248,35 @@ def _gelu_tanh_cubic_dropped(x):
     return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * x))
 
 
+def _combine_bwd_ungated(d_out, Z_rows, gates, token_row):
+    r = _ORIG_COMBINE_BWD(d_out, Z_rows, gates, token_row)
+    for j in range(gates.shape[1]):
+        r["dZ"][token_row[:, j]] = d_out
+    return r
+
+
+def _route_bwd_no_softmax_coupling(logits32, experts, dgates):
+    l64 = np.asarray(logits32, dtype=np.float32).astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dl = np.zeros(p.shape)
+    for j in range(experts.shape[1]):
+        np.put_along_axis(dl, experts[:, j:j + 1], (dgates[:, j] * np.take_along_axis(p, experts[:, j:j + 1], 1)[:, 0])[:, None], 1)
+    return dl
+
+
+def _moe_bwd_dX_first_choice(tp_size, rank, X, route, W1_r, W2_r, fwd, d_out):
+    r = _ORIG_MOE_BWD(tp_size, rank, X, route, W1_r, W2_r, fwd, d_out)
+    Xp = np.asarray(X)[route["row_token"]]
+    gb = T.tp_mlp_grouped_shard_bwd(route["group_offsets"], Xp, W1_r, W2_r, fwd["A1"], fwd["Y"], r["dZ"])
+    r["dX"] = gb["dX_perm"][route["token_row"][:, 0]]
+    return r
+
+
+_ORIG_COMBINE_BWD = T.moe_combine_bwd
+_ORIG_MOE_BWD = T.tp_moe_shard_bwd
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -290,6 +319,9 @@ MUTANTS = {
     "fp8_descale_inverted": {"fp8_quantize": _fp8_quantize_descale_inverted},
     "fp8_dgelu_uses_gelu": {"fp8_gemm_nt": _fp8_gemm_dgelu_uses_gelu},
     "gelu_tanh_cubic_dropped": {"gelu_tanh": _gelu_tanh_cubic_dropped},
+    "moe_combine_bwd_ungated": {"moe_combine_bwd": _combine_bwd_ungated},
+    "moe_route_bwd_no_softmax_coupling": {"moe_route_bwd": _route_bwd_no_softmax_coupling},
+    "moe_bwd_dX_first_choice_only": {"tp_moe_shard_bwd": _moe_bwd_dX_first_choice},
 }
 
 
