@@ -241,6 +241,47 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
                      const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
                      void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of tp_mlp_grouped_shard_fwd, expert by expert on the same expert-sorted rows (the chain
+ * rule of the dense MLP shard's backward applied to each expert's rows and weights):
+ *   dA1 = (dZ_perm·W2_r[e]ᵀ) ∘ GeLU'(A1_r)     dX_perm = dA1·W1_r[e]ᵀ   (rows of expert e)
+ *   dW1_r[e] = X_eᵀ·dA1_e ;  db1_r[e] = Σ_rows dA1_e ;  dW2_r[e] = Y_eᵀ·dZ_e
+ * An expert without rows gets zero weight and bias gradients.  Shapes as the forward's; dX_perm and
+ * dZ_perm [rows, H], dW1_r like W1_r, db1_r like b1_r, dW2_r like W2_r.  dX_perm may be the same
+ * buffer as dZ_perm (every read of dZ_perm comes first).  The experts' weight gradients are grouped
+ * GEMMs whose k dimension is the expert's rows.  workspace: tp_workspace_bytes(
+ * "tp_mlp_grouped_shard_bwd", ...) with B·S = rows, n_heads = n_groups, F = F_group (the offsets'
+ * plan and dA1). */
+int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows, int H,
+                             int F_group, int dtype, const void* X_perm, const void* W1_r, const void* W2_r,
+                             const void* A1_r, const void* Y_r, const void* dZ_perm, void* dX_perm, void* dW1_r,
+                             void* db1_r, void* dW2_r, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of tp_moe_shard_fwd on rank r, given d_out [tokens, H], the gradient of the whole MoE
+ * output (every rank receives it, as the copy / all-reduce pair gives the dense MLP its dZ), with
+ * row (t, j) = token_row[t, j]:
+ *   dZ[row] = gates[t, j]·d_out[t]            the combine's backward
+ *   dgates_r[t, j] = ⟨d_out[t], Z_r[row]⟩      (fp32; a partial: Σ_r over ranks is the gate
+ *                                              gradient, the combine being linear in the partials)
+ *   the experts' backward as tp_mlp_grouped_shard_bwd, on X's rows in dispatch order
+ *   dX_r[t] = Σ_j dX_perm[row]                 the dispatch's backward (a partial over ranks)
+ * Inputs are the forward's: X, gates, group_offsets, token_row from tp_moe_route, A1_r, Y_r, Z_r
+ * from tp_moe_shard_fwd (A1_r now required).  token_row must be a permutation of [0, tokens·k), as
+ * tp_moe_route writes it; entries outside that range are skipped.  Outputs dW1_r, db1_r, dW2_r as in
+ * tp_mlp_grouped_shard_bwd.  workspace: tp_workspace_bytes("tp_moe_shard_bwd", ...) with
+ * B·S = tokens·top_k, n_heads = E, F = F_expert (the dispatched X and dZ rows, dA1, the plan). */
+int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
+                     const void* X, const float* gates, const int* group_offsets, const int* token_row,
+                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r, const void* Z_r,
+                     const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r, void* dW2_r,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The router's logit gradient from the (complete) gate gradient, the top-k choice held fixed:
+ * with p = softmax(logits[t]) and gates[t, j] = p[expert_idx[t, j]],
+ *   d_logits[t, e] = Σ_j dgates[t, j]·p[i_j]·(δ(i_j, e) − p[e]),  i_j = expert_idx[t, j]
+ * fp32 [tokens, E]; the softmax is recomputed from the fp32 logits.  E <= 1024, top_k <= 32. */
+int tp_moe_route_bwd(int tokens, int n_experts, int top_k, const float* logits, const int* expert_idx,
+                     const float* dgates, float* d_logits, void* stream);
+
 /* FP8: the OCP 8-bit floats E4M3 (1 sign, 4 exponent bits, bias 7, 3 mantissa bits, max 448) for
  * weights and activations and E5M2 (5 exponent bits, bias 15, 2 mantissa bits, max 57344) for
  * gradients.  Forward and backward GEMMs in FP8 beside FP32 master weights
@@ -285,7 +326,8 @@ int tp_bias_grad(int rows, int cols, int dtype, const void* dy, void* db, void* 
 
 /* Workspace bytes an entry point needs for these sizes ("tp_mlp_shard_bwd", "tp_qkv_shard_bwd",
  * "tp_attn_heads_bwd", "tp_attn_out_shard_bwd", "tp_residual_ln_bwd", "tp_mlp_grouped_shard_fwd",
- * "tp_moe_route", "tp_moe_shard_fwd", "tp_fp8_quantize", "tp_bias_grad"; 0 for the others).  T = B*S; F is used by the
+ * "tp_mlp_grouped_shard_bwd", "tp_moe_route", "tp_moe_shard_fwd", "tp_moe_shard_bwd", "tp_fp8_quantize",
+ * "tp_bias_grad"; 0 for the others).  T = B*S; F is used by the
  * MLPs only, n_heads by the others (for "tp_mlp_grouped_shard_fwd" it carries n_groups).  Returns 0
  * for an unknown name or invalid sizes. */
 size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, int H,

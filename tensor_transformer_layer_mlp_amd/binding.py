@@ -41,6 +41,9 @@ _SIGNATURES = {
     "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "tp_fp8_gemm_nt": (_I, [_I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
     "tp_bias_grad": (_I, [_I, _I, _I, _P, _P, _P, _Z, _P]),
+    "tp_mlp_grouped_shard_bwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 10 + [_P, _Z, _P]),
+    "tp_moe_shard_bwd": (_I, [_I] * 8 + [_P] * 15 + [_P, _Z, _P]),
+    "tp_moe_route_bwd": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "tp_moe_shard_fwd": (_I, [_I] * 8 + [_P] * 12 + [_P, _Z, _P]),
     "tp_workspace_bytes": (_Z, [ctypes.c_char_p] + [_I] * 8),
     "tp_status_str": (ctypes.c_char_p, [_I]),
@@ -402,6 +405,65 @@ def tp_fp8_gemm_nt(A, a_descale, B, b_descale, C, bias=None, epilogue=TP_FP8_EPI
                               _ptr(aux, "aux", torch.bfloat16, True), _ptr(C, "C", torch.bfloat16),
                               _ptr(C_pre, "C_pre", torch.bfloat16, True), _stream(stream))
     _check(rc, "tp_fp8_gemm_nt")
+
+
+def tp_mlp_grouped_shard_bwd(tp_size, rank, group_offsets, H, F_group, X_perm, W1_r, W2_r, A1_r, Y_r, dZ_perm,
+                             dX_perm, dW1_r, db1_r, dW2_r, workspace, stream=None):
+    """Backward of tp_mlp_grouped_shard_fwd on expert-sorted rows (dX_perm may be dZ_perm)."""
+    G = W1_r.shape[0]
+    rows = X_perm.shape[0]
+    _, Fr = tp_shard_range(F_group, tp_size, rank) if 0 <= rank < tp_size and F_group >= tp_size >= 1 else (0, 0)
+    _need(group_offsets, G + 1, "group_offsets")
+    for t, n, name in ((X_perm, rows * H, "X_perm"), (W1_r, G * H * Fr, "W1_r"), (W2_r, G * Fr * H, "W2_r"),
+                       (A1_r, rows * Fr, "A1_r"), (Y_r, rows * Fr, "Y_r"), (dZ_perm, rows * H, "dZ_perm"),
+                       (dX_perm, rows * H, "dX_perm"), (dW1_r, G * H * Fr, "dW1_r"), (db1_r, G * Fr, "db1_r"),
+                       (dW2_r, G * Fr * H, "dW2_r")):
+        _need(t, n, name)
+    dt = X_perm.dtype
+    rc = raw().tp_mlp_grouped_shard_bwd(
+        tp_size, rank, G, _ptr(group_offsets, "group_offsets", torch.int32), rows, H, F_group, _dtype_code(X_perm),
+        _ptr(X_perm, "X_perm"), _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt), _ptr(A1_r, "A1_r", dt),
+        _ptr(Y_r, "Y_r", dt), _ptr(dZ_perm, "dZ_perm", dt), _ptr(dX_perm, "dX_perm", dt), _ptr(dW1_r, "dW1_r", dt),
+        _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt), _ptr(workspace, "workspace", None, True),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
+    _check(rc, "tp_mlp_grouped_shard_bwd")
+
+
+def tp_moe_shard_bwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, gates, group_offsets, token_row,
+                     W1_r, W2_r, A1_r, Y_r, Z_r, d_out, dX_r, dgates_r, dW1_r, db1_r, dW2_r, workspace, stream=None):
+    """Backward of tp_moe_shard_fwd on this rank (partial dX_r and gate gradients; expert weight
+    gradients of the rank's shards)."""
+    n = tokens * top_k
+    _, Fr = tp_shard_range(F_expert, tp_size, rank) if 0 <= rank < tp_size and F_expert >= tp_size >= 1 else (0, 0)
+    E = n_experts
+    for t, m, name in ((X, tokens * H, "X"), (gates, n, "gates"), (group_offsets, E + 1, "group_offsets"),
+                       (token_row, n, "token_row"), (W1_r, E * H * Fr, "W1_r"), (W2_r, E * Fr * H, "W2_r"),
+                       (A1_r, n * Fr, "A1_r"), (Y_r, n * Fr, "Y_r"), (Z_r, n * H, "Z_r"), (d_out, tokens * H, "d_out"),
+                       (dX_r, tokens * H, "dX_r"), (dgates_r, n, "dgates_r"), (dW1_r, E * H * Fr, "dW1_r"),
+                       (db1_r, E * Fr, "db1_r"), (dW2_r, E * Fr * H, "dW2_r")):
+        _need(t, m, name)
+    dt = X.dtype
+    rc = raw().tp_moe_shard_bwd(
+        tp_size, rank, tokens, H, n_experts, top_k, F_expert, _dtype_code(X), _ptr(X, "X"),
+        _ptr(gates, "gates", torch.float32), _ptr(group_offsets, "group_offsets", torch.int32),
+        _ptr(token_row, "token_row", torch.int32), _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
+        _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(Z_r, "Z_r", dt), _ptr(d_out, "d_out", dt),
+        _ptr(dX_r, "dX_r", dt), _ptr(dgates_r, "dgates_r", torch.float32), _ptr(dW1_r, "dW1_r", dt),
+        _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt), _ptr(workspace, "workspace", None, True),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))
+    _check(rc, "tp_moe_shard_bwd")
+
+
+def tp_moe_route_bwd(logits, expert_idx, dgates, d_logits, stream=None):
+    """Router logit gradient [tokens, E] from the gate gradient, the choice held fixed."""
+    tokens, E = logits.shape
+    k = expert_idx.shape[1]
+    _need(dgates, tokens * k, "dgates")
+    _need(d_logits, tokens * E, "d_logits")
+    rc = raw().tp_moe_route_bwd(tokens, E, k, _ptr(logits, "logits", torch.float32),
+                                _ptr(expert_idx, "expert_idx", torch.int32), _ptr(dgates, "dgates", torch.float32),
+                                _ptr(d_logits, "d_logits", torch.float32), _stream(stream))
+    _check(rc, "tp_moe_route_bwd")
 
 
 def tp_bias_grad(dy, db, workspace, stream=None):

@@ -555,6 +555,88 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   return TP_OK;
 }
 
+int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows, int H,
+                             int F_group, int dtype, const void* X_perm, const void* W1_r, const void* W2_r,
+                             const void* A1_r, const void* Y_r, const void* dZ_perm, void* dX_perm, void* dW1_r,
+                             void* db1_r, void* dW2_r, void* workspace, size_t workspace_bytes, void* stream) {
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, rows, H, F_group, dtype, &g);
+  if (st) return st;
+  TP_CHECK(n_groups >= 1 && n_groups <= 65535, TP_EINVAL, "n_groups %d out of range", n_groups);
+  NEED4(group_offsets, "group_offsets", n_groups + 1);
+  NEED(X_perm, "X_perm", (long)rows); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1); NEED(A1_r, "A1_r", (long)rows);
+  NEED(Y_r, "Y_r", (long)rows); NEED(dZ_perm, "dZ_perm", (long)rows); NEED(dX_perm, "dX_perm", (long)rows);
+  NEED(dW1_r, "dW1_r", 1); NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1);
+  const size_t plan = align256(grouped_ws_bytes(n_groups));
+  const size_t need = plan + align256((size_t)rows * g.Fr * (dtype == TP_BF16 ? 2 : 4));
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  TP_TRY(launch_mlp_grouped_bwd(dtype, n_groups, group_offsets, rows, H, g.Fr, X_perm, W1_r, W2_r, A1_r, Y_r, dZ_perm,
+                                (char*)workspace + plan, dX_perm, dW1_r, db1_r, dW2_r, workspace, (hipStream_t)stream),
+         "grouped mlp backward");
+  return TP_OK;
+}
+
+static size_t moe_bwd_ws(int rows, int H, int Fr, int E, int dtype) {
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  return align256(grouped_ws_bytes(E)) + align256((size_t)rows * Fr * es) + 2 * align256((size_t)rows * H * es);
+}
+
+int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
+                     const void* X, const float* gates, const int* group_offsets, const int* token_row,
+                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r, const void* Z_r,
+                     const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r, void* dW2_r,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  TP_CHECK(tokens >= 0 && top_k >= 1 && (long)tokens * top_k <= INT_MAX / 4, TP_EINVAL,
+           "tokens %d, top_k %d out of range", tokens, top_k);
+  TP_CHECK(n_experts >= 1 && n_experts <= 65535, TP_EINVAL, "n_experts %d out of range", n_experts);
+  TP_CHECK(top_k <= n_experts, TP_EINVAL, "top_k %d > n_experts %d", top_k, n_experts);
+  const int rows = tokens * top_k;
+  MlpGeom g;
+  int st = mlp_geom(tp_size, rank, rows, H, F_expert, dtype, &g);
+  if (st) return st;
+  const long n = (long)rows;
+  NEED(X, "X", (long)tokens * H); NEED4(gates, "gates", n); NEED4(group_offsets, "group_offsets", n_experts + 1);
+  NEED4(token_row, "token_row", n); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1); NEED(A1_r, "A1_r", n);
+  NEED(Y_r, "Y_r", n); NEED(Z_r, "Z_r", n * H); NEED(d_out, "d_out", (long)tokens * H);
+  NEED(dX_r, "dX_r", (long)tokens * H); NEED4(dgates_r, "dgates_r", n); NEED(dW1_r, "dW1_r", 1);
+  NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1);
+  const size_t need = moe_bwd_ws(rows, H, g.Fr, n_experts, dtype);
+  TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  char* w = (char*)workspace;
+  char* plan = w;
+  char* dA1 = plan + align256(grouped_ws_bytes(n_experts));
+  char* Xp = dA1 + align256((size_t)rows * g.Fr * es);
+  char* dZp = Xp + align256((size_t)rows * H * es);     // later also dX_perm (its reads come first)
+  hipStream_t s = (hipStream_t)stream;
+  TP_TRY(launch_moe_combine_bwd(dtype, tokens, top_k, H, d_out, X, Z_r, gates, token_row, rows, dZp, Xp, dgates_r, s),
+         "moe combine backward");
+  TP_TRY(launch_mlp_grouped_bwd(dtype, n_experts, group_offsets, rows, H, g.Fr, Xp, W1_r, W2_r, A1_r, Y_r, dZp, dA1,
+                                dZp, dW1_r, db1_r, dW2_r, plan, s), "moe experts backward");
+  TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dZp, nullptr, token_row, rows, dX_r, s), "moe dispatch backward");
+  return TP_OK;
+}
+
+int tp_moe_route_bwd(int tokens, int n_experts, int top_k, const float* logits, const int* expert_idx,
+                     const float* dgates, float* d_logits, void* stream) {
+  TP_CHECK(tokens >= 0, TP_EINVAL, "tokens %d < 0", tokens);
+  TP_CHECK(n_experts >= 1 && n_experts <= moe_max_experts(), TP_EUNSUPPORTED, "n_experts %d outside [1, %d]",
+           n_experts, moe_max_experts());
+  TP_CHECK(top_k >= 1 && top_k <= n_experts && top_k <= moe_max_top_k(), TP_EINVAL,
+           "top_k %d outside [1, min(n_experts, %d)]", top_k, moe_max_top_k());
+  TP_CHECK((long)tokens * n_experts <= INT_MAX, TP_EINVAL, "too many tokens");
+  const long n = (long)tokens * top_k;
+  NEED4(logits, "logits", (long)tokens * n_experts); NEED4(expert_idx, "expert_idx", n);
+  NEED4(dgates, "dgates", n); NEED4(d_logits, "d_logits", (long)tokens * n_experts);
+  TP_TRY(launch_moe_route_bwd(tokens, n_experts, top_k, logits, expert_idx, dgates, d_logits, (hipStream_t)stream),
+         "moe route backward");
+  return TP_OK;
+}
+
 int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, int transpose, unsigned char* q,
                     float* descale, void* workspace, size_t workspace_bytes, void* stream) {
   TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
@@ -627,6 +709,13 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   if (strcmp(fn, "tp_moe_route") == 0) {
     if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > moe_max_experts()) return 0;
     return align256(moe_route_ws_bytes(B * S, n_heads));
+  }
+  if (strcmp(fn, "tp_mlp_grouped_shard_bwd") == 0 || strcmp(fn, "tp_moe_shard_bwd") == 0) {
+    MlpGeom mg;
+    if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > 65535) return 0;
+    if (mlp_geom(tp_size, rank, B * S, H, F, dtype, &mg)) return 0;
+    if (strcmp(fn, "tp_moe_shard_bwd") == 0) return moe_bwd_ws(B * S, H, mg.Fr, n_heads, dtype);
+    return align256(grouped_ws_bytes(n_heads)) + align256((size_t)B * S * mg.Fr * (dtype == TP_BF16 ? 2 : 4));
   }
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0 || strcmp(fn, "tp_moe_shard_fwd") == 0) {
     if (n_heads < 1 || n_heads > (1 << 20)) return 0;

@@ -383,7 +383,7 @@ struct GroupedArgs {
 };
 
 
-template <class Cfg, int EPI, bool GATHER>
+template <class Cfg, int EPI, bool GATHER, bool BKM>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void gemm_bf16_grouped_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -414,9 +414,45 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   d.C = (bf16*)g.d.C + (long)row0 * g.d.ldc;
   if (g.d.C2) d.C2 = (bf16*)g.d.C2 + (long)row0 * g.d.ldc;
   if (g.d.bias) d.bias = (const bf16*)g.d.bias + (long)e * g.bias_stride;
+  if (g.d.aux) d.aux = (const bf16*)g.d.aux + (long)row0 * g.d.ld_aux;
   // k loops start at k-tile mt (mod the count): the row tiles of the same expert stream their rows
   // of A through different memory channels at the same moment (measured: fc1 2x faster)
-  gemm_tile<Cfg, true, false, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
+  gemm_tile<Cfg, true, BKM, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
+}
+
+// Grouped weight-gradient GEMM: expert e's block C_e [M, N] (at e·c_stride elements) = op(A_e)·op(B_e)
+// where A_e and B_e are the rows [off[e], off[e+1]) of two row-major matrices, both read MN-major
+// (A element (m, k) at A[(off[e] + k)·lda + m], B element (k, n) at B[(off[e] + k)·ldb + n]): the
+// experts split the k dimension, so an expert without rows gets a zero block.  The loads mask rows
+// past the expert's count, so K needs no alignment.  One workgroup per (expert, m-tile, n-tile),
+// numbered expert-major and handed out in contiguous runs per XCD as in the plain kernel: the
+// tiles an XCD runs together share one expert's rows in its L2.
+struct GroupedKArgs {
+  GemmDesc d;          // A, B, C, lda, ldb, ldc, M, N; K unused
+  const int* off;      // [groups + 1] sanitised row offsets (device)
+  int groups;
+  long c_stride;
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
+void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long per = (long)tiles_m * tiles_n, nwg = per * g.groups;
+  long wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int e = (int)(wg / per);
+  const int local = (int)(wg % per);
+  const int tm = local % tiles_m, tn = local / tiles_m;
+  GemmDesc d = g.d;
+  const int k0 = g.off[e];
+  d.K = g.off[e + 1] - k0;
+  d.A = (const bf16*)g.d.A + (long)k0 * g.d.lda;
+  d.B = (const bf16*)g.d.B + (long)k0 * g.d.ldb;
+  d.C = (bf16*)g.d.C + (long)e * g.c_stride;
+  gemm_tile<Cfg, false, false, EPI_STORE>(d, tm * Cfg::BM, tn * Cfg::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
@@ -521,13 +557,19 @@ static hipError_t grouped_t(const GroupedArgs& g, int max_mtiles, hipStream_t s)
   const long tiles = (long)max_mtiles * ((g.d.N + Cfg::BN - 1) / Cfg::BN);
   if (tiles > 0x7ffffff0L) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
-  if (g.d.a_rows) {
+  if (!g.d.a_kmajor) return hipErrorNotSupported;
+  if (g.d.b_kmajor) {            // the backward's dY·Wᵀ forms: GeLU' or plain
+    if (g.d.a_rows) return hipErrorNotSupported;
+    if (g.d.epi == EPI_DGELU) gemm_bf16_grouped_kernel<Cfg, EPI_DGELU, false, true><<<grid, Cfg::NT, 0, s>>>(g);
+    else if (g.d.epi == EPI_STORE) gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, true><<<grid, Cfg::NT, 0, s>>>(g);
+    else return hipErrorNotSupported;
+  } else if (g.d.a_rows) {
     if (g.d.epi != EPI_BIAS_GELU || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
-    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, true><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, true, false><<<grid, Cfg::NT, 0, s>>>(g);
   } else if (g.d.epi == EPI_BIAS_GELU) {
-    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, false><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, false, false><<<grid, Cfg::NT, 0, s>>>(g);
   } else if (g.d.epi == EPI_STORE) {
-    gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, false><<<grid, Cfg::NT, 0, s>>>(g);
   } else {
     return hipErrorNotSupported;
   }
@@ -540,6 +582,26 @@ hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int
   GroupedArgs g{d, off, prefix, groups, b_stride, bias_stride};
   if (max_mtiles <= 0 || d.N <= 0) return hipSuccess;
   return grouped_t<C0>(g, max_mtiles, s);
+}
+
+// Whether the tiled grouped weight-gradient kernel takes these operands (K is free: see the kernel).
+bool gemm_bf16_grouped_k_eligible(const GemmDesc& d) {
+  if (d.dtype != DT_BF16 || d.M <= 0 || d.N <= 0 || d.a_kmajor || d.b_kmajor) return false;
+  if ((d.M | d.N) & 7) return false;
+  if ((d.lda | d.ldb | d.ldc) & 7) return false;
+  if (d.lda > (1L << 22) || d.ldb > (1L << 22)) return false;
+  return ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) == 0;
+}
+
+hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
+  using Cfg = C0;
+  const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
+  const long nwg = (long)tiles_m * tiles_n * groups;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  GroupedKArgs g{d, off, groups, c_stride};
+  gemm_bf16_grouped_k_kernel<Cfg><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 }  // namespace tp

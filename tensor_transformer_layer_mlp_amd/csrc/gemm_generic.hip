@@ -129,7 +129,22 @@ __global__ __launch_bounds__(256) void gemm_generic_grouped_kernel(GemmDesc g, c
   d.C = (T*)g.C + (long)row0 * g.ldc;
   if (g.C2) d.C2 = (T*)g.C2 + (long)row0 * g.ldc;
   if (g.bias) d.bias = (const T*)g.bias + (long)e * bias_stride;
+  if (g.aux) d.aux = (const T*)g.aux + (long)row0 * g.ld_aux;
   generic_tile<T, EPI>(d, 0, blockIdx.x * GBN);
+}
+
+// Grouped weight-gradient form (see the tiled kernel): blockIdx.z is the expert, whose rows
+// [off[e], off[e+1]) of A and B form the k range; its C block sits at e·c_stride.
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_generic_grouped_k_kernel(GemmDesc g, const int* off, long c_stride) {
+  const int e = blockIdx.z;
+  GemmDesc d = g;
+  const int k0 = off[e];
+  d.K = off[e + 1] - k0;
+  d.A = (const T*)g.A + (long)k0 * g.lda;
+  d.B = (const T*)g.B + (long)k0 * g.ldb;
+  d.C = (T*)g.C + (long)e * c_stride;
+  generic_tile<T, EPI_STORE>(d, blockIdx.y * GBM, blockIdx.x * GBN);
 }
 
 template <typename T>
@@ -153,6 +168,8 @@ hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int
     gemm_generic_grouped_kernel<T, EPI_BIAS_GELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
   else if (d.epi == EPI_STORE)
     gemm_generic_grouped_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+  else if (d.epi == EPI_DGELU)
+    gemm_generic_grouped_kernel<T, EPI_DGELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
   else
     return hipErrorNotSupported;
   return hipGetLastError();
@@ -169,6 +186,15 @@ hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const 
   return d.dtype == DT_BF16
              ? launch_generic_grouped_t<bf16>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s)
              : launch_generic_grouped_t<float>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s);
+}
+
+hipError_t launch_gemm_generic_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
+  if (d.M <= 0 || d.N <= 0 || groups <= 0) return hipSuccess;
+  if ((d.M + GBM - 1) / GBM > 65535 || groups > 65535) return hipErrorInvalidValue;
+  dim3 grid((d.N + GBN - 1) / GBN, (d.M + GBM - 1) / GBM, groups);
+  if (d.dtype == DT_BF16) gemm_generic_grouped_k_kernel<bf16><<<grid, 256, 0, s>>>(d, off, c_stride);
+  else gemm_generic_grouped_k_kernel<float><<<grid, 256, 0, s>>>(d, off, c_stride);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t s) {

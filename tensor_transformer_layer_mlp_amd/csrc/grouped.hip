@@ -23,6 +23,9 @@ hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const 
 int gemm_bf16_grouped_bm(int K);
 int gemm_generic_grouped_bm();
 bool gemm_bf16_eligible(const GemmDesc& d);
+bool gemm_bf16_grouped_k_eligible(const GemmDesc& d);
+hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s);
+hipError_t launch_gemm_generic_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s);
 
 namespace {
 
@@ -86,6 +89,27 @@ __global__ __launch_bounds__(PLAN_T) void grouped_plan_kernel(const int* __restr
     carry_o = sh[PLAN_T - 1];
     __syncthreads();
   }
+}
+
+// db[e][c] = Σ_{r in [off[e], off[e+1])} dA[r·cols + c]: a workgroup per (expert, 64 columns); four
+// row phases of 64 threads each sum every fourth row (eight loads in flight per thread), then the
+// four partials are added in phase order, so the result does not depend on timing.
+template <typename T>
+__global__ __launch_bounds__(256) void grouped_colsum_kernel(const T* __restrict__ dA, int cols,
+                                                             const int* __restrict__ off, T* __restrict__ db) {
+  __shared__ float part[4][64];
+  const int e = blockIdx.y, lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int r0 = off[e], r1 = off[e + 1];
+  float acc = 0.f;
+  if (c < cols) {
+#pragma unroll 8
+    for (int r = r0 + ph; r < r1; r += 4) acc += to_f32(dA[(long)r * cols + c]);
+  }
+  part[ph][lane] = acc;
+  __syncthreads();
+  if (ph == 0 && c < cols)
+    db[(long)e * cols + c] = from_f32<T>(((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]);
 }
 
 }  // namespace
@@ -152,6 +176,97 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   }
   ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
   return launch_gemm_generic_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
+}
+
+// Backward of launch_mlp_grouped on expert-sorted operands, expert by expert (rows [off[e], off[e+1])):
+//   dA1 = (dZ·W2[e]ᵀ) ∘ GeLU'(A1)      grouped, rows split by expert, GeLU' in the epilogue
+//   dW2[e] = Y_eᵀ·dZ_e                  grouped weight gradient, the expert's rows as k
+//   db1[e] = Σ_rows dA1_e               segmented column sum
+//   dW1[e] = X_eᵀ·dA1_e                 grouped weight gradient
+//   dX = dA1·W1[e]ᵀ                     grouped, rows split by expert
+// in that order on one stream, so dX may alias dZ (both reads of dZ come first).  An expert without
+// rows gets zero weight and bias gradients.  ws: grouped_ws_bytes(groups).
+hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int rows, int H, int Fr, const void* X,
+                                  const void* W1, const void* W2, const void* A1, const void* Y, const void* dZ,
+                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s) {
+  if (groups <= 0) return hipSuccess;
+  int* off_s = (int*)ws;
+  int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
+  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of the dX GEMM's
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+
+  GemmDesc ga;                                // dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1)
+  memset(&ga, 0, sizeof(ga));
+  ga.M = rows; ga.N = Fr; ga.K = H; ga.dtype = dtype;
+  ga.A = dZ; ga.lda = H; ga.a_kmajor = true;
+  ga.B = W2; ga.ldb = H; ga.b_kmajor = true;
+  ga.C = dA1; ga.ldc = Fr; ga.epi = EPI_DGELU; ga.aux = A1; ga.ld_aux = Fr;
+  GemmDesc gx = ga;                           // dX = dA1·W1ᵀ
+  gx.N = H; gx.K = Fr; gx.A = dA1; gx.lda = Fr; gx.B = W1; gx.ldb = Fr; gx.C = dX; gx.ldc = H;
+  gx.epi = EPI_STORE; gx.aux = nullptr; gx.ld_aux = 0;
+  GemmDesc gw2;                               // dW2[e] = Y_eᵀ·dZ_e   [Fr, H]
+  memset(&gw2, 0, sizeof(gw2));
+  gw2.M = Fr; gw2.N = H; gw2.dtype = dtype; gw2.epi = EPI_STORE;
+  gw2.A = Y; gw2.lda = Fr; gw2.a_kmajor = false;
+  gw2.B = dZ; gw2.ldb = H; gw2.b_kmajor = false;
+  gw2.C = dW2; gw2.ldc = H;
+  GemmDesc gw1 = gw2;                         // dW1[e] = X_eᵀ·dA1_e  [H, Fr]
+  gw1.M = H; gw1.N = Fr; gw1.A = X; gw1.lda = H; gw1.B = dA1; gw1.ldb = Fr; gw1.C = dW1; gw1.ldc = Fr;
+
+  const bool tiled = rows > 0 && gemm_bf16_eligible(ga) && gemm_bf16_eligible(gx);
+  const int bm1 = tiled ? gemm_bf16_grouped_bm(ga.K) : gemm_generic_grouped_bm();
+  const int bm2 = tiled ? gemm_bf16_grouped_bm(gx.K) : gemm_generic_grouped_bm();
+  const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
+  if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
+  {
+    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
+    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const double fl = 2.0 * rows * (double)Fr * H;
+  const double wts = es * (double)groups * H * Fr;
+  hipError_t e;
+  if (rows > 0) {
+    ProfScope p(tiled ? "gemm_bf16_grouped<dZ.W2t, dgelu>" : "gemm_generic_grouped<dZ.W2t, dgelu>", s, fl,
+                es * (2.0 * rows * H + 3.0 * rows * Fr) + wts);
+    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s)
+              : launch_gemm_generic_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s);
+    if (e != hipSuccess) return e;
+  }
+  {
+    const bool t2 = gemm_bf16_grouped_k_eligible(gw2);
+    ProfScope p(t2 ? "gemm_bf16_grouped_k<Yt.dZ>" : "gemm_generic_grouped_k<Yt.dZ>", s, fl,
+                es * ((double)rows * Fr + (double)rows * H) + wts);
+    e = t2 ? launch_gemm_bf16_grouped_k(gw2, off_s, groups, (long)Fr * H, s)
+           : launch_gemm_generic_grouped_k(gw2, off_s, groups, (long)Fr * H, s);
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
+    dim3 grid((Fr + 63) / 64, groups);
+    if (groups > 65535) return hipErrorInvalidValue;
+    if (dtype == DT_BF16) grouped_colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
+    else grouped_colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dA1, Fr, off_s, (float*)db1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const bool t1 = gemm_bf16_grouped_k_eligible(gw1);
+    ProfScope p(t1 ? "gemm_bf16_grouped_k<Xt.dA1>" : "gemm_generic_grouped_k<Xt.dA1>", s, fl,
+                es * ((double)rows * H + (double)rows * Fr) + wts);
+    e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
+           : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);
+    if (e != hipSuccess) return e;
+  }
+  if (rows > 0) {
+    ProfScope p(tiled ? "gemm_bf16_grouped<dA1.W1t>" : "gemm_generic_grouped<dA1.W1t>", s, fl,
+                es * ((double)rows * Fr + (double)rows * H) + wts);
+    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s)
+              : launch_gemm_generic_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tp

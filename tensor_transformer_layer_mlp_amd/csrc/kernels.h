@@ -78,6 +78,12 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
                               void* A1, void* Y, void* ws, hipStream_t s, const int* row_token = nullptr,
                               int tokens = 0);
 
+// Backward of launch_mlp_grouped on expert-sorted operands (dX may alias dZ); dA1 [rows, Fr] is
+// caller scratch; ws as for the forward.  dW1 [groups, H, Fr], db1 [groups, Fr], dW2 [groups, Fr, H].
+hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int rows, int H, int Fr, const void* X,
+                                  const void* W1, const void* W2, const void* A1, const void* Y, const void* dZ,
+                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s);
+
 // FP8 (OCP E4M3) quantisation with one scale per tensor and the GEMM on codes (see fp8.hip).
 size_t fp8_quantize_ws_bytes();
 // fmt: 0 E4M3, 1 E5M2.
@@ -94,7 +100,14 @@ int moe_max_top_k();
 size_t moe_route_ws_bytes(int tokens, int experts);
 hipError_t launch_moe_route(int tokens, int experts, int top_k, const float* logits, float* gates, int* expert_idx,
                             int* group_offsets, int* row_token, int* token_row, int* ws, hipStream_t s);
+// gates nullable: unit gates (the dispatch's backward).
 hipError_t launch_moe_combine(int dtype, int tokens, int top_k, int H, const void* Z, const float* gates,
                               const int* token_row, int rows, void* out, hipStream_t s);
+// The combine's backward: dZ[r] = gate·d_out[t], Xp[r] = X[t] (Xp nullable), dgates = ⟨d_out[t], Z[r]⟩.
+hipError_t launch_moe_combine_bwd(int dtype, int tokens, int k, int H, const void* d_out, const void* X,
+                                  const void* Z, const float* gates, const int* token_row, int rows, void* dZ,
+                                  void* Xp, float* dgates, hipStream_t s);
+hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, const int* experts,
+                                const float* dgates, float* d_logits, hipStream_t s);
 
 }  // namespace tp

@@ -18,7 +18,14 @@
 //                       token_row ((token, j) -> row).  Integer work only: exact and deterministic.
 //   moe_combine_kernel  one workgroup per token: out[t] = Σ_j gate[t, j]·Z[token_row[t, j]] in fp32,
 //                       j in order; 16-byte loads of the k rows (HBM-bound).  Rows outside
-//                       [0, rows) contribute nothing.
+//                       [0, rows) contribute nothing.  Without gates every gate is 1 (the
+//                       dispatch's backward: a token's input gradient sums its k rows').
+//   moe_combine_bwd_kernel  one workgroup per token, the combine's backward: for each of its k rows
+//                       dZ[r] = gate·d_out[t], the dispatched copy X_perm[r] = X[t], and the gate
+//                       gradient ⟨d_out[t], Z[r]⟩ (fp32, reduced in a fixed order).
+//   moe_route_bwd_kernel    one wave per token: the softmax again from the fp32 logits, then
+//                       d_logits[e] = p_e·(dg(e) − Σ_j dg_j·p_{i_j}), dg(e) the gradient of the gate
+//                       that chose e (0 if none did).
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(int k, int H, const T*
     for (int j = 0; j < k; ++j) {
       const int r = token_row[t * k + j];
       if (r < 0 || r >= rows) continue;
-      const float g = gates[t * k + j];
+      const float g = gates ? gates[t * k + j] : 1.f;
       const T* src = Z + (long)r * H + c;
       if constexpr (V == 8) {
         const bf16x8 z = *(const bf16x8*)src;
@@ -209,6 +216,136 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(int k, int H, const T*
       *dst = from_f32<T>(acc[0]);
     }
   }
+}
+
+// V consecutive elements at p as fp32 (V = 8: bf16 16-byte vector, 4: fp32 vector, 1: scalar).
+template <typename T, int V>
+__device__ __forceinline__ void load_v(const T* p, float (&v)[V]) {
+  if constexpr (V == 8) {
+    const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (float)x[q];
+  } else if constexpr (V == 4) {
+    const f32x4 x = *(const f32x4*)p;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = x[q];
+  } else {
+    v[0] = to_f32(*p);
+  }
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void store_v(T* p, const float (&v)[V]) {
+  if constexpr (V == 8) {
+    bf16x8 x;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = (bf16)v[q];
+    *(bf16x8*)p = x;
+  } else if constexpr (V == 4) {
+    *(f32x4*)p = (f32x4){v[0], v[1], v[2], v[3]};
+  } else {
+    *p = from_f32<T>(v[0]);
+  }
+}
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void moe_combine_bwd_kernel(int k, int H, const T* __restrict__ d_out,
+                                                              const T* __restrict__ X, const T* __restrict__ Z,
+                                                              const float* __restrict__ gates,
+                                                              const int* __restrict__ token_row, int rows,
+                                                              T* __restrict__ dZ, T* __restrict__ Xp,
+                                                              float* __restrict__ dgates) {
+  __shared__ float red[4];
+  const long t = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int j = 0; j < k; ++j) {
+    const int r = token_row[t * k + j];
+    const bool ok = r >= 0 && r < rows;
+    const float g = gates[t * k + j];
+    float dot = 0.f;
+    if (ok) {
+      for (int c = V * threadIdx.x; c < H; c += V * 256) {
+        float o[V], z[V], dz[V];
+        load_v<T, V>(d_out + t * H + c, o);
+        load_v<T, V>(Z + (long)r * H + c, z);
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          dot += o[q] * z[q];
+          dz[q] = g * o[q];
+        }
+        store_v<T, V>(dZ + (long)r * H + c, dz);
+        if (Xp) {
+          float x[V];
+          load_v<T, V>(X + t * H + c, x);
+          store_v<T, V>(Xp + (long)r * H + c, x);
+        }
+      }
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, 64);
+    if (lane == 0) red[w] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) dgates[t * k + j] = ok ? ((red[0] + red[1]) + red[2]) + red[3] : 0.f;
+    __syncthreads();
+  }
+}
+
+constexpr int RBWD_TOKENS = 16;   // tokens (waves) per workgroup of the router backward
+
+template <int EPL>
+__global__ __launch_bounds__(64 * RBWD_TOKENS) void moe_route_bwd_kernel(int tokens, int E, int k,
+                                                                         const float* __restrict__ logits,
+                                                                         const int* __restrict__ experts,
+                                                                         const float* __restrict__ dgates,
+                                                                         float* __restrict__ d_logits) {
+  const int lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * RBWD_TOKENS + (threadIdx.x >> 6);
+  if (t >= tokens) return;                   // whole waves leave; no workgroup barrier follows
+  const float* row = logits + t * E;
+  float v[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    v[i] = (lane + 64 * i) < E ? expf(v[i] - m) : 0.f;
+    z += v[i];
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) z += __shfl_xor(z, sh, 64);
+  const float inv = 1.f / z;
+  // lane j < k holds the j-th choice and its gate gradient; s = Σ_j dg_j·p_{i_j}
+  const int my_e = lane < k ? experts[t * k + lane] : -1;
+  const float my_g = lane < k ? dgates[t * k + lane] : 0.f;
+  float sj = (my_e >= 0 && my_e < E) ? my_g * (expf(row[my_e] - m) * inv) : 0.f;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) sj += __shfl_xor(sj, sh, 64);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    float dg = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(my_e, j, 64);
+      const float gj = __shfl(my_g, j, 64);
+      if (ej == e) dg = gj;
+    }
+    if (e < E) d_logits[t * E + e] = v[i] * inv * (dg - sj);
+  }
+}
+
+template <int EPL>
+hipError_t route_bwd_t(int tokens, int E, int k, const float* logits, const int* experts, const float* dgates,
+                       float* d_logits, hipStream_t s) {
+  const int blocks = (tokens + RBWD_TOKENS - 1) / RBWD_TOKENS;
+  moe_route_bwd_kernel<EPL><<<blocks, 64 * RBWD_TOKENS, 0, s>>>(tokens, E, k, logits, experts, dgates, d_logits);
+  return hipGetLastError();
 }
 
 template <int EPL>
@@ -278,6 +415,46 @@ hipError_t launch_moe_combine(int dtype, int tokens, int k, int H, const void* Z
     else moe_combine_kernel<float, 1><<<tokens, 256, 0, s>>>(k, H, (const float*)Z, gates, token_row, rows, (float*)out);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_moe_combine_bwd(int dtype, int tokens, int k, int H, const void* d_out, const void* X,
+                                  const void* Z, const float* gates, const int* token_row, int rows, void* dZ,
+                                  void* Xp, float* dgates, hipStream_t s) {
+  if (tokens <= 0) return hipSuccess;
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  const double n = (double)tokens * k;
+  ProfScope p(Xp ? "moe_combine_bwd<dispatch X>" : "moe_combine_bwd", s, 2.0 * n * H,
+              es * ((double)tokens * H * (Xp ? 2.0 : 1.0) + n * H * (Xp ? 3.0 : 2.0)) + 12.0 * n);
+  if (dtype == DT_BF16) {
+    if (H % 8 == 0)
+      moe_combine_bwd_kernel<bf16, 8><<<tokens, 256, 0, s>>>(k, H, (const bf16*)d_out, (const bf16*)X, (const bf16*)Z,
+                                                              gates, token_row, rows, (bf16*)dZ, (bf16*)Xp, dgates);
+    else
+      moe_combine_bwd_kernel<bf16, 1><<<tokens, 256, 0, s>>>(k, H, (const bf16*)d_out, (const bf16*)X, (const bf16*)Z,
+                                                              gates, token_row, rows, (bf16*)dZ, (bf16*)Xp, dgates);
+  } else {
+    if (H % 4 == 0)
+      moe_combine_bwd_kernel<float, 4><<<tokens, 256, 0, s>>>(k, H, (const float*)d_out, (const float*)X,
+                                                               (const float*)Z, gates, token_row, rows, (float*)dZ,
+                                                               (float*)Xp, dgates);
+    else
+      moe_combine_bwd_kernel<float, 1><<<tokens, 256, 0, s>>>(k, H, (const float*)d_out, (const float*)X,
+                                                               (const float*)Z, gates, token_row, rows, (float*)dZ,
+                                                               (float*)Xp, dgates);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, const int* experts,
+                                const float* dgates, float* d_logits, hipStream_t s) {
+  if (E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || tokens < 0) return hipErrorInvalidValue;
+  if (tokens == 0) return hipSuccess;
+  ProfScope p("moe_route_bwd", s, 6.0 * tokens * E, 8.0 * tokens * E + 8.0 * tokens * k);
+  if (E <= 64) return route_bwd_t<1>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 128) return route_bwd_t<2>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 256) return route_bwd_t<4>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 512) return route_bwd_t<8>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  return route_bwd_t<16>(tokens, E, k, logits, experts, dgates, d_logits, s);
 }
 
 }  // namespace tp
