@@ -198,11 +198,15 @@ def moe_grouped(bd, torch, steps, warmup):
 
 
 def moe_layer(bd, torch, steps, warmup):
-    """The whole MoE expert block of rank 0 on the 128-expert workload, from router logits to the
-    combined partial: tp_moe_route (top-8 of 128, dispatch order) then tp_moe_shard_fwd (fc1 with
-    the dispatch gathered from X inside its operand loads, GeLU, fc2, gate-weighted combine).
-    Algorithmic bytes: logits, X, the expert weights, Y written and read, Z written and read back by
-    the combine, out written."""
+    """The whole MoE expert block of rank 0 on the 128-expert workload, forward and backward timed
+    apart.  Forward, from router logits to the combined partial: tp_moe_route (top-8 of 128,
+    dispatch order) then tp_moe_shard_fwd (fc1 with the dispatch gathered from X inside its operand
+    loads, GeLU, fc2, gate-weighted combine; A1 kept for the backward).  Backward, from the output
+    gradient: tp_moe_shard_bwd (the combine's backward with the gate gradients, the experts' grouped
+    backward, the dispatch's backward) then tp_moe_route_bwd (router logit gradient).
+    Algorithmic bytes, forward: logits, X, the expert weights, A1 and Y written, Y read, Z written
+    and read back by the combine, out written.  Backward: d_out, X, Z, A1, Y and the weights read,
+    dA1 written and read twice, dX, the weight gradients and the small gate / logit arrays."""
     from tensor_transformer_layer_mlp_amd.configs import MOE_E128 as mw
     tp, rank, E, k, H, tokens = mw.tp_size, 0, mw.n_experts, mw.top_k, mw.H, mw.tokens
     _, Fr = bd.tp_shard_range(mw.F_expert, tp, rank)
@@ -214,43 +218,64 @@ def moe_layer(bd, torch, steps, warmup):
     logits = torch.randn(tokens, E, generator=g, device="cuda")
     X = r(tokens, H)
     W1, b1, W2 = r(E, H, Fr, std=mw.w_std), r(E, Fr, std=mw.w_std), r(E, Fr, H, std=mw.w_std)
+    d_out = r(tokens, H, std=1e-2)
     i32 = dict(dtype=torch.int32, device="cuda")
     gates, ex, off = torch.empty(tokens, k, device="cuda"), torch.empty(tokens, k, **i32), torch.empty(E + 1, **i32)
     rt, tr = torch.empty(n, **i32), torch.empty(tokens, k, **i32)
-    out, Z, Y = torch.empty(tokens, H, dtype=bf, device="cuda"), torch.empty(n, H, dtype=bf, device="cuda"), \
-        torch.empty(n, Fr, dtype=bf, device="cuda")
+    e = lambda *sh: torch.empty(*sh, dtype=bf, device="cuda")  # noqa: E731
+    out, Z, Y, A1 = e(tokens, H), e(n, H), e(n, Fr), e(n, Fr)
+    dX, dW1, db1, dW2 = e(tokens, H), e(E, H, Fr), e(E, Fr), e(E, Fr, H)
+    dg, dlog = torch.empty(tokens, k, device="cuda"), torch.empty(tokens, E, device="cuda")
     ws = bd.workspace("tp_moe_shard_fwd", tp, rank, 1, n, H, E, mw.F_expert, bf)
     wsr = bd.workspace("tp_moe_route", tp, rank, 1, tokens, H, E, mw.F_expert, bf)
+    wsb = bd.workspace("tp_moe_shard_bwd", tp, rank, 1, n, H, E, mw.F_expert, bf)
 
-    def call():
+    def fwd():
         bd.tp_moe_route(tokens, E, k, logits, gates, ex, off, rt, tr, wsr)
-        bd.tp_moe_shard_fwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, b1, W2, out, Z, None,
+        bd.tp_moe_shard_fwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, b1, W2, out, Z, A1,
                             Y, ws)
-    for _ in range(warmup):
-        call()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps):
-        call()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    bd.tp_prof_collect()
-    bd.tp_prof_enable(True)
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    bd.tp_prof_enable(False)
-    kernels = {tag: kernel_roofline(c, kms, fl, by, steps) for tag, (c, kms, fl, by) in bd.tp_prof_collect().items()}
-    byts = 4.0 * tokens * E + 2.0 * tokens * H + 2.0 * (2 * E * H * Fr + E * Fr) + 2.0 * 2 * n * Fr + \
+
+    def bwd():
+        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, tr, W1, W2, A1, Y, Z, d_out, dX,
+                            dg, dW1, db1, dW2, wsb)
+        bd.tp_moe_route_bwd(logits, ex, dg, dlog)
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        bd.tp_prof_collect()
+        bd.tp_prof_enable(True)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        bd.tp_prof_enable(False)
+        return ms, {tag: kernel_roofline(c, kms, fl, by, steps) for tag, (c, kms, fl, by) in bd.tp_prof_collect().items()}
+
+    fwd()
+    ms, kernels = timed(fwd)
+    byts = 4.0 * tokens * E + 2.0 * tokens * H + 2.0 * (2 * E * H * Fr + E * Fr) + 2.0 * 3 * n * Fr + \
         2.0 * 2 * n * H + 2.0 * tokens * H
     flop = 4.0 * n * H * Fr + 2.0 * n * H
     res = {"workload": mw.name + "_rank0_route_experts_combine", "tokens": tokens, "rows": n, "ms": round(ms, 4),
            "tflops": round(flop / ms / 1e9, 2), "gb_per_s": round(byts / ms / 1e6, 1),
            "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3),
            "kernels": kernels}
-    del X, W1, W2, Z, Y, out
+    ms_b, kernels_b = timed(bwd)
+    byts_b = 2.0 * (2 * tokens * H + n * H + 2 * n * Fr + 2 * E * H * Fr) + 2.0 * 3 * n * Fr + \
+        2.0 * (tokens * H + 2 * E * H * Fr + E * Fr) + 4.0 * (2 * tokens * k + 2 * tokens * E)
+    flop_b = 8.0 * n * H * Fr + 2.0 * n * H
+    res["bwd"] = {"ms": round(ms_b, 4), "tflops": round(flop_b / ms_b / 1e9, 2),
+                  "gb_per_s": round(byts_b / ms_b / 1e6, 1), "hbm_frac": round(byts_b / ms_b / 1e6 / PEAK_HBM_GBS, 4),
+                  "gbyte_per_call": round(byts_b / 1e9, 3), "kernels": kernels_b}
+    del X, W1, W2, Z, Y, A1, out, dX, dW1, dW2, d_out, ws, wsb
     torch.cuda.empty_cache()
     return res
 
