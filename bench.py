@@ -236,8 +236,8 @@ def moe_layer(bd, torch, steps, warmup):
                             Y, ws)
 
     def bwd():
-        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, tr, W1, W2, A1, Y, Z, d_out, dX,
-                            dg, dW1, db1, dW2, wsb)
+        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, W2, A1, Y, Z, d_out,
+                            dX, dg, dW1, db1, dW2, wsb)
         bd.tp_moe_route_bwd(logits, ex, dg, dlog)
 
     def timed(call):

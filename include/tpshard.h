@@ -264,16 +264,18 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
  *                                              gradient, the combine being linear in the partials)
  *   the experts' backward as tp_mlp_grouped_shard_bwd, on X's rows in dispatch order
  *   dX_r[t] = Σ_j dX_perm[row]                 the dispatch's backward (a partial over ranks)
- * Inputs are the forward's: X, gates, group_offsets, token_row from tp_moe_route, A1_r, Y_r, Z_r
- * from tp_moe_shard_fwd (A1_r now required).  token_row must be a permutation of [0, tokens·k), as
- * tp_moe_route writes it; entries outside that range are skipped.  Outputs dW1_r, db1_r, dW2_r as in
- * tp_mlp_grouped_shard_bwd.  workspace: tp_workspace_bytes("tp_moe_shard_bwd", ...) with
- * B·S = tokens·top_k, n_heads = E, F = F_expert (the dispatched X and dZ rows, dA1, the plan). */
+ * Inputs are the forward's: X, gates, group_offsets, row_token, token_row from tp_moe_route, A1_r,
+ * Y_r, Z_r from tp_moe_shard_fwd (A1_r now required).  As in the forward, X's rows are gathered in
+ * dispatch order (row_token) inside the dW1 GEMM's operand loads; indices outside X read as zero
+ * rows.  token_row must be a permutation of [0, tokens·k), as tp_moe_route writes it; entries
+ * outside that range are skipped.  Outputs dW1_r, db1_r, dW2_r as in tp_mlp_grouped_shard_bwd.
+ * workspace: tp_workspace_bytes("tp_moe_shard_bwd", ...) with B·S = tokens·top_k, n_heads = E,
+ * F = F_expert (the dZ rows, dA1, the plan). */
 int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
-                     const void* X, const float* gates, const int* group_offsets, const int* token_row,
-                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r, const void* Z_r,
-                     const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r, void* dW2_r,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     const void* X, const float* gates, const int* group_offsets, const int* row_token,
+                     const int* token_row, const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
+                     const void* Z_r, const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r,
+                     void* dW2_r, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The router's logit gradient from the (complete) gate gradient, the top-k choice held fixed:
  * with p = softmax(logits[t]) and gates[t, j] = p[expert_idx[t, j]],

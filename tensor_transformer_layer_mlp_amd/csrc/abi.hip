@@ -580,14 +580,14 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
 
 static size_t moe_bwd_ws(int rows, int H, int Fr, int E, int dtype) {
   const size_t es = dtype == TP_BF16 ? 2 : 4;
-  return align256(grouped_ws_bytes(E)) + align256((size_t)rows * Fr * es) + 2 * align256((size_t)rows * H * es);
+  return align256(grouped_ws_bytes(E)) + align256((size_t)rows * Fr * es) + align256((size_t)rows * H * es);
 }
 
 int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
-                     const void* X, const float* gates, const int* group_offsets, const int* token_row,
-                     const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r, const void* Z_r,
-                     const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r, void* dW2_r,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     const void* X, const float* gates, const int* group_offsets, const int* row_token,
+                     const int* token_row, const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,
+                     const void* Z_r, const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r,
+                     void* dW2_r, void* workspace, size_t workspace_bytes, void* stream) {
   TP_CHECK(tokens >= 0 && top_k >= 1 && (long)tokens * top_k <= INT_MAX / 4, TP_EINVAL,
            "tokens %d, top_k %d out of range", tokens, top_k);
   TP_CHECK(n_experts >= 1 && n_experts <= 65535, TP_EINVAL, "n_experts %d out of range", n_experts);
@@ -598,7 +598,8 @@ int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   if (st) return st;
   const long n = (long)rows;
   NEED(X, "X", (long)tokens * H); NEED4(gates, "gates", n); NEED4(group_offsets, "group_offsets", n_experts + 1);
-  NEED4(token_row, "token_row", n); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1); NEED(A1_r, "A1_r", n);
+  NEED4(row_token, "row_token", n); NEED4(token_row, "token_row", n); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1);
+  NEED(A1_r, "A1_r", n);
   NEED(Y_r, "Y_r", n); NEED(Z_r, "Z_r", n * H); NEED(d_out, "d_out", (long)tokens * H);
   NEED(dX_r, "dX_r", (long)tokens * H); NEED4(dgates_r, "dgates_r", n); NEED(dW1_r, "dW1_r", 1);
   NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1);
@@ -610,13 +611,13 @@ int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   char* w = (char*)workspace;
   char* plan = w;
   char* dA1 = plan + align256(grouped_ws_bytes(n_experts));
-  char* Xp = dA1 + align256((size_t)rows * g.Fr * es);
-  char* dZp = Xp + align256((size_t)rows * H * es);     // later also dX_perm (its reads come first)
+  char* dZp = dA1 + align256((size_t)rows * g.Fr * es);  // later also dX_perm (its reads come first)
   hipStream_t s = (hipStream_t)stream;
-  TP_TRY(launch_moe_combine_bwd(dtype, tokens, top_k, H, d_out, X, Z_r, gates, token_row, rows, dZp, Xp, dgates_r, s),
-         "moe combine backward");
-  TP_TRY(launch_mlp_grouped_bwd(dtype, n_experts, group_offsets, rows, H, g.Fr, Xp, W1_r, W2_r, A1_r, Y_r, dZp, dA1,
-                                dZp, dW1_r, db1_r, dW2_r, plan, s), "moe experts backward");
+  TP_TRY(launch_moe_combine_bwd(dtype, tokens, top_k, H, d_out, X, Z_r, gates, token_row, rows, dZp, nullptr,
+                                dgates_r, s), "moe combine backward");
+  // dW1's operand X_perm is gathered from X by row_token inside its loads (no dispatched copy)
+  TP_TRY(launch_mlp_grouped_bwd(dtype, n_experts, group_offsets, rows, H, g.Fr, X, W1_r, W2_r, A1_r, Y_r, dZp, dA1,
+                                dZp, dW1_r, db1_r, dW2_r, plan, s, row_token, tokens), "moe experts backward");
   TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dZp, nullptr, token_row, rows, dX_r, s), "moe dispatch backward");
   return TP_OK;
 }

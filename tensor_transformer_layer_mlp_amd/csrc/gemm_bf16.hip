@@ -153,6 +153,26 @@ __device__ __forceinline__ void load_tile_gather(const bf16* X, unsigned bytes, 
   }
 }
 
+// The MN-major A operand with its k rows gathered (the weight gradient's Xᵀ over dispatched rows):
+// piece j of this lane (k-row k0 + r[j]) reads row src[j] of the `bytes`-byte matrix at X (element
+// (m, k) at X[src·lda + m], src = the index array's entry for that k, fetched one k-tile ahead), at
+// columns mn0 + c[j]; k past K, an index outside the matrix, or columns past the tile or matrix
+// read zeros.
+template <int IPW, int W>
+__device__ __forceinline__ void load_tile_gather_k(const bf16* X, unsigned bytes, int rows_n, long lda, int mn0,
+                                                   int mn_total, int k0, int K, TP_LDS char* dst,
+                                                   const int (&src)[IPW], const int (&r)[IPW], const int (&c)[IPW],
+                                                   int wave) {
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const bool ok = k0 + r[j] < K && src[j] >= 0 && src[j] < rows_n && c[j] < W && mn0 + c[j] < mn_total;
+    const unsigned off = (unsigned)(((long)src[j] * lda + mn0 + c[j]) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TP_LDS void*)(dst + (wave * IPW + j) * 1024), 16,
+                                             ok ? off : OOB, 0, 0, 0);
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4 v) {
   // four consecutive columns n .. n+3 of row m (N is a multiple of 8, so all four are in range)
@@ -174,10 +194,11 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
 }
 
 // One BM x BN output tile at (m0, n0): the k loop over LDS stages and the fused epilogue.
-template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false>
+template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false, bool GATHER_K = false>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
                                           int lane, int rot = 0) {
   static_assert(!GATHER || AK, "rows are gathered for a K-major A only");
+  static_assert(!GATHER_K || (!AK && !GATHER && Cfg::STAGES == 2), "k rows are gathered for an MN-major A, 2 stages");
   constexpr int LA = AK ? Cfg::BM : Cfg::PM, LB = BK ? Cfg::BN : Cfg::PN;   // rows or pitch
   constexpr int A_BYTES = Cfg::template bytes<AK, Cfg::BM>(), B_BYTES = Cfg::template bytes<BK, Cfg::BN>();
   constexpr int IPW_A = A_BYTES / 1024 / Cfg::NW, IPW_B = B_BYTES / 1024 / Cfg::NW;   // loads per wave
@@ -201,8 +222,21 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
       ga[j] = (src >= 0 && src < d.a_rows_n) ? src * (int)d.lda : -1;
     }
   }
+  // k-gathered A: the source rows of the next k-tile to load, fetched one tile ahead.  The loads are
+  // unconditional (k clamped into [0, K), K >= 1 whenever a tile is loaded) and their values are
+  // first used when that tile's loads are issued, so no wait is placed right after the fetch; the
+  // k-range check happens there too.
+  int gk[IPW_A];
+  if constexpr (GATHER_K) gbytes = (unsigned)((long)d.a_rows_n * d.lda * 2);
+  auto fetch_k = [&](int k) {
+#pragma unroll
+    for (int j = 0; j < IPW_A; ++j) gk[j] = d.a_rows[min(k + ar[j], d.K - 1)];
+  };
   auto load_a = [&](int k, TP_LDS char* dst) {
     if constexpr (GATHER) load_tile_gather<IPW_A>((const bf16*)d.A, gbytes, k, d.K, dst, ga, ac, wave);
+    else if constexpr (GATHER_K)
+      load_tile_gather_k<IPW_A, Cfg::BM>((const bf16*)d.A, gbytes, d.a_rows_n, d.lda, m0, d.M, k, d.K, dst, gk, ar,
+                                         ac, wave);
     else load_tile<AK, LA, Cfg::BM, IPW_A, Cfg::BKT>(A, m0, k, d.K, dst, ar, ac, wave);
   };
 
@@ -221,12 +255,18 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
   rot = nk > 0 ? rot % nk : 0;
   auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * BKT; };
   // prologue: tiles 0 .. STAGES-2 in flight
+  if constexpr (GATHER_K) {
+    if (nk > 0) fetch_k(kpos(0));
+  }
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
     if (t < nk) {
       load_a(kpos(t), lds + t * Cfg::STAGE);
       load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, kpos(t), d.K, lds + t * Cfg::STAGE + A_BYTES, br, bc, wave);
     }
+  if constexpr (GATHER_K) {
+    if (nk > 1) fetch_k(kpos(1));
+  }
   int cur_stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt has landed once at most the loads of the STAGES-2 younger tiles are outstanding
@@ -255,6 +295,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
       const int k1 = kpos(kt + Cfg::STAGES - 1);
       load_a(k1, nxt);
       load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + A_BYTES, br, bc, wave);
+      if constexpr (GATHER_K) {
+        if (kt + 2 < nk) fetch_k(kpos(kt + 2));
+      }
     }
 #pragma unroll
     for (int q = 0; q < NKK; ++q) {
@@ -434,7 +477,7 @@ struct GroupedKArgs {
   long c_stride;
 };
 
-template <class Cfg>
+template <class Cfg, bool GK>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -449,10 +492,12 @@ void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
   GemmDesc d = g.d;
   const int k0 = g.off[e];
   d.K = g.off[e + 1] - k0;
-  d.A = (const bf16*)g.d.A + (long)k0 * g.d.lda;
+  if constexpr (GK) d.a_rows = g.d.a_rows + k0;   // A stays the whole gathered-from matrix
+  else d.A = (const bf16*)g.d.A + (long)k0 * g.d.lda;
   d.B = (const bf16*)g.d.B + (long)k0 * g.d.ldb;
   d.C = (bf16*)g.d.C + (long)e * g.c_stride;
-  gemm_tile<Cfg, false, false, EPI_STORE>(d, tm * Cfg::BM, tn * Cfg::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+  gemm_tile<Cfg, false, false, EPI_STORE, false, GK>(d, tm * Cfg::BM, tn * Cfg::BN, (TP_LDS char*)smem, wave, lane,
+                                                      tm + tn);
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
@@ -590,6 +635,7 @@ bool gemm_bf16_grouped_k_eligible(const GemmDesc& d) {
   if ((d.M | d.N) & 7) return false;
   if ((d.lda | d.ldb | d.ldc) & 7) return false;
   if (d.lda > (1L << 22) || d.ldb > (1L << 22)) return false;
+  if (d.a_rows && (long)d.a_rows_n * d.lda * 2 > 0x7fffffffL) return false;   // one buffer range over A
   return ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) == 0;
 }
 
@@ -600,7 +646,8 @@ hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int gro
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   GroupedKArgs g{d, off, groups, c_stride};
-  gemm_bf16_grouped_k_kernel<Cfg><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
+  if (d.a_rows) gemm_bf16_grouped_k_kernel<Cfg, true><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
+  else gemm_bf16_grouped_k_kernel<Cfg, false><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

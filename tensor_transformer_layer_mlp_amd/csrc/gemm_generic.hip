@@ -56,9 +56,9 @@ __device__ __forceinline__ void generic_tile(const GemmDesc& d, int m0, int n0) 
       const int gm = m0 + m, gk = k0 + k;
       T v = from_f32<T>(0.f);
       if (gm < d.M && gk < d.K) {
-        if (d.a_rows) {          // gathered rows (K-major A only); outside [0, a_rows_n) reads zero
-          const int src = d.a_rows[gm];
-          if (src >= 0 && src < d.a_rows_n) v = A[(long)src * d.lda + gk];
+        if (d.a_rows) {          // gathered rows of the source matrix; outside [0, a_rows_n) reads zero
+          const int src = d.a_rows[d.a_kmajor ? gm : gk];
+          if (src >= 0 && src < d.a_rows_n) v = d.a_kmajor ? A[(long)src * d.lda + gk] : A[(long)src * d.lda + gm];
         } else {
           v = d.a_kmajor ? A[(long)gm * d.lda + gk] : A[(long)gk * d.lda + gm];
         }
@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256) void gemm_generic_grouped_k_kernel(GemmDesc g,
   GemmDesc d = g;
   const int k0 = off[e];
   d.K = off[e + 1] - k0;
-  d.A = (const T*)g.A + (long)k0 * g.lda;
+  if (g.a_rows) d.a_rows = g.a_rows + k0;   // A stays the whole gathered-from matrix
+  else d.A = (const T*)g.A + (long)k0 * g.lda;
   d.B = (const T*)g.B + (long)k0 * g.ldb;
   d.C = (T*)g.C + (long)e * c_stride;
   generic_tile<T, EPI_STORE>(d, blockIdx.y * GBM, blockIdx.x * GBN);

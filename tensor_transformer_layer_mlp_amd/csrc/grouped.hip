@@ -185,10 +185,13 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
 //   dW1[e] = X_eᵀ·dA1_e                 grouped weight gradient
 //   dX = dA1·W1[e]ᵀ                     grouped, rows split by expert
 // in that order on one stream, so dX may alias dZ (both reads of dZ come first).  An expert without
-// rows gets zero weight and bias gradients.  ws: grouped_ws_bytes(groups).
+// rows gets zero weight and bias gradients.  With x_rows set, row r of the expert-sorted X is row
+// x_rows[r] of the x_rows_n-row matrix at X, gathered inside dW1's operand loads.
+// ws: grouped_ws_bytes(groups).
 hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int rows, int H, int Fr, const void* X,
                                   const void* W1, const void* W2, const void* A1, const void* Y, const void* dZ,
-                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s) {
+                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s,
+                                  const int* x_rows, int x_rows_n) {
   if (groups <= 0) return hipSuccess;
   int* off_s = (int*)ws;
   int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
@@ -212,6 +215,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   gw2.C = dW2; gw2.ldc = H;
   GemmDesc gw1 = gw2;                         // dW1[e] = X_eᵀ·dA1_e  [H, Fr]
   gw1.M = H; gw1.N = Fr; gw1.A = X; gw1.lda = H; gw1.B = dA1; gw1.ldb = Fr; gw1.C = dW1; gw1.ldc = Fr;
+  gw1.a_rows = x_rows; gw1.a_rows_n = x_rows_n;
 
   const bool tiled = rows > 0 && gemm_bf16_eligible(ga) && gemm_bf16_eligible(gx);
   const int bm1 = tiled ? gemm_bf16_grouped_bm(ga.K) : gemm_generic_grouped_bm();
@@ -253,7 +257,8 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   }
   {
     const bool t1 = gemm_bf16_grouped_k_eligible(gw1);
-    ProfScope p(t1 ? "gemm_bf16_grouped_k<Xt.dA1>" : "gemm_generic_grouped_k<Xt.dA1>", s, fl,
+    ProfScope p(t1 ? (x_rows ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_bf16_grouped_k<Xt.dA1>")
+                   : (x_rows ? "gemm_generic_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1>"), s, fl,
                 es * ((double)rows * H + (double)rows * Fr) + wts);
     e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
            : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);

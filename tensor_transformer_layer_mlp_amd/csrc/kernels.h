@@ -80,9 +80,11 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
 
 // Backward of launch_mlp_grouped on expert-sorted operands (dX may alias dZ); dA1 [rows, Fr] is
 // caller scratch; ws as for the forward.  dW1 [groups, H, Fr], db1 [groups, Fr], dW2 [groups, Fr, H].
+// With x_rows set, row r of the expert-sorted X is row x_rows[r] of X (x_rows_n rows), gathered.
 hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int rows, int H, int Fr, const void* X,
                                   const void* W1, const void* W2, const void* A1, const void* Y, const void* dZ,
-                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s);
+                                  void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s,
+                                  const int* x_rows = nullptr, int x_rows_n = 0);
 
 // FP8 (OCP E4M3) quantisation with one scale per tensor and the GEMM on codes (see fp8.hip).
 size_t fp8_quantize_ws_bytes();

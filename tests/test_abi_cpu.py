@@ -253,3 +253,37 @@ def test_grouped_validation(lib):
     assert call(a15=P + 16) == -3           # workspace alignment
     assert bd.tp_workspace_bytes("tp_mlp_grouped_shard_fwd", 8, 0, 1, 1, 8192, 128, 2048, 0) >= 2 * 129 * 4
     assert ok is not base
+
+
+def test_binding_argument_counts_match_header():
+    """Each ctypes signature in the binding has as many arguments as the header's declaration."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (_, args) in bd._SIGNATURES.items():
+        m = re.search(r"\b%s\s*\(([^;]*)\)\s*;" % name, text)
+        assert m, f"{name} not declared"
+        params = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
+        assert len(params) == len(args), f"{name}: header {len(params)} arguments, binding {len(args)}"
+
+
+def test_moe_backward_validation(lib):
+    g = lib.tp_mlp_grouped_shard_bwd
+    base = [2, 0, 4, P, 64, 64, 256, 0]
+    assert g(*base, *([P] * 10), None, 0, None) == -5                          # no workspace
+    assert g(*base, *([P] * 3), None, *([P] * 6), P, 1 << 30, None) == -2      # A1 NULL
+    assert g(2, 0, 0, P, 64, 64, 256, 0, *([P] * 10), P, 1 << 30, None) == -1  # no groups
+    assert g(2, 0, 4, P, 64, 64, 1, 0, *([P] * 10), P, 1 << 30, None) == -1   # F < tp_size
+    assert g(2, 0, 4, P, 64, 64, 256, 0, *([P] * 10), MIS, 1 << 30, None) == -3
+    m = lib.tp_moe_shard_bwd
+    mb = [2, 0, 16, 64, 4, 2, 256, 0]
+    assert m(*mb, *([P] * 16), None, 0, None) == -5
+    assert m(*mb, P, P, P, None, *([P] * 12), P, 1 << 30, None) == -2          # row_token NULL
+    assert m(2, 0, 16, 64, 4, 5, 256, 0, *([P] * 16), P, 1 << 30, None) == -1  # top_k > n_experts
+    assert m(2, 0, 16, 64, 4, 2, 256, 0, *([P] * 16), P, 16, None) == -5       # workspace too small
+    r = lib.tp_moe_route_bwd
+    assert r(16, 4, 5, P, P, P, P, None) == -1                                 # top_k > E
+    assert r(16, 2048, 2, P, P, P, P, None) == -4                              # E above 1024
+    assert r(16, 4, 2, P, P, None, P, None) == -2
+    assert r(-1, 4, 2, P, P, P, P, None) == -1
+    n = bd.tp_workspace_bytes("tp_moe_shard_bwd", 8, 0, 1, 16384 * 8, 8192, 128, 2048, 0)
+    assert n >= 16384 * 8 * (8192 + 256) * 2
+    assert bd.tp_workspace_bytes("tp_mlp_grouped_shard_bwd", 8, 0, 1, 1000, 512, 4, 2048, 0) >= 1000 * 256 * 2

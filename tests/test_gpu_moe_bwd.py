@@ -80,7 +80,8 @@ def _moe_bwd(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, fwd, d_out
     o = dict(dX=empty((tokens, H), dtype), dgates=empty((tokens, k), "f32"), dW1=empty((E, H, Fr), dtype),
              db1=empty((E, Fr), dtype), dW2=empty((E, Fr, H), dtype))
     ws = bd.workspace("tp_moe_shard_bwd", tp, rank, 1, n, H, E, F_expert, TORCH_DT[dtype])
-    bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, F_expert, X, route["gates"], route["offsets"], route["token_row"],
+    bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, F_expert, X, route["gates"], route["offsets"], route["row_token"],
+                        route["token_row"],
                         dev(W["W1"]), dev(W["W2"]), fwd["A1"], fwd["Y"], fwd["Z"], d_out, o["dX"], o["dgates"],
                         o["dW1"], o["db1"], o["dW2"], ws)
     torch.cuda.synchronize()
@@ -167,7 +168,7 @@ def test_moe_bwd_full_size_rank0():
     dW1, db1, dW2 = torch.empty_like(W1), torch.empty_like(b1), torch.empty_like(W2)
     wsb = bd.workspace("tp_moe_shard_bwd", tp, rank, 1, n, H, E, mw.F_expert, bf)
     bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, route["gates"], route["offsets"],
-                        route["token_row"], W1, W2, A1, Y, Z, d_out, dX, dg, dW1, db1, dW2, wsb)
+                        route["row_token"], route["token_row"], W1, W2, A1, Y, Z, d_out, dX, dg, dW1, db1, dW2, wsb)
     torch.cuda.synchronize()
     del wsb
     off, rt, tr, gates = r["group_offsets"], r["row_token"], r["token_row"], r["gates"]
