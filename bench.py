@@ -288,8 +288,8 @@ def fp8_mlp(bd, torch, wl, steps, warmup):
     backward timed apart.  Forward: quantise X (E4M3), X·W1 (2048 x 6144 x 12288) with bias + GeLU
     (A1 kept), quantise Y, Y·W2 (2048 x 12288 x 6144).  Backward: dZ in E5M2 (plain and the
     transposed copy), dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1), dW2 = Yᵀ·dZ, dA1 in E5M2 (both copies),
-    dX = dA1·W1ᵀ, dW1 = Xᵀ·dA1, db1 = Σ_t dA1; the K-major copies of X and Y the weight gradients
-    take are quantised inside the backward.  Weights are quantised once, outside the timed region
+    dX = dA1·W1ᵀ, dW1 = Xᵀ·dA1, db1 = Σ_t dA1; dZ and dA1 are quantised once into both layouts, and
+    the K-major copies of X and Y the weight gradients take are quantised inside the backward.  Weights are quantised once, outside the timed region
     (both copies; they change once per optimizer step).  A precision variant beside the bf16 step,
     against the FP8 peak."""
     T, H = wl.T, wl.H
@@ -311,10 +311,8 @@ def fp8_mlp(bd, torch, wl, steps, warmup):
     ws = bd.workspace("tp_fp8_quantize", 1, 0, 1, 1, 1, 1, 1, bf)
     wsb = bd.workspace("tp_bias_grad", 1, 0, T, 1, Fr, 1, 1, bf)
     e4, e5 = bd.TP_FP8_E4M3, bd.TP_FP8_E5M2
-    bd.tp_fp8_quantize(W1, qW1t, sW1, ws, transpose=True)
-    bd.tp_fp8_quantize(W1, qW1, sW1, ws)
-    bd.tp_fp8_quantize(W2, qW2t, sW2, ws, transpose=True)
-    bd.tp_fp8_quantize(W2, qW2, sW2, ws)
+    bd.tp_fp8_quantize(W1, qW1, sW1, ws, q_t=qW1t)
+    bd.tp_fp8_quantize(W2, qW2, sW2, ws, q_t=qW2t)
 
     def fwd():
         bd.tp_fp8_quantize(X, qX, sX, ws)
@@ -323,15 +321,13 @@ def fp8_mlp(bd, torch, wl, steps, warmup):
         bd.tp_fp8_gemm_nt(qY, sY, qW2t, sW2, Z)
 
     def bwd():
-        bd.tp_fp8_quantize(dZ, qdZ, sdZ, ws, fmt=e5)
-        bd.tp_fp8_quantize(dZ, qdZt, sdZ, ws, transpose=True, fmt=e5)
+        bd.tp_fp8_quantize(dZ, qdZ, sdZ, ws, q_t=qdZt, fmt=e5)
         bd.tp_fp8_gemm_nt(qdZ, sdZ, qW2, sW2, dA1, epilogue=bd.TP_FP8_EPI_DGELU, aux=A1, a_fmt=e5, b_fmt=e4)
-        bd.tp_fp8_quantize(Y, qYt, sY, ws, transpose=True)
+        bd.tp_fp8_quantize(Y, None, sY, ws, q_t=qYt)
         bd.tp_fp8_gemm_nt(qYt, sY, qdZt, sdZ, dW2, a_fmt=e4, b_fmt=e5)
-        bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, fmt=e5)
-        bd.tp_fp8_quantize(dA1, qdA1t, sdA1, ws, transpose=True, fmt=e5)
+        bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, q_t=qdA1t, fmt=e5)
         bd.tp_fp8_gemm_nt(qdA1, sdA1, qW1, sW1, dX, a_fmt=e5, b_fmt=e4)
-        bd.tp_fp8_quantize(X, qXt, sX, ws, transpose=True)
+        bd.tp_fp8_quantize(X, None, sX, ws, q_t=qXt)
         bd.tp_fp8_gemm_nt(qXt, sX, qdA1t, sdA1, dW1, a_fmt=e4, b_fmt=e5)
         bd.tp_bias_grad(dA1, db1, wsb)
 

@@ -302,10 +302,12 @@ typedef enum {
 /* Per-tensor quantisation of x [rows, cols] (bf16 or fp32) to `format`:
  *   amax = max |x|;  s = vmax / amax and descale = amax / vmax in fp32 (1 and 1 when amax = 0)
  *   q = nearest code of fp32(x·s), ties to the even mantissa, saturating at ±vmax
- * vmax = 448 (E4M3) or 57344 (E5M2).  transpose != 0 writes the codes transposed, [cols, rows] (the
- * K-major copy tp_fp8_gemm_nt takes).  descale: one fp32 in device memory (written).  x must be
- * finite.  workspace: tp_workspace_bytes("tp_fp8_quantize", ...) bytes. */
-int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, int transpose, unsigned char* q,
+ * vmax = 448 (E4M3) or 57344 (E5M2).  q [rows, cols] receives the codes as they lie, q_t [cols, rows]
+ * the transposed copy (the K-major operand tp_fp8_gemm_nt takes for a matrix used along its rows);
+ * either may be NULL, not both (TP_ENULL).  Asking for both reads x twice in all (amax, then one
+ * pass writing both layouts when rows and cols are multiples of 16).  descale: one fp32 in device
+ * memory (written).  x must be finite.  workspace: tp_workspace_bytes("tp_fp8_quantize", ...). */
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, unsigned char* q, unsigned char* q_t,
                     float* descale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* GEMM on 8-bit codes, both operands K-major:

@@ -38,7 +38,7 @@ _SIGNATURES = {
     "tp_residual_ln_bwd": (_I, [_I] * 6 + [_P] * 7 + [_F] + [_P] * 4 + [_P, _Z, _P]),
     "tp_mlp_grouped_shard_fwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]),
     "tp_moe_route": (_I, [_I, _I, _I] + [_P] * 6 + [_P, _Z, _P]),
-    "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _I, _P, _P, _P, _Z, _P]),
+    "tp_fp8_quantize": (_I, [_I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "tp_fp8_gemm_nt": (_I, [_I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
     "tp_bias_grad": (_I, [_I, _I, _I, _P, _P, _P, _Z, _P]),
     "tp_mlp_grouped_shard_bwd": (_I, [_I, _I, _I, _P, _I, _I, _I, _I] + [_P] * 10 + [_P, _Z, _P]),
@@ -375,14 +375,16 @@ def tp_moe_shard_fwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, ga
     _check(rc, "tp_moe_shard_fwd")
 
 
-def tp_fp8_quantize(x, q, descale, workspace, transpose=False, fmt=TP_FP8_E4M3, stream=None):
-    """8-bit codes of a 2-D tensor x with one scale (q: uint8 [rows, cols], or [cols, rows] when
-    transpose), and its fp32 descale (a one-element device tensor).  fmt: TP_FP8_E4M3 / TP_FP8_E5M2."""
+def tp_fp8_quantize(x, q, descale, workspace, q_t=None, fmt=TP_FP8_E4M3, stream=None):
+    """8-bit codes of a 2-D tensor x with one scale: q uint8 [rows, cols] (or None) and / or q_t uint8
+    [cols, rows], the transposed copy; descale a one-element fp32 device tensor.  fmt: TP_FP8_E4M3 /
+    TP_FP8_E5M2."""
     rows, cols = x.shape
     _need(q, rows * cols, "q")
+    _need(q_t, rows * cols, "q_t")
     _need(descale, 1, "descale")
-    rc = raw().tp_fp8_quantize(rows, cols, _dtype_code(x), _ptr(x, "x"), fmt, 1 if transpose else 0,
-                               _ptr(q, "q", torch.uint8), _ptr(descale, "descale", torch.float32),
+    rc = raw().tp_fp8_quantize(rows, cols, _dtype_code(x), _ptr(x, "x"), fmt, _ptr(q, "q", torch.uint8, True),
+                               _ptr(q_t, "q_t", torch.uint8, True), _ptr(descale, "descale", torch.float32),
                                _ptr(workspace, "workspace", None, True),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                _stream(stream))

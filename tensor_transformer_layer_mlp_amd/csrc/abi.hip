@@ -638,19 +638,20 @@ int tp_moe_route_bwd(int tokens, int n_experts, int top_k, const float* logits, 
   return TP_OK;
 }
 
-int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, int transpose, unsigned char* q,
+int tp_fp8_quantize(int rows, int cols, int dtype, const void* x, int format, unsigned char* q, unsigned char* q_t,
                     float* descale, void* workspace, size_t workspace_bytes, void* stream) {
   TP_CHECK(dtype == TP_BF16 || dtype == TP_F32, TP_EINVAL, "dtype %d is neither TP_BF16 nor TP_F32", dtype);
   TP_CHECK(format == TP_FP8_E4M3 || format == TP_FP8_E5M2, TP_EINVAL, "format %d is neither E4M3 nor E5M2", format);
   TP_CHECK(rows >= 0 && cols >= 0, TP_EINVAL, "negative size %d x %d", rows, cols);
   const long n = (long)rows * cols;
-  NEED(x, "x", n); NEED(q, "q", n); NEED4(descale, "descale", 1);
+  TP_CHECK(q != nullptr || q_t != nullptr || n == 0, TP_ENULL, "q and q_t are both NULL");
+  NEED(x, "x", n); MAYBE(q, "q"); MAYBE(q_t, "q_t"); NEED4(descale, "descale", 1);
   const size_t need = align256(fp8_quantize_ws_bytes());
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  TP_TRY(launch_fp8_quantize(dtype, format, rows, cols, x, transpose != 0, q, descale, (float*)workspace,
-                             (hipStream_t)stream), "fp8 quantize");
+  TP_TRY(launch_fp8_quantize(dtype, format, rows, cols, x, q, q_t, descale, (float*)workspace, (hipStream_t)stream),
+         "fp8 quantize");
   return TP_OK;
 }
 

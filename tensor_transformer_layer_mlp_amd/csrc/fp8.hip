@@ -6,7 +6,8 @@
 // or 57344; 1 and 1 for an all-zero tensor), codes = nearest code of fp32(x·s), ties to the even
 // mantissa, saturating at ±vmax, by exact bit arithmetic on the fp32 value (no conversion
 // instruction, so the rounding is the one stated).  The transposed form writes the [cols, rows] copy a GEMM operand
-// needs K-major, through 64 x 64 LDS tiles so both the reads and the writes are whole rows.
+// needs K-major, through 64 x 64 LDS tiles so both the reads and the writes are whole rows; one pass
+// can write both layouts (16-byte pieces when rows and cols are multiples of 16).
 //
 // GEMM: C[M, N] = (A·Bᵀ)·descale_a·descale_b (+ bias) (-> GeLU, or ∘ GeLU'(aux)), A [M, K] and
 // B [N, K] codes, each E4M3 or E5M2, both K-major; bf16 out, fp32 accumulation.  The operand formats
@@ -177,6 +178,64 @@ __global__ __launch_bounds__(256) void fp8_quantize_t_kernel(int rows, int cols,
     const int c = i / 64, r = i % 64;
     const int gr = r0 + r, gc = c0 + c;
     if (gr < rows && gc < cols) q[(long)gc * rows + gr] = t[c][r];
+  }
+}
+
+// One pass writing the plain codes q [rows, cols] and / or the transposed codes qt [cols, rows] (either
+// may be null), one 64 x 64 tile per workgroup, for rows and cols multiples of 16: thread i reads 16
+// consecutive elements of tile row i / 4 (two or four 16-byte loads), stores their 16 codes plain with
+// one 16-byte store, and leaves them in LDS; after the barrier it gathers 16 codes of one tile column
+// and stores them as 16 bytes of a qt row.  Both sides are whole 16-byte pieces of rows.
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void fp8_quantize_2_kernel(int rows, int cols, const T* __restrict__ x,
+                                                             const float* __restrict__ scale,
+                                                             unsigned char* __restrict__ q,
+                                                             unsigned char* __restrict__ qt) {
+  __shared__ unsigned char t[64][64 + 16];
+  const float s = *scale;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int r = threadIdx.x >> 2, cq = 16 * (threadIdx.x & 3);
+  const int gr = r0 + r, gc = c0 + cq;
+  if (gr < rows && gc < cols) {              // gc < cols implies gc + 15 < cols (cols % 16 == 0)
+    float v[16];
+    const T* src = x + (long)gr * cols + gc;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 a = *(const bf16x8*)src, b = *(const bf16x8*)(src + 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { v[j] = (float)a[j]; v[8 + j] = (float)b[j]; }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 a = *(const f32x4*)(src + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * h + j] = a[j];
+      }
+    }
+    u32x4 w;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      unsigned u = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u |= fp8_code<FMT>(v[4 * h + j] * s) << (8 * j);
+      w[h] = u;
+    }
+    if (q) *(u32x4*)(q + (long)gr * cols + gc) = w;
+    *(u32x4*)&t[r][cq] = w;
+  }
+  if (!qt) return;                           // uniform over the workgroup: no barrier is skipped unevenly
+  __syncthreads();
+  // output row c0 + oc (an input column), output columns r0 + orq .. +15 (input rows)
+  const int oc = threadIdx.x >> 2, orq = 16 * (threadIdx.x & 3);
+  if (c0 + oc < cols && r0 + orq < rows) {   // rows % 16 == 0: the 16 input rows all exist
+    u32x4 w;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      unsigned u = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u |= (unsigned)t[orq + 4 * h + j][oc] << (8 * j);
+      w[h] = u;
+    }
+    *(u32x4*)(qt + (long)(c0 + oc) * rows + r0 + orq) = w;
   }
 }
 
@@ -367,8 +426,8 @@ hipError_t f8_run(const F8Desc& d, int fa, int fb, hipStream_t s) {
 
 size_t fp8_quantize_ws_bytes() { return (AMAX_WGS + 64) * sizeof(float); }
 
-hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const void* x, bool transpose,
-                               unsigned char* q, float* descale, float* ws, hipStream_t s) {
+hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const void* x, unsigned char* q,
+                               unsigned char* qt, float* descale, float* ws, hipStream_t s) {
   const long n = (long)rows * cols;
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
   float* part = ws;
@@ -384,15 +443,27 @@ hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (n == 0) return hipSuccess;
-  ProfScope p(transpose ? "fp8_quantize_t" : "fp8_quantize", s, (double)n, es * n + n);
+  if (n == 0 || (!q && !qt)) return hipSuccess;
+  const double outs = (q ? 1.0 : 0.0) + (qt ? 1.0 : 0.0);
+  // both layouts in one pass when the 16-element pieces tile the matrix; else one kernel per layout
+  const bool two = rows % 16 == 0 && cols % 16 == 0;
+  ProfScope p(two && qt ? (q ? "fp8_quantize_2" : "fp8_quantize_2<t>")
+                        : (q && qt ? "fp8_quantize+t" : (qt ? "fp8_quantize_t" : "fp8_quantize")),
+              s, (double)n, es * n + outs * n);
   auto go = [&](auto fmt_tag) {
     constexpr int F = decltype(fmt_tag)::value;
-    if (transpose) {
+    if (two && qt) {
       dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-      if (dtype == DT_BF16) fp8_quantize_t_kernel<bf16, F><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, q);
-      else fp8_quantize_t_kernel<float, F><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, q);
-    } else {
+      if (dtype == DT_BF16) fp8_quantize_2_kernel<bf16, F><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, q, qt);
+      else fp8_quantize_2_kernel<float, F><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, q, qt);
+      return;
+    }
+    if (qt) {
+      dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+      if (dtype == DT_BF16) fp8_quantize_t_kernel<bf16, F><<<grid, 256, 0, s>>>(rows, cols, (const bf16*)x, scale, qt);
+      else fp8_quantize_t_kernel<float, F><<<grid, 256, 0, s>>>(rows, cols, (const float*)x, scale, qt);
+    }
+    if (q) {
       const long blocks = (n + 2047) / 2048;
       if (dtype == DT_BF16)
         fp8_quantize_kernel<bf16, F><<<(unsigned)blocks, 256, 0, s>>>(n, (const bf16*)x, scale, q);

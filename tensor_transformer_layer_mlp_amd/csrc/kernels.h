@@ -89,8 +89,9 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
 // FP8 (OCP E4M3) quantisation with one scale per tensor and the GEMM on codes (see fp8.hip).
 size_t fp8_quantize_ws_bytes();
 // fmt: 0 E4M3, 1 E5M2.
-hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const void* x, bool transpose,
-                               unsigned char* q, float* descale, float* ws, hipStream_t s);
+// q [rows, cols] and qt [cols, rows] codes, each nullable.
+hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const void* x, unsigned char* q,
+                               unsigned char* qt, float* descale, float* ws, hipStream_t s);
 // fa, fb: operand formats.  epi: 0 none, 1 GeLU, 2 tanh GeLU, 3 ∘ GeLU'(aux), 4 ∘ tanh GeLU'(aux).
 hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int fa, const float* da,
                               const unsigned char* B, int fb, const float* db, const void* bias, int epi,

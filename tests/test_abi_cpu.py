@@ -124,11 +124,12 @@ def test_fp8_validation(lib):
     assert ok(fa=1, epi=3) == -2 and ok(fa=1, epi=4) == -2                         # GeLU' without aux
     assert ok(M=-1) == -1
     q = lib.tp_fp8_quantize
-    assert q(4, 4, 0, P, 0, 0, P, P, None, 0, None) == -5                          # no workspace
-    assert q(4, 4, 2, P, 0, 0, P, P, P, 1 << 20, None) == -1                       # dtype
-    assert q(4, 4, 0, P, 2, 0, P, P, P, 1 << 20, None) == -1                       # format
-    assert q(4, 4, 0, P, 1, 0, None, P, P, 1 << 20, None) == -2                    # q NULL
-    assert q(4, 4, 0, P, 1, 0, P, P, MIS, 1 << 20, None) == -3                     # workspace alignment
+    assert q(4, 4, 0, P, 0, P, None, P, None, 0, None) == -5                       # no workspace
+    assert q(4, 4, 2, P, 0, P, None, P, P, 1 << 20, None) == -1                    # dtype
+    assert q(4, 4, 0, P, 2, P, P, P, P, 1 << 20, None) == -1                       # format
+    assert q(4, 4, 0, P, 1, None, None, P, P, 1 << 20, None) == -2                 # neither output
+    assert q(4, 4, 0, P, 1, None, MIS, P, P, 1 << 20, None) == -3                  # q_t misaligned
+    assert q(4, 4, 0, P, 1, P, None, P, MIS, 1 << 20, None) == -3                  # workspace alignment
     b = lib.tp_bias_grad
     assert b(4, 4, 0, P, P, None, 0, None) == -5
     assert b(4, 4, 0, None, P, P, 1 << 20, None) == -2

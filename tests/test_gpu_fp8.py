@@ -27,12 +27,18 @@ def _quantize(x, transpose=False, fmt="e4m3"):
     rows, cols = x.shape
     q = torch.full((cols, rows) if transpose else (rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
     d = torch.full((1,), float("nan"), device="cuda")
-    bd.tp_fp8_quantize(x, q, d, _ws(), transpose=transpose, fmt=FMT[fmt])
+    if transpose:
+        bd.tp_fp8_quantize(x, None, d, _ws(), q_t=q, fmt=FMT[fmt])
+    else:
+        bd.tp_fp8_quantize(x, q, d, _ws(), fmt=FMT[fmt])
     torch.cuda.synchronize()
     return q, d
 
 
-QCASES = [(1, 1, 1.0), (7, 13, 1.0), (64, 64, 30.0), (130, 70, 1e-3), (257, 1000, 5.0), (3, 8, 0.0)]
+# (64, 64), (80, 144) and (1024, 512) take the one-pass kernel (rows and cols multiples of 16), the
+# others the separate plain and transposed kernels
+QCASES = [(1, 1, 1.0), (7, 13, 1.0), (64, 64, 30.0), (130, 70, 1e-3), (257, 1000, 5.0), (3, 8, 0.0),
+          (80, 144, 2.0), (1024, 512, 1.0)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -45,6 +51,23 @@ def test_fp8_quantize(rows, cols, std, dtype, transpose, fmt):
     rq, rd = oracle.fp8_quantize(op.f64.astype(np.float32), transpose, fmt)
     assert np.array_equal(host(q).astype(np.uint8), rq), "codes differ from the oracle's"
     assert np.float32(host(d)[0]) == rd, f"descale {host(d)[0]} != {rd}"
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", [(80, 144), (1024, 512), (130, 70), (16, 32)])
+def test_fp8_quantize_both_layouts(rows, cols, dtype, fmt):
+    """One call writing the plain and the transposed codes: each bit for bit as the oracle's."""
+    op = synth.normal(f"f8q2_{rows}_{cols}", (rows, cols), 3.0, dtype)
+    q = torch.full((rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
+    qt = torch.full((cols, rows), 0xAA, dtype=torch.uint8, device="cuda")
+    d = torch.full((1,), float("nan"), device="cuda")
+    bd.tp_fp8_quantize(dev(op), q, d, _ws(), q_t=qt, fmt=FMT[fmt])
+    torch.cuda.synchronize()
+    rq, rd = oracle.fp8_quantize(op.f64.astype(np.float32), False, fmt)
+    assert np.array_equal(host(q).astype(np.uint8), rq), "plain codes differ from the oracle's"
+    assert np.array_equal(host(qt).astype(np.uint8), np.ascontiguousarray(rq.T)), "transposed codes differ"
+    assert np.float32(host(d)[0]) == rd
 
 
 @pytest.mark.parametrize("fmt,vmax", [("e4m3", 448.0), ("e5m2", 57344.0)])
@@ -118,8 +141,8 @@ def test_fp8_mlp_forward_against_bf16_definition():
     dX, dW1, dW2, dY = f1(), f1(), f1(), f1()
     ws = _ws()
     bd.tp_fp8_quantize(dev(X), qX, dX, ws)
-    bd.tp_fp8_quantize(dev(W1), qW1t, dW1, ws, transpose=True)
-    bd.tp_fp8_quantize(dev(W2), qW2t, dW2, ws, transpose=True)
+    bd.tp_fp8_quantize(dev(W1), None, dW1, ws, q_t=qW1t)
+    bd.tp_fp8_quantize(dev(W2), None, dW2, ws, q_t=qW2t)
     Y = torch.empty(T, Fr, dtype=torch.bfloat16, device="cuda")
     bd.tp_fp8_gemm_nt(qX, dX, qW1t, dW1, Y, bias=dev(b1), epilogue=bd.TP_FP8_EPI_GELU)
     bd.tp_fp8_quantize(Y, qY, dY, ws)
@@ -154,26 +177,21 @@ def test_fp8_mlp_backward():
     # forward (keeps A1 for the backward)
     qX, qXt, qW1t, qW1, qW2t, qW2 = u8(T, H), u8(H, T), u8(Fr, H), u8(H, Fr), u8(H, Fr), u8(Fr, H)
     sX, sW1, sW2, sY, sdZ, sdA1 = f1(), f1(), f1(), f1(), f1(), f1()
-    bd.tp_fp8_quantize(dev(X), qX, sX, ws)
-    bd.tp_fp8_quantize(dev(X), qXt, sX, ws, transpose=True)
-    bd.tp_fp8_quantize(dev(W1), qW1t, sW1, ws, transpose=True)
-    bd.tp_fp8_quantize(dev(W1), qW1, sW1, ws)
-    bd.tp_fp8_quantize(dev(W2), qW2t, sW2, ws, transpose=True)
-    bd.tp_fp8_quantize(dev(W2), qW2, sW2, ws)
+    bd.tp_fp8_quantize(dev(X), qX, sX, ws, q_t=qXt)
+    bd.tp_fp8_quantize(dev(W1), qW1, sW1, ws, q_t=qW1t)
+    bd.tp_fp8_quantize(dev(W2), qW2, sW2, ws, q_t=qW2t)
     A1, Y = bf(T, Fr), bf(T, Fr)
     bd.tp_fp8_gemm_nt(qX, sX, qW1t, sW1, Y, bias=dev(b1), epilogue=bd.TP_FP8_EPI_GELU, C_pre=A1)
     qYt = u8(Fr, T)
-    bd.tp_fp8_quantize(Y, qYt, sY, ws, transpose=True)
+    bd.tp_fp8_quantize(Y, None, sY, ws, q_t=qYt)
     # backward
     qdZ, qdZt, qdA1, qdA1t = u8(T, H), u8(H, T), u8(T, Fr), u8(Fr, T)
-    bd.tp_fp8_quantize(dev(dZ), qdZ, sdZ, ws, fmt=e5)
-    bd.tp_fp8_quantize(dev(dZ), qdZt, sdZ, ws, transpose=True, fmt=e5)
+    bd.tp_fp8_quantize(dev(dZ), qdZ, sdZ, ws, q_t=qdZt, fmt=e5)
     dA1, dW2, dX, dW1 = bf(T, Fr), bf(Fr, H), bf(T, H), bf(H, Fr)
     db1 = bf(Fr)
     bd.tp_fp8_gemm_nt(qdZ, sdZ, qW2, sW2, dA1, epilogue=bd.TP_FP8_EPI_DGELU, aux=A1, a_fmt=e5, b_fmt=e4)
     bd.tp_fp8_gemm_nt(qYt, sY, qdZt, sdZ, dW2, a_fmt=e4, b_fmt=e5)
-    bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, fmt=e5)
-    bd.tp_fp8_quantize(dA1, qdA1t, sdA1, ws, transpose=True, fmt=e5)
+    bd.tp_fp8_quantize(dA1, qdA1, sdA1, ws, q_t=qdA1t, fmt=e5)
     bd.tp_fp8_gemm_nt(qdA1, sdA1, qW1, sW1, dX, a_fmt=e5, b_fmt=e4)
     bd.tp_fp8_gemm_nt(qXt, sX, qdA1t, sdA1, dW1, a_fmt=e4, b_fmt=e5)
     wsb = bd.workspace("tp_bias_grad", 1, 0, T, 1, Fr, 1, 1, torch.bfloat16)
