@@ -223,3 +223,55 @@ def test_fp8_mlp_backward():
                                                  for k in ("A1", "Y")], dZ.f64, False)
     for k in ("dX", "dW1", "db1", "dW2"):
         assert_close(got[k], ref[k], "bf16", f"{k} (exact precision)", tol=1.5e-1)
+
+
+def test_fp8_mlp_graph_replay():
+    """The FP8 MLP forward and backward (quantisations, GEMMs, bias gradient) captured in one HIP
+    graph: three replays each equal the eager result bit for bit."""
+    from test_gpu_graph import _capture
+    T, H, Fr = 256, 512, 384
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    bf = torch.bfloat16
+    r = lambda *s, std=1.0: (torch.randn(*s, generator=g, device="cuda") * std).to(bf)  # noqa: E731
+    X, W1, b1, W2, dZ = r(T, H), r(H, Fr, std=0.02), r(Fr, std=0.02), r(Fr, H, std=0.02), r(T, H)
+    u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")  # noqa: E731
+    e = lambda *s: torch.empty(*s, dtype=bf, device="cuda")  # noqa: E731
+    qX, qXt, qW1, qW1t, qW2, qW2t, qY, qYt = u8(T, H), u8(H, T), u8(H, Fr), u8(Fr, H), u8(Fr, H), u8(H, Fr), \
+        u8(T, Fr), u8(Fr, T)
+    qdZ, qdZt, qdA1, qdA1t = u8(T, H), u8(H, T), u8(T, Fr), u8(Fr, T)
+    sc = [torch.empty(1, device="cuda") for _ in range(6)]
+    A1, Y, Z, dA1, dW2, dX, dW1, db1 = e(T, Fr), e(T, Fr), e(T, H), e(T, Fr), e(Fr, H), e(T, H), e(H, Fr), e(Fr)
+    ws = _ws()
+    wsb = bd.workspace("tp_bias_grad", 1, 0, T, 1, Fr, 1, 1, bf)
+    e4, e5 = bd.TP_FP8_E4M3, bd.TP_FP8_E5M2
+
+    def call():
+        bd.tp_fp8_quantize(X, qX, sc[0], ws, q_t=qXt)
+        bd.tp_fp8_quantize(W1, qW1, sc[1], ws, q_t=qW1t)
+        bd.tp_fp8_quantize(W2, qW2, sc[2], ws, q_t=qW2t)
+        bd.tp_fp8_gemm_nt(qX, sc[0], qW1t, sc[1], Y, bias=b1, epilogue=bd.TP_FP8_EPI_GELU, C_pre=A1)
+        bd.tp_fp8_quantize(Y, qY, sc[3], ws, q_t=qYt)
+        bd.tp_fp8_gemm_nt(qY, sc[3], qW2t, sc[2], Z)
+        bd.tp_fp8_quantize(dZ, qdZ, sc[4], ws, q_t=qdZt, fmt=e5)
+        bd.tp_fp8_gemm_nt(qdZ, sc[4], qW2, sc[2], dA1, epilogue=bd.TP_FP8_EPI_DGELU, aux=A1, a_fmt=e5, b_fmt=e4)
+        bd.tp_fp8_gemm_nt(qYt, sc[3], qdZt, sc[4], dW2, a_fmt=e4, b_fmt=e5)
+        bd.tp_fp8_quantize(dA1, qdA1, sc[5], ws, q_t=qdA1t, fmt=e5)
+        bd.tp_fp8_gemm_nt(qdA1, sc[5], qW1, sc[1], dX, a_fmt=e5, b_fmt=e4)
+        bd.tp_fp8_gemm_nt(qXt, sc[0], qdA1t, sc[5], dW1, a_fmt=e4, b_fmt=e5)
+        bd.tp_bias_grad(dA1, db1, wsb)
+    call()
+    torch.cuda.synchronize()
+    bufs = dict(A1=A1, Y=Y, Z=Z, dA1=dA1, dW2=dW2, dX=dX, dW1=dW1, db1=db1, qXt=qXt, qdA1t=qdA1t)
+    eager = {key: v.clone() for key, v in bufs.items()}
+    gr = _capture(call)
+    for rep in range(3):
+        for v in bufs.values():
+            v.fill_(0 if v.dtype == torch.uint8 else -1)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for key in bufs:
+            assert torch.equal(bufs[key], eager[key]), f"replay {rep}: {key} differs from the eager call"
+        call()
+        torch.cuda.synchronize()

@@ -197,3 +197,49 @@ def test_moe_bwd_full_size_rank0():
             ref_dx[i] += da1 @ h(W1[e]).T
     assert_close(host(dX)[pick], ref_dx, dtype, "dX_r sampled tokens")
     assert_close(host(dg)[pick], ref_dg, dtype, "dgates_r sampled tokens", tol=1e-4)
+
+
+def test_moe_fwd_bwd_graph_replay():
+    """Route, block forward, block backward and router backward captured in one HIP graph: three
+    replays (buffers scrambled before each, eager calls in between) each equal the eager result."""
+    from test_gpu_graph import _capture
+    tokens, H, E, k, F_expert, tp, rank, dtype = 256, 256, 8, 2, 256, 2, 1, "bf16"
+    n = tokens * k
+    lg = torch.from_numpy(_logits(tokens, E, "bwd_graph")).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    gates, ex, off = torch.empty(tokens, k, device="cuda"), torch.empty(tokens, k, **i32), torch.empty(E + 1, **i32)
+    rt, tr = torch.empty(n, **i32), torch.empty(tokens, k, **i32)
+    X = dev(synth.normal("moeXgb", (tokens, H), 1.0, dtype))
+    d_out = dev(synth.normal("moedgb", (tokens, H), 1.0, dtype))
+    Fr, W = _expert_weights(E, H, F_expert, tp, rank, dtype)
+    W1, b1, W2 = dev(W["W1"]), dev(W["b1"]), dev(W["W2"])
+    bf = torch.bfloat16
+    e = lambda *s: torch.empty(*s, dtype=bf, device="cuda")  # noqa: E731
+    out, Z, Y, A1 = e(tokens, H), e(n, H), e(n, Fr), e(n, Fr)
+    dX, dW1, db1, dW2 = e(tokens, H), e(E, H, Fr), e(E, Fr), e(E, Fr, H)
+    dg, dlog = torch.empty(tokens, k, device="cuda"), torch.empty(tokens, E, device="cuda")
+    wsr = bd.workspace("tp_moe_route", 1, 0, 1, tokens, 1, E, 1, torch.float32)
+    wsf = bd.workspace("tp_moe_shard_fwd", tp, rank, 1, n, H, E, F_expert, bf)
+    wsb = bd.workspace("tp_moe_shard_bwd", tp, rank, 1, n, H, E, F_expert, bf)
+
+    def call():
+        bd.tp_moe_route(tokens, E, k, lg, gates, ex, off, rt, tr, wsr)
+        bd.tp_moe_shard_fwd(tp, rank, tokens, H, E, k, F_expert, X, gates, off, rt, tr, W1, b1, W2, out, Z, A1, Y, wsf)
+        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, F_expert, X, gates, off, rt, tr, W1, W2, A1, Y, Z, d_out, dX, dg,
+                            dW1, db1, dW2, wsb)
+        bd.tp_moe_route_bwd(lg, ex, dg, dlog)
+    call()
+    torch.cuda.synchronize()
+    bufs = dict(out=out, Z=Z, Y=Y, A1=A1, dX=dX, dW1=dW1, db1=db1, dW2=dW2, dg=dg, dlog=dlog)
+    eager = {key: v.clone() for key, v in bufs.items()}
+    g = _capture(call)
+    for rep in range(3):
+        for v in bufs.values():
+            v.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in bufs:
+            assert torch.equal(bufs[key], eager[key]), f"replay {rep}: {key} differs from the eager call"
+        call()
+        torch.cuda.synchronize()
