@@ -193,6 +193,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
                                   void* dA1, void* dX, void* dW1, void* db1, void* dW2, void* ws, hipStream_t s,
                                   const int* x_rows, int x_rows_n) {
   if (groups <= 0) return hipSuccess;
+  if (groups > 65535) return hipErrorInvalidValue;   // the column sum's grid y (checked before any launch)
   int* off_s = (int*)ws;
   int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
   int* prefix2 = prefix1 + (groups + 1);     // m-tiles of the dX GEMM's
@@ -249,7 +250,6 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   {
     ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
     dim3 grid((Fr + 63) / 64, groups);
-    if (groups > 65535) return hipErrorInvalidValue;
     if (dtype == DT_BF16) grouped_colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
     else grouped_colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dA1, Fr, off_s, (float*)db1);
     e = hipGetLastError();
