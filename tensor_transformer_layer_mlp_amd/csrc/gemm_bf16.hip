@@ -535,6 +535,8 @@ using C5 = Tile<256, 256, 4, 2, 4, 32>;
 using C6 = Tile<256, 256, 4, 2, 5, 32>;
 using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
 using C8 = Tile<256, 192, 4, 2, 2, 64>;   // 2 waves / SIMD, 64x96 per wave
+using C9 = Tile<256, 256, 4, 2, 2, 32>;   // the gathered weight gradient: k = 32 frees the registers
+                                          // its row indices take (no spills; 14% faster than C0)
 constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256};
 constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
@@ -645,16 +647,22 @@ bool gemm_bf16_grouped_k_eligible(const GemmDesc& d) {
   return ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) == 0;
 }
 
-hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
-  using Cfg = C0;
+template <class Cfg, bool GK>
+static hipError_t grouped_k_t(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
   const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
   const long nwg = (long)tiles_m * tiles_n * groups;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   GroupedKArgs g{d, off, groups, c_stride};
-  if (d.a_rows) gemm_bf16_grouped_k_kernel<Cfg, true><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
-  else gemm_bf16_grouped_k_kernel<Cfg, false><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
+  gemm_bf16_grouped_k_kernel<Cfg, GK><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
+  // measured on the 128-expert weight gradients: the gathered form is 14% faster with k = 32 (C0
+  // spills there), the plain form 21% slower
+  if (d.a_rows) return grouped_k_t<C9, true>(d, off, groups, c_stride, s);
+  return grouped_k_t<C0, false>(d, off, groups, c_stride, s);
 }
 
 }  // namespace tp
