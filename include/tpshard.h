@@ -241,8 +241,9 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
                      const int* token_row, const void* W1_r, const void* b1_r, const void* W2_r, void* out_r,
                      void* Z_r, void* A1_r, void* Y_r, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of tp_mlp_grouped_shard_fwd, expert by expert on the same expert-sorted rows (the chain
- * rule of the dense MLP shard's backward applied to each expert's rows and weights):
+/* Backward of tp_mlp_grouped_shard_fwd (the experts as grouped GEMMs: "Megatron-LM — 架构与原理", §6,
+ * TE GroupedLinear), expert by expert on the same expert-sorted rows — the dense MLP shard's chain
+ * rule (tp_mlp_shard_bwd) applied to each expert's rows and weights:
  *   dA1 = (dZ_perm·W2_r[e]ᵀ) ∘ GeLU'(A1_r)     dX_perm = dA1·W1_r[e]ᵀ   (rows of expert e)
  *   dW1_r[e] = X_eᵀ·dA1_e ;  db1_r[e] = Σ_rows dA1_e ;  dW2_r[e] = Y_eᵀ·dZ_e
  * An expert without rows gets zero weight and bias gradients.  Shapes as the forward's; dX_perm and
@@ -256,9 +257,10 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
                              const void* A1_r, const void* Y_r, const void* dZ_perm, void* dX_perm, void* dW1_r,
                              void* db1_r, void* dW2_r, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of tp_moe_shard_fwd on rank r, given d_out [tokens, H], the gradient of the whole MoE
- * output (every rank receives it, as the copy / all-reduce pair gives the dense MLP its dZ), with
- * row (t, j) = token_row[t, j]:
+/* Backward of tp_moe_shard_fwd on rank r — the four beats route -> dispatch -> experts -> combine of
+ * "Megatron-LM — 架构与原理", §4, taken in reverse — given d_out [tokens, H], the gradient of the whole
+ * MoE output (every rank receives it, as the copy / all-reduce pair of the same section gives the
+ * dense MLP its dZ), with row (t, j) = token_row[t, j]:
  *   dZ[row] = gates[t, j]·d_out[t]            the combine's backward
  *   dgates_r[t, j] = ⟨d_out[t], Z_r[row]⟩      (fp32; a partial: Σ_r over ranks is the gate
  *                                              gradient, the combine being linear in the partials)
@@ -277,7 +279,8 @@ int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, in
                      const void* Z_r, const void* d_out, void* dX_r, float* dgates_r, void* dW1_r, void* db1_r,
                      void* dW2_r, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The router's logit gradient from the (complete) gate gradient, the top-k choice held fixed:
+/* The router's logit gradient from the (complete) gate gradient, the top-k choice held fixed (the
+ * backward of tp_moe_route's gates, the route beat of "Megatron-LM — 架构与原理", §4):
  * with p = softmax(logits[t]) and gates[t, j] = p[expert_idx[t, j]],
  *   d_logits[t, e] = Σ_j dgates[t, j]·p[i_j]·(δ(i_j, e) − p[e]),  i_j = expert_idx[t, j]
  * fp32 [tokens, E]; the softmax is recomputed from the fp32 logits.  E <= 1024, top_k <= 32. */
