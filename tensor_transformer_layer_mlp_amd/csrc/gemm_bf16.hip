@@ -193,6 +193,82 @@ __device__ __forceinline__ void epilogue4(const GemmDesc& d, int m, int n, f32x4
   *(bf16x4*)((bf16*)d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
 }
 
+// Epilogue of a finished BM x BN tile: the wave's accumulators (wave tile at (wm, wn) inside the tile,
+// FM x FN blocks of 16 x 16, lane layout as the MFMA leaves it) with bias / bias+GeLU / GeLU' applied,
+// stored to C (and C2).
+template <class Cfg, int EPI>
+__device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds,
+                                           f32x4 (&acc)[Cfg::FM][Cfg::FN], int wm, int wn, int wave, int lane) {
+  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+  if constexpr (Cfg::BM * Cfg::BN * 2 <= Cfg::STAGES * Cfg::STAGE) {
+    // Staged epilogue: the finished tile goes through LDS (row pitch 2·BN bytes, 16-byte granule q of
+    // row r at q ^ (r & 7)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
+    // two to four rows instead of 16-row x 32-byte scraps.
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int m = m0 + wm + 16 * i + r16, n = n0 + wn + 16 * j + g4;
+        f32x4 a = acc[i][j];
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+          if (n < d.N) {
+            const bf16x4 b = *(const bf16x4*)((const bf16*)d.bias + n);
+            for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
+          }
+        }
+        if constexpr (EPI == EPI_DGELU) {
+          if (m < d.M && n < d.N) {
+            const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
+            for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.act);
+          }
+        }
+        acc[i][j] = a;
+      }
+    constexpr int RB = Cfg::BN * 2, NG = Cfg::BN / 8;   // row bytes, 16-byte granules per row
+    auto stage_out = [&](bf16* out, bool gelu) {
+      __syncthreads();              // the k loop (or the previous pass) is done with the LDS
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+          const int r = wm + 16 * i + r16, c = wn + 16 * j + g4;
+          const int ob = ((((c >> 3) ^ (r & 7)) << 4) | ((c & 7) << 1));
+          f32x4 a = acc[i][j];
+          if (gelu)
+            for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.act);
+          *(TP_LDS bf16x4*)(lds + r * RB + ob) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+        }
+      __syncthreads();
+      const int tid = wave * 64 + lane;
+#pragma unroll 4
+      for (int c = tid; c < Cfg::BM * NG; c += Cfg::NT) {
+        const int r = c / NG, q = c % NG;
+        const int m = m0 + r, n = n0 + 8 * q;
+        if (m < d.M && n < d.N)
+          *(bf16x8*)(out + (long)m * d.ldc + n) = *(const TP_LDS bf16x8*)(lds + r * RB + ((q ^ (r & 7)) << 4));
+      }
+    };
+    if constexpr (EPI == EPI_BIAS_GELU) {
+      if (d.C2) stage_out((bf16*)d.C2, false);
+      stage_out((bf16*)d.C, true);
+    } else {
+      stage_out((bf16*)d.C, false);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int m = m0 + wm + 16 * i + r16;
+      if (m >= d.M) continue;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int n = n0 + wn + 16 * j + g4;
+        if (n < d.N) epilogue4<EPI>(d, m, n, acc[i][j]);
+      }
+    }
+  }
+}
+
 // One BM x BN output tile at (m0, n0): the k loop over LDS stages and the fused epilogue.
 template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false, bool GATHER_K = false>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
@@ -315,74 +391,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
     if (++cur_stage == Cfg::STAGES) cur_stage = 0;
   }
 
-  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
-  if constexpr (Cfg::BM * Cfg::BN * 2 <= Cfg::STAGES * Cfg::STAGE) {
-    // Staged epilogue: the finished tile goes through LDS (row pitch 2·BN bytes, 16-byte granule q of
-    // row r at q ^ (r & 7)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
-    // two to four rows instead of 16-row x 32-byte scraps.
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        const int m = m0 + wm + 16 * i + r16, n = n0 + wn + 16 * j + g4;
-        f32x4 a = acc[i][j];
-        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-          if (n < d.N) {
-            const bf16x4 b = *(const bf16x4*)((const bf16*)d.bias + n);
-            for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
-          }
-        }
-        if constexpr (EPI == EPI_DGELU) {
-          if (m < d.M && n < d.N) {
-            const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
-            for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.act);
-          }
-        }
-        acc[i][j] = a;
-      }
-    constexpr int RB = Cfg::BN * 2, NG = Cfg::BN / 8;   // row bytes, 16-byte granules per row
-    auto stage_out = [&](bf16* out, bool gelu) {
-      __syncthreads();              // the k loop (or the previous pass) is done with the LDS
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-          const int r = wm + 16 * i + r16, c = wn + 16 * j + g4;
-          const int ob = ((((c >> 3) ^ (r & 7)) << 4) | ((c & 7) << 1));
-          f32x4 a = acc[i][j];
-          if (gelu)
-            for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.act);
-          *(TP_LDS bf16x4*)(lds + r * RB + ob) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-        }
-      __syncthreads();
-      const int tid = wave * 64 + lane;
-#pragma unroll 4
-      for (int c = tid; c < Cfg::BM * NG; c += Cfg::NT) {
-        const int r = c / NG, q = c % NG;
-        const int m = m0 + r, n = n0 + 8 * q;
-        if (m < d.M && n < d.N)
-          *(bf16x8*)(out + (long)m * d.ldc + n) = *(const TP_LDS bf16x8*)(lds + r * RB + ((q ^ (r & 7)) << 4));
-      }
-    };
-    if constexpr (EPI == EPI_BIAS_GELU) {
-      if (d.C2) stage_out((bf16*)d.C2, false);
-      stage_out((bf16*)d.C, true);
-    } else {
-      stage_out((bf16*)d.C, false);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-      const int m = m0 + wm + 16 * i + r16;
-      if (m >= d.M) continue;
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        const int n = n0 + wn + 16 * j + g4;
-        if (n < d.N) epilogue4<EPI>(d, m, n, acc[i][j]);
-      }
-    }
-  }
+  store_tile<Cfg, EPI>(d, m0, n0, lds, acc, wm, wn, wave, lane);
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
@@ -408,6 +417,135 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   // Tiles that run together begin their k loops at different k-tiles, so that their concurrent
   // loads of strided operand rows fall on different memory channels (measured: 2-4% per GEMM).
   gemm_tile<Cfg, AK, BK, EPI>(d, m0, n0, (TP_LDS char*)smem, wave, lane, tm + tn);
+}
+
+// Ping-pong schedule on a 256 x 192 tile (k = 64 per tile, two LDS stages, 512 threads).  The eight
+// waves form two groups of four, group g = waves 4g .. 4g+3, so each SIMD holds one wave of each
+// group.  Group g owns output rows [128g, 128g + 128) of the tile (a 2 x 2 arrangement of 64 x 96 wave
+// tiles).  Every wave alternates a memory phase (issue its share of the next k-tile's global -> LDS
+// loads, read all of its fragments of the current k-tile from LDS) and a compute phase (the k-tile's
+// MFMAs), and group 1 runs one phase behind group 0: while one wave of a SIMD multiplies, the other
+// reads LDS, so the matrix core is not left idle during the fragment reads.  All eight waves meet at
+// every phase boundary (s_barrier), which keeps the two groups exactly one phase apart.
+//
+// Tile t sits in stage t & 1.  Its B part and the rows of A group 0 uses are loaded by group 0 during
+// its memory phase of tile t-1 (after that phase's fragment reads); the rows group 1 uses by group 1
+// during its memory phase of tile t-1.
+// Each group waits for its own loads at the end of its following compute phase, so every load has two
+// phases to land, and a stage is only overwritten after both groups' reads of it have completed (the
+// memory phase ends with lgkmcnt(0) before its barrier).
+struct PPTile {
+  static constexpr int BM = 256, BN = 192, BKT = 64, NKK = 2, NT = 512, STAGES = 2;
+  static constexpr int HALF = 128;                        // A rows per group
+  static constexpr int FM = 4, FN = 6;                    // 64 x 96 per wave
+  static constexpr int A_HALF = HALF * BKT * 2;           // 16 KiB (either layout: pitch 128)
+  static constexpr int B_OFF = 2 * A_HALF;
+  static constexpr int STAGE = B_OFF + 256 * BKT * 2;     // B: 192 rows (K-major) or pitch 256 (MN-major)
+};
+
+// Phase boundaries: every wave's LDS reads (lgkmcnt) or its global -> LDS loads (vmcnt) complete, then
+// all waves of the workgroup meet.  sched_barrier keeps the compiler from moving MFMAs or memory
+// operations across the boundary.
+__device__ __forceinline__ void pp_sync_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void pp_sync_vm() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void pp_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool AK, bool BK, int EPI>
+__device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
+                                             int lane, int rot) {
+  using P = PPTile;
+  constexpr int LB = BK ? P::BN : 256;                        // B rows (K-major) or pitch (MN-major)
+  constexpr int B_BYTES = BK ? P::BN * P::BKT * 2 : 256 * P::BKT * 2;
+  constexpr int IPW_A = P::A_HALF / 1024 / 4, IPW_B = B_BYTES / 1024 / 4;   // loads per wave of a group
+  static_assert(B_BYTES % 4096 == 0 && P::STAGES * P::STAGE <= 160 * 1024, "tile layout");
+  const int g = wave >> 2, w4 = wave & 3;                     // wave-uniform
+  const Operand A{(const bf16*)d.A, d.lda, d.M};
+  const Operand B{(const bf16*)d.B, d.ldb, d.N};
+  int ar[IPW_A], ac[IPW_A], br[IPW_B], bc[IPW_B];
+#pragma unroll
+  for (int j = 0; j < IPW_A; ++j) piece<AK, P::HALF, P::BKT>((w4 * IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
+#pragma unroll
+  for (int j = 0; j < IPW_B; ++j) piece<BK, LB, P::BKT>((w4 * IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+
+  const int nk = (d.K + P::BKT - 1) / P::BKT;
+  rot = nk > 0 ? rot % nk : 0;
+  auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * P::BKT; };
+  // this wave's share of k-tile t's loads into stage st
+  auto issue = [&](int t, int st) {
+    TP_LDS char* base = lds + st * P::STAGE;
+    const int k = kpos(t);
+    load_tile<AK, P::HALF, P::HALF, IPW_A, P::BKT>(A, m0 + P::HALF * g, k, d.K, base + g * P::A_HALF, ar, ac, w4);
+    if (g == 0) load_tile<BK, LB, P::BN, IPW_B, P::BKT>(B, n0, k, d.K, base + P::B_OFF, br, bc, w4);
+  };
+
+  const int wml = (w4 >> 1) * 64, wn = (w4 & 1) * 96;         // wave tile inside the group's rows
+  f32x4 acc[P::FM][P::FN];
+#pragma unroll
+  for (int i = 0; i < P::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < P::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) issue(0, 0);
+  pp_sync_vm();                  // k-tile 0 is in stage 0
+  if (g == 1) pp_sync();         // group 1 starts one phase behind
+  for (int t = 0; t < nk; ++t) {
+    const int st = t & 1;
+    // memory phase: every fragment of this k-tile, then the next k-tile's loads (after the reads: the
+    // compiler would otherwise wait for those loads before the transposed LDS reads, which it cannot
+    // tell apart from the loads' LDS destination)
+    const TP_LDS char* at = lds + st * P::STAGE + g * P::A_HALF;
+    const TP_LDS char* bt = lds + st * P::STAGE + P::B_OFF;
+    bf16x8 af[P::NKK][P::FM], bfr[P::NKK][P::FN];
+#pragma unroll
+    for (int q = 0; q < P::NKK; ++q) {
+#pragma unroll
+      for (int i = 0; i < P::FM; ++i) af[q][i] = frag<AK, P::HALF, P::BKT>(at, wml + 16 * i, 32 * q, lane);
+#pragma unroll
+      for (int j = 0; j < P::FN; ++j) bfr[q][j] = frag<BK, LB, P::BKT>(bt, wn + 16 * j, 32 * q, lane);
+    }
+    if (t + 1 < nk) issue(t + 1, st ^ 1);
+    pp_sync_lds();
+    // compute phase
+#pragma unroll
+    for (int q = 0; q < P::NKK; ++q)
+#pragma unroll
+      for (int i = 0; i < P::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < P::FN; ++j) acc[i][j] = mfma_16x16x32_bf16(bfr[q][j], af[q][i], acc[i][j]);
+    pp_sync_vm();
+  }
+  if (g == 0) pp_sync();         // both groups have passed the same number of barriers
+  store_tile<P, EPI>(d, m0, n0, lds, acc, P::HALF * g + wml, wn, wave, lane);
+}
+
+template <bool AK, bool BK, int EPI>
+__global__ __launch_bounds__(PPTile::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_pp_kernel(GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[PPTile::STAGES * PPTile::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // workgroup -> tile order as in gemm_bf16_kernel (contiguous runs per XCD, groups of 4 tile rows)
+  constexpr int GROUP_M = 4;
+  const int nwg = tiles_m * tiles_n;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (wg / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
+  gemm_tile_pp<AK, BK, EPI>(d, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
 }
 
 // Grouped GEMM: expert e owns rows [off[e], off[e+1]) of A and C and its own B (and bias), at
@@ -507,6 +645,27 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool AK, bool BK, int EPI>
+hipError_t run_pp(const GemmDesc& d, hipStream_t s) {
+  const int tiles_m = (d.M + PPTile::BM - 1) / PPTile::BM, tiles_n = (d.N + PPTile::BN - 1) / PPTile::BN;
+  gemm_bf16_pp_kernel<AK, BK, EPI><<<tiles_m * tiles_n, PPTile::NT, 0, s>>>(d, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t run_pp_cfg(const GemmDesc& d, hipStream_t s) {
+  if (d.a_kmajor && !d.b_kmajor) {
+    if (d.epi == EPI_BIAS) return run_pp<true, false, EPI_BIAS>(d, s);
+    if (d.epi == EPI_BIAS_GELU) return run_pp<true, false, EPI_BIAS_GELU>(d, s);
+    if (d.epi == EPI_STORE) return run_pp<true, false, EPI_STORE>(d, s);
+  } else if (d.a_kmajor && d.b_kmajor) {
+    if (d.epi == EPI_DGELU) return run_pp<true, true, EPI_DGELU>(d, s);
+    if (d.epi == EPI_STORE) return run_pp<true, true, EPI_STORE>(d, s);
+  }
+  // Xᵀ·dY (both operands MN-major) is not taken: two operands of transposed LDS reads make the memory
+  // phase longer than the compute phase (measured 15% slower than the plain 256 x 192 kernel)
+  return hipErrorNotSupported;
+}
+
 template <class Cfg>
 hipError_t run_cfg(const GemmDesc& d, hipStream_t s) {
   // the layouts and epilogues the shard uses: X·W (A K-major, B MN-major) with bias / bias+GeLU /
@@ -537,12 +696,13 @@ using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
 using C8 = Tile<256, 192, 4, 2, 2, 64>;   // 2 waves / SIMD, 64x96 per wave
 using C9 = Tile<256, 256, 4, 2, 2, 32>;   // the gathered weight gradient: k = 32 frees the registers
                                           // its row indices take (no spills; 14% faster than C0)
-constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256};
-constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192};
+// 9: the ping-pong 256 x 192 kernel (gemm_bf16_pp_kernel)
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192, 192};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95};
+constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95, 1.2};
 constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
-                                     "256x256k32s4", "256x256k32s5", "256x256w4", "256x192"};
+                                     "256x256k32s4", "256x256k32s5", "256x256w4", "256x192", "256x192pp"};
 
 }  // namespace
 
@@ -571,7 +731,8 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   // modelled time: (number of 256-CU waves of tiles) x (tile area) / (relative rate)
   int best = 0;
   double best_t = 1e300;
-  for (int c : {0, 8, 1, 2, 3}) {
+  for (int c : {9, 0, 8, 1, 2, 3}) {
+    if (c == 9 && !d.a_kmajor) continue;   // the ping-pong tile takes X·W and dY·Wᵀ only
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
     const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
     if (est < best_t * 0.999) { best_t = est; best = c; }
@@ -591,6 +752,7 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 5: return run_cfg<C5>(d, s);
     case 6: return run_cfg<C6>(d, s);
     case 7: return run_cfg<C7>(d, s);
+    case 9: return run_pp_cfg(d, s);
     default: return run_cfg<C8>(d, s);
   }
 }

@@ -1,0 +1,83 @@
+"""GPU parity of the ping-pong GEMM tile (256 x 192, two groups of four waves one phase apart).
+
+The tile is chosen for large problems with a K-major A only, so these MLP shard shapes are sized to
+make the MLP's X·W and dY·Wᵀ GEMMs take it: M, N around 2100 (ragged against 256, 192 and 64), and in
+one workload a k dimension of 40, a single partial k-tile.  They cover both operand layouts it takes
+and every epilogue (bias, bias + GeLU with A1 kept, plain, ∘GeLU′).  Expected values are
+the fp64 oracle's on the same seeded inputs; the bar is the bf16 one (normwise 2e-2).
+"""
+
+import pytest
+import torch
+
+import oracle
+from gpu_harness import Shard, assert_close, empty
+from tensor_transformer_layer_mlp_amd import binding as bd
+from tensor_transformer_layer_mlp_amd.configs import LayerWorkload
+
+pytestmark = pytest.mark.gpu
+
+PP_BIG = LayerWorkload("pp_b1_s2056_h2104_nh8_f4176_tp2", 1, 2056, 2104, 8, 4176, 2, (0, 1), 0.03)
+# fc2 and the MLP's dX with K = F_r = 40
+PP_K1 = LayerWorkload("ppk1_b1_s2056_h2104_nh8_f80_tp2", 1, 2056, 2104, 8, 80, 2, (1,), 0.03)
+
+
+def cases():
+    for wl in (PP_BIG, PP_K1):
+        for r in wl.ranks:
+            yield pytest.param(wl, r, id=f"{wl.name}-r{r}")
+
+
+def pp_launches():
+    return {tag: v[0] for tag, v in bd.tp_prof_collect().items() if "256x192pp" in tag}
+
+
+@pytest.mark.parametrize("wl,rank", list(cases()))
+def test_mlp_fwd_pingpong(wl, rank):
+    sh = Shard(wl, rank, "bf16")
+    T, H = wl.T, wl.H
+    Z, A1, Y = empty((T, H), "bf16"), empty((T, sh.Fr), "bf16"), empty((T, sh.Fr), "bf16")
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        bd.tp_mlp_shard_fwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("b1"), sh.d_("W2"),
+                            sh.d_("b2"), Z, A1, Y)
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    used = pp_launches()
+    # with F_r = 40 (PP_K1) fc1 (N = 40) takes another tile
+    expect = {PP_BIG.name: 2, PP_K1.name: 1}[wl.name]
+    assert sum(used.values()) == expect, f"ping-pong launches {used}"
+    ref = oracle.tp_mlp_shard_fwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("b1"),
+                                  sh.f64("W2"), sh.f64("b2"))
+    assert_close(A1, ref["A1"], "bf16", "A1_r")
+    assert_close(Y, ref["Y"], "bf16", "Y_r")
+    assert_close(Z, ref["Z"], "bf16", "Z_r")
+
+
+@pytest.mark.parametrize("wl,rank", list(cases()))
+def test_mlp_bwd_pingpong(wl, rank):
+    sh = Shard(wl, rank, "bf16")
+    T, H, Fr = wl.T, wl.H, sh.Fr
+    o = dict(dX=empty((T, H), "bf16"), dW1=empty((H, Fr), "bf16"), db1=empty((Fr,), "bf16"),
+             dW2=empty((Fr, H), "bf16"), db2=empty((H,), "bf16"))
+    ws = bd.workspace("tp_mlp_shard_bwd", wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, wl.F, torch.bfloat16)
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        bd.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("W2"), sh.d_("A1"),
+                            sh.d_("Y"), sh.d_("dZ"), o["dX"], o["dW1"], o["db1"], o["dW2"], o["db2"], ws)
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    used = pp_launches()
+    # dA1 and dX (the weight gradients are Xᵀ·dY); with F_r = 40 (PP_K1) dA1 (N = 40) takes another tile
+    expect = {PP_BIG.name: 2, PP_K1.name: 1}[wl.name]
+    assert sum(used.values()) == expect, f"ping-pong launches {used}"
+    ref = oracle.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("W2"),
+                                  sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
+    for k in ("dX", "dW1", "db1", "dW2"):
+        assert_close(o[k], ref[k], "bf16", k)
+    if rank == 0:
+        assert_close(o["db2"], ref["db2"], "bf16", "db2")
