@@ -444,23 +444,25 @@ struct PPTile {
 };
 
 // Phase boundaries: every wave's LDS reads (lgkmcnt) or its global -> LDS loads (vmcnt) complete, then
-// all waves of the workgroup meet.  sched_barrier keeps the compiler from moving MFMAs or memory
-// operations across the boundary.
-__device__ __forceinline__ void pp_sync_lds() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void pp_sync_vm() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void pp_sync() {
+// all waves of the workgroup meet.  The waits are the s_waitcnt builtin, which the compiler's own wait
+// placement takes into account (a wait it cannot see makes it wait again later, on younger loads);
+// sched_barrier keeps the compiler from moving MFMAs or memory operations across the boundary.
+__device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+__device__ __forceinline__ void pp_sync_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) alone
+  pp_barrier();
+}
+__device__ __forceinline__ void pp_sync_vm() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();
+  pp_barrier();
+}
+__device__ __forceinline__ void pp_sync() { pp_barrier(); }
 
 template <bool AK, bool BK, int EPI>
 __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
