@@ -733,6 +733,14 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   // modelled time: (number of 256-CU waves of tiles) x (tile area) / (relative rate)
   int best = 0;
   double best_t = 1e300;
+  // Xᵀ·dY (the weight gradients): both operands come through transposed LDS reads, and the 256 x 256
+  // tile moves ≈14% fewer LDS bytes per flop than 256 x 192; on outputs of 4096 x 4096 and more it was
+  // measured faster despite its coarser rounds (its partial last round fills with the concurrent
+  // input-gradient GEMM)
+  if (!d.a_kmajor && !d.b_kmajor && (long)d.M * d.N >= 4096L * 4096L) {
+    *cfg = 0;
+    return kTileName[0];
+  }
   for (int c : {9, 0, 8, 1, 2, 3}) {
     if (c == 9 && !d.a_kmajor) continue;   // the ping-pong tile takes X·W and dY·Wᵀ only
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);

@@ -1,4 +1,6 @@
-"""GPU parity of the ping-pong GEMM tile (256 x 192, two groups of four waves one phase apart).
+"""GPU parity of the large-problem GEMM tiles: the ping-pong 256 x 192 tile (two groups of four waves
+one phase apart) on X·W and dY·Wᵀ, and the 256 x 256 tile the weight gradients Xᵀ·dY take from
+4096 x 4096 outputs on.
 
 The tile is chosen for large problems with a K-major A only, so these MLP shard shapes are sized to
 make the MLP's X·W and dY·Wᵀ GEMMs take it: M, N around 2100 (ragged against 256, 192 and 64), and in
@@ -81,3 +83,30 @@ def test_mlp_bwd_pingpong(wl, rank):
         assert_close(o[k], ref[k], "bf16", k)
     if rank == 0:
         assert_close(o["db2"], ref["db2"], "bf16", "db2")
+
+
+# both weight gradients [4104, 4104] (ragged against 256) over K = T = 136 (ragged against 64)
+WG_BIG = LayerWorkload("wg_b1_s136_h4104_nh8_f8208_tp2", 1, 136, 4104, 8, 8208, 2, (0,), 0.03)
+
+
+def test_weight_gradients_256_tile():
+    wl, rank = WG_BIG, 0
+    sh = Shard(wl, rank, "bf16")
+    T, H, Fr = wl.T, wl.H, sh.Fr
+    o = dict(dX=empty((T, H), "bf16"), dW1=empty((H, Fr), "bf16"), db1=empty((Fr,), "bf16"),
+             dW2=empty((Fr, H), "bf16"), db2=empty((H,), "bf16"))
+    ws = bd.workspace("tp_mlp_shard_bwd", wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, wl.F, torch.bfloat16)
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        bd.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("W2"), sh.d_("A1"),
+                            sh.d_("Y"), sh.d_("dZ"), o["dX"], o["dW1"], o["db1"], o["dW2"], o["db2"], ws)
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    used = {tag: v[0] for tag, v in bd.tp_prof_collect().items() if "256x256, tn" in tag}
+    assert sum(used.values()) == 2, f"256 x 256 weight-gradient launches {used}"
+    ref = oracle.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("W2"),
+                                  sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
+    for k in ("dX", "dW1", "db1", "dW2", "db2"):
+        assert_close(o[k], ref[k], "bf16", k)
