@@ -326,24 +326,30 @@ __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, i
 }
 
 // ---------------------------------------------------------------------------------------------
+// D_i = Σ_c dO_ic·O_ic for every (token, head) row: 16 lanes per row, each lane one 16-byte piece of
+// both rows (pieces past d contribute zero), summed across the 16 lanes in a fixed butterfly order;
+// 16 rows per workgroup.  Consecutive rows (heads of a token, then tokens) are contiguous in ctx and
+// dctx, so each wave reads 1 KiB runs.
 template <int D>
 __global__ __launch_bounds__(256) void attn_rowdot(int B, int S, int nh, const bf16* __restrict__ ctx,
                                                    const bf16* __restrict__ dctx, float* __restrict__ Dws) {
-  const long id = (long)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (long)B * S * nh) return;
-  const int h = (int)(id % nh);
-  const long t = id / nh;
-  const bf16* o = ctx + t * nh * D + (long)h * D;
-  const bf16* dO = dctx + t * nh * D + (long)h * D;
+  static_assert(D % 8 == 0 && D <= 128, "16 lanes of 8 elements cover a row");
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);   // row = token·nh + head
+  const int l = threadIdx.x & 15;
+  const long rows = (long)B * S * nh;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const bf16x8 a = *(const bf16x8*)(o + c), z = *(const bf16x8*)(dO + c);
+  if (row < rows && 8 * l < D) {
+    const bf16x8 a = *(const bf16x8*)(ctx + row * D + 8 * l), z = *(const bf16x8*)(dctx + row * D + 8 * l);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)z[e];
   }
-  const long b = t / S, s = t % S;
-  Dws[(b * nh + h) * S + s] = acc;
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && l == 0) {
+    const int h = (int)(row % nh);
+    const long t = row / nh, b = t / S, s = t % S;
+    Dws[(b * nh + h) * S + s] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -700,7 +706,7 @@ hipError_t bwd_t(int B, int S, int nh, const void* qkv, const void* ctx, const f
   constexpr int G = AttnShape<D>::G, KB = AttnShape<D>::KB;
   const int nqb = (S + 63) / 64;
   const long rows = (long)B * S * nh;
-  attn_rowdot<D><<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
+  attn_rowdot<D><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
   attn_bwd_dkv_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
                                                                (const bf16*)dctx, lse, ws, (bf16*)dqkv);
   attn_bwd_dq_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
