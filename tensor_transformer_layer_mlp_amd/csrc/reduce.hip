@@ -29,7 +29,20 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
   for (int j = 0; j < 8; ++j) s[j] = 0.f;
   const bool vec = (c0 + 8 <= cols) && ((ld * sizeof(T)) % 16 == 0) && (((uintptr_t)in) % 16 == 0);
   if (c0 < cols) {
-    for (int r = r0 + rg; r < r1; r += CS_RG) {
+    int r = r0 + rg;
+    if constexpr (sizeof(T) == 2) {
+      // a whole 64-row block: all eight rows' loads issued before the adds (same order of addition)
+      if (vec && r1 - r0 == CS_ROWS) {
+        bf16x8 v[CS_ROWS / CS_RG];
+#pragma unroll
+        for (int i = 0; i < CS_ROWS / CS_RG; ++i) v[i] = *(const bf16x8*)(in + (long)(r + CS_RG * i) * ld + c0);
+#pragma unroll
+        for (int i = 0; i < CS_ROWS / CS_RG; ++i)
+          for (int j = 0; j < 8; ++j) s[j] += (float)v[i][j];
+        r = r1;
+      }
+    }
+    for (; r < r1; r += CS_RG) {
       const T* p = in + (long)r * ld + c0;
       if (vec) {
         if constexpr (sizeof(T) == 2) {
@@ -63,8 +76,18 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
   __shared__ float red[4][64];
   const int c = blockIdx.x * 64 + (threadIdx.x & 63), g = threadIdx.x >> 6;
   float s = 0.f;
-  if (c < cols)
-    for (int k = g; k < chunks; k += 4) s += ws[(long)k * cols + c];
+  if (c < cols) {
+    int k = g;
+    // eight partials' loads at a time, added in the same order
+    for (; k + 28 < chunks; k += 32) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = ws[(long)(k + 4 * i) * cols + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; k < chunks; k += 4) s += ws[(long)k * cols + c];
+  }
   red[g][threadIdx.x & 63] = s;
   __syncthreads();
   if (g == 0 && c < cols) out[c] = from_f32<T>(((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x]);
