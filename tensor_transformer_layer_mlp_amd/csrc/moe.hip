@@ -26,6 +26,8 @@
 //   moe_route_bwd_kernel    one wave per token: the softmax again from the fp32 logits, then
 //                       d_logits[e] = p_e·(dg(e) − Σ_j dg_j·p_{i_j}), dg(e) the gradient of the gate
 //                       that chose e (0 if none did).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -177,47 +179,6 @@ __global__ __launch_bounds__(1024) void moe_zero_offsets_kernel(int E, int* __re
   for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = 0;
 }
 
-template <typename T, int V>
-__global__ __launch_bounds__(256) void moe_combine_kernel(int k, int H, const T* __restrict__ Z,
-                                                          const float* __restrict__ gates,
-                                                          const int* __restrict__ token_row, int rows,
-                                                          T* __restrict__ out) {
-  const long t = blockIdx.x;
-  for (int c = V * threadIdx.x; c < H; c += V * 256) {
-    float acc[V];
-#pragma unroll
-    for (int q = 0; q < V; ++q) acc[q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = token_row[t * k + j];
-      if (r < 0 || r >= rows) continue;
-      const float g = gates ? gates[t * k + j] : 1.f;
-      const T* src = Z + (long)r * H + c;
-      if constexpr (V == 8) {
-        const bf16x8 z = *(const bf16x8*)src;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += g * (float)z[q];
-      } else if constexpr (V == 4) {
-        const f32x4 z = *(const f32x4*)src;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += g * z[q];
-      } else {
-        acc[0] += g * to_f32(*src);
-      }
-    }
-    T* dst = out + t * H + c;
-    if constexpr (V == 8) {
-      bf16x8 o;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = (bf16)acc[q];
-      *(bf16x8*)dst = o;
-    } else if constexpr (V == 4) {
-      *(f32x4*)dst = (f32x4){acc[0], acc[1], acc[2], acc[3]};
-    } else {
-      *dst = from_f32<T>(acc[0]);
-    }
-  }
-}
-
 // V consecutive elements at p as fp32 (V = 8: bf16 16-byte vector, 4: fp32 vector, 1: scalar).
 template <typename T, int V>
 __device__ __forceinline__ void load_v(const T* p, float (&v)[V]) {
@@ -245,6 +206,60 @@ __device__ __forceinline__ void store_v(T* p, const float (&v)[V]) {
     *(f32x4*)p = (f32x4){v[0], v[1], v[2], v[3]};
   } else {
     *p = from_f32<T>(v[0]);
+  }
+}
+
+// V elements at p as loaded (no conversion, so the load need not complete before the next is issued).
+template <typename T, int V>
+struct RawV {
+  using type = typename std::conditional<V == 8, bf16x8, typename std::conditional<V == 4, f32x4, T>::type>::type;
+  static __device__ __forceinline__ type load(const T* p) { return *(const type*)p; }
+  static __device__ __forceinline__ float at(const type& v, int q) {
+    if constexpr (V == 1) return to_f32(v);
+    else return (float)v[q];
+  }
+};
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void moe_combine_kernel(int k, int H, const T* __restrict__ Z,
+                                                          const float* __restrict__ gates,
+                                                          const int* __restrict__ token_row, int rows,
+                                                          T* __restrict__ out) {
+  static_assert(V == 1 || (V == 8 && sizeof(T) == 2) || (V == 4 && sizeof(T) == 4), "vector width");
+  constexpr int NB = 8;   // rows whose loads are in flight together
+  using R = RawV<T, V>;
+  const long t = blockIdx.x;
+  if (rows <= 0) {   // nothing to combine: every row index is out of range
+    const float zero[V] = {};
+    for (int c = V * threadIdx.x; c < H; c += V * 256) store_v<T, V>(out + t * H + c, zero);
+    return;
+  }
+  for (int c = V * threadIdx.x; c < H; c += V * 256) {
+    float acc[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += NB) {
+      // the batch's loads first (a row outside [0, rows) or past k reads row 0, when there is one, and
+      // is skipped), then the adds in row order: the same order of addition as one row at a time
+      bool ok[NB];
+      float g[NB];
+      typename R::type z[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int j = j0 + i;
+        const int r = j < k ? token_row[t * k + j] : -1;
+        ok[i] = r >= 0 && r < rows;
+        g[i] = j < k && gates ? gates[t * k + j] : 1.f;
+        z[i] = R::load(Z + (long)(ok[i] ? r : 0) * H + c);   // row 0 exists (rows > 0)
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (!ok[i]) continue;
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] += g[i] * R::at(z[i], q);
+      }
+    }
+    store_v<T, V>(out + t * H + c, acc);
   }
 }
 
