@@ -270,37 +270,63 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(int k, int H, cons
                                                               const int* __restrict__ token_row, int rows,
                                                               T* __restrict__ dZ, T* __restrict__ Xp,
                                                               float* __restrict__ dgates) {
-  __shared__ float red[4];
+  // The token's rows in batches of eight: per 16-byte piece of the row, d_out (and X) are read once
+  // and the batch's Z pieces are in flight together; each row's gate-gradient partial accumulates
+  // over the pieces in column order and is reduced across the workgroup once per batch, in the same
+  // order as one row at a time.  A row outside [0, rows) (or past k) reads row 0, writes nothing and
+  // gets a zero gate gradient.
+  constexpr int NB = 8;
+  using R = RawV<T, V>;
+  __shared__ float red[4][NB];
   const long t = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int j = 0; j < k; ++j) {
-    const int r = token_row[t * k + j];
-    const bool ok = r >= 0 && r < rows;
-    const float g = gates[t * k + j];
-    float dot = 0.f;
-    if (ok) {
-      for (int c = V * threadIdx.x; c < H; c += V * 256) {
-        float o[V], z[V], dz[V];
-        load_v<T, V>(d_out + t * H + c, o);
-        load_v<T, V>(Z + (long)r * H + c, z);
+  for (int j0 = 0; j0 < k; j0 += NB) {
+    int r[NB];
+    bool ok[NB];
+    float g[NB], dot[NB];
 #pragma unroll
-        for (int q = 0; q < V; ++q) {
-          dot += o[q] * z[q];
-          dz[q] = g * o[q];
-        }
-        store_v<T, V>(dZ + (long)r * H + c, dz);
-        if (Xp) {
-          float x[V];
-          load_v<T, V>(X + t * H + c, x);
-          store_v<T, V>(Xp + (long)r * H + c, x);
+    for (int i = 0; i < NB; ++i) {
+      const int j = j0 + i;
+      const int rr = j < k ? token_row[t * k + j] : -1;
+      ok[i] = rr >= 0 && rr < rows;
+      r[i] = ok[i] ? rr : 0;
+      g[i] = j < k ? gates[t * k + j] : 0.f;
+      dot[i] = 0.f;
+    }
+    if (rows > 0) {
+      for (int c = V * threadIdx.x; c < H; c += V * 256) {
+        float o[V], x[V];
+        load_v<T, V>(d_out + t * H + c, o);
+        typename R::type z[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) z[i] = R::load(Z + (long)r[i] * H + c);
+        if (Xp) load_v<T, V>(X + t * H + c, x);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if (!ok[i]) continue;
+          float dz[V];
+#pragma unroll
+          for (int q = 0; q < V; ++q) {
+            dot[i] += o[q] * R::at(z[i], q);
+            dz[q] = g[i] * o[q];
+          }
+          store_v<T, V>(dZ + (long)r[i] * H + c, dz);
+          if (Xp) store_v<T, V>(Xp + (long)r[i] * H + c, x);
         }
       }
     }
 #pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, 64);
-    if (lane == 0) red[w] = dot;
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) dot[i] += __shfl_xor(dot[i], sh, 64);
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) red[w][i] = dot[i];
     __syncthreads();
-    if (threadIdx.x == 0) dgates[t * k + j] = ok ? ((red[0] + red[1]) + red[2]) + red[3] : 0.f;
+    if (threadIdx.x < NB && j0 + (int)threadIdx.x < k) {
+      const int i = threadIdx.x;
+      dgates[t * k + j0 + i] = ok[i] ? ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i] : 0.f;
+    }
     __syncthreads();
   }
 }
