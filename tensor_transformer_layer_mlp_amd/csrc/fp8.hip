@@ -309,6 +309,44 @@ struct F8Desc {
   int epi;                  // 0 none, 1 GeLU, 2 tanh GeLU, 3 ∘ GeLU'(aux), 4 ∘ tanh GeLU'(aux)
 };
 
+// Scale by the two descales, bias, GeLU / GeLU' epilogues, bf16 stores of the wave's FM x FN blocks at
+// (wm, wn) inside the tile at (m0, n0).
+template <int FM, int FN>
+__device__ __forceinline__ void f8_epilogue(const F8Desc& d, int m0, int n0, int wm, int wn, int lane,
+                                            const f32x4 (&acc)[FM][FN]) {
+  const float sc = *d.da * *d.db;
+  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm + 16 * i + r16;
+    if (m >= d.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn + 16 * j + g4;
+      if (n >= d.N) continue;
+      float a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = acc[i][j][e] * sc;
+      if (d.bias) {
+        const bf16x4 b = *(const bf16x4*)(d.bias + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
+      }
+      const long o = (long)m * d.N + n;
+      if (d.epi == 1 || d.epi == 2) {
+        if (d.C2) *(bf16x4*)(d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.epi - 1);
+      } else if (d.epi >= 3) {
+        const bf16x4 x = *(const bf16x4*)(d.aux + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.epi - 3);
+      }
+      *(bf16x4*)(d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    }
+  }
+}
+
 // FA, FB: the formats of A and B (0 E4M3, 1 E5M2).  The B fragment is the instruction's first
 // operand, so its format goes in the first selector.
 template <class Cfg, int FA, int FB>
@@ -375,42 +413,110 @@ void gemm_fp8_nt_kernel(F8Desc d, int tiles_m, int tiles_n) {
     if (++cur == Cfg::STAGES) cur = 0;
   }
 
-  const float sc = *d.da * *d.db;
-  const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+  f8_epilogue<Cfg::FM, Cfg::FN>(d, m0, n0, wm, wn, lane, acc);
+}
+
+// The ping-pong schedule on the 256 x 192 tile: the eight waves form two groups of four (one wave of
+// each per SIMD) one phase apart; group g owns tile rows [128g, 128g + 128) as 2 x 2 waves of 64 x 96.
+// Each wave alternates a memory phase (read its fragments of k-tile t from LDS, then issue its share
+// of k-tile t+1's direct loads) and a compute phase (the k-tile's MFMAs), so on each SIMD one wave
+// multiplies while the other reads.  Group g loads its own 128 rows of A, group 0 also loads B; each
+// group waits for its loads at the end of its next compute phase (two phases for every load to land),
+// and a stage is refilled only after both groups' reads of it ended.
+struct F8PP {
+  static constexpr int BM = 256, BN = 192, NT = 512, HALF = 128, FM = 4, FN = 6;
+  static constexpr int A_HALF = HALF * 128, B_OFF = 2 * A_HALF, STAGE = B_OFF + BN * 128;
+  static constexpr int IPW_A = A_HALF / 1024 / 4, IPW_B = BN * 128 / 1024 / 4;
+  static_assert(2 * STAGE <= 160 * 1024 && (BN * 128) % 4096 == 0, "tile layout");
+};
+
+// Phase boundaries (the waits through the builtin, which the compiler's own wait placement counts;
+// sched_barrier keeps MFMAs and memory operations inside their phase).
+__device__ __forceinline__ void f8_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void f8_sync_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) alone
+  f8_barrier();
+}
+__device__ __forceinline__ void f8_sync_vm() {
+  __builtin_amdgcn_sched_barrier(0);
+  f8_wait_vmcnt<0>();
+  f8_barrier();
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(F8PP::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_fp8_pp_kernel(F8Desc d, int tiles_m, int tiles_n) {
+  using P = F8PP;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * P::STAGE];
+  TP_LDS char* lds = (TP_LDS char*)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, w4 = wave & 3;
+  constexpr int GROUP_M = 4;
+  const int nwg = tiles_m * tiles_n;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (wg / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
+  const int m0 = tm * P::BM, n0 = tn * P::BN;
+
+  int ar[P::IPW_A], ac[P::IPW_A], br[P::IPW_B], bc[P::IPW_B];
+  f8_pieces<P::IPW_A>(w4, lane, ar, ac);
+  f8_pieces<P::IPW_B>(w4, lane, br, bc);
+  const int wml = (w4 >> 1) * 64, wn = (w4 & 1) * 96;
+  f32x4 acc[P::FM][P::FN];
 #pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i) {
-    const int m = m0 + wm + 16 * i + r16;
-    if (m >= d.M) continue;
+  for (int i = 0; i < P::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int n = n0 + wn + 16 * j + g4;
-      if (n >= d.N) continue;
-      float a[4];
+    for (int j = 0; j < P::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (d.K + 127) / 128;
+  const int rot = nk > 0 ? (tm + tn) % nk : 0;
+  auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * 128; };
+  auto issue = [&](int t, int st) {
+    TP_LDS char* base = lds + st * P::STAGE;
+    const int k = kpos(t);
+    f8_load<P::HALF, P::IPW_A>(d.A, d.K, d.M, m0 + P::HALF * g, k, d.K, base + g * P::A_HALF, ar, ac, w4);
+    if (g == 0) f8_load<P::BN, P::IPW_B>(d.B, d.K, d.N, n0, k, d.K, base + P::B_OFF, br, bc, w4);
+  };
+
+  if (nk > 0) issue(0, 0);
+  f8_sync_vm();                  // k-tile 0 is in stage 0
+  if (g == 1) f8_barrier();      // group 1 starts one phase behind
+  for (int t = 0; t < nk; ++t) {
+    const int st = t & 1;
+    // memory phase: this k-tile's fragments, then the next k-tile's loads
+    const TP_LDS char* at = lds + st * P::STAGE + g * P::A_HALF;
+    const TP_LDS char* bt = lds + st * P::STAGE + P::B_OFF;
+    i32x8 af[P::FM], bfr[P::FN];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = acc[i][j][e] * sc;
-      if (d.bias) {
-        const bf16x4 b = *(const bf16x4*)(d.bias + n);
+    for (int i = 0; i < P::FM; ++i) af[i] = f8_frag(at, wml + 16 * i, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] += (float)b[e];
-      }
-      const long o = (long)m * d.N + n;
-      if (d.epi == 1 || d.epi == 2) {
-        if (d.C2) *(bf16x4*)(d.C2 + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    for (int j = 0; j < P::FN; ++j) bfr[j] = f8_frag(bt, wn + 16 * j, lane);
+    if (t + 1 < nk) issue(t + 1, st ^ 1);
+    f8_sync_lds();
+    // compute phase
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.epi - 1);
-      } else if (d.epi >= 3) {
-        const bf16x4 x = *(const bf16x4*)(d.aux + o);
+    for (int i = 0; i < P::FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] *= act_grad_f((float)x[e], d.epi - 3);
-      }
-      *(bf16x4*)(d.C + o) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    }
+      for (int j = 0; j < P::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i], acc[i][j], FB, FA, 0, 127, 0, 127);
+    f8_sync_vm();
   }
+  if (g == 0) f8_barrier();      // both groups have passed the same number of barriers
+
+  f8_epilogue<P::FM, P::FN>(d, m0, n0, P::HALF * g + wml, wn, lane, acc);
 }
 
 using F8C0 = F8Tile<256, 256, 4, 2, 2>;   // 64 x 128 per wave
 using F8C1 = F8Tile<256, 128, 4, 2, 2>;   // 64 x 64 per wave
-using F8C2 = F8Tile<256, 192, 4, 2, 2>;   // 64 x 96 per wave
 
 template <class Cfg>
 hipError_t f8_run(const F8Desc& d, int fa, int fb, hipStream_t s) {
@@ -476,6 +582,17 @@ hipError_t launch_fp8_quantize(int dtype, int fmt, int rows, int cols, const voi
   return hipGetLastError();
 }
 
+namespace {
+hipError_t f8_run_pp(const F8Desc& d, int fa, int fb, hipStream_t s) {
+  const int tm = (d.M + F8PP::BM - 1) / F8PP::BM, tn = (d.N + F8PP::BN - 1) / F8PP::BN;
+  if (fa == 0 && fb == 0) gemm_fp8_pp_kernel<0, 0><<<tm * tn, F8PP::NT, 0, s>>>(d, tm, tn);
+  else if (fa == 1 && fb == 0) gemm_fp8_pp_kernel<1, 0><<<tm * tn, F8PP::NT, 0, s>>>(d, tm, tn);
+  else if (fa == 0 && fb == 1) gemm_fp8_pp_kernel<0, 1><<<tm * tn, F8PP::NT, 0, s>>>(d, tm, tn);
+  else return hipErrorNotSupported;
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int fa, const float* da,
                               const unsigned char* B, int fb, const float* db, const void* bias, int epi,
                               const void* aux, void* C, void* C2, hipStream_t s) {
@@ -484,7 +601,8 @@ hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int f
   const double flop = 2.0 * M * (double)N * K;
   const double outs = 1.0 + ((epi == 1 || epi == 2) && C2 ? 1.0 : 0.0) + (epi >= 3 ? 1.0 : 0.0);
   const double bytes = (double)M * K + (double)N * K + 2.0 * M * (double)N * outs;
-  // tile choice: (waves of 256 tiles) x tile area / relative per-tile rate, the smallest wins
+  // tile choice: (waves of 256 tiles) x tile area / relative per-tile rate, the smallest wins; the
+  // 256 x 192 tile runs on the ping-pong schedule (measured 3-6% faster than the plain one)
   const int bn[3] = {256, 192, 128};
   const double rate[3] = {1.0, 0.95, 0.8};
   int best = 0;
@@ -499,12 +617,12 @@ hipError_t launch_fp8_gemm_nt(int M, int N, int K, const unsigned char* A, int f
   }
   static const char* const tags[3][3] = {
       {"gemm_fp8_nt<256x256, e4m3 x e4m3>", "gemm_fp8_nt<256x256, e5m2 x e4m3>", "gemm_fp8_nt<256x256, e4m3 x e5m2>"},
-      {"gemm_fp8_nt<256x192, e4m3 x e4m3>", "gemm_fp8_nt<256x192, e5m2 x e4m3>", "gemm_fp8_nt<256x192, e4m3 x e5m2>"},
+      {"gemm_fp8_nt<256x192pp, e4m3 x e4m3>", "gemm_fp8_nt<256x192pp, e5m2 x e4m3>", "gemm_fp8_nt<256x192pp, e4m3 x e5m2>"},
       {"gemm_fp8_nt<256x128, e4m3 x e4m3>", "gemm_fp8_nt<256x128, e5m2 x e4m3>", "gemm_fp8_nt<256x128, e4m3 x e5m2>"}};
   const int pair = fa ? 1 : (fb ? 2 : 0);
   ProfScope p(tags[best][pair], s, flop, bytes);
   if (best == 0) return f8_run<F8C0>(d, fa, fb, s);
-  if (best == 1) return f8_run<F8C2>(d, fa, fb, s);
+  if (best == 1) return f8_run_pp(d, fa, fb, s);
   return f8_run<F8C1>(d, fa, fb, s);
 }
 
