@@ -152,7 +152,9 @@ int tp_attn_out_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_head
  * rank (the all-reduce's backward is the identity):
  *   dWo_r = ctx_rᵀ·dO ;  dbo = Σ_t dO (iff rank == 0 and dbo != NULL) ;  dctx_r = dO·Wo_rᵀ
  * dctx_r is the rank's own column block of dctx (no sum over ranks), ready for tp_attn_heads_bwd.
- * workspace: tp_workspace_bytes("tp_attn_out_shard_bwd", ...). */
+ * workspace: tp_workspace_bytes("tp_attn_out_shard_bwd", ...): the bias gradient's fp32 partials and,
+ * in bf16 when dctx_r has few output tiles (the GPT-3 shard's [2048, 1536]), fp32 partials of dctx_r
+ * over up to four slices of H, summed in slice order into dctx_r (deterministic). */
 int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
                           const void* ctx_r, const void* Wo_r, const void* dO, void* dctx_r,
                           void* dWo_r, void* dbo, void* workspace, size_t workspace_bytes,

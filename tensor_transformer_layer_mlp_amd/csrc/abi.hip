@@ -1,5 +1,6 @@
 // C ABI of libtpshard: argument validation, shard geometry, and the launch sequence of each entry
 // point.  Every check happens on the host before anything is enqueued.  See include/tpshard.h.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -174,7 +175,22 @@ size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
 
 size_t qkv_bwd_ws(int T, int Nq) { return align256(colsum_ws_bytes(T, Nq)); }
 
-size_t out_bwd_ws(int T, int H) { return align256(colsum_ws_bytes(T, H)); }
+// k-slices for the output projection's input gradient dctx = dO·Wo_rᵀ (M = T, N = nh_r·d, K = H): its
+// few output tiles would leave most CUs idle, so the k dimension is split until about 256 tiles run,
+// each slice at least 512 deep, partials summed afterwards (bf16 only).
+int out_bwd_split(int dtype, int T, int Kr, int H) {
+  if (dtype != DT_BF16 || T <= 0 || Kr <= 0) return 1;
+  const long tiles = (long)((T + 255) / 256) * ((Kr + 191) / 192);
+  if (tiles >= 128) return 1;
+  const long s = std::min<long>(std::min<long>(4, 256 / tiles), H / 512);
+  return (int)std::max<long>(s, 1);
+}
+
+size_t out_bwd_ws(int T, int H, int Kr, int dtype) {
+  const int sk = out_bwd_split(dtype, T, Kr, H);
+  const size_t parts = sk > 1 ? align256((size_t)sk * (size_t)T * (size_t)Kr * sizeof(float)) : 0;
+  return align256(colsum_ws_bytes(T, H)) + parts;
+}
 
 GemmDesc gemm_desc(int dtype, int M, int N, int K, const void* A, long lda, bool a_kmajor,
                    const void* B, long ldb, bool b_kmajor, void* C, long ldc, int epi) {
@@ -411,15 +427,27 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
   const int Kr = g.nh * g.d;
   NEED(ctx_r, "ctx_r", (long)g.T); NEED(Wo_r, "Wo_r", 1); NEED(dO, "dO", (long)g.T);
   NEED(dctx_r, "dctx_r", (long)g.T); NEED(dWo_r, "dWo_r", 1); MAYBE(dbo, "dbo");
-  const size_t need = out_bwd_ws(g.T, H);
+  const size_t need = out_bwd_ws(g.T, H, Kr, dtype);
   TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   // dWo_r = ctx_rᵀ·dO   (M = nh_r*d, N = H, K = T)
   GemmDesc g1 = gemm_desc(dtype, Kr, H, g.T, ctx_r, Kr, false, dO, H, false, dWo_r, H, EPI_STORE);
-  // dctx_r = dO·Wo_rᵀ   (M = T, N = nh_r*d, K = H)
+  // dctx_r = dO·Wo_rᵀ   (M = T, N = nh_r*d, K = H); with few output tiles, as k-slices into fp32
+  // partials behind the column-sum workspace, then summed in slice order
   GemmDesc g2 = gemm_desc(dtype, g.T, Kr, H, dO, H, true, Wo_r, H, true, dctx_r, Kr, EPI_STORE);
+  const int sk = out_bwd_split(dtype, g.T, Kr, H);
+  float* parts = (float*)((char*)workspace + align256(colsum_ws_bytes(g.T, H)));
+  if (sk > 1) {
+    GemmDesc gs = g2;
+    gs.epi = EPI_F32;
+    gs.C = parts;
+    gs.ksplit = sk;
+    gs.k_per = ((H + sk - 1) / sk + 63) / 64 * 64;
+    gs.c_split = (long)g.T * Kr;
+    if (gemm_bf16_eligible(gs) && ((uintptr_t)dctx_r & 15) == 0) g2 = gs;   // the sum stores 16-byte pieces
+  }
 
   // caller's stream: dWo;  side stream: dbo (rank 0), dctx (all independent)
   std::lock_guard<std::mutex> lk(g_side_mu);
@@ -434,6 +462,8 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
     if (rank == 0 && dbo != nullptr)
       TP_TRY(launch_colsum(dtype, dO, H, g.T, H, (float*)workspace, dbo, s2), "dbo colsum");
     TP_TRY(launch_gemm(g2, s2), "dctx gemm");
+    if (g2.epi == EPI_F32)
+      TP_TRY(launch_splitk_sum(g2.ksplit, (long)g.T * Kr, parts, dctx_r, s2), "dctx slice sum");
     return TP_OK;
   };
   const int rc = body();
@@ -731,7 +761,7 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   }
   if (strcmp(fn, "tp_attn_out_shard_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
-    return out_bwd_ws(g.T, H);
+    return out_bwd_ws(g.T, H, g.nh * g.d, dtype);
   }
   if (strcmp(fn, "tp_attn_heads_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;

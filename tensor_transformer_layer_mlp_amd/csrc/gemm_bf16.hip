@@ -200,7 +200,19 @@ template <class Cfg, int EPI>
 __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds,
                                            f32x4 (&acc)[Cfg::FM][Cfg::FN], int wm, int wn, int wave, int lane) {
   const int r16 = lane & 15, g4 = 4 * (lane >> 4);
-  if constexpr (Cfg::BM * Cfg::BN * 2 <= Cfg::STAGES * Cfg::STAGE) {
+  if constexpr (EPI == EPI_F32) {
+    // fp32 partials straight from the accumulators: four consecutive columns per lane, 16 bytes
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int m = m0 + wm + 16 * i + r16;
+      if (m >= d.M) continue;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int n = n0 + wn + 16 * j + g4;
+        if (n < d.N) *(f32x4*)((float*)d.C + (long)m * d.ldc + n) = acc[i][j];
+      }
+    }
+  } else if constexpr (Cfg::BM * Cfg::BN * 2 <= Cfg::STAGES * Cfg::STAGE) {
     // Staged epilogue: the finished tile goes through LDS (row pitch 2·BN bytes, 16-byte granule q of
     // row r at q ^ (r & 7)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
     // two to four rows instead of 16-row x 32-byte scraps.
@@ -540,14 +552,31 @@ void gemm_bf16_pp_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup -> tile order as in gemm_bf16_kernel (contiguous runs per XCD, groups of 4 tile rows)
   constexpr int GROUP_M = 4;
-  const int nwg = tiles_m * tiles_n;
+  // split-k: the grid holds ksplit copies of the tile set, copy s on k-slice s (both operands K-major)
+  const int ks = (EPI == EPI_F32 && d.ksplit > 1) ? d.ksplit : 1;
+  const int tiles = tiles_m * tiles_n, nwg = tiles * ks;
   int wg = blockIdx.x;
   if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int slice = wg / tiles;
+  wg -= slice * tiles;
   const int per_group = GROUP_M * tiles_n;
   const int first_m = (wg / per_group) * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
   const int tm = first_m + (wg % per_group) % gsize, tn = (wg % per_group) / gsize;
-  gemm_tile_pp<AK, BK, EPI>(d, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+  if constexpr (EPI == EPI_F32) {
+    static_assert(AK && BK, "split-k takes two K-major operands");
+    GemmDesc ds = d;
+    if (ks > 1) {
+      const int k0 = slice * d.k_per;
+      ds.A = (const bf16*)d.A + k0;
+      ds.B = (const bf16*)d.B + k0;
+      ds.K = max(0, min(d.k_per, d.K - k0));
+      ds.C = (float*)d.C + slice * d.c_split;
+    }
+    gemm_tile_pp<AK, BK, EPI>(ds, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+  } else {
+    gemm_tile_pp<AK, BK, EPI>(d, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+  }
 }
 
 // Grouped GEMM: expert e owns rows [off[e], off[e+1]) of A and C and its own B (and bias), at
@@ -650,7 +679,8 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
 template <bool AK, bool BK, int EPI>
 hipError_t run_pp(const GemmDesc& d, hipStream_t s) {
   const int tiles_m = (d.M + PPTile::BM - 1) / PPTile::BM, tiles_n = (d.N + PPTile::BN - 1) / PPTile::BN;
-  gemm_bf16_pp_kernel<AK, BK, EPI><<<tiles_m * tiles_n, PPTile::NT, 0, s>>>(d, tiles_m, tiles_n);
+  const int ks = (EPI == EPI_F32 && d.ksplit > 1) ? d.ksplit : 1;
+  gemm_bf16_pp_kernel<AK, BK, EPI><<<tiles_m * tiles_n * ks, PPTile::NT, 0, s>>>(d, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -662,6 +692,7 @@ hipError_t run_pp_cfg(const GemmDesc& d, hipStream_t s) {
   } else if (d.a_kmajor && d.b_kmajor) {
     if (d.epi == EPI_DGELU) return run_pp<true, true, EPI_DGELU>(d, s);
     if (d.epi == EPI_STORE) return run_pp<true, true, EPI_STORE>(d, s);
+    if (d.epi == EPI_F32) return run_pp<true, true, EPI_F32>(d, s);
   }
   // Xᵀ·dY (both operands MN-major) is not taken: two operands of transposed LDS reads make the memory
   // phase longer than the compute phase (measured 15% slower than the plain 256 x 192 kernel)
@@ -717,6 +748,9 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
   if ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) return false;
   if (d.epi == EPI_BIAS_GELU && d.C2 && (((uintptr_t)d.C2) & 15)) return false;
   if (d.epi == EPI_DGELU && ((d.ld_aux & 7) || (((uintptr_t)d.aux) & 15))) return false;
+  if (d.epi == EPI_F32)   // split-k partials: the ping-pong tile, both operands K-major, slices of whole k-tiles
+    return d.a_kmajor && d.b_kmajor && ((d.ldc & 3) == 0) &&
+           (d.ksplit <= 1 || (d.k_per > 0 && d.k_per % 64 == 0 && (long)d.k_per * d.ksplit >= d.K));
   const bool supported = (d.a_kmajor && !d.b_kmajor && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_GELU || d.epi == EPI_STORE)) ||
                          (d.a_kmajor && d.b_kmajor && (d.epi == EPI_DGELU || d.epi == EPI_STORE)) ||
                          (!d.a_kmajor && !d.b_kmajor && d.epi == EPI_STORE);
@@ -737,6 +771,10 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   // tile moves ≈14% fewer LDS bytes per flop than 256 x 192; on outputs of 4096 x 4096 and more it was
   // measured faster despite its coarser rounds (its partial last round fills with the concurrent
   // input-gradient GEMM)
+  if (d.epi == EPI_F32) {   // only the ping-pong tile writes fp32 partials
+    *cfg = 9;
+    return kTileName[9];
+  }
   if (!d.a_kmajor && !d.b_kmajor && (long)d.M * d.N >= 4096L * 4096L) {
     *cfg = 0;
     return kTileName[0];

@@ -13,7 +13,8 @@ enum Epi {
   EPI_STORE = 0,      // C = acc
   EPI_BIAS = 1,       // C = acc + bias[n]
   EPI_BIAS_GELU = 2,  // C2 = acc + bias[n] (if C2), C = GeLU(acc + bias[n])   (GeLU per `act`)
-  EPI_DGELU = 3       // C = acc * GeLU'(aux[m, n])
+  EPI_DGELU = 3,      // C = acc * GeLU'(aux[m, n])
+  EPI_F32 = 4         // C (fp32) = acc: one k-slice's partial of a split-k GEMM
 };
 
 // C[M, N] = op(A)·op(B) with the epilogue applied.  Element (m, k) of A sits at A[m*lda + k] when
@@ -34,9 +35,17 @@ struct GemmDesc {
   const int* a_rows;
   int a_rows_n;
   int act;             // the GeLU epilogues' activation: 0 exact, 1 tanh form
+  // Split-k (EPI_F32, both operands K-major): ksplit slices of k_per (a multiple of 64) k each, slice s
+  // writing its fp32 partial at C + s·c_split; 0 or 1 = no split
+  int ksplit, k_per;
+  long c_split;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// Whether the tiled kernels take this GEMM (shapes, strides, alignment, layout and epilogue).
+bool gemm_bf16_eligible(const GemmDesc& d);
+// out[i] = Σ_{s < S} parts[s·n + i] in that order, rounded to bf16 (n a multiple of 8).
+hipError_t launch_splitk_sum(int S, long n, const float* parts, void* out, hipStream_t s);
 
 // out[c] = Σ_{r < rows} in[r*ld + c] for c < cols, deterministic (fixed chunked order, fp32).
 size_t colsum_ws_bytes(int rows, int cols);

@@ -104,7 +104,31 @@ hipError_t colsum_t(const void* in, long ld, int rows, int cols, float* ws, void
   return hipGetLastError();
 }
 
+// out[i] = Σ_s parts[s·n + i] in slice order, eight elements per thread.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(int S, long n, const float* __restrict__ parts,
+                                                         bf16* __restrict__ out) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  f32x4 a = *(const f32x4*)(parts + i), b = *(const f32x4*)(parts + i + 4);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 c = *(const f32x4*)(parts + (long)s * n + i), e = *(const f32x4*)(parts + (long)s * n + i + 4);
+    a += c;
+    b += e;
+  }
+  *(bf16x8*)(out + i) = (bf16x8){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                                 (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+
 }  // namespace
+
+hipError_t launch_splitk_sum(int S, long n, const float* parts, void* out, hipStream_t s) {
+  if (n <= 0 || S <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  ProfScope p("splitk_sum", s, (double)S * n, 4.0 * S * n + 2.0 * n);
+  const long blocks = (n / 8 + 255) / 256;
+  splitk_sum_kernel<<<(unsigned)blocks, 256, 0, s>>>(S, n, parts, (bf16*)out);
+  return hipGetLastError();
+}
 
 size_t colsum_ws_bytes(int rows, int cols) {
   const size_t chunks = (size_t)(rows + CS_ROWS - 1) / CS_ROWS;

@@ -59,6 +59,36 @@ def test_out_bwd(wl, dtype, rank):
         assert torch.isnan(o["db"]).all(), "dbo is written by rank 0 only"
 
 
+# dctx_r [520, 256] has six 256 x 192 output tiles: it runs as four k-slices of H = 2048 into fp32
+# partials that are then summed in slice order
+SPLIT = LayerWorkload("outsplit_b2_s260_h2048_nh16_f8192_tp8", 2, 260, 2048, 16, 8192, 8, (0, 5), 0.02)
+
+
+@pytest.mark.parametrize("rank", SPLIT.ranks)
+def test_out_bwd_split_k(rank):
+    wl = SPLIT
+    sh = Shard(wl, rank, "bf16")
+    ctx, dO = sh.d_("ctx"), sh.d_("dO")
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        o = run_out_bwd(sh, ctx, dO)
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    tags = bd.tp_prof_collect()
+    assert "splitk_sum" in tags and any("epi4" in t for t in tags), sorted(tags)
+    ref = oracle.tp_attn_out_shard_bwd(wl.tp_size, rank, wl.B, wl.S, wl.H, wl.n_heads, sh.f64("ctx"),
+                                       sh.f64("Wo"), sh.f64("dO"))
+    assert_close(o["dctx"], ref["dctx"], "bf16", "dctx_r")
+    assert_close(o["dW"], ref["dW"], "bf16", "dWo_r")
+    if rank == 0:
+        assert_close(o["db"], ref["db"], "bf16", "dbo")
+    again = run_out_bwd(sh, ctx, dO)
+    torch.cuda.synchronize()
+    assert torch.equal(o["dctx"], again["dctx"]), "the slice sum is in a fixed order"
+
+
 @pytest.mark.parametrize("wl,dtype,rank", list(cases()))
 def test_attention_block_chain(wl, dtype, rank):
     """QKV -> attention -> output projection forward, then output projection -> attention -> QKV
