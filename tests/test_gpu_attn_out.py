@@ -179,10 +179,12 @@ def test_out_no_out_of_bounds_writes(dtype):
             assert (g.float() == -7776.0).all(), f"rank {rank}: guard band {i} overwritten"
 
 
-def test_out_graph_replay():
+@pytest.mark.parametrize("wl", [RAGGED8, SPLIT], ids=["ragged8", "split-k"])
+def test_out_graph_replay(wl):
     """Forward and backward of the output projection captured in one graph (the backward forks
-    onto the library's side stream inside the capture), replayed with eager work in between."""
-    sh = Shard(RAGGED8, 0, "bf16")
+    onto the library's side stream inside the capture; on the split-k workload its dctx is the
+    k-slice GEMM and the slice sum), replayed with eager work in between."""
+    sh = Shard(wl, 0, "bf16")
     wl = sh.wl
     O = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device="cuda")
     o = dict(dctx=torch.empty(wl.T, sh.nh * sh.d, dtype=torch.bfloat16, device="cuda"),

@@ -110,3 +110,25 @@ def test_weight_gradients_256_tile():
                                   sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
     for k in ("dX", "dW1", "db1", "dW2", "db2"):
         assert_close(o[k], ref[k], "bf16", k)
+
+
+def test_large_tiles_deterministic():
+    """Two identical calls give bitwise-equal outputs on the ping-pong and 256 x 256 tiles (fixed
+    k order per tile, no atomics)."""
+    wl, rank = PP_BIG, 1
+    sh = Shard(wl, rank, "bf16")
+    T, H, Fr = wl.T, wl.H, sh.Fr
+    ws = bd.workspace("tp_mlp_shard_bwd", wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, wl.F, torch.bfloat16)
+    runs = []
+    for _ in range(2):
+        Z, A1, Y = empty((T, H), "bf16"), empty((T, Fr), "bf16"), empty((T, Fr), "bf16")
+        bd.tp_mlp_shard_fwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("b1"), sh.d_("W2"),
+                            sh.d_("b2"), Z, A1, Y)
+        o = dict(dX=empty((T, H), "bf16"), dW1=empty((H, Fr), "bf16"), db1=empty((Fr,), "bf16"),
+                 dW2=empty((Fr, H), "bf16"), db2=empty((H,), "bf16"))
+        bd.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("W2"), sh.d_("A1"),
+                            sh.d_("Y"), sh.d_("dZ"), o["dX"], o["dW1"], o["db1"], o["dW2"], o["db2"], ws)
+        torch.cuda.synchronize()
+        runs.append(dict(Z=Z, A1=A1, Y=Y, dX=o["dX"], dW1=o["dW1"], dW2=o["dW2"], db1=o["db1"]))
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), f"{k} differs between two identical calls"
