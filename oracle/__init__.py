@@ -16,4 +16,4 @@ from .tp_shard import (shard_range, qkv_column_range, slice_qkv, slice_fc1, slic
                        moe_combine_bwd, tp_mlp_grouped_shard_bwd, tp_moe_shard_bwd, moe_route_bwd,
                        e4m3_decode, e4m3_encode, fp8_decode, fp8_encode, fp8_quantize, fp8_gemm_nt,
                        FP8_EPI_NONE, FP8_EPI_GELU, FP8_EPI_GELU_TANH, FP8_EPI_DGELU, FP8_EPI_DGELU_TANH,
-                       normwise_error)
+                       normwise_error, blockwise_error)

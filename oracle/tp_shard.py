@@ -662,9 +662,56 @@ def tp_mlp_grouped_shard_fwd(tp_size, rank, group_offsets, X_perm, W1_r, b1_r, W
 
 
 def normwise_error(got, ref):
-    """‖got − ref‖_F / ‖ref‖_F in float64 (absolute ‖got‖_F when ‖ref‖_F = 0)."""
+    """‖got − ref‖_F / ‖ref‖_F in float64 (absolute ‖got − ref‖_F when ‖ref‖_F = 0).
+
+    The per-tensor parity measure: a normwise relative error, the bar being 2e-2 for bf16 operands
+    with fp32 accumulation and 1e-5 in fp32 mode.
+    """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref)
     num = np.linalg.norm(got - ref)
     return num / den if den > 0 else num
+
+
+def _as_rows(a):
+    """A tensor viewed as a matrix: one row per index of the leading dimensions (a vector is one row)."""
+    a = np.asarray(a, dtype=np.float64)
+    if a.ndim == 0:
+        return a.reshape(1, 1)
+    if a.ndim == 1:
+        return a.reshape(1, -1)
+    return a.reshape(-1, a.shape[-1])
+
+
+def blockwise_error(got, ref, block=64):
+    """The largest local error over the block x block tiles of a tensor (viewed as a matrix).
+
+    For each tile b:  ‖got_b − ref_b‖_F / max(‖ref_b‖_F, ‖ref‖_F·√(n_b/n)),  n_b the tile's element
+    count and n the tensor's.  So a tile is held to the normwise bar relative to its own values, or,
+    where its values are smaller than the tensor's average, relative to its share of the whole
+    tensor's norm.  A defect confined to one tile (a dropped k-slice, a wrong tile offset) counts at
+    its local size instead of being diluted by the rest of the tensor.  Absolute per-tile error
+    ‖got_b − ref_b‖_F when ‖ref‖_F = 0.
+    """
+    g, r = _as_rows(got), _as_rows(ref)
+    assert g.shape == r.shape, f"shape {g.shape} vs {r.shape}"
+    R, C = r.shape
+    if R * C == 0:
+        return 0.0
+    br, bc = min(block, R), min(block, C)
+    nR, nC = -(-R // br), -(-C // bc)
+
+    def tile_sums(x):
+        pad = np.zeros((nR * br, nC * bc))
+        pad[:R, :C] = x
+        return pad.reshape(nR, br, nC, bc).sum(axis=(1, 3))
+
+    diff2 = tile_sums((g - r) ** 2)
+    ref2 = tile_sums(r * r)
+    count = tile_sums(np.ones_like(r))
+    total = np.linalg.norm(r)
+    if total == 0:
+        return float(np.sqrt(diff2.max()))
+    den = np.maximum(np.sqrt(ref2), total * np.sqrt(count / (R * C)))
+    return float((np.sqrt(diff2) / den).max())

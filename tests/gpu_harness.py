@@ -40,12 +40,18 @@ def err(got, ref):
 
 
 def assert_close(got, ref, dtype, what, tol=None):
+    """Parity of a device result with the oracle's: every element finite, the normwise relative error
+    within the bar, and the same bar on every 64 x 64 tile of the result viewed as a matrix (each
+    tile against its own norm or its share of the whole, whichever is larger), so that a defect
+    confined to a few tiles is not diluted by the rest of the tensor."""
     tol = TOL[dtype] if tol is None else tol
     g = host(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     assert g.shape == np.shape(ref), f"{what}: shape {g.shape} vs {np.shape(ref)}"
     assert np.all(np.isfinite(g)), f"{what}: non-finite output (unwritten or overflow)"
     e = oracle.normwise_error(g, ref)
     assert e <= tol, f"{what}: normwise error {e:.3e} > {tol:.0e}"
+    b = oracle.blockwise_error(g, ref)
+    assert b <= tol, f"{what}: 64x64 tile error {b:.3e} > {tol:.0e} (normwise {e:.3e})"
     return e
 
 

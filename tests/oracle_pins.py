@@ -19,6 +19,9 @@ fails.  What pins what:
   fp8         E4M3 anchors from the format's definition; every finite code against torch's
               float8_e4m3fn; encode(decode(c)) = c; midpoints to the even code; saturation; the
               amax element quantises to ±448; the GEMM on codes against scalar loops
+  checkers    normwise_error and blockwise_error (the parity measures) against hand-worked values;
+              a planted one-tile GEMM defect that the normwise measure misses and the tile-wise one
+              catches
   layernorm   scalar loops; a textbook row; zero mean / unit mean square (eps = 0); shift and scale
               invariance; constant rows; dropout-add cases by hand; finite differences through the
               fused residual + dropout + LayerNorm op; the sequence-parallel split (row blocks
@@ -742,6 +745,62 @@ def pin_moe_backward():
     _close(b1_["dgates"][:, 0], (d_out * dense["Z"]).sum(axis=1), 1e-13, "E = k = 1 dgate = <d_out, Z>")
 
 
+def pin_error_metrics():
+    """The parity checkers themselves, against values worked out by hand.
+
+    normwise_error is ‖got − ref‖_F / ‖ref‖_F: the denominator from ref (swapping got and ref
+    changes the value), the Frobenius norm (not the largest element), the absolute form for a zero
+    reference.  blockwise_error is the largest 64 x 64 tile error, each tile's difference over the
+    larger of its own norm and its share ‖ref‖_F·√(n_b/n) of the whole: the hand values below fix
+    the tiling, the share, ragged edge tiles and the view of vectors and 3-D tensors as matrices.
+    Last, a planted localised defect — one 256 x 192 output tile of a GEMM that skipped one 16-deep
+    k-step of its 2048 — is below the 2e-2 bar normwise (≈0.6%) and far above it tile-wise.
+    """
+    ne, be = T.normwise_error, T.blockwise_error
+    assert abs(ne([[3.3, 3.6]], [[3.0, 4.0]]) - 0.1) <= 1e-15, "0.5 / 5"
+    assert abs(ne([6.0, 8.0], [3.0, 4.0]) - 1.0) <= 1e-15, "‖(3, 4)‖ / ‖(3, 4)‖"
+    assert abs(ne([3.0, 4.0], [6.0, 8.0]) - 0.5) <= 1e-15, "‖(3, 4)‖ / ‖(6, 8)‖: denominator from ref"
+    assert ne([0.0, 0.0], [3.0, 4.0]) == 1.0, "zero output: error 1"
+    assert abs(ne([[2.0, 1.0], [1.0, 1.0]], np.ones((2, 2))) - 0.5) <= 1e-15, "Frobenius: 1 / 2, not max 1 / 1"
+    assert ne([3.0, 4.0], [0.0, 0.0]) == 5.0, "zero reference: absolute ‖got‖"
+    assert ne(np.ones(7), np.ones(7)) == 0.0
+
+    ones = np.ones((128, 128))
+    g = ones.copy()
+    g[:64, :64] += 0.1                  # tile (0, 0): ‖diff‖ = 6.4, own norm 64, share 128·½ = 64
+    assert abs(be(g, ones) - 0.1) <= 1e-14, f"one tile +10%: {be(g, ones)}"
+    assert abs(ne(g, ones) - 0.05) <= 1e-14
+    r = ones.copy()
+    r[64:, 64:] = 0.01                  # a tile of small values: held to its share of the whole
+    g = r.copy()
+    g[64:, 64:] += 0.001
+    want = 0.064 / (0.5 * math.sqrt(3 * 4096 + 4096 * 1e-4))
+    assert abs(be(g, r) - want) <= 1e-14 * want, f"small tile: {be(g, r)} vs {want}"
+    r = np.ones((3, 100))               # ragged: tiles 3 x 64 and 3 x 36
+    g = r.copy()
+    g[0, 70] += 1.0
+    assert abs(be(g, r) - 1.0 / math.sqrt(108)) <= 1e-14, "ragged edge tile of 108 elements"
+    v = np.ones(130)                    # a vector is one row: tiles of 64, 64 and 2 elements
+    w = v.copy()
+    w[129] = 2.0
+    assert abs(be(w, v) - 1.0 / math.sqrt(2)) <= 1e-14, "vector edge tile of 2 elements"
+    t3 = np.ones((2, 3, 64))            # leading dimensions become rows: one 6 x 64 tile
+    u3 = t3.copy()
+    u3[1, 2, 5] = 0.0
+    assert abs(be(u3, t3) - 1.0 / math.sqrt(384)) <= 1e-14, "3-D tensor as a 6 x 64 matrix"
+    assert be([0.0, 0.0, 3.0, 4.0], np.zeros(4)) == 5.0, "zero reference: absolute"
+    assert be(ones, ones) == 0.0
+
+    rng = _rng(71)
+    A = rng.standard_normal((2048, 2048))
+    B = rng.standard_normal((2048, 4608)) * 0.02
+    C = A @ B
+    bad = C.copy()
+    bad[256:512, 384:576] -= A[256:512, 1024:1040] @ B[1024:1040, 384:576]
+    assert 3e-3 <= ne(bad, C) <= 1e-2, f"planted defect normwise {ne(bad, C):.2e}"
+    assert be(bad, C) >= 5e-2, f"planted defect tile-wise {be(bad, C):.2e}"
+
+
 ALL_PINS = [pin_geometry, pin_gelu, pin_brute_forward, pin_brute_backward, pin_identities,
             pin_attention_closed_forms, pin_finite_differences, pin_grouped, pin_layernorm, pin_moe, pin_moe_backward,
-            pin_fp8]
+            pin_fp8, pin_error_metrics]

@@ -128,8 +128,11 @@ def test_fp8_gemm(M, N, K, epi, fa, fb):
 
 def test_fp8_mlp_forward_against_bf16_definition():
     """The FP8 path end to end on a GPT-shaped MLP shard forward: quantise X and the transposed
-    weights, fc1 with bias + GeLU, quantise Y, fc2; against the oracle's exact-precision MLP, within
-    the error FP8 rounding of four operands allows (a looser bar: 8e-2 normwise)."""
+    weights, fc1 with bias + GeLU, quantise Y, fc2.  Checked two ways: against the same recipe run by
+    the oracle (X and the weights quantised by the oracle, Y quantised from the GPU's own bf16 Y — the
+    value the GPU quantised — so every code is the same on both sides and each GEMM is held to the
+    bf16 bar), and against the oracle's exact-precision MLP, within the error FP8 rounding of four
+    operands allows (a looser bar: 8e-2 normwise)."""
     T, H, Fr = 512, 1024, 768
     X = synth.normal("f8mlpX", (T, H), 1.0, "bf16")
     W1 = synth.normal("f8mlpW1", (H, Fr), 0.02, "bf16")
@@ -149,6 +152,19 @@ def test_fp8_mlp_forward_against_bf16_definition():
     Z = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     bd.tp_fp8_gemm_nt(qY, dY, qW2t, dW2, Z)
     torch.cuda.synchronize()
+    f32 = lambda a: a.f64.astype(np.float32)  # noqa: E731
+    oq, g = oracle.fp8_quantize, oracle.fp8_gemm_nt
+    cX, oX = oq(f32(X))
+    cW1t, oW1 = oq(f32(W1), True)
+    cW2t, oW2 = oq(f32(W2), True)
+    for name, got, codes, gs, os_ in (("X", qX, cX, dX, oX), ("W1ᵀ", qW1t, cW1t, dW1, oW1), ("W2ᵀ", qW2t, cW2t, dW2, oW2)):
+        assert np.array_equal(got.cpu().numpy(), codes), f"codes of {name} differ from the oracle's"
+        assert np.float32(gs.item()) == np.float32(os_), f"descale of {name}"
+    emu_Y = g(cX, oX, cW1t, oW1, b1.f64, epi=oracle.FP8_EPI_GELU)["C"]
+    assert_close(Y, emu_Y, "bf16", "Y (the FP8 recipe on the oracle)")
+    cY, oY = oq(host(Y).astype(np.float32))
+    assert np.array_equal(qY.cpu().numpy(), cY), "codes of Y differ from the oracle's"
+    assert_close(Z, g(cY, oY, cW2t, oW2)["C"], "bf16", "Z (the FP8 recipe on the oracle)")
     ref = oracle.mlp_fwd(X.f64, W1.f64, b1.f64, W2.f64, None)
     assert_close(Y, ref["Y"], "bf16", "Y (fp8 fc1)", tol=8e-2)
     assert_close(Z, ref["Z"], "bf16", "Z (fp8 fc2)", tol=8e-2)

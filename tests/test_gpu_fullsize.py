@@ -106,32 +106,73 @@ def test_gpt3_175b_tp8_rank0():
     check_shard(GPT3_175B, 0)
 
 
-def test_gpt_8p3b_tp8_all_ranks_sum():
-    """All 8 ranks of the 8.3B layer in sequence on the one GPU: Σ_r Z_r and Σ_r dX_r (fp32 sums)
-    equal the unsharded layer's rows, and each rank passes its own sampled checks."""
-    wl = GPT_8P3B
+def all_ranks_identities(wl):
+    """Every rank of a layer in sequence on the one GPU, then the collectives replaced by their
+    definitions: the column-split outputs (QKV_r, ctx_r, LSE_r) concatenated over ranks equal the
+    unsharded layer's, and the row-split and input-gradient partials (Z_r, the MLP's dX_r, the QKV
+    projection's dX_r) summed in fp32 over ranks equal the unsharded ones — the column identity
+    X·[W1 W2] = [X·W1, X·W2] and the row-split exit whose partials the all-reduce adds
+    ("Megatron-LM技术演进与大规模模型训练实践", §2.1; "Megatron-LM — 架构与原理", §4).  The unsharded
+    results come from the oracle on sampled rows (and whole sampled heads for the attention)."""
     dt = "bf16"
-    rows = sample(wl.T, 32, 9)
-    Zsum = torch.zeros(wl.T, wl.H, dtype=torch.float32, device="cuda")
-    dXsum = torch.zeros_like(Zsum)
-    for r in range(wl.tp_size):
-        sh = Shard(wl, r, dt)
-        Z, A1, Y = run_mlp_fwd(sh)
+    t, B, S, H, nh_all, F, T, d = wl.tp_size, wl.B, wl.S, wl.H, wl.n_heads, wl.F, wl.T, wl.head_dim
+    rows = sample(T, 32, 9)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    Zsum, dXm, dXq = torch.zeros(T, H, **f32), torch.zeros(T, H, **f32), torch.zeros(T, H, **f32)
+    QKVcat = torch.full((T, 3 * H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ctxcat = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lsecat = torch.full((B, nh_all, S), float("nan"), **f32)
+    for r in range(t):
+        print(f"{wl.name}: rank {r} of {t}", flush=True)
+        sh = Shard(wl, r, dt, qkv_std=1.0)
+        c0, c1 = 3 * d * sh.h0, 3 * d * (sh.h0 + sh.nh)
+        QKVcat[:, c0:c1] = run_qkv_fwd(sh)
+        ctx, lse = run_attn_fwd(sh, sh.d_("QKV"))
+        ctxcat[:, d * sh.h0:d * (sh.h0 + sh.nh)] = ctx
+        lsecat[:, sh.h0:sh.h0 + sh.nh] = lse
+        Z, _, _ = run_mlp_fwd(sh)
         Zsum += Z.float()
-        dXsum += run_mlp_bwd(sh, sh.d_("A1"), sh.d_("Y"))["dX"].float()
+        dXm += run_mlp_bwd(sh, sh.d_("A1"), sh.d_("Y"))["dX"].float()
+        dXq += run_qkv_bwd(sh, sh.d_("dQKV"))["dX"].float()
+        torch.cuda.synchronize()
         del sh
     X = synth.X(wl, dt).f64[rows]
-    W1 = synth.fc1_weight(wl, 0, wl.F, dt).f64
-    b1 = synth.fc1_bias(wl, 0, wl.F, dt).f64
-    W2 = synth.fc2_weight(wl, 0, wl.F, dt).f64
+    Wq = synth.qkv_weight(wl, 0, 3 * H, dt).f64
+    bq = synth.qkv_bias(wl, 0, 3 * H, dt).f64
+    assert_close(host(QKVcat)[rows], oracle.qkv_fwd(X, Wq, bq), dt, "concat_r QKV_r rows vs unsharded")
+    dQ = synth.column_blocks("dQKV", T, 0, 3 * H, 1.0, dt).f64[rows]
+    assert_close(host(dXq)[rows], oracle.qkv_bwd(X, Wq, dQ)["dX"], dt, "sum_r qkv dX_r rows vs unsharded")
+    W1 = synth.fc1_weight(wl, 0, F, dt).f64
+    b1 = synth.fc1_bias(wl, 0, F, dt).f64
+    W2 = synth.fc2_weight(wl, 0, F, dt).f64
     b2 = synth.fc2_bias(wl, dt).f64
-    full = oracle.mlp_fwd(X, W1, b1, W2, b2)
-    assert_close(host(Zsum)[rows], full["Z"], dt, "sum_r Z_r rows vs unsharded")
-    A1 = synth.column_blocks("A1", wl.T, 0, wl.F, 1.0, dt).f64[rows]
-    Y = synth.column_blocks("Y", wl.T, 0, wl.F, 1.0, dt).f64[rows]
-    dZ = synth.upstream(wl, wl.H, dt, "dZ").f64[rows]
+    assert_close(host(Zsum)[rows], oracle.mlp_fwd(X, W1, b1, W2, b2)["Z"], dt, "sum_r Z_r rows vs unsharded")
+    A1 = synth.column_blocks("A1", T, 0, F, 1.0, dt).f64[rows]
+    Y = synth.column_blocks("Y", T, 0, F, 1.0, dt).f64[rows]
+    dZ = synth.upstream(wl, H, dt, "dZ").f64[rows]
     fb = oracle.mlp_bwd(X, W1, W2, A1, Y, dZ, True)
-    assert_close(host(dXsum)[rows], fb["dX"], dt, "sum_r dX_r rows vs unsharded")
+    assert_close(host(dXm)[rows], fb["dX"], dt, "sum_r mlp dX_r rows vs unsharded")
+    # whole heads of the concatenated attention output: the first and last head of every rank
+    ctx_h, lse_h = host(ctxcat), host(lsecat)
+    heads = sorted({h for r in range(t) for h in (oracle.shard_range(nh_all, t, r)[0],
+                                                 sum(oracle.shard_range(nh_all, t, r)) - 1)})
+    for h in heads:
+        qh_all = synth.column_blocks("QKVin", T, 3 * d * h, 3 * d * (h + 1), 1.0, dt).f64
+        for b in sorted({0, B - 1}):
+            tok = slice(b * S, (b + 1) * S)
+            rctx, rlse = oracle.attention_fwd(qh_all[tok], 1, S, 1, d)
+            assert_close(ctx_h[tok, d * h:d * (h + 1)], rctx, dt, f"concat ctx head {h} batch {b}")
+            assert_close(lse_h[b, h], rlse[0, 0], dt, f"concat lse head {h} batch {b}", tol=2e-3)
+
+
+def test_gpt2_1p5b_tp2_all_ranks_identities():
+    """GPT-2 1.5B at tp = 2: the uneven 13 / 12-head split (and 3200 MLP columns each)."""
+    all_ranks_identities(GPT2_1P5B)
+
+
+def test_gpt_8p3b_tp8_all_ranks_identities():
+    """The 8.3B layer at tp = 8: all eight ranks (4 heads of 96 and 1536 MLP columns each)."""
+    all_ranks_identities(GPT_8P3B)
 
 
 @pytest.mark.parametrize("rank", [3, 7])

@@ -277,6 +277,33 @@ _ORIG_COMBINE_BWD = T.moe_combine_bwd
 _ORIG_MOE_BWD = T.tp_moe_shard_bwd
 
 
+def _normwise_den_from_got(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    den = np.linalg.norm(got)
+    return np.linalg.norm(got - ref) / den if den > 0 else np.linalg.norm(got - ref)
+
+
+def _normwise_max_norm(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    den = np.abs(ref).max() if ref.size else 0.0
+    return np.abs(got - ref).max() / den if den > 0 else np.abs(got - ref).max()
+
+
+def _blockwise_is_normwise(got, ref, block=64):
+    return T.normwise_error(got, ref)
+
+
+def _blockwise_own_norm_only(got, ref, block=64):
+    g, r = T._as_rows(got), T._as_rows(ref)
+    worst = 0.0
+    for i in range(0, r.shape[0], block):
+        for j in range(0, r.shape[1], block):
+            rb, gb = r[i:i + block, j:j + block], g[i:i + block, j:j + block]
+            den = np.linalg.norm(rb)
+            worst = max(worst, np.linalg.norm(gb - rb) / den if den > 0 else np.linalg.norm(gb - rb))
+    return worst
+
+
 MUTANTS = {
     "gelu_tanh_approx": {"gelu": _gelu_tanh},
     "gelu_grad_drops_x_phi": {"gelu_grad": _gelu_grad_no_density},
@@ -322,6 +349,10 @@ MUTANTS = {
     "moe_combine_bwd_ungated": {"moe_combine_bwd": _combine_bwd_ungated},
     "moe_route_bwd_no_softmax_coupling": {"moe_route_bwd": _route_bwd_no_softmax_coupling},
     "moe_bwd_dX_first_choice_only": {"tp_moe_shard_bwd": _moe_bwd_dX_first_choice},
+    "normwise_denominator_from_got": {"normwise_error": _normwise_den_from_got},
+    "normwise_max_norm": {"normwise_error": _normwise_max_norm},
+    "blockwise_is_normwise": {"blockwise_error": _blockwise_is_normwise},
+    "blockwise_own_norm_only": {"blockwise_error": _blockwise_own_norm_only},
 }
 
 
