@@ -30,10 +30,12 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is ordered on it; calls return
  *    without synchronising.  Outputs are overwritten (never accumulated into).  The backward
  *    calls with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_out_shard_bwd) may
- *    run some of them on a library-owned side stream of the current device (created once, outside
- *    graph capture, default priority), forked from and joined back into `stream` with events before
- *    they return: to the caller the effect is the same as if everything ran on `stream`, and a
- *    captured graph simply gets two branches.  While per-launch timing is on, or when the environment variable TP_SERIAL is
+ *    run some of them on a library-owned side stream (one per caller stream and device, created on
+ *    first use outside graph capture, default priority; for up to 64 such pairs, after which calls
+ *    from further streams run serially on `stream`), forked from and joined back into `stream` with
+ *    events before they return: to the caller the effect is the same as if everything ran on
+ *    `stream`, independent caller streams stay independent, and a captured graph simply gets two
+ *    branches.  While per-launch timing is on, or when the environment variable TP_SERIAL is
  *    set to a non-zero value, everything runs on `stream`.
  *  - Errors: arguments are validated on the host before any launch; a negative tp_status is
  *    returned and nothing is enqueued.  A failed launch returns TP_EHIP; tp_last_error() then holds

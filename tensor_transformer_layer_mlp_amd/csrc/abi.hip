@@ -47,32 +47,45 @@ int hip_status(hipError_t e, const char* where) {
     }                                                \
   } while (0)
 
-// A per-device side stream for launches that do not depend on each other inside one call: the
-// caller's stream forks onto it through an event and joins back before the call returns, so the
-// caller still sees one ordered stream (and a captured graph gets two branches).  The side stream and
-// its events are created on first use outside graph capture and live until the process ends; the
-// mutex serialises the enqueue phase of calls that use them.  Without them, everything runs on the
-// caller's stream.
+// A side stream per caller stream, for launches that do not depend on each other inside one call:
+// the caller's stream forks onto it through an event and joins back before the call returns, so the
+// caller still sees one ordered stream (and a captured graph gets two branches).  Each (device,
+// caller stream) pair gets its own side stream and events, created on first use outside graph
+// capture and kept until the process ends, so independent caller streams share nothing; past
+// kMaxSides pairs, calls run serially on the caller's stream.  The mutex serialises the host-side
+// enqueue phase of the calls that use a side stream (the events are reused from call to call).
 struct Side {
+  int dev = -1;
+  hipStream_t caller = nullptr;
   hipStream_t s2 = nullptr;
   hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
 };
+constexpr int kMaxSides = 64;
 std::mutex g_side_mu;
-Side g_side[64];
+Side g_side[kMaxSides];
+int g_nside = 0;
 
-Side* side_stream(hipStream_t s) {
+bool serial_env() {
   static const bool serial = [] {
     const char* v = getenv("TP_SERIAL");
     return v != nullptr && v[0] != '\0' && v[0] != '0';
   }();
-  if (serial || prof_enabled()) return nullptr;
+  return serial;
+}
+
+// Call with g_side_mu held.
+Side* side_stream(hipStream_t s) {
+  if (serial_env() || prof_enabled()) return nullptr;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  Side& sd = g_side[dev];
-  if (sd.s2) return &sd;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (int i = 0; i < g_nside; ++i)
+    if (g_side[i].dev == dev && g_side[i].caller == s) return &g_side[i];
+  if (g_nside == kMaxSides) return nullptr;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
   Side n;
+  n.dev = dev;
+  n.caller = s;
   if (hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking) != hipSuccess) return nullptr;
   if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&n.mid, hipEventDisableTiming) != hipSuccess ||
@@ -82,8 +95,8 @@ Side* side_stream(hipStream_t s) {
     (void)hipStreamDestroy(n.s2);
     return nullptr;
   }
-  sd = n;
-  return &sd;
+  g_side[g_nside] = n;
+  return &g_side[g_nside++];
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -340,28 +353,26 @@ int tp_mlp_shard_bwd(int tp_size, int rank, int T, int H, int F, int dtype, cons
                               db2, workspace, workspace_bytes, TP_GELU, stream);
 }
 
-int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
-                     const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
-                     void* dWqkv_r, void* dbqkv_r, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-  HeadGeom g;
-  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g);
-  if (st) return st;
-  NEED(X, "X", (long)g.T); NEED(Wqkv_r, "Wqkv_r", 1); NEED(dQKV_r, "dQKV_r", (long)g.T);
-  NEED(dX_r, "dX_r", (long)g.T); NEED(dWqkv_r, "dWqkv_r", 1); NEED(dbqkv_r, "dbqkv_r", 1);
-  const size_t need = qkv_bwd_ws(g.T, g.Nq);
-  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+namespace {
+
+// The QKV shard backward's launches; `ws` holds the bias gradient's column-sum partials.  With
+// use_side, dbqkv and dX run on the caller stream's side stream next to dWqkv.
+int qkv_bwd_launch(int dtype, const HeadGeom& g, int H, const void* X, const void* Wqkv_r, const void* dQKV_r,
+                   void* dX_r, void* dWqkv_r, void* dbqkv_r, float* ws, hipStream_t s, bool use_side) {
   // dWqkv_r = Xᵀ·dQKV_r   (M = H, N = Nq, K = T)
   GemmDesc g1 = gemm_desc(dtype, H, g.Nq, g.T, X, H, false, dQKV_r, g.Nq, false, dWqkv_r, g.Nq, EPI_STORE);
   // dX_r = dQKV_r·Wqkv_rᵀ   (M = T, N = H, K = Nq)
   GemmDesc g2 = gemm_desc(dtype, g.T, H, g.Nq, dQKV_r, g.Nq, true, Wqkv_r, g.Nq, true, dX_r, H, EPI_STORE);
 
   // caller's stream: dWqkv;  side stream: dbqkv, dX (all three independent)
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  Side* sd = side_stream(s);
+  std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+  Side* sd = nullptr;
+  if (use_side) {
+    lk.lock();
+    sd = side_stream(s);
+  }
   hipStream_t s2 = sd ? sd->s2 : s;
   if (sd) {
     TP_TRY(hipEventRecord(sd->fork, s), "fork");
@@ -369,7 +380,7 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
   }
   auto body = [&]() -> int {
     TP_TRY(launch_gemm(g1, s), "dWqkv gemm");
-    TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, (float*)workspace, dbqkv_r, s2), "dbqkv colsum");
+    TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, ws, dbqkv_r, s2), "dbqkv colsum");
     TP_TRY(launch_gemm(g2, s2), "dX gemm");
     return TP_OK;
   };
@@ -379,6 +390,34 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
     TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
   }
   return rc;
+}
+
+int qkv_bwd_args(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype, const void* X,
+                 const void* Wqkv_r, const void* dQKV_r, void* dX_r, void* dWqkv_r, void* dbqkv_r, HeadGeom* g) {
+  int st = head_geom(tp_size, rank, B, S, H, n_heads, dtype, g);
+  if (st) return st;
+  NEED(X, "X", (long)g->T); NEED(Wqkv_r, "Wqkv_r", 1); NEED(dQKV_r, "dQKV_r", (long)g->T);
+  NEED(dX_r, "dX_r", (long)g->T); NEED(dWqkv_r, "dWqkv_r", 1); NEED(dbqkv_r, "dbqkv_r", 1);
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                     const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
+                     void* dWqkv_r, void* dbqkv_r, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  HeadGeom g;
+  int st = qkv_bwd_args(tp_size, rank, B, S, H, n_heads, dtype, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, &g);
+  if (st) return st;
+  const size_t need = qkv_bwd_ws(g.T, g.Nq);
+  TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
+  return qkv_bwd_launch(dtype, g, H, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, (float*)workspace,
+                        (hipStream_t)stream, true);
 }
 
 int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
