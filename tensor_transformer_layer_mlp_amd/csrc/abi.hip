@@ -39,6 +39,14 @@ int hip_status(hipError_t e, const char* where) {
     if (st_ != TP_OK) return st_;                    \
   } while (0)
 
+// The same, with the launches inside labelled by their call site for the per-launch timing.
+#define TP_TRY_AT(site, call, where)                 \
+  do {                                               \
+    ProfSite ps_(site);                              \
+    int st_ = hip_status((call), (where));           \
+    if (st_ != TP_OK) return st_;                    \
+  } while (0)
+
 #define TP_CHECK(cond, code, ...)                    \
   do {                                               \
     if (!(cond)) {                                   \
@@ -240,7 +248,7 @@ int tp_qkv_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
   hipStream_t s = (hipStream_t)stream;
   GemmDesc d = gemm_desc(dtype, g.T, g.Nq, H, X, H, true, Wqkv_r, g.Nq, false, QKV_r, g.Nq, EPI_BIAS);
   d.bias = bqkv_r;
-  TP_TRY(launch_gemm(d, s), "qkv gemm");
+  TP_TRY_AT("qkv_fwd", launch_gemm(d, s), "qkv gemm");
   return TP_OK;
 }
 
@@ -251,7 +259,8 @@ int tp_attn_heads_fwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
   if (st) return st;
   TP_CHECK(attn_supported_dim(g.d), TP_EUNSUPPORTED, "head_dim %d not in {16, 32, 64, 96, 128}", g.d);
   NEED(QKV_r, "QKV_r", (long)g.T); NEED(ctx_r, "ctx_r", (long)g.T); MAYBE(lse_r, "lse_r");
-  TP_TRY(launch_attn_fwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, (hipStream_t)stream), "attention fwd");
+  TP_TRY_AT("attn_fwd", launch_attn_fwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, (hipStream_t)stream),
+            "attention fwd");
   return TP_OK;
 }
 
@@ -269,12 +278,12 @@ int tp_mlp_shard_fwd_act(int tp_size, int rank, int T, int H, int F, int dtype, 
   fc1.bias = b1_r;
   fc1.C2 = A1_r;
   fc1.act = activation;
-  TP_TRY(launch_gemm(fc1, s), "fc1 gemm");
+  TP_TRY_AT("fc1", launch_gemm(fc1, s), "fc1 gemm");
   const bool add_b2 = (rank == 0 && b2 != nullptr);
   GemmDesc fc2 = gemm_desc(dtype, T, H, g.Fr, Y_r, g.Fr, true, W2_r, H, false, Z_r, H,
                            add_b2 ? EPI_BIAS : EPI_STORE);
   fc2.bias = add_b2 ? b2 : nullptr;
-  TP_TRY(launch_gemm(fc2, s), "fc2 gemm");
+  TP_TRY_AT("fc2", launch_gemm(fc2, s), "fc2 gemm");
   return TP_OK;
 }
 
@@ -327,14 +336,14 @@ int tp_mlp_shard_bwd_act(int tp_size, int rank, int T, int H, int F, int dtype, 
     TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
   }
   auto body = [&]() -> int {
-    TP_TRY(launch_gemm(g2, s), "dA1 gemm");
+    TP_TRY_AT("dA1", launch_gemm(g2, s), "dA1 gemm");
     if (sd) TP_TRY(hipEventRecord(sd->mid, s), "dA1 event");
-    TP_TRY(launch_gemm(g1, s2), "dW2 gemm");
-    if (rank == 0 && db2 != nullptr) TP_TRY(launch_colsum(dtype, dZ, H, T, H, cs2, db2, s2), "db2 colsum");
+    TP_TRY_AT("dW2", launch_gemm(g1, s2), "dW2 gemm");
+    if (rank == 0 && db2 != nullptr) TP_TRY_AT("db2", launch_colsum(dtype, dZ, H, T, H, cs2, db2, s2), "db2 colsum");
     if (sd) TP_TRY(hipStreamWaitEvent(s2, sd->mid, 0), "dA1 wait");
-    TP_TRY(launch_gemm(g4, s2), "dX gemm");
-    TP_TRY(launch_colsum(dtype, dA1, Fr, T, Fr, cs1, db1_r, s), "db1 colsum");
-    TP_TRY(launch_gemm(g3, s), "dW1 gemm");
+    TP_TRY_AT("dX_mlp", launch_gemm(g4, s2), "dX gemm");
+    TP_TRY_AT("db1", launch_colsum(dtype, dA1, Fr, T, Fr, cs1, db1_r, s), "db1 colsum");
+    TP_TRY_AT("dW1", launch_gemm(g3, s), "dW1 gemm");
     return TP_OK;
   };
   const int rc = body();
@@ -379,9 +388,9 @@ int qkv_bwd_launch(int dtype, const HeadGeom& g, int H, const void* X, const voi
     TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
   }
   auto body = [&]() -> int {
-    TP_TRY(launch_gemm(g1, s), "dWqkv gemm");
-    TP_TRY(launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, ws, dbqkv_r, s2), "dbqkv colsum");
-    TP_TRY(launch_gemm(g2, s2), "dX gemm");
+    TP_TRY_AT("dWqkv", launch_gemm(g1, s), "dWqkv gemm");
+    TP_TRY_AT("dbqkv", launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, ws, dbqkv_r, s2), "dbqkv colsum");
+    TP_TRY_AT("dX_qkv", launch_gemm(g2, s2), "dX gemm");
     return TP_OK;
   };
   const int rc = body();
@@ -434,7 +443,7 @@ int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, i
   TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  TP_TRY(launch_attn_bwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,
+  TP_TRY_AT("attn_bwd", launch_attn_bwd(dtype, B, S, g.nh, g.d, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,
                          (float*)workspace, (hipStream_t)stream), "attention bwd");
   return TP_OK;
 }
@@ -452,7 +461,7 @@ int tp_attn_out_shard_fwd(int tp_size, int rank, int B, int S, int H, int n_head
   GemmDesc d = gemm_desc(dtype, g.T, H, Kr, ctx_r, Kr, true, Wo_r, H, false, O_r, H,
                          add_bo ? EPI_BIAS : EPI_STORE);
   d.bias = add_bo ? bo : nullptr;
-  TP_TRY(launch_gemm(d, (hipStream_t)stream), "out-proj gemm");
+  TP_TRY_AT("out_fwd", launch_gemm(d, (hipStream_t)stream), "out-proj gemm");
   return TP_OK;
 }
 
@@ -497,12 +506,12 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
     TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
   }
   auto body = [&]() -> int {
-    TP_TRY(launch_gemm(g1, s), "dWo gemm");
+    TP_TRY_AT("dWo", launch_gemm(g1, s), "dWo gemm");
     if (rank == 0 && dbo != nullptr)
-      TP_TRY(launch_colsum(dtype, dO, H, g.T, H, (float*)workspace, dbo, s2), "dbo colsum");
-    TP_TRY(launch_gemm(g2, s2), "dctx gemm");
+      TP_TRY_AT("dbo", launch_colsum(dtype, dO, H, g.T, H, (float*)workspace, dbo, s2), "dbo colsum");
+    TP_TRY_AT("dctx", launch_gemm(g2, s2), "dctx gemm");
     if (g2.epi == EPI_F32)
-      TP_TRY(launch_splitk_sum(g2.ksplit, (long)g.T * Kr, parts, dctx_r, s2), "dctx slice sum");
+      TP_TRY_AT("dctx", launch_splitk_sum(g2.ksplit, (long)g.T * Kr, parts, dctx_r, s2), "dctx slice sum");
     return TP_OK;
   };
   const int rc = body();

@@ -26,10 +26,15 @@ namespace {
 
 const char* tname(int dtype) { return dtype == DT_BF16 ? "__bf16" : "float"; }
 
+// Algorithmic bytes: each operand read once, each output written once (the GeLU' epilogue also
+// reads A1; a split-k launch writes one fp32 partial per slice).
 double gemm_bytes(const GemmDesc& d) {
   const double es = d.dtype == DT_BF16 ? 2.0 : 4.0;
-  double outs = 1.0 + (d.epi == EPI_BIAS_GELU && d.C2 ? 1.0 : 0.0) + (d.epi == EPI_DGELU ? 1.0 : 0.0);
-  return es * ((double)d.M * d.K + (double)d.K * d.N + outs * (double)d.M * d.N);
+  const double mn = (double)d.M * d.N;
+  const double in = es * ((double)d.M * d.K + (double)d.K * d.N);
+  if (d.epi == EPI_F32) return in + 4.0 * (d.ksplit > 1 ? d.ksplit : 1) * mn;
+  const double outs = 1.0 + (d.epi == EPI_BIAS_GELU && d.C2 ? 1.0 : 0.0) + (d.epi == EPI_DGELU ? 1.0 : 0.0);
+  return in + es * outs * mn;
 }
 
 // Visible (query, key) pairs of a causal S x S attention: S(S+1)/2.

@@ -760,6 +760,10 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
 // Tile choice by a small cost model.  A build may pin one
 // configuration with -DTP_GEMM_FORCE_CFG=<index> (tuning).
 const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
+  if (d.epi == EPI_F32) {   // only the ping-pong tile writes fp32 partials (also in tuning builds)
+    *cfg = 9;
+    return kTileName[9];
+  }
 #ifdef TP_GEMM_FORCE_CFG
   *cfg = TP_GEMM_FORCE_CFG;
   return kTileName[TP_GEMM_FORCE_CFG];
@@ -771,10 +775,6 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   // tile moves ≈14% fewer LDS bytes per flop than 256 x 192; on outputs of 4096 x 4096 and more it was
   // measured faster despite its coarser rounds (its partial last round fills with the concurrent
   // input-gradient GEMM)
-  if (d.epi == EPI_F32) {   // only the ping-pong tile writes fp32 partials
-    *cfg = 9;
-    return kTileName[9];
-  }
   if (!d.a_kmajor && !d.b_kmajor && (long)d.M * d.N >= 4096L * 4096L) {
     *cfg = 0;
     return kTileName[0];
@@ -796,10 +796,14 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 1: return run_cfg<C1>(d, s);
     case 2: return run_cfg<C2>(d, s);
     case 3: return run_cfg<C3>(d, s);
+#ifdef TP_GEMM_FORCE_CFG
+    // deeper-pipeline and one-wave-per-SIMD tiles: measured slower on every shard shape, compiled
+    // only into tuning builds that pin a configuration
     case 4: return run_cfg<C4>(d, s);
     case 5: return run_cfg<C5>(d, s);
     case 6: return run_cfg<C6>(d, s);
     case 7: return run_cfg<C7>(d, s);
+#endif
     case 9: return run_pp_cfg(d, s);
     default: return run_cfg<C8>(d, s);
   }

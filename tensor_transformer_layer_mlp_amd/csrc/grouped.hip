@@ -155,8 +155,10 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
     if (e != hipSuccess) return e;
   }
   const double f1 = 2.0 * rows * (double)Fr * H;
-  const double by1 = es * ((double)rows * H + (double)groups * H * Fr + (A1 ? 2.0 : 1.0) * rows * Fr) +
-                     (row_token ? 4.0 * rows : 0.0);
+  // unique bytes: a gathered fc1 reads each of X's `tokens` rows once (its k rows per token come
+  // from the same lines), not the `rows` rows of a dispatched copy
+  const double by1 = es * ((double)(row_token ? tokens : rows) * H + (double)groups * H * Fr +
+                           (A1 ? 2.0 : 1.0) * rows * Fr) + (row_token ? 4.0 * rows : 0.0);
   const double by2 = es * ((double)rows * Fr + (double)groups * Fr * H + (double)rows * H);
   if (tiled) {
     {
@@ -234,7 +236,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   hipError_t e;
   if (rows > 0) {
     ProfScope p(tiled ? "gemm_bf16_grouped<dZ.W2t, dgelu>" : "gemm_generic_grouped<dZ.W2t, dgelu>", s, fl,
-                es * (2.0 * rows * H + 3.0 * rows * Fr) + wts);
+                es * ((double)rows * H + 2.0 * rows * Fr) + wts);   // dZ and A1 read, dA1 written
     e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s)
               : launch_gemm_generic_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s);
     if (e != hipSuccess) return e;
@@ -259,7 +261,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
     const bool t1 = gemm_bf16_grouped_k_eligible(gw1);
     ProfScope p(t1 ? (x_rows ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_bf16_grouped_k<Xt.dA1>")
                    : (x_rows ? "gemm_generic_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1>"), s, fl,
-                es * ((double)rows * H + (double)rows * Fr) + wts);
+                es * ((double)(x_rows ? x_rows_n : rows) * H + (double)rows * Fr) + wts);   // X's unique rows
     e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
            : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);
     if (e != hipSuccess) return e;

@@ -21,8 +21,9 @@
 //                       [0, rows) contribute nothing.  Without gates every gate is 1 (the
 //                       dispatch's backward: a token's input gradient sums its k rows').
 //   moe_combine_bwd_kernel  one workgroup per token, the combine's backward: for each of its k rows
-//                       dZ[r] = gate·d_out[t], the dispatched copy X_perm[r] = X[t], and the gate
-//                       gradient ⟨d_out[t], Z[r]⟩ (fp32, reduced in a fixed order).
+//                       dZ[r] = gate·d_out[t] and the gate gradient ⟨d_out[t], Z[r]⟩ (fp32, reduced
+//                       in a fixed order); optionally also the dispatched copy X_perm[r] = X[t] (the
+//                       MoE backward does not ask for it: its dW1 gathers X's rows inside its loads).
 //   moe_route_bwd_kernel    one wave per token: the softmax again from the fp32 logits, then
 //                       d_logits[e] = p_e·(dg(e) − Σ_j dg_j·p_{i_j}), dg(e) the gradient of the gate
 //                       that chose e (0 if none did).

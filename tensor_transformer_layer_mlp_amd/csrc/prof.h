@@ -7,6 +7,19 @@ namespace tp {
 
 bool prof_enabled();
 
+// Names the call site of the launches that follow on this thread (e.g. "fc1") until it goes out of
+// scope; the launches' records then carry "site|tag" instead of the bare kernel tag.
+class ProfSite {
+ public:
+  explicit ProfSite(const char* site);
+  ~ProfSite();
+  ProfSite(const ProfSite&) = delete;
+  ProfSite& operator=(const ProfSite&) = delete;
+
+ private:
+  const char* prev_;
+};
+
 // Brackets one kernel launch: records an event on `s` now and another when the scope ends.
 // `tag` names the kernel instantiation; flop/bytes are the launch's algorithmic work.
 class ProfScope {

@@ -24,7 +24,12 @@ size_t g_used = 0;
 
 }  // namespace
 
+thread_local const char* g_site = nullptr;
+
 bool prof_enabled() { return g_on; }
+
+ProfSite::ProfSite(const char* site) : prev_(g_site) { g_site = site; }
+ProfSite::~ProfSite() { g_site = prev_; }
 
 ProfScope::ProfScope(const char* tag, hipStream_t s, double flop, double bytes) : slot_(-1), s_(s) {
   if (!g_on) return;
@@ -35,7 +40,7 @@ ProfScope::ProfScope(const char* tag, hipStream_t s, double flop, double bytes) 
     g_recs.push_back(r);
   }
   Rec& r = g_recs[g_used];
-  r.tag = tag;
+  r.tag = g_site ? std::string(g_site) + "|" + tag : std::string(tag);
   r.flop = flop;
   r.bytes = bytes;
   if (hipEventRecord(r.a, s) != hipSuccess) return;

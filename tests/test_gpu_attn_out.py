@@ -62,11 +62,14 @@ def test_out_bwd(wl, dtype, rank):
 # dctx_r [520, 256] has six 256 x 192 output tiles: it runs as four k-slices of H = 2048 into fp32
 # partials that are then summed in slice order
 SPLIT = LayerWorkload("outsplit_b2_s260_h2048_nh16_f8192_tp8", 2, 260, 2048, 16, 8192, 8, (0, 5), 0.02)
+# H = 2056 (257 heads of 8; rank 0 holds 33 of them, rank 7 32): slices of 576, 576, 576 and 328 —
+# a shorter last slice that ends inside a 64-wide k-tile
+SPLIT_RAGGED = LayerWorkload("outsplit_b2_s260_h2056_nh257_f8224_tp8", 2, 260, 2056, 257, 8224, 8, (0, 7), 0.02)
 
 
-@pytest.mark.parametrize("rank", SPLIT.ranks)
-def test_out_bwd_split_k(rank):
-    wl = SPLIT
+@pytest.mark.parametrize("wl,rank", [(w, r) for w in (SPLIT, SPLIT_RAGGED) for r in w.ranks],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_out_bwd_split_k(wl, rank):
     sh = Shard(wl, rank, "bf16")
     ctx, dO = sh.d_("ctx"), sh.d_("dO")
     bd.tp_prof_collect()
@@ -76,8 +79,8 @@ def test_out_bwd_split_k(rank):
         torch.cuda.synchronize()
     finally:
         bd.tp_prof_enable(False)
-    tags = bd.tp_prof_collect()
-    assert "splitk_sum" in tags and any("epi4" in t for t in tags), sorted(tags)
+    tags = bd.tp_prof_collect()     # "call site|kernel tag"
+    assert "dctx|splitk_sum" in tags and any(t.startswith("dctx|") and "epi4" in t for t in tags), sorted(tags)
     ref = oracle.tp_attn_out_shard_bwd(wl.tp_size, rank, wl.B, wl.S, wl.H, wl.n_heads, sh.f64("ctx"),
                                        sh.f64("Wo"), sh.f64("dO"))
     assert_close(o["dctx"], ref["dctx"], "bf16", "dctx_r")
