@@ -129,6 +129,22 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
                      void* dWqkv_r, void* dbqkv_r, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* tp_qkv_shard_bwd for callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and errors as tp_qkv_shard_bwd,
+ * without the workspace: the bias gradient's column-sum partials (ceil(B*S/64) * 3*nh_r*d fp32
+ * values) go to a scratch array inside the library, tp_qkv_shard_bwd_noalloc_max_scratch() bytes
+ * (16 MiB) per device, held from the first call on a device until the process ends.  A shard whose
+ * partials do not fit returns TP_EWORKSPACE before anything is enqueued.  The call allocates
+ * nothing (no hipMalloc / hipFree, no stream or event; per-launch timing off) and runs every launch
+ * on `stream`.  Every call on one device shares that device's scratch: calls that overlap on one
+ * GPU (on different streams, or from different threads without ordering between them) race, so
+ * order them.  The scratch needs no clearing between calls: each call writes every partial it
+ * reads. */
+int tp_qkv_shard_bwd_noalloc(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                             const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
+                             void* dWqkv_r, void* dbqkv_r, void* stream);
+size_t tp_qkv_shard_bwd_noalloc_max_scratch(void);
+
 /* A7 — attention backward over the rank's heads, P recomputed from Q, K and the saved LSE:
  *   D_i = Σ_c dO_ic·O_ic ; dV = Pᵀ·dO ; dP = dO·Vᵀ ; dS = P∘(dP − D) ; dQ = dS·K/√d ; dK = dSᵀ·Q/√d
  * ctx_r and lse_r must be this call's forward outputs for QKV_r.  dQKV_r has QKV_r's layout.

@@ -31,6 +31,8 @@ _SIGNATURES = {
     "tp_mlp_shard_fwd_act": (_I, [_I] * 6 + [_P] * 8 + [_I, _P]),
     "tp_mlp_shard_bwd_act": (_I, [_I] * 6 + [_P] * 11 + [_P, _Z, _I, _P]),
     "tp_qkv_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
+    "tp_qkv_shard_bwd_noalloc": (_I, [_I] * 7 + [_P] * 6 + [_P]),
+    "tp_qkv_shard_bwd_noalloc_max_scratch": (_Z, []),
     "tp_attn_heads_bwd": (_I, [_I] * 7 + [_P] * 5 + [_P, _Z, _P]),
     "tp_attn_out_shard_fwd": (_I, [_I] * 7 + [_P] * 4 + [_P]),
     "tp_attn_out_shard_bwd": (_I, [_I] * 7 + [_P] * 6 + [_P, _Z, _P]),
@@ -220,6 +222,27 @@ def tp_qkv_shard_bwd(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, d
                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                 _stream(stream))
     _check(rc, "tp_qkv_shard_bwd")
+
+
+def tp_qkv_shard_bwd_noalloc(tp_size, rank, B, S, H, n_heads, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r,
+                             stream=None):
+    """tp_qkv_shard_bwd on the library's own scratch array (no workspace argument; allocates nothing)."""
+    dt = X.dtype
+    g = _heads(tp_size, rank, H, n_heads)
+    if g and B >= 0 and S >= 0:
+        T, Nq = B * S, 3 * g[0] * g[1]
+        for t, n, name in ((X, T * H, "X"), (Wqkv_r, H * Nq, "Wqkv_r"), (dQKV_r, T * Nq, "dQKV_r"),
+                           (dX_r, T * H, "dX_r"), (dWqkv_r, H * Nq, "dWqkv_r"), (dbqkv_r, Nq, "dbqkv_r")):
+            _need(t, n, name)
+    rc = raw().tp_qkv_shard_bwd_noalloc(tp_size, rank, B, S, H, n_heads, _dtype_code(X), _ptr(X, "X", dt),
+                                        _ptr(Wqkv_r, "Wqkv_r", dt), _ptr(dQKV_r, "dQKV_r", dt),
+                                        _ptr(dX_r, "dX_r", dt), _ptr(dWqkv_r, "dWqkv_r", dt),
+                                        _ptr(dbqkv_r, "dbqkv_r", dt), _stream(stream))
+    _check(rc, "tp_qkv_shard_bwd_noalloc")
+
+
+def tp_qkv_shard_bwd_noalloc_max_scratch():
+    return int(raw().tp_qkv_shard_bwd_noalloc_max_scratch())
 
 
 def tp_attn_heads_bwd(tp_size, rank, B, S, H, n_heads, QKV_r, ctx_r, lse_r, dctx_r, dQKV_r,

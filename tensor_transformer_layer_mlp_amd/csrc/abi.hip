@@ -107,6 +107,30 @@ Side* side_stream(hipStream_t s) {
   return &g_side[g_nside++];
 }
 
+// Scratch of the entry points that allocate nothing (tp_qkv_shard_bwd_noalloc): one array per
+// device, held until the process ends.  Host code never passes the array's name to a kernel (in
+// host code it is a stand-in, not a device address): its device address is looked up once per device
+// with that device current, on the first call there, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[256] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  TP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  TP_CHECK(dev >= 0 && dev < 256, TP_EUNSUPPORTED, "device %d outside the 256 the scratch table holds", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    TP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    TP_CHECK(p != nullptr && ((uintptr_t)p & 255u) == 0, TP_EHIP, "scratch address %p not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TP_OK;
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t esize(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -427,6 +451,28 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
   TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
   return qkv_bwd_launch(dtype, g, H, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, (float*)workspace,
                         (hipStream_t)stream, true);
+}
+
+size_t tp_qkv_shard_bwd_noalloc_max_scratch(void) { return kScratchBytes; }
+
+int tp_qkv_shard_bwd_noalloc(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
+                             const void* X, const void* Wqkv_r, const void* dQKV_r, void* dX_r,
+                             void* dWqkv_r, void* dbqkv_r, void* stream) {
+  HeadGeom g;
+  int st = qkv_bwd_args(tp_size, rank, B, S, H, n_heads, dtype, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, &g);
+  if (st) return st;
+  const size_t need = qkv_bwd_ws(g.T, g.Nq);
+  TP_CHECK(need <= kScratchBytes, TP_EWORKSPACE,
+           "scratch of %zu bytes needed, above the %zu bytes of the library's scratch array "
+           "(ceil(B*S/64)*3*nh_r*d*4 bytes must stay within it)", need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  // Everything on the caller's stream: no side stream or event is created here.  Every partial the
+  // column sum's second pass reads is written by its first pass in the same call, so the scratch
+  // needs no clearing.
+  return qkv_bwd_launch(dtype, g, H, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, (float*)ws,
+                        (hipStream_t)stream, false);
 }
 
 int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
