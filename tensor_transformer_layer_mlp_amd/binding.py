@@ -12,7 +12,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+# TPSHARD_LIB may name another build of the same library (the host-sanitized one for CPU tests)
+LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(_HERE, "libtpshard.so")
 
 TP_BF16, TP_F32 = 0, 1
 TP_GELU, TP_GELU_TANH = 0, 1

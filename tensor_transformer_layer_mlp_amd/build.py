@@ -1,9 +1,14 @@
 """Build libtpshard.so in-tree with hipcc for gfx950.
 
-    python -m tensor_transformer_layer_mlp_amd.build [-v]
+    python -m tensor_transformer_layer_mlp_amd.build [-v] [--sanitize]
 
 Each HIP source compiles to an object under _build/ (in parallel), then one shared library is
 linked next to this file.  Packed fp32 instructions are disabled for the device code.
+
+--sanitize builds libtpshard_san.so under _build_san/ instead: the host code instrumented with
+AddressSanitizer and UndefinedBehaviorSanitizer (device code unchanged, not sanitized), for the
+CPU-side tests of argument validation.  Load it with TPSHARD_LIB pointing at it and the ASan
+runtime preloaded (see sanitizer_env()).
 """
 
 import os
@@ -41,20 +46,43 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# host-only sanitizers: each -fsanitize= applies to the host compilation alone
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined", "-g"]
+SAN_LIB = os.path.join(PKG, "libtpshard_san.so")
+SAN_BUILD_DIR = os.path.join(ROOT, "_build_san")
+
+
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    bdir, lib = (SAN_BUILD_DIR, SAN_LIB) if sanitize else (BUILD_DIR, LIB)
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in srcs]
-    cmds = [[HIPCC, *CFLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+    objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in srcs]
+    cmds = [[HIPCC, *CFLAGS, *EXTRA.get(s, []), *extra, "-c", os.path.join(CSRC, s), "-o", o]
             for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-shared-libsan"] if sanitize else []
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *link_extra, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_env() -> dict:
+    """Environment for a CPU-only process that loads the sanitized library: the ASan runtime
+    preloaded (the Python interpreter itself is not instrumented), leak checking off (the
+    interpreter's own allocations), and TPSHARD_LIB naming the sanitized build."""
+    rt = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                        text=True).stdout.strip()
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", TPSHARD_LIB=SAN_LIB)
+    return env
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
