@@ -677,24 +677,40 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
   }
 }
 
-// Launch shape: G wave-pair groups per workgroup and KB-row blocks of the looped-over dimension,
-// chosen so that the double-buffered tiles of all groups take at most 128 KiB of LDS.
-#ifndef TP_ATTN_G
-#define TP_ATTN_G 0
+// Launch shape: G wave-pair groups per workgroup and KB-row blocks of the looped-over dimension.
+// Measured on the three GPT shards (d = 64: GPT-2 1.5B tp=2; 96: 8.3B tp=8; 128: GPT-3 tp=8):
+//   d <= 64: forward G = 2, KB = 32 (32 KiB of LDS: four workgroups share a CU; 55 -> 26 us);
+//            backward G = 1, KB = 64 (144 -> 87 us)
+//   d = 96:  G = 2, KB = 32 both ways (23 -> 20 us, 71 -> 65 us)
+//   d = 128: G = 2, KB = 64 (128 KiB of LDS, one workgroup per CU); four groups of 32 keys spill the
+//            backward's accumulators and do not speed the forward
+// A build may pin either kernel's shape for tuning.
+#ifndef TP_ATTN_FWD_G
+#define TP_ATTN_FWD_G 0
 #endif
-#ifndef TP_ATTN_KB
-#define TP_ATTN_KB 0
+#ifndef TP_ATTN_FWD_KB
+#define TP_ATTN_FWD_KB 0
+#endif
+#ifndef TP_ATTN_BWD_G
+#define TP_ATTN_BWD_G 0
+#endif
+#ifndef TP_ATTN_BWD_KB
+#define TP_ATTN_BWD_KB 0
 #endif
 template <int D>
-struct AttnShape {
-  static constexpr int KB = TP_ATTN_KB ? TP_ATTN_KB : 64;
-  static constexpr int G = TP_ATTN_G ? TP_ATTN_G
-                                     : (4 * AC<D>::template tile<KB>() >= 65536 ? 2 : 4);
+struct AttnShape {   // backward (dK/dV and dQ)
+  static constexpr int KB = TP_ATTN_BWD_KB ? TP_ATTN_BWD_KB : (D == 96 ? 32 : 64);
+  static constexpr int G = TP_ATTN_BWD_G ? TP_ATTN_BWD_G : (D <= 64 ? 1 : 2);
+};
+template <int D>
+struct AttnFwdShape {
+  static constexpr int KB = TP_ATTN_FWD_KB ? TP_ATTN_FWD_KB : (D <= 96 ? 32 : 64);
+  static constexpr int G = TP_ATTN_FWD_G ? TP_ATTN_FWD_G : 2;
 };
 
 template <int D>
 hipError_t fwd_t(int B, int S, int nh, const void* qkv, void* ctx, float* lse, hipStream_t s) {
-  constexpr int G = AttnShape<D>::G, KB = AttnShape<D>::KB;
+  constexpr int G = AttnFwdShape<D>::G, KB = AttnFwdShape<D>::KB;
   const int nqb = (S + 63) / 64;
   attn_fwd_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (bf16*)ctx, lse);
   return hipGetLastError();
