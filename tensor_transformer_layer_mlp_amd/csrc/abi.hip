@@ -212,13 +212,40 @@ int ln_geom(int tp_size, int rank, int sequence_parallel, int T, int H, int dtyp
     TP_CHECK((p) == nullptr || aligned16(p), TP_EALIGN, "%s is not 16-byte aligned", (name)); \
   } while (0)
 
-// dA1, then the db1 and db2 column-sum partials (separate: the two sums may run concurrently)
-size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
-  return align256((size_t)T * Fr * esize(dtype)) + align256(colsum_ws_bytes(T, Fr)) +
-         align256(colsum_ws_bytes(T, H));
+// k-slices for a weight gradient C[M, N] = Aᵀ·B summed over K tokens (both operands MN-major, the
+// 256 x 256 tile).  When the output has few tiles the chip runs one partial round with long k loops;
+// slicing k fills more CUs at the price of fp32 partials that a bandwidth pass sums.  Model: rounds
+// of 256 tiles x k per slice x 0.02 us (the tile's rate per unit of k) + 0.8 ps per partial element
+// (read at about 5 TB/s); each slice at least 1024 deep.  bf16 only.
+int wgrad_split(int dtype, int M, int N, int K) {
+  if (dtype != DT_BF16 || M <= 0 || N <= 0 || K < 2048) return 1;
+  const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+  int best = 1;
+  double best_t = 1e300;
+  for (int ks = 1; ks <= 4 && (long)K >= 1024L * ks; ++ks) {
+    const long rounds = (tiles * ks + 255) / 256;
+    const double t = (double)rounds * ((double)K / ks) * 0.02 + (ks > 1 ? 0.8e-6 * ks * (double)M * N : 0.0);
+    if (t < best_t * 0.97) { best_t = t; best = ks; }
+  }
+  return best;
 }
 
-size_t qkv_bwd_ws(int T, int Nq) { return align256(colsum_ws_bytes(T, Nq)); }
+size_t wgrad_ws(int dtype, int M, int N, int K) {
+  const int ks = wgrad_split(dtype, M, N, K);
+  return ks > 1 ? align256((size_t)ks * (size_t)M * (size_t)N * sizeof(float)) : 0;
+}
+
+// dA1, then the db1 and db2 column-sum partials, then the dW2 and dW1 k-slice partials (separate:
+// the sums and the two weight gradients may run concurrently)
+size_t mlp_bwd_ws(int T, int H, int Fr, int dtype) {
+  return align256((size_t)T * Fr * esize(dtype)) + align256(colsum_ws_bytes(T, Fr)) +
+         align256(colsum_ws_bytes(T, H)) + wgrad_ws(dtype, Fr, H, T) + wgrad_ws(dtype, H, Fr, T);
+}
+
+// dbqkv's column-sum partials, then dWqkv's k-slice partials (without them when split is false)
+size_t qkv_bwd_ws(int T, int H, int Nq, int dtype, bool split = true) {
+  return align256(colsum_ws_bytes(T, Nq)) + (split ? wgrad_ws(dtype, H, Nq, T) : 0);
+}
 
 // k-slices for the output projection's input gradient dctx = dO·Wo_rᵀ (M = T, N = nh_r·d, K = H): its
 // few output tiles would leave most CUs idle, so the k dimension is split until about 256 tiles run,
@@ -234,7 +261,7 @@ int out_bwd_split(int dtype, int T, int Kr, int H) {
 size_t out_bwd_ws(int T, int H, int Kr, int dtype) {
   const int sk = out_bwd_split(dtype, T, Kr, H);
   const size_t parts = sk > 1 ? align256((size_t)sk * (size_t)T * (size_t)Kr * sizeof(float)) : 0;
-  return align256(colsum_ws_bytes(T, H)) + parts;
+  return align256(colsum_ws_bytes(T, H)) + parts + wgrad_ws(dtype, Kr, H, T);
 }
 
 GemmDesc gemm_desc(int dtype, int M, int N, int K, const void* A, long lda, bool a_kmajor,
@@ -246,6 +273,27 @@ GemmDesc gemm_desc(int dtype, int M, int N, int K, const void* A, long lda, bool
   d.B = B; d.ldb = ldb; d.b_kmajor = b_kmajor;
   d.C = C; d.ldc = ldc; d.epi = epi; d.dtype = dtype;
   return d;
+}
+
+// Launches the weight gradient g (both operands MN-major, output bf16 at g.C) as ks k-slices of fp32
+// partials in `parts` followed by their sum in slice order, or in one piece when ks <= 1 or the tiled
+// kernel does not take the split form.
+hipError_t launch_wgrad(const GemmDesc& g, int ks, float* parts, hipStream_t s) {
+  if (ks > 1) {
+    GemmDesc gs = g;
+    gs.epi = EPI_F32;
+    gs.C = parts;
+    gs.ldc = g.N;
+    gs.ksplit = ks;
+    gs.k_per = ((g.K + ks - 1) / ks + 63) / 64 * 64;
+    gs.c_split = (long)g.M * g.N;
+    if (gemm_bf16_eligible(gs) && g.ldc == g.N && ((uintptr_t)g.C & 15) == 0 && ((long)g.M * g.N) % 8 == 0) {
+      hipError_t e = launch_gemm(gs, s);
+      if (e != hipSuccess) return e;
+      return launch_splitk_sum(ks, (long)g.M * g.N, parts, g.C, s);
+    }
+  }
+  return launch_gemm(g, s);
 }
 
 }  // namespace
@@ -338,6 +386,9 @@ int tp_mlp_shard_bwd_act(int tp_size, int rank, int T, int H, int F, int dtype, 
   void* dA1 = workspace;
   float* cs1 = (float*)((char*)workspace + align256((size_t)T * Fr * esize(dtype)));
   float* cs2 = (float*)((char*)cs1 + align256(colsum_ws_bytes(T, Fr)));
+  float* p2 = (float*)((char*)cs2 + align256(colsum_ws_bytes(T, H)));   // dW2's k-slice partials
+  float* p1 = (float*)((char*)p2 + wgrad_ws(dtype, Fr, H, T));          // dW1's
+  const int ks2 = wgrad_split(dtype, Fr, H, T), ks1 = wgrad_split(dtype, H, Fr, T);
 
   // dW2_r = Y_rᵀ·dZ   (M = F_r, N = H, K = T)
   GemmDesc g1 = gemm_desc(dtype, Fr, H, T, Y_r, Fr, false, dZ, H, false, dW2_r, H, EPI_STORE);
@@ -362,12 +413,12 @@ int tp_mlp_shard_bwd_act(int tp_size, int rank, int T, int H, int F, int dtype, 
   auto body = [&]() -> int {
     TP_TRY_AT("dA1", launch_gemm(g2, s), "dA1 gemm");
     if (sd) TP_TRY(hipEventRecord(sd->mid, s), "dA1 event");
-    TP_TRY_AT("dW2", launch_gemm(g1, s2), "dW2 gemm");
+    TP_TRY_AT("dW2", launch_wgrad(g1, ks2, p2, s2), "dW2 gemm");
     if (rank == 0 && db2 != nullptr) TP_TRY_AT("db2", launch_colsum(dtype, dZ, H, T, H, cs2, db2, s2), "db2 colsum");
     if (sd) TP_TRY(hipStreamWaitEvent(s2, sd->mid, 0), "dA1 wait");
     TP_TRY_AT("dX_mlp", launch_gemm(g4, s2), "dX gemm");
     TP_TRY_AT("db1", launch_colsum(dtype, dA1, Fr, T, Fr, cs1, db1_r, s), "db1 colsum");
-    TP_TRY_AT("dW1", launch_gemm(g3, s), "dW1 gemm");
+    TP_TRY_AT("dW1", launch_wgrad(g3, ks1, p1, s), "dW1 gemm");
     return TP_OK;
   };
   const int rc = body();
@@ -393,7 +444,8 @@ namespace {
 // The QKV shard backward's launches; `ws` holds the bias gradient's column-sum partials.  With
 // use_side, dbqkv and dX run on the caller stream's side stream next to dWqkv.
 int qkv_bwd_launch(int dtype, const HeadGeom& g, int H, const void* X, const void* Wqkv_r, const void* dQKV_r,
-                   void* dX_r, void* dWqkv_r, void* dbqkv_r, float* ws, hipStream_t s, bool use_side) {
+                   void* dX_r, void* dWqkv_r, void* dbqkv_r, float* ws, hipStream_t s, bool use_side,
+                   bool split) {
   // dWqkv_r = Xᵀ·dQKV_r   (M = H, N = Nq, K = T)
   GemmDesc g1 = gemm_desc(dtype, H, g.Nq, g.T, X, H, false, dQKV_r, g.Nq, false, dWqkv_r, g.Nq, EPI_STORE);
   // dX_r = dQKV_r·Wqkv_rᵀ   (M = T, N = H, K = Nq)
@@ -412,7 +464,9 @@ int qkv_bwd_launch(int dtype, const HeadGeom& g, int H, const void* X, const voi
     TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
   }
   auto body = [&]() -> int {
-    TP_TRY_AT("dWqkv", launch_gemm(g1, s), "dWqkv gemm");
+    const int ks = split ? wgrad_split(dtype, H, g.Nq, g.T) : 1;
+    float* parts = (float*)((char*)ws + align256(colsum_ws_bytes(g.T, g.Nq)));
+    TP_TRY_AT("dWqkv", launch_wgrad(g1, ks, parts, s), "dWqkv gemm");
     TP_TRY_AT("dbqkv", launch_colsum(dtype, dQKV_r, g.Nq, g.T, g.Nq, ws, dbqkv_r, s2), "dbqkv colsum");
     TP_TRY_AT("dX_qkv", launch_gemm(g2, s2), "dX gemm");
     return TP_OK;
@@ -445,12 +499,12 @@ int tp_qkv_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, in
   HeadGeom g;
   int st = qkv_bwd_args(tp_size, rank, B, S, H, n_heads, dtype, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, &g);
   if (st) return st;
-  const size_t need = qkv_bwd_ws(g.T, g.Nq);
+  const size_t need = qkv_bwd_ws(g.T, H, g.Nq, dtype);
   TP_CHECK(workspace != nullptr || need == 0, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(workspace == nullptr || ((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
   return qkv_bwd_launch(dtype, g, H, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, (float*)workspace,
-                        (hipStream_t)stream, true);
+                        (hipStream_t)stream, true, true);
 }
 
 size_t tp_qkv_shard_bwd_noalloc_max_scratch(void) { return kScratchBytes; }
@@ -461,18 +515,18 @@ int tp_qkv_shard_bwd_noalloc(int tp_size, int rank, int B, int S, int H, int n_h
   HeadGeom g;
   int st = qkv_bwd_args(tp_size, rank, B, S, H, n_heads, dtype, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, &g);
   if (st) return st;
-  const size_t need = qkv_bwd_ws(g.T, g.Nq);
+  const size_t need = qkv_bwd_ws(g.T, H, g.Nq, dtype, false);
   TP_CHECK(need <= kScratchBytes, TP_EWORKSPACE,
            "scratch of %zu bytes needed, above the %zu bytes of the library's scratch array "
            "(ceil(B*S/64)*3*nh_r*d*4 bytes must stay within it)", need, kScratchBytes);
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st) return st;
-  // Everything on the caller's stream: no side stream or event is created here.  Every partial the
-  // column sum's second pass reads is written by its first pass in the same call, so the scratch
-  // needs no clearing.
+  // Everything on the caller's stream: no side stream or event is created here, and dWqkv is never
+  // split along k (its partials would not fit the scratch).  Every partial the column sum's second
+  // pass reads is written by its first pass in the same call, so the scratch needs no clearing.
   return qkv_bwd_launch(dtype, g, H, X, Wqkv_r, dQKV_r, dX_r, dWqkv_r, dbqkv_r, (float*)ws,
-                        (hipStream_t)stream, false);
+                        (hipStream_t)stream, false, false);
 }
 
 int tp_attn_heads_bwd(int tp_size, int rank, int B, int S, int H, int n_heads, int dtype,
@@ -533,6 +587,9 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
   GemmDesc g2 = gemm_desc(dtype, g.T, Kr, H, dO, H, true, Wo_r, H, true, dctx_r, Kr, EPI_STORE);
   const int sk = out_bwd_split(dtype, g.T, Kr, H);
   float* parts = (float*)((char*)workspace + align256(colsum_ws_bytes(g.T, H)));
+  const size_t dctx_parts = sk > 1 ? align256((size_t)sk * (size_t)g.T * (size_t)Kr * sizeof(float)) : 0;
+  float* wparts = (float*)((char*)parts + dctx_parts);   // dWo's k-slice partials
+  const int ksw = wgrad_split(dtype, Kr, H, g.T);
   if (sk > 1) {
     GemmDesc gs = g2;
     gs.epi = EPI_F32;
@@ -552,7 +609,7 @@ int tp_attn_out_shard_bwd(int tp_size, int rank, int B, int S, int H, int n_head
     TP_TRY(hipStreamWaitEvent(s2, sd->fork, 0), "fork");
   }
   auto body = [&]() -> int {
-    TP_TRY_AT("dWo", launch_gemm(g1, s), "dWo gemm");
+    TP_TRY_AT("dWo", launch_wgrad(g1, ksw, wparts, s), "dWo gemm");
     if (rank == 0 && dbo != nullptr)
       TP_TRY_AT("dbo", launch_colsum(dtype, dO, H, g.T, H, (float*)workspace, dbo, s2), "dbo colsum");
     TP_TRY_AT("dctx", launch_gemm(g2, s2), "dctx gemm");
@@ -825,7 +882,7 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   HeadGeom g;
   if (strcmp(fn, "tp_qkv_shard_bwd") == 0) {
     if (head_geom(tp_size, rank, B, S, H, n_heads, dtype, &g)) return 0;
-    return qkv_bwd_ws(g.T, g.Nq);
+    return qkv_bwd_ws(g.T, H, g.Nq, dtype);
   }
   if (strcmp(fn, "tp_fp8_quantize") == 0) return align256(fp8_quantize_ws_bytes());
   if (strcmp(fn, "tp_bias_grad") == 0) {

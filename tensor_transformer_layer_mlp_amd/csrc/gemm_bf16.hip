@@ -27,6 +27,9 @@ namespace tp {
 
 namespace {
 
+#ifndef TP_GEMM_ROT_MIN_NK
+#define TP_GEMM_ROT_MIN_NK 0      // k loops shorter than this start at k-tile 0 (tuning builds)
+#endif
 constexpr unsigned OOB = 0x80000000u;   // byte offset beyond any descriptor range -> loads zero
 
 template <int BM_, int BN_, int WM_, int WN_, int ST_ = 2, int BK_ = 64, int OCC_ = 0>
@@ -340,7 +343,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
   const int nk = (d.K + BKT - 1) / BKT;
   // k-tiles are visited starting at tile `rot` (mod nk); the sum over k is the same, only its order
   // differs between tiles that use different starting points
-  rot = nk > 0 ? rot % nk : 0;
+  rot = (nk > 0 && nk >= TP_GEMM_ROT_MIN_NK) ? rot % nk : 0;
   auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * BKT; };
   // prologue: tiles 0 .. STAGES-2 in flight
   if constexpr (GATHER_K) {
@@ -418,9 +421,13 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   // (column-major inside a group): the tiles an XCD runs at once form a compact block, so both their
   // A row panels and B column panels are shared in that XCD's L2.
   constexpr int GROUP_M = 4;
-  const int nwg = tiles_m * tiles_n;
+  // split-k (fp32 partials, both operands MN-major): the grid holds ksplit copies of the tile set
+  const int ks = (EPI == EPI_F32 && d.ksplit > 1) ? d.ksplit : 1;
+  const int tiles = tiles_m * tiles_n, nwg = tiles * ks;
   int wg = blockIdx.x;
   if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int slice = wg / tiles;
+  wg -= slice * tiles;
   const int per_group = GROUP_M * tiles_n;
   const int first_m = (wg / per_group) * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
@@ -428,7 +435,20 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
   const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
   // Tiles that run together begin their k loops at different k-tiles, so that their concurrent
   // loads of strided operand rows fall on different memory channels (measured: 2-4% per GEMM).
-  gemm_tile<Cfg, AK, BK, EPI>(d, m0, n0, (TP_LDS char*)smem, wave, lane, tm + tn);
+  if constexpr (EPI == EPI_F32) {
+    static_assert(!AK && !BK, "the plain kernel's split-k takes two MN-major operands");
+    GemmDesc ds = d;
+    if (ks > 1) {   // slice s: k rows [s·k_per, min(K, (s+1)·k_per)) of both operands
+      const int k0 = slice * d.k_per;
+      ds.A = (const bf16*)d.A + (long)k0 * d.lda;
+      ds.B = (const bf16*)d.B + (long)k0 * d.ldb;
+      ds.K = max(0, min(d.k_per, d.K - k0));
+      ds.C = (float*)d.C + slice * d.c_split;
+    }
+    gemm_tile<Cfg, AK, BK, EPI>(ds, m0, n0, (TP_LDS char*)smem, wave, lane, tm + tn);
+  } else {
+    gemm_tile<Cfg, AK, BK, EPI>(d, m0, n0, (TP_LDS char*)smem, wave, lane, tm + tn);
+  }
 }
 
 // Ping-pong schedule on a 256 x 192 tile (k = 64 per tile, two LDS stages, 512 threads).  The eight
@@ -494,7 +514,7 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, 
   for (int j = 0; j < IPW_B; ++j) piece<BK, LB, P::BKT>((w4 * IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
 
   const int nk = (d.K + P::BKT - 1) / P::BKT;
-  rot = nk > 0 ? rot % nk : 0;
+  rot = (nk > 0 && nk >= TP_GEMM_ROT_MIN_NK) ? rot % nk : 0;
   auto kpos = [&](int t) { const int i = t + rot; return (i >= nk ? i - nk : i) * P::BKT; };
   // this wave's share of k-tile t's loads into stage st
   auto issue = [&](int t, int st) {
@@ -672,7 +692,8 @@ void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
 template <class Cfg, bool AK, bool BK, int EPI>
 hipError_t run(const GemmDesc& d, hipStream_t s) {
   const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
-  gemm_bf16_kernel<Cfg, AK, BK, EPI><<<tiles_m * tiles_n, Cfg::NT, 0, s>>>(d, tiles_m, tiles_n);
+  const int ks = (EPI == EPI_F32 && d.ksplit > 1) ? d.ksplit : 1;
+  gemm_bf16_kernel<Cfg, AK, BK, EPI><<<tiles_m * tiles_n * ks, Cfg::NT, 0, s>>>(d, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -748,8 +769,8 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
   if ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) return false;
   if (d.epi == EPI_BIAS_GELU && d.C2 && (((uintptr_t)d.C2) & 15)) return false;
   if (d.epi == EPI_DGELU && ((d.ld_aux & 7) || (((uintptr_t)d.aux) & 15))) return false;
-  if (d.epi == EPI_F32)   // split-k partials: the ping-pong tile, both operands K-major, slices of whole k-tiles
-    return d.a_kmajor && d.b_kmajor && ((d.ldc & 3) == 0) &&
+  if (d.epi == EPI_F32)   // split-k partials: both operands K-major (the ping-pong tile) or both MN-major
+    return d.a_kmajor == d.b_kmajor && ((d.ldc & 3) == 0) &&   // (the 256 x 256 tile), whole k-tiles per slice
            (d.ksplit <= 1 || (d.k_per > 0 && d.k_per % 64 == 0 && (long)d.k_per * d.ksplit >= d.K));
   const bool supported = (d.a_kmajor && !d.b_kmajor && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_GELU || d.epi == EPI_STORE)) ||
                          (d.a_kmajor && d.b_kmajor && (d.epi == EPI_DGELU || d.epi == EPI_STORE)) ||
@@ -760,9 +781,9 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
 // Tile choice by a small cost model.  A build may pin one
 // configuration with -DTP_GEMM_FORCE_CFG=<index> (tuning).
 const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
-  if (d.epi == EPI_F32) {   // only the ping-pong tile writes fp32 partials (also in tuning builds)
-    *cfg = 9;
-    return kTileName[9];
+  if (d.epi == EPI_F32) {   // fp32 partials: the ping-pong tile (K-major operands) or 256 x 256 (MN-major),
+    *cfg = d.a_kmajor ? 9 : 0;   // also in tuning builds
+    return kTileName[*cfg];
   }
 #ifdef TP_GEMM_FORCE_CFG
   *cfg = TP_GEMM_FORCE_CFG;
@@ -792,7 +813,9 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
   switch (cfg) {
-    case 0: return run_cfg<C0>(d, s);
+    case 0:   // the weight gradients' split-k partials take this tile only
+      if (d.epi == EPI_F32 && !d.a_kmajor && !d.b_kmajor) return run<C0, false, false, EPI_F32>(d, s);
+      return run_cfg<C0>(d, s);
     case 1: return run_cfg<C1>(d, s);
     case 2: return run_cfg<C2>(d, s);
     case 3: return run_cfg<C3>(d, s);

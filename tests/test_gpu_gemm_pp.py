@@ -132,3 +132,58 @@ def test_large_tiles_deterministic():
         runs.append(dict(Z=Z, A1=A1, Y=Y, dX=o["dX"], dW1=o["dW1"], dW2=o["dW2"], db1=o["db1"]))
     for k in runs[0]:
         assert torch.equal(runs[0][k], runs[1][k]), f"{k} differs between two identical calls"
+
+
+# few output tiles over a long token dimension: the weight gradients dW1, dW2 ([512, 512]: four
+# 256 x 256 tiles) and dWqkv ([512, 768]: six) run as four k-slices of fp32 partials over
+# K = T = 4104 (slices 1088, 1088, 1088 and 840, the last ending inside a 64-wide k-tile), summed
+# in slice order; the attention output projection's dWo ([256, 512]) likewise
+WG_SPLIT = LayerWorkload("wgsplit_b4_s1026_h512_nh8_f1024_tp2", 4, 1026, 512, 8, 1024, 2, (0, 1), 0.03)
+
+
+@pytest.mark.parametrize("rank", WG_SPLIT.ranks)
+def test_weight_gradients_split_k(rank):
+    from test_gpu_attn_out import run_out_bwd
+    from test_gpu_parity import run_qkv_bwd
+    wl = WG_SPLIT
+    sh = Shard(wl, rank, "bf16")
+    T, H, Fr = wl.T, wl.H, sh.Fr
+    ws = bd.workspace("tp_mlp_shard_bwd", wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, wl.F, torch.bfloat16)
+
+    def mlp():
+        o = dict(dX=empty((T, H), "bf16"), dW1=empty((H, Fr), "bf16"), db1=empty((Fr,), "bf16"),
+                 dW2=empty((Fr, H), "bf16"), db2=empty((H,), "bf16"))
+        bd.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.d_("X"), sh.d_("W1"), sh.d_("W2"), sh.d_("A1"),
+                            sh.d_("Y"), sh.d_("dZ"), o["dX"], o["dW1"], o["db1"], o["dW2"], o["db2"], ws)
+        return o
+
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        o = mlp()
+        q = run_qkv_bwd(sh, sh.d_("dQKV"))
+        ob = run_out_bwd(sh, sh.d_("ctx"), sh.d_("dO"))
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    tags = bd.tp_prof_collect()
+    for site in ("dW1", "dW2", "dWqkv", "dWo"):
+        assert f"{site}|splitk_sum" in tags and any(t.startswith(site + "|") and "tn, epi4" in t for t in tags), \
+            (site, sorted(tags))
+    ref = oracle.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("W2"),
+                                  sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
+    for k in ("dX", "dW1", "db1", "dW2", "db2"):
+        if k == "db2" and rank != 0:
+            continue
+        assert_close(o[k], ref[k], "bf16", k)
+    rq = oracle.tp_qkv_shard_bwd(wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, sh.f64("X"), sh.f64("Wqkv"),
+                                 sh.f64("dQKV"))
+    assert_close(q["dW"], rq["dW"], "bf16", "dWqkv")
+    assert_close(q["dX"], rq["dX"], "bf16", "qkv dX")
+    ro = oracle.tp_attn_out_shard_bwd(wl.tp_size, rank, wl.B, wl.S, H, wl.n_heads, sh.f64("ctx"), sh.f64("Wo"),
+                                      sh.f64("dO"))
+    assert_close(ob["dW"], ro["dW"], "bf16", "dWo")
+    again = mlp()
+    torch.cuda.synchronize()
+    for k in ("dW1", "dW2"):
+        assert torch.equal(o[k], again[k]), f"{k}: the slice sum is in a fixed order"
