@@ -77,3 +77,41 @@ def test_fp8_gemm_tanh_gelu():
     ref = oracle.fp8_gemm_nt(A, da, B, db, bias.f64)
     assert_close(Cp, ref["pre"], "bf16", "pre-activation")
     assert_close(C, oracle.gelu_tanh(ref["pre"]), "bf16", "tanh-form GeLU")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_gelu_elementwise(dtype):
+    """The device's exact GeLU and GeLU' elementwise, through the MLP shard at tp = 1 with identity
+    weights, zero bias and an all-ones dZ: A1 = X (one product per output, exact), Y = GeLU(X), and
+    db1 = Σ_t (dZ·W2ᵀ)∘GeLU'(A1) = Σ_t GeLU'(X_t).  X holds 8 rows of 4096 points spanning [−9, 9]
+    (bf16-representable, so both modes see the same values).  Bound: the evaluation's own error
+    (2.1e-7 for GeLU and 7e-8 for GeLU' absolute) plus the output's rounding (fp32; bf16 for Y in bf16
+    mode), against the oracle's erf-based values."""
+    T, H = 8, 4096
+    xs = np.linspace(-9.0, 9.0, T * H).reshape(T, H)
+    X = synth.make_operand(xs, "bf16").f64                      # bf16-exact points
+    op = synth.make_operand(X, dtype)
+    eye = synth.make_operand(np.eye(H), dtype)
+    zero = synth.make_operand(np.zeros(H), dtype)
+    ones = synth.make_operand(np.ones((T, H)), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Xd, I, z, dZ = dev(op), dev(eye), dev(zero), dev(ones)
+    Z, A1, Y = empty((T, H), dtype), empty((T, H), dtype), empty((T, H), dtype)
+    bd.tp_mlp_shard_fwd(1, 0, T, H, H, Xd, I, z, I, z, Z, A1, Y)
+    o = dict(dX=empty((T, H), dtype), dW1=empty((H, H), dtype), db1=empty((H,), dtype), dW2=empty((H, H), dtype),
+             db2=empty((H,), dtype))
+    wsb = bd.workspace("tp_mlp_shard_bwd", 1, 0, 1, T, H, 1, H, tdt)
+    bd.tp_mlp_shard_bwd(1, 0, T, H, H, Xd, I, I, A1, Y, dZ, o["dX"], o["dW1"], o["db1"], o["dW2"], o["db2"], wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(A1), X), "A1 = X·I must be exact"
+    g, gg = oracle.gelu(X), oracle.gelu_grad(X)
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    err = np.abs(host(Y) - g)
+    assert (err <= 2.2e-7 + rel * np.abs(g)).all(), f"GeLU: worst excess {(err - rel * np.abs(g)).max():.3e}"
+    # db1 sums the stored dA1 = GeLU'(X_t) (rounded to the storage type) over the 8 rows in fp32,
+    # then rounds the sum to the storage type
+    want = gg.sum(axis=0)
+    e1 = np.abs(host(o["db1"]) - want)
+    r_elem = (2.0 ** -9 if dtype == "bf16" else 0.0) + 8 * 2.0 ** -23
+    tol1 = 8 * 7.5e-8 + r_elem * np.abs(gg).sum(axis=0) + rel * np.abs(want)
+    assert (e1 <= tol1).all(), f"GeLU': worst excess {(e1 - tol1).max():.3e}"
