@@ -56,7 +56,7 @@ def parse():
                     help="with --pmc-pass: also one residual + LayerNorm forward and backward")
     ap.add_argument("--blas-compare", action="store_true",
                     help="also time torch.matmul on the nine GEMM shapes of the GPT-3 shard")
-    ap.add_argument("--summarize", choices=["stats", "traffic", "mfma", "hbm"],
+    ap.add_argument("--summarize", choices=["stats", "traffic", "mfma", "hbm", "lds"],
                     help="print a profile summary from rocprofv3 CSV output under --prof-dir, and exit")
     ap.add_argument("--prof-dir", default="gpurun_out/prof",
                     help="rocprofv3 output directory (stats: one kernel-trace run; traffic / hbm: the "
@@ -650,6 +650,25 @@ def summarize(what, d, kernel, tag):
                 print("%-34s %9d %10.2f %10.2f %9.2f %9.1f %7.1f%%" % (name[:34], a["grid"], a["FETCH_SIZE"] * ff / 1e6,
                                                                        b["WRITE_SIZE"] * fw / 1e6, us, byts / us / 1e3,
                                                                        100 * byts / us / 1e3 / PEAK_HBM_GBS))
+    elif what == "lds":
+        L = [e for e in _pmc_dispatches(os.path.join(d, "pmc_lds")) if _is_library(e["name"])]
+        T = [e for e in _pmc_dispatches(os.path.join(d, "pmc_ta")) if _is_library(e["name"])]
+        n = len(STEP_LABELS)
+        print("# per dispatch of the last step; cycles = GRBM_GUI_ACTIVE / 8, utilisations over 256 CUs")
+        print("# LdsUtil = SQ_LDS_IDX_ACTIVE / (cycles x 256) (indexed LDS operations only: ds_read / ds_write,")
+        print("#   not the direct global -> LDS loads); bank = SQ_LDS_BANK_CONFLICT / (cycles x 256);")
+        print("# TA, TD = TA_TA_BUSY, TD_TD_BUSY / (cycles x 256); wait LDS, wait any = SQ_WAIT_INST_LDS,")
+        print("#   SQ_WAIT_ANY / SQ_WAVE_CYCLES (shares of the waves' resident cycles)")
+        print("%-36s %7s %8s %6s %6s %6s %9s %9s" % ("dispatch", "dur us", "LdsUtil", "bank", "TA", "TD", "wait LDS",
+                                                     "wait any"))
+        labels = STEP_LABELS if len(L) % n == 0 else [short_kernel(e["name"])[:36] for e in L[-n:]]
+        for lab, a, b in zip(labels, L[-n:], T[-n:]):
+            g = a["GRBM_GUI_ACTIVE"] / 8 * 256
+            wc = max(b["SQ_WAVE_CYCLES"], 1.0)
+            print("%-36s %7.1f %7.1f%% %5.1f%% %5.1f%% %5.1f%% %8.1f%% %8.1f%%" % (
+                lab[:36], a["dur"], 100 * a["SQ_LDS_IDX_ACTIVE"] / g, 100 * a["SQ_LDS_BANK_CONFLICT"] / g,
+                100 * b["TA_TA_BUSY"] / g, 100 * b["TD_TD_BUSY"] / g, 100 * a["SQ_WAIT_INST_LDS"] / wc,
+                100 * b["SQ_WAIT_ANY"] / wc))
     elif what == "mfma":
         import numpy as np
         clk = [e for e in _pmc_dispatches(os.path.join(d, "pmc_clk")) if _is_library(e["name"])]
