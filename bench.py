@@ -249,11 +249,12 @@ def moe_layer(bd, torch, steps, warmup):
     apart.  Forward, from router logits to the combined partial: tp_moe_route (top-8 of 128,
     dispatch order) then tp_moe_shard_fwd (fc1 with the dispatch gathered from X inside its operand
     loads, GeLU, fc2, gate-weighted combine; A1 kept for the backward).  Backward, from the output
-    gradient: tp_moe_shard_bwd (the combine's backward with the gate gradients, the experts' grouped
-    backward, the dispatch's backward) then tp_moe_route_bwd (router logit gradient).
+    gradient: tp_moe_shard_bwd (the experts' grouped backward with the combine's backward folded in:
+    d_out's rows gathered and gate-scaled inside the GEMMs, the gate gradients from the dA1 GEMM's
+    row dots; then the dispatch's backward) then tp_moe_route_bwd (router logit gradient).
     Algorithmic bytes, forward: logits, X, the expert weights, A1 and Y written, Y read, Z written
-    and read back by the combine, out written.  Backward: d_out, X, Z, A1, Y and the weights read,
-    dA1 written and read twice, dX, the weight gradients and the small gate / logit arrays."""
+    and read back by the combine, out written.  Backward: d_out, X, A1, Y and the weights read, dA1
+    written and read twice, dX, the weight gradients and the small gate / logit arrays."""
     from tensor_transformer_layer_mlp_amd.configs import MOE_E128 as mw
     tp, rank, E, k, H, tokens = mw.tp_size, 0, mw.n_experts, mw.top_k, mw.H, mw.tokens
     _, Fr = bd.tp_shard_range(mw.F_expert, tp, rank)
@@ -283,7 +284,7 @@ def moe_layer(bd, torch, steps, warmup):
                             Y, ws)
 
     def bwd():
-        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, W2, A1, Y, Z, d_out,
+        bd.tp_moe_shard_bwd(tp, rank, tokens, H, E, k, mw.F_expert, X, gates, off, rt, tr, W1, W2, A1, Y, None, d_out,
                             dX, dg, dW1, db1, dW2, wsb)
         bd.tp_moe_route_bwd(logits, ex, dg, dlog)
 
@@ -316,7 +317,7 @@ def moe_layer(bd, torch, steps, warmup):
            "hbm_frac": round(byts / ms / 1e6 / PEAK_HBM_GBS, 4), "gbyte_per_call": round(byts / 1e9, 3),
            "kernels": kernels}
     ms_b, kernels_b = timed(bwd)
-    byts_b = 2.0 * (2 * tokens * H + n * H + 2 * n * Fr + 2 * E * H * Fr) + 2.0 * 3 * n * Fr + \
+    byts_b = 2.0 * (2 * tokens * H + 2 * n * Fr + 2 * E * H * Fr) + 2.0 * 3 * n * Fr + \
         2.0 * (tokens * H + 2 * E * H * Fr + E * Fr) + 4.0 * (2 * tokens * k + 2 * tokens * E)
     flop_b = 8.0 * n * H * Fr + 2.0 * n * H
     res["bwd"] = {"ms": round(ms_b, 4), "tflops": round(flop_b / ms_b / 1e9, 2),

@@ -282,17 +282,22 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
  * MoE output (every rank receives it, as the copy / all-reduce pair of the same section gives the
  * dense MLP its dZ), with row (t, j) = token_row[t, j]:
  *   dZ[row] = gates[t, j]·d_out[t]            the combine's backward
- *   dgates_r[t, j] = ⟨d_out[t], Z_r[row]⟩      (fp32; a partial: Σ_r over ranks is the gate
- *                                              gradient, the combine being linear in the partials)
+ *   dgates_r[t, j] = ⟨d_out[t], Y_r[row]·W2_r[e]⟩   (fp32; e the row's expert; Y_r[row]·W2_r[e] is
+ *                                              the row's Z before rounding; a partial: Σ_r over ranks
+ *                                              is the gate gradient, the combine being linear in them)
  *   the experts' backward as tp_mlp_grouped_shard_bwd, on X's rows in dispatch order
  *   dX_r[t] = Σ_j dX_perm[row]                 the dispatch's backward (a partial over ranks)
- * Inputs are the forward's: X, gates, group_offsets, row_token, token_row from tp_moe_route, A1_r,
- * Y_r, Z_r from tp_moe_shard_fwd (A1_r now required).  As in the forward, X's rows are gathered in
- * dispatch order (row_token) inside the dW1 GEMM's operand loads; indices outside X read as zero
- * rows.  token_row must be a permutation of [0, tokens·k), as tp_moe_route writes it; entries
- * outside that range are skipped.  Outputs dW1_r, db1_r, dW2_r as in tp_mlp_grouped_shard_bwd.
- * workspace: tp_workspace_bytes("tp_moe_shard_bwd", ...) with B·S = tokens·top_k, n_heads = E,
- * F = F_expert (the dZ rows, dA1, the plan). */
+ * dZ is never stored: d_out's rows are gathered (row_token) and scaled by their gates inside the
+ * GEMMs that use them, and the gate gradients are taken in the dA1 GEMM's epilogue as per-tile row
+ * dots of its accumulators with Y_r, summed in a fixed order.  Inputs are the forward's: X, gates,
+ * group_offsets, row_token, token_row from tp_moe_route, A1_r and Y_r from tp_moe_shard_fwd (A1_r now
+ * required); Z_r is not read and may be NULL.  As in the forward, X's rows are gathered in dispatch
+ * order (row_token) inside the dW1 GEMM's operand loads; indices outside X read as zero rows.
+ * token_row must be a permutation of [0, tokens·k) and group_offsets cover all tokens·k rows, as
+ * tp_moe_route writes them; token_row entries outside that range are skipped.  Outputs dW1_r, db1_r,
+ * dW2_r as in tp_mlp_grouped_shard_bwd.  workspace: tp_workspace_bytes("tp_moe_shard_bwd", ...) with
+ * B·S = tokens·top_k, n_heads = E, F = F_expert (the plan, dA1, the gates per row, the gate-scaled Y,
+ * the row dots, dX_perm). */
 int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
                      const void* X, const float* gates, const int* group_offsets, const int* row_token,
                      const int* token_row, const void* W1_r, const void* W2_r, const void* A1_r, const void* Y_r,

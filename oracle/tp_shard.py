@@ -521,8 +521,16 @@ def tp_moe_shard_bwd(tp_size, rank, X, route, W1_r, W2_r, fwd, d_out):
     rank receives it, as the copy / all-reduce pair makes it for the dense MLP): the combine's
     backward (dZ rows, the rank's partial gate gradient — Σ over ranks is the full one, since the
     combine is linear in the partials), the experts' grouped backward, and the dispatch's backward
-    dX[t] = Σ_j dX_perm[token_row[t, j]] (the rank's partial input gradient)."""
-    cb = moe_combine_bwd(d_out, fwd["Z"], route["gates"], route["token_row"])
+    dX[t] = Σ_j dX_perm[token_row[t, j]] (the rank's partial input gradient).  The combine's
+    backward takes each row's expert output Z[r] = Y[r]·W2_r[e] as the grouped fc2 defines it, from
+    the saved Y (not a Z the forward may have rounded to storage)."""
+    Y = np.asarray(fwd["Y"], dtype=np.float64)
+    off = route["group_offsets"]
+    Z = np.zeros((Y.shape[0], W2_r.shape[2]))
+    for e in range(W2_r.shape[0]):
+        lo, hi = int(off[e]), int(off[e + 1])
+        Z[lo:hi] = Y[lo:hi] @ W2_r[e]
+    cb = moe_combine_bwd(d_out, Z, route["gates"], route["token_row"])
     Xp = np.asarray(X)[route["row_token"]]
     g = tp_mlp_grouped_shard_bwd(route["group_offsets"], Xp, W1_r, W2_r, fwd["A1"], fwd["Y"], cb["dZ"])
     tr = route["token_row"]

@@ -459,13 +459,13 @@ def tp_moe_shard_bwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, ga
                      token_row, W1_r, W2_r, A1_r, Y_r, Z_r, d_out, dX_r, dgates_r, dW1_r, db1_r, dW2_r, workspace,
                      stream=None):
     """Backward of tp_moe_shard_fwd on this rank (partial dX_r and gate gradients; expert weight
-    gradients of the rank's shards)."""
+    gradients of the rank's shards).  Z_r is not read (None is accepted)."""
     n = tokens * top_k
     _, Fr = tp_shard_range(F_expert, tp_size, rank) if 0 <= rank < tp_size and F_expert >= tp_size >= 1 else (0, 0)
     E = n_experts
     for t, m, name in ((X, tokens * H, "X"), (gates, n, "gates"), (group_offsets, E + 1, "group_offsets"),
                        (row_token, n, "row_token"), (token_row, n, "token_row"), (W1_r, E * H * Fr, "W1_r"),
-                       (W2_r, E * Fr * H, "W2_r"), (A1_r, n * Fr, "A1_r"), (Y_r, n * Fr, "Y_r"), (Z_r, n * H, "Z_r"), (d_out, tokens * H, "d_out"),
+                       (W2_r, E * Fr * H, "W2_r"), (A1_r, n * Fr, "A1_r"), (Y_r, n * Fr, "Y_r"), (d_out, tokens * H, "d_out"),
                        (dX_r, tokens * H, "dX_r"), (dgates_r, n, "dgates_r"), (dW1_r, E * H * Fr, "dW1_r"),
                        (db1_r, E * Fr, "db1_r"), (dW2_r, E * Fr * H, "dW2_r")):
         _need(t, m, name)
@@ -475,7 +475,7 @@ def tp_moe_shard_bwd(tp_size, rank, tokens, H, n_experts, top_k, F_expert, X, ga
         _ptr(gates, "gates", torch.float32), _ptr(group_offsets, "group_offsets", torch.int32),
         _ptr(row_token, "row_token", torch.int32), _ptr(token_row, "token_row", torch.int32),
         _ptr(W1_r, "W1_r", dt), _ptr(W2_r, "W2_r", dt),
-        _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(Z_r, "Z_r", dt), _ptr(d_out, "d_out", dt),
+        _ptr(A1_r, "A1_r", dt), _ptr(Y_r, "Y_r", dt), _ptr(Z_r, "Z_r", dt, True), _ptr(d_out, "d_out", dt),
         _ptr(dX_r, "dX_r", dt), _ptr(dgates_r, "dgates_r", torch.float32), _ptr(dW1_r, "dW1_r", dt),
         _ptr(db1_r, "db1_r", dt), _ptr(dW2_r, "dW2_r", dt), _ptr(workspace, "workspace", None, True),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream))

@@ -761,7 +761,7 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
 
 static size_t moe_bwd_ws(int rows, int H, int Fr, int E, int dtype) {
   const size_t es = dtype == TP_BF16 ? 2 : 4;
-  return align256(grouped_ws_bytes(E)) + align256((size_t)rows * Fr * es) + align256((size_t)rows * H * es);
+  return align256(moe_experts_bwd_ws_bytes(E, rows, H, Fr, dtype)) + align256((size_t)rows * H * es);
 }
 
 int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, int top_k, int F_expert, int dtype,
@@ -781,25 +781,23 @@ int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   NEED(X, "X", (long)tokens * H); NEED4(gates, "gates", n); NEED4(group_offsets, "group_offsets", n_experts + 1);
   NEED4(row_token, "row_token", n); NEED4(token_row, "token_row", n); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1);
   NEED(A1_r, "A1_r", n);
-  NEED(Y_r, "Y_r", n); NEED(Z_r, "Z_r", n * H); NEED(d_out, "d_out", (long)tokens * H);
+  NEED(Y_r, "Y_r", n); MAYBE(Z_r, "Z_r"); NEED(d_out, "d_out", (long)tokens * H);
   NEED(dX_r, "dX_r", (long)tokens * H); NEED4(dgates_r, "dgates_r", n); NEED(dW1_r, "dW1_r", 1);
   NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1);
   const size_t need = moe_bwd_ws(rows, H, g.Fr, n_experts, dtype);
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  const size_t es = dtype == TP_BF16 ? 2 : 4;
-  char* w = (char*)workspace;
-  char* plan = w;
-  char* dA1 = plan + align256(grouped_ws_bytes(n_experts));
-  char* dZp = dA1 + align256((size_t)rows * g.Fr * es);  // later also dX_perm (its reads come first)
+  (void)Z_r;   // the gate gradients come from Y_r and W2_r inside the dA1 GEMM
+  char* experts_ws = (char*)workspace;
+  char* dXp = experts_ws + align256(moe_experts_bwd_ws_bytes(n_experts, rows, H, g.Fr, dtype));
   hipStream_t s = (hipStream_t)stream;
-  TP_TRY(launch_moe_combine_bwd(dtype, tokens, top_k, H, d_out, X, Z_r, gates, token_row, rows, dZp, nullptr,
-                                dgates_r, s), "moe combine backward");
-  // dW1's operand X_perm is gathered from X by row_token inside its loads (no dispatched copy)
-  TP_TRY(launch_mlp_grouped_bwd(dtype, n_experts, group_offsets, rows, H, g.Fr, X, W1_r, W2_r, A1_r, Y_r, dZp, dA1,
-                                dZp, dW1_r, db1_r, dW2_r, plan, s, row_token, tokens), "moe experts backward");
-  TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dZp, nullptr, token_row, rows, dX_r, s), "moe dispatch backward");
+  // the combine's backward is folded into the experts' GEMMs: d_out's rows are gathered by row_token
+  // and scaled by their gates inside them, and X's rows likewise inside dW1's loads
+  TP_TRY(launch_moe_experts_bwd(dtype, n_experts, group_offsets, tokens, top_k, rows, H, g.Fr, X, gates, row_token,
+                                token_row, W1_r, W2_r, A1_r, Y_r, d_out, dXp, dW1_r, db1_r, dW2_r, dgates_r,
+                                experts_ws, s), "moe experts backward");
+  TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dXp, nullptr, token_row, rows, dX_r, s), "moe dispatch backward");
   return TP_OK;
 }
 

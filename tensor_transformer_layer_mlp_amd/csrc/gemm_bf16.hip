@@ -220,12 +220,24 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
     // row r at q ^ (r & 7)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
     // two to four rows instead of 16-row x 32-byte scraps.
     wait_vmcnt<0>();
+    float rowdot[Cfg::FM];   // EPI_DGELU_GATE: this lane's part of Σ_n aux2[m, n]·acc[m, n]
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) rowdot[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j) {
         const int m = m0 + wm + 16 * i + r16, n = n0 + wn + 16 * j + g4;
         f32x4 a = acc[i][j];
+        if constexpr (EPI == EPI_DGELU_GATE) {
+          if (m < d.M && n < d.N) {
+            const bf16x4 x = *(const bf16x4*)((const bf16*)d.aux + (long)m * d.ld_aux + n);
+            const bf16x4 y = *(const bf16x4*)((const bf16*)d.aux2 + (long)m * d.ld_aux2 + n);
+            for (int e = 0; e < 4; ++e) rowdot[i] = fmaf((float)y[e], a[e], rowdot[i]);
+            const float gr = d.row_scale[m];
+            for (int e = 0; e < 4; ++e) a[e] *= gr * act_grad_f((float)x[e], d.act);
+          }
+        }
         if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
           if (n < d.N) {
             const bf16x4 b = *(const bf16x4*)((const bf16*)d.bias + n);
@@ -240,6 +252,34 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
         }
         acc[i][j] = a;
       }
+    if constexpr (EPI == EPI_DGELU_GATE) {
+      // a row's columns in this wave sit in the four lanes r16 + 16q: butterfly over them (every lane
+      // ends with the same sum), then the WN waves along n meet in LDS and are added in wave order
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i) {
+        rowdot[i] += __shfl_xor(rowdot[i], 16);
+        rowdot[i] += __shfl_xor(rowdot[i], 32);
+      }
+      __syncthreads();              // the k loop is done with the LDS
+      TP_LDS float* red = (TP_LDS float*)lds;   // [WN][BM]
+      const int wni = wave % Cfg::WN;
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) red[wni * Cfg::BM + wm + 16 * i + r16] = rowdot[i];
+      }
+      __syncthreads();
+      if (wni == 0 && lane < 16) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+          const int r = wm + 16 * i + r16;
+          if (m0 + r < d.M) {
+            float t = red[r];
+            for (int w = 1; w < Cfg::WN; ++w) t += red[w * Cfg::BM + r];
+            d.row_dot[(long)(n0 / Cfg::BN) * d.rd_stride + m0 + r] = t;
+          }
+        }
+      }
+    }
     constexpr int RB = Cfg::BN * 2, NG = Cfg::BN / 8;   // row bytes, 16-byte granules per row
     auto stage_out = [&](bf16* out, bool gelu) {
       __syncthreads();              // the k loop (or the previous pass) is done with the LDS
@@ -271,6 +311,7 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
       stage_out((bf16*)d.C, false);
     }
   } else {
+    static_assert(EPI != EPI_DGELU_GATE, "the gated epilogue takes the LDS-staged path");
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
       const int m = m0 + wm + 16 * i + r16;
@@ -285,11 +326,12 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
 }
 
 // One BM x BN output tile at (m0, n0): the k loop over LDS stages and the fused epilogue.
-template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false, bool GATHER_K = false>
+template <class Cfg, bool AK, bool BK, int EPI, bool GATHER = false, bool GATHER_K = false, bool GATHER_KB = false>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
                                           int lane, int rot = 0) {
   static_assert(!GATHER || AK, "rows are gathered for a K-major A only");
   static_assert(!GATHER_K || (!AK && !GATHER && Cfg::STAGES == 2), "k rows are gathered for an MN-major A, 2 stages");
+  static_assert(!GATHER_KB || (!BK && Cfg::STAGES == 2), "k rows are gathered for an MN-major B, 2 stages");
   constexpr int LA = AK ? Cfg::BM : Cfg::PM, LB = BK ? Cfg::BN : Cfg::PN;   // rows or pitch
   constexpr int A_BYTES = Cfg::template bytes<AK, Cfg::BM>(), B_BYTES = Cfg::template bytes<BK, Cfg::BN>();
   constexpr int IPW_A = A_BYTES / 1024 / Cfg::NW, IPW_B = B_BYTES / 1024 / Cfg::NW;   // loads per wave
@@ -323,6 +365,20 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
 #pragma unroll
     for (int j = 0; j < IPW_A; ++j) gk[j] = d.a_rows[min(k + ar[j], d.K - 1)];
   };
+  // k-gathered B: as for A, the source rows of the next k-tile, fetched one tile ahead
+  int gkb[IPW_B];
+  unsigned gbytes_b = 0;
+  if constexpr (GATHER_KB) gbytes_b = (unsigned)((long)d.b_rows_n * d.ldb * 2);
+  auto fetch_kb = [&](int k) {
+#pragma unroll
+    for (int j = 0; j < IPW_B; ++j) gkb[j] = d.b_rows[min(k + br[j], d.K - 1)];
+  };
+  auto load_b = [&](int k, TP_LDS char* dst) {
+    if constexpr (GATHER_KB)
+      load_tile_gather_k<IPW_B, Cfg::BN>((const bf16*)d.B, gbytes_b, d.b_rows_n, d.ldb, n0, d.N, k, d.K, dst, gkb,
+                                         br, bc, wave);
+    else load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, k, d.K, dst, br, bc, wave);
+  };
   auto load_a = [&](int k, TP_LDS char* dst) {
     if constexpr (GATHER) load_tile_gather<IPW_A>((const bf16*)d.A, gbytes, k, d.K, dst, ga, ac, wave);
     else if constexpr (GATHER_K)
@@ -349,14 +405,20 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
   if constexpr (GATHER_K) {
     if (nk > 0) fetch_k(kpos(0));
   }
+  if constexpr (GATHER_KB) {
+    if (nk > 0) fetch_kb(kpos(0));
+  }
 #pragma unroll
   for (int t = 0; t < Cfg::STAGES - 1; ++t)
     if (t < nk) {
       load_a(kpos(t), lds + t * Cfg::STAGE);
-      load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, kpos(t), d.K, lds + t * Cfg::STAGE + A_BYTES, br, bc, wave);
+      load_b(kpos(t), lds + t * Cfg::STAGE + A_BYTES);
     }
   if constexpr (GATHER_K) {
     if (nk > 1) fetch_k(kpos(1));
+  }
+  if constexpr (GATHER_KB) {
+    if (nk > 1) fetch_kb(kpos(1));
   }
   int cur_stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
@@ -385,9 +447,12 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int m0, int n0, TP_
       TP_LDS char* nxt = lds + ns * Cfg::STAGE;
       const int k1 = kpos(kt + Cfg::STAGES - 1);
       load_a(k1, nxt);
-      load_tile<BK, LB, Cfg::BN, IPW_B, Cfg::BKT>(B, n0, k1, d.K, nxt + A_BYTES, br, bc, wave);
+      load_b(k1, nxt + A_BYTES);
       if constexpr (GATHER_K) {
         if (kt + 2 < nk) fetch_k(kpos(kt + 2));
+      }
+      if constexpr (GATHER_KB) {
+        if (kt + 2 < nk) fetch_kb(kpos(kt + 2));
       }
     }
 #pragma unroll
@@ -647,6 +712,11 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   if (g.d.C2) d.C2 = (bf16*)g.d.C2 + (long)row0 * g.d.ldc;
   if (g.d.bias) d.bias = (const bf16*)g.d.bias + (long)e * g.bias_stride;
   if (g.d.aux) d.aux = (const bf16*)g.d.aux + (long)row0 * g.d.ld_aux;
+  if constexpr (EPI == EPI_DGELU_GATE) {
+    d.aux2 = (const bf16*)g.d.aux2 + (long)row0 * g.d.ld_aux2;
+    d.row_scale = g.d.row_scale + row0;
+    d.row_dot = g.d.row_dot + row0;
+  }
   // k loops start at k-tile mt (mod the count): the row tiles of the same expert stream their rows
   // of A through different memory channels at the same moment (measured: fc1 2x faster)
   gemm_tile<Cfg, true, BKM, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
@@ -666,7 +736,7 @@ struct GroupedKArgs {
   long c_stride;
 };
 
-template <class Cfg, bool GK>
+template <class Cfg, bool GK, bool GKB>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -683,10 +753,11 @@ void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
   d.K = g.off[e + 1] - k0;
   if constexpr (GK) d.a_rows = g.d.a_rows + k0;   // A stays the whole gathered-from matrix
   else d.A = (const bf16*)g.d.A + (long)k0 * g.d.lda;
-  d.B = (const bf16*)g.d.B + (long)k0 * g.d.ldb;
+  if constexpr (GKB) d.b_rows = g.d.b_rows + k0;  // B likewise
+  else d.B = (const bf16*)g.d.B + (long)k0 * g.d.ldb;
   d.C = (bf16*)g.d.C + (long)e * g.c_stride;
-  gemm_tile<Cfg, false, false, EPI_STORE, false, GK>(d, tm * Cfg::BM, tn * Cfg::BN, (TP_LDS char*)smem, wave, lane,
-                                                      tm + tn);
+  gemm_tile<Cfg, false, false, EPI_STORE, false, GK, GKB>(d, tm * Cfg::BM, tn * Cfg::BN, (TP_LDS char*)smem, wave,
+                                                           lane, tm + tn);
 }
 
 template <class Cfg, bool AK, bool BK, int EPI>
@@ -768,12 +839,14 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
   if (d.lda > (1L << 22) || d.ldb > (1L << 22)) return false;
   if ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) return false;
   if (d.epi == EPI_BIAS_GELU && d.C2 && (((uintptr_t)d.C2) & 15)) return false;
-  if (d.epi == EPI_DGELU && ((d.ld_aux & 7) || (((uintptr_t)d.aux) & 15))) return false;
+  if ((d.epi == EPI_DGELU || d.epi == EPI_DGELU_GATE) && ((d.ld_aux & 7) || (((uintptr_t)d.aux) & 15))) return false;
+  if (d.epi == EPI_DGELU_GATE && ((d.ld_aux2 & 7) || (((uintptr_t)d.aux2) & 15) || !d.row_scale || !d.row_dot))
+    return false;
   if (d.epi == EPI_F32)   // split-k partials: both operands K-major (the ping-pong tile) or both MN-major
     return d.a_kmajor == d.b_kmajor && ((d.ldc & 3) == 0) &&   // (the 256 x 256 tile), whole k-tiles per slice
            (d.ksplit <= 1 || (d.k_per > 0 && d.k_per % 64 == 0 && (long)d.k_per * d.ksplit >= d.K));
   const bool supported = (d.a_kmajor && !d.b_kmajor && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_GELU || d.epi == EPI_STORE)) ||
-                         (d.a_kmajor && d.b_kmajor && (d.epi == EPI_DGELU || d.epi == EPI_STORE)) ||
+                         (d.a_kmajor && d.b_kmajor && (d.epi == EPI_DGELU || d.epi == EPI_STORE || d.epi == EPI_DGELU_GATE)) ||
                          (!d.a_kmajor && !d.b_kmajor && d.epi == EPI_STORE);
   return supported;
 }
@@ -839,14 +912,21 @@ int gemm_bf16_grouped_bm(int) {
   return C0::BM;
 }
 
+// The n-tile width launch_gemm_bf16_grouped takes for this GEMM (as its tile choice below).
+int gemm_bf16_grouped_bn(const GemmDesc& d) { return (!d.b_kmajor && d.K >= 2048) ? C5::BN : C0::BN; }
+
 template <class Cfg>
 static hipError_t grouped_t(const GroupedArgs& g, int max_mtiles, hipStream_t s) {
   const long tiles = (long)max_mtiles * ((g.d.N + Cfg::BN - 1) / Cfg::BN);
   if (tiles > 0x7ffffff0L) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
   if (!g.d.a_kmajor) return hipErrorNotSupported;
-  if (g.d.b_kmajor) {            // the backward's dY·Wᵀ forms: GeLU' or plain
-    if (g.d.a_rows) return hipErrorNotSupported;
+  if (g.d.b_kmajor) {            // the backward's dY·Wᵀ forms: GeLU' or plain; gathered rows with the gate
+    if (g.d.a_rows) {
+      if (g.d.epi != EPI_DGELU_GATE || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
+      gemm_bf16_grouped_kernel<Cfg, EPI_DGELU_GATE, true, true><<<grid, Cfg::NT, 0, s>>>(g);
+      return hipGetLastError();
+    }
     if (g.d.epi == EPI_DGELU) gemm_bf16_grouped_kernel<Cfg, EPI_DGELU, false, true><<<grid, Cfg::NT, 0, s>>>(g);
     else if (g.d.epi == EPI_STORE) gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, true><<<grid, Cfg::NT, 0, s>>>(g);
     else return hipErrorNotSupported;
@@ -881,25 +961,29 @@ bool gemm_bf16_grouped_k_eligible(const GemmDesc& d) {
   if ((d.lda | d.ldb | d.ldc) & 7) return false;
   if (d.lda > (1L << 22) || d.ldb > (1L << 22)) return false;
   if (d.a_rows && (long)d.a_rows_n * d.lda * 2 > 0x7fffffffL) return false;   // one buffer range over A
+  if (d.b_rows && (long)d.b_rows_n * d.ldb * 2 > 0x7fffffffL) return false;   // and over B
   return ((((uintptr_t)d.A) | ((uintptr_t)d.B) | ((uintptr_t)d.C)) & 15) == 0;
 }
 
-template <class Cfg, bool GK>
+template <class Cfg, bool GK, bool GKB>
 static hipError_t grouped_k_t(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
   const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (d.N + Cfg::BN - 1) / Cfg::BN;
   const long nwg = (long)tiles_m * tiles_n * groups;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   GroupedKArgs g{d, off, groups, c_stride};
-  gemm_bf16_grouped_k_kernel<Cfg, GK><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
+  gemm_bf16_grouped_k_kernel<Cfg, GK, GKB><<<(unsigned)nwg, Cfg::NT, 0, s>>>(g, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {
   // measured on the 128-expert weight gradients: the gathered form is 14% faster with k = 32 (C0
   // spills there), the plain form 21% slower
-  if (d.a_rows) return grouped_k_t<C9, true>(d, off, groups, c_stride, s);
-  return grouped_k_t<C0, false>(d, off, groups, c_stride, s);
+  // (a gathered B, the MoE backward's dW2 over the output gradient's rows, takes the same tile)
+  if (d.a_rows && d.b_rows) return hipErrorNotSupported;
+  if (d.a_rows) return grouped_k_t<C9, true, false>(d, off, groups, c_stride, s);
+  if (d.b_rows) return grouped_k_t<C9, false, true>(d, off, groups, c_stride, s);
+  return grouped_k_t<C0, false, false>(d, off, groups, c_stride, s);
 }
 
 }  // namespace tp

@@ -70,7 +70,14 @@ __device__ __forceinline__ void generic_tile(const GemmDesc& d, int m0, int n0) 
       if (d.b_kmajor) { n = i / BK; k = i % BK; } else { k = i / GBN; n = i % GBN; }
       const int gn = n0 + n, gk = k0 + k;
       T v = from_f32<T>(0.f);
-      if (gn < d.N && gk < d.K) v = d.b_kmajor ? B[(long)gn * d.ldb + gk] : B[(long)gk * d.ldb + gn];
+      if (gn < d.N && gk < d.K) {
+        if (d.b_rows) {          // gathered rows of the source matrix; outside [0, b_rows_n) reads zero
+          const int src = d.b_rows[d.b_kmajor ? gn : gk];
+          if (src >= 0 && src < d.b_rows_n) v = d.b_kmajor ? B[(long)src * d.ldb + gk] : B[(long)src * d.ldb + gn];
+        } else {
+          v = d.b_kmajor ? B[(long)gn * d.ldb + gk] : B[(long)gk * d.ldb + gn];
+        }
+      }
       Bs[n][k] = v;
     }
     __syncthreads();
@@ -91,6 +98,37 @@ __device__ __forceinline__ void generic_tile(const GemmDesc& d, int m0, int n0) 
       }
     }
     __syncthreads();
+  }
+  if constexpr (EPI == EPI_DGELU_GATE) {
+    // C = row_scale[m]·acc∘GeLU'(aux), and per row Σ_n aux2[m, n]·acc over this n-tile: lane-local in
+    // (j, e) order, then over the four lanes of a row, then the two waves along n in LDS, in order
+    __shared__ float red[2][GBM];
+    float rowdot[2] = {0.f, 0.f};
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm + i * 16 + r16;
+          const int n = n0 + wn + j * 16 + 4 * g + e;
+          if (m < d.M && n < d.N) {
+            const float v = acc[i][j][e];
+            rowdot[i] = fmaf(to_f32(((const T*)d.aux2)[(long)m * d.ld_aux2 + n]), v, rowdot[i]);
+            const float x = to_f32(((const T*)d.aux)[(long)m * d.ld_aux + n]);
+            ((T*)d.C)[(long)m * d.ldc + n] = from_f32<T>(v * (d.row_scale[m] * act_grad_f(x, d.act)));
+          }
+        }
+    for (int i = 0; i < 2; ++i) {
+      rowdot[i] += __shfl_xor(rowdot[i], 16);
+      rowdot[i] += __shfl_xor(rowdot[i], 32);
+    }
+    if (lane < 16)
+      for (int i = 0; i < 2; ++i) red[wave & 1][wm + i * 16 + r16] = rowdot[i];
+    __syncthreads();
+    if ((wave & 1) == 0 && lane < 16)
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm + i * 16 + r16;
+        if (m0 + r < d.M) d.row_dot[(long)(n0 / GBN) * d.rd_stride + m0 + r] = red[0][r] + red[1][r];
+      }
+    return;
   }
   for (int i = 0; i < 2; ++i)
     for (int j = 0; j < 2; ++j)
@@ -130,6 +168,11 @@ __global__ __launch_bounds__(256) void gemm_generic_grouped_kernel(GemmDesc g, c
   if (g.C2) d.C2 = (T*)g.C2 + (long)row0 * g.ldc;
   if (g.bias) d.bias = (const T*)g.bias + (long)e * bias_stride;
   if (g.aux) d.aux = (const T*)g.aux + (long)row0 * g.ld_aux;
+  if constexpr (EPI == EPI_DGELU_GATE) {
+    d.aux2 = (const T*)g.aux2 + (long)row0 * g.ld_aux2;
+    d.row_scale = g.row_scale + row0;
+    d.row_dot = g.row_dot + row0;
+  }
   generic_tile<T, EPI>(d, 0, blockIdx.x * GBN);
 }
 
@@ -143,7 +186,8 @@ __global__ __launch_bounds__(256) void gemm_generic_grouped_k_kernel(GemmDesc g,
   d.K = off[e + 1] - k0;
   if (g.a_rows) d.a_rows = g.a_rows + k0;   // A stays the whole gathered-from matrix
   else d.A = (const T*)g.A + (long)k0 * g.lda;
-  d.B = (const T*)g.B + (long)k0 * g.ldb;
+  if (g.b_rows) d.b_rows = g.b_rows + k0;   // B likewise
+  else d.B = (const T*)g.B + (long)k0 * g.ldb;
   d.C = (T*)g.C + (long)e * c_stride;
   generic_tile<T, EPI_STORE>(d, blockIdx.y * GBM, blockIdx.x * GBN);
 }
@@ -171,6 +215,9 @@ hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int
     gemm_generic_grouped_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
   else if (d.epi == EPI_DGELU)
     gemm_generic_grouped_kernel<T, EPI_DGELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+  else if (d.epi == EPI_DGELU_GATE)
+    gemm_generic_grouped_kernel<T, EPI_DGELU_GATE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride,
+                                                                        bias_stride);
   else
     return hipErrorNotSupported;
   return hipGetLastError();
@@ -179,6 +226,7 @@ hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int
 }  // namespace
 
 int gemm_generic_grouped_bm() { return GBM; }
+int gemm_generic_grouped_bn() { return GBN; }
 
 hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
                                        long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {

@@ -21,7 +21,9 @@ hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int
 hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
                                        long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
 int gemm_bf16_grouped_bm(int K);
+int gemm_bf16_grouped_bn(const GemmDesc& d);
 int gemm_generic_grouped_bm();
+int gemm_generic_grouped_bn();
 bool gemm_bf16_eligible(const GemmDesc& d);
 bool gemm_bf16_grouped_k_eligible(const GemmDesc& d);
 hipError_t launch_gemm_bf16_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s);
@@ -262,6 +264,136 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
     ProfScope p(t1 ? (x_rows ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_bf16_grouped_k<Xt.dA1>")
                    : (x_rows ? "gemm_generic_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1>"), s, fl,
                 es * ((double)(x_rows ? x_rows_n : rows) * H + (double)rows * Fr) + wts);   // X's unique rows
+    e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
+           : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);
+    if (e != hipSuccess) return e;
+  }
+  if (rows > 0) {
+    ProfScope p(tiled ? "gemm_bf16_grouped<dA1.W1t>" : "gemm_generic_grouped<dA1.W1t>", s, fl,
+                es * ((double)rows * Fr + (double)rows * H) + wts);
+    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s)
+              : launch_gemm_generic_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The MoE experts' backward straight from the output gradient d_out [tokens, H] (no dZ [rows, H] in
+// memory).  Row r of the expert-sorted matrix is (t, j) = (row_token[r], the choice with
+// token_row[t, j] = r) with gate g_r, and dZ[r] = g_r·d_out[t]; since dZ is that row scaled, each of
+// its uses takes d_out's row through the row gather and the scale where it is cheapest:
+//   gate_row[r] = g_r,  Yg[r] = g_r·Y[r]                              (moe_row_gates)
+//   dA1 = g_r·(d_out[t]·W2[e]ᵀ) ∘ GeLU'(A1)  and, from the same accumulators before the scale,
+//   row_dot[nt, r] = Σ_{f in n-tile nt} Y[r, f]·(d_out[t]·W2[e]ᵀ)[f]   (the gated epilogue)
+//   dgates[t, j] = Σ_nt row_dot[nt, r] = ⟨d_out[t], Y[r]·W2[e]⟩        (moe_dgates, fixed order)
+//   dW2[e] = Σ_{r of e} Yg[r]ᵀ·d_out[t]                               (grouped over k, B's k rows gathered)
+//   db1[e] = Σ_{r of e} dA1[r];  dW1[e] = Σ_{r of e} X[t]ᵀ·dA1[r];  dX_perm = dA1·W1[e]ᵀ
+// The gate gradient is ⟨d_out[t], Z[r]⟩ with Z[r] = Y[r]·W2[e] not rounded to storage first.  Every
+// sum has a fixed order (repeatable bit for bit).  ws: moe_experts_bwd_ws_bytes; dX_perm [rows, H].
+size_t moe_experts_bwd_ws_bytes(int groups, int rows, int H, int Fr, int dtype) {
+  (void)H;
+  const size_t es = dtype == DT_BF16 ? 2 : 4;
+  auto a256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t nt = (size_t)(Fr + 63) / 64;   // n-tiles of the narrowest tile (the generic kernel's)
+  return a256(grouped_ws_bytes(groups)) + a256((size_t)rows * Fr * es) + a256((size_t)rows * 4) +
+         a256((size_t)rows * Fr * es) + a256(nt * rows * 4);
+}
+
+hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tokens, int k, int rows, int H, int Fr,
+                                  const void* X, const float* gates, const int* row_token, const int* token_row,
+                                  const void* W1, const void* W2, const void* A1, const void* Y, const void* d_out,
+                                  void* dX_perm, void* dW1, void* db1, void* dW2, float* dgates, void* ws,
+                                  hipStream_t s) {
+  if (groups <= 0) return hipSuccess;
+  if (groups > 65535) return hipErrorInvalidValue;   // the column sum's grid y (checked before any launch)
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  auto a256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  char* w = (char*)ws;
+  int* off_s = (int*)w;
+  int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
+  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of the dX GEMM's
+  w += a256(grouped_ws_bytes(groups));
+  void* dA1 = w;
+  w += a256((size_t)rows * Fr * (size_t)es);
+  float* gate_row = (float*)w;
+  w += a256((size_t)rows * 4);
+  void* Yg = w;
+  w += a256((size_t)rows * Fr * (size_t)es);
+  float* row_dot = (float*)w;
+
+  GemmDesc ga;                                // dA1 = gate·(d_out[t]·W2ᵀ) ∘ GeLU'(A1), row dots with Y
+  memset(&ga, 0, sizeof(ga));
+  ga.M = rows; ga.N = Fr; ga.K = H; ga.dtype = dtype;
+  ga.A = d_out; ga.lda = H; ga.a_kmajor = true; ga.a_rows = row_token; ga.a_rows_n = tokens;
+  ga.B = W2; ga.ldb = H; ga.b_kmajor = true;
+  ga.C = dA1; ga.ldc = Fr; ga.epi = EPI_DGELU_GATE; ga.aux = A1; ga.ld_aux = Fr;
+  ga.aux2 = Y; ga.ld_aux2 = Fr; ga.row_scale = gate_row; ga.row_dot = row_dot; ga.rd_stride = rows;
+  GemmDesc gx;                                // dX_perm = dA1·W1ᵀ
+  memset(&gx, 0, sizeof(gx));
+  gx.M = rows; gx.N = H; gx.K = Fr; gx.dtype = dtype; gx.epi = EPI_STORE;
+  gx.A = dA1; gx.lda = Fr; gx.a_kmajor = true;
+  gx.B = W1; gx.ldb = Fr; gx.b_kmajor = true;
+  gx.C = dX_perm; gx.ldc = H;
+  GemmDesc gw2;                               // dW2[e] = Yg_eᵀ·d_out[tokens of e]   [Fr, H]
+  memset(&gw2, 0, sizeof(gw2));
+  gw2.M = Fr; gw2.N = H; gw2.dtype = dtype; gw2.epi = EPI_STORE;
+  gw2.A = Yg; gw2.lda = Fr; gw2.a_kmajor = false;
+  gw2.B = d_out; gw2.ldb = H; gw2.b_kmajor = false; gw2.b_rows = row_token; gw2.b_rows_n = tokens;
+  gw2.C = dW2; gw2.ldc = H;
+  GemmDesc gw1 = gw2;                         // dW1[e] = X[tokens of e]ᵀ·dA1_e  [H, Fr]
+  gw1.M = H; gw1.N = Fr; gw1.A = X; gw1.lda = H; gw1.a_rows = row_token; gw1.a_rows_n = tokens;
+  gw1.B = dA1; gw1.ldb = Fr; gw1.b_rows = nullptr; gw1.b_rows_n = 0; gw1.C = dW1; gw1.ldc = Fr;
+
+  // one 32-bit buffer range covers the gathered d_out in the tiled kernels
+  const bool tiled = rows > 0 && gemm_bf16_eligible(ga) && gemm_bf16_eligible(gx) &&
+                     (long)tokens * H * 2 <= 0x7fffffffL;
+  const int bm1 = tiled ? gemm_bf16_grouped_bm(ga.K) : gemm_generic_grouped_bm();
+  const int bm2 = tiled ? gemm_bf16_grouped_bm(gx.K) : gemm_generic_grouped_bm();
+  const int bn1 = tiled ? gemm_bf16_grouped_bn(ga) : gemm_generic_grouped_bn();
+  const int ntiles = (Fr + bn1 - 1) / bn1;    // <= (Fr + 63) / 64: row_dot's room
+  const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
+  if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
+  hipError_t e;
+  {
+    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
+    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  e = launch_moe_row_gates(dtype, tokens, k, rows, Fr, gates, row_token, token_row, Y, gate_row, Yg, s);
+  if (e != hipSuccess) return e;
+  const double fl = 2.0 * rows * (double)Fr * H;
+  const double wts = es * (double)groups * H * Fr;
+  if (rows > 0) {
+    // d_out's unique rows, A1 and Y read, dA1 written, the row dots
+    ProfScope p(tiled ? "gemm_bf16_grouped<dout.W2t, gather, gate+dgelu>" : "gemm_generic_grouped<dout.W2t, gather, gate+dgelu>",
+                s, fl, es * ((double)tokens * H + 3.0 * rows * Fr) + wts + 4.0 * rows * (ntiles + 2));
+    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s)
+              : launch_gemm_generic_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_moe_dgates(tokens, k, rows, ntiles, row_dot, token_row, off_s, groups, dgates, s);
+  if (e != hipSuccess) return e;
+  {
+    const bool t2 = gemm_bf16_grouped_k_eligible(gw2);
+    ProfScope p(t2 ? "gemm_bf16_grouped_k<Ygt.dout, gather>" : "gemm_generic_grouped_k<Ygt.dout, gather>", s, fl,
+                es * ((double)rows * Fr + (double)tokens * H) + wts + 4.0 * rows);
+    e = t2 ? launch_gemm_bf16_grouped_k(gw2, off_s, groups, (long)Fr * H, s)
+           : launch_gemm_generic_grouped_k(gw2, off_s, groups, (long)Fr * H, s);
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
+    dim3 grid((Fr + 63) / 64, groups);
+    if (dtype == DT_BF16) grouped_colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
+    else grouped_colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dA1, Fr, off_s, (float*)db1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const bool t1 = gemm_bf16_grouped_k_eligible(gw1);
+    ProfScope p(t1 ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1, gather>", s, fl,
+                es * ((double)tokens * H + (double)rows * Fr) + wts + 4.0 * rows);
     e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
            : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);
     if (e != hipSuccess) return e;

@@ -14,7 +14,9 @@ enum Epi {
   EPI_BIAS = 1,       // C = acc + bias[n]
   EPI_BIAS_GELU = 2,  // C2 = acc + bias[n] (if C2), C = GeLU(acc + bias[n])   (GeLU per `act`)
   EPI_DGELU = 3,      // C = acc * GeLU'(aux[m, n])
-  EPI_F32 = 4         // C (fp32) = acc: one k-slice's partial of a split-k GEMM
+  EPI_F32 = 4,        // C (fp32) = acc: one k-slice's partial of a split-k GEMM
+  EPI_DGELU_GATE = 5  // C = row_scale[m] · acc ∘ GeLU'(aux[m, n]), and row_dot[nt·rd_stride + m] =
+                      // Σ_{n in n-tile nt} aux2[m, n] · acc (the MoE backward: gate and its gradient)
 };
 
 // C[M, N] = op(A)·op(B) with the epilogue applied.  Element (m, k) of A sits at A[m*lda + k] when
@@ -39,6 +41,15 @@ struct GemmDesc {
   // writing its fp32 partial at C + s·c_split; 0 or 1 = no split
   int ksplit, k_per;
   long c_split;
+  // EPI_DGELU_GATE: per-row scale (fp32 [M]), the second auxiliary matrix (storage type, leading
+  // dimension ld_aux2) and the per-(n-tile, row) dots (fp32, n-tile nt at nt·rd_stride)
+  const float* row_scale;
+  const void* aux2; long ld_aux2;
+  float* row_dot; long rd_stride;
+  // Row gather of an MN-major B's k rows (grouped weight gradients only): k row k of B is row
+  // b_rows[k] of the b_rows_n-row matrix at B; indices outside [0, b_rows_n) read as zero rows.
+  const int* b_rows;
+  int b_rows_n;
 };
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
@@ -119,6 +130,21 @@ hipError_t launch_moe_combine(int dtype, int tokens, int top_k, int H, const voi
 hipError_t launch_moe_combine_bwd(int dtype, int tokens, int k, int H, const void* d_out, const void* X,
                                   const void* Z, const float* gates, const int* token_row, int rows, void* dZ,
                                   void* Xp, float* dgates, hipStream_t s);
+// Row r's gate (the gate of the choice whose row r is; 0 if none) and Yg[r] = gate·Y[r].
+hipError_t launch_moe_row_gates(int dtype, int tokens, int k, int rows, int Fr, const float* gates,
+                                const int* row_token, const int* token_row, const void* Y, float* gate_row, void* Yg,
+                                hipStream_t s);
+// dgates[t, j] = Σ_{nt < ntiles} row_dot[nt·rows + token_row[t, j]] in that order (0 for a row outside
+// [off[0], off[groups]), off the sanitised offsets in device memory).
+hipError_t launch_moe_dgates(int tokens, int k, int rows, int ntiles, const float* row_dot, const int* token_row,
+                             const int* off, int groups, float* dgates, hipStream_t s);
+// The MoE experts' backward from the output gradient (no materialised dZ): see grouped.hip.
+size_t moe_experts_bwd_ws_bytes(int groups, int rows, int H, int Fr, int dtype);
+hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tokens, int k, int rows, int H, int Fr,
+                                  const void* X, const float* gates, const int* row_token, const int* token_row,
+                                  const void* W1, const void* W2, const void* A1, const void* Y, const void* d_out,
+                                  void* dX_perm, void* dW1, void* db1, void* dW2, float* dgates, void* ws,
+                                  hipStream_t s);
 hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, const int* experts,
                                 const float* dgates, float* d_logits, hipStream_t s);
 

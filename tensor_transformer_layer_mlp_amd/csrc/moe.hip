@@ -334,6 +334,55 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(int k, int H, cons
 
 constexpr int RBWD_TOKENS = 16;   // tokens (waves) per workgroup of the router backward
 
+// The MoE backward without a materialised dZ (see launch_moe_experts_bwd).  Row r's gate: the gate of
+// the (t, j) whose row it is (t = row_token[r], j the choice with token_row[t, j] = r; 0 when r has no
+// such choice), and the gate-scaled copy Yg[r] = gate·Y[r] that dW2 = Ygᵀ·d_out takes.  One thread per
+// 8 elements of a row (V = 8) or per element.
+template <typename T, int V>
+__global__ __launch_bounds__(256) void moe_row_gates_kernel(int tokens, int k, int rows, int Fr, const float* __restrict__ gates,
+                                                            const int* __restrict__ row_token,
+                                                            const int* __restrict__ token_row, const T* __restrict__ Y,
+                                                            float* __restrict__ gate_row, T* __restrict__ Yg) {
+  const int per = (Fr + V - 1) / V;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)rows * per) return;
+  const int r = (int)(i / per), c = (int)(i % per) * V;
+  const int t = row_token[r];
+  float gt = 0.f;
+  if (t >= 0 && t < tokens)
+    for (int j = 0; j < k; ++j)
+      if (token_row[(long)t * k + j] == r) {
+        gt = gates[(long)t * k + j];
+        break;
+      }
+  if (c == 0) gate_row[r] = gt;
+  const T* y = Y + (long)r * Fr + c;
+  T* o = Yg + (long)r * Fr + c;
+  if constexpr (V == 8) {
+    const bf16x8 v = *(const bf16x8*)y;
+    bf16x8 w;
+    for (int e = 0; e < 8; ++e) w[e] = (bf16)(gt * (float)v[e]);
+    *(bf16x8*)o = w;
+  } else {
+    for (int e = 0; e < V && c + e < Fr; ++e) o[e] = from_f32<T>(gt * to_f32(y[e]));
+  }
+}
+
+// dgates[t, j] = Σ_{nt < ntiles} row_dot[nt·rows + r] in that order, r = token_row[t, j]: the gate
+// gradients ⟨d_out[t], Y[r]·W2[e]⟩ from the dA1 GEMM's per-n-tile row dots.  Only rows inside the
+// experts' (sanitised, non-decreasing) offsets [off[0], off[groups]) have row dots; others give 0.
+__global__ __launch_bounds__(256) void moe_dgates_kernel(long n, int rows, int ntiles, const float* __restrict__ row_dot,
+                                                         const int* __restrict__ token_row, const int* __restrict__ off,
+                                                         int groups, float* __restrict__ dgates) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = token_row[i];
+  float v = 0.f;
+  if (r >= 0 && r < rows && r >= off[0] && r < off[groups])
+    for (int nt = 0; nt < ntiles; ++nt) v += row_dot[(long)nt * rows + r];
+  dgates[i] = v;
+}
+
 template <int EPL>
 __global__ __launch_bounds__(64 * RBWD_TOKENS) void moe_route_bwd_kernel(int tokens, int E, int k,
                                                                          const float* __restrict__ logits,
@@ -497,6 +546,38 @@ hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, c
   if (E <= 256) return route_bwd_t<4>(tokens, E, k, logits, experts, dgates, d_logits, s);
   if (E <= 512) return route_bwd_t<8>(tokens, E, k, logits, experts, dgates, d_logits, s);
   return route_bwd_t<16>(tokens, E, k, logits, experts, dgates, d_logits, s);
+}
+
+hipError_t launch_moe_row_gates(int dtype, int tokens, int k, int rows, int Fr, const float* gates,
+                                const int* row_token, const int* token_row, const void* Y, float* gate_row, void* Yg,
+                                hipStream_t s) {
+  if (rows <= 0 || Fr <= 0) return hipSuccess;
+  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  ProfScope p("moe_row_gates", s, (double)rows * Fr, 2.0 * es * rows * Fr + 8.0 * rows + 4.0 * rows * k);
+  if (dtype == DT_BF16 && Fr % 8 == 0 && ((((uintptr_t)Y) | ((uintptr_t)Yg)) & 15) == 0) {
+    const long n = (long)rows * (Fr / 8);
+    moe_row_gates_kernel<bf16, 8><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        tokens, k, rows, Fr, gates, row_token, token_row, (const bf16*)Y, gate_row, (bf16*)Yg);
+  } else if (dtype == DT_BF16) {
+    const long n = (long)rows * Fr;
+    moe_row_gates_kernel<bf16, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        tokens, k, rows, Fr, gates, row_token, token_row, (const bf16*)Y, gate_row, (bf16*)Yg);
+  } else {
+    const long n = (long)rows * Fr;
+    moe_row_gates_kernel<float, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        tokens, k, rows, Fr, gates, row_token, token_row, (const float*)Y, gate_row, (float*)Yg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_dgates(int tokens, int k, int rows, int ntiles, const float* row_dot, const int* token_row,
+                             const int* off, int groups, float* dgates, hipStream_t s) {
+  const long n = (long)tokens * k;
+  if (n <= 0) return hipSuccess;
+  ProfScope p("moe_dgates", s, (double)n * ntiles, 4.0 * n * (ntiles + 2));
+  moe_dgates_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, rows, ntiles, row_dot, token_row, off, groups,
+                                                                dgates);
+  return hipGetLastError();
 }
 
 }  // namespace tp
