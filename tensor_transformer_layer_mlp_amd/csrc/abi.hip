@@ -677,7 +677,7 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
   TP_CHECK(((uintptr_t)group_offsets & 3u) == 0, TP_EALIGN, "group_offsets is not 4-byte aligned");
   NEED(X_perm, "X_perm", (long)rows); NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1);
   NEED(Z_r, "Z_r", (long)rows); NEED(Y_r, "Y_r", (long)rows); MAYBE(A1_r, "A1_r");
-  const size_t need = align256(grouped_ws_bytes(n_groups));
+  const size_t need = align256(grouped_ws_bytes(n_groups, rows));
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
@@ -725,7 +725,7 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   NEED4(row_token, "row_token", n); NEED4(token_row, "token_row", n);
   NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1); NEED(out_r, "out_r", (long)tokens * H);
   NEED(Z_r, "Z_r", n * H); NEED(Y_r, "Y_r", n); MAYBE(A1_r, "A1_r");
-  const size_t need = align256(grouped_ws_bytes(n_experts));
+  const size_t need = align256(grouped_ws_bytes(n_experts, rows));
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
@@ -748,7 +748,7 @@ int tp_mlp_grouped_shard_bwd(int tp_size, int rank, int n_groups, const int* gro
   NEED(X_perm, "X_perm", (long)rows); NEED(W1_r, "W1_r", 1); NEED(W2_r, "W2_r", 1); NEED(A1_r, "A1_r", (long)rows);
   NEED(Y_r, "Y_r", (long)rows); NEED(dZ_perm, "dZ_perm", (long)rows); NEED(dX_perm, "dX_perm", (long)rows);
   NEED(dW1_r, "dW1_r", 1); NEED(db1_r, "db1_r", 1); NEED(dW2_r, "dW2_r", 1);
-  const size_t plan = align256(grouped_ws_bytes(n_groups));
+  const size_t plan = align256(grouped_ws_bytes(n_groups, rows));
   const size_t need = plan + align256((size_t)rows * g.Fr * (dtype == TP_BF16 ? 2 : 4));
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -896,11 +896,11 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
     if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > 65535) return 0;
     if (mlp_geom(tp_size, rank, B * S, H, F, dtype, &mg)) return 0;
     if (strcmp(fn, "tp_moe_shard_bwd") == 0) return moe_bwd_ws(B * S, H, mg.Fr, n_heads, dtype);
-    return align256(grouped_ws_bytes(n_heads)) + align256((size_t)B * S * mg.Fr * (dtype == TP_BF16 ? 2 : 4));
+    return align256(grouped_ws_bytes(n_heads, B * S)) + align256((size_t)B * S * mg.Fr * (dtype == TP_BF16 ? 2 : 4));
   }
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0 || strcmp(fn, "tp_moe_shard_fwd") == 0) {
-    if (n_heads < 1 || n_heads > (1 << 20)) return 0;
-    return align256(grouped_ws_bytes(n_heads));
+    if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > (1 << 20)) return 0;
+    return align256(grouped_ws_bytes(n_heads, B * S));
   }
   if (strcmp(fn, "tp_residual_ln_bwd") == 0) {
     int rows = 0;

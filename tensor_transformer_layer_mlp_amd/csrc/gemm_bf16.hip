@@ -531,14 +531,21 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
 // Each group waits for its own loads at the end of its following compute phase, so every load has two
 // phases to land, and a stage is only overwritten after both groups' reads of it have completed (the
 // memory phase ends with lgkmcnt(0) before its barrier).
-struct PPTile {
-  static constexpr int BM = 256, BN = 192, BKT = 64, NKK = 2, NT = 512, STAGES = 2;
+// The tile width BN is 192 (the dense GEMMs) or 256 (the grouped expert GEMMs, whose n extent is one
+// 256-wide shard): wave tiles of 64 x 96 or 64 x 128.
+template <int BN_>
+struct PPCfg {
+  static constexpr int BM = 256, BN = BN_, BKT = 64, NKK = 2, NT = 512, STAGES = 2;
   static constexpr int HALF = 128;                        // A rows per group
-  static constexpr int FM = 4, FN = 6;                    // 64 x 96 per wave
+  static constexpr int WN = 2;                            // wave columns (per group: 2 x 2 waves)
+  static constexpr int OCC = 2;                           // waves per SIMD (one of each group)
+  static constexpr int FM = 4, FN = BN / 32;              // 64 x BN/2 per wave
   static constexpr int A_HALF = HALF * BKT * 2;           // 16 KiB (either layout: pitch 128)
   static constexpr int B_OFF = 2 * A_HALF;
-  static constexpr int STAGE = B_OFF + 256 * BKT * 2;     // B: 192 rows (K-major) or pitch 256 (MN-major)
+  static constexpr int STAGE = B_OFF + 256 * BKT * 2;     // B: BN rows (K-major) or pitch 256 (MN-major)
+  static_assert(BN == 192 || BN == 256, "tile widths");
 };
+using PPTile = PPCfg<192>;
 
 // Phase boundaries: every wave's LDS reads (lgkmcnt) or its global -> LDS loads (vmcnt) complete, then
 // all waves of the workgroup meet.  The waits are the s_waitcnt builtin, which the compiler's own wait
@@ -561,10 +568,10 @@ __device__ __forceinline__ void pp_sync_vm() {
 }
 __device__ __forceinline__ void pp_sync() { pp_barrier(); }
 
-template <bool AK, bool BK, int EPI>
+template <class P, bool AK, bool BK, int EPI, bool GATHER = false>
 __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, TP_LDS char* lds, int wave,
                                              int lane, int rot) {
-  using P = PPTile;
+  static_assert(!GATHER || AK, "rows are gathered for a K-major A only");
   constexpr int LB = BK ? P::BN : 256;                        // B rows (K-major) or pitch (MN-major)
   constexpr int B_BYTES = BK ? P::BN * P::BKT * 2 : 256 * P::BKT * 2;
   constexpr int IPW_A = P::A_HALF / 1024 / 4, IPW_B = B_BYTES / 1024 / 4;   // loads per wave of a group
@@ -577,6 +584,18 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, 
   for (int j = 0; j < IPW_A; ++j) piece<AK, P::HALF, P::BKT>((w4 * IPW_A + j) * 1024 + 16 * lane, ar[j], ac[j]);
 #pragma unroll
   for (int j = 0; j < IPW_B; ++j) piece<BK, LB, P::BKT>((w4 * IPW_B + j) * 1024 + 16 * lane, br[j], bc[j]);
+  // gathered A: element offset of each piece's source row (rows of this group's half), -1 outside
+  int ga[IPW_A];
+  unsigned gbytes = 0;
+  if constexpr (GATHER) {
+    gbytes = (unsigned)((long)d.a_rows_n * d.lda * 2);
+#pragma unroll
+    for (int j = 0; j < IPW_A; ++j) {
+      const int m = m0 + P::HALF * g + ar[j];
+      const int src = m < d.M ? d.a_rows[m] : -1;
+      ga[j] = (src >= 0 && src < d.a_rows_n) ? src * (int)d.lda : -1;
+    }
+  }
 
   const int nk = (d.K + P::BKT - 1) / P::BKT;
   rot = (nk > 0 && nk >= TP_GEMM_ROT_MIN_NK) ? rot % nk : 0;
@@ -585,11 +604,12 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, 
   auto issue = [&](int t, int st) {
     TP_LDS char* base = lds + st * P::STAGE;
     const int k = kpos(t);
-    load_tile<AK, P::HALF, P::HALF, IPW_A, P::BKT>(A, m0 + P::HALF * g, k, d.K, base + g * P::A_HALF, ar, ac, w4);
+    if constexpr (GATHER) load_tile_gather<IPW_A>((const bf16*)d.A, gbytes, k, d.K, base + g * P::A_HALF, ga, ac, w4);
+    else load_tile<AK, P::HALF, P::HALF, IPW_A, P::BKT>(A, m0 + P::HALF * g, k, d.K, base + g * P::A_HALF, ar, ac, w4);
     if (g == 0) load_tile<BK, LB, P::BN, IPW_B, P::BKT>(B, n0, k, d.K, base + P::B_OFF, br, bc, w4);
   };
 
-  const int wml = (w4 >> 1) * 64, wn = (w4 & 1) * 96;         // wave tile inside the group's rows
+  const int wml = (w4 >> 1) * 64, wn = (w4 & 1) * (P::BN / 2);   // wave tile inside the group's rows
   f32x4 acc[P::FM][P::FN];
 #pragma unroll
   for (int i = 0; i < P::FM; ++i)
@@ -658,9 +678,9 @@ void gemm_bf16_pp_kernel(GemmDesc d, int tiles_m, int tiles_n) {
       ds.K = max(0, min(d.k_per, d.K - k0));
       ds.C = (float*)d.C + slice * d.c_split;
     }
-    gemm_tile_pp<AK, BK, EPI>(ds, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+    gemm_tile_pp<PPTile, AK, BK, EPI>(ds, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
   } else {
-    gemm_tile_pp<AK, BK, EPI>(d, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
+    gemm_tile_pp<PPTile, AK, BK, EPI>(d, tm * PPTile::BM, tn * PPTile::BN, (TP_LDS char*)smem, wave, lane, tm + tn);
   }
 }
 
@@ -675,12 +695,13 @@ struct GroupedArgs {
   GemmDesc d;          // A, B, C, C2, bias, lda, ldb, ldc, N, K, epi; M unused
   const int* off;      // [groups + 1] row offsets (device)
   const int* prefix;   // [groups + 1] m-tile prefix (device workspace)
+  const int* tile_expert;   // [prefix[groups]] the expert of each m-tile (device workspace)
   int groups;
   long b_stride, bias_stride;
 };
 
 
-template <class Cfg, int EPI, bool GATHER, bool BKM>
+template <class Cfg, int EPI, bool GATHER, bool BKM, bool PP = false>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void gemm_bf16_grouped_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
@@ -693,12 +714,9 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   if (slot >= chunk) return;
   const long lin = (long)(blockIdx.x % 8) * chunk + slot;
   if (lin >= total) return;
-  int lo = 0, hi = g.groups;           // largest e with prefix[e]·tiles_n <= lin
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((long)g.prefix[mid] * tiles_n <= lin) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  // expert e's slots [prefix[e]·tiles_n, prefix[e+1]·tiles_n) hold exactly the lin whose m-tile index
+  // lin / tiles_n lies in [prefix[e], prefix[e+1])
+  const int e = g.tile_expert[lin / tiles_n];
   const int cnt = g.prefix[e + 1] - g.prefix[e];      // >= 1: lin falls inside expert e's slots
   const long local = lin - (long)g.prefix[e] * tiles_n;
   const int mt = g.prefix[e] + (int)(local % cnt), nt = (int)(local / cnt);
@@ -719,7 +737,8 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   }
   // k loops start at k-tile mt (mod the count): the row tiles of the same expert stream their rows
   // of A through different memory channels at the same moment (measured: fc1 2x faster)
-  gemm_tile<Cfg, true, BKM, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
+  if constexpr (PP) gemm_tile_pp<Cfg, true, BKM, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
+  else gemm_tile<Cfg, true, BKM, EPI, GATHER>(d, 0, nt * Cfg::BN, (TP_LDS char*)smem, wave, lane, mt);
 }
 
 // Grouped weight-gradient GEMM: expert e's block C_e [M, N] (at e·c_stride elements) = op(A_e)·op(B_e)
@@ -905,52 +924,58 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
   }
 }
 
-// Every grouped GEMM uses a 256 x 256 tile (two stages of k = 64, or four of k = 32 for a long k loop
-// over an MN-major B); the tile height is still asked per k so the plan can number m-tiles.
+// Every grouped GEMM uses a 256 x 256 tile (two stages of k = 64; the ping-pong schedule for a long k
+// loop over an MN-major B); the tile height is still asked per k so the plan can number m-tiles.
 int gemm_bf16_grouped_bm(int) {
-  static_assert(C0::BM == C5::BM, "the plan numbers m-tiles of one height");
+  static_assert(C0::BM == PPCfg<256>::BM, "the plan numbers m-tiles of one height");
   return C0::BM;
 }
 
 // The n-tile width launch_gemm_bf16_grouped takes for this GEMM (as its tile choice below).
-int gemm_bf16_grouped_bn(const GemmDesc& d) { return (!d.b_kmajor && d.K >= 2048) ? C5::BN : C0::BN; }
+int gemm_bf16_grouped_bn(const GemmDesc& d) { return (!d.b_kmajor && d.K >= 2048) ? PPCfg<256>::BN : C0::BN; }
 
-template <class Cfg>
+template <class Cfg, bool PP = false>
 static hipError_t grouped_t(const GroupedArgs& g, int max_mtiles, hipStream_t s) {
   const long tiles = (long)max_mtiles * ((g.d.N + Cfg::BN - 1) / Cfg::BN);
   if (tiles > 0x7ffffff0L) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
   if (!g.d.a_kmajor) return hipErrorNotSupported;
-  if (g.d.b_kmajor) {            // the backward's dY·Wᵀ forms: GeLU' or plain; gathered rows with the gate
+  if (PP && g.d.b_kmajor) return hipErrorNotSupported;   // the ping-pong tile takes the X·W forms only
+  if constexpr (PP) {
+  } else if (g.d.b_kmajor) {     // the backward's dY·Wᵀ forms: GeLU' or plain; gathered rows with the gate
     if (g.d.a_rows) {
       if (g.d.epi != EPI_DGELU_GATE || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
-      gemm_bf16_grouped_kernel<Cfg, EPI_DGELU_GATE, true, true><<<grid, Cfg::NT, 0, s>>>(g);
+      gemm_bf16_grouped_kernel<Cfg, EPI_DGELU_GATE, true, true, PP><<<grid, Cfg::NT, 0, s>>>(g);
       return hipGetLastError();
     }
-    if (g.d.epi == EPI_DGELU) gemm_bf16_grouped_kernel<Cfg, EPI_DGELU, false, true><<<grid, Cfg::NT, 0, s>>>(g);
-    else if (g.d.epi == EPI_STORE) gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, true><<<grid, Cfg::NT, 0, s>>>(g);
+    if (g.d.epi == EPI_DGELU) gemm_bf16_grouped_kernel<Cfg, EPI_DGELU, false, true, PP><<<grid, Cfg::NT, 0, s>>>(g);
+    else if (g.d.epi == EPI_STORE) gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, true, PP><<<grid, Cfg::NT, 0, s>>>(g);
     else return hipErrorNotSupported;
-  } else if (g.d.a_rows) {
+    return hipGetLastError();
+  }
+  if (g.d.a_rows) {
     if (g.d.epi != EPI_BIAS_GELU || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
-    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, true, false><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, true, false, PP><<<grid, Cfg::NT, 0, s>>>(g);
   } else if (g.d.epi == EPI_BIAS_GELU) {
-    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, false, false><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_BIAS_GELU, false, false, PP><<<grid, Cfg::NT, 0, s>>>(g);
   } else if (g.d.epi == EPI_STORE) {
-    gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, false><<<grid, Cfg::NT, 0, s>>>(g);
+    gemm_bf16_grouped_kernel<Cfg, EPI_STORE, false, false, PP><<<grid, Cfg::NT, 0, s>>>(g);
   } else {
     return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
-// prefix[] must number m-tiles of gemm_bf16_grouped_bm(d.K) rows.
-hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
-                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
-  GroupedArgs g{d, off, prefix, groups, b_stride, bias_stride};
+// prefix[] must number m-tiles of gemm_bf16_grouped_bm(d.K) rows, tile_expert[] name their experts.
+hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, const int* tile_expert,
+                                    int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+  GroupedArgs g{d, off, prefix, tile_expert, groups, b_stride, bias_stride};
   if (max_mtiles <= 0 || d.N <= 0) return hipSuccess;
-  // a long k loop over [in, out] weights (the forward's fc1): four stages of k = 32 keep more loads in
-  // flight per CU (measured: the 128-expert fc1, k = 8192, 14% faster; both-K-major forms are not)
-  if (!d.b_kmajor && d.K >= 2048) return grouped_t<C5>(g, max_mtiles, s);
+  // a long k loop over [in, out] weights (the forward's fc1) takes the ping-pong schedule on a
+  // 256 x 256 tile (measured on the 128-expert fc1, k = 8192, gathered rows: 0.30 of peak against 0.22
+  // for four stages of k = 32 on the plain tile).  The backward's both-K-major gathered form stays on
+  // the plain tile: with the gather and the gated epilogue the ping-pong tile spills (twice as slow).
+  if (!d.b_kmajor && d.K >= 2048) return grouped_t<PPCfg<256>, true>(g, max_mtiles, s);
   return grouped_t<C0>(g, max_mtiles, s);
 }
 

@@ -148,16 +148,11 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d) {
 // the GBM-row tiles of all experts; blockIdx.y is that tile number, blockIdx.x the n-tile.
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void gemm_generic_grouped_kernel(GemmDesc g, const int* off,
-                                                                   const int* prefix, int groups,
-                                                                   long b_stride, long bias_stride) {
+                                                                   const int* prefix, const int* tile_expert,
+                                                                   int groups, long b_stride, long bias_stride) {
   const int mt = blockIdx.y;
   if (mt >= prefix[groups]) return;
-  int lo = 0, hi = groups;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= mt) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = tile_expert[mt];       // the expert whose m-tiles [prefix[e], prefix[e+1]) hold mt
   const int row0 = off[e] + (mt - prefix[e]) * GBM;
   GemmDesc d = g;
   d.M = off[e + 1] - row0;
@@ -206,17 +201,18 @@ hipError_t launch_generic_t(const GemmDesc& d, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int* prefix, int groups,
-                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int* prefix, const int* tile_expert,
+                                    int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
   dim3 grid((d.N + GBN - 1) / GBN, max_mtiles);
+  const int* te = tile_expert;
   if (d.epi == EPI_BIAS_GELU)
-    gemm_generic_grouped_kernel<T, EPI_BIAS_GELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+    gemm_generic_grouped_kernel<T, EPI_BIAS_GELU><<<grid, 256, 0, s>>>(d, off, prefix, te, groups, b_stride, bias_stride);
   else if (d.epi == EPI_STORE)
-    gemm_generic_grouped_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+    gemm_generic_grouped_kernel<T, EPI_STORE><<<grid, 256, 0, s>>>(d, off, prefix, te, groups, b_stride, bias_stride);
   else if (d.epi == EPI_DGELU)
-    gemm_generic_grouped_kernel<T, EPI_DGELU><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride, bias_stride);
+    gemm_generic_grouped_kernel<T, EPI_DGELU><<<grid, 256, 0, s>>>(d, off, prefix, te, groups, b_stride, bias_stride);
   else if (d.epi == EPI_DGELU_GATE)
-    gemm_generic_grouped_kernel<T, EPI_DGELU_GATE><<<grid, 256, 0, s>>>(d, off, prefix, groups, b_stride,
+    gemm_generic_grouped_kernel<T, EPI_DGELU_GATE><<<grid, 256, 0, s>>>(d, off, prefix, te, groups, b_stride,
                                                                         bias_stride);
   else
     return hipErrorNotSupported;
@@ -228,13 +224,15 @@ hipError_t launch_generic_grouped_t(const GemmDesc& d, const int* off, const int
 int gemm_generic_grouped_bm() { return GBM; }
 int gemm_generic_grouped_bn() { return GBN; }
 
-hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
-                                       long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
+hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, const int* tile_expert,
+                                       int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
   if (max_mtiles <= 0 || d.N <= 0) return hipSuccess;
   if (max_mtiles > 65535) return hipErrorInvalidValue;
   return d.dtype == DT_BF16
-             ? launch_generic_grouped_t<bf16>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s)
-             : launch_generic_grouped_t<float>(d, off, prefix, groups, b_stride, bias_stride, max_mtiles, s);
+             ? launch_generic_grouped_t<bf16>(d, off, prefix, tile_expert, groups, b_stride, bias_stride,
+                                              max_mtiles, s)
+             : launch_generic_grouped_t<float>(d, off, prefix, tile_expert, groups, b_stride, bias_stride,
+                                               max_mtiles, s);
 }
 
 hipError_t launch_gemm_generic_grouped_k(const GemmDesc& d, const int* off, int groups, long c_stride, hipStream_t s) {

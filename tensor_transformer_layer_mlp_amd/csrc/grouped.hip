@@ -16,10 +16,10 @@
 
 namespace tp {
 
-hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
-                                    long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
-hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, int groups,
-                                       long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int* prefix, const int* tile_expert,
+                                    int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_generic_grouped(const GemmDesc& d, const int* off, const int* prefix, const int* tile_expert,
+                                       int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s);
 int gemm_bf16_grouped_bm(int K);
 int gemm_bf16_grouped_bn(const GemmDesc& d);
 int gemm_generic_grouped_bm();
@@ -51,12 +51,17 @@ __device__ __forceinline__ int block_scan(int v, int* sh, Op op) {
 
 // off_out[i] = max(off_out[i-1], min(off_in[i], rows)) with off_out[0] = clamp(off_in[0], 0, rows):
 // a running maximum, so the clamped offsets come from one max-scan; the m-tile counts of the
-// groups then from two sum-scans.  Groups go PLAN_T at a time, carrying the last values.
+// groups then from two sum-scans.  Groups go PLAN_T at a time, carrying the last values.  Each
+// group also writes its number into tiles1 / tiles2 at its m-tiles [prefix[i], prefix[i+1]) (at
+// most cap of them, cap >= ceil(rows / bm) + groups), so a GEMM workgroup finds its expert with
+// one load instead of a binary search over the prefix.
 __global__ __launch_bounds__(PLAN_T) void grouped_plan_kernel(const int* __restrict__ off_in, int groups,
                                                               int rows, int bm1, int bm2,
                                                               int* __restrict__ off_out,
                                                               int* __restrict__ prefix1,
-                                                              int* __restrict__ prefix2) {
+                                                              int* __restrict__ prefix2,
+                                                              int* __restrict__ tiles1,
+                                                              int* __restrict__ tiles2, int cap) {
   __shared__ int sh[PLAN_T];
   int carry_o = min(max(off_in[0], 0), rows), carry_1 = 0, carry_2 = 0;
   if (threadIdx.x == 0) {
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(PLAN_T) void grouped_plan_kernel(const int* __restr
       off_out[i + 1] = o;
       prefix1[i + 1] = carry_1 + p1;
       prefix2[i + 1] = carry_2 + p2;
+      for (int t = carry_1 + p1 - (n + bm1 - 1) / bm1; t < min(carry_1 + p1, cap); ++t) tiles1[t] = i;
+      for (int t = carry_2 + p2 - (n + bm2 - 1) / bm2; t < min(carry_2 + p2, cap); ++t) tiles2[t] = i;
     }
     carry_1 += t1;
     carry_2 += t2;
@@ -116,15 +123,34 @@ __global__ __launch_bounds__(256) void grouped_colsum_kernel(const T* __restrict
 
 }  // namespace
 
-size_t grouped_ws_bytes(int groups) { return (size_t)3 * (groups + 1) * sizeof(int); }
+// The plan: the sanitised offsets and the two m-tile prefixes ([groups + 1] each), then the two
+// m-tile -> group tables (ceil(rows / 64) + groups entries each: every tile height is at least 64).
+static long plan_cap(int groups, int rows) { return (long)(rows + 63) / 64 + groups; }
+size_t grouped_ws_bytes(int groups, int rows) {
+  return (size_t)(3 * ((long)groups + 1) + 2 * plan_cap(groups, rows)) * sizeof(int);
+}
+
+// Lays out the plan in ws and launches the plan kernel.
+static hipError_t run_plan(const int* off, int groups, int rows, int bm1, int bm2, void* ws, int** off_s,
+                           int** prefix1, int** prefix2, int** tiles1, int** tiles2, hipStream_t s) {
+  const long cap = plan_cap(groups, rows);
+  if (cap > 0x7fffffffL) return hipErrorInvalidValue;
+  *off_s = (int*)ws;
+  *prefix1 = *off_s + (groups + 1);    // m-tiles of the first GEMM's tile height
+  *prefix2 = *prefix1 + (groups + 1);  // m-tiles of the second's
+  *tiles1 = *prefix2 + (groups + 1);
+  *tiles2 = *tiles1 + cap;
+  ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1) + 4.0 * cap);
+  grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, *off_s, *prefix1, *prefix2, *tiles1,
+                                           *tiles2, (int)cap);
+  return hipGetLastError();
+}
 
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
                               void* A1, void* Y, void* ws, hipStream_t s, const int* row_token, int tokens) {
   if (rows <= 0) return hipSuccess;
-  int* off_s = (int*)ws;
-  int* prefix1 = off_s + (groups + 1);       // m-tiles of fc1's tile height
-  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of fc2's
+  int *off_s, *prefix1, *prefix2, *tiles1, *tiles2;   // plan (fc1's tile height, then fc2's)
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
 
   GemmDesc fc1;
@@ -151,9 +177,7 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
   if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
   {
-    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
-    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
-    hipError_t e = hipGetLastError();
+    hipError_t e = run_plan(off, groups, rows, bm1, bm2, ws, &off_s, &prefix1, &prefix2, &tiles1, &tiles2, s);
     if (e != hipSuccess) return e;
   }
   const double f1 = 2.0 * rows * (double)Fr * H;
@@ -166,20 +190,20 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
     {
       ProfScope p(row_token ? "gemm_bf16_grouped<fc1, gather, bias+gelu>" : "gemm_bf16_grouped<fc1, bias+gelu>",
                   s, f1, by1);
-      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
+      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
       if (e != hipSuccess) return e;
     }
     ProfScope p("gemm_bf16_grouped<fc2>", s, f1, by2);
-    return launch_gemm_bf16_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
+    return launch_gemm_bf16_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, (int)maxmt2, s);
   }
   {
     ProfScope p(row_token ? "gemm_generic_grouped<fc1, gather, bias+gelu>" : "gemm_generic_grouped<fc1, bias+gelu>",
                 s, f1, by1);
-    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
+    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }
   ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
-  return launch_gemm_generic_grouped(fc2, off_s, prefix2, groups, (long)Fr * H, 0, (int)maxmt2, s);
+  return launch_gemm_generic_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, (int)maxmt2, s);
 }
 
 // Backward of launch_mlp_grouped on expert-sorted operands, expert by expert (rows [off[e], off[e+1])):
@@ -198,9 +222,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
                                   const int* x_rows, int x_rows_n) {
   if (groups <= 0) return hipSuccess;
   if (groups > 65535) return hipErrorInvalidValue;   // the column sum's grid y (checked before any launch)
-  int* off_s = (int*)ws;
-  int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
-  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of the dX GEMM's
+  int *off_s, *prefix1, *prefix2, *tiles1, *tiles2;   // plan (the dA1 GEMM's tile height, then dX's)
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
 
   GemmDesc ga;                                // dA1 = (dZ·W2ᵀ) ∘ GeLU'(A1)
@@ -228,9 +250,7 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
   if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
   {
-    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
-    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
-    hipError_t e = hipGetLastError();
+    hipError_t e = run_plan(off, groups, rows, bm1, bm2, ws, &off_s, &prefix1, &prefix2, &tiles1, &tiles2, s);
     if (e != hipSuccess) return e;
   }
   const double fl = 2.0 * rows * (double)Fr * H;
@@ -239,8 +259,8 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   if (rows > 0) {
     ProfScope p(tiled ? "gemm_bf16_grouped<dZ.W2t, dgelu>" : "gemm_generic_grouped<dZ.W2t, dgelu>", s, fl,
                 es * ((double)rows * H + 2.0 * rows * Fr) + wts);   // dZ and A1 read, dA1 written
-    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s)
-              : launch_gemm_generic_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s);
+    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, tiles1, groups, (long)Fr * H, 0, (int)maxmt1, s)
+              : launch_gemm_generic_grouped(ga, off_s, prefix1, tiles1, groups, (long)Fr * H, 0, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }
   {
@@ -271,8 +291,8 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   if (rows > 0) {
     ProfScope p(tiled ? "gemm_bf16_grouped<dA1.W1t>" : "gemm_generic_grouped<dA1.W1t>", s, fl,
                 es * ((double)rows * Fr + (double)rows * H) + wts);
-    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s)
-              : launch_gemm_generic_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s);
+    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, tiles2, groups, (long)H * Fr, 0, (int)maxmt2, s)
+              : launch_gemm_generic_grouped(gx, off_s, prefix2, tiles2, groups, (long)H * Fr, 0, (int)maxmt2, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -295,7 +315,7 @@ size_t moe_experts_bwd_ws_bytes(int groups, int rows, int H, int Fr, int dtype) 
   const size_t es = dtype == DT_BF16 ? 2 : 4;
   auto a256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t nt = (size_t)(Fr + 63) / 64;   // n-tiles of the narrowest tile (the generic kernel's)
-  return a256(grouped_ws_bytes(groups)) + a256((size_t)rows * Fr * es) + a256((size_t)rows * 4) +
+  return a256(grouped_ws_bytes(groups, rows)) + a256((size_t)rows * Fr * es) + a256((size_t)rows * 4) +
          a256((size_t)rows * Fr * es) + a256(nt * rows * 4);
 }
 
@@ -309,10 +329,9 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
   auto a256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
   char* w = (char*)ws;
-  int* off_s = (int*)w;
-  int* prefix1 = off_s + (groups + 1);       // m-tiles of the dA1 GEMM's tile height
-  int* prefix2 = prefix1 + (groups + 1);     // m-tiles of the dX GEMM's
-  w += a256(grouped_ws_bytes(groups));
+  int *off_s, *prefix1, *prefix2, *tiles1, *tiles2;   // plan (the dA1 GEMM's tile height, then dX's)
+  void* plan = w;
+  w += a256(grouped_ws_bytes(groups, rows));
   void* dA1 = w;
   w += a256((size_t)rows * Fr * (size_t)es);
   float* gate_row = (float*)w;
@@ -354,12 +373,8 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
   const long maxmt1 = (long)(rows + bm1 - 1) / bm1 + groups, maxmt2 = (long)(rows + bm2 - 1) / bm2 + groups;
   if (maxmt1 > 0x7fffffffL || maxmt2 > 0x7fffffffL) return hipErrorInvalidValue;
   hipError_t e;
-  {
-    ProfScope p("grouped_plan", s, 0.0, 12.0 * (groups + 1));
-    grouped_plan_kernel<<<1, PLAN_T, 0, s>>>(off, groups, rows, bm1, bm2, off_s, prefix1, prefix2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  e = run_plan(off, groups, rows, bm1, bm2, plan, &off_s, &prefix1, &prefix2, &tiles1, &tiles2, s);
+  if (e != hipSuccess) return e;
   e = launch_moe_row_gates(dtype, tokens, k, rows, Fr, gates, row_token, token_row, Y, gate_row, Yg, s);
   if (e != hipSuccess) return e;
   const double fl = 2.0 * rows * (double)Fr * H;
@@ -368,8 +383,8 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
     // d_out's unique rows, A1 and Y read, dA1 written, the row dots
     ProfScope p(tiled ? "gemm_bf16_grouped<dout.W2t, gather, gate+dgelu>" : "gemm_generic_grouped<dout.W2t, gather, gate+dgelu>",
                 s, fl, es * ((double)tokens * H + 3.0 * rows * Fr) + wts + 4.0 * rows * (ntiles + 2));
-    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s)
-              : launch_gemm_generic_grouped(ga, off_s, prefix1, groups, (long)Fr * H, 0, (int)maxmt1, s);
+    e = tiled ? launch_gemm_bf16_grouped(ga, off_s, prefix1, tiles1, groups, (long)Fr * H, 0, (int)maxmt1, s)
+              : launch_gemm_generic_grouped(ga, off_s, prefix1, tiles1, groups, (long)Fr * H, 0, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }
   e = launch_moe_dgates(tokens, k, rows, ntiles, row_dot, token_row, off_s, groups, dgates, s);
@@ -401,8 +416,8 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
   if (rows > 0) {
     ProfScope p(tiled ? "gemm_bf16_grouped<dA1.W1t>" : "gemm_generic_grouped<dA1.W1t>", s, fl,
                 es * ((double)rows * Fr + (double)rows * H) + wts);
-    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s)
-              : launch_gemm_generic_grouped(gx, off_s, prefix2, groups, (long)H * Fr, 0, (int)maxmt2, s);
+    e = tiled ? launch_gemm_bf16_grouped(gx, off_s, prefix2, tiles2, groups, (long)H * Fr, 0, (int)maxmt2, s)
+              : launch_gemm_generic_grouped(gx, off_s, prefix2, tiles2, groups, (long)H * Fr, 0, (int)maxmt2, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -90,7 +90,7 @@ hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* q
                            float* ws, hipStream_t s);
 
 // Grouped expert MLP shard (rows [off[e], off[e+1]) use expert e's weights); off is device memory.
-size_t grouped_ws_bytes(int groups);
+size_t grouped_ws_bytes(int groups, int rows);
 // With row_token set, row r of the expert-sorted matrix is row row_token[r] of X (tokens rows),
 // gathered inside fc1's operand loads.
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
