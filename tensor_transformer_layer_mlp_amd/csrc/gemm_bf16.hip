@@ -707,8 +707,12 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::STAGES * Cfg::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The plan's values are the same for every lane: readfirstlane keeps them (and the operand
+  // addresses made from them) in scalar registers.  Left to the compiler, a per-lane value can
+  // reach a buffer descriptor, which then costs a loop over lanes around every load.
+  const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
   const int tiles_n = (g.d.N + Cfg::BN - 1) / Cfg::BN;
-  const long total = (long)g.prefix[g.groups] * tiles_n;
+  const long total = (long)uni(g.prefix[g.groups]) * tiles_n;
   const long chunk = (total + 7) / 8;
   const long slot = blockIdx.x / 8;
   if (slot >= chunk) return;
@@ -716,13 +720,14 @@ void gemm_bf16_grouped_kernel(GroupedArgs g) {
   if (lin >= total) return;
   // expert e's slots [prefix[e]·tiles_n, prefix[e+1]·tiles_n) hold exactly the lin whose m-tile index
   // lin / tiles_n lies in [prefix[e], prefix[e+1])
-  const int e = g.tile_expert[lin / tiles_n];
-  const int cnt = g.prefix[e + 1] - g.prefix[e];      // >= 1: lin falls inside expert e's slots
-  const long local = lin - (long)g.prefix[e] * tiles_n;
-  const int mt = g.prefix[e] + (int)(local % cnt), nt = (int)(local / cnt);
-  const int row0 = g.off[e] + (mt - g.prefix[e]) * Cfg::BM;
+  const int e = uni(g.tile_expert[lin / tiles_n]);
+  const int p0 = uni(g.prefix[e]), p1 = uni(g.prefix[e + 1]);
+  const int cnt = p1 - p0;                           // >= 1: lin falls inside expert e's slots
+  const long local = lin - (long)p0 * tiles_n;
+  const int mt = uni(p0 + (int)(local % cnt)), nt = uni((int)(local / cnt));   // (divided on the vector unit)
+  const int row0 = uni(g.off[e]) + (mt - p0) * Cfg::BM;
   GemmDesc d = g.d;
-  d.M = g.off[e + 1] - row0;           // rows of this expert from row0 on (>= 1)
+  d.M = uni(g.off[e + 1]) - row0;      // rows of this expert from row0 on (>= 1)
   if constexpr (GATHER) d.a_rows = g.d.a_rows + row0;   // A stays the whole gathered-from matrix
   else d.A = (const bf16*)g.d.A + (long)row0 * g.d.lda;
   d.B = (const bf16*)g.d.B + (long)e * g.b_stride;
@@ -768,8 +773,8 @@ void gemm_bf16_grouped_k_kernel(GroupedKArgs g, int tiles_m, int tiles_n) {
   const int local = (int)(wg % per);
   const int tm = local % tiles_m, tn = local / tiles_m;
   GemmDesc d = g.d;
-  const int k0 = g.off[e];
-  d.K = g.off[e + 1] - k0;
+  const int k0 = __builtin_amdgcn_readfirstlane(g.off[e]);   // uniform: scalar operand addresses
+  d.K = __builtin_amdgcn_readfirstlane(g.off[e + 1]) - k0;
   if constexpr (GK) d.a_rows = g.d.a_rows + k0;   // A stays the whole gathered-from matrix
   else d.A = (const bf16*)g.d.A + (long)k0 * g.d.lda;
   if constexpr (GKB) d.b_rows = g.d.b_rows + k0;  // B likewise
@@ -940,9 +945,7 @@ static hipError_t grouped_t(const GroupedArgs& g, int max_mtiles, hipStream_t s)
   if (tiles > 0x7ffffff0L) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
   if (!g.d.a_kmajor) return hipErrorNotSupported;
-  if (PP && g.d.b_kmajor) return hipErrorNotSupported;   // the ping-pong tile takes the X·W forms only
-  if constexpr (PP) {
-  } else if (g.d.b_kmajor) {     // the backward's dY·Wᵀ forms: GeLU' or plain; gathered rows with the gate
+  if (g.d.b_kmajor) {     // the backward's dY·Wᵀ forms: GeLU' or plain; gathered rows with the gate
     if (g.d.a_rows) {
       if (g.d.epi != EPI_DGELU_GATE || (long)g.d.a_rows_n * g.d.lda * 2 > 0x7fffffffL) return hipErrorNotSupported;
       gemm_bf16_grouped_kernel<Cfg, EPI_DGELU_GATE, true, true, PP><<<grid, Cfg::NT, 0, s>>>(g);
@@ -971,11 +974,10 @@ hipError_t launch_gemm_bf16_grouped(const GemmDesc& d, const int* off, const int
                                     int groups, long b_stride, long bias_stride, int max_mtiles, hipStream_t s) {
   GroupedArgs g{d, off, prefix, tile_expert, groups, b_stride, bias_stride};
   if (max_mtiles <= 0 || d.N <= 0) return hipSuccess;
-  // a long k loop over [in, out] weights (the forward's fc1) takes the ping-pong schedule on a
-  // 256 x 256 tile (measured on the 128-expert fc1, k = 8192, gathered rows: 0.30 of peak against 0.22
-  // for four stages of k = 32 on the plain tile).  The backward's both-K-major gathered form stays on
-  // the plain tile: with the gather and the gated epilogue the ping-pong tile spills (twice as slow).
-  if (!d.b_kmajor && d.K >= 2048) return grouped_t<PPCfg<256>, true>(g, max_mtiles, s);
+  // a long k loop takes the ping-pong schedule on a 256 x 256 tile (measured on the 128-expert shard,
+  // k = 8192, gathered rows: fc1 0.30 of peak against 0.22 for four stages of k = 32 on the plain
+  // tile; the backward's gated dA1 0.32 against 0.31 on the plain tile)
+  if (d.K >= 2048) return grouped_t<PPCfg<256>, true>(g, max_mtiles, s);
   return grouped_t<C0>(g, max_mtiles, s);
 }
 

@@ -24,9 +24,10 @@ def _offsets(counts):
 
 
 # (rows per group, H, F_group, tp, rank): ragged groups, an empty group at each end and inside, a
-# group of one row; H = 100 and F_r = 30 take the generic kernels
+# group of one row; H = 100 and F_r = 30 take the generic kernels; H = 2056 the long-k tile
 GCASES = [([300, 0, 17, 512, 1], 256, 256, 2, 0), ([0, 64, 0, 200, 0], 128, 96, 1, 0),
-          ([5, 1, 40], 100, 60, 2, 1), ([1000, 24], 512, 1024, 4, 3)]
+          ([5, 1, 40], 100, 60, 2, 1), ([1000, 24], 512, 1024, 4, 3),
+          ([300, 0, 513, 1], 2056, 512, 2, 1)]      # k = H >= 2048: the ping-pong tile, a ragged k tail
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -72,7 +73,7 @@ def test_grouped_mlp_bwd(counts, H, Fg, tp, rank, dtype):
 
 
 BWD_CASES = [(300, 192, 6, 2, 128, 2, 1), (518, 256, 16, 4, 512, 4, 0), (64, 100, 5, 3, 60, 2, 1),
-             (8, 64, 6, 1, 16, 1, 0)]
+             (8, 64, 6, 1, 16, 1, 0), (300, 2056, 6, 2, 512, 2, 1)]   # the last: k = H on the long-k tile
 
 
 def _moe_bwd(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, fwd, d_out, z_none=False):

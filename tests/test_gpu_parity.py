@@ -354,6 +354,23 @@ def _run_grouped(off, rows, H, F_group, tp, rank, ops, dtype, Fr):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_mlp_long_k(dtype):
+    """fc1 with k = H = 2056 (>= 2048: the ping-pong 256 x 256 tile for the bf16 path, with a ragged
+    k tail) over ragged and empty groups."""
+    H, F_group, tp, rank = 2056, 512, 2, 0
+    off, rows, Fr, ops = _grouped_inputs([300, 0, 513, 1], 0, dtype, H, F_group, tp, rank, std=0.02)
+    Z, A1, Y = _run_grouped(off, rows, H, F_group, tp, rank, ops, dtype, Fr)
+    f = {k: v.f64 for k, v in ops.items()}
+    ref = oracle.tp_mlp_grouped_shard_fwd(tp, rank, off, f["X"], f["W1"], f["b1"], f["W2"])
+    a1 = np.zeros((rows, Fr))
+    for e in range(len(off) - 1):
+        a1[off[e]:off[e + 1]] = f["X"][off[e]:off[e + 1]] @ f["W1"][e] + f["b1"][e]
+    assert_close(A1, a1, dtype, "A1 (long k)")
+    assert_close(Y, oracle.gelu(a1), dtype, "Y (long k)")
+    assert_close(Z, ref, dtype, "Z (long k)")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("case", sorted(GROUP_CASES))
 def test_grouped_mlp(case, dtype):
     sizes, extra = GROUP_CASES[case]
