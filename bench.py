@@ -56,7 +56,7 @@ def parse():
                     help="with --pmc-pass: also one residual + LayerNorm forward and backward")
     ap.add_argument("--blas-compare", action="store_true",
                     help="also time torch.matmul on the nine GEMM shapes of the GPT-3 shard")
-    ap.add_argument("--summarize", choices=["stats", "traffic", "mfma", "hbm", "lds"],
+    ap.add_argument("--summarize", choices=["stats", "traffic", "mfma", "hbm", "lds", "blas"],
                     help="print a profile summary from rocprofv3 CSV output under --prof-dir, and exit")
     ap.add_argument("--prof-dir", default="gpurun_out/prof",
                     help="rocprofv3 output directory (stats: one kernel-trace run; traffic / hbm: the "
@@ -541,7 +541,7 @@ def _csv_files(d, suffix):
 def short_kernel(name):
     import re
     name = name.replace("tp::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
-    m = re.match(r"void (gemm_bf16\w*)<(.*)>\(tp::\w+(?:, int)*\)", name)
+    m = re.match(r"void (gemm_\w+)<(.*)>\([\w:, ]*\)$", name)
     if m:
         return f"{m.group(1)}<{m.group(2)}>"
     m = re.match(r"_ZN2tp12_GLOBAL__N_1(\d+)(\w+)", name)
@@ -670,6 +670,23 @@ def summarize(what, d, kernel, tag):
                 lab[:36], a["dur"], 100 * a["SQ_LDS_IDX_ACTIVE"] / g, 100 * a["SQ_LDS_BANK_CONFLICT"] / g,
                 100 * b["TA_TA_BUSY"] / g, 100 * b["TD_TD_BUSY"] / g, 100 * a["SQ_WAIT_INST_LDS"] / wc,
                 100 * b["SQ_WAIT_ANY"] / wc))
+    elif what == "blas":
+        # the JSON line of a --blas-compare run, saved as <prof-dir>/blas.log
+        line = [x for x in open(os.path.join(d, "blas.log")) if x.startswith("{")][-1]
+        j = json.loads(line)
+        bc, sites = j["blas_compare"], j["gemm_call_sites"]
+        print(f"# library: {bc['library']}, torch {bc['torch']}")
+        print("%-8s %6s %6s %6s %12s %12s %12s %12s" % ("gemm", "M", "N", "K", "BLAS us", "BLAS TF/s", "here us",
+                                                        "here TF/s"))
+        tb = th = fl = 0.0
+        for site in GEMM_SITES:
+            b, h = bc["gemms"][site], sites[site]
+            f = 2.0 * b["M"] * b["N"] * b["K"]
+            tb, th, fl = tb + b["avg_us"], th + h["avg_launch_us"], fl + f
+            print("%-8s %6d %6d %6d %12.1f %12.1f %12.1f %12.1f" % (site, b["M"], b["N"], b["K"], b["avg_us"],
+                                                                    f / b["avg_us"] / 1e6, h["avg_launch_us"],
+                                                                    f / h["avg_launch_us"] / 1e6))
+        print("%-8s %20s %12.1f %12.1f %12.1f %12.1f" % ("total", "", tb, fl / tb / 1e6, th, fl / th / 1e6))
     elif what == "mfma":
         import numpy as np
         clk = [e for e in _pmc_dispatches(os.path.join(d, "pmc_clk")) if _is_library(e["name"])]
