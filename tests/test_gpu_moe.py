@@ -71,7 +71,7 @@ def _run_block(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, Fr):
     return dict(out=out, Z=Z, Y=Y, A1=A1)
 
 
-# H = 2048 takes the four-stage tile for fc1's long k loop
+# H = 2048 takes the ping-pong 256 x 256 tile for fc1's long k loop
 BLOCK_CASES = [(300, 192, 6, 2, 128, 2, 1), (518, 256, 16, 4, 512, 4, 0), (64, 100, 5, 3, 60, 2, 1),
                (8, 64, 3, 3, 16, 1, 0), (200, 2048, 8, 2, 256, 2, 0)]
 

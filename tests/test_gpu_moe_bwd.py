@@ -123,6 +123,44 @@ def test_moe_shard_bwd(tokens, H, E, k, F_expert, tp, rank, dtype):
         assert torch.equal(g[key], g2[key]), f"{key} differs between two calls"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_moe_shard_bwd_skewed_routing(dtype):
+    """Router logits biased so that three experts take nearly every token's three choices: expert
+    groups of several m-tiles next to a one-row group and eight empty ones in the gathered, gated
+    dA1 GEMM, its row dots over several n-tiles (F_r = 640: three 256-wide tiles, the last ragged) and
+    the weight gradients' k ranges; against the oracle, and repeatable bit for bit."""
+    tokens, H, E, k, F_expert, tp, rank = 700, 256, 12, 3, 1280, 2, 1
+    lg = _logits(tokens, E, "bwd_skew")
+    lg[:, 0] += 7.0
+    lg[:, 7] += 6.0
+    lg[:, 3] += 5.0
+    route = _route_gpu(lg, k)
+    r = oracle.moe_route(lg, k)
+    counts = np.diff(r["group_offsets"])
+    # (the seeded draw gives 700, 700, 699 rows, one expert with a single row, eight without any)
+    assert counts.max() == tokens and (counts == 0).sum() == 8 and (counts == 1).sum() == 1, counts
+    Xop = synth.normal("moeXskew", (tokens, H), 1.0, dtype)
+    Fr, W = _expert_weights(E, H, F_expert, tp, rank, dtype)
+    X = dev(Xop)
+    fwd = _run_block(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, Fr)
+    dop = synth.normal("moedskew", (tokens, H), 1.0, dtype)
+    g = _moe_bwd(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, fwd, dev(dop))
+    ref = oracle.tp_moe_shard_bwd(tp, rank, Xop.f64, r, W["W1"].f64, W["W2"].f64,
+                                  {key: host(fwd[key]) for key in ("A1", "Y", "Z")}, dop.f64)
+    assert_close(g["dX"], ref["dX"], dtype, "dX_r")
+    assert_close(g["dgates"], ref["dgates"], dtype, "dgates_r", tol=1e-4)
+    for key in ("dW1", "db1", "dW2"):
+        got = host(g[key])
+        for e in range(E):
+            if counts[e] == 0:
+                assert np.all(got[e] == 0), f"{key}[{e}] of an expert without tokens is not zero"
+            else:
+                assert_close(got[e], ref[key][e], dtype, f"{key}[{e}]")
+    g2 = _moe_bwd(tp, rank, tokens, H, E, k, F_expert, dtype, X, route, W, fwd, dev(dop), z_none=True)
+    for key in g:
+        assert torch.equal(g[key], g2[key]), f"{key} differs between two calls"
+
+
 RB_CASES = [(37, 8, 2), (500, 64, 8), (300, 128, 8), (77, 200, 5), (16, 1024, 32), (5, 3, 3), (1, 1, 1)]
 
 
