@@ -336,17 +336,14 @@ constexpr int RBWD_TOKENS = 16;   // tokens (waves) per workgroup of the router 
 
 // The MoE backward without a materialised dZ (see launch_moe_experts_bwd).  Row r's gate: the gate of
 // the (t, j) whose row it is (t = row_token[r], j the choice with token_row[t, j] = r; 0 when r has no
-// such choice), and the gate-scaled copy Yg[r] = gate·Y[r] that dW2 = Ygᵀ·d_out takes.  One thread per
-// 8 elements of a row (V = 8) or per element.
-template <typename T, int V>
-__global__ __launch_bounds__(256) void moe_row_gates_kernel(int tokens, int k, int rows, int Fr, const float* __restrict__ gates,
+// such choice), one thread per row; then the gate-scaled copy Yg[r] = gate·Y[r] that dW2 = Ygᵀ·d_out
+// takes, one thread per 8 elements of a row (V = 8) or per element.
+__global__ __launch_bounds__(256) void moe_gate_rows_kernel(int tokens, int k, int rows, const float* __restrict__ gates,
                                                             const int* __restrict__ row_token,
-                                                            const int* __restrict__ token_row, const T* __restrict__ Y,
-                                                            float* __restrict__ gate_row, T* __restrict__ Yg) {
-  const int per = (Fr + V - 1) / V;
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long)rows * per) return;
-  const int r = (int)(i / per), c = (int)(i % per) * V;
+                                                            const int* __restrict__ token_row,
+                                                            float* __restrict__ gate_row) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
   const int t = row_token[r];
   float gt = 0.f;
   if (t >= 0 && t < tokens)
@@ -355,7 +352,17 @@ __global__ __launch_bounds__(256) void moe_row_gates_kernel(int tokens, int k, i
         gt = gates[(long)t * k + j];
         break;
       }
-  if (c == 0) gate_row[r] = gt;
+  gate_row[r] = gt;
+}
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void moe_scale_rows_kernel(int rows, int Fr, const float* __restrict__ gate_row,
+                                                             const T* __restrict__ Y, T* __restrict__ Yg) {
+  const int per = (Fr + V - 1) / V;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)rows * per) return;
+  const int r = (int)(i / per), c = (int)(i % per) * V;
+  const float gt = gate_row[r];
   const T* y = Y + (long)r * Fr + c;
   T* o = Yg + (long)r * Fr + c;
   if constexpr (V == 8) {
@@ -554,18 +561,22 @@ hipError_t launch_moe_row_gates(int dtype, int tokens, int k, int rows, int Fr, 
   if (rows <= 0 || Fr <= 0) return hipSuccess;
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
   ProfScope p("moe_row_gates", s, (double)rows * Fr, 2.0 * es * rows * Fr + 8.0 * rows + 4.0 * rows * k);
+  moe_gate_rows_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(tokens, k, rows, gates, row_token, token_row,
+                                                                      gate_row);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (dtype == DT_BF16 && Fr % 8 == 0 && ((((uintptr_t)Y) | ((uintptr_t)Yg)) & 15) == 0) {
     const long n = (long)rows * (Fr / 8);
-    moe_row_gates_kernel<bf16, 8><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        tokens, k, rows, Fr, gates, row_token, token_row, (const bf16*)Y, gate_row, (bf16*)Yg);
+    moe_scale_rows_kernel<bf16, 8><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, Fr, gate_row, (const bf16*)Y,
+                                                                              (bf16*)Yg);
   } else if (dtype == DT_BF16) {
     const long n = (long)rows * Fr;
-    moe_row_gates_kernel<bf16, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        tokens, k, rows, Fr, gates, row_token, token_row, (const bf16*)Y, gate_row, (bf16*)Yg);
+    moe_scale_rows_kernel<bf16, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, Fr, gate_row, (const bf16*)Y,
+                                                                              (bf16*)Yg);
   } else {
     const long n = (long)rows * Fr;
-    moe_row_gates_kernel<float, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        tokens, k, rows, Fr, gates, row_token, token_row, (const float*)Y, gate_row, (float*)Yg);
+    moe_scale_rows_kernel<float, 1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, Fr, gate_row, (const float*)Y,
+                                                                               (float*)Yg);
   }
   return hipGetLastError();
 }
