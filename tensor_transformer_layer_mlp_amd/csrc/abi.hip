@@ -793,12 +793,26 @@ int tp_moe_shard_bwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   char* dXp = experts_ws + align256(moe_experts_bwd_ws_bytes(n_experts, rows, H, g.Fr, dtype));
   hipStream_t s = (hipStream_t)stream;
   // the combine's backward is folded into the experts' GEMMs: d_out's rows are gathered by row_token
-  // and scaled by their gates inside them, and X's rows likewise inside dW1's loads
-  TP_TRY(launch_moe_experts_bwd(dtype, n_experts, group_offsets, tokens, top_k, rows, H, g.Fr, X, gates, row_token,
-                                token_row, W1_r, W2_r, A1_r, Y_r, d_out, dXp, dW1_r, db1_r, dW2_r, dgates_r,
-                                experts_ws, s), "moe experts backward");
-  TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dXp, nullptr, token_row, rows, dX_r, s), "moe dispatch backward");
-  return TP_OK;
+  // and scaled by their gates inside them, and X's rows likewise inside dW1's loads.  The two weight
+  // gradients run on the side stream next to dA1, dX_perm and the dispatch's backward.
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = side_stream(s);
+  hipStream_t s2 = sd ? sd->s2 : s;
+  auto body = [&]() -> int {
+    TP_TRY(launch_moe_experts_bwd(dtype, n_experts, group_offsets, tokens, top_k, rows, H, g.Fr, X, gates, row_token,
+                                  token_row, W1_r, W2_r, A1_r, Y_r, d_out, dXp, dW1_r, db1_r, dW2_r, dgates_r,
+                                  experts_ws, s, s2, sd ? sd->fork : nullptr, sd ? sd->mid : nullptr),
+           "moe experts backward");
+    TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, dXp, nullptr, token_row, rows, dX_r, s),
+           "moe dispatch backward");
+    return TP_OK;
+  };
+  const int rc = body();
+  if (sd) {   // join even after a failed launch, so the side stream never runs ahead of the caller's
+    TP_TRY(hipEventRecord(sd->join, s2), "join");
+    TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
+  }
+  return rc;
 }
 
 int tp_moe_route_bwd(int tokens, int n_experts, int top_k, const float* logits, const int* expert_idx,

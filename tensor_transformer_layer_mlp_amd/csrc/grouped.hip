@@ -323,9 +323,10 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
                                   const void* X, const float* gates, const int* row_token, const int* token_row,
                                   const void* W1, const void* W2, const void* A1, const void* Y, const void* d_out,
                                   void* dX_perm, void* dW1, void* db1, void* dW2, float* dgates, void* ws,
-                                  hipStream_t s) {
+                                  hipStream_t s, hipStream_t s2, hipEvent_t ev_gates, hipEvent_t ev_dA1) {
   if (groups <= 0) return hipSuccess;
   if (groups > 65535) return hipErrorInvalidValue;   // the column sum's grid y (checked before any launch)
+  const bool side = s2 != s;
   const double es = dtype == DT_BF16 ? 2.0 : 4.0;
   auto a256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
   char* w = (char*)ws;
@@ -379,6 +380,13 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
   if (e != hipSuccess) return e;
   const double fl = 2.0 * rows * (double)Fr * H;
   const double wts = es * (double)groups * H * Fr;
+  // s: dA1, the gate gradients, db1, dX_perm;  s2 (when given): dW2 (after the plan and the row gates),
+  // then dW1 (after dA1)
+  if (side) {
+    e = hipEventRecord(ev_gates, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev_gates, 0);
+    if (e != hipSuccess) return e;
+  }
   if (rows > 0) {
     // d_out's unique rows, A1 and Y read, dA1 written, the row dots
     ProfScope p(tiled ? "gemm_bf16_grouped<dout.W2t, gather, gate+dgelu>" : "gemm_generic_grouped<dout.W2t, gather, gate+dgelu>",
@@ -387,16 +395,20 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
               : launch_gemm_generic_grouped(ga, off_s, prefix1, tiles1, groups, (long)Fr * H, 0, (int)maxmt1, s);
     if (e != hipSuccess) return e;
   }
-  e = launch_moe_dgates(tokens, k, rows, ntiles, row_dot, token_row, off_s, groups, dgates, s);
-  if (e != hipSuccess) return e;
-  {
-    const bool t2 = gemm_bf16_grouped_k_eligible(gw2);
-    ProfScope p(t2 ? "gemm_bf16_grouped_k<Ygt.dout, gather>" : "gemm_generic_grouped_k<Ygt.dout, gather>", s, fl,
-                es * ((double)rows * Fr + (double)tokens * H) + wts + 4.0 * rows);
-    e = t2 ? launch_gemm_bf16_grouped_k(gw2, off_s, groups, (long)Fr * H, s)
-           : launch_gemm_generic_grouped_k(gw2, off_s, groups, (long)Fr * H, s);
+  if (side) {
+    e = hipEventRecord(ev_dA1, s);
     if (e != hipSuccess) return e;
   }
+  {
+    const bool t2 = gemm_bf16_grouped_k_eligible(gw2);
+    ProfScope p(t2 ? "gemm_bf16_grouped_k<Ygt.dout, gather>" : "gemm_generic_grouped_k<Ygt.dout, gather>", s2, fl,
+                es * ((double)rows * Fr + (double)tokens * H) + wts + 4.0 * rows);
+    e = t2 ? launch_gemm_bf16_grouped_k(gw2, off_s, groups, (long)Fr * H, s2)
+           : launch_gemm_generic_grouped_k(gw2, off_s, groups, (long)Fr * H, s2);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_moe_dgates(tokens, k, rows, ntiles, row_dot, token_row, off_s, groups, dgates, s);
+  if (e != hipSuccess) return e;
   {
     ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
     dim3 grid((Fr + 63) / 64, groups);
@@ -405,12 +417,16 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (side) {
+    e = hipStreamWaitEvent(s2, ev_dA1, 0);
+    if (e != hipSuccess) return e;
+  }
   {
     const bool t1 = gemm_bf16_grouped_k_eligible(gw1);
-    ProfScope p(t1 ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1, gather>", s, fl,
+    ProfScope p(t1 ? "gemm_bf16_grouped_k<Xt.dA1, gather>" : "gemm_generic_grouped_k<Xt.dA1, gather>", s2, fl,
                 es * ((double)tokens * H + (double)rows * Fr) + wts + 4.0 * rows);
-    e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s)
-           : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s);
+    e = t1 ? launch_gemm_bf16_grouped_k(gw1, off_s, groups, (long)H * Fr, s2)
+           : launch_gemm_generic_grouped_k(gw1, off_s, groups, (long)H * Fr, s2);
     if (e != hipSuccess) return e;
   }
   if (rows > 0) {

@@ -140,11 +140,13 @@ hipError_t launch_moe_dgates(int tokens, int k, int rows, int ntiles, const floa
                              const int* off, int groups, float* dgates, hipStream_t s);
 // The MoE experts' backward from the output gradient (no materialised dZ): see grouped.hip.
 size_t moe_experts_bwd_ws_bytes(int groups, int rows, int H, int Fr, int dtype);
+// With s2 != s, the weight gradients run on s2 (dW2 after ev_gates, dW1 after ev_dA1, both recorded on
+// s here); the caller forks s2 off s before and joins it back after.
 hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tokens, int k, int rows, int H, int Fr,
                                   const void* X, const float* gates, const int* row_token, const int* token_row,
                                   const void* W1, const void* W2, const void* A1, const void* Y, const void* d_out,
                                   void* dX_perm, void* dW1, void* db1, void* dW2, float* dgates, void* ws,
-                                  hipStream_t s);
+                                  hipStream_t s, hipStream_t s2, hipEvent_t ev_gates, hipEvent_t ev_dA1);
 hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, const int* experts,
                                 const float* dgates, float* d_logits, hipStream_t s);
 
