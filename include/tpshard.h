@@ -28,9 +28,10 @@
  *  - `dtype`: TP_BF16 (bf16 in/out, fp32 accumulation and fp32 softmax/GeLU) or TP_F32 (fp32
  *    throughout: the check mode).  Every output has that type except LSE and workspace, fp32.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is ordered on it; calls return
- *    without synchronising.  Outputs are overwritten (never accumulated into).  The backward
- *    calls with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_out_shard_bwd,
- *    tp_moe_shard_bwd) may
+ *    without synchronising.  Outputs are overwritten (never accumulated into).  The calls
+ *    with independent GEMMs (tp_mlp_shard_bwd, tp_qkv_shard_bwd, tp_attn_out_shard_bwd,
+ *    tp_moe_shard_bwd; tp_mlp_grouped_shard_fwd and tp_moe_shard_fwd, which run the second half
+ *    of the experts there) may
  *    run some of them on a library-owned side stream (one per caller stream and device, created on
  *    first use outside graph capture, default priority; for up to 64 such pairs, after which calls
  *    from further streams run serially on `stream`), forked from and joined back into `stream` with

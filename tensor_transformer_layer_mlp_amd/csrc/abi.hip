@@ -665,6 +665,28 @@ int tp_residual_ln_bwd(int tp_size, int rank, int sequence_parallel, int T, int 
   return TP_OK;
 }
 
+// Workspace of the grouped forward: room for the plans of both halves (see grouped_fwd below).
+static size_t grouped_fwd_ws(int groups, int rows) { return mlp_grouped_ws_bytes(groups, rows, true); }
+
+// The grouped expert MLP forward.  With a side stream and two or more groups, the second half of
+// the groups runs there: the halves' rows, weights and outputs are disjoint, so each half's fc2
+// overlaps the other's fc1 and the tail waves of each GEMM share the chip with the other half's
+// tiles.  Every element's arithmetic is the same as in one launch over all groups.
+static int grouped_fwd(int dtype, int groups, const int* off, int rows, int H, int Fr, const void* X,
+                       const void* W1, const void* b1, const void* W2, void* Z, void* A1, void* Y, void* ws,
+                       hipStream_t s, const int* row_token, int tokens) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = groups >= 2 ? side_stream(s) : nullptr;
+  const hipError_t e = launch_mlp_grouped(dtype, groups, off, rows, H, Fr, X, W1, b1, W2, Z, A1, Y, ws, s,
+                                          row_token, tokens, sd ? sd->s2 : nullptr, sd ? sd->fork : nullptr);
+  if (sd != nullptr) {   // joined even after a failed launch, so the side stream never outruns s
+    TP_TRY(hipEventRecord(sd->join, sd->s2), "join");
+    TP_TRY(hipStreamWaitEvent(s, sd->join, 0), "join");
+  }
+  TP_TRY(e, "grouped mlp");
+  return TP_OK;
+}
+
 int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* group_offsets, int rows,
                              int H, int F_group, int dtype, const void* X_perm, const void* W1_r,
                              const void* b1_r, const void* W2_r, void* Z_r, void* A1_r, void* Y_r,
@@ -677,13 +699,12 @@ int tp_mlp_grouped_shard_fwd(int tp_size, int rank, int n_groups, const int* gro
   TP_CHECK(((uintptr_t)group_offsets & 3u) == 0, TP_EALIGN, "group_offsets is not 4-byte aligned");
   NEED(X_perm, "X_perm", (long)rows); NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1);
   NEED(Z_r, "Z_r", (long)rows); NEED(Y_r, "Y_r", (long)rows); MAYBE(A1_r, "A1_r");
-  const size_t need = align256(grouped_ws_bytes(n_groups, rows));
+  const size_t need = grouped_fwd_ws(n_groups, rows);
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
-  TP_TRY(launch_mlp_grouped(dtype, n_groups, group_offsets, rows, H, g.Fr, X_perm, W1_r, b1_r, W2_r, Z_r,
-                            A1_r, Y_r, workspace, (hipStream_t)stream), "grouped mlp");
-  return TP_OK;
+  return grouped_fwd(dtype, n_groups, group_offsets, rows, H, g.Fr, X_perm, W1_r, b1_r, W2_r, Z_r, A1_r, Y_r,
+                     workspace, (hipStream_t)stream, nullptr, 0);
 }
 
 int tp_moe_route(int tokens, int n_experts, int top_k, const float* logits, float* gates, int* expert_idx,
@@ -725,13 +746,14 @@ int tp_moe_shard_fwd(int tp_size, int rank, int tokens, int H, int n_experts, in
   NEED4(row_token, "row_token", n); NEED4(token_row, "token_row", n);
   NEED(W1_r, "W1_r", 1); NEED(b1_r, "b1_r", 1); NEED(W2_r, "W2_r", 1); NEED(out_r, "out_r", (long)tokens * H);
   NEED(Z_r, "Z_r", n * H); NEED(Y_r, "Y_r", n); MAYBE(A1_r, "A1_r");
-  const size_t need = align256(grouped_ws_bytes(n_experts, rows));
+  const size_t need = grouped_fwd_ws(n_experts, rows);
   TP_CHECK(workspace != nullptr, TP_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   TP_CHECK(workspace_bytes >= need, TP_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   TP_CHECK(((uintptr_t)workspace & 255u) == 0, TP_EALIGN, "workspace is not 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  TP_TRY(launch_mlp_grouped(dtype, n_experts, group_offsets, rows, H, g.Fr, X, W1_r, b1_r, W2_r, Z_r, A1_r, Y_r,
-                            workspace, s, row_token, tokens), "moe experts");
+  st = grouped_fwd(dtype, n_experts, group_offsets, rows, H, g.Fr, X, W1_r, b1_r, W2_r, Z_r, A1_r, Y_r, workspace, s,
+                   row_token, tokens);
+  if (st) return st;
   TP_TRY(launch_moe_combine(dtype, tokens, top_k, H, Z_r, gates, token_row, rows, out_r, s), "moe combine");
   return TP_OK;
 }
@@ -914,7 +936,7 @@ size_t tp_workspace_bytes(const char* fn, int tp_size, int rank, int B, int S, i
   }
   if (strcmp(fn, "tp_mlp_grouped_shard_fwd") == 0 || strcmp(fn, "tp_moe_shard_fwd") == 0) {
     if (B < 0 || S < 0 || (long)B * S > INT_MAX / 4 || n_heads < 1 || n_heads > (1 << 20)) return 0;
-    return align256(grouped_ws_bytes(n_heads, B * S));
+    return grouped_fwd_ws(n_heads, B * S);
   }
   if (strcmp(fn, "tp_residual_ln_bwd") == 0) {
     int rows = 0;

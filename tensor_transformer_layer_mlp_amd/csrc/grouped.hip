@@ -146,12 +146,45 @@ static hipError_t run_plan(const int* off, int groups, int rows, int bm1, int bm
   return hipGetLastError();
 }
 
+// fc1 then fc2 of the groups [0, groups) of a plan, on s.
+static hipError_t grouped_pair(bool tiled, const GemmDesc& fc1, const GemmDesc& fc2, const int* off_s,
+                               const int* prefix1, const int* prefix2, const int* tiles1, const int* tiles2,
+                               int groups, int maxmt1, int maxmt2, double f1, double by1, double by2,
+                               hipStream_t s) {
+  const int H = fc1.K, Fr = fc1.N;
+  const bool gather = fc1.a_rows != nullptr;
+  if (tiled) {
+    {
+      ProfScope p(gather ? "gemm_bf16_grouped<fc1, gather, bias+gelu>" : "gemm_bf16_grouped<fc1, bias+gelu>",
+                  s, f1, by1);
+      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, maxmt1, s);
+      if (e != hipSuccess) return e;
+    }
+    ProfScope p("gemm_bf16_grouped<fc2>", s, f1, by2);
+    return launch_gemm_bf16_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, maxmt2, s);
+  }
+  {
+    ProfScope p(gather ? "gemm_generic_grouped<fc1, gather, bias+gelu>" : "gemm_generic_grouped<fc1, bias+gelu>",
+                s, f1, by1);
+    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, maxmt1, s);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
+  return launch_gemm_generic_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, maxmt2, s);
+}
+
+size_t mlp_grouped_ws_bytes(int groups, int rows, bool split) {
+  const size_t one = (grouped_ws_bytes(groups, rows) + 255) & ~(size_t)255;
+  return split ? 2 * one : one;
+}
+
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
-                              void* A1, void* Y, void* ws, hipStream_t s, const int* row_token, int tokens) {
+                              void* A1, void* Y, void* ws, hipStream_t s, const int* row_token, int tokens,
+                              hipStream_t s2, hipEvent_t ev_plan) {
   if (rows <= 0) return hipSuccess;
   int *off_s, *prefix1, *prefix2, *tiles1, *tiles2;   // plan (fc1's tile height, then fc2's)
-  const double es = dtype == DT_BF16 ? 2.0 : 4.0;
+  const size_t es = dtype == DT_BF16 ? 2 : 4;
 
   GemmDesc fc1;
   memset(&fc1, 0, sizeof(fc1));
@@ -186,24 +219,33 @@ hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, i
   const double by1 = es * ((double)(row_token ? tokens : rows) * H + (double)groups * H * Fr +
                            (A1 ? 2.0 : 1.0) * rows * Fr) + (row_token ? 4.0 * rows : 0.0);
   const double by2 = es * ((double)rows * Fr + (double)groups * Fr * H + (double)rows * H);
-  if (tiled) {
-    {
-      ProfScope p(row_token ? "gemm_bf16_grouped<fc1, gather, bias+gelu>" : "gemm_bf16_grouped<fc1, bias+gelu>",
-                  s, f1, by1);
-      hipError_t e = launch_gemm_bf16_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
-      if (e != hipSuccess) return e;
-    }
-    ProfScope p("gemm_bf16_grouped<fc2>", s, f1, by2);
-    return launch_gemm_bf16_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, (int)maxmt2, s);
-  }
-  {
-    ProfScope p(row_token ? "gemm_generic_grouped<fc1, gather, bias+gelu>" : "gemm_generic_grouped<fc1, bias+gelu>",
-                s, f1, by1);
-    hipError_t e = launch_gemm_generic_grouped(fc1, off_s, prefix1, tiles1, groups, (long)H * Fr, Fr, (int)maxmt1, s);
-    if (e != hipSuccess) return e;
-  }
-  ProfScope p("gemm_generic_grouped<fc2>", s, f1, by2);
-  return launch_gemm_generic_grouped(fc2, off_s, prefix2, tiles2, groups, (long)Fr * H, 0, (int)maxmt2, s);
+  if (s2 == nullptr || s2 == s || groups < 2)
+    return grouped_pair(tiled, fc1, fc2, off_s, prefix1, prefix2, tiles1, tiles2, groups, (int)maxmt1, (int)maxmt2,
+                        f1, by1, by2, s);
+
+  // Two halves of the groups: [0, h) on s with the plan above (its first h groups and their tiles
+  // are a plan of their own), [h, groups) on s2 with a second plan over the sanitised offsets from
+  // h on (already clamped and non-decreasing, so that plan keeps them as they are).  The halves'
+  // rows, weights and outputs are disjoint; every element is computed as in one launch.  (The
+  // figures handed to the per-launch timing are split evenly; the caller does not split while it
+  // is on.)
+  const int h = groups / 2;
+  hipError_t e = hipEventRecord(ev_plan, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev_plan, 0);
+  if (e != hipSuccess) return e;
+  int *off_b, *prefix1_b, *prefix2_b, *tiles1_b, *tiles2_b;
+  e = run_plan(off_s + h, groups - h, rows, bm1, bm2, (char*)ws + mlp_grouped_ws_bytes(groups, rows, false),
+               &off_b, &prefix1_b, &prefix2_b, &tiles1_b, &tiles2_b, s2);
+  if (e != hipSuccess) return e;
+  GemmDesc fc1b = fc1, fc2b = fc2;
+  fc1b.B = (const char*)W1 + (size_t)h * H * Fr * es;
+  fc1b.bias = (const char*)b1 + (size_t)h * Fr * es;
+  fc2b.B = (const char*)W2 + (size_t)h * Fr * H * es;
+  e = grouped_pair(tiled, fc1, fc2, off_s, prefix1, prefix2, tiles1, tiles2, h, (int)maxmt1, (int)maxmt2,
+                   f1 / 2, by1 / 2, by2 / 2, s);
+  if (e != hipSuccess) return e;
+  return grouped_pair(tiled, fc1b, fc2b, off_b, prefix1_b, prefix2_b, tiles1_b, tiles2_b, groups - h, (int)maxmt1,
+                      (int)maxmt2, f1 / 2, by1 / 2, by2 / 2, s2);
 }
 
 // Backward of launch_mlp_grouped on expert-sorted operands, expert by expert (rows [off[e], off[e+1])):

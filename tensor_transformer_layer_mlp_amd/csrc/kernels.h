@@ -92,11 +92,14 @@ hipError_t launch_attn_bwd(int dtype, int B, int S, int nh, int d, const void* q
 // Grouped expert MLP shard (rows [off[e], off[e+1]) use expert e's weights); off is device memory.
 size_t grouped_ws_bytes(int groups, int rows);
 // With row_token set, row r of the expert-sorted matrix is row row_token[r] of X (tokens rows),
-// gathered inside fc1's operand loads.
+// gathered inside fc1's operand loads.  With s2 (!= s) and two or more groups, the second half of
+// the groups runs on s2 (forked off s after the plan with ev_plan; the caller joins s2 back) and ws
+// holds mlp_grouped_ws_bytes(groups, rows, true) bytes, 256-byte aligned.
+size_t mlp_grouped_ws_bytes(int groups, int rows, bool split);
 hipError_t launch_mlp_grouped(int dtype, int groups, const int* off, int rows, int H, int Fr,
                               const void* X, const void* W1, const void* b1, const void* W2, void* Z,
                               void* A1, void* Y, void* ws, hipStream_t s, const int* row_token = nullptr,
-                              int tokens = 0);
+                              int tokens = 0, hipStream_t s2 = nullptr, hipEvent_t ev_plan = nullptr);
 
 // Backward of launch_mlp_grouped on expert-sorted operands (dX may alias dZ); dA1 [rows, Fr] is
 // caller scratch; ws as for the forward.  dW1 [groups, H, Fr], db1 [groups, Fr], dW2 [groups, Fr, H].
