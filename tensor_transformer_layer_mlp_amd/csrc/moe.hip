@@ -3,7 +3,8 @@
 //
 //   moe_topk_kernel     a workgroup of 16 waves owns a chunk of 64 consecutive tokens, one wave per
 //                       token at a time: the token's logits sit in registers (E/64 per lane); wave max and Σ exp
-//                       give the softmax; k rounds of a wave arg-max over (logit, id) pick the
+//                       give the softmax; k rounds of a wave arg-max over (logit, id) (cross-lane
+//                       exchanges on the VALU: DPP and permlane swaps, no LDS) pick the
 //                       experts, the larger logit first and the lower id on equal logits.  The choice
 //                       compares the fp32 logits themselves (softmax is monotone), so no rounding of
 //                       the probabilities can reorder it.  The chunk's per-expert counts (LDS integer
@@ -44,6 +45,75 @@ constexpr int MOE_CHUNK = 64;                   // tokens per routing chunk
 
 constexpr int TOPK_THREADS = 1024;
 
+// Cross-lane exchanges for wave-wide reductions without LDS traffic.  Step i hands lane l the value
+// of a partner: l ^ 1 and l ^ 2 (DPP quad permutes), the mirror of l in its 8-lane half-row and in its
+// 16-lane row (DPP row_half_mirror, row_mirror), then l ^ 16 and l ^ 32 (v_permlane16/32_swap).  Each
+// step pairs the groups the earlier steps have combined, so after all six an associative and
+// commutative operation has combined the 64 lanes in every lane.  The two swaps return {own value,
+// partner's value} in an order that depends on the lane; a commutative combine of both is the same.
+template <int STEP>
+__device__ __forceinline__ unsigned dpp_partner(unsigned v) {
+  static_assert(STEP >= 0 && STEP < 4, "DPP steps");
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float wave_max(float m) {
+  m = fmaxf(m, __uint_as_float(dpp_partner<0>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<1>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<2>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<3>(__float_as_uint(m))));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum(float z) {
+  z += __uint_as_float(dpp_partner<0>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<1>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<2>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<3>(__float_as_uint(z)));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  z = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Order key of a (logit, expert id) candidate: a larger logit, then a lower id, gives a larger key,
+// so one unsigned 64-bit comparison orders candidates exactly as the fp32 comparison of the logits
+// (ties to the lower id) does.  High word: the logit's bits mapped to an unsigned order (negative
+// values reversed, non-negative ones above them; −0 is taken as +0, which the float comparison
+// treats as equal); low word: ~id.  Key 0 lies below every candidate (a taken or absent entry).
+__device__ __forceinline__ unsigned long long cand_key(float v, int e) {
+  const unsigned u = v == 0.f ? 0u : __float_as_uint(v);
+  const unsigned hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)hi << 32) | (unsigned)~e;
+}
+__device__ __forceinline__ float key_logit(unsigned long long k) {
+  const unsigned hi = (unsigned)(k >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+__device__ __forceinline__ int key_id(unsigned long long k) { return (int)~(unsigned)k; }
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+template <int STEP>
+__device__ __forceinline__ unsigned long long key_step(unsigned long long k) {
+  const unsigned lo = dpp_partner<STEP>((unsigned)k), hi = dpp_partner<STEP>((unsigned)(k >> 32));
+  return umax64(k, ((unsigned long long)hi << 32) | lo);
+}
+// The largest key of the wave, in every lane (branch-free selects).
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  k = key_step<0>(k);
+  k = key_step<1>(k);
+  k = key_step<2>(k);
+  k = key_step<3>(k);
+  auto rl = __builtin_amdgcn_permlane16_swap((unsigned)k, (unsigned)k, false, false);
+  auto rh = __builtin_amdgcn_permlane16_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+  k = umax64(((unsigned long long)rh[0] << 32) | rl[0], ((unsigned long long)rh[1] << 32) | rl[1]);
+  rl = __builtin_amdgcn_permlane32_swap((unsigned)k, (unsigned)k, false, false);
+  rh = __builtin_amdgcn_permlane32_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+  return umax64(((unsigned long long)rh[0] << 32) | rl[0], ((unsigned long long)rh[1] << 32) | rl[1]);
+}
+
 template <int EPL>
 __global__ __launch_bounds__(TOPK_THREADS) void moe_topk_kernel(int tokens, int E, int k, const float* __restrict__ logits,
                                                        float* __restrict__ gates, int* __restrict__ experts,
@@ -63,39 +133,26 @@ __global__ __launch_bounds__(TOPK_THREADS) void moe_topk_kernel(int tokens, int 
       v[i] = e < E ? row[e] : -INFINITY;
       m = fmaxf(m, v[i]);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    m = wave_max(m);
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (lane + 64 * i < E) z += expf(v[i] - m);
+    z = wave_sum(z);
+    unsigned long long key[EPL];                 // 0: absent or already chosen
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) z += __shfl_xor(z, s, 64);
-    unsigned taken = 0;                          // bit i: entry lane + 64 i already chosen
+    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? cand_key(v[i], lane + 64 * i) : 0ull;
     for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      unsigned long long best = key[0];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {   // ascending ids: > keeps the lower
-          bv = v[i];
-          bi = e;
-        }
-      }
+      for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
+      best = wave_max_key(best);
 #pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) {
-        const float ov = __shfl_xor(bv, s, 64);
-        const int oi = __shfl_xor(bi, s, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      for (int i = 0; i < EPL; ++i) key[i] = key[i] == best ? 0ull : key[i];   // ids are unique
       if (lane == 0) {
+        const int bi = key_id(best);
         experts[(long)t * k + j] = bi;
-        gates[(long)t * k + j] = expf(bv - m) / z;
+        gates[(long)t * k + j] = expf(key_logit(best) - m) / z;
         atomicAdd(&cnt[bi], 1);
       }
     }
