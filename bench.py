@@ -58,7 +58,7 @@ def parse():
                     help="also time torch.matmul on the nine GEMM shapes of the GPT-3 shard")
     ap.add_argument("--summarize", choices=["stats", "traffic", "mfma", "hbm", "lds", "blas"],
                     help="print a profile summary from rocprofv3 CSV output under --prof-dir, and exit")
-    ap.add_argument("--prof-dir", default="gpurun_out/prof",
+    ap.add_argument("--prof-dir", default="rocprof_out",
                     help="rocprofv3 output directory (stats: one kernel-trace run; traffic / hbm: the "
                          "directory holding pmc_fetch/ and pmc_write/; mfma: pmc_clk/ and pmc_mfma/)")
     ap.add_argument("--kernel", default="gemm_bf16_kernel<Tile<256, 256, 4, 2, 2, 64, 0>, false, false, 0>",
