@@ -48,8 +48,11 @@ struct AC {
   static constexpr int PB = 2 * DP;           // LDS row pitch, bytes
   static constexpr int RS = 256 / PB;         // rows per 256-byte bank window
   static constexpr int NC32 = PB / 32;        // 32-byte chunks per row
-  static constexpr int NKK = DP / 32;         // 32-wide k-steps over d
-  static constexpr int NDB = DP / 16;         // 16-wide d blocks of the outputs
+  // 32-wide k-steps over d and 16-wide d blocks of the outputs: those that hold a column below D
+  // (the tiles keep the padded pitch; the steps past D would multiply zeros: d = 96 takes 3 and 6,
+  // not 4 and 8)
+  static constexpr int NKK = (D + 31) / 32;
+  static constexpr int NDB = (D + 15) / 16;
   template <int R> static constexpr int tile() { return R * PB; }   // R-row tile, bytes
 };
 
