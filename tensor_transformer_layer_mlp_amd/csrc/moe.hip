@@ -1,10 +1,12 @@
 // MoE routing (top-k of the router's softmax, expert-sorted dispatch order) and the gate-weighted
 // combine of the experts' rows back to tokens.
 //
-//   moe_topk_kernel     a workgroup of 16 waves owns a chunk of 64 consecutive tokens, one wave per
-//                       token at a time: the token's logits sit in registers (E/64 per lane); wave max and Σ exp
-//                       give the softmax; k rounds of a wave arg-max over (logit, id) (cross-lane
-//                       exchanges on the VALU: DPP and permlane swaps, no LDS) pick the
+//   moe_topk_rows_kernel (E <= 256) / moe_topk_kernel: a workgroup of 16 waves owns a chunk of 64
+//                       consecutive tokens, one token per 16-lane row (larger E: a wave per token,
+//                       one at a time): the token's logits sit in registers (E/16 or E/64 per lane);
+//                       max and Σ exp over the row (or wave) give the softmax; k rounds of an arg-max
+//                       over (logit, id) (cross-lane exchanges on the VALU: DPP and permlane swaps, no
+//                       LDS) pick the
 //                       experts, the larger logit first and the lower id on equal logits.  The choice
 //                       compares the fp32 logits themselves (softmax is monotone), so no rounding of
 //                       the probabilities can reorder it.  The chunk's per-expert counts (LDS integer
@@ -155,6 +157,70 @@ __global__ __launch_bounds__(TOPK_THREADS) void moe_topk_kernel(int tokens, int 
         gates[(long)t * k + j] = expf(key_logit(best) - m) / z;
         atomicAdd(&cnt[bi], 1);
       }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) counts[(long)blockIdx.x * E + e] = cnt[e];
+}
+
+// The same selection with one token per 16-lane row (four tokens per wave at once), for E <= 256:
+// lane i of a row holds entries i + 16j (EPR = E/16 of them), and every reduction is the four DPP
+// steps that stay inside the row (quad permutes, half-row and row mirrors).  A wave's tokens are
+// c0 + 4w .. c0 + 4w + 3; rows past the chunk's end compute but write nothing.
+template <int EPR>
+__global__ __launch_bounds__(TOPK_THREADS) void moe_topk_rows_kernel(int tokens, int E, int k,
+                                                                     const float* __restrict__ logits,
+                                                                     float* __restrict__ gates,
+                                                                     int* __restrict__ experts,
+                                                                     int* __restrict__ counts) {
+  constexpr int NW = TOPK_THREADS / 64;
+  static_assert(MOE_CHUNK == 4 * NW, "one token per 16-lane row of every wave");
+  __shared__ int cnt[MOE_MAX_E];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i = lane & 15;
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) cnt[e] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * MOE_CHUNK, c1 = min(tokens, c0 + MOE_CHUNK);
+  const int t = c0 + 4 * w + (lane >> 4);
+  const bool live = t < c1;
+  const float* row = logits + (long)(live ? t : c0) * E;   // c0 < tokens: a row that exists
+  float v[EPR];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < EPR; ++j) {
+    const int e = i + 16 * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+  m = fmaxf(m, __uint_as_float(dpp_partner<0>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<1>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<2>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<3>(__float_as_uint(m))));
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPR; ++j)
+    if (i + 16 * j < E) z += expf(v[j] - m);
+  z += __uint_as_float(dpp_partner<0>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<1>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<2>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<3>(__float_as_uint(z)));
+  unsigned long long key[EPR];                   // 0: absent or already chosen
+#pragma unroll
+  for (int j = 0; j < EPR; ++j) key[j] = i + 16 * j < E ? cand_key(v[j], i + 16 * j) : 0ull;
+  for (int j = 0; j < k; ++j) {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int q = 1; q < EPR; ++q) best = umax64(best, key[q]);
+    best = key_step<0>(best);
+    best = key_step<1>(best);
+    best = key_step<2>(best);
+    best = key_step<3>(best);
+#pragma unroll
+    for (int q = 0; q < EPR; ++q) key[q] = key[q] == best ? 0ull : key[q];   // ids are unique
+    if (i == 0 && live) {
+      const int bi = key_id(best);
+      experts[(long)t * k + j] = bi;
+      gates[(long)t * k + j] = expf(key_logit(best) - m) / z;
+      atomicAdd(&cnt[bi], 1);
     }
   }
   __syncthreads();
@@ -547,6 +613,13 @@ hipError_t topk_t(int tokens, int E, int k, const float* logits, float* gates, i
                                                                                      experts, counts);
   return hipGetLastError();
 }
+template <int EPR>
+hipError_t topk_rows_t(int tokens, int E, int k, const float* logits, float* gates, int* experts, int* counts,
+                       hipStream_t s) {
+  moe_topk_rows_kernel<EPR><<<(tokens + MOE_CHUNK - 1) / MOE_CHUNK, TOPK_THREADS, 0, s>>>(tokens, E, k, logits,
+                                                                                          gates, experts, counts);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -569,9 +642,10 @@ hipError_t launch_moe_route(int tokens, int E, int k, const float* logits, float
   if (tokens > 0) {
     ProfScope p("moe_topk", s, 4.0 * tokens * E, 4.0 * tokens * E + 8.0 * n + 4.0 * chunks * E);
     hipError_t e;
-    if (E <= 64) e = topk_t<1>(tokens, E, k, logits, gates, expert_idx, counts, s);
-    else if (E <= 128) e = topk_t<2>(tokens, E, k, logits, gates, expert_idx, counts, s);
-    else if (E <= 256) e = topk_t<4>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    if (E <= 32) e = topk_rows_t<2>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 64) e = topk_rows_t<4>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 128) e = topk_rows_t<8>(tokens, E, k, logits, gates, expert_idx, counts, s);
+    else if (E <= 256) e = topk_rows_t<16>(tokens, E, k, logits, gates, expert_idx, counts, s);
     else if (E <= 512) e = topk_t<8>(tokens, E, k, logits, gates, expert_idx, counts, s);
     else e = topk_t<16>(tokens, E, k, logits, gates, expert_idx, counts, s);
     if (e != hipSuccess) return e;

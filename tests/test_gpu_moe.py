@@ -55,6 +55,23 @@ def test_moe_route(tokens, E, k, ties):
         assert_close(g["gates"], r["gates"], "f32", "gates")
 
 
+@pytest.mark.parametrize("E", [16, 128, 300])
+def test_moe_route_signed_zeros(E):
+    """Logits of +0.0 and -0.0 compare equal (the fp32 comparison the routing is defined by), so the
+    lower expert id wins between them whichever sign each has: rows mixing both signs of zero with
+    negative values, per expert count that takes each kernel form (rows of 16 lanes, whole waves)."""
+    tokens, k = 70, 6
+    lg = -np.abs(synth._rng(f"zeros_{E}", 0).standard_normal((tokens, E), dtype=np.float32)) - np.float32(1)
+    sel = synth._rng(f"zeros_{E}", 1).integers(0, 3, size=(tokens, E))
+    lg[sel == 0] = np.float32(0.0)
+    lg[sel == 1] = np.float32(-0.0)
+    g = _route_gpu(lg, k)
+    r = oracle.moe_route(lg, k)
+    assert np.array_equal(host(g["experts"]).astype(np.int64), r["experts"]), "expert choice"
+    assert np.array_equal(host(g["offsets"]).astype(np.int64), r["group_offsets"]), "group offsets"
+    assert_close(g["gates"], r["gates"], "f32", "gates")
+
+
 def _expert_weights(E, H, F_expert, tp, rank, dtype, std=0.05):
     f0, Fr = oracle.shard_range(F_expert, tp, rank)
     return Fr, dict(W1=synth.normal("moeW1", (E, H, Fr), std, dtype), b1=synth.normal("moeb1", (E, Fr), std, dtype),
