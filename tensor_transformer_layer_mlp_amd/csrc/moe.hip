@@ -598,11 +598,73 @@ __global__ __launch_bounds__(64 * RBWD_TOKENS) void moe_route_bwd_kernel(int tok
   }
 }
 
+// The same gradient with one token per 16-lane row (four per wave), for E <= 256: entries i + 16q
+// of the row in lane i, the row's max and Σ exp through the four row-local DPP steps, and every lane
+// reading the token's k choices itself (the same addresses across the row).  Rows past `tokens`
+// compute nothing and write nothing.
+template <int EPR>
+__global__ __launch_bounds__(256) void moe_route_bwd_rows_kernel(int tokens, int E, int k,
+                                                                 const float* __restrict__ logits,
+                                                                 const int* __restrict__ experts,
+                                                                 const float* __restrict__ dgates,
+                                                                 float* __restrict__ d_logits) {
+  const int lane = threadIdx.x & 63, i = lane & 15;
+  const long t = (long)blockIdx.x * 16 + (threadIdx.x >> 4);   // 16 tokens per 256-thread workgroup
+  const bool live = t < tokens;
+  const float* row = logits + (live ? t : 0) * E;               // tokens >= 1: a row that exists
+  float v[EPR];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < EPR; ++q) {
+    const int e = i + 16 * q;
+    v[q] = e < E ? row[e] : -INFINITY;
+    m = fmaxf(m, v[q]);
+  }
+  m = fmaxf(m, __uint_as_float(dpp_partner<0>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<1>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<2>(__float_as_uint(m))));
+  m = fmaxf(m, __uint_as_float(dpp_partner<3>(__float_as_uint(m))));
+  float z = 0.f;
+#pragma unroll
+  for (int q = 0; q < EPR; ++q) {
+    v[q] = (i + 16 * q) < E ? expf(v[q] - m) : 0.f;
+    z += v[q];
+  }
+  z += __uint_as_float(dpp_partner<0>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<1>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<2>(__float_as_uint(z)));
+  z += __uint_as_float(dpp_partner<3>(__float_as_uint(z)));
+  const float inv = 1.f / z;
+  if (!live) return;                           // no barrier follows
+  // s = Σ_j dg_j·p_{i_j}, and each entry's own gate gradient (0 if not chosen)
+  float sj = 0.f, dg[EPR];
+#pragma unroll
+  for (int q = 0; q < EPR; ++q) dg[q] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int ej = experts[t * k + j];
+    const float gj = dgates[t * k + j];
+    if (ej >= 0 && ej < E) sj += gj * (expf(row[ej] - m) * inv);
+#pragma unroll
+    for (int q = 0; q < EPR; ++q) dg[q] = ej == i + 16 * q ? gj : dg[q];
+  }
+#pragma unroll
+  for (int q = 0; q < EPR; ++q) {
+    const int e = i + 16 * q;
+    if (e < E) d_logits[t * E + e] = v[q] * inv * (dg[q] - sj);
+  }
+}
+
 template <int EPL>
 hipError_t route_bwd_t(int tokens, int E, int k, const float* logits, const int* experts, const float* dgates,
                        float* d_logits, hipStream_t s) {
   const int blocks = (tokens + RBWD_TOKENS - 1) / RBWD_TOKENS;
   moe_route_bwd_kernel<EPL><<<blocks, 64 * RBWD_TOKENS, 0, s>>>(tokens, E, k, logits, experts, dgates, d_logits);
+  return hipGetLastError();
+}
+template <int EPR>
+hipError_t route_bwd_rows_t(int tokens, int E, int k, const float* logits, const int* experts, const float* dgates,
+                            float* d_logits, hipStream_t s) {
+  moe_route_bwd_rows_kernel<EPR><<<(tokens + 15) / 16, 256, 0, s>>>(tokens, E, k, logits, experts, dgates, d_logits);
   return hipGetLastError();
 }
 
@@ -716,9 +778,10 @@ hipError_t launch_moe_route_bwd(int tokens, int E, int k, const float* logits, c
   if (E < 1 || E > MOE_MAX_E || k < 1 || k > MOE_MAX_K || k > E || tokens < 0) return hipErrorInvalidValue;
   if (tokens == 0) return hipSuccess;
   ProfScope p("moe_route_bwd", s, 6.0 * tokens * E, 8.0 * tokens * E + 8.0 * tokens * k);
-  if (E <= 64) return route_bwd_t<1>(tokens, E, k, logits, experts, dgates, d_logits, s);
-  if (E <= 128) return route_bwd_t<2>(tokens, E, k, logits, experts, dgates, d_logits, s);
-  if (E <= 256) return route_bwd_t<4>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 32) return route_bwd_rows_t<2>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 64) return route_bwd_rows_t<4>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 128) return route_bwd_rows_t<8>(tokens, E, k, logits, experts, dgates, d_logits, s);
+  if (E <= 256) return route_bwd_rows_t<16>(tokens, E, k, logits, experts, dgates, d_logits, s);
   if (E <= 512) return route_bwd_t<8>(tokens, E, k, logits, experts, dgates, d_logits, s);
   return route_bwd_t<16>(tokens, E, k, logits, experts, dgates, d_logits, s);
 }
