@@ -257,7 +257,7 @@ __global__ __launch_bounds__(512) void moe_scatter_kernel(int tokens, int k, con
                                                           const int* __restrict__ total, int E,
                                                           int* __restrict__ offsets, int* __restrict__ row_token,
                                                           int* __restrict__ token_row) {
-  __shared__ int ex[MOE_CHUNK * MOE_MAX_K];
+  __shared__ int cnts[9 * MOE_MAX_E];            // per-expert counts: passes done, then 8 waves
   __shared__ int off[MOE_MAX_E];
   // the experts' offsets: exclusive prefix of the totals, two experts per thread then a thread scan
   {
@@ -287,15 +287,41 @@ __global__ __launch_bounds__(512) void moe_scatter_kernel(int tokens, int k, con
   const int c0 = blockIdx.x * MOE_CHUNK, c1 = min(tokens, c0 + MOE_CHUNK);
   const int n = (c1 - c0) * k;                   // the chunk's entries, token-major
   const long first = (long)c0 * k;
-  for (int i = threadIdx.x; i < n; i += 512) ex[i] = experts[first + i];
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += 512) {
-    const int e = ex[i];
+  // An entry's rank among the chunk's earlier entries of its expert, in token order: pass p takes
+  // entries [512p, 512p + 512) as eight waves of 64; within a wave each lane counts the earlier lanes
+  // with its expert (readlane of every lane, no LDS), the waves' per-expert counts go to LDS (integer
+  // adds: order-free), and an entry's rank is the count of earlier passes, then of earlier waves of
+  // its pass, then of earlier lanes.
+  int* seen = cnts;                              // per-expert count of the passes done so far
+  int* wcnt = cnts + MOE_MAX_E;                  // [8 waves][E] counts of this pass
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 512) seen[e] = 0;
+  for (int p0 = 0; p0 < n; p0 += 512) {
+    for (int q = threadIdx.x; q < 8 * E; q += 512) wcnt[q] = 0;
+    __syncthreads();
+    const int i = p0 + threadIdx.x;
+    const int e = i < n ? experts[first + i] : -1;
+    int lrank = 0;
+    for (int q = 0; q < 64; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      lrank += (q < lane && eq == e) ? 1 : 0;
+    }
+    if (e >= 0) atomicAdd(&wcnt[w * E + e], 1);
+    __syncthreads();
     int rank = 0;
-    for (int q = 0; q < i; ++q) rank += ex[q] == e;
-    const int row = off[e] + base[(long)blockIdx.x * E + e] + rank;
-    row_token[row] = c0 + i / k;
-    token_row[first + i] = row;
+    if (e >= 0) {
+      rank = seen[e] + lrank;
+      for (int v = 0; v < w; ++v) rank += wcnt[v * E + e];
+      const int row = off[e] + base[(long)blockIdx.x * E + e] + rank;
+      row_token[row] = c0 + i / k;
+      token_row[first + i] = row;
+    }
+    __syncthreads();
+    for (int e2 = threadIdx.x; e2 < E; e2 += 512) {
+      int add = 0;
+      for (int v = 0; v < 8; ++v) add += wcnt[v * E + e2];
+      seen[e2] += add;
+    }
   }
 }
 
