@@ -9,6 +9,7 @@
 // grouped GEMM kernels launch an upper bound of ceil(rows / BM) + groups m-tiles and find their
 // expert by binary search in prefix[].
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -119,6 +120,41 @@ __global__ __launch_bounds__(256) void grouped_colsum_kernel(const T* __restrict
   __syncthreads();
   if (ph == 0 && c < cols)
     db[(long)e * cols + c] = from_f32<T>(((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]);
+}
+
+// The same sums with 16-byte loads, for rows whose width is a multiple of the vector (V = 8 bf16 or
+// 4 fp32): a workgroup of 1024 threads per (expert, 8·V columns); thread (phase ph < 128, vector
+// q < 8) sums the columns of vector q over rows r0 + ph, r0 + ph + 128, ... (a few rows each, all
+// loads in flight at once); then one thread per column adds the 128 phases in order, so the result
+// does not depend on timing.
+template <typename T, int V>
+__global__ __launch_bounds__(1024) void grouped_colsum_vec_kernel(const T* __restrict__ dA, int cols,
+                                                                  const int* __restrict__ off, T* __restrict__ db) {
+  using Vec = typename std::conditional<V == 8, bf16x8, f32x4>::type;
+  constexpr int NC = 8 * V, NP = 128;            // columns per workgroup, row phases
+  __shared__ float part[NP][NC + 1];
+  const int e = blockIdx.y, q = threadIdx.x & 7, ph = threadIdx.x >> 3;
+  const int c = blockIdx.x * NC + q * V;
+  const int r0 = off[e], r1 = off[e + 1];
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.f;
+  if (c < cols) {
+#pragma unroll 8
+    for (int r = r0 + ph; r < r1; r += NP) {
+      const Vec x = *(const Vec*)(dA + (long)r * cols + c);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += (float)x[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) part[ph][q * V + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < NC && blockIdx.x * NC + threadIdx.x < cols) {
+    float t = part[0][threadIdx.x];
+    for (int p = 1; p < NP; ++p) t += part[p][threadIdx.x];
+    db[(long)e * cols + blockIdx.x * NC + threadIdx.x] = from_f32<T>(t);
+  }
 }
 
 }  // namespace
@@ -315,9 +351,17 @@ hipError_t launch_mlp_grouped_bwd(int dtype, int groups, const int* off, int row
   }
   {
     ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
-    dim3 grid((Fr + 63) / 64, groups);
-    if (dtype == DT_BF16) grouped_colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
-    else grouped_colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dA1, Fr, off_s, (float*)db1);
+    if (dtype == DT_BF16 && Fr % 8 == 0)
+      grouped_colsum_vec_kernel<bf16, 8><<<dim3((Fr + 63) / 64, groups), 1024, 0, s>>>((const bf16*)dA1, Fr, off_s,
+                                                                                     (bf16*)db1);
+    else if (dtype != DT_BF16 && Fr % 4 == 0)
+      grouped_colsum_vec_kernel<float, 4><<<dim3((Fr + 31) / 32, groups), 1024, 0, s>>>((const float*)dA1, Fr, off_s,
+                                                                                       (float*)db1);
+    else if (dtype == DT_BF16)
+      grouped_colsum_kernel<bf16><<<dim3((Fr + 63) / 64, groups), 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
+    else
+      grouped_colsum_kernel<float><<<dim3((Fr + 63) / 64, groups), 256, 0, s>>>((const float*)dA1, Fr, off_s,
+                                                                                (float*)db1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -453,9 +497,17 @@ hipError_t launch_moe_experts_bwd(int dtype, int groups, const int* off, int tok
   if (e != hipSuccess) return e;
   {
     ProfScope p("grouped_colsum", s, (double)rows * Fr, es * ((double)rows * Fr + (double)groups * Fr));
-    dim3 grid((Fr + 63) / 64, groups);
-    if (dtype == DT_BF16) grouped_colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
-    else grouped_colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dA1, Fr, off_s, (float*)db1);
+    if (dtype == DT_BF16 && Fr % 8 == 0)
+      grouped_colsum_vec_kernel<bf16, 8><<<dim3((Fr + 63) / 64, groups), 1024, 0, s>>>((const bf16*)dA1, Fr, off_s,
+                                                                                     (bf16*)db1);
+    else if (dtype != DT_BF16 && Fr % 4 == 0)
+      grouped_colsum_vec_kernel<float, 4><<<dim3((Fr + 31) / 32, groups), 1024, 0, s>>>((const float*)dA1, Fr, off_s,
+                                                                                       (float*)db1);
+    else if (dtype == DT_BF16)
+      grouped_colsum_kernel<bf16><<<dim3((Fr + 63) / 64, groups), 256, 0, s>>>((const bf16*)dA1, Fr, off_s, (bf16*)db1);
+    else
+      grouped_colsum_kernel<float><<<dim3((Fr + 63) / 64, groups), 256, 0, s>>>((const float*)dA1, Fr, off_s,
+                                                                                (float*)db1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
