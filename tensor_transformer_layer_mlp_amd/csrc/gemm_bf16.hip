@@ -217,7 +217,7 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
     }
   } else if constexpr (Cfg::BM * Cfg::BN * 2 <= Cfg::STAGES * Cfg::STAGE) {
     // Staged epilogue: the finished tile goes through LDS (row pitch 2·BN bytes, 16-byte granule q of
-    // row r at q ^ (r & 7)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
+    // row r at q ^ (r & XM)) so that each store instruction writes whole rows: 64 lanes x 16 bytes of
     // two to four rows instead of 16-row x 32-byte scraps.  The stores are non-temporal: on the
     // write-bound expert GEMMs (2.15 GB of output rows, read once by the combine) that took the MoE
     // block's forward from 2.17 to 2.09 ms and its backward from 3.46 to 3.40; the dense GEMMs did
@@ -284,6 +284,9 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
       }
     }
     constexpr int RB = Cfg::BN * 2, NG = Cfg::BN / 8;   // row bytes, 16-byte granules per row
+    // the granule swizzle stays inside a row: r & 7 when a row holds a multiple of 8 granules, r & 3
+    // for the 224-wide tile's 28
+    constexpr int XM = NG % 8 == 0 ? 7 : (NG % 4 == 0 ? 3 : 0);
     auto stage_out = [&](bf16* out, bool gelu) {
       __syncthreads();              // the k loop (or the previous pass) is done with the LDS
 #pragma unroll
@@ -291,7 +294,7 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
           const int r = wm + 16 * i + r16, c = wn + 16 * j + g4;
-          const int ob = ((((c >> 3) ^ (r & 7)) << 4) | ((c & 7) << 1));
+          const int ob = ((((c >> 3) ^ (r & XM)) << 4) | ((c & 7) << 1));
           f32x4 a = acc[i][j];
           if (gelu)
             for (int e = 0; e < 4; ++e) a[e] = act_f(a[e], d.act);
@@ -304,7 +307,7 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, int m0, int n0, TP
         const int r = c / NG, q = c % NG;
         const int m = m0 + r, n = n0 + 8 * q;
         if (m < d.M && n < d.N)   // streaming store: output tiles are written once, not re-read here
-          __builtin_nontemporal_store(*(const TP_LDS bf16x8*)(lds + r * RB + ((q ^ (r & 7)) << 4)),
+          __builtin_nontemporal_store(*(const TP_LDS bf16x8*)(lds + r * RB + ((q ^ (r & XM)) << 4)),
                                       (bf16x8*)(out + (long)m * d.ldc + n));
       }
     };
@@ -538,8 +541,9 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
 // Each group waits for its own loads at the end of its following compute phase, so every load has two
 // phases to land, and a stage is only overwritten after both groups' reads of it have completed (the
 // memory phase ends with lgkmcnt(0) before its barrier).
-// The tile width BN is 192 (the dense GEMMs) or 256 (the grouped expert GEMMs, whose n extent is one
-// 256-wide shard): wave tiles of 64 x 96 or 64 x 128.
+// The tile width BN is 192 (the dense GEMMs), 224 (dense GEMMs whose n extent it covers in fewer
+// rounds of 256 tiles) or 256 (the grouped expert GEMMs, whose n extent is one 256-wide shard): wave
+// tiles of 64 x 96, 64 x 112 or 64 x 128.
 template <int BN_>
 struct PPCfg {
   static constexpr int BM = 256, BN = BN_, BKT = 64, NKK = 2, NT = 512, STAGES = 2;
@@ -550,7 +554,7 @@ struct PPCfg {
   static constexpr int A_HALF = HALF * BKT * 2;           // 16 KiB (either layout: pitch 128)
   static constexpr int B_OFF = 2 * A_HALF;
   static constexpr int STAGE = B_OFF + 256 * BKT * 2;     // B: BN rows (K-major) or pitch 256 (MN-major)
-  static_assert(BN == 192 || BN == 256, "tile widths");
+  static_assert(BN == 192 || BN == 224 || BN == 256, "tile widths");
 };
 using PPTile = PPCfg<192>;
 
@@ -656,9 +660,10 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmDesc& d, int m0, int n0, 
   store_tile<P, EPI>(d, m0, n0, lds, acc, P::HALF * g + wml, wn, wave, lane);
 }
 
-template <bool AK, bool BK, int EPI>
-__global__ __launch_bounds__(PPTile::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int BN, bool AK, bool BK, int EPI>
+__global__ __launch_bounds__(PPCfg<BN>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_pp_kernel(GemmDesc d, int tiles_m, int tiles_n) {
+  using PPTile = PPCfg<BN>;
   __shared__ __attribute__((aligned(1024))) char smem[PPTile::STAGES * PPTile::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -799,23 +804,26 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool AK, bool BK, int EPI>
+template <int BN, bool AK, bool BK, int EPI>
 hipError_t run_pp(const GemmDesc& d, hipStream_t s) {
+  using PPTile = PPCfg<BN>;
   const int tiles_m = (d.M + PPTile::BM - 1) / PPTile::BM, tiles_n = (d.N + PPTile::BN - 1) / PPTile::BN;
   const int ks = (EPI == EPI_F32 && d.ksplit > 1) ? d.ksplit : 1;
-  gemm_bf16_pp_kernel<AK, BK, EPI><<<tiles_m * tiles_n * ks, PPTile::NT, 0, s>>>(d, tiles_m, tiles_n);
+  gemm_bf16_pp_kernel<BN, AK, BK, EPI><<<tiles_m * tiles_n * ks, PPTile::NT, 0, s>>>(d, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
+template <int BN>
 hipError_t run_pp_cfg(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && !d.b_kmajor) {
-    if (d.epi == EPI_BIAS) return run_pp<true, false, EPI_BIAS>(d, s);
-    if (d.epi == EPI_BIAS_GELU) return run_pp<true, false, EPI_BIAS_GELU>(d, s);
-    if (d.epi == EPI_STORE) return run_pp<true, false, EPI_STORE>(d, s);
+    if (d.epi == EPI_BIAS) return run_pp<BN, true, false, EPI_BIAS>(d, s);
+    if (d.epi == EPI_BIAS_GELU) return run_pp<BN, true, false, EPI_BIAS_GELU>(d, s);
+    if (d.epi == EPI_STORE) return run_pp<BN, true, false, EPI_STORE>(d, s);
   } else if (d.a_kmajor && d.b_kmajor) {
-    if (d.epi == EPI_DGELU) return run_pp<true, true, EPI_DGELU>(d, s);
-    if (d.epi == EPI_STORE) return run_pp<true, true, EPI_STORE>(d, s);
-    if (d.epi == EPI_F32) return run_pp<true, true, EPI_F32>(d, s);
+    if (d.epi == EPI_DGELU) return run_pp<BN, true, true, EPI_DGELU>(d, s);
+    if (d.epi == EPI_STORE) return run_pp<BN, true, true, EPI_STORE>(d, s);
+    if constexpr (BN == 192)   // the split-k partials take the 192-wide tile only
+      if (d.epi == EPI_F32) return run_pp<BN, true, true, EPI_F32>(d, s);
   }
   // Xᵀ·dY (both operands MN-major) is not taken: two operands of transposed LDS reads make the memory
   // phase longer than the compute phase (measured 15% slower than the plain 256 x 192 kernel)
@@ -852,13 +860,14 @@ using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
 using C8 = Tile<256, 192, 4, 2, 2, 64>;   // 2 waves / SIMD, 64x96 per wave
 using C9 = Tile<256, 256, 4, 2, 2, 32>;   // the gathered weight gradient: k = 32 frees the registers
                                           // its row indices take (no spills; 14% faster than C0)
-// 9: the ping-pong 256 x 192 kernel (gemm_bf16_pp_kernel)
-constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256, 256};
-constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192, 192};
+// 9, 10: the ping-pong kernel (gemm_bf16_pp_kernel) on 256 x 192 and 256 x 224 tiles
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192, 192, 224};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95, 1.2};
+constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95, 1.2, 1.2};
 constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
-                                     "256x256k32s4", "256x256k32s5", "256x256w4", "256x192", "256x192pp"};
+                                     "256x256k32s4", "256x256k32s5", "256x256w4", "256x192", "256x192pp",
+                                     "256x224pp"};
 
 }  // namespace
 
@@ -904,8 +913,8 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
     *cfg = 0;
     return kTileName[0];
   }
-  for (int c : {9, 0, 8, 1, 2, 3}) {
-    if (c == 9 && !d.a_kmajor) continue;   // the ping-pong tile takes X·W and dY·Wᵀ only
+  for (int c : {9, 10, 0, 8, 1, 2, 3}) {
+    if ((c == 9 || c == 10) && !d.a_kmajor) continue;   // the ping-pong tiles take X·W and dY·Wᵀ only
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
     const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
     if (est < best_t * 0.999) { best_t = est; best = c; }
@@ -931,7 +940,8 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 6: return run_cfg<C6>(d, s);
     case 7: return run_cfg<C7>(d, s);
 #endif
-    case 9: return run_pp_cfg(d, s);
+    case 9: return run_pp_cfg<192>(d, s);
+    case 10: return run_pp_cfg<224>(d, s);
     default: return run_cfg<C8>(d, s);
   }
 }

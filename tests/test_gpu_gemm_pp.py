@@ -1,6 +1,7 @@
 """GPU parity of the large-problem GEMM tiles: the ping-pong 256 x 192 tile (two groups of four waves
-one phase apart) on X·W and dY·Wᵀ, and the 256 x 256 tile the weight gradients Xᵀ·dY take from
-4096 x 4096 outputs on.
+one phase apart) on X·W and dY·Wᵀ, its 256 x 224 form (taken where it covers the n extent in fewer
+rounds of 256 tiles), and the 256 x 256 tile the weight gradients Xᵀ·dY take from 4096 x 4096
+outputs on.
 
 The tile is chosen for large problems with a K-major A only, so these MLP shard shapes are sized to
 make the MLP's X·W and dY·Wᵀ GEMMs take it: M, N around 2100 (ragged against 256, 192 and 64), and in
@@ -22,16 +23,20 @@ pytestmark = pytest.mark.gpu
 PP_BIG = LayerWorkload("pp_b1_s2056_h2104_nh8_f4176_tp2", 1, 2056, 2104, 8, 4176, 2, (0, 1), 0.03)
 # fc2 and the MLP's dX with K = F_r = 40
 PP_K1 = LayerWorkload("ppk1_b1_s2056_h2104_nh8_f80_tp2", 1, 2056, 2104, 8, 80, 2, (1,), 0.03)
+# fc1 and dA1 at M = 1800 (8 m-tiles, ragged), N = F_r = 6680 (35 n-tiles of 192 = two rounds, 30 of
+# 224 = one; the last 224-wide tile holds 184 columns), K = H = 1000 (ragged against 64): the
+# 256 x 224 tile, whose epilogue swizzles 28 granules per row
+PP_224 = LayerWorkload("pp224_b1_s1800_h1000_nh8_f13360_tp2", 1, 1800, 1000, 8, 13360, 2, (0,), 0.03)
 
 
 def cases():
-    for wl in (PP_BIG, PP_K1):
+    for wl in (PP_BIG, PP_K1, PP_224):
         for r in wl.ranks:
             yield pytest.param(wl, r, id=f"{wl.name}-r{r}")
 
 
-def pp_launches():
-    return {tag: v[0] for tag, v in bd.tp_prof_collect().items() if "256x192pp" in tag}
+def pp_launches(tile="256x192pp"):
+    return {tag: v[0] for tag, v in bd.tp_prof_collect().items() if tile in tag}
 
 
 @pytest.mark.parametrize("wl,rank", list(cases()))
@@ -47,9 +52,10 @@ def test_mlp_fwd_pingpong(wl, rank):
         torch.cuda.synchronize()
     finally:
         bd.tp_prof_enable(False)
-    used = pp_launches()
-    # with F_r = 40 (PP_K1) fc1 (N = 40) takes another tile
-    expect = {PP_BIG.name: 2, PP_K1.name: 1}[wl.name]
+    wide = wl.name == PP_224.name
+    used = pp_launches("256x224pp" if wide else "256x192pp")
+    # with F_r = 40 (PP_K1) fc1 (N = 40) takes another tile; PP_224: fc1 on the 224-wide tile
+    expect = {PP_BIG.name: 2, PP_K1.name: 1, PP_224.name: 1}[wl.name]
     assert sum(used.values()) == expect, f"ping-pong launches {used}"
     ref = oracle.tp_mlp_shard_fwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("b1"),
                                   sh.f64("W2"), sh.f64("b2"))
@@ -73,9 +79,11 @@ def test_mlp_bwd_pingpong(wl, rank):
         torch.cuda.synchronize()
     finally:
         bd.tp_prof_enable(False)
-    used = pp_launches()
-    # dA1 and dX (the weight gradients are Xᵀ·dY); with F_r = 40 (PP_K1) dA1 (N = 40) takes another tile
-    expect = {PP_BIG.name: 2, PP_K1.name: 1}[wl.name]
+    wide = wl.name == PP_224.name
+    used = pp_launches("256x224pp" if wide else "256x192pp")
+    # dA1 and dX (the weight gradients are Xᵀ·dY); with F_r = 40 (PP_K1) dA1 (N = 40) takes another
+    # tile; PP_224: dA1 on the 224-wide tile
+    expect = {PP_BIG.name: 2, PP_K1.name: 1, PP_224.name: 1}[wl.name]
     assert sum(used.values()) == expect, f"ping-pong launches {used}"
     ref = oracle.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("W2"),
                                   sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
