@@ -541,9 +541,9 @@ void gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n) {
 // Each group waits for its own loads at the end of its following compute phase, so every load has two
 // phases to land, and a stage is only overwritten after both groups' reads of it have completed (the
 // memory phase ends with lgkmcnt(0) before its barrier).
-// The tile width BN is 192 (the dense GEMMs), 224 (dense GEMMs whose n extent it covers in fewer
-// rounds of 256 tiles) or 256 (the grouped expert GEMMs, whose n extent is one 256-wide shard): wave
-// tiles of 64 x 96, 64 x 112 or 64 x 128.
+// The tile width BN is 192 (the dense GEMMs), 160 or 224 (dense GEMMs whose n extent they cover in
+// fewer or fuller rounds of 256 tiles) or 256 (the grouped expert GEMMs, whose n extent is one 256-wide
+// shard): wave tiles of 64 x 96, 64 x 80, 64 x 112 or 64 x 128.
 template <int BN_>
 struct PPCfg {
   static constexpr int BM = 256, BN = BN_, BKT = 64, NKK = 2, NT = 512, STAGES = 2;
@@ -554,7 +554,7 @@ struct PPCfg {
   static constexpr int A_HALF = HALF * BKT * 2;           // 16 KiB (either layout: pitch 128)
   static constexpr int B_OFF = 2 * A_HALF;
   static constexpr int STAGE = B_OFF + 256 * BKT * 2;     // B: BN rows (K-major) or pitch 256 (MN-major)
-  static_assert(BN == 192 || BN == 224 || BN == 256, "tile widths");
+  static_assert(BN == 160 || BN == 192 || BN == 224 || BN == 256, "tile widths");
 };
 using PPTile = PPCfg<192>;
 
@@ -860,14 +860,14 @@ using C7 = Tile<256, 256, 2, 2, 2, 64>;   // 1 wave / SIMD, 128x128 per wave
 using C8 = Tile<256, 192, 4, 2, 2, 64>;   // 2 waves / SIMD, 64x96 per wave
 using C9 = Tile<256, 256, 4, 2, 2, 32>;   // the gathered weight gradient: k = 32 frees the registers
                                           // its row indices take (no spills; 14% faster than C0)
-// 9, 10: the ping-pong kernel (gemm_bf16_pp_kernel) on 256 x 192 and 256 x 224 tiles
-constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256, 256, 256};
-constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192, 192, 224};
+// 9, 10, 11: the ping-pong kernel (gemm_bf16_pp_kernel) on 256 x 192, 256 x 224 and 256 x 160 tiles
+constexpr int kTileM[] = {256, 256, 128, 128, 256, 256, 256, 256, 256, 256, 256, 256};
+constexpr int kTileN[] = {256, 128, 256, 128, 256, 256, 256, 256, 192, 192, 224, 160};
 // relative throughput per CU of each configuration on large shapes (measured on MI355X)
-constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95, 1.2, 1.2};
+constexpr double kTileRate[] = {1.0, 0.70, 0.70, 0.50, 1.0, 1.0, 1.0, 1.0, 0.95, 1.2, 1.2, 1.04};
 constexpr const char* kTileName[] = {"256x256", "256x128", "128x256", "128x128", "256x256k32s3",
                                      "256x256k32s4", "256x256k32s5", "256x256w4", "256x192", "256x192pp",
-                                     "256x224pp"};
+                                     "256x224pp", "256x160pp"};
 
 }  // namespace
 
@@ -913,8 +913,11 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
     *cfg = 0;
     return kTileName[0];
   }
-  for (int c : {9, 10, 0, 8, 1, 2, 3}) {
-    if ((c == 9 || c == 10) && !d.a_kmajor) continue;   // the ping-pong tiles take X·W and dY·Wᵀ only
+  for (int c : {9, 10, 11, 0, 8, 1, 2, 3}) {
+    if (c >= 9 && !d.a_kmajor) continue;   // the ping-pong tiles take X·W and dY·Wᵀ only
+    // the 160-wide tile paid only on a long k loop (the GPT-3 tp=8 QKV forward, k = 12288: 246 ->
+    // 237 us, 232 tiles instead of 192); at k = 1600 and 3072 it was 1% slower than 192
+    if (c == 11 && d.K < 8192) continue;
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
     const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
     if (est < best_t * 0.999) { best_t = est; best = c; }
@@ -942,6 +945,7 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
 #endif
     case 9: return run_pp_cfg<192>(d, s);
     case 10: return run_pp_cfg<224>(d, s);
+    case 11: return run_pp_cfg<160>(d, s);
     default: return run_cfg<C8>(d, s);
   }
 }

@@ -1,6 +1,6 @@
 """GPU parity of the large-problem GEMM tiles: the ping-pong 256 x 192 tile (two groups of four waves
 one phase apart) on X·W and dY·Wᵀ, its 256 x 224 form (taken where it covers the n extent in fewer
-rounds of 256 tiles), and the 256 x 256 tile the weight gradients Xᵀ·dY take from 4096 x 4096
+rounds of 256 tiles) and 256 x 160 form (long k loops), and the 256 x 256 tile the weight gradients Xᵀ·dY take from 4096 x 4096
 outputs on.
 
 The tile is chosen for large problems with a K-major A only, so these MLP shard shapes are sized to
@@ -27,6 +27,11 @@ PP_K1 = LayerWorkload("ppk1_b1_s2056_h2104_nh8_f80_tp2", 1, 2056, 2104, 8, 80, 2
 # 224 = one; the last 224-wide tile holds 184 columns), K = H = 1000 (ragged against 64): the
 # 256 x 224 tile, whose epilogue swizzles 28 granules per row
 PP_224 = LayerWorkload("pp224_b1_s1800_h1000_nh8_f13360_tp2", 1, 1800, 1000, 8, 13360, 2, (0,), 0.03)
+# the QKV forward at k = H = 8200 (ragged against 64; a k loop long enough for the 160-wide tile),
+# M = T = 2000 (8 m-tiles, the last 208 rows: the GPT-3 shard's tile rows, where the narrower tiles
+# would take more rounds), N = one head of 3 x 1640 columns = 4920 (31 n-tiles of 160, the last one
+# 120 wide; the epilogue swizzles 20 granules per row)
+PP_160 = LayerWorkload("pp160_b1_s2000_h8200_nh5_f40_tp5", 1, 2000, 8200, 5, 40, 5, (0,), 0.01)
 
 
 def cases():
@@ -195,3 +200,22 @@ def test_weight_gradients_split_k(rank):
     torch.cuda.synchronize()
     for k in ("dW1", "dW2"):
         assert torch.equal(o[k], again[k]), f"{k}: the slice sum is in a fixed order"
+
+
+def test_qkv_fwd_160_tile():
+    wl, rank = PP_160, 0
+    sh = Shard(wl, rank, "bf16")
+    out = empty((wl.T, sh.Nq), "bf16")
+    bd.tp_prof_collect()
+    bd.tp_prof_enable(True)
+    try:
+        bd.tp_qkv_shard_fwd(wl.tp_size, rank, wl.B, wl.S, wl.H, wl.n_heads, sh.d_("X"), sh.d_("Wqkv"),
+                            sh.d_("bqkv"), out)
+        torch.cuda.synchronize()
+    finally:
+        bd.tp_prof_enable(False)
+    used = pp_launches("256x160pp")
+    assert sum(used.values()) == 1, f"160-wide launches {used}"
+    ref = oracle.tp_qkv_shard_fwd(wl.tp_size, rank, wl.B, wl.S, wl.H, wl.n_heads, sh.f64("X"), sh.f64("Wqkv"),
+                                  sh.f64("bqkv"))
+    assert_close(out, ref, "bf16", "QKV_r")
