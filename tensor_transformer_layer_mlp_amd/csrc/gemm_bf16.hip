@@ -906,20 +906,19 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
   int best = 0;
   double best_t = 1e300;
   // Xᵀ·dY (the weight gradients): both operands come through transposed LDS reads, and the 256 x 256
-  // tile moves ≈14% fewer LDS bytes per flop than 256 x 192; on outputs of 4096 x 4096 and more it was
-  // measured faster despite its coarser rounds (its partial last round fills with the concurrent
-  // input-gradient GEMM)
-  if (!d.a_kmajor && !d.b_kmajor && (long)d.M * d.N >= 4096L * 4096L) {
-    *cfg = 0;
-    return kTileName[0];
-  }
+  // tile moves ≈14% fewer LDS bytes per flop than 256 x 192; on outputs of 4096 x 4096 and more its
+  // rate there counts 1.1 (the GPT-3 weight gradients, 4.5 and 3.4 rounds of it, were measured faster
+  // on it than on 256 x 192's 6 and 4.5 rounds: its partial last round fills with the concurrent
+  // input-gradient GEMM), which still leaves 256 x 192 to an output it covers in as many rounds
+  const bool tn_big = !d.a_kmajor && !d.b_kmajor && (long)d.M * d.N >= 4096L * 4096L;
   for (int c : {9, 10, 11, 0, 8, 1, 2, 3}) {
     if (c >= 9 && !d.a_kmajor) continue;   // the ping-pong tiles take X·W and dY·Wᵀ only
     // the 160-wide tile paid only on a long k loop (the GPT-3 tp=8 QKV forward, k = 12288: 246 ->
     // 237 us, 232 tiles instead of 192); at k = 1600 and 3072 it was 1% slower than 192
     if (c == 11 && d.K < 8192) continue;
     const long t = (long)((d.M + kTileM[c] - 1) / kTileM[c]) * ((d.N + kTileN[c] - 1) / kTileN[c]);
-    const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / kTileRate[c];
+    const double rate = (tn_big && c == 0) ? 1.1 : kTileRate[c];
+    const double est = (double)((t + 255) / 256) * kTileM[c] * kTileN[c] / rate;
     if (est < best_t * 0.999) { best_t = est; best = c; }
   }
   *cfg = best;

@@ -1,7 +1,7 @@
 """GPU parity of the large-problem GEMM tiles: the ping-pong 256 x 192 tile (two groups of four waves
 one phase apart) on X·W and dY·Wᵀ, its 256 x 224 form (taken where it covers the n extent in fewer
-rounds of 256 tiles) and 256 x 160 form (long k loops), and the 256 x 256 tile the weight gradients Xᵀ·dY take from 4096 x 4096
-outputs on.
+rounds of 256 tiles) and 256 x 160 form (long k loops), and the 256 x 256 and 256 x 192 tiles of
+the weight gradients Xᵀ·dY.
 
 The tile is chosen for large problems with a K-major A only, so these MLP shard shapes are sized to
 make the MLP's X·W and dY·Wᵀ GEMMs take it: M, N around 2100 (ragged against 256, 192 and 64), and in
@@ -98,12 +98,16 @@ def test_mlp_bwd_pingpong(wl, rank):
         assert_close(o["db2"], ref["db2"], "bf16", "db2")
 
 
-# both weight gradients [4104, 4104] (ragged against 256) over K = T = 136 (ragged against 64)
-WG_BIG = LayerWorkload("wg_b1_s136_h4104_nh8_f8208_tp2", 1, 136, 4104, 8, 8208, 2, (0,), 0.03)
+# the weight gradients over K = T = 136 (ragged against 64): [4104, 3592] and [3592, 4104] (ragged
+# against 256) take the 256 x 256 tile in one round; [4104, 4104] — 289 tiles of 256 x 256 or 374 of
+# 256 x 192, two rounds either way — takes 256 x 192
+WG_256 = LayerWorkload("wg_b1_s136_h4104_nh8_f7184_tp2", 1, 136, 4104, 8, 7184, 2, (0,), 0.03)
+WG_192 = LayerWorkload("wg_b1_s136_h4104_nh8_f8208_tp2", 1, 136, 4104, 8, 8208, 2, (0,), 0.03)
 
 
-def test_weight_gradients_256_tile():
-    wl, rank = WG_BIG, 0
+@pytest.mark.parametrize("wl,tile", [(WG_256, "256x256, tn"), (WG_192, "256x192, tn")], ids=["256", "192"])
+def test_weight_gradients_tiles(wl, tile):
+    rank = 0
     sh = Shard(wl, rank, "bf16")
     T, H, Fr = wl.T, wl.H, sh.Fr
     o = dict(dX=empty((T, H), "bf16"), dW1=empty((H, Fr), "bf16"), db1=empty((Fr,), "bf16"),
@@ -117,8 +121,8 @@ def test_weight_gradients_256_tile():
         torch.cuda.synchronize()
     finally:
         bd.tp_prof_enable(False)
-    used = {tag: v[0] for tag, v in bd.tp_prof_collect().items() if "256x256, tn" in tag}
-    assert sum(used.values()) == 2, f"256 x 256 weight-gradient launches {used}"
+    used = {tag: v[0] for tag, v in bd.tp_prof_collect().items() if tile in tag}
+    assert sum(used.values()) == 2, f"{tile} weight-gradient launches {used}"
     ref = oracle.tp_mlp_shard_bwd(wl.tp_size, rank, T, H, wl.F, sh.f64("X"), sh.f64("W1"), sh.f64("W2"),
                                   sh.f64("A1"), sh.f64("Y"), sh.f64("dZ"))
     for k in ("dX", "dW1", "db1", "dW2", "db2"):
