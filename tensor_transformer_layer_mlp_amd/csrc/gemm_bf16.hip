@@ -891,11 +891,20 @@ bool gemm_bf16_eligible(const GemmDesc& d) {
   return supported;
 }
 
+// The k-split weight gradients (both operands MN-major, fp32 partials per slice): 256 x 256 (index 0,
+// rate 1.1 on this layout) or 256 x 192 (index 8, rate 0.95), by rounds of 256 tiles x tile area / rate.
+int gemm_bf16_wgrad_tile(int M, int N, int ks) {
+  const long t0 = (long)((M + 255) / 256) * ((N + 255) / 256) * ks, t8 = (long)((M + 255) / 256) * ((N + 191) / 192) * ks;
+  const double e0 = (double)((t0 + 255) / 256) * 65536 / 1.1, e8 = (double)((t8 + 255) / 256) * 49152 / 0.95;
+  return e8 < e0 * 0.999 ? 8 : 0;
+}
+
 // Tile choice by a small cost model.  A build may pin one
 // configuration with -DTP_GEMM_FORCE_CFG=<index> (tuning).
 const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
-  if (d.epi == EPI_F32) {   // fp32 partials: the ping-pong tile (K-major operands) or 256 x 256 (MN-major),
-    *cfg = d.a_kmajor ? 9 : 0;   // also in tuning builds
+  if (d.epi == EPI_F32) {   // fp32 partials: the ping-pong tile (K-major operands), or for MN-major ones
+    // (the k-split weight gradients) 256 x 256 or 256 x 192 by rounds x area / rate, also in tuning builds
+    *cfg = d.a_kmajor ? 9 : gemm_bf16_wgrad_tile(d.M, d.N, d.ksplit > 1 ? d.ksplit : 1);
     return kTileName[*cfg];
   }
 #ifdef TP_GEMM_FORCE_CFG
@@ -928,7 +937,7 @@ const char* gemm_bf16_pick(const GemmDesc& d, int* cfg) {
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
   switch (cfg) {
-    case 0:   // the weight gradients' split-k partials take this tile only
+    case 0:
       if (d.epi == EPI_F32 && !d.a_kmajor && !d.b_kmajor) return run<C0, false, false, EPI_F32>(d, s);
       return run_cfg<C0>(d, s);
     case 1: return run_cfg<C1>(d, s);
@@ -945,7 +954,9 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int cfg, hipStream_t s) {
     case 9: return run_pp_cfg<192>(d, s);
     case 10: return run_pp_cfg<224>(d, s);
     case 11: return run_pp_cfg<160>(d, s);
-    default: return run_cfg<C8>(d, s);
+    default:
+      if (d.epi == EPI_F32 && !d.a_kmajor && !d.b_kmajor) return run<C8, false, false, EPI_F32>(d, s);
+      return run_cfg<C8>(d, s);
   }
 }
 

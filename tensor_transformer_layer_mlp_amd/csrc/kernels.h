@@ -53,6 +53,8 @@ struct GemmDesc {
 };
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// The tile (0: 256 x 256, 8: 256 x 192) of an Xᵀ·dY weight gradient in ks fp32 k-slices.
+int gemm_bf16_wgrad_tile(int M, int N, int ks);
 // Whether the tiled kernels take this GEMM (shapes, strides, alignment, layout and epilogue).
 bool gemm_bf16_eligible(const GemmDesc& d);
 // out[i] = Σ_{s < S} parts[s·n + i] in that order, rounded to bf16 (n a multiple of 8).

@@ -103,9 +103,13 @@ def test_mlp_bwd_pingpong(wl, rank):
 # 256 x 192, two rounds either way — takes 256 x 192
 WG_256 = LayerWorkload("wg_b1_s136_h4104_nh8_f7184_tp2", 1, 136, 4104, 8, 7184, 2, (0,), 0.03)
 WG_192 = LayerWorkload("wg_b1_s136_h4104_nh8_f8208_tp2", 1, 136, 4104, 8, 8208, 2, (0,), 0.03)
+# k-split weight gradients (K = T = 4096, four fp32 slices summed in order): [1000, 1800] and
+# [1800, 1000] take 256 x 192 (192 slice-tiles in one round, against 128 of 256 x 256)
+WG_SPLIT = LayerWorkload("wgsplit_b1_s4096_h1000_nh8_f3600_tp2", 1, 4096, 1000, 8, 3600, 2, (0,), 0.03)
 
 
-@pytest.mark.parametrize("wl,tile", [(WG_256, "256x256, tn"), (WG_192, "256x192, tn")], ids=["256", "192"])
+@pytest.mark.parametrize("wl,tile", [(WG_256, "256x256, tn, epi0"), (WG_192, "256x192, tn, epi0"),
+                                     (WG_SPLIT, "256x192, tn, epi4")], ids=["256", "192", "192-ksplit"])
 def test_weight_gradients_tiles(wl, tile):
     rank = 0
     sh = Shard(wl, rank, "bf16")
