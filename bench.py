@@ -524,7 +524,7 @@ def residual_ln(bd, torch, wl, steps, warmup):
 STEP_LABELS = ["QKV fwd (NN+bias) 2048x4608x12288", "attn fwd", "fc1 (NN+bias+GeLU) 2048x6144x12288",
                "fc2 (NN+bias) 2048x12288x6144", "dA1 (NT+GeLU') 2048x6144x12288", "dW2 (TN) 6144x12288x2048",
                "db2 colsum partial", "db2 colsum final", "dX mlp (NT) 2048x12288x6144", "db1 colsum partial",
-               "db1 colsum final", "dW1 (TN) 12288x6144x2048", "attn rowdot", "attn bwd dK/dV", "attn bwd dQ",
+               "db1 colsum final", "dW1 (TN) 12288x6144x2048", "attn bwd dQ (+ row dots)", "attn bwd dK/dV",
                "dWqkv (TN) 12288x4608x2048", "dbqkv colsum partial", "dbqkv colsum final",
                "dX qkv (NT) 2048x12288x4608"]
 

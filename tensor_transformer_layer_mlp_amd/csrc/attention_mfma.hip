@@ -18,13 +18,14 @@
 //   Oᵀ += Vᵀ·Pᵀ  P stays in registers as the second operand; the key order of its 8 k-slots
 //                (4g+e and 16+4g+e) is matched by reading V with ds_read_b64_tr_b16.
 //   LSE = (m + log2 l)·ln 2.
-// Backward, deterministic (no atomics):
-//   rowdot  D_i = Σ_c dO_ic·O_ic                                   (fp32 workspace)
+// Backward, deterministic (no atomics), dQ first:
+//   dQ      one workgroup = 64 queries, waves of 32 queries: D_i = Σ_c dO_ic·O_ic from the wave's dO
+//           fragments and the same fragments of O (left in an fp32 workspace for dK/dV), then a loop
+//           over the key blocks up to them: S, P = exp2(t − LSE·log2 e), dP = dO·Vᵀ, dS = P∘(dP − D)
+//           in the query-owned layout, dQᵀ += Kᵀ·dSᵀ (K read transposed)
 //   dK/dV   one workgroup = 64 keys, waves of 32 keys, loop over the query blocks at or after them:
-//           Sᵀ, P = exp2(t − LSE·log2 e), dPᵀ = (dO·Vᵀ)ᵀ, dS = P∘(dP − D),
-//           dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS  (dO and Q read transposed from LDS)
-//   dQ      one workgroup = 64 queries, waves of 32 queries, loop over the key blocks up to them:
-//           S, dP, dS as above in the query-owned layout, dQᵀ += Kᵀ·dSᵀ (K read transposed).
+//           Sᵀ, P, dPᵀ, dS as above in the key-owned layout, dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS (dO and Q
+//           read transposed from LDS).
 // LDS tiles are KB rows (32 or 64) x (d padded to 32, 64 or 128) with the 32-byte chunk q of row r stored at
 // q ^ sw(r), which keeps both the 16-byte row reads and the transposed 4x16 reads spread over the
 // banks.  Tiles arrive by buffer_load_dwordx4 ... lds (two stages, next block in flight); rows past S
@@ -329,33 +330,6 @@ __global__ __launch_bounds__(128 * G) void attn_fwd_mfma(int B, int S, int nh, i
 }
 
 // ---------------------------------------------------------------------------------------------
-// D_i = Σ_c dO_ic·O_ic for every (token, head) row: 16 lanes per row, each lane one 16-byte piece of
-// both rows (pieces past d contribute zero), summed across the 16 lanes in a fixed butterfly order;
-// 16 rows per workgroup.  Consecutive rows (heads of a token, then tokens) are contiguous in ctx and
-// dctx, so each wave reads 1 KiB runs.
-template <int D>
-__global__ __launch_bounds__(256) void attn_rowdot(int B, int S, int nh, const bf16* __restrict__ ctx,
-                                                   const bf16* __restrict__ dctx, float* __restrict__ Dws) {
-  static_assert(D % 8 == 0 && D <= 128, "16 lanes of 8 elements cover a row");
-  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);   // row = token·nh + head
-  const int l = threadIdx.x & 15;
-  const long rows = (long)B * S * nh;
-  float acc = 0.f;
-  if (row < rows && 8 * l < D) {
-    const bf16x8 a = *(const bf16x8*)(ctx + row * D + 8 * l), z = *(const bf16x8*)(dctx + row * D + 8 * l);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)z[e];
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && l == 0) {
-    const int h = (int)(row % nh);
-    const long t = row / nh, b = t / S, s = t % S;
-    Dws[(b * nh + h) * S + s] = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 template <int D, int G, int KB>
 __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int nh, int nqb,
                                                              const bf16* __restrict__ qkv,
@@ -537,9 +511,10 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
 template <int D, int G, int KB>
 __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh, int nqb,
                                                             const bf16* __restrict__ qkv,
+                                                            const bf16* __restrict__ ctx,
                                                             const bf16* __restrict__ dctx,
                                                             const float* __restrict__ lse,
-                                                            const float* __restrict__ Dws,
+                                                            float* __restrict__ Dws,
                                                             bf16* __restrict__ dqkv) {
   using C = AC<D>;
   constexpr int TILE = C::template tile<KB>();
@@ -558,18 +533,27 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dq_mfma(int B, int S, int nh
   const int qw = qb * 64 + 32 * half;
   const float c = LOG2E / sqrtf((float)D);
 
+  // D_q = Σ_c dO_qc·O_qc from this wave's dO fragments and the same fragments of O: a lane's 8·NKK
+  // columns of a row, then the four lanes of the row (every lane ends with the row's sum); the waves of
+  // group 0 leave it in the workspace for the dK/dV kernel, which runs after this one
+  const bf16* orows = ctx + (long)b * S * cs + (long)h * D;
   bf16x8 qf[2][C::NKK], df[2][C::NKK];
   float lq[2], dq_[2];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
+    float dot = 0.f;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
       qf[qs][kk] = frag_global<D>(rows, rs, qw + 16 * qs, S, 32 * kk, lane);
       df[qs][kk] = frag_global<D>(dorows, cs, qw + 16 * qs, S, 32 * kk, lane);
+      const bf16x8 of = frag_global<D>(orows, cs, qw + 16 * qs, S, 32 * kk, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf((float)df[qs][kk][e], (float)of[e], dot);
     }
     const int q = qw + 16 * qs + i16;
     lq[qs] = q < S ? lse[((long)b * nh + h) * S + q] * LOG2E : INFINITY;
-    dq_[qs] = q < S ? Dws[((long)b * nh + h) * S + q] : 0.f;
+    dq_[qs] = xsum4(dot);
+    if (grp == 0 && g == 0 && q < S) Dws[((long)b * nh + h) * S + q] = dq_[qs];
   }
   f32x4 acc[2][C::NDB];
 #pragma unroll
@@ -724,12 +708,11 @@ hipError_t bwd_t(int B, int S, int nh, const void* qkv, const void* ctx, const f
                  const void* dctx, void* dqkv, float* ws, hipStream_t s) {
   constexpr int G = AttnShape<D>::G, KB = AttnShape<D>::KB;
   const int nqb = (S + 63) / 64;
-  const long rows = (long)B * S * nh;
-  attn_rowdot<D><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(B, S, nh, (const bf16*)ctx, (const bf16*)dctx, ws);
+  // dQ first: it takes D for its own queries from O and dO and leaves it in ws for dK/dV
+  attn_bwd_dq_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv, (const bf16*)ctx,
+                                                              (const bf16*)dctx, lse, ws, (bf16*)dqkv);
   attn_bwd_dkv_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
                                                                (const bf16*)dctx, lse, ws, (bf16*)dqkv);
-  attn_bwd_dq_mfma<D, G, KB><<<nqb * nh * B, 128 * G, 0, s>>>(B, S, nh, nqb, (const bf16*)qkv,
-                                                              (const bf16*)dctx, lse, ws, (bf16*)dqkv);
   return hipGetLastError();
 }
 
