@@ -89,6 +89,16 @@ __device__ __forceinline__ void load_tile(const bf16* rows, long rs, int nvalid,
   }
 }
 
+// N (<= 64) floats from src, the first nvalid in range, into dst by one wave as a direct global -> LDS
+// load: lane i (< N) writes dst[i], zero past nvalid; the lanes from N on are masked off.
+template <int N>
+__device__ __forceinline__ void load_floats(const float* src, int nvalid, TP_LDS float* dst, int lane) {
+  static_assert(N >= 1 && N <= 64, "one wave, one float per lane");
+  __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nvalid > 0 ? nvalid * 4 : 0, 0x00020000);
+  if (lane < N) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)dst, 4, lane < nvalid ? 4u * lane : OOB, 0, 0, 0);
+}
+
 // Row fragment: lane l gets row r0 + l%16, elements d0 + 8*(l/16) .. +7 (one 16-byte read).
 template <int D>
 __device__ __forceinline__ bf16x8 frag_row(const TP_LDS char* t, int r0, int d0, int lane) {
@@ -375,14 +385,16 @@ __global__ __launch_bounds__(128 * G) void attn_bwd_dkv_mfma(int B, int S, int n
 
   TP_LDS char* lds = (TP_LDS char*)smem + grp * 2 * STG;
   // the 64 threads of the group's first wave fill the LSE / D rows
+  // LSE and D come straight into LDS as well: a load into registers and a store to LDS here would
+  // make the compiler wait for every load in flight, the block's own tiles included.  Rows past S
+  // arrive as zeros, which contribute nothing: their Q and dO rows are zero, so P = 1 and dS = 0.
   auto stage = [&](int qb, TP_LDS char* dst) {
     const int q0 = qb * KB;
     load_tile<D, KB>(rows + (long)q0 * rs, rs, S - q0, dst, half, lane);
     load_tile<D, KB>(dorows + (long)q0 * cs, cs, S - q0, dst + TILE, half, lane);
-    if (half == 0 && lane < KB) {
-      const int q = q0 + lane;
-      ((TP_LDS float*)(dst + 2 * TILE))[lane] = q < S ? lse_bh[q] : INFINITY;
-      ((TP_LDS float*)(dst + 2 * TILE + 4 * KB))[lane] = q < S ? D_bh[q] : 0.f;
+    if (half == 0) {
+      load_floats<KB>(lse_bh + q0, S - q0, (TP_LDS float*)(dst + 2 * TILE), lane);
+      load_floats<KB>(D_bh + q0, S - q0, (TP_LDS float*)(dst + 2 * TILE + 4 * KB), lane);
     }
   };
   const int jq0 = 64 * kb / KB;            // first query block that reaches this key block
