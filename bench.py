@@ -619,6 +619,23 @@ def summarize(what, d, kernel, tag):
                                                                    b["WRITE_SIZE"] * fw / 1e6))
             fb = sum(a["FETCH_SIZE"] for a in fl) / len(fl) * ff
             wb = sum(b["WRITE_SIZE"] for b in wl_) / len(wl_) * fw
+            # every GEMM of the last step, in launch order (the pass runs the GPT-3 tp=8 rank-0 step; its
+            # nine GEMMs are the last nine GEMM dispatches): HBM-side bytes against the operands' unique bytes
+            gf = [e for e in f if "gemm" in short_kernel(e["name"])][-9:]
+            gw = [e for e in w if "gemm" in short_kernel(e["name"])][-9:]
+            if len(gf) == 9 and len(gw) == 9:
+                sh = gemm_site_shapes(2048, 12288, 4608, 6144)
+                print("# every GEMM of the last step: HBM-side fetch / write per dispatch, and the fetch over the")
+                print("# unique bytes of the operands it reads (A, B, and A1 for dA1's GeLU')")
+                print("# %-8s %6s %6s %6s %9s %9s %10s %8s" % ("site", "M", "N", "K", "fetch MB", "write MB",
+                                                               "unique MB", "refetch"))
+                for site, a, b in zip(sh, gf, gw):
+                    M, N, K = sh[site]
+                    uniq = 2.0 * (M * K + K * N + (M * N if site == "dA1" else 0))
+                    fm = a["FETCH_SIZE"] * ff
+                    print("# %-8s %6d %6d %6d %9.1f %9.1f %10.1f %7.2fx" % (site, M, N, K, fm / 1e6,
+                                                                           b["WRITE_SIZE"] * fw / 1e6, uniq / 1e6,
+                                                                           fm / uniq))
             print(f"trace_kernel: {kernel}")
             print(f"kernel: {tag}")
             print(f"sources_sha256: {gemm_sources_sha256()}")
